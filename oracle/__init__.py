@@ -1,0 +1,257 @@
+"""CPU oracle for the quantized linear layer -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s CPU-baseline
+leg may import this package.  It wraps ``liboracle.so`` (plain C, built from
+``oracle.c`` with gcc, no fast-math, no FP contraction) with numpy marshalling.
+It shares no code with the GPU library ``bit_quantized_linear_int8_amd``.
+
+Every function follows the page passages cited in ``oracle.c``:
+LLM.int8() (AIInfra 05Quantization01; Quantization explained part 2, §1.2),
+scale / zero-point / group granularity (模型推理量化 §4-§7) and the group
+Hadamard W4A4 scheme (分组旋转方法从W8A8到W4A4, §二, §5.1-§5.4).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+F32, F16, BF16 = 0, 1, 2
+
+CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+          "-fPIC", "-shared", "-Wall", "-Wextra"]
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with gcc (always when ``force``)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        L = ctypes.CDLL(_LIB)
+        P, I64, I32, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+        sig = {
+            "orc_f16_to_f64": (ctypes.c_double, [ctypes.c_uint16]),
+            "orc_f64_to_f16": (ctypes.c_uint16, [ctypes.c_double]),
+            "orc_f64_to_bf16": (ctypes.c_uint16, [ctypes.c_double]),
+            "orc_round_output": (None, [P, I64, ctypes.c_int, P]),
+            "orc_f16_to_f32_array": (None, [P, I64, P]),
+            "orc_outlier_cols": (None, [P, I64, I64, F, P, P, P, P]),
+            "orc_quant_rows_f32": (None, [P, I64, I64, I64, P, I32, I32, P, P, P, P]),
+            "orc_quant_rows_f16": (None, [P, I64, I64, I64, P, I32, I32, P, P, P, P]),
+            "orc_gemm_i8_i32": (I64, [P, P, I64, I64, I64, P, I64, P]),
+            "orc_qlinear_int8_mixed": (None, [P, I64, I64, P, P, P, I64, F, P, I64, P]),
+            "orc_hadamard_entry": (ctypes.c_int, [I32, I32]),
+            "orc_hadamard_rows": (None, [P, I64, I64, I32, P]),
+            "orc_pack_int4": (None, [P, I64, I64, P]),
+            "orc_unpack_int4": (None, [P, I64, I64, P]),
+            "orc_hadamard_quant_int4": (None, [P, I64, I64, I32, ctypes.c_int, I32, I32, P, P]),
+            "orc_w4a4_group_acc": (I64, [P, P, I64, I64, I64, I32, P, I64, P]),
+            "orc_qlinear_w4a4": (None, [P, I64, I64, P, P, I64, I32, P, I64, P]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _h16(x):
+    """fp16 array -> its uint16 bit patterns."""
+    return np.ascontiguousarray(x, dtype=np.float16).view(np.uint16)
+
+
+def _rows(rows):
+    if rows is None:
+        return None, 0
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    return r, int(r.size)
+
+
+# ---------------------------------------------------------------- formats
+def f16_to_f64(bits: int) -> float:
+    return lib().orc_f16_to_f64(int(bits))
+
+
+def f64_to_f16_bits(v: float) -> int:
+    return int(lib().orc_f64_to_f16(float(v)))
+
+
+def f64_to_bf16_bits(v: float) -> int:
+    return int(lib().orc_f64_to_bf16(float(v)))
+
+
+def round_output(x64: np.ndarray, dtype: int) -> np.ndarray:
+    """fp64 results -> fp32 array, or uint16 bit patterns for fp16 / bf16."""
+    x = _c(x64, np.float64)
+    out = np.empty(x.shape, np.float32 if dtype == F32 else np.uint16)
+    lib().orc_round_output(_ptr(x), x.size, dtype, _ptr(out))
+    return out
+
+
+def f16_to_f32(x16) -> np.ndarray:
+    h = _h16(x16)
+    out = np.empty(h.shape, np.float32)
+    lib().orc_f16_to_f32_array(_ptr(h), h.size, _ptr(out))
+    return out
+
+
+# ---------------------------------------------------------------- int8 path
+def outlier_cols(X16, tau: float):
+    """-> (mask u8 [K], idx i32 [count] ascending, colmax f32 [K])."""
+    h = _h16(X16)
+    M, K = h.shape
+    mask = np.zeros(K, np.uint8)
+    idx = np.zeros(max(K, 1), np.int32)
+    count = np.zeros(1, np.int32)
+    colmax = np.zeros(K, np.float32)
+    lib().orc_outlier_cols(_ptr(h), M, K, float(tau), _ptr(mask), _ptr(idx), _ptr(count), _ptr(colmax))
+    return mask, idx[: int(count[0])].copy(), colmax
+
+
+def quant_rows(x, gsize=None, mask=None, qmin=-127, qmax=127, s_in=None, z_in=None):
+    """Quantize rows of x (fp16 or fp32 array [rows x K]).  Returns (codes i8, scales f32|None)."""
+    x = np.asarray(x)
+    if x.ndim == 1:
+        x = x[None, :]
+    rows, K = x.shape
+    g = K if gsize is None else int(gsize)
+    q = np.zeros((rows, K), np.int8)
+    s_out = None if s_in is not None else np.zeros((rows, K // g), np.float32)
+    m = None if mask is None else _c(mask, np.uint8)
+    si = None if s_in is None else _c(s_in, np.float32)
+    zi = None if z_in is None else _c(z_in, np.int32)
+    if x.dtype == np.float16:
+        h = _h16(x)
+        lib().orc_quant_rows_f16(_ptr(h), rows, K, g, _ptr(m), qmin, qmax, _ptr(si), _ptr(zi), _ptr(q), _ptr(s_out))
+    else:
+        xf = _c(x, np.float32)
+        lib().orc_quant_rows_f32(_ptr(xf), rows, K, g, _ptr(m), qmin, qmax, _ptr(si), _ptr(zi), _ptr(q), _ptr(s_out))
+    return q, s_out
+
+
+def gemm_i8_i32(A, B, rows=None):
+    """C = A @ B.T with int64 sums stored as int32 ([nrows x N])."""
+    A = _c(A, np.int8)
+    B = _c(B, np.int8)
+    M, K = A.shape
+    N = B.shape[0]
+    r, nr = _rows(rows)
+    C = np.zeros((nr if r is not None else M, N), np.int32)
+    bad = lib().orc_gemm_i8_i32(_ptr(A), _ptr(B), M, K, N, _ptr(r), nr, _ptr(C))
+    if bad:
+        raise OverflowError("int32 accumulator overflow in %d results" % bad)
+    return C
+
+
+def qlinear_int8_mixed(X16, Wq, s_w, W16=None, tau=6.0, rows=None):
+    """LLM.int8() mixed linear in fp64: [nrows x N] (all rows if rows is None)."""
+    h = _h16(X16)
+    M, K = h.shape
+    Wq = _c(Wq, np.int8)
+    N = Wq.shape[0]
+    sw = _c(s_w, np.float32)
+    w16 = None if W16 is None else _h16(W16)
+    r, nr = _rows(rows)
+    out = np.zeros((nr if r is not None else M, N), np.float64)
+    lib().orc_qlinear_int8_mixed(_ptr(h), M, K, _ptr(Wq), _ptr(sw), _ptr(w16), N, float(tau),
+                                 _ptr(r), nr, _ptr(out))
+    return out
+
+
+# ---------------------------------------------------------------- W4A4 path
+def hadamard_entry(i: int, j: int) -> int:
+    return int(lib().orc_hadamard_entry(i, j))
+
+
+def hadamard_rows(X16, G: int) -> np.ndarray:
+    h = _h16(X16)
+    if h.ndim == 1:
+        h = h[None, :]
+    rows, K = h.shape
+    out = np.zeros((rows, K), np.float32)
+    lib().orc_hadamard_rows(_ptr(h), rows, K, int(G), _ptr(out))
+    return out
+
+
+def pack_int4(q) -> np.ndarray:
+    q = _c(q, np.int8)
+    if q.ndim == 1:
+        q = q[None, :]
+    rows, K = q.shape
+    out = np.zeros((rows, K // 8), np.uint32)
+    lib().orc_pack_int4(_ptr(q), rows, K, _ptr(out))
+    return out
+
+
+def unpack_int4(p, K: int) -> np.ndarray:
+    p = _c(p, np.uint32)
+    if p.ndim == 1:
+        p = p[None, :]
+    rows = p.shape[0]
+    out = np.zeros((rows, K), np.int8)
+    lib().orc_unpack_int4(_ptr(p), rows, K, _ptr(out))
+    return out
+
+
+def hadamard_quant_int4(X16, G: int, per_group: bool, qmin=-7, qmax=7):
+    """-> (packed u32 [rows x K/8], scales f32 [rows x (K/G if per_group else 1)])."""
+    h = _h16(X16)
+    if h.ndim == 1:
+        h = h[None, :]
+    rows, K = h.shape
+    packed = np.zeros((rows, K // 8), np.uint32)
+    s = np.zeros((rows, K // G if per_group else 1), np.float32)
+    lib().orc_hadamard_quant_int4(_ptr(h), rows, K, int(G), 1 if per_group else 0, qmin, qmax,
+                                  _ptr(packed), _ptr(s))
+    return packed, s
+
+
+def w4a4_group_acc(Xp, Wp, K: int, G: int, rows=None):
+    Xp = _c(Xp, np.uint32)
+    Wp = _c(Wp, np.uint32)
+    M, N = Xp.shape[0], Wp.shape[0]
+    r, nr = _rows(rows)
+    acc = np.zeros((nr if r is not None else M, N, K // G), np.int32)
+    bad = lib().orc_w4a4_group_acc(_ptr(Xp), _ptr(Wp), M, K, N, int(G), _ptr(r), nr, _ptr(acc))
+    if bad:
+        raise OverflowError("int32 accumulator overflow in %d results" % bad)
+    return acc
+
+
+def qlinear_w4a4(X16, Wp, s_w, G: int, rows=None):
+    h = _h16(X16)
+    M, K = h.shape
+    Wp = _c(Wp, np.uint32)
+    N = Wp.shape[0]
+    sw = _c(s_w, np.float32)
+    r, nr = _rows(rows)
+    out = np.zeros((nr if r is not None else M, N), np.float64)
+    lib().orc_qlinear_w4a4(_ptr(h), M, K, _ptr(Wp), _ptr(sw), N, int(G), _ptr(r), nr, _ptr(out))
+    return out

@@ -1,0 +1,400 @@
+"""Pins of the CPU oracle to what the pages and the mathematics fix.
+
+Nothing here compares the oracle with itself: every check goes against a
+value printed on a page (tests/golden), a closed form, a library routine
+(numpy, scipy, torch CPU) computing the same quantity another way, a special
+case that reduces to a textbook operation, or a rigorous error bound.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg
+from hypothesis import given, settings, strategies as st
+
+import oracle
+import synthetic
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ------------------------------------------------------------------ formats
+def test_f16_decode_all_bit_patterns_match_numpy():
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.f16_to_f64(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def test_f16_encode_matches_numpy_rounding():
+    rng = np.random.default_rng(1)
+    vals = np.concatenate([
+        rng.normal(0, 1, 4000), rng.normal(0, 3e4, 2000), rng.normal(0, 1e-5, 2000),
+        rng.normal(0, 1e-7, 1000),
+        # exact ties between neighbouring fp16 values, normal and subnormal
+        1.0 + np.arange(1, 200, 2) * 2.0 ** -11, np.arange(1, 200, 2) * 2.0 ** -25,
+        [65504.0, 65519.99, 65520.0, 70000.0, -65520.0, 0.0, -0.0, 2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -26],
+    ])
+    ref = vals.astype(np.float16).view(np.uint16)
+    got = np.array([oracle.f64_to_f16_bits(v) for v in vals], dtype=np.uint16)
+    assert np.array_equal(got, ref)
+    # ties go to the even neighbour
+    assert oracle.f64_to_f16_bits(1.0 + 2.0 ** -11) == 0x3C00
+    assert oracle.f64_to_f16_bits(1.0 + 3 * 2.0 ** -11) == 0x3C02
+
+
+def test_bf16_encode_matches_torch_rounding():
+    import torch
+    rng = np.random.default_rng(2)
+    f32 = np.concatenate([rng.normal(0, 1, 4000), rng.normal(0, 1e30, 500), rng.normal(0, 1e-39, 500),
+                          1.0 + np.arange(1, 100, 2) * 2.0 ** -8]).astype(np.float32)
+    ref = torch.from_numpy(f32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle.f64_to_bf16_bits(float(v)) for v in f32], dtype=np.uint16)
+    assert np.array_equal(got, ref)
+    assert oracle.f64_to_bf16_bits(1.0 + 2.0 ** -8) == 0x3F80          # tie -> even
+    assert oracle.f64_to_bf16_bits(3.4e38) == 0x7F80 or oracle.f64_to_bf16_bits(3.4e38) == 0x7F7F
+    assert oracle.f64_to_bf16_bits(1e39) == 0x7F80                     # overflow -> inf
+
+
+# ------------------------------------------------------------------ worked examples
+@pytest.mark.parametrize("as_f16", [False, True])
+def test_scale_example_int4(as_f16):
+    g = golden("scale_example.json")
+    x = np.array(g["W"], np.float16 if as_f16 else np.float32)
+    q, s = oracle.quant_rows(x, qmin=g["q_min"], qmax=g["q_max"])
+    s = float(s[0, 0])
+    assert round(s, g["s_printed_digits"]) == g["s_printed"]
+    assert s == np.float32(np.float32(np.abs(x.astype(np.float32)).max()) / np.float32(7))
+    i = g["W"].index(g["x_printed"])
+    assert q[0, i] == g["q_printed"]
+    assert round(q[0, i] * s, g["dequant_printed_digits"]) == g["dequant_printed"]
+    # the remaining codes follow from the same rule: -0.7/s = -5.44, -0.3/s = -2.33, 0.1/s = 0.78, 0.9/s = 7
+    assert q[0].tolist() == [-5, -2, 1, 3, 7]
+
+
+def test_outlier_collapse_example():
+    g = golden("outlier_example.json")
+    q, s = oracle.quant_rows(np.array(g["x"], np.float32), qmin=g["q_min"], qmax=g["q_max"])
+    assert round(float(s[0, 0]), g["s_printed_digits"]) == g["s_printed"]
+    assert q[0].tolist() == g["codes_printed"]
+
+
+def test_llm_int8_4096_example():
+    g = golden("llm_int8_4096.json")
+    rng = np.random.default_rng(3)
+    x = rng.uniform(-1, 1, g["hidden"]).astype(np.float16)
+    x[0], x[1] = 1.0, -1.0                       # ordinary channels reach exactly +-1
+    x[g["outlier_dim"]] = g["outlier_value"]
+    X = x[None, :]
+    # undecomposed: one scale over everything
+    q, s = oracle.quant_rows(X)
+    s = float(s[0, 0])
+    assert round(s, g["s_undecomposed_digits"]) == g["s_undecomposed_printed"]
+    assert abs(int(q[0, 0])) in g["levels_undecomposed_printed"] and q[0, 0] == -q[0, 1]
+    assert set(np.abs(q[0, 2:g["outlier_dim"]]).tolist()) <= {0, 1, 2}
+    # decomposed at threshold 6.0
+    mask, idx, colmax = oracle.outlier_cols(X, g["threshold"])
+    assert idx.tolist() == [g["outlier_dim"]]
+    q2, s2 = oracle.quant_rows(X, mask=mask)
+    s2 = float(s2[0, 0])
+    assert round(s2, g["s_split_digits"]) == g["s_split_printed"]
+    assert q2[0, 0] == g["level_split_printed"] and q2[0, 1] == -g["level_split_printed"]
+    assert q2[0, g["outlier_dim"]] == 0
+
+
+def test_affine_static_mode_closed_form():
+    # q = clip(round(x/s) + z, qmin, qmax) with ties to even (模型推理量化 §6.2)
+    q, _ = oracle.quant_rows(np.array([0.5, 1.5, 2.5, -0.5, -1.5, -2.5], np.float32),
+                             s_in=[1.0], z_in=[0], qmin=-128, qmax=127)
+    assert q[0].tolist() == [0, 2, 2, 0, -2, -2]
+    q, _ = oracle.quant_rows(np.array([1.0, -1.0, 100.0, -300.0], np.float32),
+                             s_in=[0.5], z_in=[3], qmin=-128, qmax=127)
+    assert q[0].tolist() == [5, 1, 127, -128]
+
+
+def test_zero_row_gets_safe_scale():
+    q, s = oracle.quant_rows(np.zeros((2, 16), np.float16))
+    assert s.ravel().tolist() == [1.0, 1.0] and not q.any()
+
+
+def test_int4_packing_words():
+    # codes of the two 模型推理量化 examples (§4, §5), zero-padded to 8, plus a
+    # sign pattern; element i of a word sits in bits [4i+3:4i].
+    cases = [([-5, -2, 1, 3, 7, 0, 0, 0], 0x000731EB),
+             ([0, 0, 0, 0, 0, 7, 0, 0], 0x00700000),
+             ([1, -1, 2, -2, 3, -3, 7, -7], 0x97D3E2F1),
+             ([-8, 7, 0, 0, 0, 0, 0, -1], 0xF0000078)]
+    for codes, word in cases:
+        assert int(oracle.pack_int4(np.array(codes))[0, 0]) == word
+        assert oracle.unpack_int4(np.array([word], np.uint32), 8)[0].tolist() == codes
+
+
+def test_int4_quant_via_identity_rotation_matches_examples():
+    g = golden("scale_example.json")
+    x = np.zeros(8, np.float16)
+    x[:5] = g["W"]
+    packed, s = oracle.hadamard_quant_int4(x, G=1, per_group=False)
+    assert int(packed[0, 0]) == 0x000731EB
+    assert round(float(s[0, 0]), 4) == g["s_printed"]
+
+
+# ------------------------------------------------------------------ outlier set
+def test_outlier_cols_match_numpy_definition():
+    rng = np.random.default_rng(4)
+    for M, K in [(1, 8), (7, 64), (33, 300)]:
+        X = rng.normal(0, 3, (M, K)).astype(np.float16)
+        X[0, 0] = 6.0                 # exactly at the threshold: not an outlier
+        X[-1, -1] = np.float16(-6.0039)
+        for tau in (6.0, 0.0, -1.0, float("inf")):
+            mask, idx, colmax = oracle.outlier_cols(X, tau)
+            cm = np.abs(X.astype(np.float32)).max(axis=0)
+            assert np.array_equal(colmax, cm)
+            assert idx.tolist() == np.nonzero(cm > np.float32(tau))[0].tolist()
+            assert np.array_equal(mask, (cm > np.float32(tau)).astype(np.uint8))
+        assert 0 not in oracle.outlier_cols(X[:, :1] * 0 + np.float16(6.0), 6.0)[1]
+
+
+def test_planted_outlier_sets():
+    c = synthetic.config("tiny_mixed")
+    assert oracle.outlier_cols(c["X"], 6.0)[1].tolist() == [17, 200]
+    X, W, dims = synthetic.mixed_inputs(64, 1024, 8, seed=5, n_dims=7)
+    assert set(dims.tolist()) <= set(oracle.outlier_cols(X, 6.0)[1].tolist())
+
+
+# ------------------------------------------------------------------ integer GEMM
+@settings(max_examples=40, deadline=None)
+@given(M=st.integers(1, 40), K=st.integers(1, 300), N=st.integers(1, 70), seed=st.integers(0, 2 ** 31))
+def test_gemm_i8_bruteforce(M, K, N, seed):
+    rng = np.random.default_rng(seed)
+    A = rng.integers(-128, 128, (M, K), dtype=np.int8)
+    B = rng.integers(-128, 128, (N, K), dtype=np.int8)
+    C = oracle.gemm_i8_i32(A, B)
+    assert np.array_equal(C, A.astype(np.int64) @ B.astype(np.int64).T)
+    rows = rng.choice(M, size=min(M, 3), replace=False)
+    assert np.array_equal(oracle.gemm_i8_i32(A, B, rows=rows), C[rows])
+
+
+def test_gemm_i8_overflow_detected():
+    K = 131073                               # 131073 * 128^2 > 2^31 - 1
+    A = np.full((1, K), -128, np.int8)
+    with pytest.raises(OverflowError):
+        oracle.gemm_i8_i32(A, A)
+
+
+# ------------------------------------------------------------------ mixed linear
+def _w8(W):
+    Wq, s_w = oracle.quant_rows(W)
+    return Wq, s_w[:, 0]
+
+
+def test_mixed_tau_inf_is_plain_vectorwise_w8a8():
+    X, W, _ = synthetic.mixed_inputs(24, 512, 40, seed=6, n_dims=3)
+    Wq, s_w = _w8(W)
+    out = oracle.qlinear_int8_mixed(X, Wq, s_w, tau=float("inf"))
+    Xq, s_x = oracle.quant_rows(X)
+    C = Xq.astype(np.int64) @ Wq.astype(np.int64).T
+    ref = C.astype(np.float64) * s_x.astype(np.float64) * s_w.astype(np.float64)[None, :]
+    assert np.array_equal(out, ref)
+
+
+def test_mixed_all_outliers_is_plain_fp16_gemm():
+    X, W, _ = synthetic.mixed_inputs(12, 256, 30, seed=7, n_dims=2)
+    Wq, s_w = _w8(W)
+    X64, W64 = X.astype(np.float64), W.astype(np.float64)
+    out = oracle.qlinear_int8_mixed(X, Wq, s_w, W16=W, tau=-1.0)
+    mag = np.abs(X64) @ np.abs(W64).T
+    assert np.all(np.abs(out - X64 @ W64.T) <= 1e-13 * mag + 1e-300)
+    # without W16 the fp16 weights are fp16(fp32(s_w * Wq))
+    wt = (s_w[:, None] * Wq.astype(np.float32)).astype(np.float16).astype(np.float64)
+    out2 = oracle.qlinear_int8_mixed(X, Wq, s_w, tau=-1.0)
+    assert np.all(np.abs(out2 - X64 @ wt.T) <= 1e-13 * (np.abs(X64) @ np.abs(wt).T) + 1e-300)
+
+
+def _mixed_error_bound(X, W, tau, w16_given):
+    """Rigorous bound on |out - X W^T| from |x - s q| <= s/2 per code."""
+    X32 = X.astype(np.float32)
+    W32 = W.astype(np.float32)
+    cm = np.abs(X32).max(axis=0)
+    O = cm > np.float32(tau)
+    a_x = np.where(O[None, :], 0, np.abs(X32)).max(axis=1)
+    s_x = np.where(a_x == 0, np.float32(1), a_x / np.float32(127)).astype(np.float64)
+    a_w = np.abs(W32).max(axis=1)
+    s_w = np.where(a_w == 0, np.float32(1), a_w / np.float32(127)).astype(np.float64)
+    aX = np.abs(X.astype(np.float64))
+    aW = np.abs(W.astype(np.float64))
+    nonO = (~O).astype(np.float64)
+    B = 0.5 * s_x[:, None] * ((aW * nonO) @ np.ones(X.shape[1]) + 0.5 * s_w * nonO.sum())[None, :] \
+        + 0.5 * (aX * nonO) @ np.ones(X.shape[1])[:, None] * s_w[None, :]
+    if not w16_given:
+        On = O.astype(np.float64)
+        B = B + (aX * On) @ (0.5 * s_w[:, None] + (aW + 0.5 * s_w[:, None]) * 2.0 ** -10).T * On.any()
+    return B * (1 + 1e-5) + 1e-12
+
+
+@pytest.mark.parametrize("w16_given", [True, False])
+def test_mixed_within_quantization_error_bound(w16_given):
+    X, W, dims = synthetic.mixed_inputs(40, 768, 56, seed=8, n_dims=5, p_token=0.75)
+    Wq, s_w = _w8(W)
+    out = oracle.qlinear_int8_mixed(X, Wq, s_w, W16=W if w16_given else None, tau=6.0)
+    exact = X.astype(np.float64) @ W.astype(np.float64).T
+    B = _mixed_error_bound(X, W, 6.0, w16_given)
+    assert np.all(np.abs(out - exact) <= B)
+    # the bound is tight enough that dropping the outlier part breaks it
+    Xn = X.copy()
+    Xn[:, dims] = 0
+    no_outl = oracle.qlinear_int8_mixed(Xn, Wq, s_w, W16=W, tau=6.0)
+    assert np.any(np.abs(no_outl - exact) > B)
+
+
+def test_mixed_row_sampling_matches_full():
+    X, W, _ = synthetic.mixed_inputs(20, 256, 24, seed=9, n_dims=3)
+    Wq, s_w = _w8(W)
+    full = oracle.qlinear_int8_mixed(X, Wq, s_w, tau=6.0)
+    rows = np.array([19, 0, 7])
+    assert np.array_equal(oracle.qlinear_int8_mixed(X, Wq, s_w, tau=6.0, rows=rows), full[rows])
+
+
+def test_decomposition_lowers_error():
+    c = synthetic.config("tiny_mixed")
+    X, W = c["X"], c["W"]
+    Wq, s_w = _w8(W)
+    exact = X.astype(np.float64) @ W.astype(np.float64).T
+    e_split = np.abs(oracle.qlinear_int8_mixed(X, Wq, s_w, W16=W, tau=6.0) - exact).max()
+    e_plain = np.abs(oracle.qlinear_int8_mixed(X, Wq, s_w, W16=W, tau=float("inf")) - exact).max()
+    assert e_split < e_plain / 3
+
+
+def test_output_rounding():
+    x = np.array([1.0, 1.0 + 2.0 ** -11, -70000.0, 1e-8, 3.0 + 2.0 ** -30])
+    assert np.array_equal(oracle.round_output(x, oracle.F16), x.astype(np.float16).view(np.uint16))
+    assert np.array_equal(oracle.round_output(x, oracle.F32), x.astype(np.float32))
+
+
+# ------------------------------------------------------------------ Hadamard
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16, 32, 64, 128, 256])
+def test_hadamard_orthogonal_and_sylvester(G):
+    H = np.array([[oracle.hadamard_entry(i, j) for j in range(G)] for i in range(G)], np.int64)
+    assert np.array_equal(H @ H.T, G * np.eye(G, dtype=np.int64))
+    assert np.array_equal(H, scipy.linalg.hadamard(G))
+
+
+@pytest.mark.parametrize("G", [1, 8, 64, 128, 256])
+def test_hadamard_rows_match_scipy_exactly(G):
+    X, _, _ = synthetic.mixed_inputs(6, 512, 1, seed=10 + G, n_dims=4, magnitude=("uniform", 50, 60000))
+    X[0, :8] = [65504, -65504, 2 ** -24, -(2 ** -24), 6e-5, 1, -1, 0]
+    H = scipy.linalg.hadamard(G).astype(np.float64)
+    c = 1.0 / math.sqrt(G)
+    ref = ((X.astype(np.float64).reshape(6, -1, G) @ H) * c).astype(np.float32).reshape(6, 512)
+    assert np.array_equal(oracle.hadamard_rows(X, G), ref)
+
+
+def test_hadamard_constant_row():
+    x = np.ones(128, np.float16)
+    y = oracle.hadamard_rows(x, 128)[0]
+    assert y[0] == np.float32(128 * (1.0 / math.sqrt(128.0))) and not y[1:].any()
+    packed, s = oracle.hadamard_quant_int4(x, 128, per_group=False)
+    codes = oracle.unpack_int4(packed, 128)[0]
+    assert codes[0] == 7 and not codes[1:].any()
+
+
+def test_rotation_cancels_in_the_product():
+    X, W = synthetic.w4a4_inputs(16, 512, 24, seed=11)[:2]
+    Xr = oracle.hadamard_rows(X, 128).astype(np.float64)
+    Wr = oracle.hadamard_rows(W, 128).astype(np.float64)
+    exact = X.astype(np.float64) @ W.astype(np.float64).T
+    mag = np.abs(X.astype(np.float64)) @ np.abs(W.astype(np.float64)).T
+    assert np.all(np.abs(Xr @ Wr.T - exact) <= 2.0 ** -21 * mag * 16)
+
+
+# ------------------------------------------------------------------ W4A4
+def _unpack_np(p, K):
+    p = p.astype(np.uint64)
+    nib = ((p[..., None] >> (4 * np.arange(8, dtype=np.uint64))) & 0xF).astype(np.int64)
+    nib = np.where(nib >= 8, nib - 16, nib)
+    return nib.reshape(p.shape[0], K)
+
+
+def test_pack_roundtrip_random():
+    rng = np.random.default_rng(12)
+    q = rng.integers(-8, 8, (9, 64)).astype(np.int8)
+    p = oracle.pack_int4(q)
+    assert np.array_equal(_unpack_np(p, 64), q)
+    assert np.array_equal(oracle.unpack_int4(p, 64), q)
+
+
+@pytest.mark.parametrize("G", [8, 64, 128])
+def test_hadamard_quant_int4_matches_library_composition(G):
+    X, _, _ = synthetic.mixed_inputs(5, 256, 1, seed=13, n_dims=3, magnitude=("abs_normal", 50.0))
+    H = scipy.linalg.hadamard(G).astype(np.float64)
+    xr = ((X.astype(np.float64).reshape(5, -1, G) @ H) * (1.0 / math.sqrt(G))).astype(np.float32)
+    for per_group in (False, True):
+        packed, s = oracle.hadamard_quant_int4(X, G, per_group=per_group)
+        a = np.abs(xr).max(axis=2) if per_group else np.abs(xr).reshape(5, -1).max(axis=1, keepdims=True)
+        s_ref = np.where(a == 0, np.float32(1), a / np.float32(7)).astype(np.float32)
+        assert np.array_equal(s, s_ref)
+        sb = s_ref[:, :, None] if per_group else s_ref[:, :, None]
+        q_ref = np.clip(np.rint(xr / sb), -7, 7).reshape(5, 256)
+        assert np.array_equal(_unpack_np(packed, 256), q_ref)
+
+
+@settings(max_examples=15, deadline=None)
+@given(M=st.integers(1, 12), N=st.integers(1, 20), groups=st.integers(1, 4), G=st.sampled_from([8, 64, 128]),
+       seed=st.integers(0, 2 ** 31))
+def test_w4a4_group_acc_bruteforce(M, N, groups, G, seed):
+    K = G * groups
+    rng = np.random.default_rng(seed)
+    Xp = rng.integers(0, 2 ** 32, (M, K // 8), dtype=np.uint64).astype(np.uint32)
+    Wp = rng.integers(0, 2 ** 32, (N, K // 8), dtype=np.uint64).astype(np.uint32)
+    acc = oracle.w4a4_group_acc(Xp, Wp, K, G)
+    x = _unpack_np(Xp, K).reshape(M, groups, G)
+    w = _unpack_np(Wp, K).reshape(N, groups, G)
+    assert np.array_equal(acc, np.einsum("mgk,ngk->mng", x, w))
+
+
+def test_w4a4_output_matches_dequant_matmul_and_error_bound():
+    M, K, N, G = 12, 512, 20, 128
+    X, W, _ = synthetic.w4a4_inputs(M, K, N, seed=14)
+    Wp, s_w = oracle.hadamard_quant_int4(W, G, per_group=True)
+    out = oracle.qlinear_w4a4(X, Wp, s_w, G)
+    Xp, s_x = oracle.hadamard_quant_int4(X, G, per_group=False)
+    xd = _unpack_np(Xp, K) * s_x.astype(np.float64)
+    wd = _unpack_np(Wp, K) * np.repeat(s_w.astype(np.float64), G, axis=1)
+    mag = np.abs(xd) @ np.abs(wd).T
+    assert np.all(np.abs(out - xd @ wd.T) <= 1e-12 * mag)
+    # error bound against the unquantized product (rotation is orthogonal)
+    H = scipy.linalg.hadamard(G).astype(np.float64) / math.sqrt(G)
+    xr = (X.astype(np.float64).reshape(M, -1, G) @ H).reshape(M, K)
+    wr = (W.astype(np.float64).reshape(N, -1, G) @ H).reshape(N, K)
+    sx = np.abs(xr.astype(np.float32)).max(axis=1).astype(np.float64) / 7 * (1 + 1e-6)
+    sw = np.repeat(np.abs(wr.astype(np.float32)).reshape(N, -1, G).max(axis=2) / 7, G, axis=1) * (1 + 1e-6)
+    B = 0.5 * sx[:, None] * ((np.abs(wr) + 0.5 * sw).sum(axis=1))[None, :] + 0.5 * np.abs(xr) @ sw.T
+    exact = X.astype(np.float64) @ W.astype(np.float64).T
+    slack = 2.0 ** -20 * (np.abs(xr) @ np.abs(wr).T)
+    assert np.all(np.abs(out - exact) <= B + slack)
+    # a mis-grouped weight scale breaks the dequantize-then-matmul identity
+    out_bad = oracle.qlinear_w4a4(X, Wp, s_w[:, ::-1].copy(), G)
+    assert not np.all(np.abs(out_bad - xd @ wd.T) <= 1e-6 * mag)
+
+
+def test_rotation_lowers_w4a4_error():
+    # qualitative claim of the group-rotation page (§二): rotating before int4
+    # quantization lowers the error; compared with the identity rotation and
+    # the same 128-wide weight groups.
+    M, K, N = 16, 512, 24
+    X, W, _ = synthetic.w4a4_inputs(M, K, N, seed=15)
+    exact = X.astype(np.float64) @ W.astype(np.float64).T
+    Wp, s_w = oracle.hadamard_quant_int4(W, 128, per_group=True)
+    err_rot = np.abs(oracle.qlinear_w4a4(X, Wp, s_w, 128) - exact).mean()
+    qx, sx = oracle.quant_rows(X, qmin=-7, qmax=7)
+    qw, sw = oracle.quant_rows(W, gsize=128, qmin=-7, qmax=7)
+    plain = (qx * sx.astype(np.float64)) @ (qw * np.repeat(sw.astype(np.float64), 128, axis=1)).T
+    assert err_rot < np.abs(plain - exact).mean() / 2
