@@ -1,0 +1,220 @@
+"""Python binding of libqa -- quantized linear layers on AMD MI355X (gfx950).
+
+A thin ctypes layer over the C ABI of ``include/qa.h``: every function has the
+name of the C entry point it calls, takes torch tensors that live on the GPU,
+allocates the outputs it returns, passes raw device pointers and the current
+HIP stream, and raises ``QAError`` on a non-zero status.  All arithmetic runs
+in the HIP kernels of ``libqa.so``; there is no fallback path.  If the library
+is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqa.so")
+
+QA_F32, QA_F16, QA_BF16 = 0, 1, 2
+QA_SCALE_PER_ROW, QA_SCALE_PER_GROUP = 0, 1
+
+EXPORTS = (
+    "qa_status_string", "qa_last_error",
+    "qa_outlier_cols_workspace", "qa_outlier_cols",
+    "qa_quantize_rowwise_int8",
+    "qa_qlinear_int8_mixed_workspace", "qa_qlinear_int8_mixed",
+    "qa_hadamard_quant_int4",
+    "qa_qlinear_w4a4_workspace", "qa_qlinear_w4a4",
+    "qa_gemm_i8_i32", "qa_gemm_w4a4_group_acc",
+)
+
+_DTYPE_CODE = {torch.float32: QA_F32, torch.float16: QA_F16, torch.bfloat16: QA_BF16}
+
+
+class QAError(RuntimeError):
+    def __init__(self, fn, status, detail):
+        super().__init__("%s failed: %s (%s)" % (fn, status, detail))
+        self.status = status
+        self.detail = detail
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libqa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libqa.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I32, F, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+        S = ctypes.c_int
+        sig = {
+            "qa_status_string": (ctypes.c_char_p, [S]),
+            "qa_last_error": (ctypes.c_char_p, []),
+            "qa_outlier_cols_workspace": (SZ, [I64]),
+            "qa_outlier_cols": (S, [P, I64, I64, F, P, P, P, P, P, SZ, P]),
+            "qa_quantize_rowwise_int8": (S, [P, I64, I64, P, I32, I32, P, P, P, P, P]),
+            "qa_qlinear_int8_mixed_workspace": (SZ, [I64, I64]),
+            "qa_qlinear_int8_mixed": (S, [P, I64, I64, P, P, P, I64, F, P, S, P, SZ, P]),
+            "qa_hadamard_quant_int4": (S, [P, I64, I64, I32, S, I32, I32, P, P, P]),
+            "qa_qlinear_w4a4_workspace": (SZ, [I64, I64]),
+            "qa_qlinear_w4a4": (S, [P, I64, I64, P, P, I64, I32, P, S, P, SZ, P]),
+            "qa_gemm_i8_i32": (S, [P, P, I64, I64, I64, P, P]),
+            "qa_gemm_w4a4_group_acc": (S, [P, P, I64, I64, I64, I32, P, P]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(s: int) -> str:
+    return lib().qa_status_string(int(s)).decode()
+
+
+def last_error() -> str:
+    return lib().qa_last_error().decode()
+
+
+def _check(fn: str, s: int):
+    if s != 0:
+        raise QAError(fn, status_string(s), last_error())
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t, name, dtype=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a CUDA (HIP) tensor" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _workspace(nbytes, device, ws):
+    if ws is not None:
+        return ws
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------- entry points
+def qa_outlier_cols_workspace(K: int) -> int:
+    return int(lib().qa_outlier_cols_workspace(K))
+
+
+def qa_outlier_cols(X, threshold=6.0, scratch=None, stream=None):
+    """-> (mask u8 [K], idx i32 [K] (first `count` valid), count i32 [1], colmax f32 [K])."""
+    _dev(X, "X", torch.float16)
+    M, K = X.shape
+    dev = X.device
+    mask = torch.empty(K, dtype=torch.uint8, device=dev)
+    idx = torch.empty(K, dtype=torch.int32, device=dev)
+    count = torch.empty(1, dtype=torch.int32, device=dev)
+    colmax = torch.empty(K, dtype=torch.float32, device=dev)
+    nb = qa_outlier_cols_workspace(K)
+    scratch = _workspace(nb, dev, scratch)
+    _check("qa_outlier_cols", lib().qa_outlier_cols(_p(X), M, K, float(threshold), _p(mask), _p(idx), _p(count),
+                                                     _p(colmax), _p(scratch), scratch.numel(), _stream(stream)))
+    return mask, idx, count, colmax
+
+
+def qa_quantize_rowwise_int8(X, mask=None, q_min=-127, q_max=127, s_in=None, z_in=None, stream=None):
+    """-> (Xq i8 [rows x K], s f32 [rows] or None in static mode)."""
+    _dev(X, "X", torch.float16)
+    rows, K = X.shape
+    Xq = torch.empty((rows, K), dtype=torch.int8, device=X.device)
+    s_out = None if s_in is not None else torch.empty(rows, dtype=torch.float32, device=X.device)
+    _check("qa_quantize_rowwise_int8",
+           lib().qa_quantize_rowwise_int8(_p(X), rows, K, _p(mask), int(q_min), int(q_max), _p(s_in), _p(z_in),
+                                          _p(Xq), _p(s_out), _stream(stream)))
+    return Xq, s_out
+
+
+def qa_qlinear_int8_mixed_workspace(M: int, K: int) -> int:
+    return int(lib().qa_qlinear_int8_mixed_workspace(M, K))
+
+
+def qa_qlinear_int8_mixed(X, Wq, s_w, W16=None, threshold=6.0, out_dtype=torch.float16, out=None,
+                          workspace=None, stream=None):
+    """LLM.int8() mixed-precision linear -> out [M x N] of out_dtype."""
+    _dev(X, "X", torch.float16)
+    _dev(Wq, "Wq", torch.int8)
+    _dev(s_w, "s_w", torch.float32)
+    if W16 is not None:
+        _dev(W16, "W16", torch.float16)
+    M, K = X.shape
+    N = Wq.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=X.device)
+    workspace = _workspace(qa_qlinear_int8_mixed_workspace(M, K), X.device, workspace)
+    _check("qa_qlinear_int8_mixed",
+           lib().qa_qlinear_int8_mixed(_p(X), M, K, _p(Wq), _p(s_w), _p(W16), N, float(threshold), _p(out),
+                                       _DTYPE_CODE[out.dtype], _p(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def qa_hadamard_quant_int4(X, G: int, per_group: bool, q_min=-7, q_max=7, stream=None):
+    """-> (packed u32 as int32 [rows x K/8], s f32 [rows x (K/G if per_group else 1)])."""
+    _dev(X, "X", torch.float16)
+    rows, K = X.shape
+    packed = torch.empty((rows, K // 8), dtype=torch.int32, device=X.device)
+    s = torch.empty((rows, K // G if per_group else 1), dtype=torch.float32, device=X.device)
+    _check("qa_hadamard_quant_int4",
+           lib().qa_hadamard_quant_int4(_p(X), rows, K, int(G), QA_SCALE_PER_GROUP if per_group else QA_SCALE_PER_ROW,
+                                        int(q_min), int(q_max), _p(packed), _p(s), _stream(stream)))
+    return packed, s
+
+
+def qa_qlinear_w4a4_workspace(M: int, K: int) -> int:
+    return int(lib().qa_qlinear_w4a4_workspace(M, K))
+
+
+def qa_qlinear_w4a4(X, Wp, s_w, G=128, out_dtype=torch.float32, out=None, workspace=None, stream=None):
+    """W4A4 group-Hadamard linear -> out [M x N]."""
+    _dev(X, "X", torch.float16)
+    _dev(Wp, "Wp", torch.int32)
+    _dev(s_w, "s_w", torch.float32)
+    M, K = X.shape
+    N = Wp.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=X.device)
+    workspace = _workspace(qa_qlinear_w4a4_workspace(M, K), X.device, workspace)
+    _check("qa_qlinear_w4a4",
+           lib().qa_qlinear_w4a4(_p(X), M, K, _p(Wp), _p(s_w), N, int(G), _p(out), _DTYPE_CODE[out.dtype],
+                                 _p(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def qa_gemm_i8_i32(A, B, stream=None):
+    _dev(A, "A", torch.int8)
+    _dev(B, "B", torch.int8)
+    M, K = A.shape
+    N = B.shape[0]
+    C = torch.empty((M, N), dtype=torch.int32, device=A.device)
+    _check("qa_gemm_i8_i32", lib().qa_gemm_i8_i32(_p(A), _p(B), M, K, N, _p(C), _stream(stream)))
+    return C
+
+
+def qa_gemm_w4a4_group_acc(Xp, Wp, K: int, G: int, stream=None):
+    _dev(Xp, "Xp", torch.int32)
+    _dev(Wp, "Wp", torch.int32)
+    M, N = Xp.shape[0], Wp.shape[0]
+    acc = torch.empty((M, N, K // G), dtype=torch.int32, device=Xp.device)
+    _check("qa_gemm_w4a4_group_acc",
+           lib().qa_gemm_w4a4_group_acc(_p(Xp), _p(Wp), M, K, N, int(G), _p(acc), _stream(stream)))
+    return acc

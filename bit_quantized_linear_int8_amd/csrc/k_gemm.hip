@@ -1,0 +1,523 @@
+// k_gemm.hip -- integer GEMMs of the quantized linear layer on gfx950 MFMA.
+//
+//   int8:  C = Xq * Wq^T on v_mfma_i32_16x16x64_i8 with int32 accumulation,
+//          then either an int32 store or the LLM.int8() epilogue: dequantize
+//          by s_x[m] * s_w[n] (outer product of the vector-wise scales) and
+//          add the fp16 product over the outlier columns, gathered from X and
+//          W and run on v_mfma_f32_16x16x32_f16 with the dequantized tile as
+//          the accumulator input.
+//          [AIInfra 05Quantization01, LLM.int8(): "b. INT8 矩阵乘法与反量化"
+//           and the merge of the fp16 outlier part]
+//   W4A4:  packed int4 operands (eight per 32-bit word) are unpacked into the
+//          high nibble of each int8 lane of the same MFMA, so every product is
+//          256 x the int4 product; each G-group is accumulated in int32 on its
+//          own and dequantized by s_w[n][g] * 2^-8 into an fp32 sum, scaled
+//          by s_x[m] at the end.
+//          [低比特量化加速：分组旋转方法从W8A8到W4A4, §5.4]
+//
+// Both operands are K-contiguous ([rows x K]).  A stage of BK bytes of K per
+// row is staged in LDS with the 16-byte chunk index XOR-swizzled by the row
+// (chunk c of row r lives at chunk c ^ (r & 7)), so the 16-byte fragment
+// reads of one MFMA hit distinct banks.  Global loads of stage k+1 are in
+// flight while stage k is multiplied (two LDS buffers, one barrier per stage).
+// The MFMA k-permutation only has to agree between the two operands, which
+// is what lets the int4 unpack skip the nibble interleave.
+#include "qa_device.hpp"
+#include "qa_launch.hpp"
+
+namespace qa {
+
+template <int BM_, int BN_, int WM_, int WN_>
+struct Cfg {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int BK = 128;                        // bytes of K per stage
+    static constexpr int THREADS = 64 * WM * WN;
+    static constexpr int TM = BM / WM, TN = BN / WN;      // wave tile
+    static constexpr int FM = TM / 16, FN = TN / 16;      // 16x16 fragments per wave
+    static constexpr int A_CH = BM * (BK / 16) / THREADS; // 16-byte chunks per thread
+    static constexpr int B_CH = BN * (BK / 16) / THREADS;
+    static constexpr int LDS_A = BM * BK, LDS_B = BN * BK;
+    static constexpr int LDS = 2 * (LDS_A + LDS_B);
+    static_assert(A_CH * THREADS == BM * (BK / 16) && B_CH * THREADS == BN * (BK / 16), "tile/threads");
+};
+
+// Block -> output tile.  Blocks are dispatched round-robin over the 8 XCDs
+// (block b runs on XCD b % 8); the remap gives every XCD a contiguous range of
+// tiles, walked GROUP tile-rows at a time so neighbouring blocks of one XCD
+// share A rows and B columns in its L2.
+__device__ __forceinline__ void tile_of_block(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+    const int ntiles = tiles_m * tiles_n;
+    const int per = ntiles >> 3, rem = ntiles & 7;
+    const int xcd = bid & 7, slot = bid >> 3;
+    const int t = xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+    constexpr int GROUP = 8;
+    const int gsz = GROUP * tiles_n;
+    const int g = t / gsz;
+    const int first = g * GROUP;
+    const int gm = tiles_m - first < GROUP ? tiles_m - first : GROUP;
+    const int r = t - g * gsz;
+    tm = first + r % gm;
+    tn = r / gm;
+}
+
+__device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
+
+// Global -> registers for one stage: rows [r0, r0 + ROWS) of a K-contiguous
+// byte matrix with row stride ld bytes, columns [kb, kb + 128) bytes.
+template <int NCH, int THREADS>
+__device__ __forceinline__ void g2r(const uint8_t* __restrict__ base, int64_t ld, int64_t r0, int64_t rows,
+                                    int64_t kb, int64_t kbytes, u32x4* reg) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        const int q = threadIdx.x + i * THREADS;
+        const int r = q >> 3, c = q & 7;
+        const int64_t gr = r0 + r, gk = kb + c * 16;
+        if (gr < rows && gk < kbytes)
+            reg[i] = *reinterpret_cast<const u32x4*>(base + gr * ld + gk);
+        else
+            reg[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+template <int NCH, int THREADS>
+__device__ __forceinline__ void r2s(uint8_t* lds, const u32x4* reg) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        const int q = threadIdx.x + i * THREADS;
+        *reinterpret_cast<u32x4*>(lds + swz(q >> 3, q & 7)) = reg[i];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// int8 main loop: acc[FM][FN] = A[m0.., :] * B[n0.., :]^T
+// ---------------------------------------------------------------------------
+template <class C>
+__device__ __forceinline__ void mainloop_i8(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
+                                            int64_t M, int64_t N, int64_t K, int64_t m0, int64_t n0,
+                                            uint8_t* smem, v4i (&acc)[C::FM][C::FN]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    const uint8_t* Ab = reinterpret_cast<const uint8_t*>(A);
+    const uint8_t* Bb = reinterpret_cast<const uint8_t*>(B);
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+
+    const int nk = (int)((K + C::BK - 1) / C::BK);
+    u32x4 ra[C::A_CH], rb[C::B_CH];
+    g2r<C::A_CH, C::THREADS>(Ab, K, m0, M, 0, K, ra);
+    g2r<C::B_CH, C::THREADS>(Bb, K, n0, N, 0, K, rb);
+    r2s<C::A_CH, C::THREADS>(smem, ra);
+    r2s<C::B_CH, C::THREADS>(smem + C::LDS_A, rb);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        uint8_t* sa = smem + (kt & 1) * (C::LDS_A + C::LDS_B);
+        uint8_t* sb = sa + C::LDS_A;
+        const bool more = kt + 1 < nk;
+        if (more) {
+            g2r<C::A_CH, C::THREADS>(Ab, K, m0, M, (int64_t)(kt + 1) * C::BK, K, ra);
+            g2r<C::B_CH, C::THREADS>(Bb, K, n0, N, (int64_t)(kt + 1) * C::BK, K, rb);
+        }
+#pragma unroll
+        for (int s = 0; s < C::BK / 64; ++s) {
+            const int c = s * 4 + (lane >> 4);
+            v4i fa[C::FM], fb[C::FN];
+#pragma unroll
+            for (int i = 0; i < C::FM; ++i) {
+                const int r = wm * C::TM + i * 16 + (lane & 15);
+                fa[i] = *reinterpret_cast<const v4i*>(sa + swz(r, c));
+            }
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j) {
+                const int r = wn * C::TN + j * 16 + (lane & 15);
+                fb[j] = *reinterpret_cast<const v4i*>(sb + swz(r, c));
+            }
+#pragma unroll
+            for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        }
+        if (more) {
+            uint8_t* na = smem + ((kt + 1) & 1) * (C::LDS_A + C::LDS_B);
+            r2s<C::A_CH, C::THREADS>(na, ra);
+            r2s<C::B_CH, C::THREADS>(na + C::LDS_A, rb);
+        }
+        __syncthreads();
+    }
+}
+
+template <class C>
+__global__ __launch_bounds__(C::THREADS) void k_gemm_i8_i32(const int8_t* __restrict__ A,
+                                                            const int8_t* __restrict__ B, int64_t M,
+                                                            int64_t K, int64_t N, int32_t* __restrict__ Cout,
+                                                            int tiles_m, int tiles_n) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
+    int tm, tn;
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
+    v4i acc[C::FM][C::FN];
+    mainloop_i8<C>(A, B, M, N, K, m0, n0, smem, acc);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / C::WN, wn = wave % C::WN;
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+            const int64_t col = n0 + wn * C::TN + j * 16 + (lane & 15);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t row = m0 + wm * C::TM + i * 16 + 4 * (lane >> 4) + e;
+                if (row < M && col < N) Cout[row * N + col] = acc[i][j][e];
+            }
+        }
+}
+
+__device__ __forceinline__ void store_out(void* out, int dtype, int64_t off, float v) {
+    if (dtype == 0)
+        static_cast<float*>(out)[off] = v;
+    else if (dtype == 1)
+        static_cast<uint16_t*>(out)[off] = f2h(v);
+    else
+        static_cast<uint16_t*>(out)[off] = f2bf(v);
+}
+
+template <class C>
+__global__ __launch_bounds__(C::THREADS) void k_gemm_i8_mixed(const int8_t* __restrict__ Xq,
+                                                              const int8_t* __restrict__ Wq, int64_t M,
+                                                              int64_t K, int64_t N, MixedEpilogue ep,
+                                                              int tiles_m, int tiles_n) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
+    int tm, tn;
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
+    v4i acc[C::FM][C::FN];
+    mainloop_i8<C>(Xq, Wq, M, N, K, m0, n0, smem, acc);
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    const int64_t rb = m0 + wm * C::TM, cb = n0 + wn * C::TN;
+
+    // dequantize: C * s_x[m] * s_w[n]
+    v4f cf[C::FM][C::FN];
+    float sw[C::FN];
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+        const int64_t col = cb + j * 16 + (lane & 15);
+        sw[j] = col < N ? ep.s_w[col] : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+        float sx[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t row = rb + i * 16 + 4 * (lane >> 4) + e;
+            sx[e] = row < M ? ep.s_x[row] : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cf[i][j][e] = (float)acc[i][j][e] * sx[e] * sw[j];
+    }
+
+    // fp16 outlier product over the gathered columns, 32 at a time.  The
+    // block gathers X[m0.., h] and w~[n0.., h] into LDS (free after the main
+    // loop) as [row][32] fp16, then each wave feeds them to the f16 MFMA with
+    // the dequantized tile as accumulator input.
+    const int cnt = *ep.count;
+    _Float16* xo = reinterpret_cast<_Float16*>(smem);           // [BM][32]
+    _Float16* wo = xo + C::BM * 32;                              // [BN][32]
+    for (int h0 = 0; h0 < cnt; h0 += 32) {
+        for (int t = threadIdx.x; t < (C::BM + C::BN) * 32; t += C::THREADS) {
+            const int r = t >> 5, e = t & 31, h = h0 + e;
+            uint16_t v = 0;
+            if (h < cnt) {
+                const int64_t kc = ep.idx[h];
+                if (r < C::BM) {
+                    const int64_t row = m0 + r;
+                    if (row < M) v = ep.X[row * K + kc];
+                } else {
+                    const int64_t col = n0 + (r - C::BM);
+                    if (col < N)
+                        v = ep.W16 ? ep.W16[col * K + kc] : f2h(ep.s_w[col] * (float)ep.Wq[col * K + kc]);
+                }
+            }
+            xo[t] = __builtin_bit_cast(_Float16, v);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) {
+            const int r = wm * C::TM + i * 16 + (lane & 15);
+            const v8h ao = *reinterpret_cast<const v8h*>(xo + r * 32 + (lane >> 4) * 8);
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j) {
+                const int c = wn * C::TN + j * 16 + (lane & 15);
+                const v8h bo = *reinterpret_cast<const v8h*>(wo + c * 32 + (lane >> 4) * 8);
+                cf[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, bo, cf[i][j], 0, 0, 0);
+            }
+        }
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+            const int64_t col = cb + j * 16 + (lane & 15);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t row = rb + i * 16 + 4 * (lane >> 4) + e;
+                if (row < M && col < N) store_out(ep.out, ep.out_dtype, row * N + col, cf[i][j][e]);
+            }
+        }
+}
+
+using CfgBig = Cfg<256, 256, 2, 4>;    // 8 waves, wave tile 128 x 64
+using CfgMid = Cfg<128, 128, 2, 2>;    // 4 waves, wave tile 64 x 64
+using CfgSmall = Cfg<64, 64, 2, 2>;    // 4 waves, wave tile 32 x 32
+
+template <class C>
+static dim3 grid_of(int64_t M, int64_t N, int& tm, int& tn) {
+    tm = (int)((M + C::BM - 1) / C::BM);
+    tn = (int)((N + C::BN - 1) / C::BN);
+    return dim3((unsigned)(tm * tn));
+}
+
+// Pick the largest tile that still gives every CU a block.
+static int pick_cfg(int64_t M, int64_t N) {
+    const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
+    const int64_t mid = ((M + 127) / 128) * ((N + 127) / 128);
+    if (big >= 512) return 2;
+    if (mid >= 256) return 1;
+    return 0;
+}
+
+hipError_t launch_gemm_i8_i32(const int8_t* A, const int8_t* B, int64_t M, int64_t K, int64_t N, int32_t* C,
+                              hipStream_t st) {
+    int tm, tn;
+    switch (pick_cfg(M, N)) {
+        case 2: {
+            dim3 g = grid_of<CfgBig>(M, N, tm, tn);
+            hipLaunchKernelGGL(k_gemm_i8_i32<CfgBig>, g, dim3(CfgBig::THREADS), 0, st, A, B, M, K, N, C, tm, tn);
+            break;
+        }
+        case 1: {
+            dim3 g = grid_of<CfgMid>(M, N, tm, tn);
+            hipLaunchKernelGGL(k_gemm_i8_i32<CfgMid>, g, dim3(CfgMid::THREADS), 0, st, A, B, M, K, N, C, tm, tn);
+            break;
+        }
+        default: {
+            dim3 g = grid_of<CfgSmall>(M, N, tm, tn);
+            hipLaunchKernelGGL(k_gemm_i8_i32<CfgSmall>, g, dim3(CfgSmall::THREADS), 0, st, A, B, M, K, N, C, tm,
+                               tn);
+        }
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_i8_mixed(const int8_t* Xq, const int8_t* Wq, int64_t M, int64_t K, int64_t N,
+                                const MixedEpilogue& ep, hipStream_t st) {
+    int tm, tn;
+    switch (pick_cfg(M, N)) {
+        case 2: {
+            dim3 g = grid_of<CfgBig>(M, N, tm, tn);
+            hipLaunchKernelGGL(k_gemm_i8_mixed<CfgBig>, g, dim3(CfgBig::THREADS), 0, st, Xq, Wq, M, K, N, ep, tm,
+                               tn);
+            break;
+        }
+        case 1: {
+            dim3 g = grid_of<CfgMid>(M, N, tm, tn);
+            hipLaunchKernelGGL(k_gemm_i8_mixed<CfgMid>, g, dim3(CfgMid::THREADS), 0, st, Xq, Wq, M, K, N, ep, tm,
+                               tn);
+            break;
+        }
+        default: {
+            dim3 g = grid_of<CfgSmall>(M, N, tm, tn);
+            hipLaunchKernelGGL(k_gemm_i8_mixed<CfgSmall>, g, dim3(CfgSmall::THREADS), 0, st, Xq, Wq, M, K, N, ep,
+                               tm, tn);
+        }
+    }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// W4A4: operands are packed int4 rows of K/2 bytes.  A stage holds 256 K
+// elements (128 bytes) per row; one MFMA step covers 64 elements, i.e. 8
+// packed bytes per lane (lane l: row l % 16, bytes 8 (l / 16) of the step).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ v4i unpack_hi_nibbles(u32x2 w) {
+    // element 2j of word w0 -> byte j of d0 (x16), element 2j+1 -> byte j of d1
+    v4i d;
+    d[0] = (int)((w[0] << 4) & 0xF0F0F0F0u);
+    d[1] = (int)(w[0] & 0xF0F0F0F0u);
+    d[2] = (int)((w[1] << 4) & 0xF0F0F0F0u);
+    d[3] = (int)(w[1] & 0xF0F0F0F0u);
+    return d;
+}
+
+template <class C, int G, bool STORE_ACC>
+__global__ __launch_bounds__(C::THREADS) void k_gemm_w4a4(const uint32_t* __restrict__ Xp,
+                                                          const float* __restrict__ s_x,
+                                                          const uint32_t* __restrict__ Wp,
+                                                          const float* __restrict__ s_w, int64_t M, int64_t K,
+                                                          int64_t N, void* __restrict__ out, int out_dtype,
+                                                          int tiles_m, int tiles_n) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
+    constexpr int KS = 256;                      // K elements per stage
+    constexpr int STEPS = KS / 64;               // MFMA steps per stage
+    constexpr int SPG = G / 64;                  // MFMA steps per group
+    int tm, tn;
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    const int64_t kbytes = K / 2, ng = K / G;
+    const uint8_t* Ab = reinterpret_cast<const uint8_t*>(Xp);
+    const uint8_t* Bb = reinterpret_cast<const uint8_t*>(Wp);
+
+    v4f f[C::FM][C::FN];
+    v4i acc[C::FM][C::FN];
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+            f[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+            acc[i][j] = v4i{0, 0, 0, 0};
+        }
+    float swj[C::FN];
+    int64_t colj[C::FN];
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) colj[j] = n0 + wn * C::TN + j * 16 + (lane & 15);
+
+    const int nk = (int)((kbytes + C::BK - 1) / C::BK);
+    u32x4 ra[C::A_CH], rb[C::B_CH];
+    g2r<C::A_CH, C::THREADS>(Ab, kbytes, m0, M, 0, kbytes, ra);
+    g2r<C::B_CH, C::THREADS>(Bb, kbytes, n0, N, 0, kbytes, rb);
+    r2s<C::A_CH, C::THREADS>(smem, ra);
+    r2s<C::B_CH, C::THREADS>(smem + C::LDS_A, rb);
+    __syncthreads();
+    int step = 0;                                 // global MFMA step index (64 K each)
+    const int nsteps = (int)(K / 64);
+    for (int kt = 0; kt < nk; ++kt) {
+        uint8_t* sa = smem + (kt & 1) * (C::LDS_A + C::LDS_B);
+        uint8_t* sb = sa + C::LDS_A;
+        const bool more = kt + 1 < nk;
+        if (more) {
+            g2r<C::A_CH, C::THREADS>(Ab, kbytes, m0, M, (int64_t)(kt + 1) * C::BK, kbytes, ra);
+            g2r<C::B_CH, C::THREADS>(Bb, kbytes, n0, N, (int64_t)(kt + 1) * C::BK, kbytes, rb);
+        }
+#pragma unroll
+        for (int s = 0; s < STEPS; ++s, ++step) {
+            if (step < nsteps) {
+                const int byte = s * 32 + (lane >> 4) * 8;          // within the 128-byte row
+                const int c = byte >> 4, within = byte & 15;
+                v4i fa[C::FM], fb[C::FN];
+#pragma unroll
+                for (int i = 0; i < C::FM; ++i) {
+                    const int r = wm * C::TM + i * 16 + (lane & 15);
+                    fa[i] = unpack_hi_nibbles(*reinterpret_cast<const u32x2*>(sa + swz(r, c) + within));
+                }
+#pragma unroll
+                for (int j = 0; j < C::FN; ++j) {
+                    const int r = wn * C::TN + j * 16 + (lane & 15);
+                    fb[j] = unpack_hi_nibbles(*reinterpret_cast<const u32x2*>(sb + swz(r, c) + within));
+                }
+#pragma unroll
+                for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < C::FN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                if ((step + 1) % SPG == 0) {
+                    const int64_t g = step / SPG;
+                    if constexpr (STORE_ACC) {
+                        int32_t* accp = static_cast<int32_t*>(out);
+#pragma unroll
+                        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+                            for (int j = 0; j < C::FN; ++j) {
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) {
+                                    const int64_t row = m0 + wm * C::TM + i * 16 + 4 * (lane >> 4) + e;
+                                    if (row < M && colj[j] < N)
+                                        accp[(row * N + colj[j]) * ng + g] = acc[i][j][e] >> 8;
+                                }
+                                acc[i][j] = v4i{0, 0, 0, 0};
+                            }
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < C::FN; ++j)
+                            swj[j] = colj[j] < N ? s_w[colj[j] * ng + g] * 0x1p-8f : 0.0f;
+#pragma unroll
+                        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+                            for (int j = 0; j < C::FN; ++j) {
+#pragma unroll
+                                for (int e = 0; e < 4; ++e)
+                                    f[i][j][e] = __builtin_fmaf((float)acc[i][j][e], swj[j], f[i][j][e]);
+                                acc[i][j] = v4i{0, 0, 0, 0};
+                            }
+                    }
+                }
+            }
+        }
+        if (more) {
+            uint8_t* na = smem + ((kt + 1) & 1) * (C::LDS_A + C::LDS_B);
+            r2s<C::A_CH, C::THREADS>(na, ra);
+            r2s<C::B_CH, C::THREADS>(na + C::LDS_A, rb);
+        }
+        __syncthreads();
+    }
+    if constexpr (!STORE_ACC) {
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t row = m0 + wm * C::TM + i * 16 + 4 * (lane >> 4) + e;
+                if (row >= M) continue;
+                const float sx = s_x[row];
+#pragma unroll
+                for (int j = 0; j < C::FN; ++j)
+                    if (colj[j] < N) store_out(out, out_dtype, row * N + colj[j], sx * f[i][j][e]);
+            }
+    }
+}
+
+template <int G, bool STORE_ACC>
+static void w4a4_dispatch(const uint32_t* Xp, const float* s_x, const uint32_t* Wp, const float* s_w, int64_t M,
+                          int64_t K, int64_t N, void* out, int out_dtype, hipStream_t st) {
+    int tm, tn;
+    if (((M + 127) / 128) * ((N + 127) / 128) >= 256) {
+        dim3 g = grid_of<CfgMid>(M, N, tm, tn);
+        hipLaunchKernelGGL((k_gemm_w4a4<CfgMid, G, STORE_ACC>), g, dim3(CfgMid::THREADS), 0, st, Xp, s_x, Wp, s_w,
+                           M, K, N, out, out_dtype, tm, tn);
+    } else {
+        dim3 g = grid_of<CfgSmall>(M, N, tm, tn);
+        hipLaunchKernelGGL((k_gemm_w4a4<CfgSmall, G, STORE_ACC>), g, dim3(CfgSmall::THREADS), 0, st, Xp, s_x, Wp,
+                           s_w, M, K, N, out, out_dtype, tm, tn);
+    }
+}
+
+hipError_t launch_gemm_w4a4(const uint32_t* Xp, const float* s_x, const uint32_t* Wp, const float* s_w,
+                            int64_t M, int64_t K, int64_t N, int G, void* out, int out_dtype, hipStream_t st) {
+    switch (G) {
+        case 64: w4a4_dispatch<64, false>(Xp, s_x, Wp, s_w, M, K, N, out, out_dtype, st); break;
+        case 128: w4a4_dispatch<128, false>(Xp, s_x, Wp, s_w, M, K, N, out, out_dtype, st); break;
+        case 256: w4a4_dispatch<256, false>(Xp, s_x, Wp, s_w, M, K, N, out, out_dtype, st); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_w4a4_group_acc(const uint32_t* Xp, const uint32_t* Wp, int64_t M, int64_t K, int64_t N,
+                                      int G, int32_t* acc, hipStream_t st) {
+    switch (G) {
+        case 64: w4a4_dispatch<64, true>(Xp, nullptr, Wp, nullptr, M, K, N, acc, 0, st); break;
+        case 128: w4a4_dispatch<128, true>(Xp, nullptr, Wp, nullptr, M, K, N, acc, 0, st); break;
+        case 256: w4a4_dispatch<256, true>(Xp, nullptr, Wp, nullptr, M, K, N, acc, 0, st); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace qa

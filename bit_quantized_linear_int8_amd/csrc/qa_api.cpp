@@ -1,0 +1,274 @@
+// qa_api.cpp -- the C ABI of libqa (declared in include/qa.h).
+//
+// Every entry point validates all of its arguments before it touches the HIP
+// runtime; on error it launches nothing and records a message readable with
+// qa_last_error().  Then it carves the caller's workspace and enqueues the
+// kernels on the caller's stream.  Nothing here allocates or synchronizes.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "qa.h"
+#include "qa_launch.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+qa_status fail(qa_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+qa_status ok() {
+    g_last_error[0] = '\0';
+    return QA_OK;
+}
+
+qa_status device_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(QA_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr size_t kAlign = 256;
+size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Largest K for which |sum_k q_x q_w| < 2^31 with codes in [-127, 127].
+constexpr int64_t kMaxK_i8 = 131072;
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+struct MixedLayout {
+    size_t cmax, mask, idx, count, s_x, xq, total;
+};
+
+MixedLayout mixed_layout(int64_t M, int64_t K) {
+    MixedLayout L;
+    size_t off = 0;
+    L.cmax = off; off += up(qa::outlier_scratch_bytes(K));
+    L.mask = off; off += up((size_t)K);
+    L.idx = off; off += up((size_t)K * 4);
+    L.count = off; off += up(4);
+    L.s_x = off; off += up((size_t)M * 4);
+    L.xq = off; off += up((size_t)M * (size_t)K);
+    L.total = off;
+    return L;
+}
+
+struct W4Layout {
+    size_t xp, s_x, total;
+};
+
+W4Layout w4_layout(int64_t M, int64_t K) {
+    W4Layout L;
+    size_t off = 0;
+    L.xp = off; off += up((size_t)M * (size_t)(K / 2));
+    L.s_x = off; off += up((size_t)M * 4);
+    L.total = off;
+    return L;
+}
+
+bool valid_dtype(qa_dtype d) { return d == QA_F32 || d == QA_F16 || d == QA_BF16; }
+
+}  // namespace
+
+extern "C" {
+
+const char* qa_status_string(qa_status s) {
+    switch (s) {
+        case QA_OK: return "QA_OK";
+        case QA_ERR_NULL: return "QA_ERR_NULL";
+        case QA_ERR_SHAPE: return "QA_ERR_SHAPE";
+        case QA_ERR_ALIGN: return "QA_ERR_ALIGN";
+        case QA_ERR_VALUE: return "QA_ERR_VALUE";
+        case QA_ERR_WORKSPACE: return "QA_ERR_WORKSPACE";
+        case QA_ERR_UNSUPPORTED: return "QA_ERR_UNSUPPORTED";
+        case QA_ERR_DEVICE: return "QA_ERR_DEVICE";
+    }
+    return "QA_ERR_UNKNOWN";
+}
+
+const char* qa_last_error(void) { return g_last_error; }
+
+// ----------------------------------------------------------------- outliers
+size_t qa_outlier_cols_workspace(int64_t K) { return K > 0 ? up(qa::outlier_scratch_bytes(K)) : 0; }
+
+qa_status qa_outlier_cols(const void* X_f16, int64_t M, int64_t K, float threshold, uint8_t* mask, int32_t* idx,
+                          int32_t* count, float* colmax_or_null, void* scratch, size_t scratch_bytes,
+                          void* stream) {
+    if (M < 0 || K <= 0 || K % 8 != 0)
+        return fail(QA_ERR_SHAPE, "qa_outlier_cols: need M >= 0, K > 0, K %% 8 == 0 (M=%lld K=%lld)",
+                    (long long)M, (long long)K);
+    if ((M > 0 && !X_f16) || !mask || !idx || !count || !scratch)
+        return fail(QA_ERR_NULL, "qa_outlier_cols: NULL pointer");
+    if (!aligned(X_f16, 16) || !aligned(idx, 4) || !aligned(count, 4) || !aligned(scratch, 4) ||
+        (colmax_or_null && !aligned(colmax_or_null, 4)))
+        return fail(QA_ERR_ALIGN, "qa_outlier_cols: X must be 16-byte aligned, idx/count/colmax/scratch 4-byte");
+    if (std::isnan(threshold)) return fail(QA_ERR_VALUE, "qa_outlier_cols: threshold is NaN");
+    if (scratch_bytes < qa_outlier_cols_workspace(K))
+        return fail(QA_ERR_WORKSPACE, "qa_outlier_cols: scratch %zu < %zu bytes", scratch_bytes,
+                    qa_outlier_cols_workspace(K));
+    return device_status(qa::launch_outlier_cols(static_cast<const uint16_t*>(X_f16), M, K, threshold, mask, idx,
+                                                 count, colmax_or_null, scratch, as_stream(stream)),
+                         "qa_outlier_cols");
+}
+
+// ----------------------------------------------------------------- row quant
+qa_status qa_quantize_rowwise_int8(const void* X_f16, int64_t rows, int64_t K, const uint8_t* mask_or_null,
+                                   int32_t q_min, int32_t q_max, const float* s_in_or_null,
+                                   const int32_t* z_in_or_null, int8_t* Xq, float* s_out_or_null, void* stream) {
+    const bool dynamic = s_in_or_null == nullptr;
+    if (rows < 0 || K <= 0 || K % 8 != 0)
+        return fail(QA_ERR_SHAPE, "qa_quantize_rowwise_int8: need rows >= 0, K > 0, K %% 8 == 0");
+    if (q_min > q_max || q_min < -128 || q_max > 127)
+        return fail(QA_ERR_VALUE, "qa_quantize_rowwise_int8: need -128 <= q_min <= q_max <= 127");
+    if (dynamic && (q_max <= 0 || z_in_or_null))
+        return fail(QA_ERR_VALUE, "qa_quantize_rowwise_int8: dynamic mode needs q_max > 0 and no zero-point");
+    if (rows == 0) return ok();
+    if (!X_f16 || !Xq || (dynamic && !s_out_or_null))
+        return fail(QA_ERR_NULL, "qa_quantize_rowwise_int8: NULL X, Xq, or s_out in dynamic mode");
+    if (!aligned(X_f16, 16) || !aligned(Xq, 16) || (mask_or_null && !aligned(mask_or_null, 8)) ||
+        (s_out_or_null && !aligned(s_out_or_null, 4)) || (s_in_or_null && !aligned(s_in_or_null, 4)) ||
+        (z_in_or_null && !aligned(z_in_or_null, 4)))
+        return fail(QA_ERR_ALIGN, "qa_quantize_rowwise_int8: X, Xq 16-byte, mask 8-byte, scales 4-byte aligned");
+    return device_status(qa::launch_rowquant_i8(static_cast<const uint16_t*>(X_f16), rows, K, mask_or_null, q_min,
+                                                q_max, s_in_or_null, z_in_or_null, Xq, s_out_or_null,
+                                                as_stream(stream)),
+                         "qa_quantize_rowwise_int8");
+}
+
+// ----------------------------------------------------------------- int8 mixed linear
+size_t qa_qlinear_int8_mixed_workspace(int64_t M, int64_t K) {
+    if (M < 0 || K <= 0) return 0;
+    return mixed_layout(M, K).total;
+}
+
+qa_status qa_qlinear_int8_mixed(const void* X_f16, int64_t M, int64_t K, const int8_t* Wq, const float* s_w,
+                                const void* W_f16_or_null, int64_t N, float threshold, void* out,
+                                qa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    if (M < 0 || N < 0 || K <= 0 || K % 16 != 0 || K > kMaxK_i8)
+        return fail(QA_ERR_SHAPE, "qa_qlinear_int8_mixed: need M, N >= 0, 0 < K <= %lld, K %% 16 == 0",
+                    (long long)kMaxK_i8);
+    if (std::isnan(threshold)) return fail(QA_ERR_VALUE, "qa_qlinear_int8_mixed: threshold is NaN");
+    if (!valid_dtype(out_dtype)) return fail(QA_ERR_VALUE, "qa_qlinear_int8_mixed: bad out_dtype %d", (int)out_dtype);
+    if (M == 0 || N == 0) return ok();
+    if (!X_f16 || !Wq || !s_w || !out || !workspace) return fail(QA_ERR_NULL, "qa_qlinear_int8_mixed: NULL pointer");
+    if (!aligned(X_f16, 16) || !aligned(Wq, 16) || !aligned(s_w, 4) || !aligned(workspace, kAlign) ||
+        (W_f16_or_null && !aligned(W_f16_or_null, 2)) || !aligned(out, 4))
+        return fail(QA_ERR_ALIGN, "qa_qlinear_int8_mixed: X, Wq 16-byte, workspace 256-byte, out/s_w 4-byte aligned");
+    const MixedLayout L = mixed_layout(M, K);
+    if (workspace_bytes < L.total)
+        return fail(QA_ERR_WORKSPACE, "qa_qlinear_int8_mixed: workspace %zu < %zu bytes", workspace_bytes, L.total);
+
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    uint8_t* mask = ws + L.mask;
+    int32_t* idx = reinterpret_cast<int32_t*>(ws + L.idx);
+    int32_t* count = reinterpret_cast<int32_t*>(ws + L.count);
+    float* s_x = reinterpret_cast<float*>(ws + L.s_x);
+    int8_t* xq = reinterpret_cast<int8_t*>(ws + L.xq);
+    const uint16_t* X = static_cast<const uint16_t*>(X_f16);
+    hipStream_t st = as_stream(stream);
+
+    hipError_t e = qa::launch_outlier_cols(X, M, K, threshold, mask, idx, count, nullptr, ws + L.cmax, st);
+    if (e != hipSuccess) return device_status(e, "qa_qlinear_int8_mixed (outlier columns)");
+    e = qa::launch_rowquant_i8(X, M, K, mask, -127, 127, nullptr, nullptr, xq, s_x, st);
+    if (e != hipSuccess) return device_status(e, "qa_qlinear_int8_mixed (row quantization)");
+    qa::MixedEpilogue ep;
+    ep.s_x = s_x;
+    ep.s_w = s_w;
+    ep.X = X;
+    ep.W16 = static_cast<const uint16_t*>(W_f16_or_null);
+    ep.Wq = Wq;
+    ep.idx = idx;
+    ep.count = count;
+    ep.out = out;
+    ep.out_dtype = (int)out_dtype;
+    return device_status(qa::launch_gemm_i8_mixed(xq, Wq, M, K, N, ep, st), "qa_qlinear_int8_mixed (gemm)");
+}
+
+// ----------------------------------------------------------------- Hadamard + int4
+qa_status qa_hadamard_quant_int4(const void* X_f16, int64_t rows, int64_t K, int32_t G, qa_scale_mode mode,
+                                 int32_t q_min, int32_t q_max, uint32_t* packed, float* s, void* stream) {
+    if (mode != QA_SCALE_PER_ROW && mode != QA_SCALE_PER_GROUP)
+        return fail(QA_ERR_VALUE, "qa_hadamard_quant_int4: bad scale mode %d", (int)mode);
+    if (G < 1 || G > 256 || (G & (G - 1)) != 0)
+        return fail(QA_ERR_SHAPE, "qa_hadamard_quant_int4: G must be a power of two in [1, 256] (G=%d)", G);
+    if (rows < 0 || K <= 0 || K % 8 != 0 || K % G != 0 || (mode == QA_SCALE_PER_GROUP && G < 8))
+        return fail(QA_ERR_SHAPE,
+                    "qa_hadamard_quant_int4: need rows >= 0, K > 0, K %% 8 == 0, K %% G == 0, G >= 8 per group");
+    if (q_min > q_max || q_min < -8 || q_max > 7 || q_max <= 0)
+        return fail(QA_ERR_VALUE, "qa_hadamard_quant_int4: need -8 <= q_min <= q_max <= 7, q_max > 0");
+    if (rows == 0) return ok();
+    if (!X_f16 || !packed || !s) return fail(QA_ERR_NULL, "qa_hadamard_quant_int4: NULL pointer");
+    if (!aligned(X_f16, 16) || !aligned(packed, 4) || !aligned(s, 4))
+        return fail(QA_ERR_ALIGN, "qa_hadamard_quant_int4: X 16-byte, packed/s 4-byte aligned");
+    return device_status(qa::launch_hadamard_quant_i4(static_cast<const uint16_t*>(X_f16), rows, K, G,
+                                                      mode == QA_SCALE_PER_GROUP, q_min, q_max, packed, s,
+                                                      as_stream(stream)),
+                         "qa_hadamard_quant_int4");
+}
+
+// ----------------------------------------------------------------- W4A4 linear
+size_t qa_qlinear_w4a4_workspace(int64_t M, int64_t K) {
+    if (M < 0 || K <= 0) return 0;
+    return w4_layout(M, K).total;
+}
+
+static bool w4_group_ok(int32_t G) { return G == 64 || G == 128 || G == 256; }
+
+qa_status qa_qlinear_w4a4(const void* X_f16, int64_t M, int64_t K, const uint32_t* Wp, const float* s_w, int64_t N,
+                          int32_t G, void* out, qa_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+    if (!w4_group_ok(G) || M < 0 || N < 0 || K <= 0 || K % G != 0)
+        return fail(QA_ERR_SHAPE, "qa_qlinear_w4a4: need G in {64,128,256}, M, N >= 0, K > 0, K %% G == 0");
+    if (!valid_dtype(out_dtype)) return fail(QA_ERR_VALUE, "qa_qlinear_w4a4: bad out_dtype %d", (int)out_dtype);
+    if (M == 0 || N == 0) return ok();
+    if (!X_f16 || !Wp || !s_w || !out || !workspace) return fail(QA_ERR_NULL, "qa_qlinear_w4a4: NULL pointer");
+    if (!aligned(X_f16, 16) || !aligned(Wp, 16) || !aligned(s_w, 4) || !aligned(out, 4) ||
+        !aligned(workspace, kAlign))
+        return fail(QA_ERR_ALIGN, "qa_qlinear_w4a4: X, Wp 16-byte, workspace 256-byte, out/s_w 4-byte aligned");
+    const W4Layout L = w4_layout(M, K);
+    if (workspace_bytes < L.total)
+        return fail(QA_ERR_WORKSPACE, "qa_qlinear_w4a4: workspace %zu < %zu bytes", workspace_bytes, L.total);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    uint32_t* xp = reinterpret_cast<uint32_t*>(ws + L.xp);
+    float* s_x = reinterpret_cast<float*>(ws + L.s_x);
+    hipStream_t st = as_stream(stream);
+    hipError_t e = qa::launch_hadamard_quant_i4(static_cast<const uint16_t*>(X_f16), M, K, G, false, -7, 7, xp, s_x, st);
+    if (e != hipSuccess) return device_status(e, "qa_qlinear_w4a4 (hadamard quant)");
+    return device_status(qa::launch_gemm_w4a4(xp, s_x, Wp, s_w, M, K, N, G, out, (int)out_dtype, st),
+                         "qa_qlinear_w4a4 (gemm)");
+}
+
+// ----------------------------------------------------------------- parity entry points
+qa_status qa_gemm_i8_i32(const int8_t* A, const int8_t* B, int64_t M, int64_t K, int64_t N, int32_t* C,
+                         void* stream) {
+    if (M < 0 || N < 0 || K <= 0 || K % 16 != 0)
+        return fail(QA_ERR_SHAPE, "qa_gemm_i8_i32: need M, N >= 0, K > 0, K %% 16 == 0");
+    if (M == 0 || N == 0) return ok();
+    if (!A || !B || !C) return fail(QA_ERR_NULL, "qa_gemm_i8_i32: NULL pointer");
+    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 4))
+        return fail(QA_ERR_ALIGN, "qa_gemm_i8_i32: A, B 16-byte, C 4-byte aligned");
+    return device_status(qa::launch_gemm_i8_i32(A, B, M, K, N, C, as_stream(stream)), "qa_gemm_i8_i32");
+}
+
+qa_status qa_gemm_w4a4_group_acc(const uint32_t* Xp, const uint32_t* Wp, int64_t M, int64_t K, int64_t N, int32_t G,
+                                 int32_t* acc, void* stream) {
+    if (!w4_group_ok(G) || M < 0 || N < 0 || K <= 0 || K % G != 0)
+        return fail(QA_ERR_SHAPE, "qa_gemm_w4a4_group_acc: need G in {64,128,256}, M, N >= 0, K > 0, K %% G == 0");
+    if (M == 0 || N == 0) return ok();
+    if (!Xp || !Wp || !acc) return fail(QA_ERR_NULL, "qa_gemm_w4a4_group_acc: NULL pointer");
+    if (!aligned(Xp, 16) || !aligned(Wp, 16) || !aligned(acc, 4))
+        return fail(QA_ERR_ALIGN, "qa_gemm_w4a4_group_acc: Xp, Wp 16-byte, acc 4-byte aligned");
+    return device_status(qa::launch_gemm_w4a4_group_acc(Xp, Wp, M, K, N, G, acc, as_stream(stream)),
+                         "qa_gemm_w4a4_group_acc");
+}
+
+}  // extern "C"

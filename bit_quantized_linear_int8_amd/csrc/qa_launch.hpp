@@ -1,0 +1,54 @@
+// qa_launch.hpp -- host-side launchers of the gfx950 kernels (internal).
+// Arguments are validated by the C ABI layer (qa_api.cpp) before any call.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qa {
+
+// Workspace of the outlier-column reduction: a running column max [K] as
+// uint32 bits and a ticket counter, zero-filled by the launcher itself.
+size_t outlier_scratch_bytes(int64_t K);
+
+hipError_t launch_outlier_cols(const uint16_t* X, int64_t M, int64_t K, float tau, uint8_t* mask,
+                               int32_t* idx, int32_t* count, float* colmax, void* scratch,
+                               hipStream_t st);
+
+hipError_t launch_rowquant_i8(const uint16_t* X, int64_t rows, int64_t K, const uint8_t* mask,
+                              int qmin, int qmax, const float* s_in, const int32_t* z_in,
+                              int8_t* q, float* s_out, hipStream_t st);
+
+hipError_t launch_hadamard_quant_i4(const uint16_t* X, int64_t rows, int64_t K, int G,
+                                    bool per_group, int qmin, int qmax, uint32_t* packed, float* s,
+                                    hipStream_t st);
+
+// int8 GEMM C = A * B^T (A [M x K], B [N x K]) with either an int32 store
+// (out_dtype < 0) or the LLM.int8() epilogue.
+struct MixedEpilogue {
+    const float* s_x;          // [M]
+    const float* s_w;          // [N]
+    const uint16_t* X;         // fp16 [M x K] (outlier gather)
+    const uint16_t* W16;       // fp16 [N x K] or nullptr
+    const int8_t* Wq;          // for w~ when W16 is null
+    const int32_t* idx;        // outlier list
+    const int32_t* count;      // device count
+    void* out;
+    int out_dtype;             // 0 f32, 1 f16, 2 bf16
+};
+
+hipError_t launch_gemm_i8_i32(const int8_t* A, const int8_t* B, int64_t M, int64_t K, int64_t N,
+                              int32_t* C, hipStream_t st);
+
+hipError_t launch_gemm_i8_mixed(const int8_t* Xq, const int8_t* Wq, int64_t M, int64_t K, int64_t N,
+                                const MixedEpilogue& ep, hipStream_t st);
+
+hipError_t launch_gemm_w4a4(const uint32_t* Xp, const float* s_x, const uint32_t* Wp,
+                            const float* s_w, int64_t M, int64_t K, int64_t N, int G, void* out,
+                            int out_dtype, hipStream_t st);
+
+hipError_t launch_gemm_w4a4_group_acc(const uint32_t* Xp, const uint32_t* Wp, int64_t M, int64_t K,
+                                      int64_t N, int G, int32_t* acc, hipStream_t st);
+
+}  // namespace qa

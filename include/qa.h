@@ -1,0 +1,214 @@
+/*
+ * qa.h -- C ABI of libqa, quantized linear layers for AMD Instinct MI355X
+ * (gfx950, CDNA4).
+ *
+ * Two quantized linear layers of LLM inference:
+ *   - LLM.int8() mixed precision: feature columns whose activation magnitude
+ *     exceeds a threshold stay in fp16, all other columns are quantized to
+ *     int8 with vector-wise absmax scales (per token for X, per output
+ *     channel for W), multiplied with int32 accumulation, dequantized by the
+ *     outer product of the scales and summed with the fp16 outlier product.
+ *   - W4A4 group Hadamard: each G-wide block of the K dimension is rotated by
+ *     the normalized Hadamard matrix, quantized to int4 (dynamic per-token
+ *     scales for X, per-row-per-group scales for W), packed eight per 32-bit
+ *     word, multiplied with int32 accumulation per group and dequantized.
+ *
+ * Sources, cited by page title and section:
+ *   [AIInfra-Q01]  Infrasys-AI "AIInfra" notes, page 05Quantization01 (模型量化):
+ *                  the LLM.int8() method -- outlier detection, "a. 向量级量化",
+ *                  "b. INT8 矩阵乘法与反量化", merge of the two parts.
+ *   [Scholia-IQ]   "模型推理量化" (Inference Quantization notes): §4 Scale,
+ *                  §5 Outlier, §6 Zero-point (§6.2 affine clip), §7 Granularity.
+ *   [GroupRot]     "低比特量化加速：分组旋转方法从W8A8到W4A4的实践与展望":
+ *                  §二 normalized Hadamard, §5.1 weight transform and storage,
+ *                  §5.2 online activation transform fused with quantization,
+ *                  §5.4 packing and int32 accumulation.
+ *   [QE2]          "Quantization explained, part 2" (tanjunchen.github.io),
+ *                  §1.2: threshold 6.0 on a channel's activation magnitude.
+ *
+ * Conventions shared by every entry point:
+ *   - All array arguments are DEVICE pointers allocated and owned by the
+ *     caller; the library allocates nothing and keeps no per-call state.
+ *   - Matrices are row-major.  X is [M x K] (tokens x in-features), W is
+ *     [N x K] (out-features x in-features), the output is [M x N].
+ *   - fp16 / bf16 arrays are passed as `const void*` holding IEEE binary16 /
+ *     bfloat16 bit patterns.
+ *   - `stream` is a hipStream_t (NULL: the default stream).  Every call is
+ *     asynchronous and stream-ordered; nothing synchronizes the host.
+ *   - Every argument check runs before any HIP call.  On error nothing is
+ *     launched and outputs are untouched.  Device faults surface at the
+ *     caller's next synchronization.
+ *   - Sizes and scalar arguments are checked first.  M == 0 or N == 0 (an
+ *     empty batch or layer; rows == 0 for the quantizers) is then a valid
+ *     no-op, and the pointers of empty arrays may be NULL.
+ *   - Inputs must be finite (NaN / Inf are not checked on the hot path).
+ *   - Rounding: scales are fl32(absmax / q_max) with IEEE correctly rounded
+ *     division (1.0 when absmax is 0, [Scholia-IQ §4]); codes are
+ *     clip(rint(fl32(x / s)) + z, q_min, q_max) with ties to even.
+ */
+#ifndef QA_H
+#define QA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QA_OK = 0,
+    QA_ERR_NULL = 1,        /* a required pointer is NULL */
+    QA_ERR_SHAPE = 2,       /* negative size, K not a multiple of the required step, bad G */
+    QA_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned */
+    QA_ERR_VALUE = 4,       /* q_min > q_max, range outside the code type, NaN threshold, ... */
+    QA_ERR_WORKSPACE = 5,   /* workspace smaller than the matching *_workspace() size */
+    QA_ERR_UNSUPPORTED = 6, /* a valid request this build does not implement */
+    QA_ERR_DEVICE = 7       /* a HIP launch failed; see qa_last_error() */
+} qa_status;
+
+typedef enum { QA_F32 = 0, QA_F16 = 1, QA_BF16 = 2 } qa_dtype;
+
+typedef enum { QA_SCALE_PER_ROW = 0, QA_SCALE_PER_GROUP = 1 } qa_scale_mode;
+
+/* Human-readable name of a status code (static string). */
+const char* qa_status_string(qa_status s);
+
+/* Detail of the last error raised on the calling thread ("" if none). */
+const char* qa_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * Outlier feature columns  [AIInfra-Q01, LLM.int8() detection step; QE2 §1.2]
+ *
+ * colmax[j] = max_i |X[i][j]| (fp16 widened exactly to fp32).  Column j is an
+ * outlier when colmax[j] > threshold (strict; threshold compared in fp32).
+ *   X       fp16 [M x K]
+ *   mask    u8 [K]: 1 for an outlier column, else 0
+ *   idx     i32 [K]: the outlier columns in ascending order in idx[0..count)
+ *           (entries from count on are unspecified)
+ *   count   i32 [1]: number of outlier columns
+ *   colmax  f32 [K] or NULL
+ *   scratch device buffer of qa_outlier_cols_workspace(K) bytes (any content)
+ * Errors: NULL pointers, M < 0, K <= 0, K % 8 != 0, X not 16-byte aligned,
+ * NaN threshold, small scratch.
+ * ------------------------------------------------------------------------- */
+size_t qa_outlier_cols_workspace(int64_t K);
+qa_status qa_outlier_cols(const void* X_f16, int64_t M, int64_t K, float threshold,
+                          uint8_t* mask, int32_t* idx, int32_t* count, float* colmax_or_null,
+                          void* scratch, size_t scratch_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Row-wise int8 quantization  [AIInfra-Q01 "a. 向量级量化"; Scholia-IQ §4,
+ * §6.2]
+ *
+ * One scale per row of X [rows x K] (per token for activations, per output
+ * channel for a weight [N x K]).
+ *   Dynamic (s_in == NULL): s[r] = absmax over the unmasked columns of row r
+ *     divided by q_max (1.0 if that absmax is 0), z = 0, written to s_out[r].
+ *     Requires q_max > 0 and z_in == NULL.
+ *   Static (s_in != NULL): s = s_in[r] (> 0, finite: not checked),
+ *     z = z_in ? z_in[r] : 0; s_out is ignored.
+ *   Xq[r][j] = clip(rint(x / s) + z, q_min, q_max); a masked column j
+ *     (mask[j] != 0) is skipped by the absmax and receives clip(z).
+ *   X       fp16 [rows x K]; mask u8 [K] or NULL; Xq i8 [rows x K]
+ * Errors: NULL X / Xq (or s_out in dynamic mode), rows < 0, K <= 0,
+ * K % 8 != 0, X or Xq not 16-byte aligned, q_min > q_max, range outside
+ * [-128, 127], dynamic mode with q_max <= 0 or z_in != NULL.
+ * ------------------------------------------------------------------------- */
+qa_status qa_quantize_rowwise_int8(const void* X_f16, int64_t rows, int64_t K,
+                                   const uint8_t* mask_or_null, int32_t q_min, int32_t q_max,
+                                   const float* s_in_or_null, const int32_t* z_in_or_null,
+                                   int8_t* Xq, float* s_out_or_null, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * LLM.int8() mixed-precision linear  [AIInfra-Q01: detection, "a. 向量级量化",
+ * "b. INT8 矩阵乘法与反量化", merge; QE2 §1.2]
+ *
+ *   O       = { j : max_i |X[i][j]| > threshold }            (all M rows)
+ *   s_x[m]  = max_{j not in O} |X[m][j]| / 127               (1.0 if 0)
+ *   Xq[m][j]= clip(rint(X[m][j] / s_x[m]), -127, 127), 0 for j in O
+ *   C[m][n] = sum_k Xq[m][k] * Wq[n][k]                      (int32)
+ *   out     = C * s_x[m] * s_w[n] + sum_{h in O} X[m][h] * w~[n][h]
+ * with fp16 outlier operands and fp32 accumulation; w~ = W_f16[n][h] when
+ * W_f16 is given, else fp16(fl32(s_w[n] * Wq[n][h])).
+ *   X       fp16 [M x K]
+ *   Wq, s_w the weight quantized per output channel (qa_quantize_rowwise_int8
+ *           on W [N x K], q range [-127, 127]): i8 [N x K], f32 [N]
+ *   W_f16   fp16 [N x K] or NULL
+ *   out     [M x N] of out_dtype (fp32, fp16 or bf16, round to nearest even)
+ *   workspace  qa_qlinear_int8_mixed_workspace(M, K) bytes (any content);
+ *           holds the outlier mask / list / count, s_x and Xq
+ * threshold = +inf gives plain vector-wise W8A8; a negative threshold sends
+ * every column through the fp16 product.
+ * Errors: NULL pointers, M < 0, N < 0, K <= 0, K % 16 != 0, misaligned
+ * pointers, NaN threshold, bad out_dtype, small workspace.
+ * ------------------------------------------------------------------------- */
+size_t qa_qlinear_int8_mixed_workspace(int64_t M, int64_t K);
+qa_status qa_qlinear_int8_mixed(const void* X_f16, int64_t M, int64_t K,
+                                const int8_t* Wq, const float* s_w, const void* W_f16_or_null,
+                                int64_t N, float threshold, void* out, qa_dtype out_dtype,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Block Hadamard rotation fused with int4 quantization and packing
+ * [GroupRot §二, §5.1, §5.2, §5.4; Scholia-IQ §7.3]
+ *
+ *   X'[r][b*G + j] = fl32( fl64(1/sqrt(G)) * sum_i X[r][b*G + i] * H[i][j] ),
+ *   H[i][j] = (-1)^popcount(i & j) (Sylvester order); the +-1 sum is exact.
+ *   PER_ROW:   s[r]    = absmax(X'[r][:]) / q_max                (s: [rows])
+ *   PER_GROUP: s[r][b] = absmax(X'[r][bG:(b+1)G]) / q_max        (s: [rows x K/G])
+ *   code = clip(rint(X' / s), q_min, q_max); element 8w+i of a row is the
+ *   two's-complement nibble in bits [4i+3:4i] of packed[r][w].
+ *   G = 1 is the identity rotation.
+ *   X       fp16 [rows x K]; packed u32 [rows x K/8]; s f32 as above
+ * Errors: NULL pointers, rows < 0, K <= 0, K % 8 != 0, K % G != 0, G not a
+ * power of two in [1, 256], PER_GROUP with G < 8, q range outside [-8, 7],
+ * q_max <= 0, q_min > q_max, misaligned X / packed.
+ * ------------------------------------------------------------------------- */
+qa_status qa_hadamard_quant_int4(const void* X_f16, int64_t rows, int64_t K, int32_t G,
+                                 qa_scale_mode mode, int32_t q_min, int32_t q_max,
+                                 uint32_t* packed, float* s, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * W4A4 group-Hadamard linear  [GroupRot §5.2, §5.4]
+ *
+ *   (Xp, s_x) = qa_hadamard_quant_int4(X, G, PER_ROW, -7, 7)  (on device)
+ *   acc_g[m][n] = sum_{k in group g} qx[m][k] * qw[n][k]     (int32)
+ *   out[m][n]   = s_x[m] * sum_g s_w[n][g] * acc_g[m][n]
+ *   X       fp16 [M x K]
+ *   Wp, s_w the offline weight: qa_hadamard_quant_int4(W, G, PER_GROUP, ...)
+ *           u32 [N x K/8], f32 [N x K/G]
+ *   out     [M x N] of out_dtype
+ *   workspace  qa_qlinear_w4a4_workspace(M, K) bytes (any content)
+ * Errors: NULL pointers, M < 0, N < 0, K <= 0, G not in {64, 128, 256},
+ * K % G != 0, misaligned pointers, bad out_dtype, small workspace.
+ * ------------------------------------------------------------------------- */
+size_t qa_qlinear_w4a4_workspace(int64_t M, int64_t K);
+qa_status qa_qlinear_w4a4(const void* X_f16, int64_t M, int64_t K, const uint32_t* Wp,
+                          const float* s_w, int64_t N, int32_t G, void* out, qa_dtype out_dtype,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Parity entry points: the integer accumulators of the two GEMMs, stored.
+ *
+ * qa_gemm_i8_i32  [AIInfra-Q01 "b. INT8 矩阵乘法与反量化"]
+ *   C[m][n] = sum_k A[m][k] * B[n][k]; A i8 [M x K], B i8 [N x K],
+ *   C i32 [M x N].  The caller keeps |C| < 2^31 (K * 128^2 < 2^31 suffices).
+ *   Errors: NULL, M < 0, N < 0, K <= 0, K % 16 != 0, misaligned pointers.
+ *
+ * qa_gemm_w4a4_group_acc  [GroupRot §5.4]
+ *   acc[m][n][g] = sum_{k in group g} qx[m][k] * qw[n][k] from packed int4
+ *   Xp u32 [M x K/8], Wp u32 [N x K/8]; acc i32 [M x N x K/G].
+ *   Errors: NULL, M < 0, N < 0, K <= 0, G not in {64, 128, 256},
+ *   K % G != 0, misaligned pointers.
+ * ------------------------------------------------------------------------- */
+qa_status qa_gemm_i8_i32(const int8_t* A, const int8_t* B, int64_t M, int64_t K, int64_t N,
+                         int32_t* C, void* stream);
+qa_status qa_gemm_w4a4_group_acc(const uint32_t* Xp, const uint32_t* Wp, int64_t M, int64_t K,
+                                 int64_t N, int32_t G, int32_t* acc, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QA_H */

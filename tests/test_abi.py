@@ -1,0 +1,150 @@
+"""The C ABI on the CPU: libqa.so loads, exports every entry point that
+include/qa.h declares, and rejects bad arguments before any HIP call (so no
+GPU is needed: nothing here launches a kernel)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import bit_quantized_linear_int8_amd as qa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qa.h")
+
+OK, NULL, SHAPE, ALIGN, VALUE, WORKSPACE = 0, 1, 2, 3, 4, 5
+
+# fake, suitably aligned device addresses: validation never dereferences them
+A = ctypes.c_void_p(0x10000)
+B = ctypes.c_void_p(0x20000)
+OUT = ctypes.c_void_p(0x30000)
+WS = ctypes.c_void_p(0x40000)
+MIS = ctypes.c_void_p(0x10001)        # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(qa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(qa.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(qa.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    L = qa.lib()
+    names = [L.qa_status_string(i).decode() for i in range(8)]
+    assert names == ["QA_OK", "QA_ERR_NULL", "QA_ERR_SHAPE", "QA_ERR_ALIGN", "QA_ERR_VALUE", "QA_ERR_WORKSPACE",
+                     "QA_ERR_UNSUPPORTED", "QA_ERR_DEVICE"]
+
+
+def test_workspace_sizes_are_monotone_and_cover_the_buffers():
+    L = qa.lib()
+    for M, K in [(1, 16), (16, 256), (2048, 4096)]:
+        ws = L.qa_qlinear_int8_mixed_workspace(M, K)
+        assert ws >= M * K + 4 * M + 5 * K + 4
+        assert ws % 256 == 0
+        assert L.qa_qlinear_w4a4_workspace(M, K) >= M * K // 2 + 4 * M
+    assert L.qa_qlinear_int8_mixed_workspace(-1, 16) == 0
+    assert L.qa_outlier_cols_workspace(0) == 0
+
+
+def mixed(**kw):
+    a = dict(X=A, M=16, K=256, Wq=B, s_w=OUT, W16=None, N=32, tau=6.0, out=OUT, dt=1, ws=WS, wsb=1 << 30)
+    a.update(kw)
+    return qa.lib().qa_qlinear_int8_mixed(a["X"], a["M"], a["K"], a["Wq"], a["s_w"], a["W16"], a["N"], a["tau"],
+                                          a["out"], a["dt"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), NULL), (dict(Wq=None), NULL), (dict(s_w=None), NULL), (dict(out=None), NULL),
+    (dict(ws=None), NULL),
+    (dict(M=-1), SHAPE), (dict(N=-1), SHAPE), (dict(K=0), SHAPE), (dict(K=24), SHAPE), (dict(K=131088), SHAPE),
+    (dict(X=MIS), ALIGN), (dict(Wq=MIS), ALIGN), (dict(ws=ctypes.c_void_p(0x40010)), ALIGN),
+    (dict(tau=math.nan), VALUE), (dict(dt=3), VALUE), (dict(dt=-1), VALUE),
+    (dict(wsb=100), WORKSPACE),
+    (dict(M=0), OK), (dict(N=0), OK),          # empty batch / layer: valid no-ops
+])
+def test_mixed_argument_errors(kw, status):
+    assert mixed(**kw) == status
+    if status != OK:
+        assert qa.last_error()
+
+
+def test_quantize_argument_errors():
+    f = qa.lib().qa_quantize_rowwise_int8
+    assert f(None, 4, 64, None, -127, 127, None, None, B, OUT, None) == NULL
+    assert f(A, 4, 64, None, -127, 127, None, None, B, None, None) == NULL          # dynamic needs s_out
+    assert f(A, 4, 60, None, -127, 127, None, None, B, OUT, None) == SHAPE
+    assert f(A, -4, 64, None, -127, 127, None, None, B, OUT, None) == SHAPE
+    assert f(MIS, 4, 64, None, -127, 127, None, None, B, OUT, None) == ALIGN
+    assert f(A, 4, 64, None, 5, 4, None, None, B, OUT, None) == VALUE
+    assert f(A, 4, 64, None, -129, 127, None, None, B, OUT, None) == VALUE
+    assert f(A, 4, 64, None, -127, 0, None, None, B, OUT, None) == VALUE             # dynamic q_max <= 0
+    assert f(A, 4, 64, None, -127, 127, None, WS, B, OUT, None) == VALUE             # z without s
+    assert f(A, 0, 64, None, -127, 127, None, None, B, OUT, None) == OK
+
+
+def test_outlier_argument_errors():
+    f = qa.lib().qa_outlier_cols
+    args = [A, 16, 256, 6.0, B, OUT, WS, None, WS, 1 << 20, None]
+
+    def call(i, v):
+        a = list(args)
+        a[i] = v
+        return f(*a)
+    assert call(0, None) == NULL
+    assert call(8, None) == NULL
+    assert call(2, 12) == SHAPE
+    assert call(1, -1) == SHAPE
+    assert call(0, MIS) == ALIGN
+    assert call(3, math.nan) == VALUE
+    assert call(9, 16) == WORKSPACE
+
+
+def test_hadamard_argument_errors():
+    f = qa.lib().qa_hadamard_quant_int4
+    assert f(None, 4, 256, 128, 0, -7, 7, B, OUT, None) == NULL
+    assert f(A, 4, 256, 96, 0, -7, 7, B, OUT, None) == SHAPE          # not a power of two
+    assert f(A, 4, 256, 512, 0, -7, 7, B, OUT, None) == SHAPE         # too large
+    assert f(A, 4, 200, 16, 0, -7, 7, B, OUT, None) == SHAPE          # K % G
+    assert f(A, 4, 256, 4, 1, -7, 7, B, OUT, None) == SHAPE           # per group needs G >= 8
+    assert f(A, 4, 256, 128, 2, -7, 7, B, OUT, None) == VALUE         # bad mode
+    assert f(A, 4, 256, 128, 0, -9, 7, B, OUT, None) == VALUE
+    assert f(A, 4, 256, 128, 0, -7, 8, B, OUT, None) == VALUE
+    assert f(MIS, 4, 256, 128, 0, -7, 7, B, OUT, None) == ALIGN
+    assert f(A, 0, 256, 128, 0, -7, 7, B, OUT, None) == OK
+
+
+def test_w4a4_argument_errors():
+    f = qa.lib().qa_qlinear_w4a4
+    base = [A, 16, 512, B, OUT, 32, 128, OUT, 0, WS, 1 << 30, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+    assert call(0, None) == NULL
+    assert call(6, 32) == SHAPE
+    assert call(2, 320) == SHAPE
+    assert call(3, MIS) == ALIGN
+    assert call(8, 7) == VALUE
+    assert call(10, 64) == WORKSPACE
+    g = qa.lib().qa_gemm_w4a4_group_acc
+    assert g(A, B, 4, 512, 4, 100, OUT, None) == SHAPE
+    assert g(A, None, 4, 512, 4, 128, OUT, None) == NULL
+
+
+def test_gemm_i8_argument_errors():
+    f = qa.lib().qa_gemm_i8_i32
+    assert f(None, B, 4, 64, 4, OUT, None) == NULL
+    assert f(A, B, 4, 40, 4, OUT, None) == SHAPE
+    assert f(A, MIS, 4, 64, 4, OUT, None) == ALIGN
+    assert f(A, B, 0, 64, 4, OUT, None) == OK

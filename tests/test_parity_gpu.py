@@ -1,0 +1,323 @@
+"""GPU parity: every libqa entry point against the CPU oracle on the same
+seeded inputs.
+
+Integer results (outlier sets, codes, scales, packed words, int32
+accumulators) must match bit for bit.  Float outputs must satisfy
+max |got - ref| <= 1e-3 * max |ref| (fp32 / fp16), and for bf16 outputs each
+element may also differ by one bf16 ulp of its reference value.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def qa():
+    import bit_quantized_linear_int8_amd as qa
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    qa.lib()
+    return qa
+
+
+def dev(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint32:
+        a = a.view(np.int32)
+    return torch.from_numpy(a).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def as_f64(t):
+    torch.cuda.synchronize()
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def assert_float_parity(got, ref, dtype):
+    ref = np.asarray(ref, np.float64)
+    tol = 1e-3 * np.abs(ref).max()
+    if dtype == torch.bfloat16:
+        mag = np.abs(ref)
+        ulp = np.where(mag > 0, 2.0 ** (np.floor(np.log2(np.maximum(mag, 1e-300))) - 7), 0.0)
+        tol = np.maximum(tol, ulp)
+    err = np.abs(got - ref)
+    bad = err > tol
+    assert not bad.any(), "max|diff| %g vs tol %g (%d elements over)" % (err.max(), np.max(tol), bad.sum())
+
+
+ODT = {0: torch.float32, 1: torch.float16, 2: torch.bfloat16}
+
+
+# ============================================================ outlier columns
+@pytest.mark.parametrize("M,K", [(1, 8), (3, 40), (37, 520), (64, 512), (130, 1032), (257, 4096)])
+@pytest.mark.parametrize("tau", [6.0, 0.5, -1.0, float("inf")])
+def test_outlier_cols_shapes(qa, M, K, tau):
+    X, _, _ = synthetic.mixed_inputs(M, K, 1, seed=M * 7 + K, n_dims=min(5, K // 8), p_token=0.5)
+    X[0, 0] = 6.0                                   # exactly at the threshold
+    mask, idx, count, colmax = qa.qa_outlier_cols(dev(X), tau)
+    om, oidx, ocm = oracle.outlier_cols(X, tau)
+    n = int(host(count)[0])
+    assert n == len(oidx)
+    assert np.array_equal(host(idx)[:n], oidx)
+    assert np.array_equal(host(mask), om)
+    assert np.array_equal(host(colmax), ocm)
+
+
+@pytest.mark.parametrize("name", ["tiny_mixed", "decode_mixed", "prefill_mixed"])
+def test_outlier_cols_configs(qa, name):
+    c = synthetic.config(name)
+    mask, idx, count, colmax = qa.qa_outlier_cols(dev(c["X"]), c["tau"])
+    om, oidx, ocm = oracle.outlier_cols(c["X"], c["tau"])
+    n = int(host(count)[0])
+    assert np.array_equal(host(idx)[:n], oidx)
+    assert np.array_equal(host(mask), om) and np.array_equal(host(colmax), ocm)
+    assert set(c["dims"].tolist()) <= set(oidx.tolist())
+
+
+def test_outlier_cols_reuses_dirty_scratch(qa):
+    X, _, _ = synthetic.mixed_inputs(50, 1024, 1, seed=3, n_dims=4)
+    scratch = torch.full((qa.qa_outlier_cols_workspace(1024),), 255, dtype=torch.uint8, device=DEV)
+    for _ in range(2):
+        mask, idx, count, colmax = qa.qa_outlier_cols(dev(X), 6.0, scratch=scratch)
+        om, oidx, ocm = oracle.outlier_cols(X, 6.0)
+        assert np.array_equal(host(idx)[: int(host(count)[0])], oidx)
+        assert np.array_equal(host(colmax), ocm)
+
+
+# ============================================================ row quantization
+@pytest.mark.parametrize("rows,K", [(1, 8), (5, 24), (9, 520), (33, 1032), (17, 2056), (6, 4096), (4, 8200),
+                                    (3, 8192), (2, 16392)])
+@pytest.mark.parametrize("with_mask", [False, True])
+def test_rowquant_dynamic(qa, rows, K, with_mask):
+    X, _, _ = synthetic.mixed_inputs(rows, K, 1, seed=rows + K, n_dims=min(4, K // 8), p_token=0.75)
+    X[0, :] = 0                                          # an all-zero row -> safe scale 1.0
+    mask = None
+    if with_mask:
+        mask = oracle.outlier_cols(X, 6.0)[0]
+    Xq, s = qa.qa_quantize_rowwise_int8(dev(X), mask=None if mask is None else dev(mask))
+    oq, os_ = oracle.quant_rows(X, mask=mask)
+    assert np.array_equal(host(Xq), oq)
+    assert np.array_equal(host(s), os_[:, 0])
+
+
+def test_rowquant_ties_take_the_even_code(qa):
+    # rows whose absmax is 127 (s = 1.0) and whose values sit exactly on x.5
+    K = 64
+    X = np.zeros((3, K), np.float16)
+    X[:, 0] = 127.0
+    X[0, 1:12] = [0.5, 1.5, 2.5, 3.5, -0.5, -1.5, -2.5, 100.5, -126.5, 63.5, 0.25]
+    X[1, 0] = 63.5                                       # s = fl32(63.5 / 127) = 0.5
+    X[1, 1:6] = [0.25, 0.75, 1.25, -0.25, 31.75]
+    X[2, 1:4] = [126.5, -126.5, 125.5]
+    Xq, s = qa.qa_quantize_rowwise_int8(dev(X))
+    oq, os_ = oracle.quant_rows(X)
+    assert np.array_equal(host(Xq), oq) and np.array_equal(host(s), os_[:, 0])
+    assert host(Xq)[0, 1:8].tolist() == [0, 2, 2, 4, 0, -2, -2]
+
+
+@pytest.mark.parametrize("q_min,q_max", [(-128, 127), (-127, 127), (0, 15), (-8, 7)])
+def test_rowquant_static_affine(qa, q_min, q_max):
+    rng = np.random.default_rng(q_max)
+    X = (rng.normal(0, 4, (7, 264))).astype(np.float16)
+    X[0, :6] = [0.5, 1.5, 2.5, -0.5, -1.5, -2.5]
+    s_in = rng.uniform(0.01, 1.0, 7).astype(np.float32)
+    s_in[0] = 1.0
+    z_in = rng.integers(-20, 20, 7).astype(np.int32)
+    z_in[0] = 0
+    mask = (rng.random(264) < 0.05).astype(np.uint8)
+    Xq, _ = qa.qa_quantize_rowwise_int8(dev(X), mask=dev(mask), q_min=q_min, q_max=q_max, s_in=dev(s_in),
+                                        z_in=dev(z_in))
+    oq, _ = oracle.quant_rows(X, mask=mask, qmin=q_min, qmax=q_max, s_in=s_in, z_in=z_in)
+    assert np.array_equal(host(Xq), oq)
+
+
+@pytest.mark.parametrize("name", ["decode_mixed", "prefill_mixed"])
+def test_weight_quant_configs(qa, name):
+    c = synthetic.config(name)
+    Wq, s_w = qa.qa_quantize_rowwise_int8(dev(c["W"]))
+    oq, os_ = oracle.quant_rows(c["W"])
+    assert np.array_equal(host(s_w), os_[:, 0])
+    assert np.array_equal(host(Wq), oq)
+
+
+# ============================================================ int8 GEMM, int32 accumulators
+@pytest.mark.parametrize("M,K,N", [(1, 16, 1), (37, 80, 45), (64, 128, 64), (130, 272, 140), (300, 528, 200),
+                                   (2048, 64, 2048), (1000, 400, 3000)])
+def test_gemm_i8_i32(qa, M, K, N):
+    rng = np.random.default_rng(M + K + N)
+    A = rng.integers(-128, 128, (M, K), dtype=np.int8)
+    B = rng.integers(-128, 128, (N, K), dtype=np.int8)
+    C = host(qa.qa_gemm_i8_i32(dev(A), dev(B)))
+    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, size=min(M, 40), replace=False)]))
+    assert np.array_equal(C[rows], oracle.gemm_i8_i32(A, B, rows=rows))
+
+
+def test_gemm_i8_i32_big_tiles(qa):
+    # enough 256 x 256 tiles to select the large-tile kernel, ragged in M, N, K
+    M, K, N = 4100, 144, 8200
+    rng = np.random.default_rng(11)
+    A = rng.integers(-127, 128, (M, K), dtype=np.int8)
+    B = rng.integers(-127, 128, (N, K), dtype=np.int8)
+    C = host(qa.qa_gemm_i8_i32(dev(A), dev(B)))
+    rows = np.unique(np.concatenate([[0, 255, 256, M - 1], rng.choice(M, size=24, replace=False)]))
+    assert np.array_equal(C[rows], oracle.gemm_i8_i32(A, B, rows=rows))
+
+
+# ============================================================ LLM.int8() mixed linear
+def _mixed_case(qa, X, W, tau, out_dtype, pass_w16, rows=None):
+    Wq, s_w = qa.qa_quantize_rowwise_int8(dev(W))
+    oWq, os_w = oracle.quant_rows(W)
+    assert np.array_equal(host(Wq), oWq) and np.array_equal(host(s_w), os_w[:, 0])
+    out = qa.qa_qlinear_int8_mixed(dev(X), Wq, s_w, W16=dev(W) if pass_w16 else None, threshold=tau,
+                                   out_dtype=ODT[out_dtype])
+    ref = oracle.qlinear_int8_mixed(X, oWq, os_w[:, 0], W16=W if pass_w16 else None, tau=tau, rows=rows)
+    got = as_f64(out)
+    if rows is not None:
+        got = got[rows]
+    assert_float_parity(got, ref, ODT[out_dtype])
+    return out
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 16, 1), (5, 48, 7), (16, 256, 256), (33, 528, 77), (130, 1040, 300),
+                                   (300, 272, 520)])
+@pytest.mark.parametrize("tau", [6.0, float("inf"), -1.0])
+@pytest.mark.parametrize("pass_w16", [True, False])
+def test_mixed_shapes(qa, M, K, N, tau, pass_w16):
+    X, W, _ = synthetic.mixed_inputs(M, K, N, seed=M * 31 + N, n_dims=min(5, K // 16), p_token=0.75)
+    _mixed_case(qa, X, W, tau, 0, pass_w16)
+
+
+@pytest.mark.parametrize("out_dtype", [0, 1, 2])
+def test_mixed_out_dtypes(qa, out_dtype):
+    X, W, _ = synthetic.mixed_inputs(40, 512, 96, seed=5, n_dims=3)
+    _mixed_case(qa, X, W, 6.0, out_dtype, False)
+
+
+def test_mixed_many_outliers(qa):
+    # more than 32 outlier columns: several fp16 MFMA passes in the epilogue
+    X, W, dims = synthetic.mixed_inputs(70, 1024, 130, seed=9, n_dims=75, p_token=0.5)
+    _mixed_case(qa, X, W, 6.0, 0, True)
+
+
+def test_mixed_tiny_config(qa):
+    c = synthetic.config("tiny_mixed")
+    _mixed_case(qa, c["X"], c["W"], c["tau"], c["out_dtype"], c["pass_w16"])
+
+
+def test_mixed_decode_config(qa):
+    c = synthetic.config("decode_mixed")
+    _mixed_case(qa, c["X"], c["W"], c["tau"], c["out_dtype"], c["pass_w16"])
+
+
+def test_mixed_prefill_config_sampled(qa):
+    c = synthetic.config("prefill_mixed")
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([[0, c["M"] - 1], rng.choice(c["M"], 30, replace=False)]))
+    _mixed_case(qa, c["X"], c["W"], c["tau"], c["out_dtype"], c["pass_w16"], rows=rows)
+
+
+def test_mixed_w8a8_config_sampled(qa):
+    c = synthetic.config("w8a8_ffn")
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([[0, c["M"] - 1], rng.choice(c["M"], 10, replace=False)]))
+    _mixed_case(qa, c["X"], c["W"], c["tau"], c["out_dtype"], c["pass_w16"], rows=rows)
+
+
+def test_mixed_empty_batch_and_layer(qa):
+    W = np.zeros((8, 64), np.float16)
+    Wq, s_w = qa.qa_quantize_rowwise_int8(dev(W))
+    out = qa.qa_qlinear_int8_mixed(torch.zeros((0, 64), dtype=torch.float16, device=DEV), Wq, s_w)
+    assert out.shape == (0, 8)
+    out = qa.qa_qlinear_int8_mixed(torch.zeros((4, 64), dtype=torch.float16, device=DEV), Wq[:0], s_w[:0])
+    assert out.shape == (4, 0)
+
+
+def test_mixed_is_deterministic(qa):
+    X, W, _ = synthetic.mixed_inputs(200, 1024, 300, seed=13, n_dims=6)
+    Wq, s_w = qa.qa_quantize_rowwise_int8(dev(W))
+    a = host(qa.qa_qlinear_int8_mixed(dev(X), Wq, s_w, out_dtype=torch.float32))
+    b = host(qa.qa_qlinear_int8_mixed(dev(X), Wq, s_w, out_dtype=torch.float32))
+    assert np.array_equal(a, b)
+
+
+# ============================================================ Hadamard + int4
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16, 32, 64, 128, 256])
+@pytest.mark.parametrize("per_group", [False, True])
+def test_hadamard_quant_int4(qa, G, per_group):
+    if per_group and G < 8:
+        pytest.skip("per-group scales need G >= 8")
+    rows, K = 13, max(G, 8) * 5
+    X, _, _ = synthetic.w4a4_inputs(rows, K, 1, seed=G, n_dims=min(3, K // 16))
+    X[1, :] = 0
+    packed, s = qa.qa_hadamard_quant_int4(dev(X), G, per_group)
+    op, os_ = oracle.hadamard_quant_int4(X, G, per_group)
+    assert np.array_equal(host(s), os_)
+    assert np.array_equal(host(packed).view(np.uint32), op)
+
+
+@pytest.mark.parametrize("K", [4096, 8192, 8448, 16384])
+def test_hadamard_quant_int4_row_lengths(qa, K):
+    X, _, _ = synthetic.w4a4_inputs(9, K, 1, seed=K)
+    packed, s = qa.qa_hadamard_quant_int4(dev(X), 128, False)
+    op, os_ = oracle.hadamard_quant_int4(X, 128, False)
+    assert np.array_equal(host(s), os_) and np.array_equal(host(packed).view(np.uint32), op)
+
+
+def test_hadamard_quant_int4_config(qa):
+    c = synthetic.config("w4a4_hadamard")
+    Wp, s_w = qa.qa_hadamard_quant_int4(dev(c["W"]), c["G"], True)
+    oWp, os_w = oracle.hadamard_quant_int4(c["W"], c["G"], True)
+    assert np.array_equal(host(s_w), os_w) and np.array_equal(host(Wp).view(np.uint32), oWp)
+    Xp, s_x = qa.qa_hadamard_quant_int4(dev(c["X"]), c["G"], False)
+    oXp, os_x = oracle.hadamard_quant_int4(c["X"], c["G"], False)
+    assert np.array_equal(host(s_x), os_x) and np.array_equal(host(Xp).view(np.uint32), oXp)
+
+
+# ============================================================ W4A4 GEMM
+@pytest.mark.parametrize("M,K,N,G", [(1, 64, 1, 64), (20, 256, 33, 128), (64, 384, 64, 128), (130, 512, 70, 256),
+                                     (300, 1024, 500, 64), (2048, 256, 2048, 128)])
+def test_w4a4_group_acc(qa, M, K, N, G):
+    rng = np.random.default_rng(M + N)
+    Xp = rng.integers(0, 2 ** 32, (M, K // 8), dtype=np.uint64).astype(np.uint32)
+    Wp = rng.integers(0, 2 ** 32, (N, K // 8), dtype=np.uint64).astype(np.uint32)
+    acc = host(qa.qa_gemm_w4a4_group_acc(dev(Xp), dev(Wp), K, G))
+    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, size=min(M, 16), replace=False)]))
+    assert np.array_equal(acc[rows], oracle.w4a4_group_acc(Xp, Wp, K, G, rows=rows))
+
+
+@pytest.mark.parametrize("M,K,N,G", [(1, 128, 1, 128), (24, 512, 40, 128), (77, 768, 130, 256),
+                                     (200, 1024, 300, 64)])
+def test_w4a4_linear_shapes(qa, M, K, N, G):
+    X, W, _ = synthetic.w4a4_inputs(M, K, N, seed=M + K)
+    Wp, s_w = qa.qa_hadamard_quant_int4(dev(W), G, True)
+    oWp, os_w = oracle.hadamard_quant_int4(W, G, True)
+    assert np.array_equal(host(Wp).view(np.uint32), oWp)
+    out = qa.qa_qlinear_w4a4(dev(X), Wp, s_w, G=G)
+    assert_float_parity(as_f64(out), oracle.qlinear_w4a4(X, oWp, os_w, G), torch.float32)
+
+
+def test_w4a4_config_sampled(qa):
+    c = synthetic.config("w4a4_hadamard")
+    G = c["G"]
+    Wp, s_w = qa.qa_hadamard_quant_int4(dev(c["W"]), G, True)
+    oWp, os_w = oracle.hadamard_quant_int4(c["W"], G, True)
+    assert np.array_equal(host(Wp).view(np.uint32), oWp)
+    out = as_f64(qa.qa_qlinear_w4a4(dev(c["X"]), Wp, s_w, G=G))
+    rng = np.random.default_rng(2)
+    rows = np.unique(np.concatenate([[0, c["M"] - 1], rng.choice(c["M"], 40, replace=False)]))
+    ref = oracle.qlinear_w4a4(c["X"], oWp, os_w, G, rows=rows)
+    assert_float_parity(out[rows], ref, torch.float32)
+    # int32 group accumulators of the same call, bit exact on sampled rows
+    Xp, _ = qa.qa_hadamard_quant_int4(dev(c["X"]), G, False)
+    acc = host(qa.qa_gemm_w4a4_group_acc(Xp, Wp, c["K"], G))
+    oXp, _ = oracle.hadamard_quant_int4(c["X"], G, False)
+    assert np.array_equal(acc[rows[:8]], oracle.w4a4_group_acc(oXp, oWp, c["K"], G, rows=rows[:8]))
