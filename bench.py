@@ -1,0 +1,277 @@
+"""Benchmark of the quantized linear layer on one MI355X.
+
+Headline (the JSON line's `value`): the LLM.int8() mixed-precision linear at
+the decode shape -- X fp16 [8 x 4096] with 6 outlier feature dims, W int8
+[4096 x 4096] with per-channel fp32 scales, threshold 6.0, fp16 output.  One
+step is one qa_qlinear_int8_mixed call (outlier detection, per-token int8
+quantization, int8 MFMA GEMM, dequant epilogue, fp16 outlier product) on
+inputs already resident in HBM.  Steps are replayed from a captured HIP graph
+and cycle through copies of the weight so that every step reads it from HBM
+rather than from the 256 MB Infinity Cache.  `value` is algorithmic bytes
+moved per step / step time (GB/s).
+
+Also reported (same JSON line, key "also"): whole-call throughput of the
+prefill-shape mixed linear, the W8A8 FFN shape and the W4A4 group-Hadamard
+linear, in int8 TOPS against the dense int8 MFMA peak.
+
+roofline: the decode kernel's algorithmic bytes per launch / its average
+duration from HIP events around each launch (on the launch stream).
+cpu_baseline: the CPU oracle timed on this host on whole decode steps.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "quantized-linear TOPS & % int8 MFMA peak; decode GB/s & % of 8 TB/s"
+HBM_PEAK_GBS = 8000.0
+INT8_PEAK_TOPS = 5033.2            # 256 CU x 2.4 GHz x 8192 int8 ops / clk / CU (dense)
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=256)
+    p.add_argument("--warmup", type=int, default=32)
+    p.add_argument("--no-also", action="store_true", help="skip the prefill / W8A8 / W4A4 lines")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--only", default=None,
+                   help="run one workload only (decode|prefill|w8a8|w4a4|copy), for profiling; copy is a plain "
+                        "1 GiB device copy used to calibrate HBM byte counters")
+    return p.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class GraphSteps:
+    """Capture `fns` (one launch sequence each) into one HIP graph."""
+
+    def __init__(self, torch, fns):
+        self.torch = torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for f in fns:
+                f()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        self.g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.g):
+            for f in fns:
+                f()
+        self.n = len(fns)
+
+    def replay(self):
+        self.g.replay()
+
+
+def time_graph(torch, gs, steps, warmup):
+    """Replay the graph until `warmup` then exactly `steps` steps have run
+    (steps rounded up to whole graphs); returns (ms per step, steps run)."""
+    reps_w = max(1, -(-warmup // gs.n))
+    for _ in range(reps_w):
+        gs.replay()
+    reps = max(1, -(-steps // gs.n))
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(reps):
+        gs.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3
+    n = reps * gs.n
+    return e0.elapsed_time(e1) / n, wall / n, n
+
+
+def kernel_event_ms(torch, fns, reps):
+    """Average duration of single-launch calls, each bracketed by HIP events
+    recorded on the launch stream."""
+    evs = []
+    for i in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fns[i % len(fns)]()
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in evs)
+    return sum(ts) / len(ts), ts[len(ts) // 2]
+
+
+# --------------------------------------------------------------------------- workloads
+def decode_workload(torch, qa, synthetic, dev):
+    c = synthetic.config("decode_mixed")
+    M, K, N = c["M"], c["K"], c["N"]
+    X = torch.from_numpy(c["X"]).to(dev)
+    W16 = torch.from_numpy(c["W"]).to(dev)
+    Wq, s_w = qa.qa_quantize_rowwise_int8(W16)
+    del W16
+    copies = max(2, -(-2 * MALL_BYTES // (N * K)))
+    Wqs = [Wq] + [Wq.clone() for _ in range(copies - 1)]
+    sws = [s_w] + [s_w.clone() for _ in range(copies - 1)]
+    out = torch.empty((M, N), dtype=torch.float16, device=dev)
+    ws = torch.empty(qa.qa_qlinear_int8_mixed_workspace(M, K), dtype=torch.uint8, device=dev)
+
+    def mk(i):
+        return lambda: qa.qa_qlinear_int8_mixed(X, Wqs[i], sws[i], None, c["tau"], out=out, workspace=ws)
+    fns = [mk(i) for i in range(copies)]
+    # algorithmic bytes per call: int8 weight + fp32 channel scales + fp16 X read + fp16 out written
+    nbytes = N * K + 4 * N + 2 * M * K + 2 * M * N
+    return c, fns, nbytes, copies
+
+
+def prefill_like(torch, qa, synthetic, dev, name):
+    c = synthetic.config(name)
+    M, K, N = c["M"], c["K"], c["N"]
+    X = torch.from_numpy(c["X"]).to(dev)
+    W16 = torch.from_numpy(c["W"]).to(dev)
+    Wq, s_w = qa.qa_quantize_rowwise_int8(W16)
+    del W16
+    odt = {0: torch.float32, 1: torch.float16, 2: torch.bfloat16}[c["out_dtype"]]
+    out = torch.empty((M, N), dtype=odt, device=dev)
+    ws = torch.empty(qa.qa_qlinear_int8_mixed_workspace(M, K), dtype=torch.uint8, device=dev)
+    fns = [lambda: qa.qa_qlinear_int8_mixed(X, Wq, s_w, None, c["tau"], out=out, workspace=ws)]
+    return c, fns, 2 * M * N * K
+
+
+def w4a4_workload(torch, qa, synthetic, dev):
+    c = synthetic.config("w4a4_hadamard")
+    M, K, N, G = c["M"], c["K"], c["N"], c["G"]
+    X = torch.from_numpy(c["X"]).to(dev)
+    Wp, s_w = qa.qa_hadamard_quant_int4(torch.from_numpy(c["W"]).to(dev), G, True)
+    out = torch.empty((M, N), dtype=torch.float32, device=dev)
+    ws = torch.empty(qa.qa_qlinear_w4a4_workspace(M, K), dtype=torch.uint8, device=dev)
+    fns = [lambda: qa.qa_qlinear_w4a4(X, Wp, s_w, G=G, out=out, workspace=ws)]
+    return c, fns, 2 * M * N * K
+
+
+# --------------------------------------------------------------------------- CPU oracle baseline
+def cpu_baseline(c, nbytes, seconds):
+    import numpy as np
+    import oracle
+    Wq, s_w = oracle.quant_rows(c["W"])
+    s_w = s_w[:, 0]
+    oracle.qlinear_int8_mixed(c["X"], Wq, s_w, tau=c["tau"])         # warm
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.qlinear_int8_mixed(c["X"], Wq, s_w, tau=c["tau"])
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    per = el / n
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    return {"value": round(nbytes / per / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "%d whole decode steps (all 8 tokens x 4096 channels) of the plain-C oracle, %.1f s, "
+                      "%.1f ms per step" % (n, el, per * 1e3)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build runs on a single MI355X and has no multi-GPU "
+              "path (--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import bit_quantized_linear_int8_amd as qa
+    import synthetic
+    qa.lib()
+    dev = torch.device("cuda:0")
+
+    result = None
+    also = []
+    if args.only == "copy":
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record()
+        for _ in range(reps):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        print(json.dumps({"copy_bytes": n, "ms": round(ms, 4), "read_write_GBs": round(2 * n / (ms * 1e-3) / 1e9, 1)}))
+        return
+    if args.only in (None, "decode"):
+        log("[bench] decode_mixed: building inputs")
+        c, fns, nbytes, copies = decode_workload(torch, qa, synthetic, dev)
+        gs = GraphSteps(torch, fns)
+        log("[bench] decode_mixed: timing %d steps (graph of %d)" % (args.steps, gs.n))
+        ms, wall_ms, n = time_graph(torch, gs, args.steps, args.warmup)
+        k_avg, k_med = kernel_event_ms(torch, fns, max(args.steps, copies))
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        ach = nbytes / (k_avg * 1e-3) / 1e9
+        result = {
+            "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": n,
+            "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "i8", "data": "synthetic",
+            "config": {"workload": "decode_mixed: LLM.int8() mixed linear, X fp16 [8 x 4096] (6 outlier dims), "
+                                   "W int8 [4096 x 4096] + fp32 channel scales, threshold 6.0, fp16 out",
+                       "M": c["M"], "K": c["K"], "N": c["N"], "threshold": c["tau"], "weight_copies": copies,
+                       "bytes_per_step": nbytes, "launch": "HIP graph replay", "wall_ms_per_step": round(wall_ms, 6)},
+            "roofline": {"bound": "hbm", "kernel": "k_decode_mixed", "achieved": round(ach, 2),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                         "traffic": None, "kernel_ms_avg": round(k_avg, 6), "kernel_ms_median": round(k_med, 6)},
+        }
+        log("[bench] decode: %.1f GB/s per step, kernel %.2f us (events)" % (gbs, k_avg * 1e3))
+        if not args.no_cpu:
+            log("[bench] cpu oracle baseline (~%.0f s)" % args.cpu_seconds)
+            result["cpu_baseline"] = cpu_baseline(c, nbytes, args.cpu_seconds)
+        del fns, gs
+        torch.cuda.empty_cache()
+
+    run_also = (args.only is None and not args.no_also) or args.only in ("prefill", "w8a8", "w4a4")
+    if run_also:
+        todo = []
+        for name, key in (("prefill_mixed", "prefill"), ("w8a8_ffn", "w8a8"), ("w4a4_hadamard", "w4a4")):
+            if args.only in (None, key):
+                todo.append((name, key))
+        for name, key in todo:
+            log("[bench] %s: building inputs" % name)
+            if key == "w4a4":
+                c, fns, ops = w4a4_workload(torch, qa, synthetic, dev)
+            else:
+                c, fns, ops = prefill_like(torch, qa, synthetic, dev, name)
+            gs = GraphSteps(torch, fns * 4)
+            st = min(args.steps, 64)
+            log("[bench] %s: timing %d calls" % (name, st))
+            ms, wall_ms, n = time_graph(torch, gs, st, min(args.warmup, 8))
+            tops = ops / (ms * 1e-3) / 1e12
+            also.append({"workload": name, "M": c["M"], "K": c["K"], "N": c["N"], "ms_per_call": round(ms, 5),
+                         "int8_tops": round(tops, 2), "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
+                         "calls": n, "note": "whole call (all kernels), graph replay, weights warm"})
+            log("[bench] %s: %.3f ms per call, %.1f TOPS" % (name, ms, tops))
+            del fns, gs
+            torch.cuda.empty_cache()
+
+    if result is None:
+        print(json.dumps({"also": also}))
+        return
+    result["also"] = also
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

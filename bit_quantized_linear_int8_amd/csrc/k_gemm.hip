@@ -62,20 +62,17 @@ __device__ __forceinline__ void tile_of_block(int bid, int tiles_m, int tiles_n,
 
 __device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
 
-// Global -> registers for one stage: rows [r0, r0 + ROWS) of a K-contiguous
-// byte matrix with row stride ld bytes, columns [kb, kb + 128) bytes.
+// Global -> registers for one stage: rows [0, ROWS) of the block's rows of a
+// K-contiguous byte matrix (row stride ld bytes; `rs` covers the block's first
+// row to the end of the matrix, so rows past the end read zeros), byte columns
+// [kb, kb + 128); chunks at or past kbytes read zeros.
 template <int NCH, int THREADS>
-__device__ __forceinline__ void g2r(const uint8_t* __restrict__ base, int64_t ld, int64_t r0, int64_t rows,
-                                    int64_t kb, int64_t kbytes, u32x4* reg) {
+__device__ __forceinline__ void g2r(rsrc_t rs, uint32_t ld, uint32_t kb, uint32_t kbytes, u32x4* reg) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
         const int q = threadIdx.x + i * THREADS;
-        const int r = q >> 3, c = q & 7;
-        const int64_t gr = r0 + r, gk = kb + c * 16;
-        if (gr < rows && gk < kbytes)
-            reg[i] = *reinterpret_cast<const u32x4*>(base + gr * ld + gk);
-        else
-            reg[i] = u32x4{0u, 0u, 0u, 0u};
+        const uint32_t r = q >> 3, gk = kb + (q & 7) * 16;
+        reg[i] = bload16(rs, gk < kbytes ? r * ld + gk : kOOB);
     }
 }
 
@@ -95,7 +92,7 @@ template <class C>
 __device__ __forceinline__ void mainloop_i8(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
                                             int64_t M, int64_t N, int64_t K, int64_t m0, int64_t n0,
                                             uint8_t* smem, v4i (&acc)[C::FM][C::FN]) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int wm = wave / C::WN, wn = wave % C::WN;
     const uint8_t* Ab = reinterpret_cast<const uint8_t*>(A);
     const uint8_t* Bb = reinterpret_cast<const uint8_t*>(B);
@@ -105,9 +102,12 @@ __device__ __forceinline__ void mainloop_i8(const int8_t* __restrict__ A, const 
         for (int j = 0; j < C::FN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
     const int nk = (int)((K + C::BK - 1) / C::BK);
+    const rsrc_t rsa = make_rsrc(Ab + m0 * K, (M - m0) * K);
+    const rsrc_t rsb = make_rsrc(Bb + n0 * K, (N - n0) * K);
+    const uint32_t ld = (uint32_t)K, kbytes = (uint32_t)K;
     u32x4 ra[C::A_CH], rb[C::B_CH];
-    g2r<C::A_CH, C::THREADS>(Ab, K, m0, M, 0, K, ra);
-    g2r<C::B_CH, C::THREADS>(Bb, K, n0, N, 0, K, rb);
+    g2r<C::A_CH, C::THREADS>(rsa, ld, 0, kbytes, ra);
+    g2r<C::B_CH, C::THREADS>(rsb, ld, 0, kbytes, rb);
     r2s<C::A_CH, C::THREADS>(smem, ra);
     r2s<C::B_CH, C::THREADS>(smem + C::LDS_A, rb);
     __syncthreads();
@@ -116,8 +116,8 @@ __device__ __forceinline__ void mainloop_i8(const int8_t* __restrict__ A, const 
         uint8_t* sb = sa + C::LDS_A;
         const bool more = kt + 1 < nk;
         if (more) {
-            g2r<C::A_CH, C::THREADS>(Ab, K, m0, M, (int64_t)(kt + 1) * C::BK, K, ra);
-            g2r<C::B_CH, C::THREADS>(Bb, K, n0, N, (int64_t)(kt + 1) * C::BK, K, rb);
+            g2r<C::A_CH, C::THREADS>(rsa, ld, (uint32_t)(kt + 1) * C::BK, kbytes, ra);
+            g2r<C::B_CH, C::THREADS>(rsb, ld, (uint32_t)(kt + 1) * C::BK, kbytes, rb);
         }
 #pragma unroll
         for (int s = 0; s < C::BK / 64; ++s) {
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_i8_i32(const int8_t* __rest
     const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
     v4i acc[C::FM][C::FN];
     mainloop_i8<C>(A, B, M, N, K, m0, n0, smem, acc);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int wm = wave / C::WN, wn = wave % C::WN;
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
@@ -195,26 +195,24 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_i8_mixed(const int8_t* __re
     v4i acc[C::FM][C::FN];
     mainloop_i8<C>(Xq, Wq, M, N, K, m0, n0, smem, acc);
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int wm = wave / C::WN, wn = wave % C::WN;
     const int64_t rb = m0 + wm * C::TM, cb = n0 + wn * C::TN;
 
     // dequantize: C * s_x[m] * s_w[n]
     v4f cf[C::FM][C::FN];
     float sw[C::FN];
+    const rsrc_t rsw = make_rsrc(ep.s_w + cb, (N - cb) * 4);
+    const rsrc_t rsx = make_rsrc(ep.s_x + rb, (M - rb) * 4);
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
-        const int64_t col = cb + j * 16 + (lane & 15);
-        sw[j] = col < N ? ep.s_w[col] : 0.0f;
-    }
+    for (int j = 0; j < C::FN; ++j)
+        sw[j] = __builtin_bit_cast(float, bload4(rsw, (uint32_t)(j * 16 + (lane & 15)) * 4));
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) {
         float sx[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int64_t row = rb + i * 16 + 4 * (lane >> 4) + e;
-            sx[e] = row < M ? ep.s_x[row] : 0.0f;
-        }
+        for (int e = 0; e < 4; ++e)
+            sx[e] = __builtin_bit_cast(float, bload4(rsx, (uint32_t)(i * 16 + 4 * (lane >> 4) + e) * 4));
 #pragma unroll
         for (int j = 0; j < C::FN; ++j)
 #pragma unroll
@@ -228,19 +226,27 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_i8_mixed(const int8_t* __re
     const int cnt = *ep.count;
     _Float16* xo = reinterpret_cast<_Float16*>(smem);           // [BM][32]
     _Float16* wo = xo + C::BM * 32;                              // [BN][32]
+    const rsrc_t rxo = make_rsrc(ep.X + m0 * K, (M - m0) * K * 2);
+    const rsrc_t rwo = ep.W16 ? make_rsrc(ep.W16 + n0 * K, (N - n0) * K * 2) : make_rsrc(ep.Wq + n0 * K, (N - n0) * K);
+    const rsrc_t rsn = make_rsrc(ep.s_w + n0, (N - n0) * 4);
     for (int h0 = 0; h0 < cnt; h0 += 32) {
+        // this thread always serves outlier slot e = t % 32 (THREADS % 32 == 0)
+        const int e = threadIdx.x & 31;
+        const rsrc_t ridx = make_rsrc(ep.idx + h0, (int64_t)(cnt - h0) * 4);
+        const uint32_t kc = bload4(ridx, (uint32_t)e * 4);
+        const bool valid = h0 + e < cnt;
         for (int t = threadIdx.x; t < (C::BM + C::BN) * 32; t += C::THREADS) {
-            const int r = t >> 5, e = t & 31, h = h0 + e;
-            uint16_t v = 0;
-            if (h < cnt) {
-                const int64_t kc = ep.idx[h];
-                if (r < C::BM) {
-                    const int64_t row = m0 + r;
-                    if (row < M) v = ep.X[row * K + kc];
+            const uint32_t r = t >> 5;
+            uint16_t v;
+            if (r < (uint32_t)C::BM) {
+                v = bload2(rxo, valid ? (r * (uint32_t)K + kc) * 2 : kOOB);
+            } else {
+                const uint32_t rr = r - C::BM;
+                if (ep.W16) {
+                    v = bload2(rwo, valid ? (rr * (uint32_t)K + kc) * 2 : kOOB);
                 } else {
-                    const int64_t col = n0 + (r - C::BM);
-                    if (col < N)
-                        v = ep.W16 ? ep.W16[col * K + kc] : f2h(ep.s_w[col] * (float)ep.Wq[col * K + kc]);
+                    const int8_t q = (int8_t)bload1(rwo, valid ? rr * (uint32_t)K + kc : kOOB);
+                    v = f2h(__builtin_bit_cast(float, bload4(rsn, rr * 4)) * (float)q);
                 }
             }
             xo[t] = __builtin_bit_cast(_Float16, v);
@@ -356,6 +362,8 @@ __device__ __forceinline__ v4i unpack_hi_nibbles(u32x2 w) {
     return d;
 }
 
+constexpr int W4_SW_LDS = 4096;                 // floats of per-group weight scales kept in LDS
+
 template <class C, int G, bool STORE_ACC>
 __global__ __launch_bounds__(C::THREADS) void k_gemm_w4a4(const uint32_t* __restrict__ Xp,
                                                           const float* __restrict__ s_x,
@@ -364,17 +372,32 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_w4a4(const uint32_t* __rest
                                                           int64_t N, void* __restrict__ out, int out_dtype,
                                                           int tiles_m, int tiles_n) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
+    __shared__ float sws[STORE_ACC ? 1 : W4_SW_LDS];   // s_w[n0 + c][g] * 2^-8 as [g][c]
     constexpr int KS = 256;                      // K elements per stage
     constexpr int STEPS = KS / 64;               // MFMA steps per stage
     constexpr int SPG = G / 64;                  // MFMA steps per group
     int tm, tn;
     tile_of_block(blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int wm = wave / C::WN, wn = wave % C::WN;
     const int64_t kbytes = K / 2, ng = K / G;
     const uint8_t* Ab = reinterpret_cast<const uint8_t*>(Xp);
     const uint8_t* Bb = reinterpret_cast<const uint8_t*>(Wp);
+    const rsrc_t rsa = make_rsrc(Ab + m0 * kbytes, (M - m0) * kbytes);
+    const rsrc_t rsb = make_rsrc(Bb + n0 * kbytes, (N - n0) * kbytes);
+    const uint32_t ld = (uint32_t)kbytes;
+
+    // per-group weight scales of this block's columns, staged once in LDS
+    // when they fit (else read per group from L2)
+    const bool sw_in_lds = !STORE_ACC && ng * C::BN <= W4_SW_LDS;
+    const rsrc_t rsw = make_rsrc(s_w + (STORE_ACC ? 0 : n0 * ng), STORE_ACC ? 0 : (N - n0) * ng * 4);
+    if (sw_in_lds) {
+        for (int t = threadIdx.x; t < ng * C::BN; t += C::THREADS) {
+            const int cc = t / (int)ng, g = t - cc * (int)ng;        // coalesced over g
+            sws[g * C::BN + cc] = __builtin_bit_cast(float, bload4(rsw, (uint32_t)t * 4)) * 0x1p-8f;
+        }
+    }
 
     v4f f[C::FM][C::FN];
     v4i acc[C::FM][C::FN];
@@ -385,15 +408,14 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_w4a4(const uint32_t* __rest
             f[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
             acc[i][j] = v4i{0, 0, 0, 0};
         }
-    float swj[C::FN];
-    int64_t colj[C::FN];
+    int ccol[C::FN];                               // block-local column of each fragment
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j) colj[j] = n0 + wn * C::TN + j * 16 + (lane & 15);
+    for (int j = 0; j < C::FN; ++j) ccol[j] = wn * C::TN + j * 16 + (lane & 15);
 
     const int nk = (int)((kbytes + C::BK - 1) / C::BK);
     u32x4 ra[C::A_CH], rb[C::B_CH];
-    g2r<C::A_CH, C::THREADS>(Ab, kbytes, m0, M, 0, kbytes, ra);
-    g2r<C::B_CH, C::THREADS>(Bb, kbytes, n0, N, 0, kbytes, rb);
+    g2r<C::A_CH, C::THREADS>(rsa, ld, 0, (uint32_t)kbytes, ra);
+    g2r<C::B_CH, C::THREADS>(rsb, ld, 0, (uint32_t)kbytes, rb);
     r2s<C::A_CH, C::THREADS>(smem, ra);
     r2s<C::B_CH, C::THREADS>(smem + C::LDS_A, rb);
     __syncthreads();
@@ -404,8 +426,8 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_w4a4(const uint32_t* __rest
         uint8_t* sb = sa + C::LDS_A;
         const bool more = kt + 1 < nk;
         if (more) {
-            g2r<C::A_CH, C::THREADS>(Ab, kbytes, m0, M, (int64_t)(kt + 1) * C::BK, kbytes, ra);
-            g2r<C::B_CH, C::THREADS>(Bb, kbytes, n0, N, (int64_t)(kt + 1) * C::BK, kbytes, rb);
+            g2r<C::A_CH, C::THREADS>(rsa, ld, (uint32_t)(kt + 1) * C::BK, (uint32_t)kbytes, ra);
+            g2r<C::B_CH, C::THREADS>(rsb, ld, (uint32_t)(kt + 1) * C::BK, (uint32_t)kbytes, rb);
         }
 #pragma unroll
         for (int s = 0; s < STEPS; ++s, ++step) {
@@ -429,25 +451,28 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_w4a4(const uint32_t* __rest
                     for (int j = 0; j < C::FN; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
                 if ((step + 1) % SPG == 0) {
-                    const int64_t g = step / SPG;
+                    const int g = step / SPG;
                     if constexpr (STORE_ACC) {
                         int32_t* accp = static_cast<int32_t*>(out);
 #pragma unroll
                         for (int i = 0; i < C::FM; ++i)
 #pragma unroll
                             for (int j = 0; j < C::FN; ++j) {
+                                const int64_t col = n0 + ccol[j];
 #pragma unroll
                                 for (int e = 0; e < 4; ++e) {
                                     const int64_t row = m0 + wm * C::TM + i * 16 + 4 * (lane >> 4) + e;
-                                    if (row < M && colj[j] < N)
-                                        accp[(row * N + colj[j]) * ng + g] = acc[i][j][e] >> 8;
+                                    if (row < M && col < N) accp[(row * N + col) * ng + g] = acc[i][j][e] >> 8;
                                 }
                                 acc[i][j] = v4i{0, 0, 0, 0};
                             }
                     } else {
+                        float swj[C::FN];
 #pragma unroll
                         for (int j = 0; j < C::FN; ++j)
-                            swj[j] = colj[j] < N ? s_w[colj[j] * ng + g] * 0x1p-8f : 0.0f;
+                            swj[j] = sw_in_lds ? sws[g * C::BN + ccol[j]]
+                                               : __builtin_bit_cast(float, bload4(rsw, (uint32_t)(ccol[j] * ng + g) * 4)) *
+                                                     0x1p-8f;
 #pragma unroll
                         for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -469,16 +494,19 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_w4a4(const uint32_t* __rest
         __syncthreads();
     }
     if constexpr (!STORE_ACC) {
+        const rsrc_t rsx = make_rsrc(s_x + m0, (M - m0) * 4);
 #pragma unroll
         for (int i = 0; i < C::FM; ++i)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int64_t row = m0 + wm * C::TM + i * 16 + 4 * (lane >> 4) + e;
-                if (row >= M) continue;
-                const float sx = s_x[row];
+                const int rl = wm * C::TM + i * 16 + 4 * (lane >> 4) + e;
+                const float sx = __builtin_bit_cast(float, bload4(rsx, (uint32_t)rl * 4));
+                const int64_t row = m0 + rl;
 #pragma unroll
-                for (int j = 0; j < C::FN; ++j)
-                    if (colj[j] < N) store_out(out, out_dtype, row * N + colj[j], sx * f[i][j][e]);
+                for (int j = 0; j < C::FN; ++j) {
+                    const int64_t col = n0 + ccol[j];
+                    if (row < M && col < N) store_out(out, out_dtype, row * N + col, sx * f[i][j][e]);
+                }
             }
     }
 }

@@ -10,6 +10,9 @@
 //   低比特量化加速：分组旋转方法从W8A8到W4A4: §二 normalized Hadamard on
 //     G-wide blocks, §5.2 rotation fused with dynamic quantization, §5.4
 //     eight int4 per 32-bit word.
+//
+// All global reads are raw buffer loads (hardware range check, zeros outside)
+// so every load of a wave is issued before the first one is waited for.
 #include "qa_device.hpp"
 #include "qa_launch.hpp"
 
@@ -24,96 +27,182 @@ __global__ void k_zero_u32(uint32_t* __restrict__ p, int64_t n) {
         p[i] = 0u;
 }
 
-// ---------------------------------------------------------------------------
-// Outlier columns.  Each block reduces a tile of OC_ROWS rows x OC_COLS
-// columns (every lane owns 8 adjacent columns, one 16-byte load per row),
-// folds the four waves in LDS and merges into the running column max with a
-// device-scope atomic max on the fp32 bits (non-negative floats order like
-// their bit patterns).  The last block to finish (ticket) turns the column
-// max into the mask and the ascending outlier list with a ballot scan.
-// ---------------------------------------------------------------------------
-constexpr int OC_COLS = 512;
-constexpr int OC_ROWS = 64;
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-__global__ __launch_bounds__(256) void k_outlier_cols(
-    const uint16_t* __restrict__ X, int64_t M, int64_t K, float tau, uint32_t* __restrict__ cmax,
-    uint32_t* __restrict__ ticket, uint8_t* __restrict__ mask, int32_t* __restrict__ idx,
-    int32_t* __restrict__ count, float* __restrict__ colmax_out) {
-    __shared__ float red[4][OC_COLS];
-    __shared__ int is_last;
-    __shared__ int wave_tot[4];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t c0 = (int64_t)blockIdx.x * OC_COLS + lane * 8;
-    const int64_t r0 = (int64_t)blockIdx.y * OC_ROWS;
-    float m[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) m[j] = 0.0f;
-    if (c0 < K) {
-        const int64_t rend = r0 + OC_ROWS < M ? r0 + OC_ROWS : M;
-#pragma unroll 4
-        for (int64_t r = r0 + wave; r < rend; r += 4) {
-            u32x4 v = *reinterpret_cast<const u32x4*>(X + r * K + c0);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                uint16_t h = (uint16_t)(v[j >> 1] >> (16 * (j & 1)));
-                m[j] = fmaxf(m[j], __builtin_fabsf(h2f(h)));
-            }
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) red[wave][lane * 8 + j] = m[j];
-    __syncthreads();
-    for (int cc = threadIdx.x; cc < OC_COLS; cc += 256) {
-        float v = fmaxf(fmaxf(red[0][cc], red[1][cc]), fmaxf(red[2][cc], red[3][cc]));
-        int64_t col = (int64_t)blockIdx.x * OC_COLS + cc;
-        if (col < K) atomicMax(&cmax[col], __builtin_bit_cast(uint32_t, v));
-    }
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        unsigned total = gridDim.x * gridDim.y;
-        is_last = (atomicAdd(ticket, 1u) == total - 1u);
-    }
-    __syncthreads();
-    if (!is_last) return;
-    __threadfence();
-    int running = 0;
-    for (int64_t base = 0; base < K; base += 256) {
-        const int64_t col = base + threadIdx.x;
-        bool o = false;
-        if (col < K) {
-            uint32_t b = __hip_atomic_load(&cmax[col], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            float cm = __builtin_bit_cast(float, b);
-            o = cm > tau;
-            mask[col] = o ? 1 : 0;
-            if (colmax_out) colmax_out[col] = cm;
-        }
-        const uint64_t bal = __ballot(o);
-        const int pre = __popcll(bal & ((1ull << lane) - 1ull));
-        if (lane == 0) wave_tot[wave] = __popcll(bal);
-        __syncthreads();
-        int off = running;
-        for (int w = 0; w < wave; ++w) off += wave_tot[w];
-        if (o) idx[off + pre] = (int32_t)col;
-        running += wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) *count = running;
+// Two 16-bit unsigned maxima in one instruction (v_pk_max_u16).
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t,
+                              __builtin_elementwise_max(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
 }
 
-size_t outlier_scratch_bytes(int64_t K) { return (size_t)(K + 64) * 4; }
+// ---------------------------------------------------------------------------
+// Outlier columns.  A block owns a strip of 64 columns (one 128-byte line per
+// row: 8 lanes x 16 bytes) and a segment of rows; a wave instruction reads 8
+// full lines.  The column max runs on the sign-cleared fp16 bit patterns
+// (magnitudes of fp16 values order like their bits) with packed 16-bit max,
+// folded across lanes and waves.  Column j is an outlier when its max exceeds
+// the threshold; the block ORs the strip's 64 outlier bits into one 64-bit
+// flag word (only when some bit is set, so most blocks issue no atomic at
+// all -- atomics on one address serialize at the memory side).  The running
+// column max itself is only merged (atomic max) when the caller asks for it.
+// ---------------------------------------------------------------------------
+constexpr int OC_STRIP = 64;
+constexpr int OC_UNR = 8;                       // loads in flight per lane
+constexpr int OC_PASS = 256 * 64;               // columns compacted per pass
+
+template <bool WANT_MAX>
+__global__ __launch_bounds__(256) void k_outlier_scan(const uint16_t* __restrict__ X, int64_t M, int64_t K,
+                                                      int64_t seg_rows, float tau,
+                                                      unsigned long long* __restrict__ flags,
+                                                      uint32_t* __restrict__ cmax) {
+    __shared__ uint32_t red[4][32];
+    const int t = threadIdx.x, lane = t & 63, wave = wave_id();
+    const int64_t c0 = (int64_t)blockIdx.x * OC_STRIP;
+    const int64_t r0 = (int64_t)blockIdx.y * seg_rows;
+    const int64_t r1 = r0 + seg_rows < M ? r0 + seg_rows : M;
+    const int64_t nrows = r1 > r0 ? r1 - r0 : 0;
+    // range: from (r0, c0) to the end of row r1 - 1; rows past the segment read zeros
+    const rsrc_t rs = make_rsrc(X + r0 * K + c0, (nrows * K - c0) * 2);
+    const int chunk = lane & 7, rsub = lane >> 3;
+    const uint32_t coff = (c0 + chunk * 8 + 8 <= K) ? (uint32_t)chunk * 16 : kOOB;
+    uint32_t m[4] = {0u, 0u, 0u, 0u};
+    for (int64_t rb = 0; rb < nrows; rb += 32 * OC_UNR) {
+        u32x4 v[OC_UNR];
+#pragma unroll
+        for (int u = 0; u < OC_UNR; ++u) {
+            const uint32_t r = (uint32_t)(rb + u * 32 + wave * 8 + rsub);
+            v[u] = bload16(rs, coff == kOOB ? kOOB : r * (uint32_t)K * 2 + coff);
+        }
+#pragma unroll
+        for (int u = 0; u < OC_UNR; ++u)
+#pragma unroll
+            for (int d = 0; d < 4; ++d) m[d] = pk_max_u16(m[d], v[u][d] & 0x7fff7fffu);
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int o = 8; o < 64; o <<= 1) m[d] = pk_max_u16(m[d], (uint32_t)__shfl_xor((int)m[d], o, QA_WAVE));
+    if (rsub == 0) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) red[wave][chunk * 4 + d] = m[d];
+    }
+    __syncthreads();
+    if (wave == 0) {
+        // lane j: column c0 + j
+        const int w = lane >> 1;
+        const uint32_t a = pk_max_u16(pk_max_u16(red[0][w], red[1][w]), pk_max_u16(red[2][w], red[3][w]));
+        const float cm = h2f((uint16_t)((lane & 1) ? (a >> 16) : (a & 0xffffu)));
+        const int64_t col = c0 + lane;
+        const unsigned long long bits = __ballot(col < K && cm > tau);
+        if (lane == 0 && bits) atomicOr(&flags[blockIdx.x], bits);
+        if (WANT_MAX && col < K) atomicMax(&cmax[col], __builtin_bit_cast(uint32_t, cm));
+    }
+}
+
+// Ascending outlier list from the flag words: thread t owns columns
+// [t C, t C + C) of each pass of up to 16384 columns, so one block-wide scan of
+// the per-thread counts places every outlier.  Optionally writes the byte
+// mask and the column max.  Run by one block of 256 threads.
+__device__ void outlier_compact(const unsigned long long* __restrict__ flags, const uint32_t* __restrict__ cmax,
+                                int64_t K, uint8_t* __restrict__ mask, int32_t* __restrict__ idx,
+                                int32_t* __restrict__ count, float* __restrict__ colmax_out, int* wsum) {
+    const int t = threadIdx.x, lane = t & 63, wave = wave_id();
+    const int64_t nw = (K + 63) / 64;
+    const rsrc_t rf = make_rsrc(flags, nw * 8);
+    int running = 0;
+    for (int64_t pb = 0; pb < K; pb += OC_PASS) {
+        const int64_t pk = K - pb < OC_PASS ? K - pb : OC_PASS;
+        const int C = (int)((pk + 255) / 256);                // <= 64 columns per thread
+        const int64_t cb = pb + (int64_t)t * C;
+        // the (at most two) flag words covering [cb, cb + C)
+        const int64_t w0 = cb >> 6;
+        const u32x2 a0 = bload8(rf, (uint32_t)w0 * 8), a1 = bload8(rf, (uint32_t)(w0 + 1) * 8);
+        const unsigned long long f0 = a0[0] | ((unsigned long long)a0[1] << 32);
+        const unsigned long long f1 = a1[0] | ((unsigned long long)a1[1] << 32);
+        const int sh = (int)(cb & 63);
+        unsigned long long fl = sh ? ((f0 >> sh) | (f1 << (64 - sh))) : f0;
+        int64_t lim = pb + pk - cb;                            // valid columns of this thread
+        lim = lim < 0 ? 0 : (lim > C ? C : lim);
+        fl = lim >= 64 ? fl : (fl & ((1ull << lim) - 1ull));
+        if (mask || colmax_out) {
+            for (int i = 0; i < (int)lim; ++i) {
+                const int64_t col = cb + i;
+                if (mask) mask[col] = (uint8_t)((fl >> i) & 1ull);
+                if (colmax_out) colmax_out[col] = __builtin_bit_cast(float, cmax[col]);
+            }
+        }
+        const int cnt = __popcll(fl);
+        int x = cnt;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(x, d, QA_WAVE);
+            if (lane >= d) x += y;
+        }
+        if (lane == 63) wsum[wave] = x;
+        __syncthreads();
+        int off = running + x - cnt;
+        for (int w = 0; w < wave; ++w) off += wsum[w];
+        while (fl) {
+            const int i = __builtin_ctzll(fl);
+            fl &= fl - 1ull;
+            idx[off++] = (int32_t)(cb + i);
+        }
+        running += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+        __syncthreads();
+    }
+    if (t == 0) *count = running;
+}
+
+__global__ __launch_bounds__(256) void k_outlier_finalize(const unsigned long long* __restrict__ flags,
+                                                          const uint32_t* __restrict__ cmax, int64_t K,
+                                                          uint8_t* __restrict__ mask, int32_t* __restrict__ idx,
+                                                          int32_t* __restrict__ count, float* __restrict__ colmax_out) {
+    __shared__ int wsum[4];
+    outlier_compact(flags, cmax, K, mask, idx, count, colmax_out, wsum);
+}
+
+size_t outlier_scratch_bytes(int64_t K) { return (size_t)((K + 63) / 64) * 8 + (size_t)K * 4 + 64; }
+
+// flags [ceil(K/64)] u64 first, then the column max [K] u32
+static void outlier_scan(const uint16_t* X, int64_t M, int64_t K, float tau, void* scratch, bool want_max,
+                         hipStream_t st) {
+    unsigned long long* flags = static_cast<unsigned long long*>(scratch);
+    const int64_t nw = (K + 63) / 64;
+    uint32_t* cmax = reinterpret_cast<uint32_t*>(flags + nw);
+    const int64_t nz = 2 * nw + (want_max ? K : 0);
+    hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((nz + 255) / 256 < 1024 ? (nz + 255) / 256 : 1024)),
+                       dim3(256), 0, st, reinterpret_cast<uint32_t*>(flags), nz);
+    // row segments: about 512 blocks, at least 256 rows per segment, and a
+    // segment's byte span below 2^30 (32-bit buffer offsets)
+    const int64_t strips = nw;
+    int64_t segs = (512 + strips - 1) / strips;
+    const int64_t max_segs = M > 0 ? (M + 255) / 256 : 1;
+    if (segs > max_segs) segs = max_segs;
+    if (segs < 1) segs = 1;
+    int64_t seg_rows = M > 0 ? (M + segs - 1) / segs : 1;
+    const int64_t span_rows = ((int64_t)1 << 30) / (2 * K);
+    if (seg_rows > span_rows) seg_rows = span_rows;
+    seg_rows = (seg_rows + 31) / 32 * 32;
+    if (seg_rows > span_rows) seg_rows -= 32;
+    segs = M > 0 ? (M + seg_rows - 1) / seg_rows : 1;
+    dim3 grid((unsigned)strips, (unsigned)segs);
+    if (want_max)
+        hipLaunchKernelGGL(k_outlier_scan<true>, grid, dim3(256), 0, st, X, M, K, seg_rows, tau, flags, cmax);
+    else
+        hipLaunchKernelGGL(k_outlier_scan<false>, grid, dim3(256), 0, st, X, M, K, seg_rows, tau, flags, cmax);
+}
 
 hipError_t launch_outlier_cols(const uint16_t* X, int64_t M, int64_t K, float tau, uint8_t* mask,
-                               int32_t* idx, int32_t* count, float* colmax, void* scratch,
-                               hipStream_t st) {
-    uint32_t* cmax = static_cast<uint32_t*>(scratch);
-    uint32_t* ticket = cmax + K;
-    const int64_t nz = K + 1;
-    hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((nz + 255) / 256 < 1024 ? (nz + 255) / 256 : 1024)),
-                       dim3(256), 0, st, cmax, nz);
-    dim3 grid((unsigned)((K + OC_COLS - 1) / OC_COLS), (unsigned)(M > 0 ? (M + OC_ROWS - 1) / OC_ROWS : 1));
-    hipLaunchKernelGGL(k_outlier_cols, grid, dim3(256), 0, st, X, M, K, tau, cmax, ticket, mask, idx,
-                       count, colmax);
+                               int32_t* idx, int32_t* count, float* colmax, void* scratch, hipStream_t st) {
+    outlier_scan(X, M, K, tau, scratch, colmax != nullptr, st);
+    unsigned long long* flags = static_cast<unsigned long long*>(scratch);
+    const uint32_t* cmax = reinterpret_cast<const uint32_t*>(flags + (K + 63) / 64);
+    hipLaunchKernelGGL(k_outlier_finalize, dim3(1), dim3(256), 0, st, flags, cmax, K, mask, idx, count, colmax);
+    return hipGetLastError();
+}
+
+hipError_t launch_outlier_flags(const uint16_t* X, int64_t M, int64_t K, float tau, void* scratch, hipStream_t st) {
+    outlier_scan(X, M, K, tau, scratch, false, st);
     return hipGetLastError();
 }
 
@@ -121,79 +210,118 @@ hipError_t launch_outlier_cols(const uint16_t* X, int64_t M, int64_t K, float ta
 // Row-wise int8 quantization: one wave per row, 8 elements (16 bytes) per
 // lane and chunk.  NC > 0 keeps the row in registers (K <= 512 * NC); NC == 0
 // reads the row twice (absmax pass, then quantize pass).
+//
+// Masks: MASK_BYTES -- caller's byte per column (nonzero = masked), applied per
+// value; MASK_FLAGS -- outlier flag bits (one byte per 8-column chunk, the flag
+// words of the outlier scan), turned into 16-bit keep words through a
+// 256-entry table in LDS and ANDed into the fp16 bits.  In MASK_FLAGS mode
+// block 0 also writes the ascending outlier list and its count.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void unpack8(const u32x4& v, float* x) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = h2f((uint16_t)(v[j >> 1] >> (16 * (j & 1))));
-}
+enum { MASK_NONE = 0, MASK_BYTES = 1, MASK_FLAGS = 2 };
 
-template <bool STATIC>
-__device__ __forceinline__ uint64_t quant8(const float* x, uint64_t mk, float s, float r, int z, int qmin,
-                                           int qmax) {
-    uint64_t out = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        int code;
-        if ((mk >> (8 * j)) & 0xffu) {
-            code = clampi(z, qmin, qmax);
-        } else if (STATIC) {
-            double t = (double)__builtin_rintf(x[j] / s) + (double)z;
-            t = t < (double)qmin ? (double)qmin : (t > (double)qmax ? (double)qmax : t);
-            code = (int)t;
-        } else {
-            code = clampi((int)quot_rne(x[j], s, r), qmin, qmax);
-        }
-        out |= (uint64_t)(uint8_t)(int8_t)code << (8 * j);
-    }
-    return out;
-}
-
-__device__ __forceinline__ float absmax8(const float* x, uint64_t mk) {
-    float a = 0.0f;
+// masked elements -> 0 (before the absmax and the quantizer)
+__device__ __forceinline__ void apply_mask(float* x, u32x2 mk) {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-        if (!((mk >> (8 * j)) & 0xffu)) a = fmaxf(a, __builtin_fabsf(x[j]));
+        if ((mk[j >> 2] >> (8 * (j & 3))) & 0xffu) x[j] = 0.0f;
+}
+
+__device__ __forceinline__ float absmax8(const float* x) {
+    float a = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a = fmaxf(a, __builtin_fabsf(x[j]));
     return a;
 }
 
-template <int NC, bool STATIC>
-__global__ __launch_bounds__(256) void k_rowquant_i8(const uint16_t* __restrict__ X, int64_t rows,
-                                                     int64_t K, const uint8_t* __restrict__ mask,
-                                                     int qmin, int qmax, const float* __restrict__ s_in,
-                                                     const int32_t* __restrict__ z_in,
-                                                     int8_t* __restrict__ q, float* __restrict__ s_out) {
+// static (affine) codes: clip(rint(x / s) + z, qmin, qmax); masked -> clip(z)
+__device__ __forceinline__ u32x2 codes8_static(const float* x, u32x2 mk, float s, int z, int qmin, int qmax) {
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        int code;
+        if ((mk[j >> 2] >> (8 * (j & 3))) & 0xffu) {
+            code = clampi(z, qmin, qmax);
+        } else {
+            double t = (double)__builtin_rintf(x[j] / s) + (double)z;
+            t = t < (double)qmin ? (double)qmin : (t > (double)qmax ? (double)qmax : t);
+            code = (int)t;
+        }
+        w[j >> 2] |= ((uint32_t)code & 0xffu) << (8 * (j & 3));
+    }
+    return u32x2{w[0], w[1]};
+}
+
+// dynamic codes with the clip of a narrower [qmin, qmax] than [-qmax, qmax]
+__device__ __forceinline__ u32x2 clip_codes(u32x2 c, int qmin) {
+    if (qmin <= -127) return c;
+    uint32_t w[2] = {c[0], c[1]};
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+        uint32_t o = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            int q = (int8_t)(w[d] >> (8 * j));
+            q = q < qmin ? qmin : q;
+            o |= ((uint32_t)q & 0xffu) << (8 * j);
+        }
+        w[d] = o;
+    }
+    return u32x2{w[0], w[1]};
+}
+
+template <int NC, bool STATIC, int MASK>
+__global__ __launch_bounds__(256) void k_rowquant_i8(const uint16_t* __restrict__ X, int64_t rows, int64_t K,
+                                                     const uint8_t* __restrict__ mask, int qmin, int qmax,
+                                                     const float* __restrict__ s_in, const int32_t* __restrict__ z_in,
+                                                     int8_t* __restrict__ q, float* __restrict__ s_out,
+                                                     int32_t* __restrict__ idx, int32_t* __restrict__ count) {
+    __shared__ u32x4 lut[MASK == MASK_FLAGS ? 256 : 1];
+    __shared__ int wsum[4];
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if constexpr (MASK == MASK_FLAGS) {
+        const uint32_t b = threadIdx.x;              // keep words of an 8-bit outlier pattern
+        u32x4 k;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+            k[d] = (((b >> (2 * d)) & 1u) ? 0u : 0xffffu) | (((b >> (2 * d + 1)) & 1u) ? 0u : 0xffff0000u);
+        lut[b] = k;
+        if (blockIdx.x == 0)
+            outlier_compact(reinterpret_cast<const unsigned long long*>(mask), nullptr, K, nullptr, idx, count,
+                            nullptr, wsum);
+        __syncthreads();
+    }
+    const int64_t row = (int64_t)blockIdx.x * 4 + wave_id();
     if (row >= rows) return;
     const int64_t nch = K >> 3;
-    const uint16_t* xr = X + row * K;
+    const rsrc_t rx = make_rsrc(X + row * K, K * 2);
+    const rsrc_t rm = make_rsrc(mask, MASK == MASK_NONE ? 0 : (MASK == MASK_BYTES ? K : nch));
     int8_t* qr = q + row * K;
-    float s, r = 1.0f;
+    float s = 1.0f, r = 1.0f;
     int z = 0;
+    if constexpr (STATIC) {
+        s = s_in[row];
+        z = z_in ? z_in[row] : 0;
+    }
+    // chunk ch: fp16 bits with MASK_FLAGS already applied, byte mask for MASK_BYTES
+    auto load = [&](int64_t ch, u32x4& v, u32x2& mk) {
+        v = bload16(rx, (uint32_t)ch * 16);
+        mk = u32x2{0u, 0u};
+        if constexpr (MASK == MASK_FLAGS) v &= lut[bload1(rm, (uint32_t)ch)];
+        if constexpr (MASK == MASK_BYTES) mk = bload8(rm, (uint32_t)ch * 8);
+    };
     if constexpr (NC > 0) {
         u32x4 v[NC];
-        uint64_t mk[NC];
-        float amax = 0.0f;
+        u32x2 mk[NC];
 #pragma unroll
-        for (int i = 0; i < NC; ++i) {
-            const int64_t ch = lane + 64 * i;
-            if (ch < nch) {
-                v[i] = *reinterpret_cast<const u32x4*>(xr + ch * 8);
-                mk[i] = mask ? *reinterpret_cast<const uint64_t*>(mask + ch * 8) : 0ull;
-            } else {
-                v[i] = u32x4{0u, 0u, 0u, 0u};
-                mk[i] = 0ull;
-            }
-        }
-        if constexpr (STATIC) {
-            s = s_in[row];
-            z = z_in ? z_in[row] : 0;
-        } else {
+        for (int i = 0; i < NC; ++i) load(lane + 64 * i, v[i], mk[i]);
+        if constexpr (!STATIC) {
+            float amax = 0.0f;
 #pragma unroll
             for (int i = 0; i < NC; ++i) {
                 float x[8];
                 unpack8(v[i], x);
-                amax = fmaxf(amax, absmax8(x, mk[i]));
+                if constexpr (MASK == MASK_BYTES) apply_mask(x, mk[i]);
+                amax = fmaxf(amax, absmax8(x));
             }
             amax = wave_max(amax);
             s = amax == 0.0f ? 1.0f : amax / (float)qmax;
@@ -206,20 +334,27 @@ __global__ __launch_bounds__(256) void k_rowquant_i8(const uint16_t* __restrict_
             if (ch < nch) {
                 float x[8];
                 unpack8(v[i], x);
-                *reinterpret_cast<uint64_t*>(qr + ch * 8) = quant8<STATIC>(x, mk[i], s, r, z, qmin, qmax);
+                u32x2 c;
+                if constexpr (STATIC) {
+                    c = codes8_static(x, mk[i], s, z, qmin, qmax);
+                } else {
+                    if constexpr (MASK == MASK_BYTES) apply_mask(x, mk[i]);
+                    c = clip_codes(codes8_dyn(x, s, r), qmin);
+                }
+                *reinterpret_cast<u32x2*>(qr + ch * 8) = c;
             }
         }
     } else {
-        if constexpr (STATIC) {
-            s = s_in[row];
-            z = z_in ? z_in[row] : 0;
-        } else {
+        if constexpr (!STATIC) {
             float amax = 0.0f;
             for (int64_t ch = lane; ch < nch; ch += 64) {
+                u32x4 v;
+                u32x2 mk;
+                load(ch, v, mk);
                 float x[8];
-                unpack8(*reinterpret_cast<const u32x4*>(xr + ch * 8), x);
-                uint64_t mk = mask ? *reinterpret_cast<const uint64_t*>(mask + ch * 8) : 0ull;
-                amax = fmaxf(amax, absmax8(x, mk));
+                unpack8(v, x);
+                if constexpr (MASK == MASK_BYTES) apply_mask(x, mk);
+                amax = fmaxf(amax, absmax8(x));
             }
             amax = wave_max(amax);
             s = amax == 0.0f ? 1.0f : amax / (float)qmax;
@@ -227,22 +362,31 @@ __global__ __launch_bounds__(256) void k_rowquant_i8(const uint16_t* __restrict_
             if (lane == 0) s_out[row] = s;
         }
         for (int64_t ch = lane; ch < nch; ch += 64) {
+            u32x4 v;
+            u32x2 mk;
+            load(ch, v, mk);
             float x[8];
-            unpack8(*reinterpret_cast<const u32x4*>(xr + ch * 8), x);
-            uint64_t mk = mask ? *reinterpret_cast<const uint64_t*>(mask + ch * 8) : 0ull;
-            *reinterpret_cast<uint64_t*>(qr + ch * 8) = quant8<STATIC>(x, mk, s, r, z, qmin, qmax);
+            unpack8(v, x);
+            u32x2 c;
+            if constexpr (STATIC) {
+                c = codes8_static(x, mk, s, z, qmin, qmax);
+            } else {
+                if constexpr (MASK == MASK_BYTES) apply_mask(x, mk);
+                c = clip_codes(codes8_dyn(x, s, r), qmin);
+            }
+            *reinterpret_cast<u32x2*>(qr + ch * 8) = c;
         }
     }
 }
 
-template <bool STATIC>
-static void rowquant_dispatch(const uint16_t* X, int64_t rows, int64_t K, const uint8_t* mask, int qmin,
-                              int qmax, const float* s_in, const int32_t* z_in, int8_t* q, float* s_out,
-                              hipStream_t st) {
+template <bool STATIC, int MASK>
+static void rowquant_dispatch(const uint16_t* X, int64_t rows, int64_t K, const uint8_t* mask, int qmin, int qmax,
+                              const float* s_in, const int32_t* z_in, int8_t* q, float* s_out, int32_t* idx,
+                              int32_t* count, hipStream_t st) {
     const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
     const int64_t nch = K / 8;
-#define QA_RQ(NC) hipLaunchKernelGGL((k_rowquant_i8<NC, STATIC>), grid, block, 0, st, X, rows, K, mask, qmin, \
-                                     qmax, s_in, z_in, q, s_out)
+#define QA_RQ(NC) hipLaunchKernelGGL((k_rowquant_i8<NC, STATIC, MASK>), grid, block, 0, st, X, rows, K, mask, qmin, \
+                                     qmax, s_in, z_in, q, s_out, idx, count)
     if (nch <= 64) QA_RQ(1);
     else if (nch <= 128) QA_RQ(2);
     else if (nch <= 256) QA_RQ(4);
@@ -252,13 +396,21 @@ static void rowquant_dispatch(const uint16_t* X, int64_t rows, int64_t K, const 
 #undef QA_RQ
 }
 
-hipError_t launch_rowquant_i8(const uint16_t* X, int64_t rows, int64_t K, const uint8_t* mask, int qmin,
-                              int qmax, const float* s_in, const int32_t* z_in, int8_t* q, float* s_out,
-                              hipStream_t st) {
+hipError_t launch_rowquant_i8(const uint16_t* X, int64_t rows, int64_t K, const uint8_t* mask, int qmin, int qmax,
+                              const float* s_in, const int32_t* z_in, int8_t* q, float* s_out, hipStream_t st) {
     if (s_in)
-        rowquant_dispatch<true>(X, rows, K, mask, qmin, qmax, s_in, z_in, q, s_out, st);
+        rowquant_dispatch<true, MASK_BYTES>(X, rows, K, mask, qmin, qmax, s_in, z_in, q, s_out, nullptr, nullptr, st);
+    else if (mask)
+        rowquant_dispatch<false, MASK_BYTES>(X, rows, K, mask, qmin, qmax, s_in, z_in, q, s_out, nullptr, nullptr, st);
     else
-        rowquant_dispatch<false>(X, rows, K, mask, qmin, qmax, s_in, z_in, q, s_out, st);
+        rowquant_dispatch<false, MASK_NONE>(X, rows, K, mask, qmin, qmax, s_in, z_in, q, s_out, nullptr, nullptr, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_rowquant_i8_flags(const uint16_t* X, int64_t rows, int64_t K, const void* scratch, int8_t* q,
+                                    float* s_out, int32_t* idx, int32_t* count, hipStream_t st) {
+    rowquant_dispatch<false, MASK_FLAGS>(X, rows, K, static_cast<const uint8_t*>(scratch), -127, 127, nullptr,
+                                         nullptr, q, s_out, idx, count, st);
     return hipGetLastError();
 }
 
@@ -300,14 +452,18 @@ __device__ __forceinline__ void fwht_chunk(const u32x4& v, double c, int lane, f
     for (int j = 0; j < 8; ++j) xo[j] = (float)(y[j] * c);
 }
 
-__device__ __forceinline__ uint32_t pack_codes(const float* x, float s, float r, int qmin, int qmax) {
-    uint32_t w = 0;
+// int4 codes of 8 values (|x / s| <= 7 (1 + 2^-23)) packed into one word,
+// element j in bits [4j+3:4j]; clipped to [qmin, qmax].
+__device__ __forceinline__ uint32_t pack_codes(const float* x, float s, float r, int qmin) {
+    const u32x2 c = clip_codes(codes8_dyn(x, s, r), qmin);
+    uint32_t w[2];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        int code = clampi((int)quot_rne(x[j], s, r), qmin, qmax);
-        w |= ((uint32_t)code & 0xFu) << (4 * j);
+    for (int d = 0; d < 2; ++d) {
+        uint32_t a = c[d] & 0x0f0f0f0fu;          // nibbles of 4 codes in bytes
+        a = (a | (a >> 4)) & 0x00ff00ffu;        // codes 0,1 in byte 0; 2,3 in byte 2
+        w[d] = (a | (a >> 8)) & 0xffffu;
     }
-    return w;
+    return w[0] | (w[1] << 16);
 }
 
 __device__ __forceinline__ float absmax8f(const float* x) {
@@ -323,19 +479,20 @@ __global__ __launch_bounds__(256) void k_hq4_row(const uint16_t* __restrict__ X,
                                                  int qmin, int qmax, double c, uint32_t* __restrict__ packed,
                                                  float* __restrict__ s_out) {
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t row = (int64_t)blockIdx.x * 4 + wave_id();
     if (row >= rows) return;
     const int64_t nch = K >> 3;
-    const uint16_t* xr = X + row * K;
+    const rsrc_t rx = make_rsrc(X + row * K, K * 2);
     uint32_t* pr = packed + row * nch;
     if constexpr (NC > 0) {
+        u32x4 v[NC];
+#pragma unroll
+        for (int i = 0; i < NC; ++i) v[i] = bload16(rx, (uint32_t)(lane + 64 * i) * 16);
         float xs[NC][8];
         float amax = 0.0f;
 #pragma unroll
         for (int i = 0; i < NC; ++i) {
-            const int64_t ch = lane + 64 * i;
-            u32x4 v = ch < nch ? *reinterpret_cast<const u32x4*>(xr + ch * 8) : u32x4{0u, 0u, 0u, 0u};
-            fwht_chunk<G>(v, c, lane, xs[i]);
+            fwht_chunk<G>(v[i], c, lane, xs[i]);
             amax = fmaxf(amax, absmax8f(xs[i]));
         }
         amax = wave_max(amax);
@@ -345,15 +502,14 @@ __global__ __launch_bounds__(256) void k_hq4_row(const uint16_t* __restrict__ X,
 #pragma unroll
         for (int i = 0; i < NC; ++i) {
             const int64_t ch = lane + 64 * i;
-            if (ch < nch) pr[ch] = pack_codes(xs[i], s, r, qmin, qmax);
+            if (ch < nch) pr[ch] = pack_codes(xs[i], s, r, qmin);
         }
     } else {
         float amax = 0.0f;
         for (int64_t base = 0; base < nch; base += 64) {
             const int64_t ch = base + lane;
-            u32x4 v = ch < nch ? *reinterpret_cast<const u32x4*>(xr + ch * 8) : u32x4{0u, 0u, 0u, 0u};
             float xo[8];
-            fwht_chunk<G>(v, c, lane, xo);
+            fwht_chunk<G>(bload16(rx, (uint32_t)ch * 16), c, lane, xo);
             amax = fmaxf(amax, absmax8f(xo));
         }
         amax = wave_max(amax);
@@ -362,10 +518,9 @@ __global__ __launch_bounds__(256) void k_hq4_row(const uint16_t* __restrict__ X,
         if (lane == 0) s_out[row] = s;
         for (int64_t base = 0; base < nch; base += 64) {
             const int64_t ch = base + lane;
-            u32x4 v = ch < nch ? *reinterpret_cast<const u32x4*>(xr + ch * 8) : u32x4{0u, 0u, 0u, 0u};
             float xo[8];
-            fwht_chunk<G>(v, c, lane, xo);
-            if (ch < nch) pr[ch] = pack_codes(xo, s, r, qmin, qmax);
+            fwht_chunk<G>(bload16(rx, (uint32_t)ch * 16), c, lane, xo);
+            if (ch < nch) pr[ch] = pack_codes(xo, s, r, qmin);
         }
     }
 }
@@ -376,22 +531,21 @@ __global__ __launch_bounds__(256) void k_hq4_group(const uint16_t* __restrict__ 
                                                    int qmin, int qmax, double c, uint32_t* __restrict__ packed,
                                                    float* __restrict__ s_out) {
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t row = (int64_t)blockIdx.x * 4 + wave_id();
     if (row >= rows) return;
     const int64_t nch = K >> 3;
     const int64_t ngr = K / G;
-    const uint16_t* xr = X + row * K;
+    const rsrc_t rx = make_rsrc(X + row * K, K * 2);
     uint32_t* pr = packed + row * nch;
     for (int64_t base = 0; base < nch; base += 64) {
         const int64_t ch = base + lane;
-        u32x4 v = ch < nch ? *reinterpret_cast<const u32x4*>(xr + ch * 8) : u32x4{0u, 0u, 0u, 0u};
         float xo[8];
-        fwht_chunk<G>(v, c, lane, xo);
+        fwht_chunk<G>(bload16(rx, (uint32_t)ch * 16), c, lane, xo);
         float amax = group_max(absmax8f(xo), G / 8);
         const float s = amax == 0.0f ? 1.0f : amax / (float)qmax;
         const float r = 1.0f / s;
         if (ch < nch) {
-            pr[ch] = pack_codes(xo, s, r, qmin, qmax);
+            pr[ch] = pack_codes(xo, s, r, qmin);
             if ((lane & (G / 8 - 1)) == 0) s_out[row * ngr + (ch * 8) / G] = s;
         }
     }

@@ -46,14 +46,13 @@ constexpr int64_t kMaxK_i8 = 131072;
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 struct MixedLayout {
-    size_t cmax, mask, idx, count, s_x, xq, total;
+    size_t cmax, idx, count, s_x, xq, total;
 };
 
 MixedLayout mixed_layout(int64_t M, int64_t K) {
     MixedLayout L;
     size_t off = 0;
     L.cmax = off; off += up(qa::outlier_scratch_bytes(K));
-    L.mask = off; off += up((size_t)K);
     L.idx = off; off += up((size_t)K * 4);
     L.count = off; off += up(4);
     L.s_x = off; off += up((size_t)M * 4);
@@ -103,8 +102,8 @@ size_t qa_outlier_cols_workspace(int64_t K) { return K > 0 ? up(qa::outlier_scra
 qa_status qa_outlier_cols(const void* X_f16, int64_t M, int64_t K, float threshold, uint8_t* mask, int32_t* idx,
                           int32_t* count, float* colmax_or_null, void* scratch, size_t scratch_bytes,
                           void* stream) {
-    if (M < 0 || K <= 0 || K % 8 != 0)
-        return fail(QA_ERR_SHAPE, "qa_outlier_cols: need M >= 0, K > 0, K %% 8 == 0 (M=%lld K=%lld)",
+    if (M < 0 || K <= 0 || K % 8 != 0 || K > ((int64_t)1 << 22))
+        return fail(QA_ERR_SHAPE, "qa_outlier_cols: need M >= 0, 0 < K <= 2^22, K %% 8 == 0 (M=%lld K=%lld)",
                     (long long)M, (long long)K);
     if ((M > 0 && !X_f16) || !mask || !idx || !count || !scratch)
         return fail(QA_ERR_NULL, "qa_outlier_cols: NULL pointer");
@@ -167,18 +166,22 @@ qa_status qa_qlinear_int8_mixed(const void* X_f16, int64_t M, int64_t K, const i
     if (workspace_bytes < L.total)
         return fail(QA_ERR_WORKSPACE, "qa_qlinear_int8_mixed: workspace %zu < %zu bytes", workspace_bytes, L.total);
 
+    const uint16_t* X = static_cast<const uint16_t*>(X_f16);
+    hipStream_t st = as_stream(stream);
+    if (qa::decode_supported(M, K))
+        return device_status(qa::launch_decode_mixed(X, M, K, Wq, s_w, static_cast<const uint16_t*>(W_f16_or_null),
+                                                     N, threshold, out, (int)out_dtype, st),
+                             "qa_qlinear_int8_mixed (decode kernel)");
+
     uint8_t* ws = static_cast<uint8_t*>(workspace);
-    uint8_t* mask = ws + L.mask;
     int32_t* idx = reinterpret_cast<int32_t*>(ws + L.idx);
     int32_t* count = reinterpret_cast<int32_t*>(ws + L.count);
     float* s_x = reinterpret_cast<float*>(ws + L.s_x);
     int8_t* xq = reinterpret_cast<int8_t*>(ws + L.xq);
-    const uint16_t* X = static_cast<const uint16_t*>(X_f16);
-    hipStream_t st = as_stream(stream);
 
-    hipError_t e = qa::launch_outlier_cols(X, M, K, threshold, mask, idx, count, nullptr, ws + L.cmax, st);
+    hipError_t e = qa::launch_outlier_flags(X, M, K, threshold, ws + L.cmax, st);
     if (e != hipSuccess) return device_status(e, "qa_qlinear_int8_mixed (outlier columns)");
-    e = qa::launch_rowquant_i8(X, M, K, mask, -127, 127, nullptr, nullptr, xq, s_x, st);
+    e = qa::launch_rowquant_i8_flags(X, M, K, ws + L.cmax, xq, s_x, idx, count, st);
     if (e != hipSuccess) return device_status(e, "qa_qlinear_int8_mixed (row quantization)");
     qa::MixedEpilogue ep;
     ep.s_x = s_x;

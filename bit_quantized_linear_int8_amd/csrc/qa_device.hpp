@@ -48,6 +48,78 @@ __device__ __forceinline__ float group_max(float v, int width) {
     return v;
 }
 
+// ---------------------------------------------------------------------------
+// Buffer loads.  A buffer resource descriptor carries a base address and a
+// byte range; raw buffer loads outside the range return zeros, so bounds are
+// checked by the hardware and loads never need a branch (a branch around a
+// load makes the compiler wait for it inside the branch).
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+constexpr uint32_t kOOB = 0x80000000u;        // an offset past every range used here
+
+// Descriptor for [base, base + bytes), bytes clamped to 2^31 - 1.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    const int n = bytes <= 0 ? 0 : (bytes >= 0x7fffffffLL ? 0x7fffffff : (int)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ u32x2 bload8(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t bload4(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ uint16_t bload2(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ uint8_t bload1(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
+
+// The 8 fp16 values of a 16-byte chunk, widened to fp32.
+__device__ __forceinline__ void unpack8(const u32x4& v, float* x) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = h2f((uint16_t)(v[j >> 1] >> (16 * (j & 1))));
+}
+
+// Wave index within the block as a wave-uniform (scalar) value, so values
+// derived from it (row pointers, buffer descriptors) stay in SGPRs.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// Dynamic-scale codes of 8 values with |x / s| <= q_max (1 + 2^-23), q_max <= 127.
+// Fast path: t = fl(x * r + 128) with r = fl32(1/s) (one fused multiply-add).
+// |x*r - x/s| <= 128 * 2^-24 and the rounding of t adds at most 2^-17, so
+// |t - (x/s + 128)| <= 2^-16, and fl(x/s) lies within 2^-18 of x/s: unless t
+// is within 2^-14 of a rounding boundary (n + 1/2), rint(t) - 128 equals
+// rint(fl(x/s)).  A chunk with any element that close takes the correctly
+// rounded division instead.  Codes are within [-q_max, q_max] by the bound,
+// so rint(t) is in [1, 255] and v_cvt_pk_u8_f32 packs it exactly; XOR 0x80
+// turns each byte into the two's-complement code.
+__device__ __forceinline__ u32x2 codes8_dyn(const float* x, float s, float r) {
+    float n[8];
+    float dmax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float t = __builtin_fmaf(x[j], r, 128.0f);
+        n[j] = __builtin_rintf(t);
+        dmax = fmaxf(dmax, __builtin_fabsf(t - n[j]));
+    }
+    if (dmax > 0.5f - 0x1p-14f) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) n[j] = __builtin_rintf(x[j] / s) + 128.0f;
+    }
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lo = __builtin_amdgcn_cvt_pk_u8_f32(n[j], j, lo);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hi = __builtin_amdgcn_cvt_pk_u8_f32(n[j + 4], j, hi);
+    return u32x2{lo ^ 0x80808080u, hi ^ 0x80808080u};
+}
+
 // Quantize one value whose quotient by the scale is bounded by q_max(1+2^-23)
 // (dynamic absmax scales): the quotient is formed with the reciprocal r and
 // the exact IEEE division is used only when that product lies within 2^-14

@@ -8,17 +8,26 @@
 
 namespace qa {
 
-// Workspace of the outlier-column reduction: a running column max [K] as
-// uint32 bits and a ticket counter, zero-filled by the launcher itself.
+// Scratch of the outlier-column scan: one 64-bit flag word per 64 columns and
+// the running column max [K]; zero-filled by the launchers themselves.
 size_t outlier_scratch_bytes(int64_t K);
 
+// Public outlier detection: scan + one-block finalize (mask, list, count, max).
 hipError_t launch_outlier_cols(const uint16_t* X, int64_t M, int64_t K, float tau, uint8_t* mask,
-                               int32_t* idx, int32_t* count, float* colmax, void* scratch,
-                               hipStream_t st);
+                               int32_t* idx, int32_t* count, float* colmax, void* scratch, hipStream_t st);
+
+// Outlier flag words only (for the mixed linear, which consumes them in the
+// row quantizer).
+hipError_t launch_outlier_flags(const uint16_t* X, int64_t M, int64_t K, float tau, void* scratch, hipStream_t st);
 
 hipError_t launch_rowquant_i8(const uint16_t* X, int64_t rows, int64_t K, const uint8_t* mask,
                               int qmin, int qmax, const float* s_in, const int32_t* z_in,
                               int8_t* q, float* s_out, hipStream_t st);
+
+// Dynamic [-127, 127] row quantization with the outlier flags of `scratch`
+// (launch_outlier_flags) as the mask; also writes the ascending outlier list.
+hipError_t launch_rowquant_i8_flags(const uint16_t* X, int64_t rows, int64_t K, const void* scratch, int8_t* q,
+                                    float* s_out, int32_t* idx, int32_t* count, hipStream_t st);
 
 hipError_t launch_hadamard_quant_i4(const uint16_t* X, int64_t rows, int64_t K, int G,
                                     bool per_group, int qmin, int qmax, uint32_t* packed, float* s,
@@ -43,6 +52,12 @@ hipError_t launch_gemm_i8_i32(const int8_t* A, const int8_t* B, int64_t M, int64
 
 hipError_t launch_gemm_i8_mixed(const int8_t* Xq, const int8_t* Wq, int64_t M, int64_t K, int64_t N,
                                 const MixedEpilogue& ep, hipStream_t st);
+
+// Fused single-kernel LLM.int8() linear for decode shapes (no workspace).
+bool decode_supported(int64_t M, int64_t K);
+hipError_t launch_decode_mixed(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* s_w,
+                               const uint16_t* W16, int64_t N, float tau, void* out, int out_dtype,
+                               hipStream_t st);
 
 hipError_t launch_gemm_w4a4(const uint32_t* Xp, const float* s_x, const uint32_t* Wp,
                             const float* s_w, int64_t M, int64_t K, int64_t N, int G, void* out,

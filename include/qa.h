@@ -89,8 +89,8 @@ const char* qa_last_error(void);
  *   count   i32 [1]: number of outlier columns
  *   colmax  f32 [K] or NULL
  *   scratch device buffer of qa_outlier_cols_workspace(K) bytes (any content)
- * Errors: NULL pointers, M < 0, K <= 0, K % 8 != 0, X not 16-byte aligned,
- * NaN threshold, small scratch.
+ * Errors: NULL pointers, M < 0, K <= 0, K > 2^22, K % 8 != 0, X not 16-byte
+ * aligned, NaN threshold, small scratch.
  * ------------------------------------------------------------------------- */
 size_t qa_outlier_cols_workspace(int64_t K);
 qa_status qa_outlier_cols(const void* X_f16, int64_t M, int64_t K, float threshold,

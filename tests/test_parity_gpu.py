@@ -208,6 +208,23 @@ def test_mixed_many_outliers(qa):
     _mixed_case(qa, X, W, 6.0, 0, True)
 
 
+@pytest.mark.parametrize("M,K,N", [(1, 256, 1), (3, 512, 17), (4, 768, 40), (7, 1024, 33), (8, 4096, 64),
+                                   (9, 2048, 48), (12, 256, 100), (16, 4096, 20)])
+@pytest.mark.parametrize("tau", [6.0, float("inf"), -1.0])
+@pytest.mark.parametrize("pass_w16", [True, False])
+def test_mixed_decode_kernel_shapes(qa, M, K, N, tau, pass_w16):
+    # M <= 16 with K % 256 == 0, K <= 4096 runs the fused single-kernel path
+    X, W, _ = synthetic.mixed_inputs(M, K, N, seed=M * 13 + K + N, n_dims=6, magnitude=("abs_normal", 20.0),
+                                     p_token=1.0)
+    _mixed_case(qa, X, W, tau, 1, pass_w16)
+
+
+def test_mixed_decode_kernel_many_outliers(qa):
+    X, W, _ = synthetic.mixed_inputs(8, 4096, 96, seed=21, n_dims=300, p_token=0.6)
+    for dt in (0, 1, 2):
+        _mixed_case(qa, X, W, 6.0, dt, False)
+
+
 def test_mixed_tiny_config(qa):
     c = synthetic.config("tiny_mixed")
     _mixed_case(qa, c["X"], c["W"], c["tau"], c["out_dtype"], c["pass_w16"])
