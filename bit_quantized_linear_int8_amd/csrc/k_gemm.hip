@@ -22,10 +22,23 @@
 // flight while stage k is multiplied (two LDS buffers, one barrier per stage).
 // The MFMA k-permutation only has to agree between the two operands, which
 // is what lets the int4 unpack skip the nibble interleave.
+#include <utility>
+
 #include "qa_device.hpp"
 #include "qa_launch.hpp"
 
 namespace qa {
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [0, N), so
+// register arrays are always indexed by constants.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 template <int BM_, int BN_, int WM_, int WN_>
 struct Cfg {
@@ -148,6 +161,138 @@ __device__ __forceinline__ void mainloop_i8(const int8_t* __restrict__ A, const 
     }
 }
 
+// ---------------------------------------------------------------------------
+// int8 main loop with direct global -> LDS loads (gfx950 buffer_load ... lds).
+// WM x WN waves, wave tile (BM/WM) x (BN/WN).  K advances 64 bytes per stage;
+// four LDS stages, three in flight.  A DMA instruction writes 64 lanes x 16
+// bytes = 1 KB of LDS at consecutive addresses, so the XOR swizzle of the
+// stage layout (chunk c of row r stored at chunk c ^ ((r >> 1) & 3), which
+// makes the 16-byte fragment reads of 8 consecutive rows hit 8 different bank
+// groups) is produced by choosing which global chunk each lane fetches.  The
+// waits are explicit: s_waitcnt vmcnt(n) for this wave's stage-kt loads, then
+// a bare s_barrier (a __syncthreads would also drain the younger stages).
+// With two waves per SIMD (8 waves) one wave's LDS reads and barrier wait
+// overlap the other's MFMAs, so the loop itself is not software-pipelined.
+// ---------------------------------------------------------------------------
+template <int BM_, int BN_, int WM_, int WN_>
+struct CfgD {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NW = WM * WN;
+    static constexpr int BK = 64, STAGES = 4, THREADS = 64 * NW;
+    static constexpr int TM = BM / WM, TN = BN / WN;
+    static constexpr int FM = TM / 16, FN = TN / 16;
+    static constexpr int A_INS = BM / (16 * NW), B_INS = BN / (16 * NW);   // 1 KB loads per wave per stage
+    static constexpr int LDS_A = BM * BK, LDS_B = BN * BK, STAGE = LDS_A + LDS_B;
+    static constexpr int LDS = STAGES * STAGE;
+    static_assert(A_INS * 16 * NW == BM && B_INS * 16 * NW == BN, "stage rows must split evenly over waves");
+};
+
+__device__ __forceinline__ int swz64(int r, int c) { return r * 64 + ((c ^ ((r >> 1) & 3)) << 4); }
+
+// s_waitcnt immediate waiting for vmcnt <= n only (gfx9 encoding)
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Workgroup barrier that also keeps the compiler from moving memory accesses
+// across it (the DMA writes and the fragment reads of the same LDS stage).
+__device__ __forceinline__ void block_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <class C>
+__device__ __forceinline__ void mainloop_i8_dma(rsrc_t rsa, rsrc_t rsb, uint32_t K, uint8_t* smem,
+                                                v4i (&acc)[C::FM][C::FN]) {
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    constexpr int PER_STAGE = C::A_INS + C::B_INS;
+    uint32_t oa[C::A_INS], ca[C::A_INS], ob[C::B_INS], cb[C::B_INS];
+#pragma unroll
+    for (int q = 0; q < C::A_INS; ++q) {
+        const int P = (wave * C::A_INS + q) * 64 + lane;      // physical 16-byte chunk of the stage
+        const int r = P >> 2, c = (P & 3) ^ ((r >> 1) & 3);
+        oa[q] = (uint32_t)r * K + c * 16;
+        ca[q] = c * 16;
+    }
+#pragma unroll
+    for (int q = 0; q < C::B_INS; ++q) {
+        const int P = (wave * C::B_INS + q) * 64 + lane;
+        const int r = P >> 2, c = (P & 3) ^ ((r >> 1) & 3);
+        ob[q] = (uint32_t)r * K + c * 16;
+        cb[q] = c * 16;
+    }
+    const int nk = (int)((K + C::BK - 1) / C::BK);
+    auto issue = [&](int kt) __attribute__((always_inline)) {
+        uint8_t* st = smem + (kt % C::STAGES) * C::STAGE;
+        const uint32_t k0 = (uint32_t)kt * C::BK;
+#pragma unroll
+        for (int q = 0; q < C::A_INS; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)(st + (wave * C::A_INS + q) * 1024), 16,
+                                                     k0 + ca[q] < K ? oa[q] + k0 : kOOB, 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < C::B_INS; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void*)(st + C::LDS_A + (wave * C::B_INS + q) * 1024),
+                                                     16, k0 + cb[q] < K ? ob[q] + k0 : kOOB, 0, 0, 0);
+    };
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+    issue(0);
+    if (nk > 1) issue(1);
+    if (nk > 2) issue(2);
+
+    // Stage kt + 3 reuses the buffer of stage kt - 1.  Every wave's reads of
+    // that stage completed before its MFMAs of iteration kt - 1 (which consume
+    // them), hence before it arrived at the barrier of iteration kt.
+    const int c = lane >> 4;
+    for (int kt = 0; kt < nk; ++kt) {
+        const int ahead = (kt + 2 < nk - 1 ? kt + 2 : nk - 1) - kt;   // stages issued after kt
+        if (ahead >= 2)
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PER_STAGE));
+        else if (ahead == 1)
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_STAGE));
+        else
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        block_barrier();
+        if (kt + 3 < nk) issue(kt + 3);
+        const uint8_t* sa = smem + (kt % C::STAGES) * C::STAGE;
+        const uint8_t* sb = sa + C::LDS_A;
+        v4i fa[C::FM], fb[C::FN];
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+            fb[j] = *reinterpret_cast<const v4i*>(sb + swz64(wn * C::TN + j * 16 + (lane & 15), c));
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+            fa[i] = *reinterpret_cast<const v4i*>(sa + swz64(wm * C::TM + i * 16 + (lane & 15), c));
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();
+}
+
+template <class C>
+struct IsDma { static constexpr bool value = false; };
+template <int BM_, int BN_, int WM_, int WN_>
+struct IsDma<CfgD<BM_, BN_, WM_, WN_>> { static constexpr bool value = true; };
+
+template <class C>
+__device__ __forceinline__ void mainloop_any(const int8_t* __restrict__ A, const int8_t* __restrict__ B, int64_t M,
+                                             int64_t N, int64_t K, int64_t m0, int64_t n0, uint8_t* smem,
+                                             v4i (&acc)[C::FM][C::FN]) {
+    if constexpr (IsDma<C>::value) {
+        const rsrc_t rsa = make_rsrc(A + m0 * K, (M - m0) * K);
+        const rsrc_t rsb = make_rsrc(B + n0 * K, (N - n0) * K);
+        mainloop_i8_dma<C>(rsa, rsb, (uint32_t)K, smem, acc);
+    } else {
+        mainloop_i8<C>(A, B, M, N, K, m0, n0, smem, acc);
+    }
+}
+
 template <class C>
 __global__ __launch_bounds__(C::THREADS) void k_gemm_i8_i32(const int8_t* __restrict__ A,
                                                             const int8_t* __restrict__ B, int64_t M,
@@ -158,7 +303,7 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_i8_i32(const int8_t* __rest
     tile_of_block(blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
     v4i acc[C::FM][C::FN];
-    mainloop_i8<C>(A, B, M, N, K, m0, n0, smem, acc);
+    mainloop_any<C>(A, B, M, N, K, m0, n0, smem, acc);
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int wm = wave / C::WN, wn = wave % C::WN;
 #pragma unroll
@@ -193,94 +338,104 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_i8_mixed(const int8_t* __re
     tile_of_block(blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
     v4i acc[C::FM][C::FN];
-    mainloop_i8<C>(Xq, Wq, M, N, K, m0, n0, smem, acc);
+    mainloop_any<C>(Xq, Wq, M, N, K, m0, n0, smem, acc);
 
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int wm = wave / C::WN, wn = wave % C::WN;
     const int64_t rb = m0 + wm * C::TM, cb = n0 + wn * C::TN;
 
-    // dequantize: C * s_x[m] * s_w[n]
-    v4f cf[C::FM][C::FN];
-    float sw[C::FN];
+    // Epilogue, one 16-row fragment at a time: dequantize C * s_x[m] * s_w[n],
+    // then add the fp16 outlier product on v_mfma_f32_16x16x32_f16 with the
+    // dequantized tile as the accumulator input.  The block gathers X[m0.., h]
+    // and w~[n0.., h] for up to OCAP outlier columns into LDS (free after the
+    // main loop) once; more columns are gathered in further passes.
+    constexpr int OCAP = 96;
+    constexpr int OST = OCAP + 8;                             // padded row stride (halves)
+    static_assert((C::BM + C::BN) * OST * 2 <= C::LDS, "outlier staging exceeds LDS");
+    _Float16* xo = reinterpret_cast<_Float16*>(smem);         // [BM][OST]
+    _Float16* wo = xo + C::BM * OST;                           // [BN][OST]
+    const int cnt = *ep.count;
     const rsrc_t rsw = make_rsrc(ep.s_w + cb, (N - cb) * 4);
     const rsrc_t rsx = make_rsrc(ep.s_x + rb, (M - rb) * 4);
+    const rsrc_t rxo = make_rsrc(ep.X + m0 * K, (M - m0) * K * 2);
+    const rsrc_t rwo = ep.W16 ? make_rsrc(ep.W16 + n0 * K, (N - n0) * K * 2) : make_rsrc(ep.Wq + n0 * K, (N - n0) * K);
+    const rsrc_t rsn = make_rsrc(ep.s_w + n0, (N - n0) * 4);
+    auto stage = [&](int hs) __attribute__((always_inline)) {
+        const int e = threadIdx.x % OCAP;                     // this thread's outlier slot
+        const rsrc_t ridx = make_rsrc(ep.idx + hs, (int64_t)(cnt - hs) * 4);
+        const uint32_t kc = bload4(ridx, (uint32_t)e * 4);
+        const bool valid = hs + e < cnt;
+        for (int t = threadIdx.x; t < (C::BM + C::BN) * OCAP; t += C::THREADS) {
+            const uint32_t r = t / OCAP, ee = t - r * OCAP;
+            const uint32_t k = ee == (uint32_t)e ? kc : bload4(ridx, ee * 4);
+            const bool ok = ee == (uint32_t)e ? valid : (hs + (int)ee < cnt);
+            uint16_t v;
+            if (r < (uint32_t)C::BM) {
+                v = bload2(rxo, ok ? (r * (uint32_t)K + k) * 2 : kOOB);
+            } else {
+                const uint32_t rr = r - C::BM;
+                if (ep.W16) {
+                    v = bload2(rwo, ok ? (rr * (uint32_t)K + k) * 2 : kOOB);
+                } else {
+                    const int8_t q = (int8_t)bload1(rwo, ok ? rr * (uint32_t)K + k : kOOB);
+                    v = f2h(__builtin_bit_cast(float, bload4(rsn, rr * 4)) * (float)q);
+                }
+            }
+            xo[r * OST + ee] = __builtin_bit_cast(_Float16, v);
+        }
+    };
+    if (cnt > 0 && cnt <= OCAP) {
+        stage(0);
+        __syncthreads();
+    }
+    float sw[C::FN];
 #pragma unroll
     for (int j = 0; j < C::FN; ++j)
         sw[j] = __builtin_bit_cast(float, bload4(rsw, (uint32_t)(j * 16 + (lane & 15)) * 4));
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i) {
+    static_for<C::FM>([&](auto I) __attribute__((always_inline)) {
+        constexpr int i = decltype(I)::value;
         float sx[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             sx[e] = __builtin_bit_cast(float, bload4(rsx, (uint32_t)(i * 16 + 4 * (lane >> 4) + e) * 4));
+        v4f cf[C::FN];
 #pragma unroll
         for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) cf[i][j][e] = (float)acc[i][j][e] * sx[e] * sw[j];
-    }
-
-    // fp16 outlier product over the gathered columns, 32 at a time.  The
-    // block gathers X[m0.., h] and w~[n0.., h] into LDS (free after the main
-    // loop) as [row][32] fp16, then each wave feeds them to the f16 MFMA with
-    // the dequantized tile as accumulator input.
-    const int cnt = *ep.count;
-    _Float16* xo = reinterpret_cast<_Float16*>(smem);           // [BM][32]
-    _Float16* wo = xo + C::BM * 32;                              // [BN][32]
-    const rsrc_t rxo = make_rsrc(ep.X + m0 * K, (M - m0) * K * 2);
-    const rsrc_t rwo = ep.W16 ? make_rsrc(ep.W16 + n0 * K, (N - n0) * K * 2) : make_rsrc(ep.Wq + n0 * K, (N - n0) * K);
-    const rsrc_t rsn = make_rsrc(ep.s_w + n0, (N - n0) * 4);
-    for (int h0 = 0; h0 < cnt; h0 += 32) {
-        // this thread always serves outlier slot e = t % 32 (THREADS % 32 == 0)
-        const int e = threadIdx.x & 31;
-        const rsrc_t ridx = make_rsrc(ep.idx + h0, (int64_t)(cnt - h0) * 4);
-        const uint32_t kc = bload4(ridx, (uint32_t)e * 4);
-        const bool valid = h0 + e < cnt;
-        for (int t = threadIdx.x; t < (C::BM + C::BN) * 32; t += C::THREADS) {
-            const uint32_t r = t >> 5;
-            uint16_t v;
-            if (r < (uint32_t)C::BM) {
-                v = bload2(rxo, valid ? (r * (uint32_t)K + kc) * 2 : kOOB);
-            } else {
-                const uint32_t rr = r - C::BM;
-                if (ep.W16) {
-                    v = bload2(rwo, valid ? (rr * (uint32_t)K + kc) * 2 : kOOB);
-                } else {
-                    const int8_t q = (int8_t)bload1(rwo, valid ? rr * (uint32_t)K + kc : kOOB);
-                    v = f2h(__builtin_bit_cast(float, bload4(rsn, rr * 4)) * (float)q);
+            for (int e = 0; e < 4; ++e) cf[j][e] = (float)acc[i][j][e] * sx[e] * sw[j];
+        for (int hs = 0; hs < cnt; hs += OCAP) {
+            if (cnt > OCAP) {                                 // gather this pass (block-uniform)
+                __syncthreads();
+                stage(hs);
+                __syncthreads();
+            }
+            const int hn = cnt - hs < OCAP ? cnt - hs : OCAP;
+            for (int h0 = 0; h0 < hn; h0 += 32) {
+                const int r = wm * C::TM + i * 16 + (lane & 15);
+                const v8h ao = *reinterpret_cast<const v8h*>(xo + r * OST + h0 + (lane >> 4) * 8);
+#pragma unroll
+                for (int j = 0; j < C::FN; ++j) {
+                    const int c = wn * C::TN + j * 16 + (lane & 15);
+                    const v8h bo = *reinterpret_cast<const v8h*>(wo + c * OST + h0 + (lane >> 4) * 8);
+                    cf[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, bo, cf[j], 0, 0, 0);
                 }
             }
-            xo[t] = __builtin_bit_cast(_Float16, v);
         }
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i) {
-            const int r = wm * C::TM + i * 16 + (lane & 15);
-            const v8h ao = *reinterpret_cast<const v8h*>(xo + r * 32 + (lane >> 4) * 8);
-#pragma unroll
-            for (int j = 0; j < C::FN; ++j) {
-                const int c = wn * C::TN + j * 16 + (lane & 15);
-                const v8h bo = *reinterpret_cast<const v8h*>(wo + c * 32 + (lane >> 4) * 8);
-                cf[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, bo, cf[i][j], 0, 0, 0);
-            }
-        }
-        __syncthreads();
-    }
-
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i)
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) {
             const int64_t col = cb + j * 16 + (lane & 15);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int64_t row = rb + i * 16 + 4 * (lane >> 4) + e;
-                if (row < M && col < N) store_out(ep.out, ep.out_dtype, row * N + col, cf[i][j][e]);
+                if (row < M && col < N) store_out(ep.out, ep.out_dtype, row * N + col, cf[j][e]);
             }
         }
+    });
 }
 
-using CfgBig = Cfg<256, 256, 2, 4>;    // 8 waves, wave tile 128 x 64
-using CfgMid = Cfg<128, 128, 2, 2>;    // 4 waves, wave tile 64 x 64
+using CfgBig = CfgD<256, 256, 2, 4>;   // 8 waves, wave tile 128 x 64, LDS-DMA stages
+using CfgMid = Cfg<128, 128, 2, 2>;    // 4 waves, wave tile 64 x 64 (register-staged)
+using CfgMidR = CfgMid;
 using CfgSmall = Cfg<64, 64, 2, 2>;    // 4 waves, wave tile 32 x 32
 
 template <class C>
@@ -290,11 +445,11 @@ static dim3 grid_of(int64_t M, int64_t N, int& tm, int& tn) {
     return dim3((unsigned)(tm * tn));
 }
 
-// Pick the largest tile that still gives every CU a block.
+// The largest tile that still gives every one of the 256 CUs a block.
 static int pick_cfg(int64_t M, int64_t N) {
     const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
     const int64_t mid = ((M + 127) / 128) * ((N + 127) / 128);
-    if (big >= 512) return 2;
+    if (big >= 256) return 2;
     if (mid >= 256) return 1;
     return 0;
 }
@@ -516,8 +671,8 @@ static void w4a4_dispatch(const uint32_t* Xp, const float* s_x, const uint32_t* 
                           int64_t K, int64_t N, void* out, int out_dtype, hipStream_t st) {
     int tm, tn;
     if (((M + 127) / 128) * ((N + 127) / 128) >= 256) {
-        dim3 g = grid_of<CfgMid>(M, N, tm, tn);
-        hipLaunchKernelGGL((k_gemm_w4a4<CfgMid, G, STORE_ACC>), g, dim3(CfgMid::THREADS), 0, st, Xp, s_x, Wp, s_w,
+        dim3 g = grid_of<CfgMidR>(M, N, tm, tn);
+        hipLaunchKernelGGL((k_gemm_w4a4<CfgMidR, G, STORE_ACC>), g, dim3(CfgMidR::THREADS), 0, st, Xp, s_x, Wp, s_w,
                            M, K, N, out, out_dtype, tm, tn);
     } else {
         dim3 g = grid_of<CfgSmall>(M, N, tm, tn);

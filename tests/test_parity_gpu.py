@@ -172,6 +172,19 @@ def test_gemm_i8_i32_big_tiles(qa):
     assert np.array_equal(C[rows], oracle.gemm_i8_i32(A, B, rows=rows))
 
 
+@pytest.mark.parametrize("K", [64, 128, 192, 256, 320, 528])
+def test_gemm_i8_i32_largest_tiles(qa, K):
+    # >= 1024 tiles of 256 x 256 selects the largest tile; ragged M and N, and
+    # every parity of the stage count of the software pipeline
+    M, N = 8200, 8230
+    rng = np.random.default_rng(K)
+    A = rng.integers(-128, 128, (M, K), dtype=np.int8)
+    B = rng.integers(-128, 128, (N, K), dtype=np.int8)
+    C = host(qa.qa_gemm_i8_i32(dev(A), dev(B)))
+    rows = np.unique(np.concatenate([[0, 255, 256, 8191, M - 1], rng.choice(M, size=11, replace=False)]))
+    assert np.array_equal(C[rows], oracle.gemm_i8_i32(A, B, rows=rows))
+
+
 # ============================================================ LLM.int8() mixed linear
 def _mixed_case(qa, X, W, tau, out_dtype, pass_w16, rows=None):
     Wq, s_w = qa.qa_quantize_rowwise_int8(dev(W))
