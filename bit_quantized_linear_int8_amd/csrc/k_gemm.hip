@@ -100,6 +100,10 @@ __device__ __forceinline__ void r2s(uint8_t* lds, const u32x4* reg) {
 
 // ---------------------------------------------------------------------------
 // int8 main loop: acc[FM][FN] = A[m0.., :] * B[n0.., :]^T
+// The MFMA takes the B fragment as its first operand, so it produces the
+// transposed 16 x 16 tile: lane l, element e of acc[i][j] holds output row
+// i*16 + l%16 and column j*16 + 4*(l/16) + e of the wave tile (four
+// consecutive columns per lane, stored with one vector store).
 // ---------------------------------------------------------------------------
 template <class C>
 __device__ __forceinline__ void mainloop_i8(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
@@ -150,7 +154,7 @@ __device__ __forceinline__ void mainloop_i8(const int8_t* __restrict__ A, const 
             for (int i = 0; i < C::FM; ++i)
 #pragma unroll
                 for (int j = 0; j < C::FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fb[j], fa[i], acc[i][j], 0, 0, 0);
         }
         if (more) {
             uint8_t* na = smem + ((kt + 1) & 1) * (C::LDS_A + C::LDS_B);
@@ -270,7 +274,7 @@ __device__ __forceinline__ void mainloop_i8_dma(rsrc_t rsa, rsrc_t rsb, uint32_t
         for (int i = 0; i < C::FM; ++i)
 #pragma unroll
             for (int j = 0; j < C::FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fb[j], fa[i], acc[i][j], 0, 0, 0);
     }
     __syncthreads();
 }
@@ -306,17 +310,23 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_i8_i32(const int8_t* __rest
     mainloop_any<C>(A, B, M, N, K, m0, n0, smem, acc);
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int wm = wave / C::WN, wn = wave % C::WN;
+    const bool vec = (N & 3) == 0;
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i)
+    for (int i = 0; i < C::FM; ++i) {
+        const int64_t row = m0 + wm * C::TM + i * 16 + (lane & 15);
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) {
-            const int64_t col = n0 + wn * C::TN + j * 16 + (lane & 15);
+            const int64_t col = n0 + wn * C::TN + j * 16 + 4 * (lane >> 4);
+            if (row >= M) continue;
+            if (vec) {
+                if (col < N) *reinterpret_cast<v4i*>(Cout + row * N + col) = acc[i][j];
+            } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t row = m0 + wm * C::TM + i * 16 + 4 * (lane >> 4) + e;
-                if (row < M && col < N) Cout[row * N + col] = acc[i][j][e];
+                for (int e = 0; e < 4; ++e)
+                    if (col + e < N) Cout[row * N + col + e] = acc[i][j][e];
             }
         }
+    }
 }
 
 __device__ __forceinline__ void store_out(void* out, int dtype, int64_t off, float v) {
@@ -326,6 +336,26 @@ __device__ __forceinline__ void store_out(void* out, int dtype, int64_t off, flo
         static_cast<uint16_t*>(out)[off] = f2h(v);
     else
         static_cast<uint16_t*>(out)[off] = f2bf(v);
+}
+
+// Four consecutive outputs v[0..3] at out[off .. off + 3]; `vec` means off is
+// a multiple of 4 and all four are in range, else only the first n are.
+__device__ __forceinline__ void store_out4(void* out, int dtype, int64_t off, const v4f& v, bool vec, int n) {
+    if (vec) {
+        if (dtype == 0) {
+            *reinterpret_cast<v4f*>(static_cast<float*>(out) + off) = v;
+        } else {
+            uint16_t h[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h[e] = dtype == 1 ? f2h(v[e]) : f2bf(v[e]);
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + off) =
+                u32x2{(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (e < n) store_out(out, dtype, off + e, v[e]);
+    }
 }
 
 template <class C>
@@ -338,71 +368,85 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_i8_mixed(const int8_t* __re
     tile_of_block(blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
     v4i acc[C::FM][C::FN];
-    mainloop_any<C>(Xq, Wq, M, N, K, m0, n0, smem, acc);
-
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int wm = wave / C::WN, wn = wave % C::WN;
     const int64_t rb = m0 + wm * C::TM, cb = n0 + wn * C::TN;
 
+    // The epilogue's scales and the outlier count are loaded before the main
+    // loop so their latency hides behind it.
+    const rsrc_t rsw = make_rsrc(ep.s_w + cb, (N - cb) * 4);
+    const rsrc_t rsx = make_rsrc(ep.s_x + rb, (M - rb) * 4);
+    const int cnt = (int)bload4(make_rsrc(ep.count, 4), 0);
+    float sw[C::FN][4], sxv[C::FM];
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            sw[j][e] = __builtin_bit_cast(float, bload4(rsw, (uint32_t)(j * 16 + 4 * (lane >> 4) + e) * 4));
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+        sxv[i] = __builtin_bit_cast(float, bload4(rsx, (uint32_t)(i * 16 + (lane & 15)) * 4));
+
+    mainloop_any<C>(Xq, Wq, M, N, K, m0, n0, smem, acc);
+
     // Epilogue, one 16-row fragment at a time: dequantize C * s_x[m] * s_w[n],
-    // then add the fp16 outlier product on v_mfma_f32_16x16x32_f16 with the
+    // then add the fp16 outlier product on v_mfma_f32_16x16x32_f16 (operands
+    // in the same transposed order as the int8 main loop) with the
     // dequantized tile as the accumulator input.  The block gathers X[m0.., h]
     // and w~[n0.., h] for up to OCAP outlier columns into LDS (free after the
-    // main loop) once; more columns are gathered in further passes.
+    // main loop), zero-padded to a multiple of 32; more columns take further
+    // passes.  One thread owns one row of X or W and loads only real columns.
     constexpr int OCAP = 96;
     constexpr int OST = OCAP + 8;                             // padded row stride (halves)
     static_assert((C::BM + C::BN) * OST * 2 <= C::LDS, "outlier staging exceeds LDS");
-    _Float16* xo = reinterpret_cast<_Float16*>(smem);         // [BM][OST]
-    _Float16* wo = xo + C::BM * OST;                           // [BN][OST]
-    const int cnt = *ep.count;
-    const rsrc_t rsw = make_rsrc(ep.s_w + cb, (N - cb) * 4);
-    const rsrc_t rsx = make_rsrc(ep.s_x + rb, (M - rb) * 4);
+    _Float16* xo = reinterpret_cast<_Float16*>(smem);         // [BM][OST], then [BN][OST] for w~
     const rsrc_t rxo = make_rsrc(ep.X + m0 * K, (M - m0) * K * 2);
     const rsrc_t rwo = ep.W16 ? make_rsrc(ep.W16 + n0 * K, (N - n0) * K * 2) : make_rsrc(ep.Wq + n0 * K, (N - n0) * K);
     const rsrc_t rsn = make_rsrc(ep.s_w + n0, (N - n0) * 4);
     auto stage = [&](int hs) __attribute__((always_inline)) {
-        const int e = threadIdx.x % OCAP;                     // this thread's outlier slot
-        const rsrc_t ridx = make_rsrc(ep.idx + hs, (int64_t)(cnt - hs) * 4);
-        const uint32_t kc = bload4(ridx, (uint32_t)e * 4);
-        const bool valid = hs + e < cnt;
-        for (int t = threadIdx.x; t < (C::BM + C::BN) * OCAP; t += C::THREADS) {
-            const uint32_t r = t / OCAP, ee = t - r * OCAP;
-            const uint32_t k = ee == (uint32_t)e ? kc : bload4(ridx, ee * 4);
-            const bool ok = ee == (uint32_t)e ? valid : (hs + (int)ee < cnt);
-            uint16_t v;
-            if (r < (uint32_t)C::BM) {
-                v = bload2(rxo, ok ? (r * (uint32_t)K + k) * 2 : kOOB);
-            } else {
-                const uint32_t rr = r - C::BM;
-                if (ep.W16) {
-                    v = bload2(rwo, ok ? (rr * (uint32_t)K + k) * 2 : kOOB);
-                } else {
-                    const int8_t q = (int8_t)bload1(rwo, ok ? rr * (uint32_t)K + k : kOOB);
-                    v = f2h(__builtin_bit_cast(float, bload4(rsn, rr * 4)) * (float)q);
+        const int hn = cnt - hs < OCAP ? cnt - hs : OCAP;
+        const int hp = (hn + 31) & ~31;
+        const rsrc_t ridx = make_rsrc(ep.idx + hs, (int64_t)hn * 4);
+        for (int r = threadIdx.x; r < C::BM + C::BN; r += C::THREADS) {
+            const bool isx = r < C::BM;
+            const uint32_t rr = isx ? r : r - C::BM;
+            const float swr = isx || ep.W16 ? 0.0f : __builtin_bit_cast(float, bload4(rsn, rr * 4));
+            for (int h = 0; h < hp; h += 8) {
+                uint32_t v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const uint32_t k = bload4(ridx, (uint32_t)(h + u) * 4);   // zero past hn
+                    const bool ok = h + u < hn;
+                    if (isx)
+                        v[u] = bload2(rxo, ok ? (rr * (uint32_t)K + k) * 2 : kOOB);
+                    else if (ep.W16)
+                        v[u] = bload2(rwo, ok ? (rr * (uint32_t)K + k) * 2 : kOOB);
+                    else
+                        v[u] = bload1(rwo, ok ? rr * (uint32_t)K + k : kOOB);
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    uint16_t hv = (uint16_t)v[u];
+                    if (!isx && !ep.W16) hv = h + u < hn ? f2h(swr * (float)(int8_t)(uint8_t)v[u]) : 0;
+                    xo[r * OST + h + u] = __builtin_bit_cast(_Float16, hv);
                 }
             }
-            xo[r * OST + ee] = __builtin_bit_cast(_Float16, v);
         }
     };
     if (cnt > 0 && cnt <= OCAP) {
         stage(0);
         __syncthreads();
     }
-    float sw[C::FN];
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j)
-        sw[j] = __builtin_bit_cast(float, bload4(rsw, (uint32_t)(j * 16 + (lane & 15)) * 4));
+    const _Float16* wo = xo + C::BM * OST;
+    const bool vec = (N & 3) == 0;
     static_for<C::FM>([&](auto I) __attribute__((always_inline)) {
         constexpr int i = decltype(I)::value;
-        float sx[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            sx[e] = __builtin_bit_cast(float, bload4(rsx, (uint32_t)(i * 16 + 4 * (lane >> 4) + e) * 4));
+        const float sx = sxv[i];
         v4f cf[C::FN];
 #pragma unroll
         for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) cf[j][e] = (float)acc[i][j][e] * sx[e] * sw[j];
+            for (int e = 0; e < 4; ++e) cf[j][e] = (float)acc[i][j][e] * sx * sw[j][e];
         for (int hs = 0; hs < cnt; hs += OCAP) {
             if (cnt > OCAP) {                                 // gather this pass (block-uniform)
                 __syncthreads();
@@ -417,18 +461,16 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_i8_mixed(const int8_t* __re
                 for (int j = 0; j < C::FN; ++j) {
                     const int c = wn * C::TN + j * 16 + (lane & 15);
                     const v8h bo = *reinterpret_cast<const v8h*>(wo + c * OST + h0 + (lane >> 4) * 8);
-                    cf[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, bo, cf[j], 0, 0, 0);
+                    cf[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bo, ao, cf[j], 0, 0, 0);
                 }
             }
         }
+        const int64_t row = rb + i * 16 + (lane & 15);
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) {
-            const int64_t col = cb + j * 16 + (lane & 15);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t row = rb + i * 16 + 4 * (lane >> 4) + e;
-                if (row < M && col < N) store_out(ep.out, ep.out_dtype, row * N + col, cf[j][e]);
-            }
+            const int64_t col = cb + j * 16 + 4 * (lane >> 4);
+            if (row < M && col < N)
+                store_out4(ep.out, ep.out_dtype, row * N + col, cf[j], vec, (int)(N - col < 4 ? N - col : 4));
         }
     });
 }
