@@ -15,7 +15,12 @@ prefill-shape mixed linear, the W8A8 FFN shape and the W4A4 group-Hadamard
 linear, in int8 TOPS against the dense int8 MFMA peak.
 
 roofline: the decode kernel's algorithmic bytes per launch / its average
-duration from HIP events around each launch (on the launch stream).
+launch duration, from HIP events recorded on the launch stream around the
+timed region (every step is exactly one launch of that kernel).  `traffic` is
+the HBM bytes per launch read from profiles/traffic.json (rocprofv3 FETCH_SIZE
+and WRITE_SIZE of that kernel, each scaled by the same counter's reading for a
+plain copy of known size, written by profile_counters.py), or null when that
+record is missing or was taken on a different kernel source.
 cpu_baseline: the CPU oracle timed on this host on whole decode steps.
 """
 from __future__ import annotations
@@ -97,20 +102,21 @@ def time_graph(torch, gs, steps, warmup):
     return e0.elapsed_time(e1) / n, wall / n, n
 
 
-def kernel_event_ms(torch, fns, reps):
-    """Average duration of single-launch calls, each bracketed by HIP events
-    recorded on the launch stream."""
-    evs = []
-    for i in range(reps):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        fns[i % len(fns)]()
-        b.record()
-        evs.append((a, b))
-    torch.cuda.synchronize()
-    ts = sorted(a.elapsed_time(b) for a, b in evs)
-    return sum(ts) / len(ts), ts[len(ts) // 2]
+def recorded_traffic(kernel, source):
+    """HBM bytes per launch of `kernel` from profiles/traffic.json, or None if
+    there is no record or it was taken on a different version of `source`."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel)
+        with open(os.path.join(ROOT, source), "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source") != source or rec.get("source_sha256") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
 
 
 # --------------------------------------------------------------------------- workloads
@@ -220,9 +226,8 @@ def main():
         gs = GraphSteps(torch, fns)
         log("[bench] decode_mixed: timing %d steps (graph of %d)" % (args.steps, gs.n))
         ms, wall_ms, n = time_graph(torch, gs, args.steps, args.warmup)
-        k_avg, k_med = kernel_event_ms(torch, fns, max(args.steps, copies))
         gbs = nbytes / (ms * 1e-3) / 1e9
-        ach = nbytes / (k_avg * 1e-3) / 1e9
+        ach = gbs                       # one launch of the decode kernel per step
         result = {
             "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": n,
             "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak",
@@ -233,9 +238,11 @@ def main():
                        "bytes_per_step": nbytes, "launch": "HIP graph replay", "wall_ms_per_step": round(wall_ms, 6)},
             "roofline": {"bound": "hbm", "kernel": "k_decode_mixed", "achieved": round(ach, 2),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                         "traffic": None, "kernel_ms_avg": round(k_avg, 6), "kernel_ms_median": round(k_med, 6)},
+                         "traffic": recorded_traffic("k_decode_mixed",
+                                                     "bit_quantized_linear_int8_amd/csrc/k_decode.hip"),
+                         "kernel_ms_avg": round(ms, 6), "algorithmic_bytes": nbytes},
         }
-        log("[bench] decode: %.1f GB/s per step, kernel %.2f us (events)" % (gbs, k_avg * 1e3))
+        log("[bench] decode: %.1f GB/s, %.2f us per launch" % (gbs, ms * 1e3))
         if not args.no_cpu:
             log("[bench] cpu oracle baseline (~%.0f s)" % args.cpu_seconds)
             result["cpu_baseline"] = cpu_baseline(c, nbytes, args.cpu_seconds)

@@ -2,17 +2,20 @@
 // tokens) as one fused kernel on gfx950.
 //
 // Decode is bound by streaming the int8 weight from HBM; the activation is a
-// few KB.  Every workgroup owns 16 output channels; its four waves split K in
-// quarters.  A workgroup
-//   1. issues its X loads, then ALL of its weight loads (directly in the
-//      B-operand layout of v_mfma_i32_16x16x64_i8, 16 x 16 bytes per lane),
+// few KB.  Every workgroup owns 16 output channels and has eight waves; wave w
+// multiplies the 64-byte K steps w, w + 8, w + 16, ... so each weight load
+// instruction of the block covers 16 rows x 512 contiguous bytes.  A workgroup
+//   1. issues its X loads (thread t owns the 8-column chunk t of every token),
+//      the scale of the channel it writes in the epilogue, then ALL of its
+//      weight loads (directly in the B-operand layout of
+//      v_mfma_i32_16x16x64_i8, 16 bytes per lane and step),
 //   2. while the weight bytes are in flight, recomputes -- identically in every
 //      workgroup -- the outlier columns (column max over the tokens, on the
 //      sign-cleared fp16 bit patterns with packed 16-bit max), the per-token
 //      scales and the int8 codes of X into LDS (the A operand), the ascending
 //      outlier list, the fp16 outlier activations, and starts the gather of
 //      the fp16 outlier weights,
-//   3. multiplies its K quarter on the MFMA, sums the four int32 partial tiles
+//   3. multiplies its K steps on the MFMA, sums the eight int32 partial tiles
 //      in LDS, dequantizes by s_x[m] * s_w[n] and adds the outlier product.
 // Loads retire in order (vmcnt), so the X loads go first: the prologue only
 // waits for X, not for the weight stream behind it.
@@ -27,9 +30,11 @@
 namespace qa {
 
 constexpr int DEC_MAXK = 4096;             // K <= 4096, K % 256 == 0
-constexpr int DEC_MAXSTEPS = DEC_MAXK / 256;
+constexpr int DEC_WAVES = 8, DEC_THREADS = 64 * DEC_WAVES;
+constexpr int DEC_MAXSTEPS = DEC_MAXK / 64 / DEC_WAVES;   // MFMA steps per wave
 constexpr int DEC_LDA = DEC_MAXK + 16;     // LDS row stride of the codes (spreads banks)
 constexpr int DEC_OCAP = 64;               // outliers whose operands are staged in LDS
+static_assert(DEC_MAXK / 8 == DEC_THREADS, "one 8-column chunk of X per thread");
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
@@ -42,214 +47,230 @@ __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
 __device__ __forceinline__ float half_lo(uint32_t v) { return h2f((uint16_t)(v & 0xffffu)); }
 __device__ __forceinline__ float half_hi(uint32_t v) { return h2f((uint16_t)(v >> 16)); }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS accesses
+// (lgkmcnt(0)), not for its global loads, so the weight stream stays in
+// flight across it (__syncthreads also waits for every outstanding load).
+// The memory clobbers keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);      // gfx9 encoding: lgkmcnt(0), vmcnt and expcnt not waited
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Maximum of an unsigned value over the 64 lanes, returned wave-uniform.
+// DPP moves (quad_perm [1,0,3,2], [2,3,0,1], row_half_mirror, row_mirror)
+// reduce each row of 16 lanes without LDS traffic; the four row maxima are
+// combined on the scalar unit.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+    const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+    const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+    return max(a, b);
+}
+
+// Number of set bits of a 64-bit lane mask held by lanes below this one.
+__device__ __forceinline__ int bits_below(uint64_t m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Element i of a 4-word vector by selects (no dynamically indexed registers).
+__device__ __forceinline__ uint32_t pick4(const u32x4& v, int i) {
+    const uint32_t lo = (i & 1) ? v[1] : v[0], hi = (i & 1) ? v[3] : v[2];
+    return (i & 2) ? hi : lo;
+}
+
 template <int MB>
-__global__ __launch_bounds__(256) void k_decode_mixed(const uint16_t* __restrict__ X, int M, int K,
-                                                      const int8_t* __restrict__ Wq, const float* __restrict__ s_w,
-                                                      const uint16_t* __restrict__ W16, int64_t N, float tau,
-                                                      void* __restrict__ out, int out_dtype) {
-    __shared__ __attribute__((aligned(16))) int8_t aq[16 * DEC_LDA];
+__global__ __launch_bounds__(DEC_THREADS) void k_decode_mixed(const uint16_t* __restrict__ X, int M, int K,
+                                                              const int8_t* __restrict__ Wq,
+                                                              const float* __restrict__ s_w,
+                                                              const uint16_t* __restrict__ W16, int64_t N, float tau,
+                                                              void* __restrict__ out, int out_dtype) {
+    __shared__ __attribute__((aligned(16))) int8_t aq[MB * DEC_LDA];
     __shared__ int32_t oidx[DEC_MAXK];
-    __shared__ int32_t red[4][256];
+    __shared__ int32_t red[DEC_WAVES][256];
     __shared__ float xo[DEC_OCAP][16];       // outlier activations  [h][m]
     __shared__ float wo[DEC_OCAP][16];       // outlier weights w~   [h][channel]
-    __shared__ uint32_t rmax[4][MB];
+    __shared__ uint32_t rmax[DEC_WAVES][MB];
     __shared__ float sx_s[16];
-    __shared__ int wtot[4];
+    __shared__ int wtot[DEC_WAVES];
 
     const int t = threadIdx.x, lane = t & 63, wave = wave_id();
     const int64_t n0 = (int64_t)blockIdx.x * 16;
-    const int steps = K >> 8;                         // 64-wide MFMA steps per wave
-    const int kw = wave * (K >> 2);                   // this wave's K quarter
+    const int S = K >> 6;                             // 64-byte MFMA steps in K
     const int nch = K >> 3;                           // 8-column chunks of X
+    const bool own = t < nch;
 
-    // 1a. X chunks: thread t owns chunks t and t + 256 (8 columns each).  Up to
-    //     8 tokens they stay in registers; beyond that the code pass re-reads.
-    constexpr bool KEEPX = MB <= 8;
-    const rsrc_t rsx = make_rsrc(X, (int64_t)M * K * 2);           // tokens past M read zeros
-    auto xload = [&](int m, int i) -> u32x4 {
-        const int c = t + 256 * i;
-        return bload16(rsx, c < nch ? (uint32_t)(m * K + 8 * c) * 2 : kOOB);
-    };
-    u32x4 xv[KEEPX ? MB : 1][2];
-    if constexpr (KEEPX) {
+    // 1a. X chunk t of every token (tokens past M read zeros)
+    const rsrc_t rsx = make_rsrc(X, (int64_t)M * K * 2);
+    u32x4 xv[MB];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int m = 0; m < MB; ++m) xv[m][i] = xload(m, i);
-    }
-    // 1b. the weight slice: row n0 + lane % 16, bytes kw + 64 s + 16 (lane / 16)
+    for (int m = 0; m < MB; ++m) xv[m] = bload16(rsx, own ? (uint32_t)(m * K + 8 * t) * 2 : kOOB);
+    // 1b. scale of channel n0 + t % 16 (outlier gather and epilogue), ahead of
+    //     the weight stream so that nothing in the prologue waits for the latter
+    const rsrc_t rsn = make_rsrc(s_w + n0, (N - n0) * 4);
+    const float swg = __builtin_bit_cast(float, bload4(rsn, (uint32_t)(t & 15) * 4));
+    // Every wave has issued its X loads before any wave issues weight loads,
+    // so the X requests are not queued behind weight traffic (no wait here).
+    __builtin_amdgcn_s_barrier();
+    // 1c. the weight slice: row n0 + lane % 16, bytes 64 s + 16 (lane / 16) of step s = wave + 8 j
     v4i wv[DEC_MAXSTEPS];
     const rsrc_t rsw = make_rsrc(Wq + n0 * K, (N - n0) * K);       // channels past N read zeros
     {
-        const uint32_t wo0 = (uint32_t)((lane & 15) * K + kw + 16 * (lane >> 4));
+        const uint32_t wo0 = (uint32_t)((lane & 15) * K + 16 * (lane >> 4));
 #pragma unroll
-        for (int s = 0; s < DEC_MAXSTEPS; ++s)
-            wv[s] = __builtin_bit_cast(v4i, bload16(rsw, s < steps ? wo0 + 64 * s : kOOB));
+        for (int j = 0; j < DEC_MAXSTEPS; ++j) {
+            const int s = wave + DEC_WAVES * j;
+            wv[j] = __builtin_bit_cast(v4i, bload16(rsw, s < S ? wo0 + 64 * s : kOOB));
+        }
     }
 
     // 2a. column max over the tokens on |x| bit patterns (fp16 magnitudes order
-    //     like their bits), outlier flags per chunk (8 bits), then the per-token
-    //     absmax over the non-outlier columns.
-    uint32_t flags[2];
-    u32x4 keepw[2];                                   // 0xffff per ordinary column, 0 per outlier
-    uint32_t ra[MB];
+    //     like their bits), outlier flags of the chunk (8 bits), then the
+    //     per-token absmax over the non-outlier columns.
+    uint32_t cm[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int m = 0; m < MB; ++m) ra[m] = 0u;
+    for (int m = 0; m < MB; ++m)
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        u32x4 xt[MB];
+        for (int d = 0; d < 4; ++d) cm[d] = pk_max_u16(cm[d], xv[m][d] & 0x7fff7fffu);
+    uint32_t flags = 0;
+    uint32_t keep[4];
 #pragma unroll
-        for (int m = 0; m < MB; ++m) {
-            if constexpr (KEEPX)
-                xt[m] = xv[m][i];
-            else
-                xt[m] = xload(m, i);
-        }
-        uint32_t cm[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int m = 0; m < MB; ++m)
-#pragma unroll
-            for (int d = 0; d < 4; ++d) cm[d] = pk_max_u16(cm[d], xt[m][d] & 0x7fff7fffu);
-        uint32_t f = 0;
-        uint32_t keep[4];
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const bool olo = half_lo(cm[d]) > tau, ohi = half_hi(cm[d]) > tau;
-            f |= (olo ? 1u : 0u) << (2 * d);
-            f |= (ohi ? 1u : 0u) << (2 * d + 1);
-            keep[d] = (olo ? 0u : 0xffffu) | (ohi ? 0u : 0xffff0000u);
-        }
-        f = (t + 256 * i < nch) ? f : 0u;
-        flags[i] = f;
-        keepw[i] = u32x4{keep[0], keep[1], keep[2], keep[3]};
-#pragma unroll
-        for (int m = 0; m < MB; ++m)
-#pragma unroll
-            for (int d = 0; d < 4; ++d) ra[m] = pk_max_u16(ra[m], xt[m][d] & 0x7fff7fffu & keep[d]);
+    for (int d = 0; d < 4; ++d) {
+        const bool olo = half_lo(cm[d]) > tau, ohi = half_hi(cm[d]) > tau;
+        flags |= (olo ? 1u : 0u) << (2 * d);
+        flags |= (ohi ? 1u : 0u) << (2 * d + 1);
+        keep[d] = (olo ? 0u : 0xffffu) | (ohi ? 0u : 0xffff0000u);
     }
+    flags = own ? flags : 0u;
+    const u32x4 keepw = u32x4{keep[0], keep[1], keep[2], keep[3]};   // 0xffff per ordinary column
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
-        uint32_t a = max(ra[m] & 0xffffu, ra[m] >> 16);
+        uint32_t r = 0u;
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) a = max(a, (uint32_t)__shfl_xor((int)a, o, QA_WAVE));
+        for (int d = 0; d < 4; ++d) r = pk_max_u16(r, xv[m][d] & 0x7fff7fffu & keep[d]);
+        const uint32_t a = wave_max_u32(max(r & 0xffffu, r >> 16));
         if (lane == 0) rmax[wave][m] = a;
     }
 
-    // 2b. ascending outlier list (block-wide exclusive scan per chunk slot);
-    //     the owner of an outlier column also stages its activations.
-    int base = 0;
+    // 2b. ascending outlier list (block-wide exclusive scan over the chunks,
+    //     the in-wave part from one ballot per flag bit); the owner of an
+    //     outlier column also stages its activations.
+    {
+        int below = 0, wsum = 0;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int cnt = __popc(flags[i]);
-        int x = cnt;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            int y = __shfl_up(x, d, QA_WAVE);
-            if (lane >= d) x += y;
+        for (int b = 0; b < 8; ++b) {
+            const uint64_t mb = __ballot((flags >> b) & 1u);
+            below += bits_below(mb);
+            wsum += __popcll(mb);
         }
-        if (lane == 63) wtot[wave] = x;
-        __syncthreads();
-        int off = base + x - cnt;
+        if (lane == 0) wtot[wave] = wsum;
+        lds_barrier();
+
+        int off = below;
         for (int w = 0; w < wave; ++w) off += wtot[w];
-        const int c = t + 256 * i;
-        uint32_t f = flags[i];
+        uint32_t f = flags;
         while (f) {
             const int j = __builtin_ctz(f);
             f &= f - 1u;
-            oidx[off] = 8 * c + j;
+            oidx[off] = 8 * t + j;
             if (off < DEC_OCAP) {
 #pragma unroll
                 for (int m = 0; m < MB; ++m) {
-                    const uint32_t w32 = KEEPX ? xv[KEEPX ? m : 0][i][j >> 1]
-                                               : (uint32_t)bload2(rsx, (uint32_t)(m * K + 8 * c + j) * 2);
-                    xo[off][m] = KEEPX ? ((j & 1) ? half_hi(w32) : half_lo(w32)) : half_lo(w32);
+                    const uint32_t w32 = pick4(xv[m], j >> 1);
+                    xo[off][m] = (j & 1) ? half_hi(w32) : half_lo(w32);
                 }
             }
             ++off;
         }
-        base += wtot[0] + wtot[1] + wtot[2] + wtot[3];
-        __syncthreads();
     }
-    const int count = base;
-
-    // 2c. start the gather of the fp16 outlier weights w~[n][h] (first 64)
-    const int gch = t & 15, gh = t >> 4;              // channel n0 + gch, outlier slots gh + 16 q
-    const rsrc_t rsn = make_rsrc(s_w + n0, (N - n0) * 4);
-    const rsrc_t rs16 = make_rsrc(W16 ? W16 + n0 * K : nullptr, W16 ? (N - n0) * K * 2 : 0);
-    const float swg = __builtin_bit_cast(float, bload4(rsn, (uint32_t)gch * 4));
-    float gw[DEC_OCAP / 16];
+    int count = 0;
 #pragma unroll
-    for (int q = 0; q < DEC_OCAP / 16; ++q) {
-        const int h = gh + 16 * q;
+    for (int w = 0; w < DEC_WAVES; ++w) count += wtot[w];
+    lds_barrier();
+
+
+    // 2c. start the gather of the outlier weights (first 64): the fp16 W[n][h]
+    //     or the int8 code Wq[n][h], as the aligned 32-bit word holding it.
+    //     The loads are unconditional (the descriptor is selected) and their
+    //     values are used only after the MFMA, so no wait lands here.
+    const int gch = t & 15, gh = t >> 4;              // channel n0 + gch, outlier slots gh + 32 q
+    const rsrc_t rs16 = make_rsrc(W16 ? W16 + n0 * K : nullptr, W16 ? (N - n0) * K * 2 : 0);
+    const rsrc_t rsg = W16 ? rs16 : rsw;
+    constexpr int GQ = DEC_OCAP / (DEC_THREADS / 16);
+    uint32_t graw[GQ], gsh[GQ];
+#pragma unroll
+    for (int q = 0; q < GQ; ++q) {
+        const int h = gh + (DEC_THREADS / 16) * q;
         const uint32_t k = (uint32_t)oidx[h < count ? h : 0];
-        const uint32_t off = h < count ? (uint32_t)gch * K + k : kOOB;
-        if (W16)
-            gw[q] = h2f(bload2(rs16, off == kOOB ? kOOB : off * 2));
-        else
-            gw[q] = h2f(f2h(swg * (float)(int8_t)bload1(rsw, off)));
+        const uint32_t e = (uint32_t)gch * K + k;     // element offset in the channel block
+        const uint32_t b = W16 ? 2 * e : e;           // byte offset
+        graw[q] = bload4(rsg, h < count ? (b & ~3u) : kOOB);
+        gsh[q] = (b & 3u) * 8;
     }
 
     // 2d. per-token scales (every thread derives the same values), int8 codes
     float sxm[MB];
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
-        const uint32_t ab = max(max(rmax[0][m], rmax[1][m]), max(rmax[2][m], rmax[3][m]));
+        uint32_t ab = 0u;
+#pragma unroll
+        for (int w = 0; w < DEC_WAVES; ++w) ab = max(ab, rmax[w][m]);
         const float a = h2f((uint16_t)ab);
         sxm[m] = a == 0.0f ? 1.0f : a / 127.0f;
         if (t == m) sx_s[m] = sxm[m];
     }
+    if (own) {
 #pragma unroll
-    for (int m = 0; m < MB; ++m) {
-        if (m >= M) break;
-        const float s = sxm[m], r = 1.0f / s;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int c = t + 256 * i;
-            if (c >= nch) continue;
-            u32x4 xc;
-            if constexpr (KEEPX)
-                xc = xv[m][i];
-            else
-                xc = xload(m, i);
-            float xf[8];
-            unpack8(xc & keepw[i], xf);                   // outlier columns -> 0 -> code 0
-            const u32x2 cw = codes8_dyn(xf, s, r);
-            const uint32_t lo = cw[0], hi = cw[1];
-            *reinterpret_cast<u32x2*>(aq + m * DEC_LDA + 8 * c) = u32x2{lo, hi};
+        for (int m = 0; m < MB; ++m) {
+            if (m < M) {
+                const float s = sxm[m], r = 1.0f / s;
+                float xf[8];
+                unpack8(xv[m] & keepw, xf);                // outlier columns -> 0 -> code 0
+                *reinterpret_cast<u32x2*>(aq + m * DEC_LDA + 8 * t) = codes8_dyn(xf, s, r);
+            }
         }
     }
-    __syncthreads();
+    lds_barrier();
 
-    // 3a. int32 MFMA over this wave's K quarter
+    // 3a. int32 MFMA over this wave's K steps
     v4i acc = v4i{0, 0, 0, 0};
     const int arow = lane & 15;
 #pragma unroll
-    for (int s = 0; s < DEC_MAXSTEPS; ++s) {
-        if (s < steps) {
+    for (int j = 0; j < DEC_MAXSTEPS; ++j) {
+        const int s = wave + DEC_WAVES * j;
+        if (s < S) {
             v4i fa = v4i{0, 0, 0, 0};
-            if (arow < M) fa = *reinterpret_cast<const v4i*>(aq + arow * DEC_LDA + kw + 64 * s + 16 * (lane >> 4));
-            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa, wv[s], acc, 0, 0, 0);
+            if (arow < M) fa = *reinterpret_cast<const v4i*>(aq + arow * DEC_LDA + 64 * s + 16 * (lane >> 4));
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa, wv[j], acc, 0, 0, 0);
         }
     }
+    // acc: lane l, element e = token 4 (l / 16) + e, channel l % 16
 #pragma unroll
     for (int e = 0; e < 4; ++e) red[wave][(4 * (lane >> 4) + e) * 16 + (lane & 15)] = acc[e];
 #pragma unroll
-    for (int q = 0; q < DEC_OCAP / 16; ++q)
-        if (gh + 16 * q < DEC_OCAP) wo[gh + 16 * q][gch] = gw[q];
-    __syncthreads();
+    for (int q = 0; q < GQ; ++q) {
+        const uint32_t v = graw[q] >> gsh[q];         // zero for an empty slot
+        wo[gh + (DEC_THREADS / 16) * q][gch] = W16 ? h2f((uint16_t)v) : h2f(f2h(swg * (float)(int8_t)(uint8_t)v));
+    }
+    lds_barrier();
 
-    // 3b. epilogue: thread t -> token m = t / 16, channel n0 + t % 16
+    // 3b. epilogue: thread t < 256 -> token m = t / 16, channel n0 + t % 16
     const int m = t >> 4, ch = t & 15;
     const int64_t n = n0 + ch;
-    if (m < M && n < N) {
-        const int32_t c = red[0][t] + red[1][t] + red[2][t] + red[3][t];
-        const float sw = s_w[n];
-        float v = (float)c * sx_s[m] * sw;
+    if (t < 256 && m < M && n < N) {
+        int32_t c = 0;
+#pragma unroll
+        for (int w = 0; w < DEC_WAVES; ++w) c += red[w][t];
+        float v = (float)c * sx_s[m] * swg;
         const int hs = count < DEC_OCAP ? count : DEC_OCAP;
         for (int h = 0; h < hs; ++h) v = v + xo[h][m] * wo[h][ch];
         for (int h = DEC_OCAP; h < count; ++h) {          // beyond the staged outliers
             const int k = oidx[h];
-            const float wt = W16 ? h2f(W16[n * K + k]) : h2f(f2h(sw * (float)Wq[n * K + k]));
+            const float wt = W16 ? h2f(W16[n * K + k]) : h2f(f2h(swg * (float)Wq[n * K + k]));
             v = v + h2f(X[(int64_t)m * K + k]) * wt;
         }
         const int64_t o = (int64_t)m * N + n;
@@ -269,7 +290,7 @@ bool decode_supported(int64_t M, int64_t K) {
 hipError_t launch_decode_mixed(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* s_w,
                                const uint16_t* W16, int64_t N, float tau, void* out, int out_dtype,
                                hipStream_t st) {
-    const dim3 grid((unsigned)((N + 15) / 16)), block(256);
+    const dim3 grid((unsigned)((N + 15) / 16)), block(DEC_THREADS);
     if (M <= 4)
         hipLaunchKernelGGL(k_decode_mixed<4>, grid, block, 0, st, X, (int)M, (int)K, Wq, s_w, W16, N, tau, out,
                            out_dtype);

@@ -1,0 +1,108 @@
+"""HBM traffic of one kernel from rocprofv3 counter runs, for bench.py.
+
+Reads four rocprofv3 output databases (rocpd SQLite, `counters_collection`
+view): a FETCH_SIZE run and a WRITE_SIZE run of the kernel's workload, and
+the same two counters over a plain device-to-device copy of known size
+(`bench.py --only copy`).  Each counter of the kernel (median over its
+dispatches, KiB per dispatch summed over all counter instances) is scaled by
+copy_bytes / (the same counter's reading for the copy), which turns the raw
+counter into bytes.  Writes the result into profiles/traffic.json under the
+kernel's name, with the SHA-256 of the kernel's source file (bench.py reports
+the figure only while that source is unchanged), and prints a summary.
+
+usage: python profile_counters.py --kernel k_decode_mixed \\
+           --source bit_quantized_linear_int8_amd/csrc/k_decode.hip \\
+           --fetch F.db --write W.db --copy-fetch CF.db --copy-write CW.db \\
+           [--copy-bytes 1073741824] [--workload decode_mixed] [--command "..."]
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import hashlib
+import json
+import os
+import sqlite3
+import statistics
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def per_dispatch(db_path, counter):
+    """{kernel name: [counter value per dispatch]} from one rocpd database."""
+    db = sqlite3.connect(db_path)
+    cur = db.cursor()
+    cols = [d[1] for d in cur.execute("pragma table_info(counters_collection)")]
+    ci = {c: i for i, c in enumerate(cols)}
+    name_col = "kernel_name" if "kernel_name" in ci else "name"
+    acc = collections.defaultdict(lambda: collections.defaultdict(float))
+    for r in cur.execute("select * from counters_collection"):
+        if r[ci["counter_name"]] != counter:
+            continue
+        acc[r[ci[name_col]]][r[ci["dispatch_id"]]] += float(r[ci["value"]])
+    return {k: list(v.values()) for k, v in acc.items()}
+
+
+def kernel_value(db_path, counter, kernel):
+    rows = per_dispatch(db_path, counter)
+    hits = {k: v for k, v in rows.items() if kernel in k}
+    if not hits:
+        raise SystemExit("no dispatch of %r with %s in %s" % (kernel, counter, db_path))
+    vals = [x for v in hits.values() for x in v]
+    return statistics.median(vals), len(vals)
+
+
+def copy_value(db_path, counter):
+    """Reading of the largest dispatch (the 1 GiB copy) in the copy run."""
+    rows = per_dispatch(db_path, counter)
+    return max(max(v) for v in rows.values())
+
+
+def main():
+    p = argparse.ArgumentParser()
+    p.add_argument("--kernel", required=True)
+    p.add_argument("--source", required=True, help="kernel source, relative to the repository root")
+    p.add_argument("--fetch", required=True)
+    p.add_argument("--write", required=True)
+    p.add_argument("--copy-fetch", required=True)
+    p.add_argument("--copy-write", required=True)
+    p.add_argument("--copy-bytes", type=int, default=1 << 30)
+    p.add_argument("--workload", default="")
+    p.add_argument("--command", default="")
+    a = p.parse_args()
+
+    f_kib, nf = kernel_value(a.fetch, "FETCH_SIZE", a.kernel)
+    w_kib, nw = kernel_value(a.write, "WRITE_SIZE", a.kernel)
+    cf_kib = copy_value(a.copy_fetch, "FETCH_SIZE")
+    cw_kib = copy_value(a.copy_write, "WRITE_SIZE")
+    ff = a.copy_bytes / (cf_kib * 1024.0)
+    fw = a.copy_bytes / (cw_kib * 1024.0)
+    fetch_b = f_kib * 1024.0 * ff
+    write_b = w_kib * 1024.0 * fw
+    with open(os.path.join(ROOT, a.source), "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    rec = {
+        "workload": a.workload, "source": a.source, "source_sha256": sha,
+        "fetch_size_kib_per_dispatch": round(f_kib, 1), "write_size_kib_per_dispatch": round(w_kib, 1),
+        "dispatches": [nf, nw],
+        "copy_bytes": a.copy_bytes, "copy_fetch_size_kib": round(cf_kib, 1), "copy_write_size_kib": round(cw_kib, 1),
+        "fetch_scale": round(ff, 4), "write_scale": round(fw, 4),
+        "hbm_bytes_per_launch": int(round(fetch_b + write_b)),
+        "fetch_bytes_per_launch": int(round(fetch_b)), "write_bytes_per_launch": int(round(write_b)),
+        "command": a.command,
+    }
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    data = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            data = json.load(f)
+    data[a.kernel] = rec
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps({a.kernel: rec}, indent=1))
+
+
+if __name__ == "__main__":
+    main()
