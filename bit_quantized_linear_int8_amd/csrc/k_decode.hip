@@ -36,14 +36,6 @@ constexpr int DEC_LDA = DEC_MAXK + 16;     // LDS row stride of the codes (sprea
 constexpr int DEC_OCAP = 64;               // outliers whose operands are staged in LDS
 static_assert(DEC_MAXK / 8 == DEC_THREADS, "one 8-column chunk of X per thread");
 
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-
-// Two 16-bit unsigned maxima in one instruction (v_pk_max_u16).
-__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
-    return __builtin_bit_cast(uint32_t,
-                              __builtin_elementwise_max(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
-}
-
 __device__ __forceinline__ float half_lo(uint32_t v) { return h2f((uint16_t)(v & 0xffffu)); }
 __device__ __forceinline__ float half_hi(uint32_t v) { return h2f((uint16_t)(v >> 16)); }
 
@@ -56,25 +48,6 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_s_waitcnt(0xC07F);      // gfx9 encoding: lgkmcnt(0), vmcnt and expcnt not waited
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-}
-
-// Maximum of an unsigned value over the 64 lanes, returned wave-uniform.
-// DPP moves (quad_perm [1,0,3,2], [2,3,0,1], row_half_mirror, row_mirror)
-// reduce each row of 16 lanes without LDS traffic; the four row maxima are
-// combined on the scalar unit.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
-    const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
-    const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
-    return max(a, b);
-}
-
-// Number of set bits of a 64-bit lane mask held by lanes below this one.
-__device__ __forceinline__ int bits_below(uint64_t m) {
-    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
 // Element i of a 4-word vector by selects (no dynamically indexed registers).

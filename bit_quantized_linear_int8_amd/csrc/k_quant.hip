@@ -27,14 +27,6 @@ __global__ void k_zero_u32(uint32_t* __restrict__ p, int64_t n) {
         p[i] = 0u;
 }
 
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-
-// Two 16-bit unsigned maxima in one instruction (v_pk_max_u16).
-__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
-    return __builtin_bit_cast(uint32_t,
-                              __builtin_elementwise_max(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
-}
-
 // ---------------------------------------------------------------------------
 // Outlier columns.  A block owns a strip of 64 columns (one 128-byte line per
 // row: 8 lanes x 16 bytes) and a segment of rows; a wave instruction reads 8
@@ -525,6 +517,106 @@ __global__ __launch_bounds__(256) void k_hq4_row(const uint16_t* __restrict__ X,
     }
 }
 
+// Per-row scale with the whole row in registers and the butterfly almost all
+// in-lane: K = 512 NC WPR, WPR waves per row (each owns K / WPR contiguous
+// elements, whole G-blocks), NC chunks of 8 elements per lane; the WPR waves
+// of a row combine their absmax through LDS.
+// With CPB = G/8 chunks per G-block, a lane holds
+//   LPB == 1 (NC >= CPB): chunks lane*NC .. lane*NC + NC - 1 (whole blocks);
+//   LPB  > 1 (NC <  CPB): chunks (lane/LPB)*CPB + lane%LPB + LPB*i of one block,
+// so element bits 0-2 are in the chunk, the chunk slots carry the remaining
+// in-block bits except the lowest log2(LPB) chunk bits, which sit in the lane
+// index and take one DPP quad exchange per bit.  The stages commute and every
+// partial sum is exact in fp64, so their order does not matter.
+template <int G, int NC, int WPR>
+__global__ __launch_bounds__(256) void k_hq4_row_reg(const uint16_t* __restrict__ X, int64_t rows, int64_t K,
+                                                     int qmin, int qmax, double c, uint32_t* __restrict__ packed,
+                                                     float* __restrict__ s_out) {
+    constexpr int CPB = G / 8;
+    constexpr int LPB = CPB > NC ? CPB / NC : 1;
+    static_assert(CPB >= 1 && LPB <= 4 && (LPB > 1 ? CPB % NC == 0 : NC % CPB == 0), "unsupported G / NC");
+    static_assert(WPR == 1 || WPR == 2 || WPR == 4, "waves per row");
+    __shared__ uint32_t red[4];
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int64_t row = (int64_t)blockIdx.x * (4 / WPR) + wave / WPR;
+    const int part = wave % WPR;                      // which K / WPR slice of the row
+    const bool live = row < rows;                     // every wave reaches the barrier below
+    const rsrc_t rx = make_rsrc(X + row * K, live ? K * 2 : 0);
+    uint32_t* pr = packed + row * (K >> 3) + part * 64 * NC;
+    auto chunk = [&](int i) -> int {
+        return LPB == 1 ? lane * NC + i : (lane / LPB) * CPB + (lane % LPB) + LPB * i;
+    };
+    const uint32_t pbase = (uint32_t)part * 64 * NC * 16;
+    u32x4 v[NC];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) v[i] = bload16(rx, pbase + (uint32_t)chunk(i) * 16);
+    double y[NC][8];
+#pragma unroll
+    for (int i = 0; i < NC; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[i][j] = (double)h2f((uint16_t)(v[i][j >> 1] >> (16 * (j & 1))));
+    // element bits (strides 1, 2, 4 inside a chunk)
+#pragma unroll
+    for (int h = 1; h < 8 && h < G; h <<= 1)
+#pragma unroll
+        for (int i = 0; i < NC; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if ((j & h) == 0) {
+                    const double a = y[i][j], b = y[i][j + h];
+                    y[i][j] = a + b;
+                    y[i][j + h] = a - b;
+                }
+    // chunk-slot bits
+    constexpr int SLOT_SPAN = LPB == 1 ? CPB : NC;
+#pragma unroll
+    for (int h = 1; h < SLOT_SPAN; h <<= 1)
+#pragma unroll
+        for (int i = 0; i < NC; ++i)
+            if ((i & h) == 0)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const double a = y[i][j], b = y[i + h][j];
+                    y[i][j] = a + b;
+                    y[i + h][j] = a - b;
+                }
+    // lane bits: partner lane ^ d; the lower lane keeps a + b, the upper p - y = a - b
+#pragma unroll
+    for (int d = 1; d < LPB; d <<= 1) {
+        const double sg = (lane & d) ? -1.0 : 1.0;
+#pragma unroll
+        for (int i = 0; i < NC; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const double p = d == 1 ? dpp_xor_f64<1>(y[i][j]) : dpp_xor_f64<2>(y[i][j]);
+                y[i][j] = __builtin_fma(sg, y[i][j], p);
+            }
+    }
+    float xs[NC][8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xs[i][j] = (float)(y[i][j] * c);
+        amax = fmaxf(amax, absmax8f(xs[i]));
+    }
+    uint32_t ab = wave_max_u32(__builtin_bit_cast(uint32_t, amax));       // amax >= 0: bits order like values
+    if constexpr (WPR > 1) {
+        if (lane == 0) red[wave] = ab;
+        __syncthreads();
+        const int w0 = wave - part;
+#pragma unroll
+        for (int q = 0; q < WPR; ++q) ab = max(ab, red[w0 + q]);
+    }
+    if (!live) return;
+    amax = __builtin_bit_cast(float, ab);
+    const float s = amax == 0.0f ? 1.0f : amax / (float)qmax;
+    const float r = 1.0f / s;
+    if (lane == 0 && part == 0) s_out[row] = s;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) pr[chunk(i)] = pack_codes(xs[i], s, r, qmin);
+}
+
 // Per-group scale (G >= 8): the G/8 lanes of a block reduce their absmax.
 template <int G>
 __global__ __launch_bounds__(256) void k_hq4_group(const uint16_t* __restrict__ X, int64_t rows, int64_t K,
@@ -551,6 +643,25 @@ __global__ __launch_bounds__(256) void k_hq4_group(const uint16_t* __restrict__ 
     }
 }
 
+// k_hq4_row_reg<G, NC> handles K == 512 NC when G / NC fits its lane mapping.
+template <int G, int NC>
+constexpr bool hq4_row_reg_ok() {
+    return G >= 8 && (G / 8 > NC ? (G / 8) / NC <= 4 && (G / 8) % NC == 0 : NC % (G / 8) == 0);
+}
+
+template <int G, int NC, int WPR>
+static bool hq4_row_reg_try(const uint16_t* X, int64_t rows, int64_t K, int qmin, int qmax, double c,
+                            uint32_t* packed, float* s, hipStream_t st) {
+    if constexpr (hq4_row_reg_ok<G, NC>()) {
+        if (K != 512 * NC * WPR) return false;
+        const dim3 grid((unsigned)((rows + 4 / WPR - 1) / (4 / WPR))), block(256);
+        hipLaunchKernelGGL((k_hq4_row_reg<G, NC, WPR>), grid, block, 0, st, X, rows, K, qmin, qmax, c, packed, s);
+        return true;
+    } else {
+        return false;
+    }
+}
+
 template <int G>
 static void hq4_dispatch(const uint16_t* X, int64_t rows, int64_t K, bool per_group, int qmin, int qmax,
                          uint32_t* packed, float* s, hipStream_t st) {
@@ -562,6 +673,14 @@ static void hq4_dispatch(const uint16_t* X, int64_t rows, int64_t K, bool per_gr
         return;
     }
     const int64_t nch = K / 8;
+    // two waves per row where the lane mapping allows it (more waves to hide latency)
+    if (hq4_row_reg_try<G, 2, 1>(X, rows, K, qmin, qmax, c, packed, s, st) ||
+        hq4_row_reg_try<G, 2, 2>(X, rows, K, qmin, qmax, c, packed, s, st) ||
+        hq4_row_reg_try<G, 4, 2>(X, rows, K, qmin, qmax, c, packed, s, st) ||
+        hq4_row_reg_try<G, 8, 1>(X, rows, K, qmin, qmax, c, packed, s, st) ||
+        hq4_row_reg_try<G, 4, 1>(X, rows, K, qmin, qmax, c, packed, s, st) ||
+        hq4_row_reg_try<G, 8, 2>(X, rows, K, qmin, qmax, c, packed, s, st))
+        return;
 #define QA_HQ(NC) hipLaunchKernelGGL((k_hq4_row<G, NC>), grid, block, 0, st, X, rows, K, qmin, qmax, c, packed, s)
     if (nch <= 64) QA_HQ(1);
     else if (nch <= 128) QA_HQ(2);

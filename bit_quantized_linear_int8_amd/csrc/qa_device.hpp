@@ -135,6 +135,45 @@ __device__ __forceinline__ float quot_rne(float x, float s, float r) {
     return n;
 }
 
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Two 16-bit unsigned maxima in one instruction (v_pk_max_u16).
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t,
+                              __builtin_elementwise_max(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
+}
+
+// Maximum of an unsigned value over the 64 lanes, returned wave-uniform.
+// DPP moves (quad_perm [1,0,3,2], [2,3,0,1], row_half_mirror, row_mirror)
+// reduce each row of 16 lanes without LDS traffic; the four row maxima are
+// combined on the scalar unit.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+    const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+    const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+    return max(a, b);
+}
+
+// Number of set bits of a 64-bit lane mask held by lanes below this one.
+__device__ __forceinline__ int bits_below(uint64_t m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Exchange of a double with the lane whose index differs in bit d (d = 1 or
+// 2) by DPP quad permutations of its two 32-bit halves (no LDS traffic).
+template <int D>
+__device__ __forceinline__ double dpp_xor_f64(double v) {
+    static_assert(D == 1 || D == 2, "quad permutations only");
+    constexpr int ctrl = D == 1 ? 0xB1 : 0x4E;     // quad_perm [1,0,3,2] / [2,3,0,1]
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, ctrl, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), ctrl, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, (uint64_t)lo | ((uint64_t)hi << 32));
+}
+
 __device__ __forceinline__ int clampi(int v, int lo, int hi) {
     return v < lo ? lo : (v > hi ? hi : v);
 }

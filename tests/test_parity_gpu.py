@@ -294,6 +294,20 @@ def test_hadamard_quant_int4(qa, G, per_group):
     assert np.array_equal(host(packed).view(np.uint32), op)
 
 
+@pytest.mark.parametrize("K", [1024, 2048, 4096, 8192])
+@pytest.mark.parametrize("G", [8, 16, 32, 64, 128, 256])
+def test_hadamard_quant_int4_row_in_registers(qa, K, G):
+    """Per-row scales at K = 512 * NC * WPR: the row is held in registers by
+    one or two waves, and all but the lowest chunk bits of a block are
+    in-lane; 13 rows leave the last workgroup partly past the end."""
+    X, _, _ = synthetic.w4a4_inputs(13, K, 1, seed=K + G)
+    X[5, :] = 0
+    packed, s = qa.qa_hadamard_quant_int4(dev(X), G, False)
+    op, os_ = oracle.hadamard_quant_int4(X, G, False)
+    assert np.array_equal(host(s), os_)
+    assert np.array_equal(host(packed).view(np.uint32), op)
+
+
 @pytest.mark.parametrize("K", [4096, 8192, 8448, 16384])
 def test_hadamard_quant_int4_row_lengths(qa, K):
     X, _, _ = synthetic.w4a4_inputs(9, K, 1, seed=K)
