@@ -98,6 +98,11 @@ __device__ __forceinline__ void r2s(uint8_t* lds, const u32x4* reg) {
     }
 }
 
+// No-op for the main loops' `after_issue` hook.
+struct NoHook {
+    __device__ __forceinline__ void operator()() const {}
+};
+
 // ---------------------------------------------------------------------------
 // int8 main loop: acc[FM][FN] = A[m0.., :] * B[n0.., :]^T
 // The MFMA takes the B fragment as its first operand, so it produces the
@@ -105,10 +110,10 @@ __device__ __forceinline__ void r2s(uint8_t* lds, const u32x4* reg) {
 // i*16 + l%16 and column j*16 + 4*(l/16) + e of the wave tile (four
 // consecutive columns per lane, stored with one vector store).
 // ---------------------------------------------------------------------------
-template <class C>
+template <class C, class F = NoHook>
 __device__ __forceinline__ void mainloop_i8(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
                                             int64_t M, int64_t N, int64_t K, int64_t m0, int64_t n0,
-                                            uint8_t* smem, v4i (&acc)[C::FM][C::FN]) {
+                                            uint8_t* smem, v4i (&acc)[C::FM][C::FN], F&& after_issue = F{}) {
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int wm = wave / C::WN, wn = wave % C::WN;
     const uint8_t* Ab = reinterpret_cast<const uint8_t*>(A);
@@ -125,6 +130,7 @@ __device__ __forceinline__ void mainloop_i8(const int8_t* __restrict__ A, const 
     u32x4 ra[C::A_CH], rb[C::B_CH];
     g2r<C::A_CH, C::THREADS>(rsa, ld, 0, kbytes, ra);
     g2r<C::B_CH, C::THREADS>(rsb, ld, 0, kbytes, rb);
+    after_issue();
     r2s<C::A_CH, C::THREADS>(smem, ra);
     r2s<C::B_CH, C::THREADS>(smem + C::LDS_A, rb);
     __syncthreads();
@@ -205,9 +211,11 @@ __device__ __forceinline__ void block_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <class C>
+// `after_issue` runs once the first stages' loads are in flight (the caller
+// issues its own early loads there).
+template <class C, class F = NoHook>
 __device__ __forceinline__ void mainloop_i8_dma(rsrc_t rsa, rsrc_t rsb, uint32_t K, uint8_t* smem,
-                                                v4i (&acc)[C::FM][C::FN]) {
+                                                v4i (&acc)[C::FM][C::FN], F&& after_issue = F{}) {
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int wm = wave / C::WN, wn = wave % C::WN;
     constexpr int PER_STAGE = C::A_INS + C::B_INS;
@@ -246,6 +254,7 @@ __device__ __forceinline__ void mainloop_i8_dma(rsrc_t rsa, rsrc_t rsb, uint32_t
     issue(0);
     if (nk > 1) issue(1);
     if (nk > 2) issue(2);
+    after_issue();
 
     // Stage kt + 3 reuses the buffer of stage kt - 1.  Every wave's reads of
     // that stage completed before its MFMAs of iteration kt - 1 (which consume
@@ -284,16 +293,16 @@ struct IsDma { static constexpr bool value = false; };
 template <int BM_, int BN_, int WM_, int WN_>
 struct IsDma<CfgD<BM_, BN_, WM_, WN_>> { static constexpr bool value = true; };
 
-template <class C>
+template <class C, class F = NoHook>
 __device__ __forceinline__ void mainloop_any(const int8_t* __restrict__ A, const int8_t* __restrict__ B, int64_t M,
                                              int64_t N, int64_t K, int64_t m0, int64_t n0, uint8_t* smem,
-                                             v4i (&acc)[C::FM][C::FN]) {
+                                             v4i (&acc)[C::FM][C::FN], F&& after_issue = F{}) {
     if constexpr (IsDma<C>::value) {
         const rsrc_t rsa = make_rsrc(A + m0 * K, (M - m0) * K);
         const rsrc_t rsb = make_rsrc(B + n0 * K, (N - n0) * K);
-        mainloop_i8_dma<C>(rsa, rsb, (uint32_t)K, smem, acc);
+        mainloop_i8_dma<C>(rsa, rsb, (uint32_t)K, smem, acc, after_issue);
     } else {
-        mainloop_i8<C>(A, B, M, N, K, m0, n0, smem, acc);
+        mainloop_i8<C>(A, B, M, N, K, m0, n0, smem, acc, after_issue);
     }
 }
 
@@ -387,7 +396,38 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_i8_mixed(const int8_t* __re
     for (int i = 0; i < C::FM; ++i)
         sxv[i] = __builtin_bit_cast(float, bload4(rsx, (uint32_t)(i * 16 + (lane & 15)) * 4));
 
-    mainloop_any<C>(Xq, Wq, M, N, K, m0, n0, smem, acc);
+    // Up to PRE outlier columns: the list is read here with the scales, and
+    // the gather of this thread's row of X or w~ is issued in the main loop's
+    // hook, behind the first stages' loads; the values wait in registers.
+    constexpr int PRE = 8;
+    static_assert(C::THREADS >= C::BM + C::BN, "one thread per gathered row");
+    const rsrc_t rxo = make_rsrc(ep.X + m0 * K, (M - m0) * K * 2);
+    const rsrc_t rwo = ep.W16 ? make_rsrc(ep.W16 + n0 * K, (N - n0) * K * 2) : make_rsrc(ep.Wq + n0 * K, (N - n0) * K);
+    const rsrc_t rsn = make_rsrc(ep.s_w + n0, (N - n0) * 4);
+    const int prow = threadIdx.x;                             // gather row: X rows, then W rows
+    const bool pisx = prow < C::BM;
+    const uint32_t prr = pisx ? prow : prow - C::BM;
+    uint32_t pk[PRE], pv[PRE];
+    {
+        const rsrc_t ridx = make_rsrc(ep.idx, (int64_t)PRE * 4);
+#pragma unroll
+        for (int u = 0; u < PRE; ++u) pk[u] = bload4(ridx, (uint32_t)u * 4);
+    }
+    const float pswr = pisx || ep.W16 ? 0.0f : __builtin_bit_cast(float, bload4(rsn, prr * 4));
+    auto prefetch = [&]() __attribute__((always_inline)) {
+        const bool any = cnt > 0 && cnt <= PRE && prow < C::BM + C::BN;
+#pragma unroll
+        for (int u = 0; u < PRE; ++u) {
+            const bool ok = any && u < cnt;
+            if (pisx)
+                pv[u] = bload2(rxo, ok ? (prr * (uint32_t)K + pk[u]) * 2 : kOOB);
+            else if (ep.W16)
+                pv[u] = bload2(rwo, ok ? (prr * (uint32_t)K + pk[u]) * 2 : kOOB);
+            else
+                pv[u] = bload1(rwo, ok ? prr * (uint32_t)K + pk[u] : kOOB);
+        }
+    };
+    mainloop_any<C>(Xq, Wq, M, N, K, m0, n0, smem, acc, prefetch);
 
     // Epilogue, one 16-row fragment at a time: dequantize C * s_x[m] * s_w[n],
     // then add the fp16 outlier product on v_mfma_f32_16x16x32_f16 (operands
@@ -400,9 +440,6 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_i8_mixed(const int8_t* __re
     constexpr int OST = OCAP + 8;                             // padded row stride (halves)
     static_assert((C::BM + C::BN) * OST * 2 <= C::LDS, "outlier staging exceeds LDS");
     _Float16* xo = reinterpret_cast<_Float16*>(smem);         // [BM][OST], then [BN][OST] for w~
-    const rsrc_t rxo = make_rsrc(ep.X + m0 * K, (M - m0) * K * 2);
-    const rsrc_t rwo = ep.W16 ? make_rsrc(ep.W16 + n0 * K, (N - n0) * K * 2) : make_rsrc(ep.Wq + n0 * K, (N - n0) * K);
-    const rsrc_t rsn = make_rsrc(ep.s_w + n0, (N - n0) * 4);
     auto stage = [&](int hs) __attribute__((always_inline)) {
         const int hn = cnt - hs < OCAP ? cnt - hs : OCAP;
         const int hp = (hn + 31) & ~31;
@@ -433,12 +470,25 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_i8_mixed(const int8_t* __re
             }
         }
     };
-    if (cnt > 0 && cnt <= OCAP) {
+    if (cnt > 0 && cnt <= PRE) {
+        if (prow < C::BM + C::BN) {                         // the prefetched columns, zero-padded to 32
+#pragma unroll
+            for (int u = 0; u < 32; ++u) {
+                uint16_t hv = 0;
+                if (u < PRE && u < cnt) {
+                    hv = (uint16_t)pv[u < PRE ? u : 0];
+                    if (!pisx && !ep.W16) hv = f2h(pswr * (float)(int8_t)(uint8_t)pv[u < PRE ? u : 0]);
+                }
+                xo[prow * OST + u] = __builtin_bit_cast(_Float16, hv);
+            }
+        }
+        __syncthreads();
+    } else if (cnt > PRE && cnt <= OCAP) {
         stage(0);
         __syncthreads();
     }
     const _Float16* wo = xo + C::BM * OST;
-    const bool vec = (N & 3) == 0;
+    const bool vec = ((ep.ldo | N) & 3) == 0;
     static_for<C::FM>([&](auto I) __attribute__((always_inline)) {
         constexpr int i = decltype(I)::value;
         const float sx = sxv[i];
@@ -470,12 +520,13 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_i8_mixed(const int8_t* __re
         for (int j = 0; j < C::FN; ++j) {
             const int64_t col = cb + j * 16 + 4 * (lane >> 4);
             if (row < M && col < N)
-                store_out4(ep.out, ep.out_dtype, row * N + col, cf[j], vec, (int)(N - col < 4 ? N - col : 4));
+                store_out4(ep.out, ep.out_dtype, row * ep.ldo + col, cf[j], vec, (int)(N - col < 4 ? N - col : 4));
         }
     });
 }
 
 using CfgBig = CfgD<256, 256, 2, 4>;   // 8 waves, wave tile 128 x 64, LDS-DMA stages
+using CfgTail = CfgD<256, 128, 2, 4>;  // 8 waves, wave tile 128 x 32, LDS-DMA stages
 using CfgMid = Cfg<128, 128, 2, 2>;    // 4 waves, wave tile 64 x 64 (register-staged)
 using CfgMidR = CfgMid;
 using CfgSmall = Cfg<64, 64, 2, 2>;    // 4 waves, wave tile 32 x 32
@@ -519,9 +570,38 @@ hipError_t launch_gemm_i8_i32(const int8_t* A, const int8_t* B, int64_t M, int64
     return hipGetLastError();
 }
 
+// Output columns [0, split) get 256 x 256 tiles in whole rounds over the 256
+// CUs, the rest a second launch of 256 x 128 tiles: without it the last
+// partial round of big tiles leaves most CUs idle.
+// Returns 0 when no split helps.
+static int64_t tail_split(int64_t M, int64_t N) {
+    const int64_t tm = (M + 255) / 256, tn = (N + 255) / 256, nb = tm * tn;
+    if (nb <= 256 || nb % 256 == 0) return 0;
+    const int64_t cols = (nb / 256) * 256 / tm;               // whole tile columns in the full rounds
+    const int64_t split = cols * 256;
+    return cols >= 1 && split < N ? split : 0;
+}
+
 hipError_t launch_gemm_i8_mixed(const int8_t* Xq, const int8_t* Wq, int64_t M, int64_t K, int64_t N,
                                 const MixedEpilogue& ep, hipStream_t st) {
     int tm, tn;
+    if (pick_cfg(M, N) == 2) {
+        if (const int64_t split = tail_split(M, N)) {
+            dim3 g = grid_of<CfgBig>(M, split, tm, tn);
+            hipLaunchKernelGGL(k_gemm_i8_mixed<CfgBig>, g, dim3(CfgBig::THREADS), 0, st, Xq, Wq, M, K, split, ep,
+                               tm, tn);
+            const int esz = ep.out_dtype == 0 ? 4 : 2;
+            MixedEpilogue et = ep;
+            et.s_w = ep.s_w + split;
+            et.W16 = ep.W16 ? ep.W16 + split * K : nullptr;
+            et.Wq = ep.Wq + split * K;
+            et.out = static_cast<uint8_t*>(ep.out) + split * esz;
+            g = grid_of<CfgTail>(M, N - split, tm, tn);
+            hipLaunchKernelGGL(k_gemm_i8_mixed<CfgTail>, g, dim3(CfgTail::THREADS), 0, st, Xq, Wq + split * K, M, K,
+                               N - split, et, tm, tn);
+            return hipGetLastError();
+        }
+    }
     switch (pick_cfg(M, N)) {
         case 2: {
             dim3 g = grid_of<CfgBig>(M, N, tm, tn);

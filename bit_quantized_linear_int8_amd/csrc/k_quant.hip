@@ -19,50 +19,42 @@
 namespace qa {
 
 // ---------------------------------------------------------------------------
-// Zero fill (used instead of hipMemsetAsync so the sequence can be captured).
-// ---------------------------------------------------------------------------
-__global__ void k_zero_u32(uint32_t* __restrict__ p, int64_t n) {
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
-         i += (int64_t)gridDim.x * blockDim.x)
-        p[i] = 0u;
-}
-
-// ---------------------------------------------------------------------------
 // Outlier columns.  A block owns a strip of 64 columns (one 128-byte line per
 // row: 8 lanes x 16 bytes) and a segment of rows; a wave instruction reads 8
 // full lines.  The column max runs on the sign-cleared fp16 bit patterns
 // (magnitudes of fp16 values order like their bits) with packed 16-bit max,
 // folded across lanes and waves.  Column j is an outlier when its max exceeds
-// the threshold; the block ORs the strip's 64 outlier bits into one 64-bit
-// flag word (only when some bit is set, so most blocks issue no atomic at
-// all -- atomics on one address serialize at the memory side).  The running
-// column max itself is only merged (atomic max) when the caller asks for it.
+// the threshold; lane 0 writes the strip's 64 outlier bits as one 64-bit
+// word of this row segment's partial flag set (plain stores: no atomics, no
+// clearing), and the column max of the segment when the caller asks for it.
+// Consumers OR the partial words (and max the partial column maxima).
 // ---------------------------------------------------------------------------
 constexpr int OC_STRIP = 64;
 constexpr int OC_UNR = 8;                       // loads in flight per lane
 constexpr int OC_PASS = 256 * 64;               // columns compacted per pass
 
+constexpr int OC_SEG_MAX = 8;                  // row segments of the scan (partial flag sets)
+
 template <bool WANT_MAX>
 __global__ __launch_bounds__(256) void k_outlier_scan(const uint16_t* __restrict__ X, int64_t M, int64_t K,
-                                                      int64_t seg_rows, float tau,
-                                                      unsigned long long* __restrict__ flags,
-                                                      uint32_t* __restrict__ cmax) {
+                                                      float tau, unsigned long long* __restrict__ flags_p,
+                                                      uint32_t* __restrict__ cmax_p) {
     __shared__ uint32_t red[4][32];
     const int t = threadIdx.x, lane = t & 63, wave = wave_id();
     const int64_t c0 = (int64_t)blockIdx.x * OC_STRIP;
-    const int64_t r0 = (int64_t)blockIdx.y * seg_rows;
-    const int64_t r1 = r0 + seg_rows < M ? r0 + seg_rows : M;
-    const int64_t nrows = r1 > r0 ? r1 - r0 : 0;
-    // range: from (r0, c0) to the end of row r1 - 1; rows past the segment read zeros
-    const rsrc_t rs = make_rsrc(X + r0 * K + c0, (nrows * K - c0) * 2);
+    const int64_t nw = (K + 63) / 64;
+    const int seg = blockIdx.y, nseg = gridDim.y;
     const int chunk = lane & 7, rsub = lane >> 3;
     const uint32_t coff = (c0 + chunk * 8 + 8 <= K) ? (uint32_t)chunk * 16 : kOOB;
     uint32_t m[4] = {0u, 0u, 0u, 0u};
-    for (int64_t rb = 0; rb < nrows; rb += 32 * OC_UNR) {
+    // this segment's row blocks: rb = 256 (seg + nseg j)
+    for (int64_t rb = (int64_t)seg * 32 * OC_UNR; rb < M; rb += (int64_t)nseg * 32 * OC_UNR) {
+        const int64_t nr = M - rb < 32 * OC_UNR ? M - rb : 32 * OC_UNR;
+        const rsrc_t rs = make_rsrc(X + rb * K + c0, (nr * K - c0) * 2);   // rows past the block read zeros
         u32x4 v[OC_UNR];
 #pragma unroll
         for (int u = 0; u < OC_UNR; ++u) {
-            const uint32_t r = (uint32_t)(rb + u * 32 + wave * 8 + rsub);
+            const uint32_t r = (uint32_t)(u * 32 + wave * 8 + rsub);
             v[u] = bload16(rs, coff == kOOB ? kOOB : r * (uint32_t)K * 2 + coff);
         }
 #pragma unroll
@@ -80,14 +72,15 @@ __global__ __launch_bounds__(256) void k_outlier_scan(const uint16_t* __restrict
     }
     __syncthreads();
     if (wave == 0) {
-        // lane j: column c0 + j
+        // lane j: column c0 + j.  Every (strip, segment) slot is overwritten, so
+        // the scratch needs no clearing between calls.
         const int w = lane >> 1;
         const uint32_t a = pk_max_u16(pk_max_u16(red[0][w], red[1][w]), pk_max_u16(red[2][w], red[3][w]));
         const float cm = h2f((uint16_t)((lane & 1) ? (a >> 16) : (a & 0xffffu)));
         const int64_t col = c0 + lane;
         const unsigned long long bits = __ballot(col < K && cm > tau);
-        if (lane == 0 && bits) atomicOr(&flags[blockIdx.x], bits);
-        if (WANT_MAX && col < K) atomicMax(&cmax[col], __builtin_bit_cast(uint32_t, cm));
+        if (lane == 0) flags_p[(int64_t)seg * nw + blockIdx.x] = bits;
+        if (WANT_MAX && col < K) cmax_p[(int64_t)seg * K + col] = __builtin_bit_cast(uint32_t, cm);
     }
 }
 
@@ -95,12 +88,12 @@ __global__ __launch_bounds__(256) void k_outlier_scan(const uint16_t* __restrict
 // [t C, t C + C) of each pass of up to 16384 columns, so one block-wide scan of
 // the per-thread counts places every outlier.  Optionally writes the byte
 // mask and the column max.  Run by one block of 256 threads.
-__device__ void outlier_compact(const unsigned long long* __restrict__ flags, const uint32_t* __restrict__ cmax,
-                                int64_t K, uint8_t* __restrict__ mask, int32_t* __restrict__ idx,
-                                int32_t* __restrict__ count, float* __restrict__ colmax_out, int* wsum) {
+// `word(w)` returns flag word w (the OR of the scan's partial words).
+template <class WordF>
+__device__ void outlier_compact(WordF word, const uint32_t* __restrict__ cmax_p, int nseg, int64_t K,
+                                uint8_t* __restrict__ mask, int32_t* __restrict__ idx, int32_t* __restrict__ count,
+                                float* __restrict__ colmax_out, int* wsum) {
     const int t = threadIdx.x, lane = t & 63, wave = wave_id();
-    const int64_t nw = (K + 63) / 64;
-    const rsrc_t rf = make_rsrc(flags, nw * 8);
     int running = 0;
     for (int64_t pb = 0; pb < K; pb += OC_PASS) {
         const int64_t pk = K - pb < OC_PASS ? K - pb : OC_PASS;
@@ -108,9 +101,7 @@ __device__ void outlier_compact(const unsigned long long* __restrict__ flags, co
         const int64_t cb = pb + (int64_t)t * C;
         // the (at most two) flag words covering [cb, cb + C)
         const int64_t w0 = cb >> 6;
-        const u32x2 a0 = bload8(rf, (uint32_t)w0 * 8), a1 = bload8(rf, (uint32_t)(w0 + 1) * 8);
-        const unsigned long long f0 = a0[0] | ((unsigned long long)a0[1] << 32);
-        const unsigned long long f1 = a1[0] | ((unsigned long long)a1[1] << 32);
+        const unsigned long long f0 = word(w0), f1 = word(w0 + 1);
         const int sh = (int)(cb & 63);
         unsigned long long fl = sh ? ((f0 >> sh) | (f1 << (64 - sh))) : f0;
         int64_t lim = pb + pk - cb;                            // valid columns of this thread
@@ -120,7 +111,13 @@ __device__ void outlier_compact(const unsigned long long* __restrict__ flags, co
             for (int i = 0; i < (int)lim; ++i) {
                 const int64_t col = cb + i;
                 if (mask) mask[col] = (uint8_t)((fl >> i) & 1ull);
-                if (colmax_out) colmax_out[col] = __builtin_bit_cast(float, cmax[col]);
+                if (colmax_out) {
+                    uint32_t cm = 0u;                  // magnitudes: bits order like values
+#pragma unroll
+                    for (int sg = 0; sg < OC_SEG_MAX; ++sg)
+                        if (sg < nseg) cm = max(cm, cmax_p[(int64_t)sg * K + col]);
+                    colmax_out[col] = __builtin_bit_cast(float, cm);
+                }
             }
         }
         const int cnt = __popcll(fl);
@@ -145,56 +142,68 @@ __device__ void outlier_compact(const unsigned long long* __restrict__ flags, co
     if (t == 0) *count = running;
 }
 
-__global__ __launch_bounds__(256) void k_outlier_finalize(const unsigned long long* __restrict__ flags,
-                                                          const uint32_t* __restrict__ cmax, int64_t K,
+__global__ __launch_bounds__(256) void k_outlier_finalize(const unsigned long long* __restrict__ flags_p,
+                                                          const uint32_t* __restrict__ cmax_p, int nseg, int64_t K,
                                                           uint8_t* __restrict__ mask, int32_t* __restrict__ idx,
                                                           int32_t* __restrict__ count, float* __restrict__ colmax_out) {
     __shared__ int wsum[4];
-    outlier_compact(flags, cmax, K, mask, idx, count, colmax_out, wsum);
+    const int64_t nw = (K + 63) / 64;
+    const rsrc_t rf = make_rsrc(flags_p, (int64_t)nseg * nw * 8);
+    auto word = [&](int64_t w) -> unsigned long long {
+        unsigned long long f = 0ull;
+#pragma unroll
+        for (int sg = 0; sg < OC_SEG_MAX; ++sg) {             // all loads in flight at once
+            const u32x2 a = bload8(rf, w < nw && sg < nseg ? (uint32_t)(sg * nw + w) * 8 : kOOB);
+            f |= a[0] | ((unsigned long long)a[1] << 32);
+        }
+        return f;
+    };
+    outlier_compact(word, cmax_p, nseg, K, mask, idx, count, colmax_out, wsum);
 }
 
-size_t outlier_scratch_bytes(int64_t K) { return (size_t)((K + 63) / 64) * 8 + (size_t)K * 4 + 64; }
-
-// flags [ceil(K/64)] u64 first, then the column max [K] u32
-static void outlier_scan(const uint16_t* X, int64_t M, int64_t K, float tau, void* scratch, bool want_max,
-                         hipStream_t st) {
-    unsigned long long* flags = static_cast<unsigned long long*>(scratch);
-    const int64_t nw = (K + 63) / 64;
-    uint32_t* cmax = reinterpret_cast<uint32_t*>(flags + nw);
-    const int64_t nz = 2 * nw + (want_max ? K : 0);
-    hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((nz + 255) / 256 < 1024 ? (nz + 255) / 256 : 1024)),
-                       dim3(256), 0, st, reinterpret_cast<uint32_t*>(flags), nz);
-    // row segments: about 512 blocks, at least 256 rows per segment, and a
-    // segment's byte span below 2^30 (32-bit buffer offsets)
-    const int64_t strips = nw;
+// Row segments of the scan: about 512 workgroups (strips x segments), at most
+// OC_SEG_MAX segments and one per 256 rows.
+static int outlier_segments(int64_t M, int64_t K) {
+    const int64_t strips = (K + 63) / 64;
     int64_t segs = (512 + strips - 1) / strips;
-    const int64_t max_segs = M > 0 ? (M + 255) / 256 : 1;
-    if (segs > max_segs) segs = max_segs;
-    if (segs < 1) segs = 1;
-    int64_t seg_rows = M > 0 ? (M + segs - 1) / segs : 1;
-    const int64_t span_rows = ((int64_t)1 << 30) / (2 * K);
-    if (seg_rows > span_rows) seg_rows = span_rows;
-    seg_rows = (seg_rows + 31) / 32 * 32;
-    if (seg_rows > span_rows) seg_rows -= 32;
-    segs = M > 0 ? (M + seg_rows - 1) / seg_rows : 1;
-    dim3 grid((unsigned)strips, (unsigned)segs);
+    const int64_t by_rows = M > 0 ? (M + 255) / 256 : 1;
+    if (segs > by_rows) segs = by_rows;
+    if (segs > OC_SEG_MAX) segs = OC_SEG_MAX;
+    return segs < 1 ? 1 : (int)segs;
+}
+
+// partial flags [OC_SEG_MAX x ceil(K/64)] u64, then partial column max [OC_SEG_MAX x K] u32
+size_t outlier_scratch_bytes(int64_t K) {
+    return (size_t)OC_SEG_MAX * ((size_t)((K + 63) / 64) * 8 + (size_t)K * 4) + 64;
+}
+
+static int outlier_scan(const uint16_t* X, int64_t M, int64_t K, float tau, void* scratch, bool want_max,
+                        hipStream_t st) {
+    unsigned long long* flags_p = static_cast<unsigned long long*>(scratch);
+    const int64_t nw = (K + 63) / 64;
+    uint32_t* cmax_p = reinterpret_cast<uint32_t*>(flags_p + OC_SEG_MAX * nw);
+    const int segs = outlier_segments(M, K);
+    dim3 grid((unsigned)nw, (unsigned)segs);
     if (want_max)
-        hipLaunchKernelGGL(k_outlier_scan<true>, grid, dim3(256), 0, st, X, M, K, seg_rows, tau, flags, cmax);
+        hipLaunchKernelGGL(k_outlier_scan<true>, grid, dim3(256), 0, st, X, M, K, tau, flags_p, cmax_p);
     else
-        hipLaunchKernelGGL(k_outlier_scan<false>, grid, dim3(256), 0, st, X, M, K, seg_rows, tau, flags, cmax);
+        hipLaunchKernelGGL(k_outlier_scan<false>, grid, dim3(256), 0, st, X, M, K, tau, flags_p, cmax_p);
+    return segs;
 }
 
 hipError_t launch_outlier_cols(const uint16_t* X, int64_t M, int64_t K, float tau, uint8_t* mask,
                                int32_t* idx, int32_t* count, float* colmax, void* scratch, hipStream_t st) {
-    outlier_scan(X, M, K, tau, scratch, colmax != nullptr, st);
-    unsigned long long* flags = static_cast<unsigned long long*>(scratch);
-    const uint32_t* cmax = reinterpret_cast<const uint32_t*>(flags + (K + 63) / 64);
-    hipLaunchKernelGGL(k_outlier_finalize, dim3(1), dim3(256), 0, st, flags, cmax, K, mask, idx, count, colmax);
+    const int segs = outlier_scan(X, M, K, tau, scratch, colmax != nullptr, st);
+    unsigned long long* flags_p = static_cast<unsigned long long*>(scratch);
+    const uint32_t* cmax_p = reinterpret_cast<const uint32_t*>(flags_p + OC_SEG_MAX * ((K + 63) / 64));
+    hipLaunchKernelGGL(k_outlier_finalize, dim3(1), dim3(256), 0, st, flags_p, cmax_p, segs, K, mask, idx, count,
+                       colmax);
     return hipGetLastError();
 }
 
-hipError_t launch_outlier_flags(const uint16_t* X, int64_t M, int64_t K, float tau, void* scratch, hipStream_t st) {
-    outlier_scan(X, M, K, tau, scratch, false, st);
+hipError_t launch_outlier_flags(const uint16_t* X, int64_t M, int64_t K, float tau, void* scratch, int* segs,
+                                hipStream_t st) {
+    *segs = outlier_scan(X, M, K, tau, scratch, false, st);
     return hipGetLastError();
 }
 
@@ -204,10 +213,12 @@ hipError_t launch_outlier_flags(const uint16_t* X, int64_t M, int64_t K, float t
 // reads the row twice (absmax pass, then quantize pass).
 //
 // Masks: MASK_BYTES -- caller's byte per column (nonzero = masked), applied per
-// value; MASK_FLAGS -- outlier flag bits (one byte per 8-column chunk, the flag
-// words of the outlier scan), turned into 16-bit keep words through a
-// 256-entry table in LDS and ANDed into the fp16 bits.  In MASK_FLAGS mode
-// block 0 also writes the ascending outlier list and its count.
+// value; MASK_FLAGS -- outlier flag bits: every workgroup ORs the outlier
+// scan's nseg partial flag sets into one bit per column in LDS, and a byte of
+// it (one 8-column chunk) selects 16-bit keep words from a 256-entry table in
+// LDS, ANDed into the fp16 bits.  In MASK_FLAGS mode block 0 also writes the
+// ascending outlier list and its count; in MASK_NONE mode a non-null `count`
+// is set to 0 (no outliers).
 // ---------------------------------------------------------------------------
 enum { MASK_NONE = 0, MASK_BYTES = 1, MASK_FLAGS = 2 };
 
@@ -261,13 +272,16 @@ __device__ __forceinline__ u32x2 clip_codes(u32x2 c, int qmin) {
     return u32x2{w[0], w[1]};
 }
 
+constexpr int RQ_FLAG_WORDS = 2048;             // merged flag words in LDS: K <= 131072
+
 template <int NC, bool STATIC, int MASK>
 __global__ __launch_bounds__(256) void k_rowquant_i8(const uint16_t* __restrict__ X, int64_t rows, int64_t K,
-                                                     const uint8_t* __restrict__ mask, int qmin, int qmax,
+                                                     const uint8_t* __restrict__ mask, int nseg, int qmin, int qmax,
                                                      const float* __restrict__ s_in, const int32_t* __restrict__ z_in,
                                                      int8_t* __restrict__ q, float* __restrict__ s_out,
                                                      int32_t* __restrict__ idx, int32_t* __restrict__ count) {
     __shared__ u32x4 lut[MASK == MASK_FLAGS ? 256 : 1];
+    __shared__ unsigned long long flw[MASK == MASK_FLAGS ? RQ_FLAG_WORDS : 1];
     __shared__ int wsum[4];
     const int lane = threadIdx.x & 63;
     if constexpr (MASK == MASK_FLAGS) {
@@ -277,16 +291,30 @@ __global__ __launch_bounds__(256) void k_rowquant_i8(const uint16_t* __restrict_
         for (int d = 0; d < 4; ++d)
             k[d] = (((b >> (2 * d)) & 1u) ? 0u : 0xffffu) | (((b >> (2 * d + 1)) & 1u) ? 0u : 0xffff0000u);
         lut[b] = k;
-        if (blockIdx.x == 0)
-            outlier_compact(reinterpret_cast<const unsigned long long*>(mask), nullptr, K, nullptr, idx, count,
-                            nullptr, wsum);
+        const int64_t nw = (K + 63) / 64;
+        const rsrc_t rf = make_rsrc(mask, (int64_t)nseg * nw * 8);
+        for (int64_t w = threadIdx.x; w < nw; w += 256) {
+            unsigned long long f = 0ull;
+#pragma unroll
+            for (int sg = 0; sg < OC_SEG_MAX; ++sg) {         // all loads in flight at once
+                const u32x2 a = bload8(rf, sg < nseg ? (uint32_t)(sg * nw + w) * 8 : kOOB);
+                f |= a[0] | ((unsigned long long)a[1] << 32);
+            }
+            flw[w] = f;
+        }
         __syncthreads();
+        if (blockIdx.x == 0)
+            outlier_compact([&](int64_t w) -> unsigned long long { return w < nw ? flw[w] : 0ull; }, nullptr, 0, K,
+                            nullptr, idx, count, nullptr, wsum);
     }
+    if constexpr (MASK == MASK_NONE)
+        if (count && blockIdx.x == 0 && threadIdx.x == 0) *count = 0;
     const int64_t row = (int64_t)blockIdx.x * 4 + wave_id();
     if (row >= rows) return;
     const int64_t nch = K >> 3;
     const rsrc_t rx = make_rsrc(X + row * K, K * 2);
-    const rsrc_t rm = make_rsrc(mask, MASK == MASK_NONE ? 0 : (MASK == MASK_BYTES ? K : nch));
+    const rsrc_t rm = make_rsrc(mask, MASK == MASK_BYTES ? K : 0);
+    const uint8_t* flb = reinterpret_cast<const uint8_t*>(flw);
     int8_t* qr = q + row * K;
     float s = 1.0f, r = 1.0f;
     int z = 0;
@@ -298,7 +326,7 @@ __global__ __launch_bounds__(256) void k_rowquant_i8(const uint16_t* __restrict_
     auto load = [&](int64_t ch, u32x4& v, u32x2& mk) {
         v = bload16(rx, (uint32_t)ch * 16);
         mk = u32x2{0u, 0u};
-        if constexpr (MASK == MASK_FLAGS) v &= lut[bload1(rm, (uint32_t)ch)];
+        if constexpr (MASK == MASK_FLAGS) v &= lut[ch < nch ? flb[ch] : 0];
         if constexpr (MASK == MASK_BYTES) mk = bload8(rm, (uint32_t)ch * 8);
     };
     if constexpr (NC > 0) {
@@ -372,13 +400,13 @@ __global__ __launch_bounds__(256) void k_rowquant_i8(const uint16_t* __restrict_
 }
 
 template <bool STATIC, int MASK>
-static void rowquant_dispatch(const uint16_t* X, int64_t rows, int64_t K, const uint8_t* mask, int qmin, int qmax,
-                              const float* s_in, const int32_t* z_in, int8_t* q, float* s_out, int32_t* idx,
+static void rowquant_dispatch(const uint16_t* X, int64_t rows, int64_t K, const uint8_t* mask, int nseg, int qmin,
+                              int qmax, const float* s_in, const int32_t* z_in, int8_t* q, float* s_out, int32_t* idx,
                               int32_t* count, hipStream_t st) {
     const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
     const int64_t nch = K / 8;
-#define QA_RQ(NC) hipLaunchKernelGGL((k_rowquant_i8<NC, STATIC, MASK>), grid, block, 0, st, X, rows, K, mask, qmin, \
-                                     qmax, s_in, z_in, q, s_out, idx, count)
+#define QA_RQ(NC) hipLaunchKernelGGL((k_rowquant_i8<NC, STATIC, MASK>), grid, block, 0, st, X, rows, K, mask, nseg, \
+                                     qmin, qmax, s_in, z_in, q, s_out, idx, count)
     if (nch <= 64) QA_RQ(1);
     else if (nch <= 128) QA_RQ(2);
     else if (nch <= 256) QA_RQ(4);
@@ -391,18 +419,28 @@ static void rowquant_dispatch(const uint16_t* X, int64_t rows, int64_t K, const 
 hipError_t launch_rowquant_i8(const uint16_t* X, int64_t rows, int64_t K, const uint8_t* mask, int qmin, int qmax,
                               const float* s_in, const int32_t* z_in, int8_t* q, float* s_out, hipStream_t st) {
     if (s_in)
-        rowquant_dispatch<true, MASK_BYTES>(X, rows, K, mask, qmin, qmax, s_in, z_in, q, s_out, nullptr, nullptr, st);
+        rowquant_dispatch<true, MASK_BYTES>(X, rows, K, mask, 0, qmin, qmax, s_in, z_in, q, s_out, nullptr, nullptr,
+                                            st);
     else if (mask)
-        rowquant_dispatch<false, MASK_BYTES>(X, rows, K, mask, qmin, qmax, s_in, z_in, q, s_out, nullptr, nullptr, st);
+        rowquant_dispatch<false, MASK_BYTES>(X, rows, K, mask, 0, qmin, qmax, s_in, z_in, q, s_out, nullptr, nullptr,
+                                             st);
     else
-        rowquant_dispatch<false, MASK_NONE>(X, rows, K, mask, qmin, qmax, s_in, z_in, q, s_out, nullptr, nullptr, st);
+        rowquant_dispatch<false, MASK_NONE>(X, rows, K, mask, 0, qmin, qmax, s_in, z_in, q, s_out, nullptr, nullptr,
+                                            st);
     return hipGetLastError();
 }
 
-hipError_t launch_rowquant_i8_flags(const uint16_t* X, int64_t rows, int64_t K, const void* scratch, int8_t* q,
-                                    float* s_out, int32_t* idx, int32_t* count, hipStream_t st) {
-    rowquant_dispatch<false, MASK_FLAGS>(X, rows, K, static_cast<const uint8_t*>(scratch), -127, 127, nullptr,
+hipError_t launch_rowquant_i8_flags(const uint16_t* X, int64_t rows, int64_t K, const void* scratch, int nseg,
+                                    int8_t* q, float* s_out, int32_t* idx, int32_t* count, hipStream_t st) {
+    rowquant_dispatch<false, MASK_FLAGS>(X, rows, K, static_cast<const uint8_t*>(scratch), nseg, -127, 127, nullptr,
                                          nullptr, q, s_out, idx, count, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_rowquant_i8_no_outliers(const uint16_t* X, int64_t rows, int64_t K, int8_t* q, float* s_out,
+                                          int32_t* count, hipStream_t st) {
+    rowquant_dispatch<false, MASK_NONE>(X, rows, K, nullptr, 0, -127, 127, nullptr, nullptr, q, s_out, nullptr, count,
+                                        st);
     return hipGetLastError();
 }
 

@@ -179,10 +179,18 @@ qa_status qa_qlinear_int8_mixed(const void* X_f16, int64_t M, int64_t K, const i
     float* s_x = reinterpret_cast<float*>(ws + L.s_x);
     int8_t* xq = reinterpret_cast<int8_t*>(ws + L.xq);
 
-    hipError_t e = qa::launch_outlier_flags(X, M, K, threshold, ws + L.cmax, st);
-    if (e != hipSuccess) return device_status(e, "qa_qlinear_int8_mixed (outlier columns)");
-    e = qa::launch_rowquant_i8_flags(X, M, K, ws + L.cmax, xq, s_x, idx, count, st);
-    if (e != hipSuccess) return device_status(e, "qa_qlinear_int8_mixed (row quantization)");
+    hipError_t e;
+    if (!(threshold < 65504.0f)) {
+        // no finite fp16 magnitude exceeds the threshold: no outlier columns
+        e = qa::launch_rowquant_i8_no_outliers(X, M, K, xq, s_x, count, st);
+        if (e != hipSuccess) return device_status(e, "qa_qlinear_int8_mixed (row quantization)");
+    } else {
+        int segs = 1;
+        e = qa::launch_outlier_flags(X, M, K, threshold, ws + L.cmax, &segs, st);
+        if (e != hipSuccess) return device_status(e, "qa_qlinear_int8_mixed (outlier columns)");
+        e = qa::launch_rowquant_i8_flags(X, M, K, ws + L.cmax, segs, xq, s_x, idx, count, st);
+        if (e != hipSuccess) return device_status(e, "qa_qlinear_int8_mixed (row quantization)");
+    }
     qa::MixedEpilogue ep;
     ep.s_x = s_x;
     ep.s_w = s_w;
@@ -192,6 +200,7 @@ qa_status qa_qlinear_int8_mixed(const void* X_f16, int64_t M, int64_t K, const i
     ep.idx = idx;
     ep.count = count;
     ep.out = out;
+    ep.ldo = N;
     ep.out_dtype = (int)out_dtype;
     return device_status(qa::launch_gemm_i8_mixed(xq, Wq, M, K, N, ep, st), "qa_qlinear_int8_mixed (gemm)");
 }

@@ -8,8 +8,9 @@
 
 namespace qa {
 
-// Scratch of the outlier-column scan: one 64-bit flag word per 64 columns and
-// the running column max [K]; zero-filled by the launchers themselves.
+// Scratch of the outlier-column scan: up to 32 row segments' partial flag
+// words (one 64-bit word per 64 columns) and partial column maxima [K], all
+// overwritten by every scan (no clearing).
 size_t outlier_scratch_bytes(int64_t K);
 
 // Public outlier detection: scan + one-block finalize (mask, list, count, max).
@@ -17,17 +18,23 @@ hipError_t launch_outlier_cols(const uint16_t* X, int64_t M, int64_t K, float ta
                                int32_t* idx, int32_t* count, float* colmax, void* scratch, hipStream_t st);
 
 // Outlier flag words only (for the mixed linear, which consumes them in the
-// row quantizer).
-hipError_t launch_outlier_flags(const uint16_t* X, int64_t M, int64_t K, float tau, void* scratch, hipStream_t st);
+// row quantizer); *segs receives the number of partial flag sets written.
+hipError_t launch_outlier_flags(const uint16_t* X, int64_t M, int64_t K, float tau, void* scratch, int* segs,
+                                hipStream_t st);
 
 hipError_t launch_rowquant_i8(const uint16_t* X, int64_t rows, int64_t K, const uint8_t* mask,
                               int qmin, int qmax, const float* s_in, const int32_t* z_in,
                               int8_t* q, float* s_out, hipStream_t st);
 
 // Dynamic [-127, 127] row quantization with the outlier flags of `scratch`
-// (launch_outlier_flags) as the mask; also writes the ascending outlier list.
-hipError_t launch_rowquant_i8_flags(const uint16_t* X, int64_t rows, int64_t K, const void* scratch, int8_t* q,
-                                    float* s_out, int32_t* idx, int32_t* count, hipStream_t st);
+// (launch_outlier_flags, nseg partial sets) as the mask; also writes the
+// ascending outlier list and its count.
+hipError_t launch_rowquant_i8_flags(const uint16_t* X, int64_t rows, int64_t K, const void* scratch, int nseg,
+                                    int8_t* q, float* s_out, int32_t* idx, int32_t* count, hipStream_t st);
+
+// Dynamic [-127, 127] row quantization with no outlier columns; *count = 0.
+hipError_t launch_rowquant_i8_no_outliers(const uint16_t* X, int64_t rows, int64_t K, int8_t* q, float* s_out,
+                                          int32_t* count, hipStream_t st);
 
 hipError_t launch_hadamard_quant_i4(const uint16_t* X, int64_t rows, int64_t K, int G,
                                     bool per_group, int qmin, int qmax, uint32_t* packed, float* s,
@@ -44,6 +51,7 @@ struct MixedEpilogue {
     const int32_t* idx;        // outlier list
     const int32_t* count;      // device count
     void* out;
+    int64_t ldo;               // row stride of out, in elements
     int out_dtype;             // 0 f32, 1 f16, 2 bf16
 };
 

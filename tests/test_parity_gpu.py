@@ -255,6 +255,16 @@ def test_mixed_prefill_config_sampled(qa):
     _mixed_case(qa, c["X"], c["W"], c["tau"], c["out_dtype"], c["pass_w16"], rows=rows)
 
 
+@pytest.mark.parametrize("pass_w16", [False, True])
+def test_mixed_tail_split(qa, pass_w16):
+    """More 256 x 256 tiles than whole rounds over the 256 CUs: the trailing
+    output columns go to a second launch of 128 x 128 tiles writing into the
+    same output rows (ragged M and a ragged tail width)."""
+    M, K, N = 300, 128, 129 * 256 + 72
+    X, W, _ = synthetic.mixed_inputs(M, K, N, seed=5, n_dims=3, magnitude=("uniform", 6.0, 60.0))
+    _mixed_case(qa, X, W, 6.0, 1, pass_w16)               # fp16 output
+
+
 def test_mixed_w8a8_config_sampled(qa):
     c = synthetic.config("w8a8_ffn")
     rng = np.random.default_rng(1)
