@@ -788,11 +788,209 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_w4a4(const uint32_t* __rest
     }
 }
 
+// ---------------------------------------------------------------------------
+// W4A4 on the LDS-DMA pipeline: eight waves, wave tile 64 x 64, K advances 64
+// packed bytes (128 elements, two MFMA steps) per stage through four LDS
+// stages.  A lane's fragment of one step is 8 packed bytes (row l % 16, bytes
+// 32 s + 8 (l / 16) of the stage), unpacked into the high nibbles.  The block's
+// per-group weight scales (x 2^-8) are staged in LDS as [group][column] when
+// they fit.  Operands enter the MFMA in the transposed order of the int8 path
+// (lane l, element e: row l % 16, column 4 (l / 16) + e of a fragment).
+// ---------------------------------------------------------------------------
+constexpr int W4D_SW_LDS = 8192;                 // floats of per-group weight scales kept in LDS
+
+template <class C, int G, bool STORE_ACC>
+__device__ __forceinline__ void w4a4_dma_body(const uint32_t* __restrict__ Xp, const float* __restrict__ s_x,
+                                              const uint32_t* __restrict__ Wp, const float* __restrict__ s_w,
+                                              int64_t M, int64_t K, int64_t N, void* __restrict__ out,
+                                              int out_dtype, int tiles_m, int tiles_n, uint8_t* smem, float* sws) {
+    constexpr int SPG = G / 64;                       // MFMA steps per group
+    int tm, tn;
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    const uint32_t kbytes = (uint32_t)(K / 2);        // packed bytes per row
+    const int64_t ng = K / G;
+    const rsrc_t rsa = make_rsrc(reinterpret_cast<const uint8_t*>(Xp) + m0 * kbytes, (M - m0) * kbytes);
+    const rsrc_t rsb = make_rsrc(reinterpret_cast<const uint8_t*>(Wp) + n0 * kbytes, (N - n0) * kbytes);
+
+    const bool sw_in_lds = !STORE_ACC && ng * C::BN <= W4D_SW_LDS;
+    const rsrc_t rsw = make_rsrc(s_w + (STORE_ACC ? 0 : n0 * ng), STORE_ACC ? 0 : (N - n0) * ng * 4);
+    if (sw_in_lds) {
+        for (int t = threadIdx.x; t < ng * C::BN; t += C::THREADS) {
+            const int cc = t / (int)ng, g = t - cc * (int)ng;           // coalesced over g
+            sws[g * C::BN + cc] = __builtin_bit_cast(float, bload4(rsw, (uint32_t)t * 4)) * 0x1p-8f;
+        }
+    }
+    __syncthreads();
+
+    uint32_t oa[C::A_INS], ca[C::A_INS], ob[C::B_INS], cb[C::B_INS];
+#pragma unroll
+    for (int q = 0; q < C::A_INS; ++q) {
+        const int P = (wave * C::A_INS + q) * 64 + lane;
+        const int r = P >> 2, c = (P & 3) ^ ((r >> 1) & 3);
+        oa[q] = (uint32_t)r * kbytes + c * 16;
+        ca[q] = c * 16;
+    }
+#pragma unroll
+    for (int q = 0; q < C::B_INS; ++q) {
+        const int P = (wave * C::B_INS + q) * 64 + lane;
+        const int r = P >> 2, c = (P & 3) ^ ((r >> 1) & 3);
+        ob[q] = (uint32_t)r * kbytes + c * 16;
+        cb[q] = c * 16;
+    }
+    constexpr int PER_STAGE = C::A_INS + C::B_INS;
+    const int nk = (int)((kbytes + C::BK - 1) / C::BK);
+    const int nsteps = (int)(K / 64);
+    auto issue = [&](int kt) __attribute__((always_inline)) {
+        uint8_t* st = smem + (kt % C::STAGES) * C::STAGE;
+        const uint32_t k0 = (uint32_t)kt * C::BK;
+#pragma unroll
+        for (int q = 0; q < C::A_INS; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)(st + (wave * C::A_INS + q) * 1024), 16,
+                                                     k0 + ca[q] < kbytes ? oa[q] + k0 : kOOB, 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < C::B_INS; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void*)(st + C::LDS_A + (wave * C::B_INS + q) * 1024),
+                                                     16, k0 + cb[q] < kbytes ? ob[q] + k0 : kOOB, 0, 0, 0);
+    };
+
+    v4i acc[C::FM][C::FN];
+    v4f f[C::FM][C::FN];
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+            acc[i][j] = v4i{0, 0, 0, 0};
+            f[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        }
+    issue(0);
+    if (nk > 1) issue(1);
+    if (nk > 2) issue(2);
+    for (int kt = 0; kt < nk; ++kt) {
+        const int ahead = (kt + 2 < nk - 1 ? kt + 2 : nk - 1) - kt;   // stages issued after kt
+        if (ahead >= 2)
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PER_STAGE));
+        else if (ahead == 1)
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_STAGE));
+        else
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        block_barrier();
+        if (kt + 3 < nk) issue(kt + 3);
+        const uint8_t* sa = smem + (kt % C::STAGES) * C::STAGE;
+        const uint8_t* sb = sa + C::LDS_A;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const int step = 2 * kt + s2;
+            if (step >= nsteps) break;
+            const int byte = s2 * 32 + (lane >> 4) * 8;
+            const int c = byte >> 4, within = byte & 15;
+            v4i fa[C::FM], fb[C::FN];
+#pragma unroll
+            for (int i = 0; i < C::FM; ++i)
+                fa[i] = unpack_hi_nibbles(
+                    *reinterpret_cast<const u32x2*>(sa + swz64(wm * C::TM + i * 16 + (lane & 15), c) + within));
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+                fb[j] = unpack_hi_nibbles(
+                    *reinterpret_cast<const u32x2*>(sb + swz64(wn * C::TN + j * 16 + (lane & 15), c) + within));
+            // A group of at most two steps starts at a step known at compile
+            // time (step = 2 kt + s2): its first MFMA takes a zero accumulator
+            // instead of clearing the accumulators after each dequant.
+            const bool fresh = SPG <= 2 && (SPG == 1 || s2 == 0);
+#pragma unroll
+            for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fb[j], fa[i], fresh ? v4i{0, 0, 0, 0} : acc[i][j],
+                                                                      0, 0, 0);
+            if ((step + 1) % SPG == 0) {
+                const int g = step / SPG;
+                if constexpr (STORE_ACC) {
+                    int32_t* accp = static_cast<int32_t*>(out);
+#pragma unroll
+                    for (int i = 0; i < C::FM; ++i) {
+                        const int64_t row = m0 + wm * C::TM + i * 16 + (lane & 15);
+#pragma unroll
+                        for (int j = 0; j < C::FN; ++j) {
+                            const int64_t col = n0 + wn * C::TN + j * 16 + 4 * (lane >> 4);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (row < M && col + e < N) accp[(row * N + col + e) * ng + g] = acc[i][j][e] >> 8;
+                            if constexpr (SPG > 2) acc[i][j] = v4i{0, 0, 0, 0};
+                        }
+                    }
+                } else {
+                    v4f swj[C::FN];
+#pragma unroll
+                    for (int j = 0; j < C::FN; ++j) {
+                        const int cl = wn * C::TN + j * 16 + 4 * (lane >> 4);   // block-local column
+                        if (sw_in_lds) {
+                            swj[j] = *reinterpret_cast<const v4f*>(sws + g * C::BN + cl);
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                swj[j][e] = __builtin_bit_cast(float, bload4(rsw, (uint32_t)((cl + e) * ng + g) * 4)) *
+                                            0x1p-8f;
+                        }
+                    }
+#pragma unroll
+                    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+                        for (int j = 0; j < C::FN; ++j) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                f[i][j][e] = __builtin_fmaf((float)acc[i][j][e], swj[j][e], f[i][j][e]);
+                            if constexpr (SPG > 2) acc[i][j] = v4i{0, 0, 0, 0};
+                        }
+                }
+            }
+        }
+    }
+    if constexpr (!STORE_ACC) {
+        const rsrc_t rsx = make_rsrc(s_x + m0, (M - m0) * 4);
+        const bool vec = (N & 3) == 0;
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) {
+            const int rl = wm * C::TM + i * 16 + (lane & 15);
+            const float sx = __builtin_bit_cast(float, bload4(rsx, (uint32_t)rl * 4));
+            const int64_t row = m0 + rl;
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j) {
+                const int64_t col = n0 + wn * C::TN + j * 16 + 4 * (lane >> 4);
+                v4f o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = sx * f[i][j][e];
+                if (row < M && col < N) store_out4(out, out_dtype, row * N + col, o, vec, (int)(N - col < 4 ? N - col : 4));
+            }
+        }
+    }
+}
+
+template <class C, int G, bool STORE_ACC>
+__global__ __launch_bounds__(C::THREADS) void k_gemm_w4a4_dma(const uint32_t* __restrict__ Xp,
+                                                              const float* __restrict__ s_x,
+                                                              const uint32_t* __restrict__ Wp,
+                                                              const float* __restrict__ s_w, int64_t M, int64_t K,
+                                                              int64_t N, void* __restrict__ out, int out_dtype,
+                                                              int tiles_m, int tiles_n) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
+    __shared__ __attribute__((aligned(16))) float sws[STORE_ACC ? 4 : W4D_SW_LDS];
+    w4a4_dma_body<C, G, STORE_ACC>(Xp, s_x, Wp, s_w, M, K, N, out, out_dtype, tiles_m, tiles_n, smem, sws);
+}
+
+using CfgW4 = CfgD<128, 256, 2, 4>;     // 8 waves, wave tile 64 x 64, LDS-DMA stages
+
 template <int G, bool STORE_ACC>
 static void w4a4_dispatch(const uint32_t* Xp, const float* s_x, const uint32_t* Wp, const float* s_w, int64_t M,
                           int64_t K, int64_t N, void* out, int out_dtype, hipStream_t st) {
     int tm, tn;
-    if (((M + 127) / 128) * ((N + 127) / 128) >= 256) {
+    if (((M + 127) / 128) * ((N + 255) / 256) >= 256) {
+        dim3 g = grid_of<CfgW4>(M, N, tm, tn);
+        hipLaunchKernelGGL((k_gemm_w4a4_dma<CfgW4, G, STORE_ACC>), g, dim3(CfgW4::THREADS), 0, st, Xp, s_x, Wp, s_w,
+                           M, K, N, out, out_dtype, tm, tn);
+    } else if (((M + 127) / 128) * ((N + 127) / 128) >= 256) {
         dim3 g = grid_of<CfgMidR>(M, N, tm, tn);
         hipLaunchKernelGGL((k_gemm_w4a4<CfgMidR, G, STORE_ACC>), g, dim3(CfgMidR::THREADS), 0, st, Xp, s_x, Wp, s_w,
                            M, K, N, out, out_dtype, tm, tn);

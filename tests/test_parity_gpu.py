@@ -338,7 +338,10 @@ def test_hadamard_quant_int4_config(qa):
 
 # ============================================================ W4A4 GEMM
 @pytest.mark.parametrize("M,K,N,G", [(1, 64, 1, 64), (20, 256, 33, 128), (64, 384, 64, 128), (130, 512, 70, 256),
-                                     (300, 1024, 500, 64), (2048, 256, 2048, 128)])
+                                     (300, 1024, 500, 64), (2048, 256, 2048, 128),
+                                     # >= 256 tiles of 128 x 256 (eight-wave LDS-DMA kernel), ragged M and N,
+                                     # K ending half-way through a 128-element stage
+                                     (1030, 320, 7976, 64), (2100, 384, 4100, 128), (1100, 512, 7700, 256)])
 def test_w4a4_group_acc(qa, M, K, N, G):
     rng = np.random.default_rng(M + N)
     Xp = rng.integers(0, 2 ** 32, (M, K // 8), dtype=np.uint64).astype(np.uint32)
@@ -357,6 +360,20 @@ def test_w4a4_linear_shapes(qa, M, K, N, G):
     assert np.array_equal(host(Wp).view(np.uint32), oWp)
     out = qa.qa_qlinear_w4a4(dev(X), Wp, s_w, G=G)
     assert_float_parity(as_f64(out), oracle.qlinear_w4a4(X, oWp, os_w, G), torch.float32)
+
+
+@pytest.mark.parametrize("M,K,N,G", [(1030, 320, 7976, 64), (2100, 384, 4100, 128), (1100, 512, 7700, 256)])
+def test_w4a4_linear_large_sampled(qa, M, K, N, G):
+    """Shapes with >= 256 tiles of 128 x 256 (the eight-wave LDS-DMA kernel):
+    ragged M and N, K ending half-way through a stage; sampled rows."""
+    X, W, _ = synthetic.w4a4_inputs(M, K, N, seed=M + G)
+    Wp, s_w = qa.qa_hadamard_quant_int4(dev(W), G, True)
+    oWp, os_w = oracle.hadamard_quant_int4(W, G, True)
+    assert np.array_equal(host(Wp).view(np.uint32), oWp)
+    out = as_f64(qa.qa_qlinear_w4a4(dev(X), Wp, s_w, G=G))
+    rng = np.random.default_rng(M)
+    rows = np.unique(np.concatenate([[0, 127, 128, M - 1], rng.choice(M, 12, replace=False)]))
+    assert_float_parity(out[rows], oracle.qlinear_w4a4(X, oWp, os_w, G, rows=rows), torch.float32)
 
 
 def test_w4a4_config_sampled(qa):
