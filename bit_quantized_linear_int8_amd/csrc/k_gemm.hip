@@ -526,7 +526,7 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_i8_mixed(const int8_t* __re
 }
 
 using CfgBig = CfgD<256, 256, 2, 4>;   // 8 waves, wave tile 128 x 64, LDS-DMA stages
-using CfgTail = CfgD<256, 128, 2, 4>;  // 8 waves, wave tile 128 x 32, LDS-DMA stages
+using CfgTail = CfgD<128, 256, 2, 4>;  // 8 waves, wave tile 64 x 64, LDS-DMA stages
 using CfgMid = Cfg<128, 128, 2, 2>;    // 4 waves, wave tile 64 x 64 (register-staged)
 using CfgMidR = CfgMid;
 using CfgSmall = Cfg<64, 64, 2, 2>;    // 4 waves, wave tile 32 x 32
@@ -571,7 +571,7 @@ hipError_t launch_gemm_i8_i32(const int8_t* A, const int8_t* B, int64_t M, int64
 }
 
 // Output columns [0, split) get 256 x 256 tiles in whole rounds over the 256
-// CUs, the rest a second launch of 256 x 128 tiles: without it the last
+// CUs, the rest a second launch of 128 x 256 tiles: without it the last
 // partial round of big tiles leaves most CUs idle.
 // Returns 0 when no split helps.
 static int64_t tail_split(int64_t M, int64_t N) {

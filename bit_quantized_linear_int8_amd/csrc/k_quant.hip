@@ -284,6 +284,18 @@ __global__ __launch_bounds__(256) void k_rowquant_i8(const uint16_t* __restrict_
     __shared__ unsigned long long flw[MASK == MASK_FLAGS ? RQ_FLAG_WORDS : 1];
     __shared__ int wsum[4];
     const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + wave_id();
+    const bool live = row < rows;
+    const int64_t nch = K >> 3;
+    const rsrc_t rx = make_rsrc(X + (live ? row : 0) * K, live ? K * 2 : 0);
+    // A row held in registers is loaded before the flag merge below, so the
+    // two latencies overlap (loads retire in order: waiting for the flag
+    // words also waits for these).
+    u32x4 vpre[NC > 0 ? NC : 1];
+    if constexpr (NC > 0) {
+#pragma unroll
+        for (int i = 0; i < NC; ++i) vpre[i] = bload16(rx, (uint32_t)(lane + 64 * i) * 16);
+    }
     if constexpr (MASK == MASK_FLAGS) {
         const uint32_t b = threadIdx.x;              // keep words of an 8-bit outlier pattern
         u32x4 k;
@@ -309,10 +321,7 @@ __global__ __launch_bounds__(256) void k_rowquant_i8(const uint16_t* __restrict_
     }
     if constexpr (MASK == MASK_NONE)
         if (count && blockIdx.x == 0 && threadIdx.x == 0) *count = 0;
-    const int64_t row = (int64_t)blockIdx.x * 4 + wave_id();
-    if (row >= rows) return;
-    const int64_t nch = K >> 3;
-    const rsrc_t rx = make_rsrc(X + row * K, K * 2);
+    if (!live) return;
     const rsrc_t rm = make_rsrc(mask, MASK == MASK_BYTES ? K : 0);
     const uint8_t* flb = reinterpret_cast<const uint8_t*>(flw);
     int8_t* qr = q + row * K;
@@ -323,17 +332,23 @@ __global__ __launch_bounds__(256) void k_rowquant_i8(const uint16_t* __restrict_
         z = z_in ? z_in[row] : 0;
     }
     // chunk ch: fp16 bits with MASK_FLAGS already applied, byte mask for MASK_BYTES
-    auto load = [&](int64_t ch, u32x4& v, u32x2& mk) {
-        v = bload16(rx, (uint32_t)ch * 16);
+    auto mask_of = [&](int64_t ch, u32x4& v, u32x2& mk) {
         mk = u32x2{0u, 0u};
         if constexpr (MASK == MASK_FLAGS) v &= lut[ch < nch ? flb[ch] : 0];
         if constexpr (MASK == MASK_BYTES) mk = bload8(rm, (uint32_t)ch * 8);
+    };
+    auto load = [&](int64_t ch, u32x4& v, u32x2& mk) {
+        v = bload16(rx, (uint32_t)ch * 16);
+        mask_of(ch, v, mk);
     };
     if constexpr (NC > 0) {
         u32x4 v[NC];
         u32x2 mk[NC];
 #pragma unroll
-        for (int i = 0; i < NC; ++i) load(lane + 64 * i, v[i], mk[i]);
+        for (int i = 0; i < NC; ++i) {
+            v[i] = vpre[i];
+            mask_of(lane + 64 * i, v[i], mk[i]);
+        }
         if constexpr (!STATIC) {
             float amax = 0.0f;
 #pragma unroll
