@@ -7,8 +7,9 @@ It shares no code with the GPU library ``bit_quantized_linear_int8_amd``.
 
 Every function follows the page passages cited in ``oracle.c``:
 LLM.int8() (AIInfra 05Quantization01; Quantization explained part 2, §1.2),
-scale / zero-point / group granularity (模型推理量化 §4-§7) and the group
-Hadamard W4A4 scheme (分组旋转方法从W8A8到W4A4, §二, §5.1-§5.4).
+scale / zero-point / group granularity (模型推理量化 §4-§7), the group
+Hadamard W4A4 scheme (分组旋转方法从W8A8到W4A4, §二, §5.1-§5.4) and the
+SmoothQuant migration (Quantization explained part 2, §4.2).
 """
 from __future__ import annotations
 
@@ -58,6 +59,11 @@ def lib() -> ctypes.CDLL:
             "orc_quant_rows_f16": (None, [P, I64, I64, I64, P, I32, I32, P, P, P, P]),
             "orc_gemm_i8_i32": (I64, [P, P, I64, I64, I64, P, I64, P]),
             "orc_qlinear_int8_mixed": (None, [P, I64, I64, P, P, P, I64, F, P, I64, P]),
+            "orc_col_absmax_f32": (None, [P, I64, I64, P]),
+            "orc_smooth_factors": (None, [P, P, I64, ctypes.c_double, P]),
+            "orc_smooth_apply_f32": (None, [P, I64, I64, P, ctypes.c_int, P]),
+            "orc_smooth_quant_f32": (None, [P, I64, I64, P, ctypes.c_int, ctypes.c_int, P, P]),
+            "orc_qlinear_int8_smooth": (None, [P, I64, I64, P, ctypes.c_int, P, P, I64, P, I64, P]),
             "orc_hadamard_entry": (ctypes.c_int, [I32, I32]),
             "orc_hadamard_rows": (None, [P, I64, I64, I32, P]),
             "orc_pack_int4": (None, [P, I64, I64, P]),
@@ -182,6 +188,72 @@ def qlinear_int8_mixed(X16, Wq, s_w, W16=None, tau=6.0, rows=None):
     out = np.zeros((nr if r is not None else M, N), np.float64)
     lib().orc_qlinear_int8_mixed(_ptr(h), M, K, _ptr(Wq), _ptr(sw), _ptr(w16), N, float(tau),
                                  _ptr(r), nr, _ptr(out))
+    return out
+
+
+# ---------------------------------------------------------------- SmoothQuant
+SMOOTH_DIVIDE, SMOOTH_MULTIPLY = 0, 1
+
+
+def _f32_matrix(a):
+    """fp16 (widened exactly) or fp32 matrix as contiguous fp32 [rows x K]."""
+    a = np.asarray(a)
+    if a.ndim == 1:
+        a = a[None, :]
+    return f16_to_f32(a) if a.dtype == np.float16 else _c(a, np.float32)
+
+
+def col_absmax(A):
+    """max_r |A[r, j]| per column of an fp16 or fp32 matrix -> f32 [K]."""
+    a = _f32_matrix(A)
+    rows, K = a.shape
+    out = np.zeros(K, np.float32)
+    lib().orc_col_absmax_f32(_ptr(a), rows, K, _ptr(out))
+    return out
+
+
+def smooth_factors(cx, cw, alpha=0.5):
+    """Migration factors s_j = cx_j^alpha / cw_j^(1-alpha) (1 where a max is 0) -> f32 [K]."""
+    cx = _c(cx, np.float32)
+    cw = _c(cw, np.float32)
+    s = np.zeros(cx.size, np.float32)
+    lib().orc_smooth_factors(_ptr(cx), _ptr(cw), cx.size, float(alpha), _ptr(s))
+    return s
+
+
+def smooth_apply(A, s, op):
+    """A / s (SMOOTH_DIVIDE, activations) or A * s (SMOOTH_MULTIPLY, weights) per column, fp32."""
+    a = _f32_matrix(A)
+    rows, K = a.shape
+    sv = _c(s, np.float32)
+    out = np.zeros((rows, K), np.float32)
+    lib().orc_smooth_apply_f32(_ptr(a), rows, K, _ptr(sv), int(op), _ptr(out))
+    return out
+
+
+def smooth_quantize(A, s, op, per_tensor=False):
+    """Smoothing + [-127, 127] absmax codes -> (codes i8 [rows x K], scales f32 [rows])."""
+    a = _f32_matrix(A)
+    rows, K = a.shape
+    sv = _c(s, np.float32)
+    q = np.zeros((rows, K), np.int8)
+    s_out = np.zeros(rows, np.float32)
+    lib().orc_smooth_quant_f32(_ptr(a), rows, K, _ptr(sv), int(op), int(bool(per_tensor)), _ptr(q), _ptr(s_out))
+    return q, s_out
+
+
+def qlinear_int8_smooth(X16, s, Wq, s_w, per_tensor=False, rows=None):
+    """SmoothQuant W8A8 linear in fp64: [nrows x N] (all rows if rows is None)."""
+    h = _h16(X16)
+    M, K = h.shape
+    sv = _c(s, np.float32)
+    Wq = _c(Wq, np.int8)
+    N = Wq.shape[0]
+    sw = _c(s_w, np.float32)
+    r, nr = _rows(rows)
+    out = np.zeros((nr if r is not None else M, N), np.float64)
+    lib().orc_qlinear_int8_smooth(_ptr(h), M, K, _ptr(sv), int(bool(per_tensor)), _ptr(Wq), _ptr(sw), N,
+                                  _ptr(r), nr, _ptr(out))
     return out
 
 

@@ -25,7 +25,9 @@
  *                  word and int32 accumulation.
  *   [QE2]          "Quantization explained, part 2" (tanjunchen.github.io):
  *                  §1.2, threshold 6.0 on a channel's activation magnitude and
- *                  the 4096-wide row with one value of 70.
+ *                  the 4096-wide row with one value of 70; §4.2 SmoothQuant,
+ *                  the per-input-channel migration Y = (X diag(s)^-1)(diag(s) W)
+ *                  with s_j = max|X_j|^alpha / max|W_j|^(1-alpha).
  *
  * Arithmetic rules (the pages leave these open; the readings are fixed here):
  *   - fp16 inputs are widened exactly; all float reductions are fp64.
@@ -38,6 +40,10 @@
  *     fp64 multiply by fl64(1/sqrt(G)) and one rounding to fp32.
  *   - int4 packing: element 8w+i of a row sits in bits [4i+3:4i] of word w,
  *     two's complement.
+ *   - SmoothQuant: s_j = fl32(pow(cx_j, alpha) / pow(cw_j, 1 - alpha)) in
+ *     fp64, and s_j = 1 when cx_j or cw_j is 0 (the formula is undefined or
+ *     zero there).  Activations become fl32(x / s_j), weights fl32(w * s_j),
+ *     one IEEE fp32 operation each, before the absmax quantizer.
  */
 #include <math.h>
 #include <stdint.h>
@@ -304,6 +310,104 @@ void orc_qlinear_int8_mixed(const uint16_t* X, int64_t M, int64_t K,
     free(wt);
     free(idx);
     free(mask);
+}
+
+/* ---------------------------------------------------------------------------
+ * SmoothQuant  [QE2 §4.2]
+ * Equivalent per-input-channel scaling: column j of X is divided by s_j and
+ * column j of the weight (row j of the page's W, column j of our [N x K]
+ * layout) is multiplied by s_j, so X W^T is unchanged in exact arithmetic.
+ * ------------------------------------------------------------------------- */
+
+/* colmax[j] = max_r |a[r][j]| (0 when rows == 0). */
+void orc_col_absmax_f32(const float* a, int64_t rows, int64_t K, float* colmax)
+{
+    for (int64_t j = 0; j < K; ++j)
+        colmax[j] = 0.0f;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t j = 0; j < K; ++j) {
+            float v = fabsf(a[r * K + j]);
+            if (v > colmax[j])
+                colmax[j] = v;
+        }
+}
+
+/* s_j = cx_j^alpha / cw_j^(1-alpha); 1 when either maximum is 0. */
+void orc_smooth_factors(const float* cx, const float* cw, int64_t K, double alpha, float* s)
+{
+    for (int64_t j = 0; j < K; ++j) {
+        if (cx[j] == 0.0f || cw[j] == 0.0f) {
+            s[j] = 1.0f;
+            continue;
+        }
+        double num = pow((double)cx[j], alpha);
+        double den = pow((double)cw[j], 1.0 - alpha);
+        s[j] = (float)(num / den);
+    }
+}
+
+/* out = a / s (op 0, activations) or a * s (op 1, weights), per column. */
+void orc_smooth_apply_f32(const float* a, int64_t rows, int64_t K, const float* s, int op, float* out)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t j = 0; j < K; ++j) {
+            float v = a[r * K + j];
+            out[r * K + j] = op == 0 ? v / s[j] : v * s[j];
+        }
+}
+
+/* Smoothing followed by symmetric [-127, 127] absmax quantization with one
+ * scale per row (per_tensor == 0) or one scale for the whole matrix, written
+ * to every s_out[r] (per_tensor != 0). */
+void orc_smooth_quant_f32(const float* a, int64_t rows, int64_t K, const float* s, int op, int per_tensor,
+                          int8_t* q, float* s_out)
+{
+    size_t n = (size_t)(rows * K > 0 ? rows * K : 1);
+    float* h = (float*)malloc(sizeof(float) * n);
+    orc_smooth_apply_f32(a, rows, K, s, op, h);
+    if (!per_tensor) {
+        orc_quant_rows_f32(h, rows, K, K, NULL, -127, 127, NULL, NULL, q, s_out);
+    } else {
+        float m = 0.0f;
+        for (int64_t i = 0; i < rows * K; ++i)
+            if (fabsf(h[i]) > m)
+                m = fabsf(h[i]);
+        float st = (m == 0.0f) ? 1.0f : m / 127.0f;
+        for (int64_t r = 0; r < rows; ++r)
+            s_out[r] = st;
+        orc_quant_rows_f32(h, rows, K, K, NULL, -127, 127, s_out, NULL, q, NULL);
+    }
+    free(h);
+}
+
+/* SmoothQuant W8A8 linear: Xs = X / s, activation codes and scales from
+ * orc_smooth_quant_f32, C = Xq Wq^T (int32), out = C * s_x[m] * s_w[n].
+ * Wq, s_w come from the smoothed weight (op 1).  Output fp64 [nrows x N]. */
+void orc_qlinear_int8_smooth(const uint16_t* X, int64_t M, int64_t K, const float* s, int per_tensor,
+                             const int8_t* Wq, const float* s_w, int64_t N, const int64_t* rows, int64_t nrows,
+                             double* out)
+{
+    if (!rows)
+        nrows = M;
+    size_t n = (size_t)(M * K > 0 ? M * K : 1);
+    float* xf = (float*)malloc(sizeof(float) * n);
+    int8_t* xq = (int8_t*)malloc(n);
+    float* s_x = (float*)malloc(sizeof(float) * (size_t)(M > 0 ? M : 1));
+    orc_f16_to_f32_array(X, M * K, xf);
+    orc_smooth_quant_f32(xf, M, K, s, 0, per_tensor, xq, s_x);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t ri = 0; ri < nrows; ++ri) {
+        int64_t m = rows ? rows[ri] : ri;
+        for (int64_t nn = 0; nn < N; ++nn) {
+            int64_t c = 0;
+            for (int64_t k = 0; k < K; ++k)
+                c += (int64_t)xq[m * K + k] * (int64_t)Wq[nn * K + k];
+            out[ri * N + nn] = (double)c * (double)s_x[m] * (double)s_w[nn];
+        }
+    }
+    free(s_x);
+    free(xq);
+    free(xf);
 }
 
 /* ---------------------------------------------------------------------------

@@ -88,6 +88,20 @@ def w4a4_inputs(M, K, N, seed=0, n_dims=6, x_mag=50.0, w_std=0.02, w_spike_p=0.0
     return _f16(X64), W, dims
 
 
+def smoothquant_toy(T=32, C_in=16, C_out=8, outlier_channel=3, outlier_gain=60.0, w_gain=0.1, seed=0):
+    """The SmoothQuant demonstration inputs of "Quantization explained, part 2"
+    §4.5: torch's CPU generator seeded with `seed` draws X [T x C_in] (standard
+    normal; one channel scaled by outlier_gain), then W [C_in x C_out] (standard
+    normal times w_gain).  Returns float32 numpy arrays X and W in the page's
+    layout (W is [in x out])."""
+    import torch
+    g = torch.Generator().manual_seed(seed)
+    X = torch.randn(T, C_in, generator=g)
+    X[:, outlier_channel] *= outlier_gain
+    W = torch.randn(C_in, C_out, generator=g) * w_gain
+    return X.numpy().astype(np.float32), W.numpy().astype(np.float32)
+
+
 def config(name: str) -> dict:
     """The five workloads at full size.  Keys: X (fp16 [M x K]), W (fp16
     [N x K]), dims (planted outlier dims), tau, out_dtype, G, pass_w16, M, K, N."""

@@ -398,3 +398,167 @@ def test_rotation_lowers_w4a4_error():
     qw, sw = oracle.quant_rows(W, gsize=128, qmin=-7, qmax=7)
     plain = (qx * sx.astype(np.float64)) @ (qw * np.repeat(sw.astype(np.float64), 128, axis=1)).T
     assert err_rot < np.abs(plain - exact).mean() / 2
+
+
+# ------------------------------------------------------------------ SmoothQuant
+def _f32_ulp(x):
+    x = np.abs(np.asarray(x, np.float32))
+    return np.spacing(x).astype(np.float64)
+
+
+def test_smoothquant_page_example():
+    """The printed demonstration of "Quantization explained, part 2" §4.5:
+    per-tensor W8A8 error 0.108 without and 0.054 with alpha = 0.5 smoothing,
+    and an equivalence error of order 1e-6."""
+    g = golden("smoothquant_toy.json")
+    X, W = synthetic.smoothquant_toy(g["T"], g["C_in"], g["C_out"], g["outlier_channel"], g["outlier_gain"],
+                                     g["w_gain"], g["seed"])
+    Wt = np.ascontiguousarray(W.T)                     # our layout: [out x in]
+    Y = X.astype(np.float64) @ W.astype(np.float64)
+    s = oracle.smooth_factors(oracle.col_absmax(X), oracle.col_absmax(Wt), g["alpha"])
+    Xh = oracle.smooth_apply(X, s, oracle.SMOOTH_DIVIDE)
+    Wh = oracle.smooth_apply(Wt, s, oracle.SMOOTH_MULTIPLY)
+    eq = np.abs(Xh.astype(np.float64) @ Wh.astype(np.float64).T - Y).max()
+    assert eq < 10 * g["equivalence_printed_order"]
+
+    def w8a8_err(sv):
+        qx, sx = oracle.smooth_quantize(X, sv, oracle.SMOOTH_DIVIDE, per_tensor=True)
+        qw, sw = oracle.smooth_quantize(Wt, sv, oracle.SMOOTH_MULTIPLY, per_tensor=True)
+        deq_x = qx.astype(np.float64) * sx.astype(np.float64)[:, None]
+        deq_w = qw.astype(np.float64) * sw.astype(np.float64)[:, None]
+        return np.abs(Y - deq_x @ deq_w.T).mean()
+
+    d = g["printed_digits"]
+    assert round(w8a8_err(np.ones(g["C_in"], np.float32)), d) == g["err_raw_printed"]
+    assert round(w8a8_err(s), d) == g["err_smooth_printed"]
+
+
+@pytest.mark.parametrize("alpha", [0.25, 0.5, 0.75])
+def test_smooth_column_maxima_closed_form(alpha):
+    """After migration the column maxima are cx^(1-a) cw^(1-a) (activations)
+    and cx^a cw^a (weights); at a = 0.5 both equal sqrt(cx cw)."""
+    X, W, _ = synthetic.mixed_inputs(64, 256, 48, seed=21, n_dims=4)
+    cx = np.abs(X.astype(np.float64)).max(axis=0)
+    cw = np.abs(W.astype(np.float64)).max(axis=0)
+    s = oracle.smooth_factors(oracle.col_absmax(X), oracle.col_absmax(W), alpha)
+    mx = np.abs(oracle.smooth_apply(X, s, oracle.SMOOTH_DIVIDE)).max(axis=0)
+    mw = np.abs(oracle.smooth_apply(W, s, oracle.SMOOTH_MULTIPLY)).max(axis=0)
+    ex = cx ** (1 - alpha) * cw ** (1 - alpha)
+    ew = cx ** alpha * cw ** alpha
+    # s carries one fp32 rounding, the applied value another
+    assert np.all(np.abs(mx - ex) <= 2.5 * 2.0 ** -24 * ex)
+    assert np.all(np.abs(mw - ew) <= 2.5 * 2.0 ** -24 * ew)
+    if alpha == 0.5:
+        assert np.all(np.abs(mx - mw) <= 5 * 2.0 ** -24 * ex)
+
+
+def test_smooth_alpha_extremes():
+    """alpha = 1 moves all of the range into the weight (activation column
+    maxima become exactly 1); alpha = 0 gives s = 1/max|W_j| (weight column
+    maxima 1 up to one rounding), as the formula reads."""
+    X, W, _ = synthetic.mixed_inputs(32, 128, 40, seed=22, n_dims=3)
+    cx, cw = oracle.col_absmax(X), oracle.col_absmax(W)
+    s1 = oracle.smooth_factors(cx, cw, 1.0)
+    assert np.array_equal(s1, cx)
+    assert np.array_equal(np.abs(oracle.smooth_apply(X, s1, oracle.SMOOTH_DIVIDE)).max(axis=0), np.ones(128, np.float32))
+    s0 = oracle.smooth_factors(cx, cw, 0.0)
+    assert np.array_equal(s0, (np.float32(1) / cw).astype(np.float32))
+    mw = np.abs(oracle.smooth_apply(W, s0, oracle.SMOOTH_MULTIPLY)).max(axis=0).astype(np.float64)
+    assert np.all(np.abs(mw - 1.0) <= 2.0 ** -23)
+
+
+def test_col_absmax_matches_numpy():
+    X, W, _ = synthetic.mixed_inputs(37, 200, 11, seed=23, n_dims=2)
+    assert np.array_equal(oracle.col_absmax(X), np.abs(X.astype(np.float32)).max(axis=0))
+    assert np.array_equal(oracle.col_absmax(W), np.abs(W.astype(np.float32)).max(axis=0))
+
+
+def test_smooth_zero_columns_keep_factor_one():
+    cx = np.array([0.0, 3.0, 0.0, 2.0], np.float32)
+    cw = np.array([1.0, 0.0, 0.0, 0.5], np.float32)
+    s = oracle.smooth_factors(cx, cw, 0.5)
+    assert np.array_equal(s[:3], np.ones(3, np.float32))
+    assert s[3] == np.float32(2.0)                                        # sqrt(2 / 0.5)
+
+
+def test_smoothing_is_an_equivalence_within_rounding():
+    """X^ W^T = X W^T up to the two fp32 roundings of each smoothed operand:
+    x/s (1 + d1) * w s (1 + d2), |d1|, |d2| <= 2^-24."""
+    X, W, _ = synthetic.mixed_inputs(48, 512, 64, seed=24, n_dims=5)
+    s = oracle.smooth_factors(oracle.col_absmax(X), oracle.col_absmax(W), 0.5)
+    Xh = oracle.smooth_apply(X, s, oracle.SMOOTH_DIVIDE).astype(np.float64)
+    Wh = oracle.smooth_apply(W, s, oracle.SMOOTH_MULTIPLY).astype(np.float64)
+    X64, W64 = X.astype(np.float64), W.astype(np.float64)
+    bound = (2 * 2.0 ** -24 + 2.0 ** -47) * (np.abs(X64) @ np.abs(W64).T) * (1 + 1e-12)
+    assert np.all(np.abs(Xh @ Wh.T - X64 @ W64.T) <= bound)
+    # a dropped factor on one side breaks it
+    assert not np.all(np.abs(X64 @ Wh.T - X64 @ W64.T) <= bound)
+
+
+def test_smooth_quantize_scales():
+    """Per-row scales are the absmax quantizer of the smoothed rows; the
+    per-tensor scale is the largest per-row scale (fl32(a/127) is monotone),
+    broadcast to every row."""
+    X, W, _ = synthetic.mixed_inputs(30, 256, 8, seed=25, n_dims=3)
+    s = oracle.smooth_factors(oracle.col_absmax(X), oracle.col_absmax(W), 0.5)
+    Xh = oracle.smooth_apply(X, s, oracle.SMOOTH_DIVIDE)
+    a = np.abs(Xh).max(axis=1)
+    q, sr = oracle.smooth_quantize(X, s, oracle.SMOOTH_DIVIDE)
+    assert np.array_equal(sr, (a / np.float32(127)).astype(np.float32))
+    assert np.array_equal(q, np.clip(np.rint(Xh / sr[:, None]), -127, 127).astype(np.int8))
+    qt, st_ = oracle.smooth_quantize(X, s, oracle.SMOOTH_DIVIDE, per_tensor=True)
+    assert np.all(st_ == sr.max())
+    assert np.array_equal(qt, np.clip(np.rint(Xh / st_[0]), -127, 127).astype(np.int8))
+
+
+def test_smooth_linear_with_unit_factors_is_vectorwise_w8a8():
+    X, W, _ = synthetic.mixed_inputs(24, 512, 40, seed=26, n_dims=3)
+    one = np.ones(512, np.float32)
+    Wq, s_w = oracle.smooth_quantize(W, one, oracle.SMOOTH_MULTIPLY)
+    Wq_ref, s_w_ref = _w8(W)
+    assert np.array_equal(Wq, Wq_ref) and np.array_equal(s_w, s_w_ref)
+    out = oracle.qlinear_int8_smooth(X, one, Wq, s_w)
+    assert np.array_equal(out, oracle.qlinear_int8_mixed(X, Wq, s_w, tau=float("inf")))
+
+
+@pytest.mark.parametrize("e", [-3, 5])
+def test_smooth_linear_power_of_two_factor_changes_nothing(e):
+    """A uniform factor 2^e scales X^ and W^ exactly, so codes are unchanged and
+    s_x s_w is the same product: the output is identical."""
+    X, W, _ = synthetic.mixed_inputs(20, 256, 30, seed=27, n_dims=2)
+    one = np.ones(256, np.float32)
+    p2 = np.full(256, 2.0 ** e, np.float32)
+    for per_tensor in (False, True):
+        Wq1, sw1 = oracle.smooth_quantize(W, one, oracle.SMOOTH_MULTIPLY)
+        Wq2, sw2 = oracle.smooth_quantize(W, p2, oracle.SMOOTH_MULTIPLY)
+        assert np.array_equal(Wq1, Wq2)
+        a = oracle.qlinear_int8_smooth(X, one, Wq1, sw1, per_tensor=per_tensor)
+        b = oracle.qlinear_int8_smooth(X, p2, Wq2, sw2, per_tensor=per_tensor)
+        assert np.array_equal(a, b)
+
+
+def test_smooth_linear_matches_integer_matmul_composition():
+    X, W, _ = synthetic.mixed_inputs(9, 128, 13, seed=28, n_dims=2)
+    s = oracle.smooth_factors(oracle.col_absmax(X), oracle.col_absmax(W), 0.5)
+    Wq, s_w = oracle.smooth_quantize(W, s, oracle.SMOOTH_MULTIPLY)
+    for per_tensor in (False, True):
+        qx, sx = oracle.smooth_quantize(X, s, oracle.SMOOTH_DIVIDE, per_tensor=per_tensor)
+        C = qx.astype(np.int64) @ Wq.astype(np.int64).T
+        ref = C.astype(np.float64) * sx.astype(np.float64)[:, None] * s_w.astype(np.float64)[None, :]
+        out = oracle.qlinear_int8_smooth(X, s, Wq, s_w, per_tensor=per_tensor)
+        assert np.array_equal(out, ref)
+        rows = np.array([8, 0, 3])
+        assert np.array_equal(oracle.qlinear_int8_smooth(X, s, Wq, s_w, per_tensor, rows=rows), out[rows])
+
+
+@pytest.mark.parametrize("per_tensor", [False, True])
+def test_smoothing_lowers_w8a8_error_on_outlier_activations(per_tensor):
+    X, W, _ = synthetic.mixed_inputs(64, 1024, 96, seed=29, n_dims=6, magnitude=("uniform", 20.0, 100.0))
+    exact = X.astype(np.float64) @ W.astype(np.float64).T
+    one = np.ones(1024, np.float32)
+    s = oracle.smooth_factors(oracle.col_absmax(X), oracle.col_absmax(W), 0.5)
+    errs = []
+    for sv in (one, s):
+        Wq, s_w = oracle.smooth_quantize(W, sv, oracle.SMOOTH_MULTIPLY)
+        errs.append(np.abs(oracle.qlinear_int8_smooth(X, sv, Wq, s_w, per_tensor=per_tensor) - exact).mean())
+    assert errs[1] < errs[0] / 2
