@@ -18,13 +18,16 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqa.so")
 
 QA_F32, QA_F16, QA_BF16 = 0, 1, 2
-QA_SCALE_PER_ROW, QA_SCALE_PER_GROUP = 0, 1
+QA_SCALE_PER_ROW, QA_SCALE_PER_GROUP, QA_SCALE_PER_TENSOR = 0, 1, 2
+QA_SMOOTH_DIVIDE, QA_SMOOTH_MULTIPLY = 0, 1
 
 EXPORTS = (
     "qa_status_string", "qa_last_error",
     "qa_outlier_cols_workspace", "qa_outlier_cols",
     "qa_quantize_rowwise_int8",
     "qa_qlinear_int8_mixed_workspace", "qa_qlinear_int8_mixed",
+    "qa_col_absmax_workspace", "qa_col_absmax", "qa_smooth_factors", "qa_quantize_smooth_int8",
+    "qa_qlinear_int8_smooth_workspace", "qa_qlinear_int8_smooth",
     "qa_hadamard_quant_int4",
     "qa_qlinear_w4a4_workspace", "qa_qlinear_w4a4",
     "qa_gemm_i8_i32", "qa_gemm_w4a4_group_acc",
@@ -60,6 +63,12 @@ def lib() -> ctypes.CDLL:
             "qa_quantize_rowwise_int8": (S, [P, I64, I64, P, I32, I32, P, P, P, P, P]),
             "qa_qlinear_int8_mixed_workspace": (SZ, [I64, I64]),
             "qa_qlinear_int8_mixed": (S, [P, I64, I64, P, P, P, I64, F, P, S, P, SZ, P]),
+            "qa_col_absmax_workspace": (SZ, [I64]),
+            "qa_col_absmax": (S, [P, I64, I64, P, S, P, SZ, P]),
+            "qa_smooth_factors": (S, [P, P, I64, F, P, P]),
+            "qa_quantize_smooth_int8": (S, [P, I64, I64, P, S, S, P, P, P]),
+            "qa_qlinear_int8_smooth_workspace": (SZ, [I64, I64]),
+            "qa_qlinear_int8_smooth": (S, [P, I64, I64, P, S, P, P, I64, P, S, P, SZ, P]),
             "qa_hadamard_quant_int4": (S, [P, I64, I64, I32, S, I32, I32, P, P, P]),
             "qa_qlinear_w4a4_workspace": (SZ, [I64, I64]),
             "qa_qlinear_w4a4": (S, [P, I64, I64, P, P, I64, I32, P, S, P, SZ, P]),
@@ -165,6 +174,76 @@ def qa_qlinear_int8_mixed(X, Wq, s_w, W16=None, threshold=6.0, out_dtype=torch.f
     _check("qa_qlinear_int8_mixed",
            lib().qa_qlinear_int8_mixed(_p(X), M, K, _p(Wq), _p(s_w), _p(W16), N, float(threshold), _p(out),
                                        _DTYPE_CODE[out.dtype], _p(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def qa_col_absmax_workspace(K: int) -> int:
+    return int(lib().qa_col_absmax_workspace(K))
+
+
+def qa_col_absmax(A, colmax=None, accumulate=False, scratch=None, stream=None):
+    """Column absolute maxima of A fp16 [rows x K] -> colmax f32 [K] (maxed into
+    the given colmax when accumulate)."""
+    _dev(A, "A", torch.float16)
+    rows, K = A.shape
+    if colmax is None:
+        if accumulate:
+            raise ValueError("accumulate needs the running colmax")
+        colmax = torch.empty(K, dtype=torch.float32, device=A.device)
+    _dev(colmax, "colmax", torch.float32)
+    scratch = _workspace(qa_col_absmax_workspace(K), A.device, scratch)
+    _check("qa_col_absmax", lib().qa_col_absmax(_p(A), rows, K, _p(colmax), int(bool(accumulate)), _p(scratch),
+                                                 scratch.numel(), _stream(stream)))
+    return colmax
+
+
+def qa_smooth_factors(act_absmax, w_absmax, alpha=0.5, stream=None):
+    """SmoothQuant migration factors -> s f32 [K]."""
+    _dev(act_absmax, "act_absmax", torch.float32)
+    _dev(w_absmax, "w_absmax", torch.float32)
+    K = act_absmax.numel()
+    if w_absmax.numel() != K:
+        raise ValueError("act_absmax and w_absmax differ in length")
+    s = torch.empty(K, dtype=torch.float32, device=act_absmax.device)
+    _check("qa_smooth_factors", lib().qa_smooth_factors(_p(act_absmax), _p(w_absmax), K, float(alpha), _p(s),
+                                                         _stream(stream)))
+    return s
+
+
+def qa_quantize_smooth_int8(A, s, multiply=False, per_tensor=False, stream=None):
+    """Smoothing (A / s, or A * s for a weight) + int8 absmax codes -> (q i8 [rows x K], s_out f32 [rows])."""
+    _dev(A, "A", torch.float16)
+    _dev(s, "s", torch.float32)
+    rows, K = A.shape
+    q = torch.empty((rows, K), dtype=torch.int8, device=A.device)
+    s_out = torch.empty(rows, dtype=torch.float32, device=A.device)
+    _check("qa_quantize_smooth_int8",
+           lib().qa_quantize_smooth_int8(_p(A), rows, K, _p(s), QA_SMOOTH_MULTIPLY if multiply else QA_SMOOTH_DIVIDE,
+                                         QA_SCALE_PER_TENSOR if per_tensor else QA_SCALE_PER_ROW, _p(q), _p(s_out),
+                                         _stream(stream)))
+    return q, s_out
+
+
+def qa_qlinear_int8_smooth_workspace(M: int, K: int) -> int:
+    return int(lib().qa_qlinear_int8_smooth_workspace(M, K))
+
+
+def qa_qlinear_int8_smooth(X, s, Wq, s_w, per_tensor=False, out_dtype=torch.float16, out=None, workspace=None,
+                           stream=None):
+    """SmoothQuant W8A8 linear -> out [M x N] of out_dtype."""
+    _dev(X, "X", torch.float16)
+    _dev(s, "s", torch.float32)
+    _dev(Wq, "Wq", torch.int8)
+    _dev(s_w, "s_w", torch.float32)
+    M, K = X.shape
+    N = Wq.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=X.device)
+    workspace = _workspace(qa_qlinear_int8_smooth_workspace(M, K), X.device, workspace)
+    _check("qa_qlinear_int8_smooth",
+           lib().qa_qlinear_int8_smooth(_p(X), M, K, _p(s), QA_SCALE_PER_TENSOR if per_tensor else QA_SCALE_PER_ROW,
+                                        _p(Wq), _p(s_w), N, _p(out), _DTYPE_CODE[out.dtype], _p(workspace),
+                                        workspace.numel(), _stream(stream)))
     return out
 
 

@@ -207,6 +207,31 @@ hipError_t launch_outlier_flags(const uint16_t* X, int64_t M, int64_t K, float t
     return hipGetLastError();
 }
 
+// Column absolute maxima (the activation and weight statistics of the
+// SmoothQuant migration): the scan above with no threshold, then one thread
+// per column maxes the segments' partial maxima (and the caller's running
+// maximum when accumulating; non-negative floats order like their bits).
+__global__ __launch_bounds__(256) void k_colmax_merge(const uint32_t* __restrict__ cmax_p, int nseg, int64_t K,
+                                                      float* __restrict__ colmax, int accumulate) {
+    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (j >= K) return;
+    uint32_t m = accumulate ? __builtin_bit_cast(uint32_t, colmax[j]) : 0u;
+#pragma unroll
+    for (int sg = 0; sg < OC_SEG_MAX; ++sg)
+        if (sg < nseg) m = max(m, cmax_p[(int64_t)sg * K + j]);
+    colmax[j] = __builtin_bit_cast(float, m);
+}
+
+hipError_t launch_col_absmax(const uint16_t* A, int64_t rows, int64_t K, float* colmax, bool accumulate,
+                             void* scratch, hipStream_t st) {
+    const int segs = outlier_scan(A, rows, K, __builtin_inff(), scratch, true, st);
+    const uint32_t* cmax_p =
+        reinterpret_cast<const uint32_t*>(static_cast<unsigned long long*>(scratch) + OC_SEG_MAX * ((K + 63) / 64));
+    hipLaunchKernelGGL(k_colmax_merge, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, st, cmax_p, segs, K, colmax,
+                       accumulate ? 1 : 0);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // Row-wise int8 quantization: one wave per row, 8 elements (16 bytes) per
 // lane and chunk.  NC > 0 keeps the row in registers (K <= 512 * NC); NC == 0

@@ -43,6 +43,10 @@ size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 // Largest K for which |sum_k q_x q_w| < 2^31 with codes in [-127, 127].
 constexpr int64_t kMaxK_i8 = 131072;
 
+// Row quantizers address a row with 32-bit byte offsets (16 bytes of fp16
+// and 32 bytes of factors per 8 columns).
+constexpr int64_t kMaxK_quant = (int64_t)1 << 26;
+
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 struct MixedLayout {
@@ -54,6 +58,20 @@ MixedLayout mixed_layout(int64_t M, int64_t K) {
     size_t off = 0;
     L.cmax = off; off += up(qa::outlier_scratch_bytes(K));
     L.idx = off; off += up((size_t)K * 4);
+    L.count = off; off += up(4);
+    L.s_x = off; off += up((size_t)M * 4);
+    L.xq = off; off += up((size_t)M * (size_t)K);
+    L.total = off;
+    return L;
+}
+
+struct SmoothLayout {
+    size_t count, s_x, xq, total;
+};
+
+SmoothLayout smooth_layout(int64_t M, int64_t K) {
+    SmoothLayout L;
+    size_t off = 0;
     L.count = off; off += up(4);
     L.s_x = off; off += up((size_t)M * 4);
     L.xq = off; off += up((size_t)M * (size_t)K);
@@ -124,8 +142,8 @@ qa_status qa_quantize_rowwise_int8(const void* X_f16, int64_t rows, int64_t K, c
                                    int32_t q_min, int32_t q_max, const float* s_in_or_null,
                                    const int32_t* z_in_or_null, int8_t* Xq, float* s_out_or_null, void* stream) {
     const bool dynamic = s_in_or_null == nullptr;
-    if (rows < 0 || K <= 0 || K % 8 != 0)
-        return fail(QA_ERR_SHAPE, "qa_quantize_rowwise_int8: need rows >= 0, K > 0, K %% 8 == 0");
+    if (rows < 0 || K <= 0 || K % 8 != 0 || K > kMaxK_quant)
+        return fail(QA_ERR_SHAPE, "qa_quantize_rowwise_int8: need rows >= 0, 0 < K <= 2^26, K %% 8 == 0");
     if (q_min > q_max || q_min < -128 || q_max > 127)
         return fail(QA_ERR_VALUE, "qa_quantize_rowwise_int8: need -128 <= q_min <= q_max <= 127");
     if (dynamic && (q_max <= 0 || z_in_or_null))
@@ -203,6 +221,101 @@ qa_status qa_qlinear_int8_mixed(const void* X_f16, int64_t M, int64_t K, const i
     ep.ldo = N;
     ep.out_dtype = (int)out_dtype;
     return device_status(qa::launch_gemm_i8_mixed(xq, Wq, M, K, N, ep, st), "qa_qlinear_int8_mixed (gemm)");
+}
+
+// ----------------------------------------------------------------- SmoothQuant
+size_t qa_col_absmax_workspace(int64_t K) { return qa_outlier_cols_workspace(K); }
+
+qa_status qa_col_absmax(const void* A_f16, int64_t rows, int64_t K, float* colmax, int accumulate, void* scratch,
+                        size_t scratch_bytes, void* stream) {
+    if (rows < 0 || K <= 0 || K % 8 != 0 || K > ((int64_t)1 << 22))
+        return fail(QA_ERR_SHAPE, "qa_col_absmax: need rows >= 0, 0 < K <= 2^22, K %% 8 == 0 (rows=%lld K=%lld)",
+                    (long long)rows, (long long)K);
+    if (rows == 0) return ok();
+    if (!A_f16 || !colmax || !scratch) return fail(QA_ERR_NULL, "qa_col_absmax: NULL pointer");
+    if (!aligned(A_f16, 16) || !aligned(colmax, 4) || !aligned(scratch, 4))
+        return fail(QA_ERR_ALIGN, "qa_col_absmax: A must be 16-byte aligned, colmax/scratch 4-byte");
+    if (scratch_bytes < qa_col_absmax_workspace(K))
+        return fail(QA_ERR_WORKSPACE, "qa_col_absmax: scratch %zu < %zu bytes", scratch_bytes,
+                    qa_col_absmax_workspace(K));
+    return device_status(qa::launch_col_absmax(static_cast<const uint16_t*>(A_f16), rows, K, colmax, accumulate != 0,
+                                               scratch, as_stream(stream)),
+                         "qa_col_absmax");
+}
+
+qa_status qa_smooth_factors(const float* act_absmax, const float* w_absmax, int64_t K, float alpha, float* s,
+                            void* stream) {
+    if (K < 0) return fail(QA_ERR_SHAPE, "qa_smooth_factors: K < 0");
+    if (!(alpha >= 0.0f && alpha <= 1.0f)) return fail(QA_ERR_VALUE, "qa_smooth_factors: alpha must be in [0, 1]");
+    if (K == 0) return ok();
+    if (!act_absmax || !w_absmax || !s) return fail(QA_ERR_NULL, "qa_smooth_factors: NULL pointer");
+    if (!aligned(act_absmax, 4) || !aligned(w_absmax, 4) || !aligned(s, 4))
+        return fail(QA_ERR_ALIGN, "qa_smooth_factors: arrays must be 4-byte aligned");
+    return device_status(qa::launch_smooth_factors(act_absmax, w_absmax, K, alpha, s, as_stream(stream)),
+                         "qa_smooth_factors");
+}
+
+qa_status qa_quantize_smooth_int8(const void* A_f16, int64_t rows, int64_t K, const float* s, qa_smooth_op op,
+                                  qa_scale_mode mode, int8_t* q, float* s_out, void* stream) {
+    if (rows < 0 || K <= 0 || K % 8 != 0 || K > kMaxK_quant)
+        return fail(QA_ERR_SHAPE, "qa_quantize_smooth_int8: need rows >= 0, 0 < K <= 2^26, K %% 8 == 0");
+    if (op != QA_SMOOTH_DIVIDE && op != QA_SMOOTH_MULTIPLY)
+        return fail(QA_ERR_VALUE, "qa_quantize_smooth_int8: bad op %d", (int)op);
+    if (mode != QA_SCALE_PER_ROW && mode != QA_SCALE_PER_TENSOR)
+        return fail(QA_ERR_VALUE, "qa_quantize_smooth_int8: mode must be PER_ROW or PER_TENSOR (%d)", (int)mode);
+    if (rows == 0) return ok();
+    if (!A_f16 || !s || !q || !s_out) return fail(QA_ERR_NULL, "qa_quantize_smooth_int8: NULL pointer");
+    if (!aligned(A_f16, 16) || !aligned(q, 16) || !aligned(s, 4) || !aligned(s_out, 4))
+        return fail(QA_ERR_ALIGN, "qa_quantize_smooth_int8: A, q 16-byte, s, s_out 4-byte aligned");
+    return device_status(qa::launch_smoothquant_i8(static_cast<const uint16_t*>(A_f16), rows, K, s,
+                                                   op == QA_SMOOTH_MULTIPLY, mode == QA_SCALE_PER_TENSOR, q, s_out,
+                                                   nullptr, as_stream(stream)),
+                         "qa_quantize_smooth_int8");
+}
+
+size_t qa_qlinear_int8_smooth_workspace(int64_t M, int64_t K) {
+    if (M < 0 || K <= 0) return 0;
+    return smooth_layout(M, K).total;
+}
+
+qa_status qa_qlinear_int8_smooth(const void* X_f16, int64_t M, int64_t K, const float* s, qa_scale_mode mode,
+                                 const int8_t* Wq, const float* s_w, int64_t N, void* out, qa_dtype out_dtype,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+    if (M < 0 || N < 0 || K <= 0 || K % 16 != 0 || K > kMaxK_i8)
+        return fail(QA_ERR_SHAPE, "qa_qlinear_int8_smooth: need M, N >= 0, 0 < K <= %lld, K %% 16 == 0",
+                    (long long)kMaxK_i8);
+    if (mode != QA_SCALE_PER_ROW && mode != QA_SCALE_PER_TENSOR)
+        return fail(QA_ERR_VALUE, "qa_qlinear_int8_smooth: mode must be PER_ROW or PER_TENSOR (%d)", (int)mode);
+    if (!valid_dtype(out_dtype)) return fail(QA_ERR_VALUE, "qa_qlinear_int8_smooth: bad out_dtype %d", (int)out_dtype);
+    if (M == 0 || N == 0) return ok();
+    if (!X_f16 || !s || !Wq || !s_w || !out || !workspace)
+        return fail(QA_ERR_NULL, "qa_qlinear_int8_smooth: NULL pointer");
+    if (!aligned(X_f16, 16) || !aligned(Wq, 16) || !aligned(s, 4) || !aligned(s_w, 4) || !aligned(out, 4) ||
+        !aligned(workspace, kAlign))
+        return fail(QA_ERR_ALIGN, "qa_qlinear_int8_smooth: X, Wq 16-byte, workspace 256-byte, s/s_w/out 4-byte");
+    const SmoothLayout L = smooth_layout(M, K);
+    if (workspace_bytes < L.total)
+        return fail(QA_ERR_WORKSPACE, "qa_qlinear_int8_smooth: workspace %zu < %zu bytes", workspace_bytes, L.total);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    int32_t* count = reinterpret_cast<int32_t*>(ws + L.count);
+    float* s_x = reinterpret_cast<float*>(ws + L.s_x);
+    int8_t* xq = reinterpret_cast<int8_t*>(ws + L.xq);
+    hipStream_t st = as_stream(stream);
+    const uint16_t* X = static_cast<const uint16_t*>(X_f16);
+    hipError_t e = qa::launch_smoothquant_i8(X, M, K, s, false, mode == QA_SCALE_PER_TENSOR, xq, s_x, count, st);
+    if (e != hipSuccess) return device_status(e, "qa_qlinear_int8_smooth (smoothing quantization)");
+    qa::MixedEpilogue ep;
+    ep.s_x = s_x;
+    ep.s_w = s_w;
+    ep.X = X;
+    ep.W16 = nullptr;
+    ep.Wq = Wq;
+    ep.idx = count;            // never read: the count is 0
+    ep.count = count;
+    ep.out = out;
+    ep.ldo = N;
+    ep.out_dtype = (int)out_dtype;
+    return device_status(qa::launch_gemm_i8_mixed(xq, Wq, M, K, N, ep, st), "qa_qlinear_int8_smooth (gemm)");
 }
 
 // ----------------------------------------------------------------- Hadamard + int4

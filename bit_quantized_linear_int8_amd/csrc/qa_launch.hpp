@@ -36,6 +36,18 @@ hipError_t launch_rowquant_i8_flags(const uint16_t* X, int64_t rows, int64_t K, 
 hipError_t launch_rowquant_i8_no_outliers(const uint16_t* X, int64_t rows, int64_t K, int8_t* q, float* s_out,
                                           int32_t* count, hipStream_t st);
 
+// Column absolute maxima of A [rows x K] (maxed into colmax when accumulating);
+// scratch as for the outlier scan.
+hipError_t launch_col_absmax(const uint16_t* A, int64_t rows, int64_t K, float* colmax, bool accumulate,
+                             void* scratch, hipStream_t st);
+
+// SmoothQuant migration factors and the smoothing fused with [-127, 127]
+// absmax quantization (per row, or per tensor broadcast into s_out[rows]);
+// a non-null count is set to 0 for the GEMM epilogue.
+hipError_t launch_smooth_factors(const float* cx, const float* cw, int64_t K, float alpha, float* s, hipStream_t st);
+hipError_t launch_smoothquant_i8(const uint16_t* X, int64_t rows, int64_t K, const float* sm, bool multiply,
+                                 bool per_tensor, int8_t* q, float* s_out, int32_t* count, hipStream_t st);
+
 hipError_t launch_hadamard_quant_i4(const uint16_t* X, int64_t rows, int64_t K, int G,
                                     bool per_group, int qmin, int qmax, uint32_t* packed, float* s,
                                     hipStream_t st);

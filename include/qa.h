@@ -2,7 +2,7 @@
  * qa.h -- C ABI of libqa, quantized linear layers for AMD Instinct MI355X
  * (gfx950, CDNA4).
  *
- * Two quantized linear layers of LLM inference:
+ * Quantized linear layers of LLM inference:
  *   - LLM.int8() mixed precision: feature columns whose activation magnitude
  *     exceeds a threshold stay in fp16, all other columns are quantized to
  *     int8 with vector-wise absmax scales (per token for X, per output
@@ -12,6 +12,10 @@
  *     the normalized Hadamard matrix, quantized to int4 (dynamic per-token
  *     scales for X, per-row-per-group scales for W), packed eight per 32-bit
  *     word, multiplied with int32 accumulation per group and dequantized.
+ *   - SmoothQuant W8A8: activation columns are divided by per-channel
+ *     migration factors and the weight's input channels multiplied by them,
+ *     so both quantize to int8 with plain absmax scales (per token or per
+ *     tensor for X, per output channel for W) and no fp16 branch.
  *
  * Sources, cited by page title and section:
  *   [AIInfra-Q01]  Infrasys-AI "AIInfra" notes, page 05Quantization01 (模型量化):
@@ -24,7 +28,10 @@
  *                  §5.2 online activation transform fused with quantization,
  *                  §5.4 packing and int32 accumulation.
  *   [QE2]          "Quantization explained, part 2" (tanjunchen.github.io),
- *                  §1.2: threshold 6.0 on a channel's activation magnitude.
+ *                  §1.2: threshold 6.0 on a channel's activation magnitude;
+ *                  §4.2: SmoothQuant, the per-input-channel migration
+ *                  X W = (X diag(s)^-1)(diag(s) W), s_j = max|X_j|^alpha /
+ *                  max|W_j|^(1-alpha); §4.4: factors fixed offline.
  *
  * Conventions shared by every entry point:
  *   - All array arguments are DEVICE pointers allocated and owned by the
@@ -69,7 +76,10 @@ typedef enum {
 
 typedef enum { QA_F32 = 0, QA_F16 = 1, QA_BF16 = 2 } qa_dtype;
 
-typedef enum { QA_SCALE_PER_ROW = 0, QA_SCALE_PER_GROUP = 1 } qa_scale_mode;
+typedef enum { QA_SCALE_PER_ROW = 0, QA_SCALE_PER_GROUP = 1, QA_SCALE_PER_TENSOR = 2 } qa_scale_mode;
+
+/* SmoothQuant side: activations are divided by the factors, weights multiplied. */
+typedef enum { QA_SMOOTH_DIVIDE = 0, QA_SMOOTH_MULTIPLY = 1 } qa_smooth_op;
 
 /* Human-readable name of a status code (static string). */
 const char* qa_status_string(qa_status s);
@@ -112,7 +122,7 @@ qa_status qa_outlier_cols(const void* X_f16, int64_t M, int64_t K, float thresho
  *     (mask[j] != 0) is skipped by the absmax and receives clip(z).
  *   X       fp16 [rows x K]; mask u8 [K] or NULL; Xq i8 [rows x K]
  * Errors: NULL X / Xq (or s_out in dynamic mode), rows < 0, K <= 0,
- * K % 8 != 0, X or Xq not 16-byte aligned, q_min > q_max, range outside
+ * K > 2^26, K % 8 != 0, X or Xq not 16-byte aligned, q_min > q_max, range outside
  * [-128, 127], dynamic mode with q_max <= 0 or z_in != NULL.
  * ------------------------------------------------------------------------- */
 qa_status qa_quantize_rowwise_int8(const void* X_f16, int64_t rows, int64_t K,
@@ -187,6 +197,82 @@ size_t qa_qlinear_w4a4_workspace(int64_t M, int64_t K);
 qa_status qa_qlinear_w4a4(const void* X_f16, int64_t M, int64_t K, const uint32_t* Wp,
                           const float* s_w, int64_t N, int32_t G, void* out, qa_dtype out_dtype,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Column absolute maxima  [QE2 §4.2: max|X_j| and max|W_j| per input channel]
+ *
+ *   colmax[j] = max_r |A[r][j]|  (accumulate == 0)
+ *   colmax[j] = max(colmax[j], max_r |A[r][j]|)  (accumulate != 0: a running
+ *               maximum over calibration batches; colmax must then hold
+ *               non-negative finite values, e.g. from an earlier call)
+ * For activations A = X [M x K]; for the weight A = W [N x K] gives the
+ * maximum over output channels of each input channel.  Exact (fp16 widened).
+ *   A       fp16 [rows x K]; colmax f32 [K]
+ *   scratch device buffer of qa_col_absmax_workspace(K) bytes (any content)
+ * rows == 0 is a no-op.
+ * Errors: NULL pointers, rows < 0, K <= 0, K > 2^22, K % 8 != 0, A not
+ * 16-byte aligned, small scratch.
+ * ------------------------------------------------------------------------- */
+size_t qa_col_absmax_workspace(int64_t K);
+qa_status qa_col_absmax(const void* A_f16, int64_t rows, int64_t K, float* colmax, int accumulate,
+                        void* scratch, size_t scratch_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * SmoothQuant migration factors  [QE2 §4.2]
+ *
+ *   s[j] = fl32( pow(act_absmax[j], alpha) / pow(w_absmax[j], 1 - alpha) )
+ * evaluated in fp64 (alpha widened exactly from fp32); s[j] = 1 when either
+ * maximum is 0.  alpha = 0.5 splits the range evenly; alpha = 1 gives
+ * s = act_absmax (activation columns scaled to magnitude 1); alpha = 0 gives
+ * s = 1 / w_absmax.  The fp64 pow of the device math library may differ from
+ * another implementation's by one rounding, so s can differ in the last fp32
+ * bit; the smoothing below takes s as given.
+ *   act_absmax, w_absmax  f32 [K], non-negative finite
+ *   s       f32 [K]
+ * Errors: NULL pointers, K < 0, alpha NaN or outside [0, 1].  K == 0 is a
+ * no-op.
+ * ------------------------------------------------------------------------- */
+qa_status qa_smooth_factors(const float* act_absmax, const float* w_absmax, int64_t K, float alpha, float* s,
+                            void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Smoothing fused with int8 quantization  [QE2 §4.2; Scholia-IQ §4, §7]
+ *
+ *   a^[r][j] = fl32(A[r][j] / s[j])   (QA_SMOOTH_DIVIDE: activations)
+ *   a^[r][j] = fl32(A[r][j] * s[j])   (QA_SMOOTH_MULTIPLY: the weight W [N x K],
+ *                                      offline)
+ *   QA_SCALE_PER_ROW:    s_out[r] = fl32(max_j |a^[r][j]| / 127)
+ *   QA_SCALE_PER_TENSOR: s_out[r] = fl32(max_{r,j} |a^[r][j]| / 127) for every r
+ *   (1.0 for an all-zero row / tensor)
+ *   q[r][j]  = clip(rint(a^[r][j] / s_out[r]), -127, 127)
+ *   A       fp16 [rows x K]; s f32 [K], positive finite; q i8 [rows x K];
+ *   s_out   f32 [rows]
+ * Errors: NULL pointers, rows < 0, K <= 0, K > 2^26, K % 8 != 0, A or q not
+ * 16-byte aligned, bad op, mode not PER_ROW / PER_TENSOR.  rows == 0 is a
+ * no-op.
+ * ------------------------------------------------------------------------- */
+qa_status qa_quantize_smooth_int8(const void* A_f16, int64_t rows, int64_t K, const float* s, qa_smooth_op op,
+                                  qa_scale_mode mode, int8_t* q, float* s_out, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * SmoothQuant W8A8 linear  [QE2 §4.2, §4.4; AIInfra-Q01 "b. INT8 矩阵乘法与反量化"]
+ *
+ *   (Xq, s_x) = qa_quantize_smooth_int8(X, s, QA_SMOOTH_DIVIDE, mode)  (on device)
+ *   C[m][n]   = sum_k Xq[m][k] * Wq[n][k]                              (int32)
+ *   out       = C * s_x[m] * s_w[n]
+ *   X       fp16 [M x K]; s f32 [K] (qa_smooth_factors)
+ *   Wq, s_w the smoothed weight: qa_quantize_smooth_int8(W, s,
+ *           QA_SMOOTH_MULTIPLY, QA_SCALE_PER_ROW): i8 [N x K], f32 [N]
+ *   mode    QA_SCALE_PER_ROW (per token) or QA_SCALE_PER_TENSOR for X
+ *   out     [M x N] of out_dtype
+ *   workspace  qa_qlinear_int8_smooth_workspace(M, K) bytes (any content)
+ * Errors: NULL pointers, M < 0, N < 0, K <= 0, K % 16 != 0, K > 131072,
+ * misaligned pointers, bad mode or out_dtype, small workspace.
+ * ------------------------------------------------------------------------- */
+size_t qa_qlinear_int8_smooth_workspace(int64_t M, int64_t K);
+qa_status qa_qlinear_int8_smooth(const void* X_f16, int64_t M, int64_t K, const float* s, qa_scale_mode mode,
+                                 const int8_t* Wq, const float* s_w, int64_t N, void* out, qa_dtype out_dtype,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Parity entry points: the integer accumulators of the two GEMMs, stored.

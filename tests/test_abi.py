@@ -84,6 +84,7 @@ def test_quantize_argument_errors():
     assert f(A, 4, 64, None, -127, 127, None, None, B, None, None) == NULL          # dynamic needs s_out
     assert f(A, 4, 60, None, -127, 127, None, None, B, OUT, None) == SHAPE
     assert f(A, -4, 64, None, -127, 127, None, None, B, OUT, None) == SHAPE
+    assert f(A, 4, (1 << 26) + 8, None, -127, 127, None, None, B, OUT, None) == SHAPE
     assert f(MIS, 4, 64, None, -127, 127, None, None, B, OUT, None) == ALIGN
     assert f(A, 4, 64, None, 5, 4, None, None, B, OUT, None) == VALUE
     assert f(A, 4, 64, None, -129, 127, None, None, B, OUT, None) == VALUE
@@ -148,3 +149,85 @@ def test_gemm_i8_argument_errors():
     assert f(A, B, 4, 40, 4, OUT, None) == SHAPE
     assert f(A, MIS, 4, 64, 4, OUT, None) == ALIGN
     assert f(A, B, 0, 64, 4, OUT, None) == OK
+
+
+def test_col_absmax_argument_errors():
+    f = qa.lib().qa_col_absmax
+    args = [A, 16, 256, OUT, 0, WS, 1 << 20, None]
+
+    def call(i, v):
+        a = list(args)
+        a[i] = v
+        return f(*a)
+    assert call(0, None) == NULL
+    assert call(3, None) == NULL
+    assert call(5, None) == NULL
+    assert call(2, 12) == SHAPE
+    assert call(2, 0) == SHAPE
+    assert call(1, -1) == SHAPE
+    assert call(2, (1 << 22) + 8) == SHAPE
+    assert call(0, MIS) == ALIGN
+    assert call(6, 16) == WORKSPACE
+    assert call(1, 0) == OK                                    # no rows: no-op
+    assert qa.lib().qa_col_absmax_workspace(256) == qa.lib().qa_outlier_cols_workspace(256)
+
+
+def test_smooth_factors_argument_errors():
+    f = qa.lib().qa_smooth_factors
+    assert f(None, B, 64, 0.5, OUT, None) == NULL
+    assert f(A, B, 64, 0.5, None, None) == NULL
+    assert f(A, B, -1, 0.5, OUT, None) == SHAPE
+    assert f(A, B, 64, -0.1, OUT, None) == VALUE
+    assert f(A, B, 64, 1.5, OUT, None) == VALUE
+    assert f(A, B, 64, math.nan, OUT, None) == VALUE
+    assert f(ctypes.c_void_p(0x10002), B, 64, 0.5, OUT, None) == ALIGN
+    assert f(A, B, 0, 0.5, OUT, None) == OK
+
+
+def test_quantize_smooth_argument_errors():
+    f = qa.lib().qa_quantize_smooth_int8
+    args = [A, 4, 64, B, 0, 0, OUT, WS, None]
+
+    def call(i, v):
+        a = list(args)
+        a[i] = v
+        return f(*a)
+    assert call(0, None) == NULL
+    assert call(3, None) == NULL
+    assert call(7, None) == NULL
+    assert call(2, 60) == SHAPE
+    assert call(2, (1 << 26) + 8) == SHAPE
+    assert call(1, -1) == SHAPE
+    assert call(4, 2) == VALUE                                 # bad op
+    assert call(5, 1) == VALUE                                 # per-group is not a mode here
+    assert call(0, MIS) == ALIGN
+    assert call(6, MIS) == ALIGN
+    assert call(1, 0) == OK
+    a = list(args)
+    a[1], a[5] = 0, 2                                          # per tensor is a valid mode
+    assert f(*a) == OK
+
+
+def test_smooth_linear_argument_errors():
+    f = qa.lib().qa_qlinear_int8_smooth
+    base = [A, 16, 256, B, 0, B, OUT, 32, OUT, 1, WS, 1 << 30, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+    assert call(0, None) == NULL
+    assert call(3, None) == NULL
+    assert call(10, None) == NULL
+    assert call(2, 24) == SHAPE
+    assert call(2, 131088) == SHAPE
+    assert call(1, -1) == SHAPE
+    assert call(4, 1) == VALUE
+    assert call(9, 3) == VALUE
+    assert call(0, MIS) == ALIGN
+    assert call(10, ctypes.c_void_p(0x40010)) == ALIGN
+    assert call(11, 100) == WORKSPACE
+    assert call(1, 0) == OK and call(7, 0) == OK
+    L = qa.lib()
+    for M, K in [(1, 16), (2048, 4096)]:
+        assert L.qa_qlinear_int8_smooth_workspace(M, K) >= M * K + 4 * M + 4
