@@ -11,8 +11,9 @@ rather than from the 256 MB Infinity Cache.  `value` is algorithmic bytes
 moved per step / step time (GB/s).
 
 Also reported (same JSON line, key "also"): whole-call throughput of the
-prefill-shape mixed linear, the W8A8 FFN shape and the W4A4 group-Hadamard
-linear, in int8 TOPS against the dense int8 MFMA peak.
+prefill-shape mixed linear, the W8A8 FFN shape, the W4A4 group-Hadamard
+linear and the SmoothQuant W8A8 linear on the prefill and FFN data, in int8
+TOPS against the dense int8 MFMA peak.
 
 roofline: the decode kernel's algorithmic bytes per launch / its average
 launch duration, from HIP events recorded on the launch stream around the
@@ -46,11 +47,12 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=256)
     p.add_argument("--warmup", type=int, default=32)
-    p.add_argument("--no-also", action="store_true", help="skip the prefill / W8A8 / W4A4 lines")
+    p.add_argument("--no-also", action="store_true", help="skip the prefill / W8A8 / W4A4 / SmoothQuant lines")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--only", default=None,
-                   help="run one workload only (decode|prefill|w8a8|w4a4|copy), for profiling; copy is a plain "
+                   help="run one workload only (decode|prefill|w8a8|w4a4|smooth_prefill|smooth_ffn|copy), for "
+                        "profiling; copy is a plain "
                         "1 GiB device copy used to calibrate HBM byte counters")
     return p.parse_args()
 
@@ -155,6 +157,24 @@ def prefill_like(torch, qa, synthetic, dev, name):
     return c, fns, 2 * M * N * K
 
 
+def smooth_workload(torch, qa, synthetic, dev, name, per_tensor):
+    """SmoothQuant W8A8 on a workload's data: device calibration (column maxima
+    of X and W, alpha = 0.5 factors), offline smoothed weight, then the timed
+    call (smoothing + int8 quantization of X, int8 GEMM, dequant)."""
+    c = synthetic.config(name)
+    M, K, N = c["M"], c["K"], c["N"]
+    X = torch.from_numpy(c["X"]).to(dev)
+    W16 = torch.from_numpy(c["W"]).to(dev)
+    s = qa.qa_smooth_factors(qa.qa_col_absmax(X), qa.qa_col_absmax(W16), 0.5)
+    Wq, s_w = qa.qa_quantize_smooth_int8(W16, s, multiply=True)
+    del W16
+    odt = {0: torch.float32, 1: torch.float16, 2: torch.bfloat16}[c["out_dtype"]]
+    out = torch.empty((M, N), dtype=odt, device=dev)
+    ws = torch.empty(qa.qa_qlinear_int8_smooth_workspace(M, K), dtype=torch.uint8, device=dev)
+    fns = [lambda: qa.qa_qlinear_int8_smooth(X, s, Wq, s_w, per_tensor=per_tensor, out=out, workspace=ws)]
+    return c, fns, 2 * M * N * K
+
+
 def w4a4_workload(torch, qa, synthetic, dev):
     c = synthetic.config("w4a4_hadamard")
     M, K, N, G = c["M"], c["K"], c["N"], c["G"]
@@ -249,16 +269,24 @@ def main():
         del fns, gs
         torch.cuda.empty_cache()
 
-    run_also = (args.only is None and not args.no_also) or args.only in ("prefill", "w8a8", "w4a4")
+    keys = ("prefill", "w8a8", "w4a4", "smooth_prefill", "smooth_ffn")
+    run_also = (args.only is None and not args.no_also) or args.only in keys
     if run_also:
         todo = []
-        for name, key in (("prefill_mixed", "prefill"), ("w8a8_ffn", "w8a8"), ("w4a4_hadamard", "w4a4")):
+        for name, key in (("prefill_mixed", "prefill"), ("w8a8_ffn", "w8a8"), ("w4a4_hadamard", "w4a4"),
+                          ("prefill_mixed", "smooth_prefill"), ("w8a8_ffn", "smooth_ffn")):
             if args.only in (None, key):
                 todo.append((name, key))
         for name, key in todo:
-            log("[bench] %s: building inputs" % name)
+            log("[bench] %s: building inputs" % key)
             if key == "w4a4":
                 c, fns, ops = w4a4_workload(torch, qa, synthetic, dev)
+            elif key == "smooth_prefill":
+                c, fns, ops = smooth_workload(torch, qa, synthetic, dev, name, per_tensor=False)
+                name = "smoothquant_prefill: X/s per-token int8, %s data" % name
+            elif key == "smooth_ffn":
+                c, fns, ops = smooth_workload(torch, qa, synthetic, dev, name, per_tensor=True)
+                name = "smoothquant_ffn: X/s per-tensor int8, %s data" % name
             else:
                 c, fns, ops = prefill_like(torch, qa, synthetic, dev, name)
             gs = GraphSteps(torch, fns * 4)
