@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
             "orc_quant_rows_f16": (None, [P, I64, I64, I64, P, I32, I32, P, P, P, P]),
             "orc_gemm_i8_i32": (I64, [P, P, I64, I64, I64, P, I64, P]),
             "orc_qlinear_int8_mixed": (None, [P, I64, I64, P, P, P, I64, F, P, I64, P]),
+            "orc_outlier_topk": (None, [P, I64, I64, I64, P, P, P, P]),
+            "orc_qlinear_int8_topk": (None, [P, I64, I64, P, P, P, I64, I64, P, I64, P]),
             "orc_col_absmax_f32": (None, [P, I64, I64, P]),
             "orc_smooth_factors": (None, [P, P, I64, ctypes.c_double, P]),
             "orc_smooth_apply_f32": (None, [P, I64, I64, P, ctypes.c_int, P]),
@@ -139,6 +141,33 @@ def outlier_cols(X16, tau: float):
     colmax = np.zeros(K, np.float32)
     lib().orc_outlier_cols(_ptr(h), M, K, float(tau), _ptr(mask), _ptr(idx), _ptr(count), _ptr(colmax))
     return mask, idx[: int(count[0])].copy(), colmax
+
+
+def outlier_topk(X16, k: int):
+    """The k columns of largest max |x| (ties: lower column first)
+    -> (mask u8 [K], idx i32 [count] ascending, colmax f32 [K])."""
+    h = _h16(X16)
+    M, K = h.shape
+    mask = np.zeros(K, np.uint8)
+    idx = np.zeros(max(K, 1), np.int32)
+    count = np.zeros(1, np.int32)
+    colmax = np.zeros(K, np.float32)
+    lib().orc_outlier_topk(_ptr(h), M, K, int(k), _ptr(mask), _ptr(idx), _ptr(count), _ptr(colmax))
+    return mask, idx[: int(count[0])].copy(), colmax
+
+
+def qlinear_int8_topk(X16, Wq, s_w, W16=None, k=0, rows=None):
+    """LLM.int8() linear with the top-k columns decomposed, fp64 [nrows x N]."""
+    h = _h16(X16)
+    M, K = h.shape
+    Wq = _c(Wq, np.int8)
+    N = Wq.shape[0]
+    sw = _c(s_w, np.float32)
+    w16 = None if W16 is None else _h16(W16)
+    r, nr = _rows(rows)
+    out = np.zeros((nr if r is not None else M, N), np.float64)
+    lib().orc_qlinear_int8_topk(_ptr(h), M, K, _ptr(Wq), _ptr(sw), _ptr(w16), N, int(k), _ptr(r), nr, _ptr(out))
+    return out
 
 
 def quant_rows(x, gsize=None, mask=None, qmin=-127, qmax=127, s_in=None, z_in=None):

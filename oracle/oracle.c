@@ -152,6 +152,40 @@ void orc_outlier_cols(const uint16_t* X, int64_t M, int64_t K, float tau,
 }
 
 /* ---------------------------------------------------------------------------
+ * Top-k decomposition  [AIInfra-Q01, advice for training: raise the share of
+ * decomposed feature dimensions to the largest-magnitude 1-2%]
+ * O = the k columns with the largest max_i |x_ij|, chosen one at a time as
+ * the largest remaining maximum, equal maxima in ascending column order.
+ * k is clamped to [0, K].  idx lists O in ascending order.
+ * ------------------------------------------------------------------------- */
+void orc_outlier_topk(const uint16_t* X, int64_t M, int64_t K, int64_t k,
+                      uint8_t* mask, int32_t* idx, int32_t* count, float* colmax)
+{
+    float* cm = (float*)malloc(sizeof(float) * (size_t)(K > 0 ? K : 1));
+    int32_t none = 0;
+    orc_outlier_cols(X, M, K, INFINITY, mask, idx, &none, cm);    /* column maxima; no column exceeds +inf */
+    if (k < 0) k = 0;
+    if (k > K) k = K;
+    for (int64_t j = 0; j < K; ++j)
+        mask[j] = 0;
+    for (int64_t r = 0; r < k; ++r) {
+        int64_t best = -1;
+        for (int64_t j = 0; j < K; ++j)
+            if (!mask[j] && (best < 0 || cm[j] > cm[best]))
+                best = j;
+        mask[best] = 1;
+    }
+    int32_t n = 0;
+    for (int64_t j = 0; j < K; ++j)
+        if (mask[j])
+            idx[n++] = (int32_t)j;
+    *count = n;
+    if (colmax)
+        memcpy(colmax, cm, sizeof(float) * (size_t)K);
+    free(cm);
+}
+
+/* ---------------------------------------------------------------------------
  * Quantization of rows, [Scholia-IQ §4, §6.2, §7.3; AIInfra-Q01 "a. 向量级量化"]
  *
  * x is [rows x K] fp32; every `gsize` consecutive columns of a row share one
@@ -262,17 +296,48 @@ int64_t orc_gemm_i8_i32(const int8_t* A, const int8_t* B, int64_t M, int64_t K, 
  *   6. out = outlier part + normal part                  [merge step]
  * Output is fp64 [nrows x N]; round with orc_round_output.
  * ------------------------------------------------------------------------- */
+static void orc_mixed_with_set(const uint16_t* X, int64_t M, int64_t K,
+                               const int8_t* Wq, const float* s_w, const uint16_t* W16,
+                               int64_t N, const uint8_t* mask, const int32_t* idx, int32_t count,
+                               const int64_t* rows, int64_t nrows, double* out);
+
 void orc_qlinear_int8_mixed(const uint16_t* X, int64_t M, int64_t K,
                             const int8_t* Wq, const float* s_w, const uint16_t* W16,
                             int64_t N, float tau, const int64_t* rows, int64_t nrows,
                             double* out)
 {
-    if (!rows)
-        nrows = M;
     uint8_t* mask = (uint8_t*)calloc((size_t)(K > 0 ? K : 1), 1);
     int32_t* idx = (int32_t*)calloc((size_t)(K > 0 ? K : 1), sizeof(int32_t));
     int32_t count = 0;
     orc_outlier_cols(X, M, K, tau, mask, idx, &count, NULL);
+    orc_mixed_with_set(X, M, K, Wq, s_w, W16, N, mask, idx, count, rows, nrows, out);
+    free(idx);
+    free(mask);
+}
+
+/* The same linear with the outlier set O chosen as the top-k columns. */
+void orc_qlinear_int8_topk(const uint16_t* X, int64_t M, int64_t K,
+                           const int8_t* Wq, const float* s_w, const uint16_t* W16,
+                           int64_t N, int64_t k, const int64_t* rows, int64_t nrows,
+                           double* out)
+{
+    uint8_t* mask = (uint8_t*)calloc((size_t)(K > 0 ? K : 1), 1);
+    int32_t* idx = (int32_t*)calloc((size_t)(K > 0 ? K : 1), sizeof(int32_t));
+    int32_t count = 0;
+    orc_outlier_topk(X, M, K, k, mask, idx, &count, NULL);
+    orc_mixed_with_set(X, M, K, Wq, s_w, W16, N, mask, idx, count, rows, nrows, out);
+    free(idx);
+    free(mask);
+}
+
+/* Steps 2-6 for a given outlier set (mask, ascending idx, count). */
+static void orc_mixed_with_set(const uint16_t* X, int64_t M, int64_t K,
+                               const int8_t* Wq, const float* s_w, const uint16_t* W16,
+                               int64_t N, const uint8_t* mask, const int32_t* idx, int32_t count,
+                               const int64_t* rows, int64_t nrows, double* out)
+{
+    if (!rows)
+        nrows = M;
 
     /* fp16 outlier weights w~, gathered as doubles [N x count] */
     double* wt = (double*)malloc(sizeof(double) * (size_t)(N * count > 0 ? N * count : 1));
@@ -308,8 +373,6 @@ void orc_qlinear_int8_mixed(const uint16_t* X, int64_t M, int64_t K,
         free(xq);
     }
     free(wt);
-    free(idx);
-    free(mask);
 }
 
 /* ---------------------------------------------------------------------------

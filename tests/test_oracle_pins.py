@@ -562,3 +562,54 @@ def test_smoothing_lowers_w8a8_error_on_outlier_activations(per_tensor):
         Wq, s_w = oracle.smooth_quantize(W, sv, oracle.SMOOTH_MULTIPLY)
         errs.append(np.abs(oracle.qlinear_int8_smooth(X, sv, Wq, s_w, per_tensor=per_tensor) - exact).mean())
     assert errs[1] < errs[0] / 2
+
+
+# ------------------------------------------------------------------ top-k decomposition
+def _topk_ref(X, k):
+    """The k largest column maxima, ties to the lower column, via a stable sort."""
+    cm = np.abs(X.astype(np.float32)).max(axis=0)
+    order = np.argsort(-cm.astype(np.float64), kind="stable")
+    return np.sort(order[: max(0, min(k, X.shape[1]))]).astype(np.int32)
+
+
+@pytest.mark.parametrize("k", [0, 1, 3, 17, 64, 200, 256, 300])
+def test_topk_set_matches_stable_sort_with_ties(k):
+    rng = np.random.default_rng(41)
+    # small integers: many equal column maxima
+    X = rng.integers(-6, 7, size=(9, 256)).astype(np.float16)
+    mask, idx, cm = oracle.outlier_topk(X, k)
+    ref = _topk_ref(X, k)
+    assert np.array_equal(idx, ref)
+    assert mask.sum() == len(ref) and np.all(mask[ref] == 1)
+    assert np.array_equal(cm, np.abs(X.astype(np.float32)).max(axis=0))
+
+
+def test_topk_equals_threshold_set_without_boundary_ties():
+    X, _, dims = synthetic.mixed_inputs(64, 1024, 1, seed=42, n_dims=9, magnitude=("uniform", 8.0, 60.0))
+    _, idx_t, cm = oracle.outlier_cols(X, 6.0)
+    assert len(np.unique(cm[cm > 6.0])) == len(idx_t)            # no ties among the outliers
+    _, idx_k, _ = oracle.outlier_topk(X, len(idx_t))
+    assert np.array_equal(idx_k, idx_t)
+    Wq, s_w = oracle.quant_rows(synthetic.normal_f16(np.random.default_rng(1), (40, 1024), 0.02))
+    a = oracle.qlinear_int8_topk(X, Wq, s_w[:, 0], k=len(idx_t))
+    b = oracle.qlinear_int8_mixed(X, Wq, s_w[:, 0], tau=6.0)
+    assert np.array_equal(a, b)
+
+
+def test_topk_linear_extremes_reduce_to_pinned_cases():
+    X, W, _ = synthetic.mixed_inputs(12, 256, 30, seed=43, n_dims=3)
+    Wq, s_w = _w8(W)
+    assert np.array_equal(oracle.qlinear_int8_topk(X, Wq, s_w, k=0),
+                          oracle.qlinear_int8_mixed(X, Wq, s_w, tau=float("inf")))
+    assert np.array_equal(oracle.qlinear_int8_topk(X, Wq, s_w, W16=W, k=256),
+                          oracle.qlinear_int8_mixed(X, Wq, s_w, W16=W, tau=-1.0))
+
+
+def test_raising_the_decomposed_share_lowers_error():
+    """The pages advise decomposing the top 1-2% of dimensions rather than
+    about 0.1%; on heavy-tailed activations the error drops."""
+    X, W, _ = synthetic.mixed_inputs(128, 2048, 64, seed=44, n_dims=0, x_dist="t3")
+    Wq, s_w = _w8(W)
+    exact = X.astype(np.float64) @ W.astype(np.float64).T
+    errs = [np.abs(oracle.qlinear_int8_topk(X, Wq, s_w, W16=W, k=k) - exact).mean() for k in (2, 21, 41)]
+    assert errs[2] < errs[1] < errs[0]
