@@ -23,9 +23,10 @@ QA_SMOOTH_DIVIDE, QA_SMOOTH_MULTIPLY = 0, 1
 
 EXPORTS = (
     "qa_status_string", "qa_last_error",
-    "qa_outlier_cols_workspace", "qa_outlier_cols",
+    "qa_outlier_cols_workspace", "qa_outlier_cols", "qa_outlier_topk",
     "qa_quantize_rowwise_int8",
     "qa_qlinear_int8_mixed_workspace", "qa_qlinear_int8_mixed",
+    "qa_qlinear_int8_topk_workspace", "qa_qlinear_int8_topk",
     "qa_col_absmax_workspace", "qa_col_absmax", "qa_smooth_factors", "qa_quantize_smooth_int8",
     "qa_qlinear_int8_smooth_workspace", "qa_qlinear_int8_smooth",
     "qa_hadamard_quant_int4",
@@ -60,6 +61,9 @@ def lib() -> ctypes.CDLL:
             "qa_last_error": (ctypes.c_char_p, []),
             "qa_outlier_cols_workspace": (SZ, [I64]),
             "qa_outlier_cols": (S, [P, I64, I64, F, P, P, P, P, P, SZ, P]),
+            "qa_outlier_topk": (S, [P, I64, I64, I64, P, P, P, P, P, SZ, P]),
+            "qa_qlinear_int8_topk_workspace": (SZ, [I64, I64]),
+            "qa_qlinear_int8_topk": (S, [P, I64, I64, I64, P, P, P, I64, P, S, P, SZ, P]),
             "qa_quantize_rowwise_int8": (S, [P, I64, I64, P, I32, I32, P, P, P, P, P]),
             "qa_qlinear_int8_mixed_workspace": (SZ, [I64, I64]),
             "qa_qlinear_int8_mixed": (S, [P, I64, I64, P, P, P, I64, F, P, S, P, SZ, P]),
@@ -140,6 +144,28 @@ def qa_outlier_cols(X, threshold=6.0, scratch=None, stream=None):
     _check("qa_outlier_cols", lib().qa_outlier_cols(_p(X), M, K, float(threshold), _p(mask), _p(idx), _p(count),
                                                      _p(colmax), _p(scratch), scratch.numel(), _stream(stream)))
     return mask, idx, count, colmax
+
+
+def qa_outlier_topk(X, k: int, scratch=None, stream=None):
+    """The k columns of largest max |x| (ties: lower column first)
+    -> (mask u8 [K], idx i32 [K] (first `count` valid), count i32 [1], colmax f32 [K])."""
+    _dev(X, "X", torch.float16)
+    M, K = X.shape
+    dev = X.device
+    mask = torch.empty(K, dtype=torch.uint8, device=dev)
+    idx = torch.empty(K, dtype=torch.int32, device=dev)
+    count = torch.empty(1, dtype=torch.int32, device=dev)
+    colmax = torch.empty(K, dtype=torch.float32, device=dev)
+    scratch = _workspace(qa_outlier_cols_workspace(K), dev, scratch)
+    _check("qa_outlier_topk", lib().qa_outlier_topk(_p(X), M, K, int(k), _p(mask), _p(idx), _p(count), _p(colmax),
+                                                     _p(scratch), scratch.numel(), _stream(stream)))
+    return mask, idx, count, colmax
+
+
+def topk_count(share: float, K: int) -> int:
+    """Number of decomposed columns for a share of the K dimensions: ceil(share * K)."""
+    import math
+    return min(K, max(0, math.ceil(share * K)))
 
 
 def qa_quantize_rowwise_int8(X, mask=None, q_min=-127, q_max=127, s_in=None, z_in=None, stream=None):
@@ -244,6 +270,29 @@ def qa_qlinear_int8_smooth(X, s, Wq, s_w, per_tensor=False, out_dtype=torch.floa
            lib().qa_qlinear_int8_smooth(_p(X), M, K, _p(s), QA_SCALE_PER_TENSOR if per_tensor else QA_SCALE_PER_ROW,
                                         _p(Wq), _p(s_w), N, _p(out), _DTYPE_CODE[out.dtype], _p(workspace),
                                         workspace.numel(), _stream(stream)))
+    return out
+
+
+def qa_qlinear_int8_topk_workspace(M: int, K: int) -> int:
+    return int(lib().qa_qlinear_int8_topk_workspace(M, K))
+
+
+def qa_qlinear_int8_topk(X, Wq, s_w, k: int, W16=None, out_dtype=torch.float16, out=None, workspace=None,
+                         stream=None):
+    """LLM.int8() linear with the top-k columns decomposed -> out [M x N] of out_dtype."""
+    _dev(X, "X", torch.float16)
+    _dev(Wq, "Wq", torch.int8)
+    _dev(s_w, "s_w", torch.float32)
+    if W16 is not None:
+        _dev(W16, "W16", torch.float16)
+    M, K = X.shape
+    N = Wq.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=X.device)
+    workspace = _workspace(qa_qlinear_int8_topk_workspace(M, K), X.device, workspace)
+    _check("qa_qlinear_int8_topk",
+           lib().qa_qlinear_int8_topk(_p(X), M, K, int(k), _p(Wq), _p(s_w), _p(W16), N, _p(out),
+                                      _DTYPE_CODE[out.dtype], _p(workspace), workspace.numel(), _stream(stream)))
     return out
 
 

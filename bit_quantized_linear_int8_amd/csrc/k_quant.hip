@@ -207,6 +207,140 @@ hipError_t launch_outlier_flags(const uint16_t* X, int64_t M, int64_t K, float t
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Top-k decomposition: the outlier set is the k columns with the largest
+// column maximum, equal maxima taken in ascending column order.  One block
+// of 1024 threads, after the scan above with no threshold: it merges the
+// segments' partial maxima into LDS (K <= TOPK_MAXK), finds the k-th largest
+// value by a radix select (four 8-bit digits, most significant first; the
+// maxima are non-negative, so their bit patterns order like the values), and
+// writes the selection as segment 0's flag words (the scan left the other
+// segments' words zero), so the flag consumers see exactly the top-k set.
+// ---------------------------------------------------------------------------
+constexpr int TOPK_MAXK = 32768;
+constexpr int TOPK_THREADS = 1024;
+
+__global__ __launch_bounds__(TOPK_THREADS) void k_topk_select(unsigned long long* __restrict__ flags_p,
+                                                              uint32_t* __restrict__ cmax_p, int nseg, int64_t K,
+                                                              int64_t k) {
+    __shared__ uint32_t vals[TOPK_MAXK];
+    __shared__ uint32_t hist[256];
+    __shared__ uint32_t wsum[TOPK_THREADS / 64];
+    __shared__ uint32_t sel[2];                         // digit found, count above it
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int64_t nw = (K + 63) / 64;
+    for (int64_t j = t; j < K; j += TOPK_THREADS) {
+        uint32_t m = 0u;
+#pragma unroll
+        for (int sg = 0; sg < OC_SEG_MAX; ++sg)
+            if (sg < nseg) m = max(m, cmax_p[(int64_t)sg * K + j]);
+        vals[j] = m;
+    }
+    // k-th largest value: prefix of the digits fixed so far
+    uint32_t prefix = 0u, pmask = 0u, remaining = (uint32_t)k;
+    for (int shift = 24; shift >= 0 && k > 0; shift -= 8) {
+        for (int i = t; i < 256; i += TOPK_THREADS) hist[i] = 0u;
+        __syncthreads();
+        for (int64_t j = t; j < K; j += TOPK_THREADS) {
+            const uint32_t v = vals[j];
+            if ((v & pmask) == prefix) atomicAdd(&hist[(v >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // lane l holds digits 255 - 4l .. 252 - 4l; inclusive sums from the top
+            uint32_t h[4], c = 0u;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                h[i] = hist[255 - 4 * lane - i];
+                c += h[i];
+            }
+            uint32_t incl = c;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t y = (uint32_t)__shfl_up((int)incl, o, QA_WAVE);
+                if (lane >= o) incl += y;
+            }
+            uint32_t above = incl - c;                  // count in digits above this lane's four
+            const bool mine = above < remaining && remaining <= incl;
+            if (mine) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (above + h[i] >= remaining) {
+                        sel[0] = 255u - 4u * lane - i;
+                        sel[1] = above;
+                        break;
+                    }
+                    above += h[i];
+                }
+            }
+        }
+        __syncthreads();
+        prefix |= sel[0] << shift;
+        pmask |= 255u << shift;
+        remaining -= sel[1];
+        __syncthreads();
+    }
+    // remaining = how many columns equal to the k-th value are taken (lowest first)
+    const uint32_t kth = prefix;
+    const int64_t per = (nw + TOPK_THREADS - 1) / TOPK_THREADS;  // flag words per thread
+    const int64_t w0 = (int64_t)t * per, w1 = w0 + per < nw ? w0 + per : nw;
+    uint32_t ties = 0u;
+    for (int64_t w = w0; w < w1; ++w)
+        for (int b = 0; b < 64; ++b) {
+            const int64_t j = w * 64 + b;
+            ties += (k > 0 && j < K && vals[j] == kth) ? 1u : 0u;
+        }
+    // exclusive scan of the tie counts in column order
+    uint32_t x = ties;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = (uint32_t)__shfl_up((int)x, o, QA_WAVE);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    uint32_t before = x - ties;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    for (int64_t w = w0; w < w1; ++w) {
+        unsigned long long word = 0ull;
+        for (int b = 0; b < 64; ++b) {
+            const int64_t j = w * 64 + b;
+            if (k <= 0 || j >= K) continue;
+            const uint32_t v = vals[j];
+            bool take = v > kth;
+            if (v == kth) {
+                take = before < remaining;
+                ++before;
+            }
+            if (take) word |= 1ull << b;
+        }
+        flags_p[w] = word;
+    }
+}
+
+hipError_t launch_outlier_topk_flags(const uint16_t* X, int64_t M, int64_t K, int64_t k, void* scratch, int* segs,
+                                     hipStream_t st) {
+    *segs = outlier_scan(X, M, K, __builtin_inff(), scratch, true, st);
+    unsigned long long* flags_p = static_cast<unsigned long long*>(scratch);
+    uint32_t* cmax_p = reinterpret_cast<uint32_t*>(flags_p + OC_SEG_MAX * ((K + 63) / 64));
+    hipLaunchKernelGGL(k_topk_select, dim3(1), dim3(TOPK_THREADS), 0, st, flags_p, cmax_p, *segs, K, k);
+    return hipGetLastError();
+}
+
+hipError_t launch_outlier_topk(const uint16_t* X, int64_t M, int64_t K, int64_t k, uint8_t* mask, int32_t* idx,
+                               int32_t* count, float* colmax, void* scratch, hipStream_t st) {
+    int segs = 1;
+    hipError_t e = launch_outlier_topk_flags(X, M, K, k, scratch, &segs, st);
+    if (e != hipSuccess) return e;
+    unsigned long long* flags_p = static_cast<unsigned long long*>(scratch);
+    const uint32_t* cmax_p = reinterpret_cast<const uint32_t*>(flags_p + OC_SEG_MAX * ((K + 63) / 64));
+    hipLaunchKernelGGL(k_outlier_finalize, dim3(1), dim3(256), 0, st, flags_p, cmax_p, segs, K, mask, idx, count,
+                       colmax);
+    return hipGetLastError();
+}
+
+int64_t topk_max_columns() { return TOPK_MAXK; }
+
 // Column absolute maxima (the activation and weight statistics of the
 // SmoothQuant migration): the scan above with no threshold, then one thread
 // per column maxes the segments' partial maxima (and the caller's running

@@ -137,6 +137,25 @@ qa_status qa_outlier_cols(const void* X_f16, int64_t M, int64_t K, float thresho
                          "qa_outlier_cols");
 }
 
+qa_status qa_outlier_topk(const void* X_f16, int64_t M, int64_t K, int64_t k, uint8_t* mask, int32_t* idx,
+                          int32_t* count, float* colmax_or_null, void* scratch, size_t scratch_bytes, void* stream) {
+    if (M < 0 || K <= 0 || K % 8 != 0 || K > qa::topk_max_columns())
+        return fail(QA_ERR_SHAPE, "qa_outlier_topk: need M >= 0, 0 < K <= %lld, K %% 8 == 0 (M=%lld K=%lld)",
+                    (long long)qa::topk_max_columns(), (long long)M, (long long)K);
+    if (k < 0 || k > K) return fail(QA_ERR_VALUE, "qa_outlier_topk: need 0 <= k <= K (k=%lld)", (long long)k);
+    if ((M > 0 && !X_f16) || !mask || !idx || !count || !scratch)
+        return fail(QA_ERR_NULL, "qa_outlier_topk: NULL pointer");
+    if (!aligned(X_f16, 16) || !aligned(idx, 4) || !aligned(count, 4) || !aligned(scratch, 8) ||
+        (colmax_or_null && !aligned(colmax_or_null, 4)))
+        return fail(QA_ERR_ALIGN, "qa_outlier_topk: X must be 16-byte aligned, scratch 8-byte, idx/count/colmax 4-byte");
+    if (scratch_bytes < qa_outlier_cols_workspace(K))
+        return fail(QA_ERR_WORKSPACE, "qa_outlier_topk: scratch %zu < %zu bytes", scratch_bytes,
+                    qa_outlier_cols_workspace(K));
+    return device_status(qa::launch_outlier_topk(static_cast<const uint16_t*>(X_f16), M, K, k, mask, idx, count,
+                                                 colmax_or_null, scratch, as_stream(stream)),
+                         "qa_outlier_topk");
+}
+
 // ----------------------------------------------------------------- row quant
 qa_status qa_quantize_rowwise_int8(const void* X_f16, int64_t rows, int64_t K, const uint8_t* mask_or_null,
                                    int32_t q_min, int32_t q_max, const float* s_in_or_null,
@@ -221,6 +240,51 @@ qa_status qa_qlinear_int8_mixed(const void* X_f16, int64_t M, int64_t K, const i
     ep.ldo = N;
     ep.out_dtype = (int)out_dtype;
     return device_status(qa::launch_gemm_i8_mixed(xq, Wq, M, K, N, ep, st), "qa_qlinear_int8_mixed (gemm)");
+}
+
+// ----------------------------------------------------------------- top-k mixed linear
+size_t qa_qlinear_int8_topk_workspace(int64_t M, int64_t K) { return qa_qlinear_int8_mixed_workspace(M, K); }
+
+qa_status qa_qlinear_int8_topk(const void* X_f16, int64_t M, int64_t K, int64_t k, const int8_t* Wq, const float* s_w,
+                               const void* W_f16_or_null, int64_t N, void* out, qa_dtype out_dtype, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    if (M < 0 || N < 0 || K <= 0 || K % 16 != 0 || K > qa::topk_max_columns())
+        return fail(QA_ERR_SHAPE, "qa_qlinear_int8_topk: need M, N >= 0, 0 < K <= %lld, K %% 16 == 0",
+                    (long long)qa::topk_max_columns());
+    if (k < 0 || k > K) return fail(QA_ERR_VALUE, "qa_qlinear_int8_topk: need 0 <= k <= K (k=%lld)", (long long)k);
+    if (!valid_dtype(out_dtype)) return fail(QA_ERR_VALUE, "qa_qlinear_int8_topk: bad out_dtype %d", (int)out_dtype);
+    if (M == 0 || N == 0) return ok();
+    if (!X_f16 || !Wq || !s_w || !out || !workspace) return fail(QA_ERR_NULL, "qa_qlinear_int8_topk: NULL pointer");
+    if (!aligned(X_f16, 16) || !aligned(Wq, 16) || !aligned(s_w, 4) || !aligned(workspace, kAlign) ||
+        (W_f16_or_null && !aligned(W_f16_or_null, 2)) || !aligned(out, 4))
+        return fail(QA_ERR_ALIGN, "qa_qlinear_int8_topk: X, Wq 16-byte, workspace 256-byte, out/s_w 4-byte aligned");
+    const MixedLayout L = mixed_layout(M, K);
+    if (workspace_bytes < L.total)
+        return fail(QA_ERR_WORKSPACE, "qa_qlinear_int8_topk: workspace %zu < %zu bytes", workspace_bytes, L.total);
+    const uint16_t* X = static_cast<const uint16_t*>(X_f16);
+    hipStream_t st = as_stream(stream);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    int32_t* idx = reinterpret_cast<int32_t*>(ws + L.idx);
+    int32_t* count = reinterpret_cast<int32_t*>(ws + L.count);
+    float* s_x = reinterpret_cast<float*>(ws + L.s_x);
+    int8_t* xq = reinterpret_cast<int8_t*>(ws + L.xq);
+    int segs = 1;
+    hipError_t e = qa::launch_outlier_topk_flags(X, M, K, k, ws + L.cmax, &segs, st);
+    if (e != hipSuccess) return device_status(e, "qa_qlinear_int8_topk (top-k columns)");
+    e = qa::launch_rowquant_i8_flags(X, M, K, ws + L.cmax, segs, xq, s_x, idx, count, st);
+    if (e != hipSuccess) return device_status(e, "qa_qlinear_int8_topk (row quantization)");
+    qa::MixedEpilogue ep;
+    ep.s_x = s_x;
+    ep.s_w = s_w;
+    ep.X = X;
+    ep.W16 = static_cast<const uint16_t*>(W_f16_or_null);
+    ep.Wq = Wq;
+    ep.idx = idx;
+    ep.count = count;
+    ep.out = out;
+    ep.ldo = N;
+    ep.out_dtype = (int)out_dtype;
+    return device_status(qa::launch_gemm_i8_mixed(xq, Wq, M, K, N, ep, st), "qa_qlinear_int8_topk (gemm)");
 }
 
 // ----------------------------------------------------------------- SmoothQuant

@@ -36,6 +36,15 @@ hipError_t launch_rowquant_i8_flags(const uint16_t* X, int64_t rows, int64_t K, 
 hipError_t launch_rowquant_i8_no_outliers(const uint16_t* X, int64_t rows, int64_t K, int8_t* q, float* s_out,
                                           int32_t* count, hipStream_t st);
 
+// Top-k decomposition: the k columns with the largest column maximum (ties
+// to the lower column) as the outlier set.  K <= topk_max_columns().
+int64_t topk_max_columns();
+hipError_t launch_outlier_topk(const uint16_t* X, int64_t M, int64_t K, int64_t k, uint8_t* mask, int32_t* idx,
+                               int32_t* count, float* colmax, void* scratch, hipStream_t st);
+// Flag words only (consumed by launch_rowquant_i8_flags with *segs sets).
+hipError_t launch_outlier_topk_flags(const uint16_t* X, int64_t M, int64_t K, int64_t k, void* scratch, int* segs,
+                                     hipStream_t st);
+
 // Column absolute maxima of A [rows x K] (maxed into colmax when accumulating);
 // scratch as for the outlier scan.
 hipError_t launch_col_absmax(const uint16_t* A, int64_t rows, int64_t K, float* colmax, bool accumulate,

@@ -21,6 +21,8 @@
  *   [AIInfra-Q01]  Infrasys-AI "AIInfra" notes, page 05Quantization01 (模型量化):
  *                  the LLM.int8() method -- outlier detection, "a. 向量级量化",
  *                  "b. INT8 矩阵乘法与反量化", merge of the two parts.
+ *                  Its advice for training: decompose the largest-magnitude
+ *                  1-2% of feature dimensions instead of about 0.1% (top-k).
  *   [Scholia-IQ]   "模型推理量化" (Inference Quantization notes): §4 Scale,
  *                  §5 Outlier, §6 Zero-point (§6.2 affine clip), §7 Granularity.
  *   [GroupRot]     "低比特量化加速：分组旋转方法从W8A8到W4A4的实践与展望":
@@ -108,6 +110,22 @@ qa_status qa_outlier_cols(const void* X_f16, int64_t M, int64_t K, float thresho
                           void* scratch, size_t scratch_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Top-k outlier columns  [AIInfra-Q01: decompose the largest-magnitude 1-2%
+ * of feature dimensions]
+ *
+ * Same outputs as qa_outlier_cols, but the set is the k columns with the
+ * largest colmax[j] = max_i |X[i][j]|; equal maxima are taken in ascending
+ * column order, so exactly k columns are chosen.  k = ceil(p K) decomposes
+ * the share p of the dimensions.
+ *   scratch qa_outlier_cols_workspace(K) bytes (any content)
+ * Errors: as qa_outlier_cols, plus K > 32768 (QA_ERR_SHAPE), k < 0 or
+ * k > K (QA_ERR_VALUE).
+ * ------------------------------------------------------------------------- */
+qa_status qa_outlier_topk(const void* X_f16, int64_t M, int64_t K, int64_t k, uint8_t* mask, int32_t* idx,
+                          int32_t* count, float* colmax_or_null, void* scratch, size_t scratch_bytes,
+                          void* stream);
+
+/* ---------------------------------------------------------------------------
  * Row-wise int8 quantization  [AIInfra-Q01 "a. 向量级量化"; Scholia-IQ §4,
  * §6.2]
  *
@@ -158,6 +176,23 @@ qa_status qa_qlinear_int8_mixed(const void* X_f16, int64_t M, int64_t K,
                                 const int8_t* Wq, const float* s_w, const void* W_f16_or_null,
                                 int64_t N, float threshold, void* out, qa_dtype out_dtype,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * LLM.int8() linear with top-k decomposition  [AIInfra-Q01: decomposition
+ * share raised to the top 1-2% of feature dimensions]
+ *
+ * qa_qlinear_int8_mixed with O = the k columns of qa_outlier_topk instead of
+ * the threshold set; everything else (scales, codes, GEMM, fp16 outlier
+ * product) is identical.  k = 0 is plain vector-wise W8A8; k = K sends every
+ * column through the fp16 product.
+ *   workspace  qa_qlinear_int8_topk_workspace(M, K) bytes (any content)
+ * Errors: as qa_qlinear_int8_mixed (no threshold), plus K > 32768
+ * (QA_ERR_SHAPE), k < 0 or k > K (QA_ERR_VALUE).
+ * ------------------------------------------------------------------------- */
+size_t qa_qlinear_int8_topk_workspace(int64_t M, int64_t K);
+qa_status qa_qlinear_int8_topk(const void* X_f16, int64_t M, int64_t K, int64_t k, const int8_t* Wq,
+                               const float* s_w, const void* W_f16_or_null, int64_t N, void* out,
+                               qa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Block Hadamard rotation fused with int4 quantization and packing

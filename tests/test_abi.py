@@ -231,3 +231,44 @@ def test_smooth_linear_argument_errors():
     L = qa.lib()
     for M, K in [(1, 16), (2048, 4096)]:
         assert L.qa_qlinear_int8_smooth_workspace(M, K) >= M * K + 4 * M + 4
+
+
+def test_outlier_topk_argument_errors():
+    f = qa.lib().qa_outlier_topk
+    args = [A, 16, 256, 3, B, OUT, WS, None, WS, 1 << 20, None]
+
+    def call(i, v):
+        a = list(args)
+        a[i] = v
+        return f(*a)
+    assert call(0, None) == NULL
+    assert call(8, None) == NULL
+    assert call(2, 12) == SHAPE
+    assert call(2, 32776) == SHAPE                             # beyond the LDS-resident selection
+    assert call(1, -1) == SHAPE
+    assert call(3, -1) == VALUE
+    assert call(3, 257) == VALUE
+    assert call(0, MIS) == ALIGN
+    assert call(9, 16) == WORKSPACE
+
+
+def test_topk_linear_argument_errors():
+    f = qa.lib().qa_qlinear_int8_topk
+    base = [A, 16, 256, 4, B, OUT, None, 32, OUT, 1, WS, 1 << 30, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+    assert call(0, None) == NULL
+    assert call(10, None) == NULL
+    assert call(2, 24) == SHAPE
+    assert call(2, 32784) == SHAPE
+    assert call(3, -2) == VALUE
+    assert call(3, 300) == VALUE
+    assert call(9, 5) == VALUE
+    assert call(4, MIS) == ALIGN
+    assert call(11, 64) == WORKSPACE
+    assert call(1, 0) == OK and call(7, 0) == OK
+    assert qa.lib().qa_qlinear_int8_topk_workspace(64, 512) == qa.lib().qa_qlinear_int8_mixed_workspace(64, 512)
+    assert qa.topk_count(0.01, 4096) == 41 and qa.topk_count(0.02, 4096) == 82 and qa.topk_count(0.0, 64) == 0
