@@ -12,8 +12,9 @@ moved per step / step time (GB/s).
 
 Also reported (same JSON line, key "also"): whole-call throughput of the
 prefill-shape mixed linear, the W8A8 FFN shape, the W4A4 group-Hadamard
-linear and the SmoothQuant W8A8 linear on the prefill and FFN data, in int8
-TOPS against the dense int8 MFMA peak.
+linear, the SmoothQuant W8A8 linear on the prefill and FFN data and the
+top-2% decomposition on the prefill data, in int8 TOPS against the dense
+int8 MFMA peak.
 
 roofline: the decode kernel's algorithmic bytes per launch / its average
 launch duration, from HIP events recorded on the launch stream around the
@@ -51,7 +52,8 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--only", default=None,
-                   help="run one workload only (decode|prefill|w8a8|w4a4|smooth_prefill|smooth_ffn|copy), for "
+                   help="run one workload only (decode|prefill|w8a8|w4a4|smooth_prefill|smooth_ffn|topk_prefill|"
+                        "copy), for "
                         "profiling; copy is a plain "
                         "1 GiB device copy used to calibrate HBM byte counters")
     return p.parse_args()
@@ -175,6 +177,21 @@ def smooth_workload(torch, qa, synthetic, dev, name, per_tensor):
     return c, fns, 2 * M * N * K
 
 
+def topk_workload(torch, qa, synthetic, dev, name, share):
+    """LLM.int8() with the top `share` of the K dimensions decomposed (instead
+    of the threshold) on a workload's data."""
+    c = synthetic.config(name)
+    M, K, N = c["M"], c["K"], c["N"]
+    X = torch.from_numpy(c["X"]).to(dev)
+    Wq, s_w = qa.qa_quantize_rowwise_int8(torch.from_numpy(c["W"]).to(dev))
+    k = qa.topk_count(share, K)
+    odt = {0: torch.float32, 1: torch.float16, 2: torch.bfloat16}[c["out_dtype"]]
+    out = torch.empty((M, N), dtype=odt, device=dev)
+    ws = torch.empty(qa.qa_qlinear_int8_topk_workspace(M, K), dtype=torch.uint8, device=dev)
+    fns = [lambda: qa.qa_qlinear_int8_topk(X, Wq, s_w, k, out=out, workspace=ws)]
+    return c, fns, 2 * M * N * K, k
+
+
 def w4a4_workload(torch, qa, synthetic, dev):
     c = synthetic.config("w4a4_hadamard")
     M, K, N, G = c["M"], c["K"], c["N"], c["G"]
@@ -269,12 +286,13 @@ def main():
         del fns, gs
         torch.cuda.empty_cache()
 
-    keys = ("prefill", "w8a8", "w4a4", "smooth_prefill", "smooth_ffn")
+    keys = ("prefill", "w8a8", "w4a4", "smooth_prefill", "smooth_ffn", "topk_prefill")
     run_also = (args.only is None and not args.no_also) or args.only in keys
     if run_also:
         todo = []
         for name, key in (("prefill_mixed", "prefill"), ("w8a8_ffn", "w8a8"), ("w4a4_hadamard", "w4a4"),
-                          ("prefill_mixed", "smooth_prefill"), ("w8a8_ffn", "smooth_ffn")):
+                          ("prefill_mixed", "smooth_prefill"), ("w8a8_ffn", "smooth_ffn"),
+                          ("prefill_mixed", "topk_prefill")):
             if args.only in (None, key):
                 todo.append((name, key))
         for name, key in todo:
@@ -284,6 +302,9 @@ def main():
             elif key == "smooth_prefill":
                 c, fns, ops = smooth_workload(torch, qa, synthetic, dev, name, per_tensor=False)
                 name = "smoothquant_prefill: X/s per-token int8, %s data" % name
+            elif key == "topk_prefill":
+                c, fns, ops, k = topk_workload(torch, qa, synthetic, dev, name, 0.02)
+                name = "topk_prefill: LLM.int8() with the top 2%% (%d) of dims in fp16, %s data" % (k, name)
             elif key == "smooth_ffn":
                 c, fns, ops = smooth_workload(torch, qa, synthetic, dev, name, per_tensor=True)
                 name = "smoothquant_ffn: X/s per-tensor int8, %s data" % name

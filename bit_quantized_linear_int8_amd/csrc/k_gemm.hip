@@ -399,7 +399,7 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_i8_mixed(const int8_t* __re
     // Up to PRE outlier columns: the list is read here with the scales, and
     // the gather of this thread's row of X or w~ is issued in the main loop's
     // hook, behind the first stages' loads; the values wait in registers.
-    constexpr int PRE = 8;
+    constexpr int PRE = OUTLIER_PREFETCH;
     static_assert(C::THREADS >= C::BM + C::BN, "one thread per gathered row");
     const rsrc_t rxo = make_rsrc(ep.X + m0 * K, (M - m0) * K * 2);
     const rsrc_t rwo = ep.W16 ? make_rsrc(ep.W16 + n0 * K, (N - n0) * K * 2) : make_rsrc(ep.Wq + n0 * K, (N - n0) * K);
@@ -438,22 +438,65 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_i8_mixed(const int8_t* __re
     // passes.  One thread owns one row of X or W and loads only real columns.
     constexpr int OCAP = 96;
     constexpr int OST = OCAP + 8;                             // padded row stride (halves)
-    static_assert((C::BM + C::BN) * OST * 2 <= C::LDS, "outlier staging exceeds LDS");
     _Float16* xo = reinterpret_cast<_Float16*>(smem);         // [BM][OST], then [BN][OST] for w~
+    // One pass of up to OCAP outlier columns into LDS.  The pass's column
+    // list (and the weight rows' scales) go to LDS first.  X rows come from
+    // the compact outlier rows (contiguous 16-byte loads) when the row
+    // quantizer wrote them, else they are gathered like the weight rows: a
+    // thread owns one column of a 32-column slab and RSTEP-spaced rows, and
+    // issues 8 gathers before it writes any, so a pass costs a few load
+    // latencies (the accumulators are live here, so registers are scarce).
+    constexpr int RSTEP = C::THREADS / 32;
+    constexpr int GB = 8;                                     // gathers in flight per thread
+    int* hidx = reinterpret_cast<int*>(smem + (C::BM + C::BN) * OST * 2);
+    float* swl = reinterpret_cast<float*>(hidx + OCAP);
+    static_assert((C::BM + C::BN) * OST * 2 + (OCAP + C::BN) * 4 <= C::LDS, "outlier staging exceeds LDS");
+    const bool use_xo = ep.Xo != nullptr && cnt <= XO_CAP;
     auto stage = [&](int hs) __attribute__((always_inline)) {
         const int hn = cnt - hs < OCAP ? cnt - hs : OCAP;
         const int hp = (hn + 31) & ~31;
-        const rsrc_t ridx = make_rsrc(ep.idx + hs, (int64_t)hn * 4);
-        for (int r = threadIdx.x; r < C::BM + C::BN; r += C::THREADS) {
-            const bool isx = r < C::BM;
-            const uint32_t rr = isx ? r : r - C::BM;
-            const float swr = isx || ep.W16 ? 0.0f : __builtin_bit_cast(float, bload4(rsn, rr * 4));
-            for (int h = 0; h < hp; h += 8) {
-                uint32_t v[8];
+        {
+            const rsrc_t ridx = make_rsrc(ep.idx + hs, (int64_t)hn * 4);
+            for (int h = threadIdx.x; h < hp; h += C::THREADS) hidx[h] = (int)bload4(ridx, (uint32_t)h * 4);
+            if (!ep.W16)
+                for (int r = threadIdx.x; r < C::BN; r += C::THREADS)
+                    swl[r] = __builtin_bit_cast(float, bload4(rsn, (uint32_t)r * 4));
+        }
+        if (use_xo) {
+            const rsrc_t rxc = make_rsrc(ep.Xo + m0 * XO_CAP, (M - m0) * XO_CAP * 2);
+            const int c = threadIdx.x & 3;
+            for (int hq = 0; hq < hp; hq += 32) {
+                const int h = hq + 8 * c;
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const uint32_t k = bload4(ridx, (uint32_t)(h + u) * 4);   // zero past hn
-                    const bool ok = h + u < hn;
+                for (int r0 = 0; r0 < C::BM; r0 += C::THREADS / 4) {
+                    const int r = r0 + (threadIdx.x >> 2);
+                    if (r < C::BM) {
+                        u32x4 v = bload16(rxc, (uint32_t)(r * XO_CAP + hs + h) * 2);
+#pragma unroll
+                        for (int d = 0; d < 4; ++d) {
+                            const uint32_t lo = h + 2 * d < hn ? 0xffffu : 0u;
+                            const uint32_t hi = h + 2 * d + 1 < hn ? 0xffff0000u : 0u;
+                            v[d] &= lo | hi;
+                        }
+                        *reinterpret_cast<u32x4*>(xo + r * OST + h) = v;
+                    }
+                }
+            }
+        }
+        __syncthreads();                                      // the column list
+        const int hl = threadIdx.x & 31, rs = threadIdx.x >> 5;
+        for (int hq = 0; hq < hp; hq += 32) {
+            const int h = hq + hl;
+            const bool hok = h < hn;
+            const uint32_t k = (uint32_t)hidx[h];
+            for (int rb = use_xo ? C::BM : 0; rb < C::BM + C::BN; rb += RSTEP * GB) {
+                uint32_t v[GB];
+#pragma unroll
+                for (int u = 0; u < GB; ++u) {
+                    const int r = rb + rs + RSTEP * u;
+                    const bool ok = hok && r < C::BM + C::BN;
+                    const bool isx = r < C::BM;
+                    const uint32_t rr = isx ? r : r - C::BM;
                     if (isx)
                         v[u] = bload2(rxo, ok ? (rr * (uint32_t)K + k) * 2 : kOOB);
                     else if (ep.W16)
@@ -462,10 +505,13 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_i8_mixed(const int8_t* __re
                         v[u] = bload1(rwo, ok ? rr * (uint32_t)K + k : kOOB);
                 }
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    uint16_t hv = (uint16_t)v[u];
-                    if (!isx && !ep.W16) hv = h + u < hn ? f2h(swr * (float)(int8_t)(uint8_t)v[u]) : 0;
-                    xo[r * OST + h + u] = __builtin_bit_cast(_Float16, hv);
+                for (int u = 0; u < GB; ++u) {
+                    const int r = rb + rs + RSTEP * u;
+                    if (r < C::BM + C::BN) {
+                        uint16_t hv = (uint16_t)v[u];
+                        if (r >= C::BM && !ep.W16) hv = hok ? f2h(swl[r - C::BM] * (float)(int8_t)(uint8_t)v[u]) : 0;
+                        xo[r * OST + h] = __builtin_bit_cast(_Float16, hv);
+                    }
                 }
             }
         }

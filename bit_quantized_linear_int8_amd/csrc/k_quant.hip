@@ -210,59 +210,91 @@ hipError_t launch_outlier_flags(const uint16_t* X, int64_t M, int64_t K, float t
 // ---------------------------------------------------------------------------
 // Top-k decomposition: the outlier set is the k columns with the largest
 // column maximum, equal maxima taken in ascending column order.  One block
-// of 1024 threads, after the scan above with no threshold: it merges the
-// segments' partial maxima into LDS (K <= TOPK_MAXK), finds the k-th largest
-// value by a radix select (four 8-bit digits, most significant first; the
-// maxima are non-negative, so their bit patterns order like the values), and
-// writes the selection as segment 0's flag words (the scan left the other
-// segments' words zero), so the flag consumers see exactly the top-k set.
+// of 1024 threads, after the scan above with no threshold.  The maxima are
+// fp16 magnitudes, so a 15-bit key (the sign-cleared fp16 pattern, which
+// orders like the value) identifies each; the block merges the segments'
+// partial maxima into LDS keys (K <= TOPK_MAXK), finds the k-th largest key
+// by a two-pass radix select (bits 14..8, then 7..0) with one histogram per
+// wave (same-bin LDS atomics then only collide inside a wave), ranks the
+// ties in column order with a block scan, and writes the selection as
+// segment 0's flag words (the scan left the other segments' words zero), so
+// the flag consumers see exactly the top-k set.  Thread t owns the TC
+// consecutive columns [t TC, t TC + TC), TC = K / 1024 rounded up to a power
+// of two, so a flag word is assembled from 64 / TC threads.
 // ---------------------------------------------------------------------------
 constexpr int TOPK_MAXK = 32768;
 constexpr int TOPK_THREADS = 1024;
+constexpr int TOPK_WAVES = TOPK_THREADS / 64;
 
 __global__ __launch_bounds__(TOPK_THREADS) void k_topk_select(unsigned long long* __restrict__ flags_p,
-                                                              uint32_t* __restrict__ cmax_p, int nseg, int64_t K,
-                                                              int64_t k) {
-    __shared__ uint32_t vals[TOPK_MAXK];
-    __shared__ uint32_t hist[256];
-    __shared__ uint32_t wsum[TOPK_THREADS / 64];
+                                                              const uint32_t* __restrict__ cmax_p, int nseg,
+                                                              int64_t K, int64_t k) {
+    __shared__ uint16_t keys[TOPK_MAXK];
+    __shared__ uint32_t hist[TOPK_WAVES][256];
+    __shared__ unsigned long long wout[TOPK_MAXK / 64];
+    __shared__ uint32_t wsum[TOPK_WAVES];
     __shared__ uint32_t sel[2];                         // digit found, count above it
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int64_t nw = (K + 63) / 64;
-    for (int64_t j = t; j < K; j += TOPK_THREADS) {
-        uint32_t m = 0u;
+    // merge the segments: four columns per thread and pass, all 4 x OC_SEG_MAX
+    // loads in flight before the first is used (out-of-range ones read 0)
+    const rsrc_t rc = make_rsrc(cmax_p, (int64_t)nseg * K * 4);
+    for (int64_t j0 = 0; j0 < K; j0 += 4 * TOPK_THREADS) {
+        uint32_t v[4][OC_SEG_MAX];
 #pragma unroll
-        for (int sg = 0; sg < OC_SEG_MAX; ++sg)
-            if (sg < nseg) m = max(m, cmax_p[(int64_t)sg * K + j]);
-        vals[j] = m;
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int sg = 0; sg < OC_SEG_MAX; ++sg) {
+                const int64_t j = j0 + u * TOPK_THREADS + t;
+                v[u][sg] = bload4(rc, sg < nseg && j < K ? (uint32_t)(sg * K + j) * 4 : kOOB);
+            }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            uint32_t m = 0u;
+#pragma unroll
+            for (int sg = 0; sg < OC_SEG_MAX; ++sg) m = max(m, v[u][sg]);
+            const int64_t j = j0 + u * TOPK_THREADS + t;
+            if (j < K) keys[j] = f2h(__builtin_bit_cast(float, m));   // exact: m is an fp16 magnitude
+        }
     }
-    // k-th largest value: prefix of the digits fixed so far
+    for (int64_t w = t; w < nw; w += TOPK_THREADS) wout[w] = 0ull;
+    int tc = 1;                                          // columns per thread, a power of two
+    while ((int64_t)tc * TOPK_THREADS < K) tc <<= 1;
+    const int64_t c0 = (int64_t)t * tc;
+    // k-th largest key: digits fixed so far in `prefix` (under `pmask`)
     uint32_t prefix = 0u, pmask = 0u, remaining = (uint32_t)k;
-    for (int shift = 24; shift >= 0 && k > 0; shift -= 8) {
-        for (int i = t; i < 256; i += TOPK_THREADS) hist[i] = 0u;
+    for (int pass = 0; pass < 2 && k > 0; ++pass) {
+        const int shift = pass == 0 ? 8 : 0;
+        for (int i = lane; i < 256; i += 64) hist[wave][i] = 0u;
         __syncthreads();
-        for (int64_t j = t; j < K; j += TOPK_THREADS) {
-            const uint32_t v = vals[j];
-            if ((v & pmask) == prefix) atomicAdd(&hist[(v >> shift) & 255u], 1u);
+        for (int c = 0; c < tc; ++c) {
+            const int64_t j = c0 + c;
+            if (j < K) {
+                const uint32_t key = keys[j];
+                if ((key & pmask) == prefix) atomicAdd(&hist[wave][(key >> shift) & 255u], 1u);
+            }
         }
         __syncthreads();
         if (wave == 0) {
-            // lane l holds digits 255 - 4l .. 252 - 4l; inclusive sums from the top
-            uint32_t h[4], c = 0u;
+            // lane l holds digits 255 - 4l .. 252 - 4l, summed over the waves;
+            // inclusive sums from the top digit down
+            uint32_t h[4], cs = 0u;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                h[i] = hist[255 - 4 * lane - i];
-                c += h[i];
+                uint32_t a = 0u;
+#pragma unroll
+                for (int w = 0; w < TOPK_WAVES; ++w) a += hist[w][255 - 4 * lane - i];
+                h[i] = a;
+                cs += a;
             }
-            uint32_t incl = c;
+            uint32_t incl = cs;
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) {
                 const uint32_t y = (uint32_t)__shfl_up((int)incl, o, QA_WAVE);
                 if (lane >= o) incl += y;
             }
-            uint32_t above = incl - c;                  // count in digits above this lane's four
-            const bool mine = above < remaining && remaining <= incl;
-            if (mine) {
+            uint32_t above = incl - cs;                 // count in digits above this lane's four
+            if (above < remaining && remaining <= incl) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     if (above + h[i] >= remaining) {
@@ -280,18 +312,14 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk_select(unsigned long long
         remaining -= sel[1];
         __syncthreads();
     }
-    // remaining = how many columns equal to the k-th value are taken (lowest first)
+    // remaining = how many columns equal to the k-th key are taken (lowest first)
     const uint32_t kth = prefix;
-    const int64_t per = (nw + TOPK_THREADS - 1) / TOPK_THREADS;  // flag words per thread
-    const int64_t w0 = (int64_t)t * per, w1 = w0 + per < nw ? w0 + per : nw;
     uint32_t ties = 0u;
-    for (int64_t w = w0; w < w1; ++w)
-        for (int b = 0; b < 64; ++b) {
-            const int64_t j = w * 64 + b;
-            ties += (k > 0 && j < K && vals[j] == kth) ? 1u : 0u;
-        }
-    // exclusive scan of the tie counts in column order
-    uint32_t x = ties;
+    for (int c = 0; c < tc; ++c) {
+        const int64_t j = c0 + c;
+        ties += (k > 0 && j < K && keys[j] == kth) ? 1u : 0u;
+    }
+    uint32_t x = ties;                                   // exclusive scan in column order
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
         const uint32_t y = (uint32_t)__shfl_up((int)x, o, QA_WAVE);
@@ -301,21 +329,21 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk_select(unsigned long long
     __syncthreads();
     uint32_t before = x - ties;
     for (int w = 0; w < wave; ++w) before += wsum[w];
-    for (int64_t w = w0; w < w1; ++w) {
-        unsigned long long word = 0ull;
-        for (int b = 0; b < 64; ++b) {
-            const int64_t j = w * 64 + b;
-            if (k <= 0 || j >= K) continue;
-            const uint32_t v = vals[j];
-            bool take = v > kth;
-            if (v == kth) {
-                take = before < remaining;
-                ++before;
-            }
-            if (take) word |= 1ull << b;
+    unsigned long long bits = 0ull;                      // this thread's columns, bit c = column c0 + c
+    for (int c = 0; c < tc; ++c) {
+        const int64_t j = c0 + c;
+        if (k <= 0 || j >= K) continue;
+        const uint32_t key = keys[j];
+        bool take = key > kth;
+        if (key == kth) {
+            take = before < remaining;
+            ++before;
         }
-        flags_p[w] = word;
+        if (take) bits |= 1ull << c;
     }
+    if (bits) atomicOr(&wout[c0 >> 6], bits << (c0 & 63));
+    __syncthreads();
+    for (int64_t w = t; w < nw; w += TOPK_THREADS) flags_p[w] = wout[w];
 }
 
 hipError_t launch_outlier_topk_flags(const uint16_t* X, int64_t M, int64_t K, int64_t k, void* scratch, int* segs,
@@ -438,9 +466,12 @@ __global__ __launch_bounds__(256) void k_rowquant_i8(const uint16_t* __restrict_
                                                      const uint8_t* __restrict__ mask, int nseg, int qmin, int qmax,
                                                      const float* __restrict__ s_in, const int32_t* __restrict__ z_in,
                                                      int8_t* __restrict__ q, float* __restrict__ s_out,
-                                                     int32_t* __restrict__ idx, int32_t* __restrict__ count) {
+                                                     int32_t* __restrict__ idx, int32_t* __restrict__ count,
+                                                     uint16_t* __restrict__ xo) {
     __shared__ u32x4 lut[MASK == MASK_FLAGS ? 256 : 1];
     __shared__ unsigned long long flw[MASK == MASK_FLAGS ? RQ_FLAG_WORDS : 1];
+    __shared__ uint32_t wpre[MASK == MASK_FLAGS && NC > 0 ? RQ_FLAG_WORDS : 1];
+    __shared__ uint32_t wtot[4];
     __shared__ int wsum[4];
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + wave_id();
@@ -464,7 +495,10 @@ __global__ __launch_bounds__(256) void k_rowquant_i8(const uint16_t* __restrict_
         lut[b] = k;
         const int64_t nw = (K + 63) / 64;
         const rsrc_t rf = make_rsrc(mask, (int64_t)nseg * nw * 8);
-        for (int64_t w = threadIdx.x; w < nw; w += 256) {
+        // thread t merges the flag words [t per, (t + 1) per)
+        const int64_t per = (nw + 255) / 256, w0 = (int64_t)threadIdx.x * per, w1 = w0 + per < nw ? w0 + per : nw;
+        uint32_t own = 0u;
+        for (int64_t w = w0; w < w1; ++w) {
             unsigned long long f = 0ull;
 #pragma unroll
             for (int sg = 0; sg < OC_SEG_MAX; ++sg) {         // all loads in flight at once
@@ -472,6 +506,25 @@ __global__ __launch_bounds__(256) void k_rowquant_i8(const uint16_t* __restrict_
                 f |= a[0] | ((unsigned long long)a[1] << 32);
             }
             flw[w] = f;
+            own += (uint32_t)__popcll(f);
+        }
+        if constexpr (NC > 0) {
+            if (xo) {
+                // rank of each flag word's first column in the outlier list,
+                // within its owner wave (the waves' totals are added when read)
+                uint32_t x = own;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const uint32_t y = (uint32_t)__shfl_up((int)x, o, QA_WAVE);
+                    if (lane >= o) x += y;
+                }
+                if (lane == 63) wtot[wave_id()] = x;
+                uint32_t run = x - own;
+                for (int64_t w = w0; w < w1; ++w) {
+                    wpre[w] = run;
+                    run += (uint32_t)__popcll(flw[w]);
+                }
+            }
         }
         __syncthreads();
         if (blockIdx.x == 0)
@@ -507,6 +560,34 @@ __global__ __launch_bounds__(256) void k_rowquant_i8(const uint16_t* __restrict_
         for (int i = 0; i < NC; ++i) {
             v[i] = vpre[i];
             mask_of(lane + 64 * i, v[i], mk[i]);
+        }
+        if constexpr (MASK == MASK_FLAGS) {
+            // this row's outlier values, in list order, into xo[row][0 .. XO_CAP),
+            // when the GEMM will read them (more columns than it prefetches)
+            const int64_t nw = (K + 63) / 64, per = (nw + 255) / 256;
+            const uint32_t t0 = wtot[0], t1 = wtot[1], t2 = wtot[2];
+            if (xo && t0 + t1 + t2 + wtot[3] > (uint32_t)OUTLIER_PREFETCH) {
+#pragma unroll
+                for (int i = 0; i < NC; ++i) {
+                    const int64_t ch = lane + 64 * i;
+                    const uint32_t fb = ch < nch ? flb[ch] : 0u;
+                    if (fb) {
+                        const int64_t w = ch >> 3;
+                        const int ow = (int)((w / per) >> 6);          // wave that ranked word w
+                        const uint32_t woff = (ow > 0 ? t0 : 0u) + (ow > 1 ? t1 : 0u) + (ow > 2 ? t2 : 0u);
+                        const unsigned long long fw = flw[w];
+                        const int sh = (int)(ch & 7) * 8;
+                        uint32_t rank = wpre[w] + woff + (uint32_t)__popcll(sh ? fw & ((1ull << sh) - 1ull) : 0ull);
+                        for (int b = 0; b < 8; ++b) {
+                            if ((fb >> b) & 1u) {
+                                if (rank < (uint32_t)XO_CAP)
+                                    xo[row * XO_CAP + rank] = (uint16_t)(vpre[i][b >> 1] >> (16 * (b & 1)));
+                                ++rank;
+                            }
+                        }
+                    }
+                }
+            }
         }
         if constexpr (!STATIC) {
             float amax = 0.0f;
@@ -576,11 +657,11 @@ __global__ __launch_bounds__(256) void k_rowquant_i8(const uint16_t* __restrict_
 template <bool STATIC, int MASK>
 static void rowquant_dispatch(const uint16_t* X, int64_t rows, int64_t K, const uint8_t* mask, int nseg, int qmin,
                               int qmax, const float* s_in, const int32_t* z_in, int8_t* q, float* s_out, int32_t* idx,
-                              int32_t* count, hipStream_t st) {
+                              int32_t* count, hipStream_t st, uint16_t* xo = nullptr) {
     const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
     const int64_t nch = K / 8;
 #define QA_RQ(NC) hipLaunchKernelGGL((k_rowquant_i8<NC, STATIC, MASK>), grid, block, 0, st, X, rows, K, mask, nseg, \
-                                     qmin, qmax, s_in, z_in, q, s_out, idx, count)
+                                     qmin, qmax, s_in, z_in, q, s_out, idx, count, xo)
     if (nch <= 64) QA_RQ(1);
     else if (nch <= 128) QA_RQ(2);
     else if (nch <= 256) QA_RQ(4);
@@ -604,10 +685,13 @@ hipError_t launch_rowquant_i8(const uint16_t* X, int64_t rows, int64_t K, const 
     return hipGetLastError();
 }
 
+bool rowquant_writes_xo(int64_t K) { return K / 8 <= 1024; }      // rows held in registers (NC > 0)
+
 hipError_t launch_rowquant_i8_flags(const uint16_t* X, int64_t rows, int64_t K, const void* scratch, int nseg,
-                                    int8_t* q, float* s_out, int32_t* idx, int32_t* count, hipStream_t st) {
+                                    int8_t* q, float* s_out, int32_t* idx, int32_t* count, uint16_t* xo,
+                                    hipStream_t st) {
     rowquant_dispatch<false, MASK_FLAGS>(X, rows, K, static_cast<const uint8_t*>(scratch), nseg, -127, 127, nullptr,
-                                         nullptr, q, s_out, idx, count, st);
+                                         nullptr, q, s_out, idx, count, st, rowquant_writes_xo(K) ? xo : nullptr);
     return hipGetLastError();
 }
 

@@ -50,7 +50,7 @@ constexpr int64_t kMaxK_quant = (int64_t)1 << 26;
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 struct MixedLayout {
-    size_t cmax, idx, count, s_x, xq, total;
+    size_t cmax, idx, count, s_x, xq, xo, total;
 };
 
 MixedLayout mixed_layout(int64_t M, int64_t K) {
@@ -61,6 +61,7 @@ MixedLayout mixed_layout(int64_t M, int64_t K) {
     L.count = off; off += up(4);
     L.s_x = off; off += up((size_t)M * 4);
     L.xq = off; off += up((size_t)M * (size_t)K);
+    L.xo = off; off += up((size_t)M * qa::XO_CAP * 2);
     L.total = off;
     return L;
 }
@@ -215,6 +216,7 @@ qa_status qa_qlinear_int8_mixed(const void* X_f16, int64_t M, int64_t K, const i
     int32_t* count = reinterpret_cast<int32_t*>(ws + L.count);
     float* s_x = reinterpret_cast<float*>(ws + L.s_x);
     int8_t* xq = reinterpret_cast<int8_t*>(ws + L.xq);
+    uint16_t* xo = reinterpret_cast<uint16_t*>(ws + L.xo);
 
     hipError_t e;
     if (!(threshold < 65504.0f)) {
@@ -225,7 +227,7 @@ qa_status qa_qlinear_int8_mixed(const void* X_f16, int64_t M, int64_t K, const i
         int segs = 1;
         e = qa::launch_outlier_flags(X, M, K, threshold, ws + L.cmax, &segs, st);
         if (e != hipSuccess) return device_status(e, "qa_qlinear_int8_mixed (outlier columns)");
-        e = qa::launch_rowquant_i8_flags(X, M, K, ws + L.cmax, segs, xq, s_x, idx, count, st);
+        e = qa::launch_rowquant_i8_flags(X, M, K, ws + L.cmax, segs, xq, s_x, idx, count, xo, st);
         if (e != hipSuccess) return device_status(e, "qa_qlinear_int8_mixed (row quantization)");
     }
     qa::MixedEpilogue ep;
@@ -236,6 +238,7 @@ qa_status qa_qlinear_int8_mixed(const void* X_f16, int64_t M, int64_t K, const i
     ep.Wq = Wq;
     ep.idx = idx;
     ep.count = count;
+    ep.Xo = qa::rowquant_writes_xo(K) ? xo : nullptr;
     ep.out = out;
     ep.ldo = N;
     ep.out_dtype = (int)out_dtype;
@@ -268,10 +271,11 @@ qa_status qa_qlinear_int8_topk(const void* X_f16, int64_t M, int64_t K, int64_t 
     int32_t* count = reinterpret_cast<int32_t*>(ws + L.count);
     float* s_x = reinterpret_cast<float*>(ws + L.s_x);
     int8_t* xq = reinterpret_cast<int8_t*>(ws + L.xq);
+    uint16_t* xo = reinterpret_cast<uint16_t*>(ws + L.xo);
     int segs = 1;
     hipError_t e = qa::launch_outlier_topk_flags(X, M, K, k, ws + L.cmax, &segs, st);
     if (e != hipSuccess) return device_status(e, "qa_qlinear_int8_topk (top-k columns)");
-    e = qa::launch_rowquant_i8_flags(X, M, K, ws + L.cmax, segs, xq, s_x, idx, count, st);
+    e = qa::launch_rowquant_i8_flags(X, M, K, ws + L.cmax, segs, xq, s_x, idx, count, xo, st);
     if (e != hipSuccess) return device_status(e, "qa_qlinear_int8_topk (row quantization)");
     qa::MixedEpilogue ep;
     ep.s_x = s_x;
@@ -281,6 +285,7 @@ qa_status qa_qlinear_int8_topk(const void* X_f16, int64_t M, int64_t K, int64_t 
     ep.Wq = Wq;
     ep.idx = idx;
     ep.count = count;
+    ep.Xo = qa::rowquant_writes_xo(K) ? xo : nullptr;
     ep.out = out;
     ep.ldo = N;
     ep.out_dtype = (int)out_dtype;
@@ -376,6 +381,7 @@ qa_status qa_qlinear_int8_smooth(const void* X_f16, int64_t M, int64_t K, const 
     ep.Wq = Wq;
     ep.idx = count;            // never read: the count is 0
     ep.count = count;
+    ep.Xo = nullptr;
     ep.out = out;
     ep.ldo = N;
     ep.out_dtype = (int)out_dtype;

@@ -26,11 +26,23 @@ hipError_t launch_rowquant_i8(const uint16_t* X, int64_t rows, int64_t K, const 
                               int qmin, int qmax, const float* s_in, const int32_t* z_in,
                               int8_t* q, float* s_out, hipStream_t st);
 
+// Width of the compact outlier rows: xo[m][r] holds X[m][idx[r]] (fp16) for
+// the first XO_CAP outlier columns, written by the flag-masked row
+// quantizer and read by the GEMM epilogue with contiguous loads.
+constexpr int XO_CAP = 256;
+// Up to this many outlier columns the GEMM gathers X and w~ itself (issued
+// behind its first pipeline stages); the compact rows serve larger counts.
+constexpr int OUTLIER_PREFETCH = 8;
+
 // Dynamic [-127, 127] row quantization with the outlier flags of `scratch`
 // (launch_outlier_flags, nseg partial sets) as the mask; also writes the
-// ascending outlier list and its count.
+// ascending outlier list and its count, and the compact outlier rows xo
+// [rows x XO_CAP] when rowquant_writes_xo(K) (entries past the count are
+// left as they were).
+bool rowquant_writes_xo(int64_t K);
 hipError_t launch_rowquant_i8_flags(const uint16_t* X, int64_t rows, int64_t K, const void* scratch, int nseg,
-                                    int8_t* q, float* s_out, int32_t* idx, int32_t* count, hipStream_t st);
+                                    int8_t* q, float* s_out, int32_t* idx, int32_t* count, uint16_t* xo,
+                                    hipStream_t st);
 
 // Dynamic [-127, 127] row quantization with no outlier columns; *count = 0.
 hipError_t launch_rowquant_i8_no_outliers(const uint16_t* X, int64_t rows, int64_t K, int8_t* q, float* s_out,
@@ -71,6 +83,7 @@ struct MixedEpilogue {
     const int8_t* Wq;          // for w~ when W16 is null
     const int32_t* idx;        // outlier list
     const int32_t* count;      // device count
+    const uint16_t* Xo;        // compact outlier rows [M x XO_CAP] or nullptr (then X is gathered)
     void* out;
     int64_t ldo;               // row stride of out, in elements
     int out_dtype;             // 0 f32, 1 f16, 2 bf16

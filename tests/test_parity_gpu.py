@@ -221,6 +221,20 @@ def test_mixed_many_outliers(qa):
     _mixed_case(qa, X, W, 6.0, 0, True)
 
 
+@pytest.mark.parametrize("M,K,N,n_dims,pass_w16", [
+    (300, 2048, 520, 150, False),    # 96 < count <= 256: several staging passes from the compact rows
+    (300, 2048, 520, 150, True),
+    (600, 4096, 300, 256, False),    # exactly the compact-row capacity
+    (70, 1024, 260, 300, False),     # count > 256: X gathered as well
+    (40, 8208, 96, 20, True),        # K > 8192: rows not held in registers, X gathered
+    (513, 1024, 1030, 40, False),    # big tiles with a tail launch, count between the prefetch and one pass
+])
+def test_mixed_outlier_staging_paths(qa, M, K, N, n_dims, pass_w16):
+    X, W, dims = synthetic.mixed_inputs(M, K, N, seed=M + n_dims, n_dims=n_dims, p_token=0.6,
+                                        magnitude=("uniform", 6.5, 60.0))
+    _mixed_case(qa, X, W, 6.0, 1, pass_w16)
+
+
 @pytest.mark.parametrize("M,K,N", [(1, 256, 1), (3, 512, 17), (4, 768, 40), (7, 1024, 33), (8, 4096, 64),
                                    (9, 2048, 48), (12, 256, 100), (16, 4096, 20)])
 @pytest.mark.parametrize("tau", [6.0, float("inf"), -1.0])
