@@ -61,6 +61,9 @@ def lib() -> ctypes.CDLL:
             "orc_qlinear_int8_mixed": (None, [P, I64, I64, P, P, P, I64, F, P, I64, P]),
             "orc_outlier_topk": (None, [P, I64, I64, I64, P, P, P, P]),
             "orc_qlinear_int8_topk": (None, [P, I64, I64, P, P, P, I64, I64, P, I64, P]),
+            "orc_minmax_params": (None, [P, I64, I32, I32, P, P]),
+            "orc_quant_rows_asym_f32": (None, [P, I64, I64, I32, I32, P, P, P, P]),
+            "orc_qlinear_int8_asym": (None, [P, I64, I64, P, P, P, I64, P, I64, P]),
             "orc_col_absmax_f32": (None, [P, I64, I64, P]),
             "orc_smooth_factors": (None, [P, P, I64, ctypes.c_double, P]),
             "orc_smooth_apply_f32": (None, [P, I64, I64, P, ctypes.c_int, P]),
@@ -217,6 +220,43 @@ def qlinear_int8_mixed(X16, Wq, s_w, W16=None, tau=6.0, rows=None):
     out = np.zeros((nr if r is not None else M, N), np.float64)
     lib().orc_qlinear_int8_mixed(_ptr(h), M, K, _ptr(Wq), _ptr(sw), _ptr(w16), N, float(tau),
                                  _ptr(r), nr, _ptr(out))
+    return out
+
+
+# ---------------------------------------------------------------- asymmetric (zero-point)
+def minmax_params(x, qmin, qmax):
+    """Min-max affine parameters of one vector -> (s f32, z int)."""
+    xf = _c(np.asarray(x, np.float32).ravel(), np.float32)
+    s = np.zeros(1, np.float32)
+    z = np.zeros(1, np.int32)
+    lib().orc_minmax_params(_ptr(xf), xf.size, int(qmin), int(qmax), _ptr(s), _ptr(z))
+    return s[0], int(z[0])
+
+
+def quant_rows_asym(x, qmin=-128, qmax=127):
+    """Per-row asymmetric codes of an fp16 or fp32 matrix -> (codes i8, s f32 [rows], z i32 [rows],
+    row sums of the codes i32 [rows])."""
+    a = _f32_matrix(x)
+    rows, K = a.shape
+    q = np.zeros((rows, K), np.int8)
+    s = np.zeros(rows, np.float32)
+    z = np.zeros(rows, np.int32)
+    rs = np.zeros(rows, np.int32)
+    lib().orc_quant_rows_asym_f32(_ptr(a), rows, K, int(qmin), int(qmax), _ptr(q), _ptr(s), _ptr(z), _ptr(rs))
+    return q, s, z, rs
+
+
+def qlinear_int8_asym(X16, Wq, s_w, z_w=None, rows=None):
+    """W8A8 linear with asymmetric per-token activations, fp64 [nrows x N]."""
+    h = _h16(X16)
+    M, K = h.shape
+    Wq = _c(Wq, np.int8)
+    N = Wq.shape[0]
+    sw = _c(s_w, np.float32)
+    zw = None if z_w is None else _c(z_w, np.int32)
+    r, nr = _rows(rows)
+    out = np.zeros((nr if r is not None else M, N), np.float64)
+    lib().orc_qlinear_int8_asym(_ptr(h), M, K, _ptr(Wq), _ptr(sw), _ptr(zw), N, _ptr(r), nr, _ptr(out))
     return out
 
 

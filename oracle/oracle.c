@@ -40,6 +40,10 @@
  *     fp64 multiply by fl64(1/sqrt(G)) and one rounding to fp32.
  *   - int4 packing: element 8w+i of a row sits in bits [4i+3:4i] of word w,
  *     two's complement.
+ *   - Asymmetric (zero-point) parameters, per row: lo = min(min_j x_j, 0),
+ *     hi = max(max_j x_j, 0) (the range holds real 0, which z stands for),
+ *     s = fl32(fl32(hi - lo) / (qmax - qmin)) (1.0 when hi == lo),
+ *     z = clip(qmin - rint(fl32(lo / s)), qmin, qmax); codes by the affine rule.
  *   - SmoothQuant: s_j = fl32(pow(cx_j, alpha) / pow(cw_j, 1 - alpha)) in
  *     fp64, and s_j = 1 when cx_j or cw_j is 0 (the formula is undefined or
  *     zero there).  Activations become fl32(x / s_j), weights fl32(w * s_j),
@@ -373,6 +377,78 @@ static void orc_mixed_with_set(const uint16_t* X, int64_t M, int64_t K,
         free(xq);
     }
     free(wt);
+}
+
+/* ---------------------------------------------------------------------------
+ * Asymmetric (affine) quantization  [Scholia-IQ §6: q = round(x/s) + z,
+ * x^ = s (q - z), z is the integer standing for real 0; §6.2: the integer
+ * grid shifted onto a range such as [-0.2, 1.7], q clipped to [qmin, qmax]]
+ * The pages leave the choice of s and z open; the min-max rule is taken:
+ * the grid spans [lo, hi] = [min(min x, 0), max(max x, 0)], lo -> qmin.
+ * ------------------------------------------------------------------------- */
+void orc_minmax_params(const float* x, int64_t n, int32_t qmin, int32_t qmax, float* s_out, int32_t* z_out)
+{
+    float lo = 0.0f, hi = 0.0f;
+    for (int64_t j = 0; j < n; ++j) {
+        if (x[j] < lo) lo = x[j];
+        if (x[j] > hi) hi = x[j];
+    }
+    float s = 1.0f;
+    if (hi != lo) {
+        float d = hi - lo;                                  /* fp32, correctly rounded */
+        s = d / (float)(qmax - qmin);
+    }
+    double z = (double)qmin - (double)rintf(lo / s);
+    if (z < qmin) z = qmin;
+    if (z > qmax) z = qmax;
+    *s_out = s;
+    *z_out = (int32_t)z;
+}
+
+/* Per-row asymmetric codes of fp32 rows: (s, z) from orc_minmax_params, then
+ * q = clip(rint(x/s) + z), and the row sums of the codes. */
+void orc_quant_rows_asym_f32(const float* x, int64_t rows, int64_t K, int32_t qmin, int32_t qmax,
+                             int8_t* q, float* s_out, int32_t* z_out, int32_t* rowsum)
+{
+    for (int64_t r = 0; r < rows; ++r) {
+        orc_minmax_params(x + r * K, K, qmin, qmax, &s_out[r], &z_out[r]);
+        orc_quant_rows_f32(x + r * K, 1, K, K, NULL, qmin, qmax, &s_out[r], &z_out[r], q + r * K, NULL);
+        int64_t sum = 0;
+        for (int64_t j = 0; j < K; ++j)
+            sum += q[r * K + j];
+        if (rowsum)
+            rowsum[r] = (int32_t)sum;
+    }
+}
+
+/* W8A8 linear with asymmetric per-token activations: out[m][n] =
+ * sum_k s_x[m] (xq[m][k] - z_x[m]) * s_w[n] (wq[n][k] - z_w[n]), the
+ * integer sum exact in int64.  z_w may be NULL (symmetric weight).
+ * Activation codes in [-128, 127].  Output fp64 [nrows x N]. */
+void orc_qlinear_int8_asym(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* s_w,
+                           const int32_t* z_w, int64_t N, const int64_t* rows, int64_t nrows, double* out)
+{
+    if (!rows)
+        nrows = M;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t ri = 0; ri < nrows; ++ri) {
+        int64_t m = rows ? rows[ri] : ri;
+        float* xf = (float*)malloc(sizeof(float) * (size_t)(K > 0 ? K : 1));
+        int8_t* xq = (int8_t*)malloc((size_t)(K > 0 ? K : 1));
+        float s_x;
+        int32_t z_x;
+        orc_f16_to_f32_array(X + m * K, K, xf);
+        orc_quant_rows_asym_f32(xf, 1, K, -128, 127, xq, &s_x, &z_x, NULL);
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t zw = z_w ? z_w[n] : 0;
+            int64_t acc = 0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += ((int64_t)xq[k] - z_x) * ((int64_t)Wq[n * K + k] - zw);
+            out[ri * N + n] = (double)acc * (double)s_x * (double)s_w[n];
+        }
+        free(xq);
+        free(xf);
+    }
 }
 
 /* ---------------------------------------------------------------------------

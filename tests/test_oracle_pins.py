@@ -613,3 +613,83 @@ def test_raising_the_decomposed_share_lowers_error():
     exact = X.astype(np.float64) @ W.astype(np.float64).T
     errs = [np.abs(oracle.qlinear_int8_topk(X, Wq, s_w, W16=W, k=k) - exact).mean() for k in (2, 21, 41)]
     assert errs[2] < errs[1] < errs[0]
+
+
+# ------------------------------------------------------------------ asymmetric (zero-point)
+def test_zero_point_grid_on_a_nonnegative_range():
+    """Inference Quantization notes §6: data in [0, 6] wastes half of a signed
+    int4 grid; shifted by z it uses all 16 levels, 0 -> q_min = z, 6 -> q_max."""
+    x = np.linspace(0.0, 6.0, 61).astype(np.float32)
+    s, z = oracle.minmax_params(x, -8, 7)
+    assert s == np.float32(np.float32(6.0) / np.float32(15)) and z == -8
+    q, sr, zr, _ = oracle.quant_rows_asym(x[None, :], -8, 7)
+    assert q[0, 0] == -8 and q[0, -1] == 7
+    assert set(q[0].tolist()) == set(range(-8, 8))
+    assert sr[0] * (q[0, 0] - zr[0]) == 0.0                       # real 0 is exact
+
+
+def test_zero_point_grid_on_a_shifted_range():
+    """§6.2: a range such as [-0.2, 1.7] gets the whole grid; real 0 maps to z."""
+    x = np.array([-0.2, 0.0, 0.35, 1.1, 1.7], np.float32)
+    s, z = oracle.minmax_params(x, -128, 127)
+    assert s == np.float32(np.float32(np.float32(1.7) - np.float32(-0.2)) / np.float32(255))
+    assert z == -128 + int(np.rint(np.float32(0.2) / s))          # -101
+    q, sr, zr, _ = oracle.quant_rows_asym(x[None, :])
+    assert q[0, 0] == -128 and q[0, 1] == z and q[0, -1] == 127
+    assert np.all(np.abs(sr[0] * (q[0].astype(np.float64) - zr[0]) - x) <= sr[0] / 2 * (1 + 1e-6))
+
+
+def test_zero_point_symmetric_range_and_zero_row():
+    a = np.float32(3.0)
+    x = np.array([-a, -1.0, 0.5, a], np.float32)
+    assert oracle.minmax_params(x, -128, 127)[1] == 0             # -128 - rint(-127.5) = 0 (ties to even)
+    q, s, z, rs = oracle.quant_rows_asym(np.zeros((2, 16), np.float32))
+    assert np.all(s == 1.0) and np.all(z == -128) and np.all(q == -128) and np.all(rs == -128 * 16)
+
+
+def test_asymmetric_codes_within_half_a_step():
+    X, _, _ = synthetic.mixed_inputs(40, 300, 1, seed=51, n_dims=3, magnitude=("uniform", 10.0, 60.0))
+    X[:5] = np.abs(X[:5]) + np.float16(2.0)                     # rows away from 0 on one side
+    X[5:10] = -np.abs(X[5:10]) - np.float16(1.0)
+    Xf = X.astype(np.float32)
+    q, s, z, rs = oracle.quant_rows_asym(X)
+    deq = s[:, None].astype(np.float64) * (q.astype(np.float64) - z[:, None])
+    assert np.all(np.abs(deq - Xf) <= s[:, None] / 2 * (1 + 1e-6) + 1e-30)
+    assert np.array_equal(rs, q.astype(np.int64).sum(axis=1))
+    assert np.array_equal(q, np.clip(np.rint(Xf / s[:, None]) + z[:, None], -128, 127).astype(np.int8))
+
+
+def test_asymmetric_linear_is_the_dequantized_product():
+    X, W, _ = synthetic.mixed_inputs(11, 160, 23, seed=52, n_dims=2)
+    Wq, s_w = _w8(W)
+    qw, sw2, zw, _ = oracle.quant_rows_asym(W)
+    for wq, swv, zwv in ((Wq, s_w, None), (qw, sw2, zw)):
+        q, s, z, _ = oracle.quant_rows_asym(X)
+        dz = zwv if zwv is not None else np.zeros(len(swv), np.int32)
+        acc = (q.astype(np.int64) - z[:, None]) @ (wq.astype(np.int64) - dz[:, None]).T
+        ref = acc.astype(np.float64) * s.astype(np.float64)[:, None] * swv.astype(np.float64)[None, :]
+        out = oracle.qlinear_int8_asym(X, wq, swv, z_w=zwv)
+        assert np.array_equal(out, ref)
+        rows = np.array([10, 0, 4])
+        assert np.array_equal(oracle.qlinear_int8_asym(X, wq, swv, z_w=zwv, rows=rows), out[rows])
+
+
+def test_zero_point_helps_one_sided_activations():
+    """The pages attribute zero-point's edge over absmax to one-sided values:
+    on non-negative activations the shifted grid has about half the step
+    (max/255 against max/127), so the activation error halves and the W8A8
+    output error drops."""
+    rng = np.random.default_rng(53)
+    X = np.maximum(rng.normal(0.5, 1.0, (64, 512)), 0).astype(np.float16)
+    W = synthetic.normal_f16(rng, (48, 512), 0.02)
+    X64 = X.astype(np.float64)
+    q, s, z, _ = oracle.quant_rows_asym(X)
+    qs, ss = oracle.quant_rows(X)
+    e_act_asym = np.abs(s[:, None] * (q.astype(np.float64) - z[:, None]) - X64).mean()
+    e_act_sym = np.abs(ss * qs.astype(np.float64) - X64).mean()
+    assert e_act_asym < 0.6 * e_act_sym
+    Wq, s_w = _w8(W)
+    exact = X64 @ W.astype(np.float64).T
+    e_asym = np.abs(oracle.qlinear_int8_asym(X, Wq, s_w) - exact).mean()
+    e_sym = np.abs(oracle.qlinear_int8_mixed(X, Wq, s_w, tau=float("inf")) - exact).mean()
+    assert e_asym < e_sym
