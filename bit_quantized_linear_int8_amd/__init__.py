@@ -27,6 +27,7 @@ EXPORTS = (
     "qa_quantize_rowwise_int8",
     "qa_qlinear_int8_mixed_workspace", "qa_qlinear_int8_mixed",
     "qa_qlinear_int8_topk_workspace", "qa_qlinear_int8_topk",
+    "qa_quantize_rowwise_int8_asym", "qa_int8_row_sums", "qa_qlinear_int8_asym_workspace", "qa_qlinear_int8_asym",
     "qa_col_absmax_workspace", "qa_col_absmax", "qa_smooth_factors", "qa_quantize_smooth_int8",
     "qa_qlinear_int8_smooth_workspace", "qa_qlinear_int8_smooth",
     "qa_hadamard_quant_int4",
@@ -67,6 +68,10 @@ def lib() -> ctypes.CDLL:
             "qa_quantize_rowwise_int8": (S, [P, I64, I64, P, I32, I32, P, P, P, P, P]),
             "qa_qlinear_int8_mixed_workspace": (SZ, [I64, I64]),
             "qa_qlinear_int8_mixed": (S, [P, I64, I64, P, P, P, I64, F, P, S, P, SZ, P]),
+            "qa_quantize_rowwise_int8_asym": (S, [P, I64, I64, I32, I32, P, P, P, P, P]),
+            "qa_int8_row_sums": (S, [P, I64, I64, P, P]),
+            "qa_qlinear_int8_asym_workspace": (SZ, [I64, I64]),
+            "qa_qlinear_int8_asym": (S, [P, I64, I64, P, P, P, P, I64, P, S, P, SZ, P]),
             "qa_col_absmax_workspace": (SZ, [I64]),
             "qa_col_absmax": (S, [P, I64, I64, P, S, P, SZ, P]),
             "qa_smooth_factors": (S, [P, P, I64, F, P, P]),
@@ -200,6 +205,54 @@ def qa_qlinear_int8_mixed(X, Wq, s_w, W16=None, threshold=6.0, out_dtype=torch.f
     _check("qa_qlinear_int8_mixed",
            lib().qa_qlinear_int8_mixed(_p(X), M, K, _p(Wq), _p(s_w), _p(W16), N, float(threshold), _p(out),
                                        _DTYPE_CODE[out.dtype], _p(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def qa_quantize_rowwise_int8_asym(X, q_min=-128, q_max=127, stream=None):
+    """Per-row min-max zero-point codes -> (q i8 [rows x K], s f32 [rows], z i32 [rows], rowsum i32 [rows])."""
+    _dev(X, "X", torch.float16)
+    rows, K = X.shape
+    d = X.device
+    q = torch.empty((rows, K), dtype=torch.int8, device=d)
+    s = torch.empty(rows, dtype=torch.float32, device=d)
+    z = torch.empty(rows, dtype=torch.int32, device=d)
+    rs = torch.empty(rows, dtype=torch.int32, device=d)
+    _check("qa_quantize_rowwise_int8_asym",
+           lib().qa_quantize_rowwise_int8_asym(_p(X), rows, K, int(q_min), int(q_max), _p(q), _p(s), _p(z), _p(rs),
+                                               _stream(stream)))
+    return q, s, z, rs
+
+
+def qa_int8_row_sums(A, stream=None):
+    """Row sums of an int8 matrix -> i32 [rows]."""
+    _dev(A, "A", torch.int8)
+    rows, K = A.shape
+    sums = torch.empty(rows, dtype=torch.int32, device=A.device)
+    _check("qa_int8_row_sums", lib().qa_int8_row_sums(_p(A), rows, K, _p(sums), _stream(stream)))
+    return sums
+
+
+def qa_qlinear_int8_asym_workspace(M: int, K: int) -> int:
+    return int(lib().qa_qlinear_int8_asym_workspace(M, K))
+
+
+def qa_qlinear_int8_asym(X, Wq, s_w, w_rowsum, z_w=None, out_dtype=torch.float16, out=None, workspace=None,
+                         stream=None):
+    """W8A8 linear with per-token zero-point activations -> out [M x N] of out_dtype."""
+    _dev(X, "X", torch.float16)
+    _dev(Wq, "Wq", torch.int8)
+    _dev(s_w, "s_w", torch.float32)
+    _dev(w_rowsum, "w_rowsum", torch.int32)
+    if z_w is not None:
+        _dev(z_w, "z_w", torch.int32)
+    M, K = X.shape
+    N = Wq.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=X.device)
+    workspace = _workspace(qa_qlinear_int8_asym_workspace(M, K), X.device, workspace)
+    _check("qa_qlinear_int8_asym",
+           lib().qa_qlinear_int8_asym(_p(X), M, K, _p(Wq), _p(s_w), _p(z_w), _p(w_rowsum), N, _p(out),
+                                      _DTYPE_CODE[out.dtype], _p(workspace), workspace.numel(), _stream(stream)))
     return out
 
 

@@ -571,6 +571,73 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_i8_mixed(const int8_t* __re
     });
 }
 
+// ---------------------------------------------------------------------------
+// int8 GEMM with zero-point (asymmetric) dequantization:
+//   sum_k (xq - z_x[m]) (wq - z_w[n]) = C - z_x[m] a[n] - z_w[n] r_x[m],
+//   a[n] = r_w[n] - K z_w[n],  r_x / r_w = row sums of the codes,
+// evaluated in int32 (exact while the result fits, K <= 32768), then
+// out = that * s_x[m] * s_w[n].  ZW = false: symmetric weight (z_w = 0).
+// ---------------------------------------------------------------------------
+template <class C, bool ZW>
+__global__ __launch_bounds__(C::THREADS) void k_gemm_i8_asym(const int8_t* __restrict__ Xq,
+                                                             const int8_t* __restrict__ Wq, int64_t M, int64_t K,
+                                                             int64_t N, AsymEpilogue ep, int tiles_m, int tiles_n) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
+    int tm, tn;
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
+    v4i acc[C::FM][C::FN];
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    const int64_t rb = m0 + wm * C::TM, cb = n0 + wn * C::TN;
+    // per-column and per-row terms, loaded before the main loop
+    const rsrc_t rsw = make_rsrc(ep.s_w + cb, (N - cb) * 4);
+    const rsrc_t rrw = make_rsrc(ep.r_w + cb, (N - cb) * 4);
+    const rsrc_t rzw = make_rsrc(ZW ? ep.z_w + cb : ep.r_w, ZW ? (N - cb) * 4 : 0);
+    const rsrc_t rsx = make_rsrc(ep.s_x + rb, (M - rb) * 4);
+    const rsrc_t rzx = make_rsrc(ep.z_x + rb, (M - rb) * 4);
+    const rsrc_t rrx = make_rsrc(ZW ? ep.r_x + rb : ep.z_x, ZW ? (M - rb) * 4 : 0);
+    float sw[C::FN][4], sxv[C::FM];
+    int32_t an[C::FN][4], zwv[ZW ? C::FN : 1][4], zxv[C::FM], rxv[ZW ? C::FM : 1];
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t off = (uint32_t)(j * 16 + 4 * (lane >> 4) + e) * 4;
+            sw[j][e] = __builtin_bit_cast(float, bload4(rsw, off));
+            const int32_t z = ZW ? (int32_t)bload4(rzw, off) : 0;
+            an[j][e] = (int32_t)bload4(rrw, off) - (int32_t)K * z;
+            if constexpr (ZW) zwv[j][e] = z;
+        }
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+        const uint32_t off = (uint32_t)(i * 16 + (lane & 15)) * 4;
+        sxv[i] = __builtin_bit_cast(float, bload4(rsx, off));
+        zxv[i] = (int32_t)bload4(rzx, off);
+        if constexpr (ZW) rxv[i] = (int32_t)bload4(rrx, off);
+    }
+    mainloop_any<C>(Xq, Wq, M, N, K, m0, n0, smem, acc);
+    const bool vec = ((ep.ldo | N) & 3) == 0;
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+        const int64_t row = rb + i * 16 + (lane & 15);
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+            v4f cf;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                // wrap-around int32 arithmetic: exact whenever the result fits
+                uint32_t c = (uint32_t)acc[i][j][e] - (uint32_t)zxv[i] * (uint32_t)an[j][e];
+                if constexpr (ZW) c -= (uint32_t)zwv[j][e] * (uint32_t)rxv[i];
+                cf[e] = (float)(int32_t)c * sxv[i] * sw[j][e];
+            }
+            const int64_t col = cb + j * 16 + 4 * (lane >> 4);
+            if (row < M && col < N)
+                store_out4(ep.out, ep.out_dtype, row * ep.ldo + col, cf, vec, (int)(N - col < 4 ? N - col : 4));
+        }
+    }
+}
+
 using CfgBig = CfgD<256, 256, 2, 4>;   // 8 waves, wave tile 128 x 64, LDS-DMA stages
 using CfgTail = CfgD<128, 256, 2, 4>;  // 8 waves, wave tile 64 x 64, LDS-DMA stages
 using CfgMid = Cfg<128, 128, 2, 2>;    // 4 waves, wave tile 64 x 64 (register-staged)
@@ -1066,6 +1133,58 @@ hipError_t launch_gemm_w4a4_group_acc(const uint32_t* Xp, const uint32_t* Wp, in
         case 256: w4a4_dispatch<256, true>(Xp, nullptr, Wp, nullptr, M, K, N, acc, 0, st); break;
         default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+
+template <bool ZW>
+static void launch_asym_cfgs(const int8_t* Xq, const int8_t* Wq, int64_t M, int64_t K, int64_t N,
+                             const AsymEpilogue& ep, hipStream_t st) {
+    int tm, tn;
+    if (pick_cfg(M, N) == 2) {
+        if (const int64_t split = tail_split(M, N)) {
+            dim3 g = grid_of<CfgBig>(M, split, tm, tn);
+            hipLaunchKernelGGL((k_gemm_i8_asym<CfgBig, ZW>), g, dim3(CfgBig::THREADS), 0, st, Xq, Wq, M, K, split,
+                               ep, tm, tn);
+            const int esz = ep.out_dtype == 0 ? 4 : 2;
+            AsymEpilogue et = ep;
+            et.s_w = ep.s_w + split;
+            et.r_w = ep.r_w + split;
+            et.z_w = ep.z_w ? ep.z_w + split : nullptr;
+            et.out = static_cast<uint8_t*>(ep.out) + split * esz;
+            g = grid_of<CfgTail>(M, N - split, tm, tn);
+            hipLaunchKernelGGL((k_gemm_i8_asym<CfgTail, ZW>), g, dim3(CfgTail::THREADS), 0, st, Xq, Wq + split * K,
+                               M, K, N - split, et, tm, tn);
+            return;
+        }
+    }
+    switch (pick_cfg(M, N)) {
+        case 2: {
+            dim3 g = grid_of<CfgBig>(M, N, tm, tn);
+            hipLaunchKernelGGL((k_gemm_i8_asym<CfgBig, ZW>), g, dim3(CfgBig::THREADS), 0, st, Xq, Wq, M, K, N, ep,
+                               tm, tn);
+            break;
+        }
+        case 1: {
+            dim3 g = grid_of<CfgMid>(M, N, tm, tn);
+            hipLaunchKernelGGL((k_gemm_i8_asym<CfgMid, ZW>), g, dim3(CfgMid::THREADS), 0, st, Xq, Wq, M, K, N, ep,
+                               tm, tn);
+            break;
+        }
+        default: {
+            dim3 g = grid_of<CfgSmall>(M, N, tm, tn);
+            hipLaunchKernelGGL((k_gemm_i8_asym<CfgSmall, ZW>), g, dim3(CfgSmall::THREADS), 0, st, Xq, Wq, M, K, N,
+                               ep, tm, tn);
+        }
+    }
+}
+
+hipError_t launch_gemm_i8_asym(const int8_t* Xq, const int8_t* Wq, int64_t M, int64_t K, int64_t N,
+                               const AsymEpilogue& ep, hipStream_t st) {
+    if (ep.z_w)
+        launch_asym_cfgs<true>(Xq, Wq, M, K, N, ep, st);
+    else
+        launch_asym_cfgs<false>(Xq, Wq, M, K, N, ep, st);
     return hipGetLastError();
 }
 

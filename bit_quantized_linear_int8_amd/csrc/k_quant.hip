@@ -703,6 +703,161 @@ hipError_t launch_rowquant_i8_no_outliers(const uint16_t* X, int64_t rows, int64
 }
 
 // ---------------------------------------------------------------------------
+// Asymmetric (zero-point) row quantization: per row, the min-max grid over
+// [lo, hi] = [min(min x, 0), max(max x, 0)]: s = fl32(fl32(hi - lo) / (qmax -
+// qmin)) (1.0 when hi == lo), z = clip(qmin - rint(fl32(lo / s))), codes
+// clip(rint(fl32(x / s)) + z), and the row sum of the codes (int32).  One
+// wave per row as in k_rowquant_i8 (chunks past the row read 0, which is in
+// the range anyway).
+// Codes: |x / s| <= (qmax - qmin)(1 + 2^-23) <= 255.0001, so t = fma(x, r, 256)
+// with r = fl32(1/s) lies in (0, 512): |x r - x/s| <= 255.0001 * 2^-24, the
+// rounding of t adds at most 2^-16 and fl(x/s) is within 2^-17 of x/s, so
+// t - 256 is within 4e-5 < 2^-14 of fl(x/s); unless t is that close to
+// n + 1/2, rint(t) - 256 = rint(fl(x/s)).  Chunks with such a t take the
+// correctly rounded division.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void minmax8(const float* x, float& lo, float& hi) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        lo = fminf(lo, x[j]);
+        hi = fmaxf(hi, x[j]);
+    }
+}
+
+__device__ __forceinline__ u32x2 codes8_asym(const float* x, float s, float r, int z, int qmin, int qmax, int& sum) {
+    float n[8];
+    float dmax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float t = __builtin_fmaf(x[j], r, 256.0f);
+        n[j] = __builtin_rintf(t);
+        dmax = fmaxf(dmax, __builtin_fabsf(t - n[j]));
+    }
+    if (dmax > 0.5f - 0x1p-14f) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) n[j] = __builtin_rintf(x[j] / s) + 256.0f;
+    }
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int c = clampi((int)n[j] - 256 + z, qmin, qmax);
+        sum += c;
+        w[j >> 2] |= ((uint32_t)c & 0xffu) << (8 * (j & 3));
+    }
+    return u32x2{w[0], w[1]};
+}
+
+__device__ __forceinline__ int wave_sum_i32(int v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, QA_WAVE);
+    return v;
+}
+
+template <int NC>
+__global__ __launch_bounds__(256) void k_rowquant_i8_asym(const uint16_t* __restrict__ X, int64_t rows, int64_t K,
+                                                          int qmin, int qmax, int8_t* __restrict__ q,
+                                                          float* __restrict__ s_out, int32_t* __restrict__ z_out,
+                                                          int32_t* __restrict__ rowsum) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + wave_id();
+    if (row >= rows) return;
+    const int64_t nch = K >> 3;
+    const rsrc_t rx = make_rsrc(X + row * K, K * 2);
+    int8_t* qr = q + row * K;
+    float lo = 0.0f, hi = 0.0f;
+    u32x4 v[NC > 0 ? NC : 1];
+    if constexpr (NC > 0) {
+#pragma unroll
+        for (int i = 0; i < NC; ++i) v[i] = bload16(rx, (uint32_t)(lane + 64 * i) * 16);
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+            float x[8];
+            unpack8(v[i], x);
+            minmax8(x, lo, hi);
+        }
+    } else {
+        for (int64_t ch = lane; ch < nch; ch += 64) {
+            float x[8];
+            unpack8(bload16(rx, (uint32_t)ch * 16), x);
+            minmax8(x, lo, hi);
+        }
+    }
+    hi = wave_max(hi);
+    lo = -wave_max(-lo);
+    const float s = hi != lo ? (hi - lo) / (float)(qmax - qmin) : 1.0f;
+    const int z = clampi(qmin - (int)__builtin_rintf(lo / s), qmin, qmax);
+    const float r = 1.0f / s;
+    int sum = 0;
+    if constexpr (NC > 0) {
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+            const int64_t ch = lane + 64 * i;
+            if (ch < nch) {
+                float x[8];
+                unpack8(v[i], x);
+                *reinterpret_cast<u32x2*>(qr + ch * 8) = codes8_asym(x, s, r, z, qmin, qmax, sum);
+            }
+        }
+    } else {
+        for (int64_t ch = lane; ch < nch; ch += 64) {
+            float x[8];
+            unpack8(bload16(rx, (uint32_t)ch * 16), x);
+            *reinterpret_cast<u32x2*>(qr + ch * 8) = codes8_asym(x, s, r, z, qmin, qmax, sum);
+        }
+    }
+    sum = wave_sum_i32(sum);
+    if (lane == 0) {
+        s_out[row] = s;
+        z_out[row] = z;
+        if (rowsum) rowsum[row] = sum;
+    }
+}
+
+hipError_t launch_rowquant_i8_asym(const uint16_t* X, int64_t rows, int64_t K, int qmin, int qmax, int8_t* q,
+                                   float* s_out, int32_t* z_out, int32_t* rowsum, hipStream_t st) {
+    const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+    const int64_t nch = K / 8;
+#define QA_RA(NC) hipLaunchKernelGGL((k_rowquant_i8_asym<NC>), grid, block, 0, st, X, rows, K, qmin, qmax, q, s_out, \
+                                     z_out, rowsum)
+    if (nch <= 64) QA_RA(1);
+    else if (nch <= 128) QA_RA(2);
+    else if (nch <= 256) QA_RA(4);
+    else if (nch <= 512) QA_RA(8);
+    else if (nch <= 1024) QA_RA(16);
+    else QA_RA(0);
+#undef QA_RA
+    return hipGetLastError();
+}
+
+// Row sums of int8 rows (K % 16 == 0): one wave per row, 16 bytes per lane.
+__global__ __launch_bounds__(256) void k_row_sums_i8(const int8_t* __restrict__ A, int64_t rows, int64_t K,
+                                                     int32_t* __restrict__ sums) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + wave_id();
+    if (row >= rows) return;
+    const rsrc_t ra = make_rsrc(A + row * K, K);
+    int sum = 0;
+    for (int64_t c0 = 0; c0 < K; c0 += 64 * 16 * 4) {
+        u32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = bload16(ra, (uint32_t)(c0 + (u * 64 + lane) * 16));
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) sum += (int)(int8_t)(v[u][d] >> (8 * b));
+    }
+    sum = wave_sum_i32(sum);
+    if (lane == 0) sums[row] = sum;
+}
+
+hipError_t launch_row_sums_i8(const int8_t* A, int64_t rows, int64_t K, int32_t* sums, hipStream_t st) {
+    hipLaunchKernelGGL(k_row_sums_i8, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, A, rows, K, sums);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Block Hadamard rotation + int4 quantization + packing.  One wave per row;
 // lane l owns the 8 adjacent elements of chunk ch = l + 64 i.  A G-block spans
 // G/8 lanes (G >= 8) or part of one lane (G < 8).  The butterfly runs in fp64:

@@ -80,6 +80,25 @@ SmoothLayout smooth_layout(int64_t M, int64_t K) {
     return L;
 }
 
+struct AsymLayout {
+    size_t s_x, z_x, r_x, xq, total;
+};
+
+AsymLayout asym_layout(int64_t M, int64_t K) {
+    AsymLayout L;
+    size_t off = 0;
+    L.s_x = off; off += up((size_t)M * 4);
+    L.z_x = off; off += up((size_t)M * 4);
+    L.r_x = off; off += up((size_t)M * 4);
+    L.xq = off; off += up((size_t)M * (size_t)K);
+    L.total = off;
+    return L;
+}
+
+// K bound of the zero-point linear: sum_k (xq - z_x)(wq - z_w) has |.| <= 255^2 K
+// and is evaluated in int32.
+constexpr int64_t kMaxK_asym = 32768;
+
 struct W4Layout {
     size_t xp, s_x, total;
 };
@@ -290,6 +309,77 @@ qa_status qa_qlinear_int8_topk(const void* X_f16, int64_t M, int64_t K, int64_t 
     ep.ldo = N;
     ep.out_dtype = (int)out_dtype;
     return device_status(qa::launch_gemm_i8_mixed(xq, Wq, M, K, N, ep, st), "qa_qlinear_int8_topk (gemm)");
+}
+
+// ----------------------------------------------------------------- zero-point (asymmetric)
+qa_status qa_quantize_rowwise_int8_asym(const void* X_f16, int64_t rows, int64_t K, int32_t q_min, int32_t q_max,
+                                        int8_t* q, float* s_out, int32_t* z_out, int32_t* rowsum_or_null,
+                                        void* stream) {
+    if (rows < 0 || K <= 0 || K % 8 != 0 || K > kMaxK_quant)
+        return fail(QA_ERR_SHAPE, "qa_quantize_rowwise_int8_asym: need rows >= 0, 0 < K <= 2^26, K %% 8 == 0");
+    if (q_min >= q_max || q_min < -128 || q_max > 127)
+        return fail(QA_ERR_VALUE, "qa_quantize_rowwise_int8_asym: need -128 <= q_min < q_max <= 127");
+    if (rows == 0) return ok();
+    if (!X_f16 || !q || !s_out || !z_out) return fail(QA_ERR_NULL, "qa_quantize_rowwise_int8_asym: NULL pointer");
+    if (!aligned(X_f16, 16) || !aligned(q, 16) || !aligned(s_out, 4) || !aligned(z_out, 4) ||
+        (rowsum_or_null && !aligned(rowsum_or_null, 4)))
+        return fail(QA_ERR_ALIGN, "qa_quantize_rowwise_int8_asym: X, q 16-byte, s/z/rowsum 4-byte aligned");
+    return device_status(qa::launch_rowquant_i8_asym(static_cast<const uint16_t*>(X_f16), rows, K, q_min, q_max, q,
+                                                     s_out, z_out, rowsum_or_null, as_stream(stream)),
+                         "qa_quantize_rowwise_int8_asym");
+}
+
+qa_status qa_int8_row_sums(const int8_t* A, int64_t rows, int64_t K, int32_t* sums, void* stream) {
+    if (rows < 0 || K <= 0 || K % 16 != 0 || K > kMaxK_quant)
+        return fail(QA_ERR_SHAPE, "qa_int8_row_sums: need rows >= 0, 0 < K <= 2^26, K %% 16 == 0");
+    if (rows == 0) return ok();
+    if (!A || !sums) return fail(QA_ERR_NULL, "qa_int8_row_sums: NULL pointer");
+    if (!aligned(A, 16) || !aligned(sums, 4))
+        return fail(QA_ERR_ALIGN, "qa_int8_row_sums: A 16-byte, sums 4-byte aligned");
+    return device_status(qa::launch_row_sums_i8(A, rows, K, sums, as_stream(stream)), "qa_int8_row_sums");
+}
+
+size_t qa_qlinear_int8_asym_workspace(int64_t M, int64_t K) {
+    if (M < 0 || K <= 0) return 0;
+    return asym_layout(M, K).total;
+}
+
+qa_status qa_qlinear_int8_asym(const void* X_f16, int64_t M, int64_t K, const int8_t* Wq, const float* s_w,
+                               const int32_t* z_w_or_null, const int32_t* w_rowsum, int64_t N, void* out,
+                               qa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    if (M < 0 || N < 0 || K <= 0 || K % 16 != 0 || K > kMaxK_asym)
+        return fail(QA_ERR_SHAPE, "qa_qlinear_int8_asym: need M, N >= 0, 0 < K <= %lld, K %% 16 == 0",
+                    (long long)kMaxK_asym);
+    if (!valid_dtype(out_dtype)) return fail(QA_ERR_VALUE, "qa_qlinear_int8_asym: bad out_dtype %d", (int)out_dtype);
+    if (M == 0 || N == 0) return ok();
+    if (!X_f16 || !Wq || !s_w || !w_rowsum || !out || !workspace)
+        return fail(QA_ERR_NULL, "qa_qlinear_int8_asym: NULL pointer");
+    if (!aligned(X_f16, 16) || !aligned(Wq, 16) || !aligned(s_w, 4) || !aligned(w_rowsum, 4) || !aligned(out, 4) ||
+        (z_w_or_null && !aligned(z_w_or_null, 4)) || !aligned(workspace, kAlign))
+        return fail(QA_ERR_ALIGN, "qa_qlinear_int8_asym: X, Wq 16-byte, workspace 256-byte, other arrays 4-byte");
+    const AsymLayout L = asym_layout(M, K);
+    if (workspace_bytes < L.total)
+        return fail(QA_ERR_WORKSPACE, "qa_qlinear_int8_asym: workspace %zu < %zu bytes", workspace_bytes, L.total);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    float* s_x = reinterpret_cast<float*>(ws + L.s_x);
+    int32_t* z_x = reinterpret_cast<int32_t*>(ws + L.z_x);
+    int32_t* r_x = reinterpret_cast<int32_t*>(ws + L.r_x);
+    int8_t* xq = reinterpret_cast<int8_t*>(ws + L.xq);
+    hipStream_t st = as_stream(stream);
+    hipError_t e = qa::launch_rowquant_i8_asym(static_cast<const uint16_t*>(X_f16), M, K, -128, 127, xq, s_x, z_x,
+                                               r_x, st);
+    if (e != hipSuccess) return device_status(e, "qa_qlinear_int8_asym (row quantization)");
+    qa::AsymEpilogue ep;
+    ep.s_x = s_x;
+    ep.z_x = z_x;
+    ep.r_x = r_x;
+    ep.s_w = s_w;
+    ep.z_w = z_w_or_null;
+    ep.r_w = w_rowsum;
+    ep.out = out;
+    ep.ldo = N;
+    ep.out_dtype = (int)out_dtype;
+    return device_status(qa::launch_gemm_i8_asym(xq, Wq, M, K, N, ep, st), "qa_qlinear_int8_asym (gemm)");
 }
 
 // ----------------------------------------------------------------- SmoothQuant

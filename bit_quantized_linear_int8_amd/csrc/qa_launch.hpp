@@ -92,6 +92,27 @@ struct MixedEpilogue {
 hipError_t launch_gemm_i8_i32(const int8_t* A, const int8_t* B, int64_t M, int64_t K, int64_t N,
                               int32_t* C, hipStream_t st);
 
+// Zero-point dequantization of the int8 GEMM (see k_gemm_i8_asym).
+struct AsymEpilogue {
+    const float* s_x;          // [M]
+    const int32_t* z_x;        // [M]
+    const int32_t* r_x;        // [M] row sums of Xq (read only with z_w)
+    const float* s_w;          // [N]
+    const int32_t* z_w;        // [N] or nullptr (symmetric weight)
+    const int32_t* r_w;        // [N] row sums of Wq
+    void* out;
+    int64_t ldo;
+    int out_dtype;
+};
+hipError_t launch_gemm_i8_asym(const int8_t* Xq, const int8_t* Wq, int64_t M, int64_t K, int64_t N,
+                               const AsymEpilogue& ep, hipStream_t st);
+
+// Per-row asymmetric (min-max) int8 quantization with the row sums of the
+// codes; and plain row sums of int8 rows.
+hipError_t launch_rowquant_i8_asym(const uint16_t* X, int64_t rows, int64_t K, int qmin, int qmax, int8_t* q,
+                                   float* s_out, int32_t* z_out, int32_t* rowsum, hipStream_t st);
+hipError_t launch_row_sums_i8(const int8_t* A, int64_t rows, int64_t K, int32_t* sums, hipStream_t st);
+
 hipError_t launch_gemm_i8_mixed(const int8_t* Xq, const int8_t* Wq, int64_t M, int64_t K, int64_t N,
                                 const MixedEpilogue& ep, hipStream_t st);
 

@@ -234,6 +234,57 @@ qa_status qa_qlinear_w4a4(const void* X_f16, int64_t M, int64_t K, const uint32_
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Asymmetric (zero-point) row quantization  [Scholia-IQ §6: q = round(x/s) +
+ * z, x^ = s (q - z), z the integer that stands for real 0; §6.2: the grid
+ * shifted onto the data's range, q clipped to [q_min, q_max]]
+ *
+ * Per row r (the pages leave the choice of s and z open; min-max is taken):
+ *   lo = min(min_j X[r][j], 0), hi = max(max_j X[r][j], 0)
+ *   s  = fl32(fl32(hi - lo) / (q_max - q_min))      (1.0 when hi == lo)
+ *   z  = clip(q_min - rint(fl32(lo / s)), q_min, q_max)
+ *   q[r][j]   = clip(rint(fl32(X[r][j] / s)) + z, q_min, q_max)
+ *   rowsum[r] = sum_j q[r][j]                          (if rowsum != NULL)
+ *   X fp16 [rows x K]; q i8 [rows x K]; s_out f32, z_out i32, rowsum i32 [rows]
+ * Errors: NULL pointers, rows < 0, K <= 0, K > 2^26, K % 8 != 0, X or q not
+ * 16-byte aligned, q_min >= q_max or outside [-128, 127].
+ * ------------------------------------------------------------------------- */
+qa_status qa_quantize_rowwise_int8_asym(const void* X_f16, int64_t rows, int64_t K, int32_t q_min, int32_t q_max,
+                                        int8_t* q, float* s_out, int32_t* z_out, int32_t* rowsum_or_null,
+                                        void* stream);
+
+/* Row sums of int8 rows: sums[r] = sum_j A[r][j] (the weight term of the
+ * zero-point correction below for a weight quantized without zero-point).
+ * Errors: NULL pointers, rows < 0, K <= 0, K > 2^26, K % 16 != 0, A not
+ * 16-byte aligned. */
+qa_status qa_int8_row_sums(const int8_t* A, int64_t rows, int64_t K, int32_t* sums, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * W8A8 linear with zero-point activations  [Scholia-IQ §6, §6.2;
+ * AIInfra-Q01 "b. INT8 矩阵乘法与反量化"]
+ *
+ *   (Xq, s_x, z_x) = qa_quantize_rowwise_int8_asym(X, -128, 127)  (per token,
+ *                    on device)
+ *   out[m][n] = s_x[m] s_w[n] sum_k (Xq[m][k] - z_x[m]) (Wq[n][k] - z_w[n])
+ * evaluated as C - z_x a[n] - z_w[n] r_x[m] with C the int32 GEMM,
+ * a[n] = w_rowsum[n] - K z_w[n] and r_x the activation code sums (exact).
+ *   Wq i8 [N x K], s_w f32 [N]: the weight (symmetric from
+ *           qa_quantize_rowwise_int8, or asymmetric from
+ *           qa_quantize_rowwise_int8_asym with z_w = its z_out)
+ *   z_w     i32 [N] or NULL (zero-point 0)
+ *   w_rowsum  i32 [N]: sum_k Wq[n][k] (rowsum_out of the asymmetric
+ *           quantizer, or qa_int8_row_sums)
+ *   out     [M x N] of out_dtype
+ *   workspace  qa_qlinear_int8_asym_workspace(M, K) bytes (any content)
+ * Errors: NULL pointers, M < 0, N < 0, K <= 0, K % 16 != 0, K > 32768 (the
+ * integer sum must fit int32), misaligned pointers, bad out_dtype, small
+ * workspace.
+ * ------------------------------------------------------------------------- */
+size_t qa_qlinear_int8_asym_workspace(int64_t M, int64_t K);
+qa_status qa_qlinear_int8_asym(const void* X_f16, int64_t M, int64_t K, const int8_t* Wq, const float* s_w,
+                               const int32_t* z_w_or_null, const int32_t* w_rowsum, int64_t N, void* out,
+                               qa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Column absolute maxima  [QE2 §4.2: max|X_j| and max|W_j| per input channel]
  *
  *   colmax[j] = max_r |A[r][j]|  (accumulate == 0)

@@ -272,3 +272,47 @@ def test_topk_linear_argument_errors():
     assert call(1, 0) == OK and call(7, 0) == OK
     assert qa.lib().qa_qlinear_int8_topk_workspace(64, 512) == qa.lib().qa_qlinear_int8_mixed_workspace(64, 512)
     assert qa.topk_count(0.01, 4096) == 41 and qa.topk_count(0.02, 4096) == 82 and qa.topk_count(0.0, 64) == 0
+
+
+def test_asym_quantize_argument_errors():
+    f = qa.lib().qa_quantize_rowwise_int8_asym
+    args = [A, 4, 64, -128, 127, B, OUT, WS, None, None]
+
+    def call(i, v):
+        a = list(args)
+        a[i] = v
+        return f(*a)
+    assert call(0, None) == NULL
+    assert call(6, None) == NULL
+    assert call(7, None) == NULL
+    assert call(2, 60) == SHAPE
+    assert call(1, -1) == SHAPE
+    assert f(A, 4, 64, 5, 5, B, OUT, WS, None, None) == VALUE    # q_min == q_max
+    assert f(A, 4, 64, -129, 127, B, OUT, WS, None, None) == VALUE
+    assert call(0, MIS) == ALIGN
+    assert call(1, 0) == OK
+    g = qa.lib().qa_int8_row_sums
+    assert g(None, 4, 64, OUT, None) == NULL
+    assert g(A, 4, 72, OUT, None) == SHAPE
+    assert g(MIS, 4, 64, OUT, None) == ALIGN
+    assert g(A, 0, 64, OUT, None) == OK
+
+
+def test_asym_linear_argument_errors():
+    f = qa.lib().qa_qlinear_int8_asym
+    base = [A, 16, 256, B, OUT, None, OUT, 32, OUT, 1, WS, 1 << 30, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+    assert call(0, None) == NULL
+    assert call(6, None) == NULL                               # the weight row sums are required
+    assert call(10, None) == NULL
+    assert call(2, 24) == SHAPE
+    assert call(2, 32784) == SHAPE                             # int32 bound of the zero-point sum
+    assert call(9, 4) == VALUE
+    assert call(3, MIS) == ALIGN
+    assert call(11, 64) == WORKSPACE
+    assert call(1, 0) == OK and call(7, 0) == OK
+    assert qa.lib().qa_qlinear_int8_asym_workspace(64, 512) >= 64 * 512 + 12 * 64
