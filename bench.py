@@ -13,8 +13,8 @@ moved per step / step time (GB/s).
 Also reported (same JSON line, key "also"): whole-call throughput of the
 prefill-shape mixed linear, the W8A8 FFN shape, the W4A4 group-Hadamard
 linear, the SmoothQuant W8A8 linear on the prefill and FFN data and the
-top-2% decomposition on the prefill data, in int8 TOPS against the dense
-int8 MFMA peak.
+top-2% decomposition and the zero-point W8A8 linear on the prefill data, in
+int8 TOPS against the dense int8 MFMA peak.
 
 roofline: the decode kernel's algorithmic bytes per launch / its average
 launch duration, from HIP events recorded on the launch stream around the
@@ -53,7 +53,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--only", default=None,
                    help="run one workload only (decode|prefill|w8a8|w4a4|smooth_prefill|smooth_ffn|topk_prefill|"
-                        "copy), for "
+                        "asym_prefill|copy), for "
                         "profiling; copy is a plain "
                         "1 GiB device copy used to calibrate HBM byte counters")
     return p.parse_args()
@@ -192,6 +192,20 @@ def topk_workload(torch, qa, synthetic, dev, name, share):
     return c, fns, 2 * M * N * K, k
 
 
+def asym_workload(torch, qa, synthetic, dev, name):
+    """W8A8 with per-token zero-point activations and a zero-point weight on a
+    workload's data."""
+    c = synthetic.config(name)
+    M, K, N = c["M"], c["K"], c["N"]
+    X = torch.from_numpy(c["X"]).to(dev)
+    Wq, s_w, z_w, rw = qa.qa_quantize_rowwise_int8_asym(torch.from_numpy(c["W"]).to(dev))
+    odt = {0: torch.float32, 1: torch.float16, 2: torch.bfloat16}[c["out_dtype"]]
+    out = torch.empty((M, N), dtype=odt, device=dev)
+    ws = torch.empty(qa.qa_qlinear_int8_asym_workspace(M, K), dtype=torch.uint8, device=dev)
+    fns = [lambda: qa.qa_qlinear_int8_asym(X, Wq, s_w, rw, z_w=z_w, out=out, workspace=ws)]
+    return c, fns, 2 * M * N * K
+
+
 def w4a4_workload(torch, qa, synthetic, dev):
     c = synthetic.config("w4a4_hadamard")
     M, K, N, G = c["M"], c["K"], c["N"], c["G"]
@@ -286,13 +300,13 @@ def main():
         del fns, gs
         torch.cuda.empty_cache()
 
-    keys = ("prefill", "w8a8", "w4a4", "smooth_prefill", "smooth_ffn", "topk_prefill")
+    keys = ("prefill", "w8a8", "w4a4", "smooth_prefill", "smooth_ffn", "topk_prefill", "asym_prefill")
     run_also = (args.only is None and not args.no_also) or args.only in keys
     if run_also:
         todo = []
         for name, key in (("prefill_mixed", "prefill"), ("w8a8_ffn", "w8a8"), ("w4a4_hadamard", "w4a4"),
                           ("prefill_mixed", "smooth_prefill"), ("w8a8_ffn", "smooth_ffn"),
-                          ("prefill_mixed", "topk_prefill")):
+                          ("prefill_mixed", "topk_prefill"), ("prefill_mixed", "asym_prefill")):
             if args.only in (None, key):
                 todo.append((name, key))
         for name, key in todo:
@@ -305,6 +319,9 @@ def main():
             elif key == "topk_prefill":
                 c, fns, ops, k = topk_workload(torch, qa, synthetic, dev, name, 0.02)
                 name = "topk_prefill: LLM.int8() with the top 2%% (%d) of dims in fp16, %s data" % (k, name)
+            elif key == "asym_prefill":
+                c, fns, ops = asym_workload(torch, qa, synthetic, dev, name)
+                name = "asym_prefill: W8A8 with zero-point activations and weight, %s data" % name
             elif key == "smooth_ffn":
                 c, fns, ops = smooth_workload(torch, qa, synthetic, dev, name, per_tensor=True)
                 name = "smoothquant_ffn: X/s per-tensor int8, %s data" % name
