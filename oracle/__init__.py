@@ -9,7 +9,9 @@ Every function follows the page passages cited in ``oracle.c``:
 LLM.int8() (AIInfra 05Quantization01; Quantization explained part 2, §1.2),
 scale / zero-point / group granularity (模型推理量化 §4-§7), the group
 Hadamard W4A4 scheme (分组旋转方法从W8A8到W4A4, §二, §5.1-§5.4) and the
-SmoothQuant migration (Quantization explained part 2, §4.2).
+SmoothQuant migration (Quantization explained part 2, §4.2), zero-point
+quantization (模型推理量化 §6) and the FlatQuant Kronecker transform (AIInfra
+05Quantization01, FlatQuant section).
 """
 from __future__ import annotations
 
@@ -61,6 +63,10 @@ def lib() -> ctypes.CDLL:
             "orc_qlinear_int8_mixed": (None, [P, I64, I64, P, P, P, I64, F, P, I64, P]),
             "orc_outlier_topk": (None, [P, I64, I64, I64, P, P, P, P]),
             "orc_qlinear_int8_topk": (None, [P, I64, I64, P, P, P, I64, I64, P, I64, P]),
+            "orc_kron_sizes": (None, [I64, P, P]),
+            "orc_kron_transform_f32": (None, [P, I64, I64, I64, P, P, P]),
+            "orc_kron_quant_int4": (None, [P, I64, I64, I64, I64, P, P, I64, I32, I32, P, P]),
+            "orc_qlinear_kron_w4a4": (None, [P, I64, I64, I64, I64, P, P, P, P, I64, I32, P, I64, P]),
             "orc_minmax_params": (None, [P, I64, I32, I32, P, P]),
             "orc_quant_rows_asym_f32": (None, [P, I64, I64, I32, I32, P, P, P, P]),
             "orc_qlinear_int8_asym": (None, [P, I64, I64, P, P, P, I64, P, I64, P]),
@@ -220,6 +226,60 @@ def qlinear_int8_mixed(X16, Wq, s_w, W16=None, tau=6.0, rows=None):
     out = np.zeros((nr if r is not None else M, N), np.float64)
     lib().orc_qlinear_int8_mixed(_ptr(h), M, K, _ptr(Wq), _ptr(sw), _ptr(w16), N, float(tau),
                                  _ptr(r), nr, _ptr(out))
+    return out
+
+
+# ---------------------------------------------------------------- Kronecker transform (FlatQuant apply side)
+def kron_sizes(n: int):
+    """(n1, n2) with n1 n2 = n, n1 <= n2, n1 + n2 smallest."""
+    a = np.zeros(1, np.int64)
+    b = np.zeros(1, np.int64)
+    lib().orc_kron_sizes(int(n), _ptr(a), _ptr(b))
+    return int(a[0]), int(b[0])
+
+
+def kron_transform(x, P1, P2):
+    """Rows of x (fp16 or fp32, [rows x n1 n2]) -> fp32 rows of P1^T X~ P2."""
+    a = _f32_matrix(x)
+    rows, n = a.shape
+    p1 = _c(P1, np.float32)
+    p2 = _c(P2, np.float32)
+    n1, n2 = p1.shape[0], p2.shape[0]
+    assert n1 * n2 == n
+    out = np.zeros((rows, n), np.float32)
+    lib().orc_kron_transform_f32(_ptr(a), rows, n1, n2, _ptr(p1), _ptr(p2), _ptr(out))
+    return out
+
+
+def kron_quant_int4(X16, P1, P2, per_group_G=None, qmin=-7, qmax=7):
+    """Transform + int4 codes + packing -> (packed u32 [rows x K/8], s f32 [rows x groups])."""
+    h = _h16(X16)
+    if h.ndim == 1:
+        h = h[None, :]
+    rows, K = h.shape
+    p1 = _c(P1, np.float32)
+    p2 = _c(P2, np.float32)
+    g = K if per_group_G is None else int(per_group_G)
+    packed = np.zeros((rows, K // 8), np.uint32)
+    s = np.zeros((rows, K // g), np.float32)
+    lib().orc_kron_quant_int4(_ptr(h), rows, K, p1.shape[0], p2.shape[0], _ptr(p1), _ptr(p2), g, int(qmin),
+                              int(qmax), _ptr(packed), _ptr(s))
+    return packed, s
+
+
+def qlinear_kron_w4a4(X16, P1, P2, Wp, s_w, G=128, rows=None):
+    """W4A4 linear with the Kronecker transform of X, fp64 [nrows x N]."""
+    h = _h16(X16)
+    M, K = h.shape
+    p1 = _c(P1, np.float32)
+    p2 = _c(P2, np.float32)
+    wp = _c(Wp, np.uint32)
+    sw = _c(s_w, np.float32)
+    N = wp.shape[0]
+    r, nr = _rows(rows)
+    out = np.zeros((nr if r is not None else M, N), np.float64)
+    lib().orc_qlinear_kron_w4a4(_ptr(h), M, K, p1.shape[0], p2.shape[0], _ptr(p1), _ptr(p2), _ptr(wp), _ptr(sw), N,
+                                int(G), _ptr(r), nr, _ptr(out))
     return out
 
 

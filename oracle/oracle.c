@@ -23,6 +23,12 @@
  *                  offline weight transform, §5.2 online activation transform
  *                  fused with dynamic quantization, §5.4 eight int4 per 32-bit
  *                  word and int32 accumulation.
+ *   [FlatQuant]    AIInfra 05Quantization01, FlatQuant section (the apply
+ *                  stage: X~ = X reshaped to [k x n1 x n2],
+ *                  X' = X~ x1 P1^T x2 P2, dynamic int4 codes of X', int4
+ *                  GEMM with the offline-transformed weight; Kronecker sizes
+ *                  argmin (n1 + n2) with n1 n2 = n, n1 <= n2), and
+ *                  "从离群值到平坦线" §2 (4096 = 64 x 64).
  *   [QE2]          "Quantization explained, part 2" (tanjunchen.github.io):
  *                  §1.2, threshold 6.0 on a channel's activation magnitude and
  *                  the 4096-wide row with one value of 70; §4.2 SmoothQuant,
@@ -44,6 +50,10 @@
  *     hi = max(max_j x_j, 0) (the range holds real 0, which z stands for),
  *     s = fl32(fl32(hi - lo) / (qmax - qmin)) (1.0 when hi == lo),
  *     z = clip(qmin - rint(fl32(lo / s)), qmin, qmax); codes by the affine rule.
+ *   - Kronecker transform of a row x (X~[i][j] = x[i n2 + j]): X' = P1^T X~ P2,
+ *     i.e. x (P1 (x) P2); mode 1 first, each output a chain of fp32 fused
+ *     multiply-adds over the contraction index in ascending order, from 0
+ *     (the codes are decided on these fp32 values).
  *   - SmoothQuant: s_j = fl32(pow(cx_j, alpha) / pow(cw_j, 1 - alpha)) in
  *     fp64, and s_j = 1 when cx_j or cw_j is 0 (the formula is undefined or
  *     zero there).  Activations become fl32(x / s_j), weights fl32(w * s_j),
@@ -377,6 +387,114 @@ static void orc_mixed_with_set(const uint16_t* X, int64_t M, int64_t K,
         free(xq);
     }
     free(wt);
+}
+
+/* ---------------------------------------------------------------------------
+ * Kronecker affine transform  [FlatQuant]
+ * ------------------------------------------------------------------------- */
+
+void orc_pack_int4(const int8_t* q, int64_t rows, int64_t K, uint32_t* packed);
+void orc_unpack_int4(const uint32_t* packed, int64_t rows, int64_t K, int8_t* q);
+
+/* (n1, n2) minimizing n1 + n2 over n1 n2 = n, n1 <= n2. */
+void orc_kron_sizes(int64_t n, int64_t* n1, int64_t* n2)
+{
+    int64_t b1 = 1, b2 = n;
+    for (int64_t a = 1; a * a <= n; ++a) {
+        if (n % a != 0)
+            continue;
+        if (a + n / a < b1 + b2) {
+            b1 = a;
+            b2 = n / a;
+        }
+    }
+    *n1 = b1;
+    *n2 = b2;
+}
+
+/* out[r] = reshape( P1^T X~_r P2 ), X~_r = x[r] as [n1 x n2] row-major.
+ * P1 [n1 x n1], P2 [n2 x n2] row-major.  Mode 1 first:
+ *   Y[a][j]  = sum_i P1[i][a] X~[i][j]     (fmaf chain, i ascending)
+ *   X'[a][b] = sum_j Y[a][j] P2[j][b]      (fmaf chain, j ascending) */
+void orc_kron_transform_f32(const float* x, int64_t rows, int64_t n1, int64_t n2, const float* P1,
+                            const float* P2, float* out)
+{
+    int64_t n = n1 * n2;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const float* xt = x + r * n;
+        float* y = (float*)malloc(sizeof(float) * (size_t)(n > 0 ? n : 1));
+        for (int64_t a = 0; a < n1; ++a)
+            for (int64_t j = 0; j < n2; ++j) {
+                float acc = 0.0f;
+                for (int64_t i = 0; i < n1; ++i)
+                    acc = fmaf(P1[i * n1 + a], xt[i * n2 + j], acc);
+                y[a * n2 + j] = acc;
+            }
+        for (int64_t a = 0; a < n1; ++a)
+            for (int64_t b = 0; b < n2; ++b) {
+                float acc = 0.0f;
+                for (int64_t j = 0; j < n2; ++j)
+                    acc = fmaf(y[a * n2 + j], P2[j * n2 + b], acc);
+                out[r * n + a * n2 + b] = acc;
+            }
+        free(y);
+    }
+}
+
+/* Transform + int4 codes (one scale per gsize columns; gsize = K: per row)
+ * + packing, as the Hadamard path does after its rotation. */
+void orc_kron_quant_int4(const uint16_t* X, int64_t rows, int64_t K, int64_t n1, int64_t n2,
+                         const float* P1, const float* P2, int64_t gsize, int32_t qmin, int32_t qmax,
+                         uint32_t* packed, float* s)
+{
+    size_t n = (size_t)(rows * K > 0 ? rows * K : 1);
+    float* xf = (float*)malloc(sizeof(float) * n);
+    float* xt = (float*)malloc(sizeof(float) * n);
+    int8_t* q = (int8_t*)malloc(n);
+    orc_f16_to_f32_array(X, rows * K, xf);
+    orc_kron_transform_f32(xf, rows, n1, n2, P1, P2, xt);
+    orc_quant_rows_f32(xt, rows, K, gsize, NULL, qmin, qmax, NULL, NULL, q, s);
+    orc_pack_int4(q, rows, K, packed);
+    free(q);
+    free(xt);
+    free(xf);
+}
+
+/* W4A4 linear with the Kronecker transform of X (per-token int4 scale) and
+ * the offline-transformed weight (Wp, s_w per (row, G-group)):
+ * out[m][n] = s_x[m] sum_g s_w[n][g] sum_{k in g} qx[m][k] qw[n][k]. */
+void orc_qlinear_kron_w4a4(const uint16_t* X, int64_t M, int64_t K, int64_t n1, int64_t n2, const float* P1,
+                           const float* P2, const uint32_t* Wp, const float* s_w, int64_t N, int32_t G,
+                           const int64_t* rows, int64_t nrows, double* out)
+{
+    if (!rows)
+        nrows = M;
+    int64_t ng = K / G;
+    int8_t* wq = (int8_t*)malloc((size_t)(N * K > 0 ? N * K : 1));
+    orc_unpack_int4(Wp, N, K, wq);
+    for (int64_t ri = 0; ri < nrows; ++ri) {
+        int64_t m = rows ? rows[ri] : ri;
+        uint32_t* xp = (uint32_t*)malloc(sizeof(uint32_t) * (size_t)(K / 8 > 0 ? K / 8 : 1));
+        int8_t* xq = (int8_t*)malloc((size_t)K);
+        float s_x = 0.0f;
+        orc_kron_quant_int4(X + m * K, 1, K, n1, n2, P1, P2, K, -7, 7, xp, &s_x);
+        orc_unpack_int4(xp, 1, K, xq);
+#pragma omp parallel for schedule(static)
+        for (int64_t n = 0; n < N; ++n) {
+            double sum = 0.0;
+            for (int64_t g = 0; g < ng; ++g) {
+                int64_t a = 0;
+                for (int64_t k = g * G; k < (g + 1) * G; ++k)
+                    a += (int64_t)xq[k] * (int64_t)wq[n * K + k];
+                sum += (double)s_w[n * ng + g] * (double)a;
+            }
+            out[ri * N + n] = (double)s_x * sum;
+        }
+        free(xq);
+        free(xp);
+    }
+    free(wq);
 }
 
 /* ---------------------------------------------------------------------------

@@ -102,6 +102,24 @@ def smoothquant_toy(T=32, C_in=16, C_out=8, outlier_channel=3, outlier_gain=60.0
     return X.numpy().astype(np.float32), W.numpy().astype(np.float32)
 
 
+def kron_factors(n1, n2, seed=0, kind="orthogonal"):
+    """Stand-ins for FlatQuant's learned Kronecker factors (learning them needs
+    calibration data): P1 [n1 x n1], P2 [n2 x n2] as float32.  kind:
+    "orthogonal" -- Q of the QR factorization of a standard normal matrix;
+    "general" -- identity plus N(0, 0.3 / sqrt(n)) noise (invertible, not
+    orthogonal, not symmetric)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for n in (n1, n2):
+        if kind == "orthogonal":
+            q, r = np.linalg.qr(rng.normal(0.0, 1.0, size=(n, n)))
+            q = q * np.sign(np.diag(r))[None, :]
+            out.append(q.astype(np.float32))
+        else:
+            out.append((np.eye(n) + rng.normal(0.0, 0.3 / np.sqrt(n), size=(n, n))).astype(np.float32))
+    return out[0], out[1]
+
+
 def config(name: str) -> dict:
     """The five workloads at full size.  Keys: X (fp16 [M x K]), W (fp16
     [N x K]), dims (planted outlier dims), tau, out_dtype, G, pass_w16, M, K, N."""

@@ -693,3 +693,117 @@ def test_zero_point_helps_one_sided_activations():
     e_asym = np.abs(oracle.qlinear_int8_asym(X, Wq, s_w) - exact).mean()
     e_sym = np.abs(oracle.qlinear_int8_mixed(X, Wq, s_w, tau=float("inf")) - exact).mean()
     assert e_asym < e_sym
+
+
+# ------------------------------------------------------------------ Kronecker transform (FlatQuant)
+def test_kron_sizes_page_examples():
+    for c in golden("kron_sizes.json")["cases"]:
+        assert oracle.kron_sizes(c["n"]) == (c["n1_printed"], c["n2_printed"])
+
+
+def test_kron_sizes_bruteforce():
+    for n in list(range(1, 600)) + [11008, 14336, 28672]:
+        pairs = [(a, n // a) for a in range(1, n + 1) if n % a == 0 and a <= n // a]
+        best = min(pairs, key=lambda p: p[0] + p[1])
+        assert oracle.kron_sizes(n) == best
+
+
+def _gamma(n):
+    u = 2.0 ** -24
+    return n * u / (1 - n * u)
+
+
+@pytest.mark.parametrize("n1,n2", [(4, 8), (8, 8), (16, 32), (64, 64)])
+def test_kron_transform_is_the_kronecker_product(n1, n2):
+    """x (P1 (x) P2) within the error bound of two fp32 dot-product chains."""
+    rng = np.random.default_rng(n1 * 100 + n2)
+    X = rng.normal(0, 2.0, (7, n1 * n2)).astype(np.float16)
+    P1, P2 = synthetic.kron_factors(n1, n2, seed=n2, kind="general")
+    P1 = P1 + rng.normal(0, 0.2, P1.shape).astype(np.float32)   # clearly non-symmetric
+    got = oracle.kron_transform(X, P1, P2).astype(np.float64)
+    X64, A, B = X.astype(np.float64), P1.astype(np.float64), P2.astype(np.float64)
+    ref = X64 @ np.kron(A, B)
+    Xt = np.abs(X64).reshape(-1, n1, n2)
+    e1 = _gamma(n1) * np.einsum("ia,rij->raj", np.abs(A), Xt)          # stage-1 error bound
+    Y = np.abs(np.einsum("ia,rij->raj", A, X64.reshape(-1, n1, n2)))
+    bound = (_gamma(n2) * np.einsum("raj,jb->rab", Y + e1, np.abs(B)) + np.einsum("raj,jb->rab", e1, np.abs(B)))
+    assert np.all(np.abs(got - ref) <= bound.reshape(got.shape) * (1 + 1e-6) + 1e-30)
+    # the other reading of the mode-2 product (P2 transposed) is a different map
+    alt = X64 @ np.kron(A, B.T)
+    assert np.abs(got - alt).max() > 1e3 * bound.max()
+
+
+def test_kron_identity_and_permutations_are_exact():
+    rng = np.random.default_rng(71)
+    X = rng.normal(0, 3.0, (5, 96)).astype(np.float16)
+    assert np.array_equal(oracle.kron_transform(X, np.eye(8, dtype=np.float32), np.eye(12, dtype=np.float32)),
+                          X.astype(np.float32))
+    p1, p2 = rng.permutation(8), rng.permutation(12)
+    P1 = np.eye(8, dtype=np.float32)[p1]
+    P2 = np.eye(12, dtype=np.float32)[p2]
+    ref = (X.astype(np.float64) @ np.kron(P1.astype(np.float64), P2.astype(np.float64))).astype(np.float32)
+    assert np.array_equal(oracle.kron_transform(X, P1, P2), ref)
+
+
+@pytest.mark.parametrize("n1,n2", [(2, 4), (8, 8), (16, 32), (64, 64)])
+def test_kron_of_hadamards_is_the_sylvester_hadamard(n1, n2):
+    """H_n1 (x) H_n2 = H_n (Sylvester order): on small integers every partial
+    sum is exact, so the transform equals the integer product."""
+    rng = np.random.default_rng(n1 + n2)
+    X = rng.integers(-8, 9, (6, n1 * n2))
+    H1 = scipy.linalg.hadamard(n1).astype(np.float32)
+    H2 = scipy.linalg.hadamard(n2).astype(np.float32)
+    got = oracle.kron_transform(X.astype(np.float16), H1, H2)
+    assert np.array_equal(got.astype(np.int64), X @ scipy.linalg.hadamard(n1 * n2))
+
+
+def test_kron_weight_transform_cancels_in_the_product():
+    """(X P)(P^-1 W^T) = X W^T: the weight rows take P1^-T, P2^-T."""
+    X, W, _ = synthetic.mixed_inputs(16, 256, 24, seed=72, n_dims=3)
+    P1, P2 = synthetic.kron_factors(16, 16, seed=73, kind="general")
+    P1w = np.linalg.inv(P1.astype(np.float64)).T.astype(np.float32)
+    P2w = np.linalg.inv(P2.astype(np.float64)).T.astype(np.float32)
+    Xt = oracle.kron_transform(X, P1, P2).astype(np.float64)
+    Wt = oracle.kron_transform(W, P1w, P2w).astype(np.float64)
+    exact = X.astype(np.float64) @ W.astype(np.float64).T
+    mag = np.abs(X.astype(np.float64)) @ np.abs(W.astype(np.float64)).T
+    assert np.all(np.abs(Xt @ Wt.T - exact) <= 1e-5 * mag.max())
+
+
+def test_kron_quant_int4_is_transform_then_codes():
+    X, _, _ = synthetic.mixed_inputs(9, 512, 1, seed=74, n_dims=3)
+    P1, P2 = synthetic.kron_factors(16, 32, seed=75)
+    for G in (None, 128):
+        packed, s = oracle.kron_quant_int4(X, P1, P2, per_group_G=G)
+        q, s_ref = oracle.quant_rows(oracle.kron_transform(X, P1, P2), gsize=G, qmin=-7, qmax=7)
+        assert np.array_equal(s, s_ref)
+        assert np.array_equal(_unpack_np(packed, 512), q)
+
+
+def test_kron_w4a4_linear_is_the_dequantized_product():
+    X, W, _ = synthetic.mixed_inputs(6, 256, 20, seed=76, n_dims=2)
+    P1, P2 = synthetic.kron_factors(16, 16, seed=77)
+    Wp, s_w = oracle.kron_quant_int4(W, P1, P2, per_group_G=64)
+    Xp, s_x = oracle.kron_quant_int4(X, P1, P2)
+    qx, qw = _unpack_np(Xp, 256).astype(np.int64), _unpack_np(Wp, 256).astype(np.int64)
+    ref = np.zeros((6, 20))
+    for g in range(4):
+        acc = qx[:, g * 64:(g + 1) * 64] @ qw[:, g * 64:(g + 1) * 64].T
+        ref += acc.astype(np.float64) * s_w[:, g].astype(np.float64)[None, :]
+    ref *= s_x[:, 0].astype(np.float64)[:, None]
+    out = oracle.qlinear_kron_w4a4(X, P1, P2, Wp, s_w, G=64)
+    assert np.allclose(out, ref, rtol=1e-12, atol=0)
+    rows = np.array([5, 0, 2])
+    assert np.array_equal(oracle.qlinear_kron_w4a4(X, P1, P2, Wp, s_w, G=64, rows=rows), out[rows])
+
+
+def test_orthogonal_kron_transform_lowers_w4a4_error():
+    """The flatness argument: an orthogonal transform spreads the outlier
+    channels, so W4A4 on (X P, W P) is closer to X W^T than on (X, W)."""
+    X, W, _ = synthetic.w4a4_inputs(64, 1024, 48, seed=78)
+    exact = X.astype(np.float64) @ W.astype(np.float64).T
+    errs = []
+    for P1, P2 in ((np.eye(32, dtype=np.float32), np.eye(32, dtype=np.float32)), synthetic.kron_factors(32, 32, 79)):
+        Wp, s_w = oracle.kron_quant_int4(W, P1, P2, per_group_G=128)
+        errs.append(np.abs(oracle.qlinear_kron_w4a4(X, P1, P2, Wp, s_w, G=128) - exact).mean())
+    assert errs[1] < 0.75 * errs[0]
