@@ -30,7 +30,7 @@ EXPORTS = (
     "qa_quantize_rowwise_int8_asym", "qa_int8_row_sums", "qa_qlinear_int8_asym_workspace", "qa_qlinear_int8_asym",
     "qa_col_absmax_workspace", "qa_col_absmax", "qa_smooth_factors", "qa_quantize_smooth_int8",
     "qa_qlinear_int8_smooth_workspace", "qa_qlinear_int8_smooth",
-    "qa_hadamard_quant_int4",
+    "qa_hadamard_quant_int4", "qa_kron_quant_int4", "qa_qlinear_kron_w4a4_workspace", "qa_qlinear_kron_w4a4",
     "qa_qlinear_w4a4_workspace", "qa_qlinear_w4a4",
     "qa_gemm_i8_i32", "qa_gemm_w4a4_group_acc",
 )
@@ -79,6 +79,9 @@ def lib() -> ctypes.CDLL:
             "qa_qlinear_int8_smooth_workspace": (SZ, [I64, I64]),
             "qa_qlinear_int8_smooth": (S, [P, I64, I64, P, S, P, P, I64, P, S, P, SZ, P]),
             "qa_hadamard_quant_int4": (S, [P, I64, I64, I32, S, I32, I32, P, P, P]),
+            "qa_kron_quant_int4": (S, [P, I64, I64, I64, I64, P, P, S, I32, I32, I32, P, P, P]),
+            "qa_qlinear_kron_w4a4_workspace": (SZ, [I64, I64]),
+            "qa_qlinear_kron_w4a4": (S, [P, I64, I64, I64, I64, P, P, P, P, I64, I32, P, S, P, SZ, P]),
             "qa_qlinear_w4a4_workspace": (SZ, [I64, I64]),
             "qa_qlinear_w4a4": (S, [P, I64, I64, P, P, I64, I32, P, S, P, SZ, P]),
             "qa_gemm_i8_i32": (S, [P, P, I64, I64, I64, P, P]),
@@ -359,6 +362,46 @@ def qa_hadamard_quant_int4(X, G: int, per_group: bool, q_min=-7, q_max=7, stream
            lib().qa_hadamard_quant_int4(_p(X), rows, K, int(G), QA_SCALE_PER_GROUP if per_group else QA_SCALE_PER_ROW,
                                         int(q_min), int(q_max), _p(packed), _p(s), _stream(stream)))
     return packed, s
+
+
+def qa_kron_quant_int4(X, P1, P2, G=None, q_min=-7, q_max=7, stream=None):
+    """Kronecker transform P1^T X~ P2 of each row + int4 codes -> (packed u32 as int32 [rows x K/8],
+    s f32 [rows x (K/G if G else 1)])."""
+    _dev(X, "X", torch.float16)
+    _dev(P1, "P1", torch.float32)
+    _dev(P2, "P2", torch.float32)
+    rows, K = X.shape
+    n1, n2 = P1.shape[0], P2.shape[0]
+    packed = torch.empty((rows, K // 8), dtype=torch.int32, device=X.device)
+    s = torch.empty((rows, K // G if G else 1), dtype=torch.float32, device=X.device)
+    _check("qa_kron_quant_int4",
+           lib().qa_kron_quant_int4(_p(X), rows, K, n1, n2, _p(P1), _p(P2),
+                                    QA_SCALE_PER_GROUP if G else QA_SCALE_PER_ROW, int(G or 0), int(q_min), int(q_max),
+                                    _p(packed), _p(s), _stream(stream)))
+    return packed, s
+
+
+def qa_qlinear_kron_w4a4_workspace(M: int, K: int) -> int:
+    return int(lib().qa_qlinear_kron_w4a4_workspace(M, K))
+
+
+def qa_qlinear_kron_w4a4(X, P1, P2, Wp, s_w, G=128, out_dtype=torch.float32, out=None, workspace=None, stream=None):
+    """W4A4 linear with the Kronecker transform of X -> out [M x N]."""
+    _dev(X, "X", torch.float16)
+    _dev(P1, "P1", torch.float32)
+    _dev(P2, "P2", torch.float32)
+    _dev(Wp, "Wp", torch.int32)
+    _dev(s_w, "s_w", torch.float32)
+    M, K = X.shape
+    N = Wp.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=X.device)
+    workspace = _workspace(qa_qlinear_kron_w4a4_workspace(M, K), X.device, workspace)
+    _check("qa_qlinear_kron_w4a4",
+           lib().qa_qlinear_kron_w4a4(_p(X), M, K, P1.shape[0], P2.shape[0], _p(P1), _p(P2), _p(Wp), _p(s_w), N,
+                                      int(G), _p(out), _DTYPE_CODE[out.dtype], _p(workspace), workspace.numel(),
+                                      _stream(stream)))
+    return out
 
 
 def qa_qlinear_w4a4_workspace(M: int, K: int) -> int:

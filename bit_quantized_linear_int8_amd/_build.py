@@ -18,7 +18,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqa.so")
 
 ARCH = "gfx950"
-SOURCES = ["qa_api.cpp", "k_quant.hip", "k_smooth.hip", "k_gemm.hip", "k_decode.hip"]
+SOURCES = ["qa_api.cpp", "k_quant.hip", "k_smooth.hip", "k_kron.hip", "k_gemm.hip", "k_decode.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -441,24 +441,6 @@ __device__ __forceinline__ u32x2 codes8_static(const float* x, u32x2 mk, float s
     return u32x2{w[0], w[1]};
 }
 
-// dynamic codes with the clip of a narrower [qmin, qmax] than [-qmax, qmax]
-__device__ __forceinline__ u32x2 clip_codes(u32x2 c, int qmin) {
-    if (qmin <= -127) return c;
-    uint32_t w[2] = {c[0], c[1]};
-#pragma unroll
-    for (int d = 0; d < 2; ++d) {
-        uint32_t o = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            int q = (int8_t)(w[d] >> (8 * j));
-            q = q < qmin ? qmin : q;
-            o |= ((uint32_t)q & 0xffu) << (8 * j);
-        }
-        w[d] = o;
-    }
-    return u32x2{w[0], w[1]};
-}
-
 constexpr int RQ_FLAG_WORDS = 2048;             // merged flag words in LDS: K <= 131072
 
 template <int NC, bool STATIC, int MASK>
@@ -897,25 +879,6 @@ __device__ __forceinline__ void fwht_chunk(const u32x4& v, double c, int lane, f
 
 // int4 codes of 8 values (|x / s| <= 7 (1 + 2^-23)) packed into one word,
 // element j in bits [4j+3:4j]; clipped to [qmin, qmax].
-__device__ __forceinline__ uint32_t pack_codes(const float* x, float s, float r, int qmin) {
-    const u32x2 c = clip_codes(codes8_dyn(x, s, r), qmin);
-    uint32_t w[2];
-#pragma unroll
-    for (int d = 0; d < 2; ++d) {
-        uint32_t a = c[d] & 0x0f0f0f0fu;          // nibbles of 4 codes in bytes
-        a = (a | (a >> 4)) & 0x00ff00ffu;        // codes 0,1 in byte 0; 2,3 in byte 2
-        w[d] = (a | (a >> 8)) & 0xffffu;
-    }
-    return w[0] | (w[1] << 16);
-}
-
-__device__ __forceinline__ float absmax8f(const float* x) {
-    float a = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) a = fmaxf(a, __builtin_fabsf(x[j]));
-    return a;
-}
-
 // Per-row scale, row held in registers (NC > 0) or recomputed (NC == 0).
 template <int G, int NC>
 __global__ __launch_bounds__(256) void k_hq4_row(const uint16_t* __restrict__ X, int64_t rows, int64_t K,

@@ -64,13 +64,6 @@ __device__ __forceinline__ void smooth8(const u32x4& v, const u32x4& f0, const u
     }
 }
 
-__device__ __forceinline__ float absmax8f(const float* x) {
-    float a = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) a = fmaxf(a, __builtin_fabsf(x[j]));
-    return a;
-}
-
 template <int NC, int OP, int PHASE>
 __global__ __launch_bounds__(256) void k_smoothquant_i8(const uint16_t* __restrict__ X, int64_t rows, int64_t K,
                                                         const float* __restrict__ sm, int8_t* __restrict__ q,

@@ -532,6 +532,65 @@ qa_status qa_qlinear_w4a4(const void* X_f16, int64_t M, int64_t K, const uint32_
                          "qa_qlinear_w4a4 (gemm)");
 }
 
+// ----------------------------------------------------------------- Kronecker transform (FlatQuant)
+qa_status qa_kron_quant_int4(const void* X_f16, int64_t rows, int64_t K, int64_t n1, int64_t n2, const float* P1,
+                             const float* P2, qa_scale_mode mode, int32_t G, int32_t q_min, int32_t q_max,
+                             uint32_t* packed, float* s, void* stream) {
+    if (mode != QA_SCALE_PER_ROW && mode != QA_SCALE_PER_GROUP)
+        return fail(QA_ERR_VALUE, "qa_kron_quant_int4: bad scale mode %d", (int)mode);
+    if (rows < 0 || K <= 0 || n1 <= 0 || n2 <= 0 || n1 * n2 != K)
+        return fail(QA_ERR_SHAPE, "qa_kron_quant_int4: need rows >= 0, n1 n2 == K > 0 (K=%lld n1=%lld n2=%lld)",
+                    (long long)K, (long long)n1, (long long)n2);
+    if (q_min > q_max || q_min < -8 || q_max > 7 || q_max <= 0)
+        return fail(QA_ERR_VALUE, "qa_kron_quant_int4: need -8 <= q_min <= q_max <= 7, q_max > 0");
+    const int g = mode == QA_SCALE_PER_GROUP ? G : 0;
+    if (mode == QA_SCALE_PER_GROUP && (G <= 0 || K % G != 0))
+        return fail(QA_ERR_SHAPE, "qa_kron_quant_int4: per-group needs 0 < G, K %% G == 0 (G=%d)", G);
+    if (!qa::kron_supported(n1, n2, g))
+        return fail(QA_ERR_UNSUPPORTED,
+                    "qa_kron_quant_int4: no kernel for n1=%lld n2=%lld G=%d (sizes 8x8, 8x16, 16x16, 16x32, 32x32, "
+                    "32x64, 64x64, 64x128; per group 8 <= G <= 512, G <= 8 n1 n2 / R^2)",
+                    (long long)n1, (long long)n2, g);
+    if (rows == 0) return ok();
+    if (!X_f16 || !P1 || !P2 || !packed || !s) return fail(QA_ERR_NULL, "qa_kron_quant_int4: NULL pointer");
+    if (!aligned(X_f16, 16) || !aligned(P1, 16) || !aligned(P2, 16) || !aligned(packed, 4) || !aligned(s, 4))
+        return fail(QA_ERR_ALIGN, "qa_kron_quant_int4: X, P1, P2 16-byte, packed/s 4-byte aligned");
+    return device_status(qa::launch_kron_quant_i4(static_cast<const uint16_t*>(X_f16), rows, n1, n2, P1, P2, g, q_min,
+                                                  q_max, packed, s, as_stream(stream)),
+                         "qa_kron_quant_int4");
+}
+
+size_t qa_qlinear_kron_w4a4_workspace(int64_t M, int64_t K) { return qa_qlinear_w4a4_workspace(M, K); }
+
+qa_status qa_qlinear_kron_w4a4(const void* X_f16, int64_t M, int64_t K, int64_t n1, int64_t n2, const float* P1,
+                               const float* P2, const uint32_t* Wp, const float* s_w, int64_t N, int32_t G, void* out,
+                               qa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!w4_group_ok(G) || M < 0 || N < 0 || K <= 0 || K % G != 0 || n1 <= 0 || n2 <= 0 || n1 * n2 != K)
+        return fail(QA_ERR_SHAPE, "qa_qlinear_kron_w4a4: need G in {64,128,256}, M, N >= 0, K %% G == 0, n1 n2 == K");
+    if (!qa::kron_supported(n1, n2, 0))
+        return fail(QA_ERR_UNSUPPORTED, "qa_qlinear_kron_w4a4: no kernel for n1=%lld n2=%lld", (long long)n1,
+                    (long long)n2);
+    if (!valid_dtype(out_dtype)) return fail(QA_ERR_VALUE, "qa_qlinear_kron_w4a4: bad out_dtype %d", (int)out_dtype);
+    if (M == 0 || N == 0) return ok();
+    if (!X_f16 || !P1 || !P2 || !Wp || !s_w || !out || !workspace)
+        return fail(QA_ERR_NULL, "qa_qlinear_kron_w4a4: NULL pointer");
+    if (!aligned(X_f16, 16) || !aligned(P1, 16) || !aligned(P2, 16) || !aligned(Wp, 16) || !aligned(s_w, 4) ||
+        !aligned(out, 4) || !aligned(workspace, kAlign))
+        return fail(QA_ERR_ALIGN, "qa_qlinear_kron_w4a4: X, P1, P2, Wp 16-byte, workspace 256-byte, out/s_w 4-byte");
+    const W4Layout L = w4_layout(M, K);
+    if (workspace_bytes < L.total)
+        return fail(QA_ERR_WORKSPACE, "qa_qlinear_kron_w4a4: workspace %zu < %zu bytes", workspace_bytes, L.total);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    uint32_t* xp = reinterpret_cast<uint32_t*>(ws + L.xp);
+    float* s_x = reinterpret_cast<float*>(ws + L.s_x);
+    hipStream_t st = as_stream(stream);
+    hipError_t e = qa::launch_kron_quant_i4(static_cast<const uint16_t*>(X_f16), M, n1, n2, P1, P2, 0, -7, 7, xp, s_x,
+                                            st);
+    if (e != hipSuccess) return device_status(e, "qa_qlinear_kron_w4a4 (transform + quant)");
+    return device_status(qa::launch_gemm_w4a4(xp, s_x, Wp, s_w, M, K, N, G, out, (int)out_dtype, st),
+                         "qa_qlinear_kron_w4a4 (gemm)");
+}
+
 // ----------------------------------------------------------------- parity entry points
 qa_status qa_gemm_i8_i32(const int8_t* A, const int8_t* B, int64_t M, int64_t K, int64_t N, int32_t* C,
                          void* stream) {

@@ -178,4 +178,44 @@ __device__ __forceinline__ int clampi(int v, int lo, int hi) {
     return v < lo ? lo : (v > hi ? hi : v);
 }
 
+// dynamic codes with the clip of a narrower [qmin, qmax] than [-qmax, qmax]
+__device__ __forceinline__ u32x2 clip_codes(u32x2 c, int qmin) {
+    if (qmin <= -127) return c;
+    uint32_t w[2] = {c[0], c[1]};
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+        uint32_t o = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            int q = (int8_t)(w[d] >> (8 * j));
+            q = q < qmin ? qmin : q;
+            o |= ((uint32_t)q & 0xffu) << (8 * j);
+        }
+        w[d] = o;
+    }
+    return u32x2{w[0], w[1]};
+}
+
+// Eight int4 codes of one chunk as one 32-bit word: element i in bits
+// [4i+3 : 4i], two's complement.
+__device__ __forceinline__ uint32_t pack_codes(const float* x, float s, float r, int qmin) {
+    const u32x2 c = clip_codes(codes8_dyn(x, s, r), qmin);
+    uint32_t w[2];
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+        uint32_t a = c[d] & 0x0f0f0f0fu;          // nibbles of 4 codes in bytes
+        a = (a | (a >> 4)) & 0x00ff00ffu;        // codes 0,1 in byte 0; 2,3 in byte 2
+        w[d] = (a | (a >> 8)) & 0xffffu;
+    }
+    return w[0] | (w[1] << 16);
+}
+
+// Largest magnitude of eight values.
+__device__ __forceinline__ float absmax8f(const float* x) {
+    float a = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a = fmaxf(a, __builtin_fabsf(x[j]));
+    return a;
+}
+
 }  // namespace qa

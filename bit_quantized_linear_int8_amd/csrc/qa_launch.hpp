@@ -69,6 +69,14 @@ hipError_t launch_smooth_factors(const float* cx, const float* cw, int64_t K, fl
 hipError_t launch_smoothquant_i8(const uint16_t* X, int64_t rows, int64_t K, const float* sm, bool multiply,
                                  bool per_tensor, int8_t* q, float* s_out, int32_t* count, hipStream_t st);
 
+// Kronecker transform X' = P1^T X~ P2 of each row (n1 n2 = K) fused with int4
+// codes: per row (G == 0) or per G-wide group; kron_supported(n1, n2, G)
+// tells which sizes have a kernel.
+bool kron_supported(int64_t n1, int64_t n2, int G);
+hipError_t launch_kron_quant_i4(const uint16_t* X, int64_t rows, int64_t n1, int64_t n2, const float* P1,
+                                const float* P2, int G, int qmin, int qmax, uint32_t* packed, float* s,
+                                hipStream_t st);
+
 hipError_t launch_hadamard_quant_i4(const uint16_t* X, int64_t rows, int64_t K, int G,
                                     bool per_group, int qmin, int qmax, uint32_t* packed, float* s,
                                     hipStream_t st);

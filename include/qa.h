@@ -8,6 +8,8 @@
  *     int8 with vector-wise absmax scales (per token for X, per output
  *     channel for W), multiplied with int32 accumulation, dequantized by the
  *     outer product of the scales and summed with the fp16 outlier product.
+ *   - FlatQuant's Kronecker transform (P = P1 (x) P2) fused with int4
+ *     quantization, feeding the same W4A4 GEMM.
  *   - W4A4 group Hadamard: each G-wide block of the K dimension is rotated by
  *     the normalized Hadamard matrix, quantized to int4 (dynamic per-token
  *     scales for X, per-row-per-group scales for W), packed eight per 32-bit
@@ -23,6 +25,10 @@
  *                  "b. INT8 矩阵乘法与反量化", merge of the two parts.
  *                  Its advice for training: decompose the largest-magnitude
  *                  1-2% of feature dimensions instead of about 0.1% (top-k).
+ *                  Its FlatQuant section: the apply stage reshapes each token
+ *                  to X~ [n1 x n2] and computes X~ x1 P1^T x2 P2 with
+ *                  P = P1 (x) P2, fused with dynamic int4 quantization; the
+ *                  sizes minimize n1 + n2 (8192 -> 64 x 128).
  *   [Scholia-IQ]   "模型推理量化" (Inference Quantization notes): §4 Scale,
  *                  §5 Outlier, §6 Zero-point (§6.2 affine clip), §7 Granularity.
  *   [GroupRot]     "低比特量化加速：分组旋转方法从W8A8到W4A4的实践与展望":
@@ -359,6 +365,51 @@ size_t qa_qlinear_int8_smooth_workspace(int64_t M, int64_t K);
 qa_status qa_qlinear_int8_smooth(const void* X_f16, int64_t M, int64_t K, const float* s, qa_scale_mode mode,
                                  const int8_t* Wq, const float* s_w, int64_t N, void* out, qa_dtype out_dtype,
                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Kronecker affine transform fused with int4 quantization  [AIInfra-Q01,
+ * FlatQuant section: X~ x1 P1^T x2 P2, P = P1 (x) P2, dynamic int4 codes in one
+ * kernel]
+ *
+ * Each row x (K = n1 n2) is read as X~[i][j] = x[i n2 + j] and transformed to
+ * X' = P1^T X~ P2 (= x (P1 (x) P2)), mode 1 first, every output one fp32 chain
+ * of fused multiply-adds over the contraction index in ascending order:
+ *   Y[a][j]  = sum_i P1[i][a] X~[i][j],   X'[a][b] = sum_j Y[a][j] P2[j][b].
+ * Then int4 codes of X' as qa_hadamard_quant_int4 makes them (PER_ROW: one
+ * scale per row; PER_GROUP: per G-wide group), packed eight per word.
+ * Activations take the learned P1, P2; the offline weight takes P1^-T, P2^-T
+ * (the same matrices when they are orthogonal), so X' W'^T = X W^T.
+ *   X       fp16 [rows x K]; P1 f32 [n1 x n1], P2 f32 [n2 x n2] row-major
+ *   packed  u32 [rows x K/8]; s f32 [rows] or [rows x K/G]
+ * Sizes with a kernel: (n1, n2) in {(8,8), (8,16), (16,16), (16,32), (32,32),
+ * (32,64), (64,64), (64,128)} -- the minimal-sum splits of 64 .. 8192; per
+ * group, G a multiple of 8 with a group inside one wave's chunks.
+ * Errors: NULL pointers, rows < 0, n1 n2 != K (QA_ERR_SHAPE), no kernel for
+ * the sizes (QA_ERR_UNSUPPORTED), bad mode / q range, misaligned pointers.
+ * ------------------------------------------------------------------------- */
+qa_status qa_kron_quant_int4(const void* X_f16, int64_t rows, int64_t K, int64_t n1, int64_t n2, const float* P1,
+                             const float* P2, qa_scale_mode mode, int32_t G, int32_t q_min, int32_t q_max,
+                             uint32_t* packed, float* s, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * W4A4 linear with the Kronecker transform  [AIInfra-Q01, FlatQuant section:
+ * transform + dynamic int4 of X in one kernel, int4 GEMM with the
+ * pre-transformed int4 weight]
+ *
+ *   (Xp, s_x) = qa_kron_quant_int4(X, n1, n2, P1, P2, PER_ROW, -7, 7)
+ *   out[m][n] = s_x[m] sum_g s_w[n][g] sum_{k in g} qx[m][k] qw[n][k]
+ *   Wp, s_w  the offline weight: qa_kron_quant_int4(W, n1, n2, P1^-T, P2^-T,
+ *            PER_GROUP, G, -7, 7): u32 [N x K/8], f32 [N x K/G]
+ *   out      [M x N] of out_dtype
+ *   workspace  qa_qlinear_kron_w4a4_workspace(M, K) bytes (any content)
+ * Errors: NULL pointers, M < 0, N < 0, G not in {64, 128, 256}, K % G != 0,
+ * n1 n2 != K, unsupported sizes, misaligned pointers, bad out_dtype, small
+ * workspace.
+ * ------------------------------------------------------------------------- */
+size_t qa_qlinear_kron_w4a4_workspace(int64_t M, int64_t K);
+qa_status qa_qlinear_kron_w4a4(const void* X_f16, int64_t M, int64_t K, int64_t n1, int64_t n2, const float* P1,
+                               const float* P2, const uint32_t* Wp, const float* s_w, int64_t N, int32_t G, void* out,
+                               qa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Parity entry points: the integer accumulators of the two GEMMs, stored.

@@ -13,7 +13,7 @@ import bit_quantized_linear_int8_amd as qa
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "qa.h")
 
-OK, NULL, SHAPE, ALIGN, VALUE, WORKSPACE = 0, 1, 2, 3, 4, 5
+OK, NULL, SHAPE, ALIGN, VALUE, WORKSPACE, UNSUPPORTED = 0, 1, 2, 3, 4, 5, 6
 
 # fake, suitably aligned device addresses: validation never dereferences them
 A = ctypes.c_void_p(0x10000)
@@ -316,3 +316,37 @@ def test_asym_linear_argument_errors():
     assert call(11, 64) == WORKSPACE
     assert call(1, 0) == OK and call(7, 0) == OK
     assert qa.lib().qa_qlinear_int8_asym_workspace(64, 512) >= 64 * 512 + 12 * 64
+
+
+def test_kron_argument_errors():
+    f = qa.lib().qa_kron_quant_int4
+    base = [A, 4, 4096, 64, 64, B, OUT, 0, 0, -7, 7, OUT, WS, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+    assert call(0, None) == NULL
+    assert call(5, None) == NULL
+    assert call(4, 32) == SHAPE                                # n1 n2 != K
+    assert call(1, -1) == SHAPE
+    assert f(A, 4, 96, 8, 12, B, OUT, 0, 0, -7, 7, OUT, WS, None) == UNSUPPORTED
+    assert call(7, 2) == VALUE                                 # per-tensor is not a mode here
+    assert call(9, -9) == VALUE
+    assert f(A, 4, 4096, 64, 64, B, OUT, 1, 100, -7, 7, OUT, WS, None) == SHAPE   # K % G
+    assert call(5, ctypes.c_void_p(0x20004)) == ALIGN
+    assert call(1, 0) == OK
+    g = qa.lib().qa_qlinear_kron_w4a4
+    gb = [A, 16, 4096, 64, 64, B, OUT, B, OUT, 32, 128, OUT, 0, WS, 1 << 30, None]
+
+    def callg(i, v):
+        a = list(gb)
+        a[i] = v
+        return g(*a)
+    assert callg(0, None) == NULL
+    assert callg(10, 96) == SHAPE
+    assert callg(3, 32) == SHAPE
+    assert g(A, 16, 96, 8, 12, B, OUT, B, OUT, 32, 32, OUT, 0, WS, 1 << 30, None) == SHAPE     # G
+    assert callg(12, 5) == VALUE
+    assert callg(14, 64) == WORKSPACE
+    assert callg(1, 0) == OK
