@@ -82,6 +82,9 @@ def lib() -> ctypes.CDLL:
             "orc_hadamard_quant_int4": (None, [P, I64, I64, I32, ctypes.c_int, I32, I32, P, P]),
             "orc_w4a4_group_acc": (I64, [P, P, I64, I64, I64, I32, P, I64, P]),
             "orc_qlinear_w4a4": (None, [P, I64, I64, P, P, I64, I32, P, I64, P]),
+            "orc_hadamard_quant_int8": (None, [P, I64, I64, I32, I32, I32, P, P]),
+            "orc_w4a8_group_acc": (I64, [P, P, I64, I64, I64, I32, P, I64, P]),
+            "orc_qlinear_w4a8": (None, [P, I64, I64, P, P, I64, I32, P, I64, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -455,4 +458,42 @@ def qlinear_w4a4(X16, Wp, s_w, G: int, rows=None):
     r, nr = _rows(rows)
     out = np.zeros((nr if r is not None else M, N), np.float64)
     lib().orc_qlinear_w4a4(_ptr(h), M, K, _ptr(Wp), _ptr(sw), N, int(G), _ptr(r), nr, _ptr(out))
+    return out
+
+
+# ---------------------------------------------------------------- W4A8 path
+def hadamard_quant_int8(X16, G: int, qmin=-127, qmax=127):
+    """-> (codes i8 [rows x K], per-row scales f32 [rows])."""
+    h = _h16(X16)
+    if h.ndim == 1:
+        h = h[None, :]
+    rows, K = h.shape
+    q = np.zeros((rows, K), np.int8)
+    s = np.zeros(rows, np.float32)
+    lib().orc_hadamard_quant_int8(_ptr(h), rows, K, int(G), qmin, qmax, _ptr(q), _ptr(s))
+    return q, s
+
+
+def w4a8_group_acc(Xq, Wp, G: int, rows=None):
+    Xq = _c(Xq, np.int8)
+    Wp = _c(Wp, np.uint32)
+    M, K = Xq.shape
+    N = Wp.shape[0]
+    r, nr = _rows(rows)
+    acc = np.zeros((nr if r is not None else M, N, K // G), np.int32)
+    bad = lib().orc_w4a8_group_acc(_ptr(Xq), _ptr(Wp), M, K, N, int(G), _ptr(r), nr, _ptr(acc))
+    if bad:
+        raise OverflowError("int32 accumulator overflow in %d results" % bad)
+    return acc
+
+
+def qlinear_w4a8(X16, Wp, s_w, G: int, rows=None):
+    h = _h16(X16)
+    M, K = h.shape
+    Wp = _c(Wp, np.uint32)
+    N = Wp.shape[0]
+    sw = _c(s_w, np.float32)
+    r, nr = _rows(rows)
+    out = np.zeros((nr if r is not None else M, N), np.float64)
+    lib().orc_qlinear_w4a8(_ptr(h), M, K, _ptr(Wp), _ptr(sw), N, int(G), _ptr(r), nr, _ptr(out))
     return out

@@ -13,7 +13,9 @@
  *                  "b. INT8 矩阵乘法与反量化" (int32 accumulation, dequant by
  *                  the outer product of the scales), and the merge of the fp16
  *                  outlier product with the int8 part.
- *   [Scholia-IQ]   "模型推理量化" (Inference Quantization notes): §4 Scale
+ *   [Scholia-IQ]   "模型推理量化" (Inference Quantization notes): §2.1-§2.2
+ *                  the WxAy notation (W4A8: 4-bit weights, 8-bit
+ *                  activations), §4 Scale
  *                  (s = max|x|/qmax, q = round(x/s), x^ = s*q, all-zero input
  *                  needs a safe scale), §5 Outlier, §6 Zero-point and §6.2
  *                  affine clip q = clip(round(x/s)+z, qmin, qmax), §7.3
@@ -28,7 +30,8 @@
  *                  X' = X~ x1 P1^T x2 P2, dynamic int4 codes of X', int4
  *                  GEMM with the offline-transformed weight; Kronecker sizes
  *                  argmin (n1 + n2) with n1 n2 = n, n1 <= n2), and
- *                  "从离群值到平坦线" §2 (4096 = 64 x 64).
+ *                  "从离群值到平坦线" §2 (4096 = 64 x 64), §4 (a transform
+ *                  fitted for W4A4 serves W4A8 unchanged).
  *   [QE2]          "Quantization explained, part 2" (tanjunchen.github.io):
  *                  §1.2, threshold 6.0 on a channel's activation magnitude and
  *                  the 4096-wide row with one value of 70; §4.2 SmoothQuant,
@@ -819,6 +822,85 @@ void orc_qlinear_w4a4(const uint16_t* X, int64_t M, int64_t K, const uint32_t* W
         }
         free(xq);
         free(xp);
+    }
+    free(wq);
+}
+
+/* ---------------------------------------------------------------------------
+ * W4A8: 4-bit weights, 8-bit activations  [Scholia-IQ §2.1-§2.2; FlatQuant
+ * §4 (the W4A4 transform reused for W4A8); GroupRot §5.2 (online rotation
+ * fused with dynamic per-token quantization), §5.4 (int32 accumulation)]
+ *   X' = X * blockdiag(H_G) (as for W4A4); s_x = fl32(absmax(row of X')/127);
+ *   int8 codes in [-127, 127]; the weight is the offline W4A4 weight (per-group
+ *   int4 of W * blockdiag(H_G));
+ *   out[m][n] = s_x[m] * sum_g s_w[n][g] * acc_g   (fp64), acc_g the exact
+ *   integer sum of the group's products.
+ * ------------------------------------------------------------------------- */
+void orc_hadamard_quant_int8(const uint16_t* X, int64_t rows, int64_t K, int32_t G,
+                             int32_t qmin, int32_t qmax, int8_t* q, float* s)
+{
+    size_t n = (size_t)(rows * K > 0 ? rows * K : 1);
+    float* xr = (float*)malloc(sizeof(float) * n);
+    orc_hadamard_rows(X, rows, K, G, xr);
+    orc_quant_rows_f32(xr, rows, K, K, NULL, qmin, qmax, NULL, NULL, q, s);
+    free(xr);
+}
+
+/* acc[ri][n][g] = sum_{k in group g} Xq[m][k] * qw[n][k], m = rows[ri].
+ * Returns the count of results outside int32. */
+int64_t orc_w4a8_group_acc(const int8_t* Xq, const uint32_t* Wp, int64_t M, int64_t K,
+                           int64_t N, int32_t G, const int64_t* rows, int64_t nrows,
+                           int32_t* acc)
+{
+    if (!rows)
+        nrows = M;
+    int64_t ng = K / G, bad = 0;
+    int8_t* wq = (int8_t*)malloc((size_t)(N * K > 0 ? N * K : 1));
+    orc_unpack_int4(Wp, N, K, wq);
+#pragma omp parallel for schedule(dynamic, 1) reduction(+ : bad)
+    for (int64_t ri = 0; ri < nrows; ++ri) {
+        int64_t m = rows ? rows[ri] : ri;
+        const int8_t* xq = Xq + m * K;
+        for (int64_t n = 0; n < N; ++n)
+            for (int64_t g = 0; g < ng; ++g) {
+                int64_t a = 0;
+                for (int64_t k = g * G; k < (g + 1) * G; ++k)
+                    a += (int64_t)xq[k] * (int64_t)wq[n * K + k];
+                if (a > INT32_MAX || a < INT32_MIN)
+                    ++bad;
+                acc[(ri * N + n) * ng + g] = (int32_t)a;
+            }
+    }
+    free(wq);
+    return bad;
+}
+
+void orc_qlinear_w4a8(const uint16_t* X, int64_t M, int64_t K, const uint32_t* Wp,
+                      const float* s_w, int64_t N, int32_t G, const int64_t* rows,
+                      int64_t nrows, double* out)
+{
+    if (!rows)
+        nrows = M;
+    int64_t ng = K / G;
+    int8_t* wq = (int8_t*)malloc((size_t)(N * K > 0 ? N * K : 1));
+    orc_unpack_int4(Wp, N, K, wq);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t ri = 0; ri < nrows; ++ri) {
+        int64_t m = rows ? rows[ri] : ri;
+        int8_t* xq = (int8_t*)malloc((size_t)(K > 0 ? K : 1));
+        float s_x = 0.0f;
+        orc_hadamard_quant_int8(X + m * K, 1, K, G, -127, 127, xq, &s_x);
+        for (int64_t n = 0; n < N; ++n) {
+            double sum = 0.0;
+            for (int64_t g = 0; g < ng; ++g) {
+                int64_t a = 0;
+                for (int64_t k = g * G; k < (g + 1) * G; ++k)
+                    a += (int64_t)xq[k] * (int64_t)wq[n * K + k];
+                sum += (double)s_w[n * ng + g] * (double)a;
+            }
+            out[ri * N + n] = (double)s_x * sum;
+        }
+        free(xq);
     }
     free(wq);
 }

@@ -400,6 +400,99 @@ def test_rotation_lowers_w4a4_error():
     assert err_rot < np.abs(plain - exact).mean() / 2
 
 
+# ------------------------------------------------------------------ W4A8
+@pytest.mark.parametrize("G", [64, 256])
+def test_hadamard_quant_int8_unit_vectors(G):
+    # x = v e_i in one block: the rotated block is v/sqrt(G) times row i of H_G
+    # (exact for G = 64, 256), every other block is 0, so the codes are
+    # +-127 in H_G's sign pattern and s = fl32(|v|/sqrt(G) / 127)
+    K = 2 * G
+    for i, v, b in [(0, 8.0, 0), (5, -24.0, 1), (G - 1, 0.5, 0), (G // 2 + 3, 1000.0, 1)]:
+        x = np.zeros(K, np.float16)
+        x[b * G + i] = v
+        q, s = oracle.hadamard_quant_int8(x, G)
+        a = np.float32(abs(v) / math.sqrt(G))
+        assert s[0] == a / np.float32(127)
+        H = scipy.linalg.hadamard(G)
+        want = np.zeros(K, np.int64)
+        want[b * G:(b + 1) * G] = 127 * np.sign(v) * H[i]
+        assert np.array_equal(q[0], want)
+
+
+@pytest.mark.parametrize("G", [8, 64, 128])
+def test_hadamard_quant_int8_matches_library_composition(G):
+    X, _, _ = synthetic.mixed_inputs(5, 256, 1, seed=16, n_dims=3, magnitude=("abs_normal", 50.0))
+    X[2] = 0
+    H = scipy.linalg.hadamard(G).astype(np.float64)
+    xr = ((X.astype(np.float64).reshape(5, -1, G) @ H) * (1.0 / math.sqrt(G))).astype(np.float32).reshape(5, 256)
+    q, s = oracle.hadamard_quant_int8(X, G)
+    a = np.abs(xr).max(axis=1)
+    s_ref = np.where(a == 0, np.float32(1), a / np.float32(127)).astype(np.float32)
+    assert np.array_equal(s, s_ref) and s[2] == 1.0
+    assert np.array_equal(q, np.clip(np.rint(xr / s_ref[:, None]), -127, 127))
+    # rounding to nearest: each code is within half a step of the rotated value
+    err = np.abs(q * s.astype(np.float64)[:, None] - xr.astype(np.float64))
+    assert np.all(err <= 0.5 * s.astype(np.float64)[:, None] * (1 + 1e-6))
+    assert np.all(np.abs(q[[0, 1, 3, 4]]).max(axis=1) == 127)
+
+
+@settings(max_examples=15, deadline=None)
+@given(M=st.integers(1, 12), N=st.integers(1, 20), groups=st.integers(1, 4), G=st.sampled_from([8, 64, 256]),
+       seed=st.integers(0, 2 ** 31))
+def test_w4a8_group_acc_bruteforce(M, N, groups, G, seed):
+    K = G * groups
+    rng = np.random.default_rng(seed)
+    Xq = rng.integers(-128, 128, (M, K)).astype(np.int8)
+    Wp = rng.integers(0, 2 ** 32, (N, K // 8), dtype=np.uint64).astype(np.uint32)
+    acc = oracle.w4a8_group_acc(Xq, Wp, G)
+    w = _unpack_np(Wp, K).reshape(N, groups, G)
+    assert np.array_equal(acc, np.einsum("mgk,ngk->mng", Xq.astype(np.int64).reshape(M, groups, G), w))
+    rows = np.array([M - 1, 0])
+    assert np.array_equal(oracle.w4a8_group_acc(Xq, Wp, G, rows=rows), acc[rows])
+
+
+def test_w4a8_output_matches_dequant_matmul_and_error_bound():
+    M, K, N, G = 12, 512, 20, 128
+    X, W, _ = synthetic.w4a4_inputs(M, K, N, seed=17)
+    Wp, s_w = oracle.hadamard_quant_int4(W, G, per_group=True)
+    out = oracle.qlinear_w4a8(X, Wp, s_w, G)
+    q, s_x = oracle.hadamard_quant_int8(X, G)
+    xd = q * s_x.astype(np.float64)[:, None]
+    wd = _unpack_np(Wp, K) * np.repeat(s_w.astype(np.float64), G, axis=1)
+    mag = np.abs(xd) @ np.abs(wd).T
+    assert np.all(np.abs(out - xd @ wd.T) <= 1e-12 * mag)
+    # error bound against the unquantized product (rotation is orthogonal)
+    H = scipy.linalg.hadamard(G).astype(np.float64) / math.sqrt(G)
+    xr = (X.astype(np.float64).reshape(M, -1, G) @ H).reshape(M, K)
+    wr = (W.astype(np.float64).reshape(N, -1, G) @ H).reshape(N, K)
+    sx = np.abs(xr.astype(np.float32)).max(axis=1).astype(np.float64) / 127 * (1 + 1e-6)
+    sw = np.repeat(np.abs(wr.astype(np.float32)).reshape(N, -1, G).max(axis=2) / 7, G, axis=1) * (1 + 1e-6)
+    B = 0.5 * sx[:, None] * ((np.abs(wr) + 0.5 * sw).sum(axis=1))[None, :] + 0.5 * np.abs(xr) @ sw.T
+    exact = X.astype(np.float64) @ W.astype(np.float64).T
+    slack = 2.0 ** -20 * (np.abs(xr) @ np.abs(wr).T)
+    assert np.all(np.abs(out - exact) <= B + slack)
+    rows = np.array([11, 0, 5])
+    assert np.array_equal(oracle.qlinear_w4a8(X, Wp, s_w, G, rows=rows), out[rows])
+
+
+def test_w4a8_error_below_w4a4():
+    # the point of 8-bit activations: with the same rotated int4 weight, the
+    # output error falls to the weight-only level (rotated activations kept
+    # unquantized), clearly below W4A4's
+    M, K, N, G = 16, 1024, 24, 128
+    X, W, _ = synthetic.w4a4_inputs(M, K, N, seed=18)
+    exact = X.astype(np.float64) @ W.astype(np.float64).T
+    Wp, s_w = oracle.hadamard_quant_int4(W, G, per_group=True)
+    e8 = np.abs(oracle.qlinear_w4a8(X, Wp, s_w, G) - exact).mean()
+    e4 = np.abs(oracle.qlinear_w4a4(X, Wp, s_w, G) - exact).mean()
+    H = scipy.linalg.hadamard(G).astype(np.float64) / math.sqrt(G)
+    xr = (X.astype(np.float64).reshape(M, -1, G) @ H).reshape(M, K)
+    wd = _unpack_np(Wp, K) * np.repeat(s_w.astype(np.float64), G, axis=1)
+    e_w = np.abs(xr @ wd.T - exact).mean()
+    assert e8 < 0.75 * e4
+    assert abs(e8 - e_w) < 0.05 * e_w
+
+
 # ------------------------------------------------------------------ SmoothQuant
 def _f32_ulp(x):
     x = np.abs(np.asarray(x, np.float32))
