@@ -32,7 +32,8 @@ EXPORTS = (
     "qa_qlinear_int8_smooth_workspace", "qa_qlinear_int8_smooth",
     "qa_hadamard_quant_int4", "qa_kron_quant_int4", "qa_qlinear_kron_w4a4_workspace", "qa_qlinear_kron_w4a4",
     "qa_qlinear_w4a4_workspace", "qa_qlinear_w4a4",
-    "qa_gemm_i8_i32", "qa_gemm_w4a4_group_acc",
+    "qa_hadamard_quant_int8", "qa_qlinear_w4a8_workspace", "qa_qlinear_w4a8",
+    "qa_gemm_i8_i32", "qa_gemm_w4a4_group_acc", "qa_gemm_w4a8_group_acc",
 )
 
 _DTYPE_CODE = {torch.float32: QA_F32, torch.float16: QA_F16, torch.bfloat16: QA_BF16}
@@ -86,6 +87,10 @@ def lib() -> ctypes.CDLL:
             "qa_qlinear_w4a4": (S, [P, I64, I64, P, P, I64, I32, P, S, P, SZ, P]),
             "qa_gemm_i8_i32": (S, [P, P, I64, I64, I64, P, P]),
             "qa_gemm_w4a4_group_acc": (S, [P, P, I64, I64, I64, I32, P, P]),
+            "qa_hadamard_quant_int8": (S, [P, I64, I64, I32, I32, I32, P, P, P]),
+            "qa_qlinear_w4a8_workspace": (SZ, [I64, I64]),
+            "qa_qlinear_w4a8": (S, [P, I64, I64, P, P, I64, I32, P, S, P, SZ, P]),
+            "qa_gemm_w4a8_group_acc": (S, [P, P, I64, I64, I64, I32, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -424,6 +429,38 @@ def qa_qlinear_w4a4(X, Wp, s_w, G=128, out_dtype=torch.float32, out=None, worksp
     return out
 
 
+def qa_hadamard_quant_int8(X, G: int, q_min=-127, q_max=127, stream=None):
+    """Hadamard rotation + per-row int8 codes -> (q i8 [rows x K], s f32 [rows])."""
+    _dev(X, "X", torch.float16)
+    rows, K = X.shape
+    q = torch.empty((rows, K), dtype=torch.int8, device=X.device)
+    s = torch.empty(rows, dtype=torch.float32, device=X.device)
+    _check("qa_hadamard_quant_int8",
+           lib().qa_hadamard_quant_int8(_p(X), rows, K, int(G), int(q_min), int(q_max), _p(q), _p(s),
+                                        _stream(stream)))
+    return q, s
+
+
+def qa_qlinear_w4a8_workspace(M: int, K: int) -> int:
+    return int(lib().qa_qlinear_w4a8_workspace(M, K))
+
+
+def qa_qlinear_w4a8(X, Wp, s_w, G=128, out_dtype=torch.float32, out=None, workspace=None, stream=None):
+    """W4A8 group-Hadamard linear (int8 activations, offline int4 weight) -> out [M x N]."""
+    _dev(X, "X", torch.float16)
+    _dev(Wp, "Wp", torch.int32)
+    _dev(s_w, "s_w", torch.float32)
+    M, K = X.shape
+    N = Wp.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=X.device)
+    workspace = _workspace(qa_qlinear_w4a8_workspace(M, K), X.device, workspace)
+    _check("qa_qlinear_w4a8",
+           lib().qa_qlinear_w4a8(_p(X), M, K, _p(Wp), _p(s_w), N, int(G), _p(out), _DTYPE_CODE[out.dtype],
+                                 _p(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
 def qa_gemm_i8_i32(A, B, stream=None):
     _dev(A, "A", torch.int8)
     _dev(B, "B", torch.int8)
@@ -441,4 +478,15 @@ def qa_gemm_w4a4_group_acc(Xp, Wp, K: int, G: int, stream=None):
     acc = torch.empty((M, N, K // G), dtype=torch.int32, device=Xp.device)
     _check("qa_gemm_w4a4_group_acc",
            lib().qa_gemm_w4a4_group_acc(_p(Xp), _p(Wp), M, K, N, int(G), _p(acc), _stream(stream)))
+    return acc
+
+
+def qa_gemm_w4a8_group_acc(Xq, Wp, G: int, stream=None):
+    _dev(Xq, "Xq", torch.int8)
+    _dev(Wp, "Wp", torch.int32)
+    M, K = Xq.shape
+    N = Wp.shape[0]
+    acc = torch.empty((M, N, K // G), dtype=torch.int32, device=Xq.device)
+    _check("qa_gemm_w4a8_group_acc",
+           lib().qa_gemm_w4a8_group_acc(_p(Xq), _p(Wp), M, K, N, int(G), _p(acc), _stream(stream)))
     return acc

@@ -904,7 +904,11 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_w4a4(const uint32_t* __rest
 // ---------------------------------------------------------------------------
 // W4A4 on the LDS-DMA pipeline: eight waves, wave tile 64 x 64, K advances 64
 // packed bytes (128 elements, two MFMA steps) per stage through four LDS
-// stages.  A lane's fragment of one step is 8 packed bytes (row l % 16, bytes
+// stages.  A8 (W4A8): the activation operand is int8 codes instead, 128 bytes
+// per row and stage (eight 16-byte chunks, XOR-swizzled by row % 8), and each
+// fragment's bytes are permuted (v_perm_b32) into the even/odd element order
+// the weight's nibble unpack produces, so both operands share one k order;
+// the products then carry 16 (weight in the high nibble) instead of 256.  A lane's fragment of one step is 8 packed bytes (row l % 16, bytes
 // 32 s + 8 (l / 16) of the stage), unpacked into the high nibbles.  The block's
 // per-group weight scales (x 2^-8) are staged in LDS as [group][column] when
 // they fit.  Operands enter the MFMA in the transposed order of the int8 path
@@ -912,20 +916,38 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_w4a4(const uint32_t* __rest
 // ---------------------------------------------------------------------------
 constexpr int W4D_SW_LDS = 8192;                 // floats of per-group weight scales kept in LDS
 
-template <class C, int G, bool STORE_ACC>
+// The even/odd order of unpack_hi_nibbles for 16 int8 codes read in order.
+__device__ __forceinline__ v4i perm_even_odd(const u32x4& a) {
+    return v4i{(int)__builtin_amdgcn_perm(a[1], a[0], 0x06040200u), (int)__builtin_amdgcn_perm(a[1], a[0], 0x07050301u),
+               (int)__builtin_amdgcn_perm(a[3], a[2], 0x06040200u), (int)__builtin_amdgcn_perm(a[3], a[2], 0x07050301u)};
+}
+
+template <class C, bool A8>
+struct W4Stage {
+    static constexpr int A_ROW = A8 ? 128 : 64;                 // activation bytes per row and stage
+    static constexpr int LDS_A = C::BM * A_ROW;
+    static constexpr int A_INS = A8 ? 2 * C::A_INS : C::A_INS;  // 1 KB DMA instructions per wave
+    static constexpr int STAGE = LDS_A + C::LDS_B;
+    static constexpr int LDS = C::STAGES * STAGE;
+};
+
+template <class C, int G, bool STORE_ACC, bool A8 = false>
 __device__ __forceinline__ void w4a4_dma_body(const uint32_t* __restrict__ Xp, const float* __restrict__ s_x,
                                               const uint32_t* __restrict__ Wp, const float* __restrict__ s_w,
                                               int64_t M, int64_t K, int64_t N, void* __restrict__ out,
                                               int out_dtype, int tiles_m, int tiles_n, uint8_t* smem, float* sws) {
     constexpr int SPG = G / 64;                       // MFMA steps per group
+    using S = W4Stage<C, A8>;
+    constexpr float SCALE = A8 ? 0x1p-4f : 0x1p-8f;   // the nibble shift(s) in each product
     int tm, tn;
     tile_of_block(blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int wm = wave / C::WN, wn = wave % C::WN;
-    const uint32_t kbytes = (uint32_t)(K / 2);        // packed bytes per row
+    const uint32_t kbytes = (uint32_t)(K / 2);        // packed weight bytes per row
+    const uint32_t abytes = A8 ? (uint32_t)K : kbytes;   // activation bytes per row
     const int64_t ng = K / G;
-    const rsrc_t rsa = make_rsrc(reinterpret_cast<const uint8_t*>(Xp) + m0 * kbytes, (M - m0) * kbytes);
+    const rsrc_t rsa = make_rsrc(reinterpret_cast<const uint8_t*>(Xp) + m0 * abytes, (M - m0) * abytes);
     const rsrc_t rsb = make_rsrc(reinterpret_cast<const uint8_t*>(Wp) + n0 * kbytes, (N - n0) * kbytes);
 
     const bool sw_in_lds = !STORE_ACC && ng * C::BN <= W4D_SW_LDS;
@@ -933,17 +955,24 @@ __device__ __forceinline__ void w4a4_dma_body(const uint32_t* __restrict__ Xp, c
     if (sw_in_lds) {
         for (int t = threadIdx.x; t < ng * C::BN; t += C::THREADS) {
             const int cc = t / (int)ng, g = t - cc * (int)ng;           // coalesced over g
-            sws[g * C::BN + cc] = __builtin_bit_cast(float, bload4(rsw, (uint32_t)t * 4)) * 0x1p-8f;
+            sws[g * C::BN + cc] = __builtin_bit_cast(float, bload4(rsw, (uint32_t)t * 4)) * SCALE;
         }
     }
     __syncthreads();
 
-    uint32_t oa[C::A_INS], ca[C::A_INS], ob[C::B_INS], cb[C::B_INS];
+    uint32_t oa[S::A_INS], ca[S::A_INS], ob[C::B_INS], cb[C::B_INS];
 #pragma unroll
-    for (int q = 0; q < C::A_INS; ++q) {
-        const int P = (wave * C::A_INS + q) * 64 + lane;
-        const int r = P >> 2, c = (P & 3) ^ ((r >> 1) & 3);
-        oa[q] = (uint32_t)r * kbytes + c * 16;
+    for (int q = 0; q < S::A_INS; ++q) {
+        const int P = (wave * S::A_INS + q) * 64 + lane;
+        int r, c;
+        if constexpr (A8) {
+            r = P >> 3;
+            c = (P & 7) ^ (r & 7);
+        } else {
+            r = P >> 2;
+            c = (P & 3) ^ ((r >> 1) & 3);
+        }
+        oa[q] = (uint32_t)r * abytes + c * 16;
         ca[q] = c * 16;
     }
 #pragma unroll
@@ -953,19 +982,20 @@ __device__ __forceinline__ void w4a4_dma_body(const uint32_t* __restrict__ Xp, c
         ob[q] = (uint32_t)r * kbytes + c * 16;
         cb[q] = c * 16;
     }
-    constexpr int PER_STAGE = C::A_INS + C::B_INS;
+    constexpr int PER_STAGE = S::A_INS + C::B_INS;
     const int nk = (int)((kbytes + C::BK - 1) / C::BK);
     const int nsteps = (int)(K / 64);
     auto issue = [&](int kt) __attribute__((always_inline)) {
-        uint8_t* st = smem + (kt % C::STAGES) * C::STAGE;
+        uint8_t* st = smem + (kt % C::STAGES) * S::STAGE;
         const uint32_t k0 = (uint32_t)kt * C::BK;
+        const uint32_t a0 = (uint32_t)kt * S::A_ROW;
 #pragma unroll
-        for (int q = 0; q < C::A_INS; ++q)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)(st + (wave * C::A_INS + q) * 1024), 16,
-                                                     k0 + ca[q] < kbytes ? oa[q] + k0 : kOOB, 0, 0, 0);
+        for (int q = 0; q < S::A_INS; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)(st + (wave * S::A_INS + q) * 1024), 16,
+                                                     a0 + ca[q] < abytes ? oa[q] + a0 : kOOB, 0, 0, 0);
 #pragma unroll
         for (int q = 0; q < C::B_INS; ++q)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void*)(st + C::LDS_A + (wave * C::B_INS + q) * 1024),
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void*)(st + S::LDS_A + (wave * C::B_INS + q) * 1024),
                                                      16, k0 + cb[q] < kbytes ? ob[q] + k0 : kOOB, 0, 0, 0);
     };
 
@@ -991,8 +1021,8 @@ __device__ __forceinline__ void w4a4_dma_body(const uint32_t* __restrict__ Xp, c
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         block_barrier();
         if (kt + 3 < nk) issue(kt + 3);
-        const uint8_t* sa = smem + (kt % C::STAGES) * C::STAGE;
-        const uint8_t* sb = sa + C::LDS_A;
+        const uint8_t* sa = smem + (kt % C::STAGES) * S::STAGE;
+        const uint8_t* sb = sa + S::LDS_A;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
             const int step = 2 * kt + s2;
@@ -1001,9 +1031,15 @@ __device__ __forceinline__ void w4a4_dma_body(const uint32_t* __restrict__ Xp, c
             const int c = byte >> 4, within = byte & 15;
             v4i fa[C::FM], fb[C::FN];
 #pragma unroll
-            for (int i = 0; i < C::FM; ++i)
-                fa[i] = unpack_hi_nibbles(
-                    *reinterpret_cast<const u32x2*>(sa + swz64(wm * C::TM + i * 16 + (lane & 15), c) + within));
+            for (int i = 0; i < C::FM; ++i) {
+                const int r = wm * C::TM + i * 16 + (lane & 15);
+                if constexpr (A8) {
+                    const int c8 = 4 * s2 + (lane >> 4);                  // elements 16 c8 .. 16 c8 + 15
+                    fa[i] = perm_even_odd(*reinterpret_cast<const u32x4*>(sa + r * 128 + ((c8 ^ (r & 7)) * 16)));
+                } else {
+                    fa[i] = unpack_hi_nibbles(*reinterpret_cast<const u32x2*>(sa + swz64(r, c) + within));
+                }
+            }
 #pragma unroll
             for (int j = 0; j < C::FN; ++j)
                 fb[j] = unpack_hi_nibbles(
@@ -1030,7 +1066,8 @@ __device__ __forceinline__ void w4a4_dma_body(const uint32_t* __restrict__ Xp, c
                             const int64_t col = n0 + wn * C::TN + j * 16 + 4 * (lane >> 4);
 #pragma unroll
                             for (int e = 0; e < 4; ++e)
-                                if (row < M && col + e < N) accp[(row * N + col + e) * ng + g] = acc[i][j][e] >> 8;
+                                if (row < M && col + e < N)
+                                    accp[(row * N + col + e) * ng + g] = acc[i][j][e] >> (A8 ? 4 : 8);
                             if constexpr (SPG > 2) acc[i][j] = v4i{0, 0, 0, 0};
                         }
                     }
@@ -1045,7 +1082,7 @@ __device__ __forceinline__ void w4a4_dma_body(const uint32_t* __restrict__ Xp, c
 #pragma unroll
                             for (int e = 0; e < 4; ++e)
                                 swj[j][e] = __builtin_bit_cast(float, bload4(rsw, (uint32_t)((cl + e) * ng + g) * 4)) *
-                                            0x1p-8f;
+                                            SCALE;
                         }
                     }
 #pragma unroll
@@ -1093,6 +1130,20 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_w4a4_dma(const uint32_t* __
     w4a4_dma_body<C, G, STORE_ACC>(Xp, s_x, Wp, s_w, M, K, N, out, out_dtype, tiles_m, tiles_n, smem, sws);
 }
 
+// W4A8: int8 activation codes Xq [M x K] against the packed int4 weight.
+template <class C, int G, bool STORE_ACC>
+__global__ __launch_bounds__(C::THREADS) void k_gemm_w4a8_dma(const int8_t* __restrict__ Xq,
+                                                              const float* __restrict__ s_x,
+                                                              const uint32_t* __restrict__ Wp,
+                                                              const float* __restrict__ s_w, int64_t M, int64_t K,
+                                                              int64_t N, void* __restrict__ out, int out_dtype,
+                                                              int tiles_m, int tiles_n) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[W4Stage<C, true>::LDS];
+    __shared__ __attribute__((aligned(16))) float sws[STORE_ACC ? 4 : W4D_SW_LDS];
+    w4a4_dma_body<C, G, STORE_ACC, true>(reinterpret_cast<const uint32_t*>(Xq), s_x, Wp, s_w, M, K, N, out,
+                                         out_dtype, tiles_m, tiles_n, smem, sws);
+}
+
 using CfgW4 = CfgD<128, 256, 2, 4>;     // 8 waves, wave tile 64 x 64, LDS-DMA stages
 
 template <int G, bool STORE_ACC>
@@ -1120,6 +1171,37 @@ hipError_t launch_gemm_w4a4(const uint32_t* Xp, const float* s_x, const uint32_t
         case 64: w4a4_dispatch<64, false>(Xp, s_x, Wp, s_w, M, K, N, out, out_dtype, st); break;
         case 128: w4a4_dispatch<128, false>(Xp, s_x, Wp, s_w, M, K, N, out, out_dtype, st); break;
         case 256: w4a4_dispatch<256, false>(Xp, s_x, Wp, s_w, M, K, N, out, out_dtype, st); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int G, bool STORE_ACC>
+static void w4a8_dispatch(const int8_t* Xq, const float* s_x, const uint32_t* Wp, const float* s_w, int64_t M,
+                          int64_t K, int64_t N, void* out, int out_dtype, hipStream_t st) {
+    int tm, tn;
+    dim3 g = grid_of<CfgW4>(M, N, tm, tn);
+    hipLaunchKernelGGL((k_gemm_w4a8_dma<CfgW4, G, STORE_ACC>), g, dim3(CfgW4::THREADS), 0, st, Xq, s_x, Wp, s_w, M,
+                       K, N, out, out_dtype, tm, tn);
+}
+
+hipError_t launch_gemm_w4a8(const int8_t* Xq, const float* s_x, const uint32_t* Wp, const float* s_w, int64_t M,
+                            int64_t K, int64_t N, int G, void* out, int out_dtype, hipStream_t st) {
+    switch (G) {
+        case 64: w4a8_dispatch<64, false>(Xq, s_x, Wp, s_w, M, K, N, out, out_dtype, st); break;
+        case 128: w4a8_dispatch<128, false>(Xq, s_x, Wp, s_w, M, K, N, out, out_dtype, st); break;
+        case 256: w4a8_dispatch<256, false>(Xq, s_x, Wp, s_w, M, K, N, out, out_dtype, st); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_w4a8_group_acc(const int8_t* Xq, const uint32_t* Wp, int64_t M, int64_t K, int64_t N, int G,
+                                      int32_t* acc, hipStream_t st) {
+    switch (G) {
+        case 64: w4a8_dispatch<64, true>(Xq, nullptr, Wp, nullptr, M, K, N, acc, 0, st); break;
+        case 128: w4a8_dispatch<128, true>(Xq, nullptr, Wp, nullptr, M, K, N, acc, 0, st); break;
+        case 256: w4a8_dispatch<256, true>(Xq, nullptr, Wp, nullptr, M, K, N, acc, 0, st); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -877,19 +877,28 @@ __device__ __forceinline__ void fwht_chunk(const u32x4& v, double c, int lane, f
     for (int j = 0; j < 8; ++j) xo[j] = (float)(y[j] * c);
 }
 
-// int4 codes of 8 values (|x / s| <= 7 (1 + 2^-23)) packed into one word,
-// element j in bits [4j+3:4j]; clipped to [qmin, qmax].
+// The codes of chunk ch (8 values, |x / s| <= q_max (1 + 2^-23)), clipped
+// below at qmin: I8, eight int8 codes at out + 8 ch; otherwise eight int4
+// codes packed into the word out[ch], element j in bits [4j+3:4j].
+template <bool I8>
+__device__ __forceinline__ void store_codes(void* out, int64_t ch, const float* x, float s, float r, int qmin) {
+    if constexpr (I8)
+        reinterpret_cast<u32x2*>(out)[ch] = clip_codes(codes8_dyn(x, s, r), qmin);
+    else
+        reinterpret_cast<uint32_t*>(out)[ch] = pack_codes(x, s, r, qmin);
+}
+
 // Per-row scale, row held in registers (NC > 0) or recomputed (NC == 0).
-template <int G, int NC>
+template <int G, int NC, bool I8>
 __global__ __launch_bounds__(256) void k_hq4_row(const uint16_t* __restrict__ X, int64_t rows, int64_t K,
-                                                 int qmin, int qmax, double c, uint32_t* __restrict__ packed,
+                                                 int qmin, int qmax, double c, void* __restrict__ codes,
                                                  float* __restrict__ s_out) {
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + wave_id();
     if (row >= rows) return;
     const int64_t nch = K >> 3;
     const rsrc_t rx = make_rsrc(X + row * K, K * 2);
-    uint32_t* pr = packed + row * nch;
+    void* pr = reinterpret_cast<uint8_t*>(codes) + row * nch * (I8 ? 8 : 4);
     if constexpr (NC > 0) {
         u32x4 v[NC];
 #pragma unroll
@@ -908,7 +917,7 @@ __global__ __launch_bounds__(256) void k_hq4_row(const uint16_t* __restrict__ X,
 #pragma unroll
         for (int i = 0; i < NC; ++i) {
             const int64_t ch = lane + 64 * i;
-            if (ch < nch) pr[ch] = pack_codes(xs[i], s, r, qmin);
+            if (ch < nch) store_codes<I8>(pr, ch, xs[i], s, r, qmin);
         }
     } else {
         float amax = 0.0f;
@@ -926,7 +935,7 @@ __global__ __launch_bounds__(256) void k_hq4_row(const uint16_t* __restrict__ X,
             const int64_t ch = base + lane;
             float xo[8];
             fwht_chunk<G>(bload16(rx, (uint32_t)ch * 16), c, lane, xo);
-            if (ch < nch) pr[ch] = pack_codes(xo, s, r, qmin);
+            if (ch < nch) store_codes<I8>(pr, ch, xo, s, r, qmin);
         }
     }
 }
@@ -942,9 +951,9 @@ __global__ __launch_bounds__(256) void k_hq4_row(const uint16_t* __restrict__ X,
 // in-block bits except the lowest log2(LPB) chunk bits, which sit in the lane
 // index and take one DPP quad exchange per bit.  The stages commute and every
 // partial sum is exact in fp64, so their order does not matter.
-template <int G, int NC, int WPR>
+template <int G, int NC, int WPR, bool I8>
 __global__ __launch_bounds__(256) void k_hq4_row_reg(const uint16_t* __restrict__ X, int64_t rows, int64_t K,
-                                                     int qmin, int qmax, double c, uint32_t* __restrict__ packed,
+                                                     int qmin, int qmax, double c, void* __restrict__ codes,
                                                      float* __restrict__ s_out) {
     constexpr int CPB = G / 8;
     constexpr int LPB = CPB > NC ? CPB / NC : 1;
@@ -956,7 +965,7 @@ __global__ __launch_bounds__(256) void k_hq4_row_reg(const uint16_t* __restrict_
     const int part = wave % WPR;                      // which K / WPR slice of the row
     const bool live = row < rows;                     // every wave reaches the barrier below
     const rsrc_t rx = make_rsrc(X + row * K, live ? K * 2 : 0);
-    uint32_t* pr = packed + row * (K >> 3) + part * 64 * NC;
+    const int64_t ch0 = row * (K >> 3) + part * 64 * NC;
     auto chunk = [&](int i) -> int {
         return LPB == 1 ? lane * NC + i : (lane / LPB) * CPB + (lane % LPB) + LPB * i;
     };
@@ -1028,7 +1037,7 @@ __global__ __launch_bounds__(256) void k_hq4_row_reg(const uint16_t* __restrict_
     const float r = 1.0f / s;
     if (lane == 0 && part == 0) s_out[row] = s;
 #pragma unroll
-    for (int i = 0; i < NC; ++i) pr[chunk(i)] = pack_codes(xs[i], s, r, qmin);
+    for (int i = 0; i < NC; ++i) store_codes<I8>(codes, ch0 + chunk(i), xs[i], s, r, qmin);
 }
 
 // Per-group scale (G >= 8): the G/8 lanes of a block reduce their absmax.
@@ -1063,39 +1072,42 @@ constexpr bool hq4_row_reg_ok() {
     return G >= 8 && (G / 8 > NC ? (G / 8) / NC <= 4 && (G / 8) % NC == 0 : NC % (G / 8) == 0);
 }
 
-template <int G, int NC, int WPR>
+template <int G, int NC, int WPR, bool I8>
 static bool hq4_row_reg_try(const uint16_t* X, int64_t rows, int64_t K, int qmin, int qmax, double c,
-                            uint32_t* packed, float* s, hipStream_t st) {
+                            void* codes, float* s, hipStream_t st) {
     if constexpr (hq4_row_reg_ok<G, NC>()) {
         if (K != 512 * NC * WPR) return false;
         const dim3 grid((unsigned)((rows + 4 / WPR - 1) / (4 / WPR))), block(256);
-        hipLaunchKernelGGL((k_hq4_row_reg<G, NC, WPR>), grid, block, 0, st, X, rows, K, qmin, qmax, c, packed, s);
+        hipLaunchKernelGGL((k_hq4_row_reg<G, NC, WPR, I8>), grid, block, 0, st, X, rows, K, qmin, qmax, c, codes,
+                           s);
         return true;
     } else {
         return false;
     }
 }
 
-template <int G>
+template <int G, bool I8 = false>
 static void hq4_dispatch(const uint16_t* X, int64_t rows, int64_t K, bool per_group, int qmin, int qmax,
-                         uint32_t* packed, float* s, hipStream_t st) {
+                         void* codes, float* s, hipStream_t st) {
     const double c = 1.0 / __builtin_sqrt((double)G);
     const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
     if (per_group) {
-        if constexpr (G >= 8)
-            hipLaunchKernelGGL((k_hq4_group<G>), grid, block, 0, st, X, rows, K, qmin, qmax, c, packed, s);
+        if constexpr (G >= 8 && !I8)
+            hipLaunchKernelGGL((k_hq4_group<G>), grid, block, 0, st, X, rows, K, qmin, qmax, c,
+                               static_cast<uint32_t*>(codes), s);
         return;
     }
     const int64_t nch = K / 8;
     // two waves per row where the lane mapping allows it (more waves to hide latency)
-    if (hq4_row_reg_try<G, 2, 1>(X, rows, K, qmin, qmax, c, packed, s, st) ||
-        hq4_row_reg_try<G, 2, 2>(X, rows, K, qmin, qmax, c, packed, s, st) ||
-        hq4_row_reg_try<G, 4, 2>(X, rows, K, qmin, qmax, c, packed, s, st) ||
-        hq4_row_reg_try<G, 8, 1>(X, rows, K, qmin, qmax, c, packed, s, st) ||
-        hq4_row_reg_try<G, 4, 1>(X, rows, K, qmin, qmax, c, packed, s, st) ||
-        hq4_row_reg_try<G, 8, 2>(X, rows, K, qmin, qmax, c, packed, s, st))
+    if (hq4_row_reg_try<G, 2, 1, I8>(X, rows, K, qmin, qmax, c, codes, s, st) ||
+        hq4_row_reg_try<G, 2, 2, I8>(X, rows, K, qmin, qmax, c, codes, s, st) ||
+        hq4_row_reg_try<G, 4, 2, I8>(X, rows, K, qmin, qmax, c, codes, s, st) ||
+        hq4_row_reg_try<G, 8, 1, I8>(X, rows, K, qmin, qmax, c, codes, s, st) ||
+        hq4_row_reg_try<G, 4, 1, I8>(X, rows, K, qmin, qmax, c, codes, s, st) ||
+        hq4_row_reg_try<G, 8, 2, I8>(X, rows, K, qmin, qmax, c, codes, s, st))
         return;
-#define QA_HQ(NC) hipLaunchKernelGGL((k_hq4_row<G, NC>), grid, block, 0, st, X, rows, K, qmin, qmax, c, packed, s)
+#define QA_HQ(NC) \
+    hipLaunchKernelGGL((k_hq4_row<G, NC, I8>), grid, block, 0, st, X, rows, K, qmin, qmax, c, codes, s)
     if (nch <= 64) QA_HQ(1);
     else if (nch <= 128) QA_HQ(2);
     else if (nch <= 256) QA_HQ(4);
@@ -1116,6 +1128,24 @@ hipError_t launch_hadamard_quant_i4(const uint16_t* X, int64_t rows, int64_t K, 
         case 64: hq4_dispatch<64>(X, rows, K, per_group, qmin, qmax, packed, s, st); break;
         case 128: hq4_dispatch<128>(X, rows, K, per_group, qmin, qmax, packed, s, st); break;
         case 256: hq4_dispatch<256>(X, rows, K, per_group, qmin, qmax, packed, s, st); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+// The same rotation with per-row int8 codes (W4A8 activations).
+hipError_t launch_hadamard_quant_i8(const uint16_t* X, int64_t rows, int64_t K, int G, int qmin, int qmax,
+                                    int8_t* q, float* s, hipStream_t st) {
+    switch (G) {
+        case 1: hq4_dispatch<1, true>(X, rows, K, false, qmin, qmax, q, s, st); break;
+        case 2: hq4_dispatch<2, true>(X, rows, K, false, qmin, qmax, q, s, st); break;
+        case 4: hq4_dispatch<4, true>(X, rows, K, false, qmin, qmax, q, s, st); break;
+        case 8: hq4_dispatch<8, true>(X, rows, K, false, qmin, qmax, q, s, st); break;
+        case 16: hq4_dispatch<16, true>(X, rows, K, false, qmin, qmax, q, s, st); break;
+        case 32: hq4_dispatch<32, true>(X, rows, K, false, qmin, qmax, q, s, st); break;
+        case 64: hq4_dispatch<64, true>(X, rows, K, false, qmin, qmax, q, s, st); break;
+        case 128: hq4_dispatch<128, true>(X, rows, K, false, qmin, qmax, q, s, st); break;
+        case 256: hq4_dispatch<256, true>(X, rows, K, false, qmin, qmax, q, s, st); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

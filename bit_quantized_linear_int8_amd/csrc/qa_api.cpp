@@ -112,6 +112,15 @@ W4Layout w4_layout(int64_t M, int64_t K) {
     return L;
 }
 
+W4Layout w4a8_layout(int64_t M, int64_t K) {
+    W4Layout L;
+    size_t off = 0;
+    L.xp = off; off += up((size_t)M * (size_t)K);
+    L.s_x = off; off += up((size_t)M * 4);
+    L.total = off;
+    return L;
+}
+
 bool valid_dtype(qa_dtype d) { return d == QA_F32 || d == QA_F16 || d == QA_BF16; }
 
 }  // namespace
@@ -532,6 +541,54 @@ qa_status qa_qlinear_w4a4(const void* X_f16, int64_t M, int64_t K, const uint32_
                          "qa_qlinear_w4a4 (gemm)");
 }
 
+// ----------------------------------------------------------------- W4A8
+qa_status qa_hadamard_quant_int8(const void* X_f16, int64_t rows, int64_t K, int32_t G, int32_t q_min, int32_t q_max,
+                                 int8_t* q, float* s, void* stream) {
+    if (G < 1 || G > 256 || (G & (G - 1)) != 0)
+        return fail(QA_ERR_SHAPE, "qa_hadamard_quant_int8: G must be a power of two in [1, 256] (G=%d)", G);
+    if (rows < 0 || K <= 0 || K % 8 != 0 || K % G != 0)
+        return fail(QA_ERR_SHAPE, "qa_hadamard_quant_int8: need rows >= 0, K > 0, K %% 8 == 0, K %% G == 0");
+    if (q_min > q_max || q_min < -128 || q_max > 127 || q_max <= 0)
+        return fail(QA_ERR_VALUE, "qa_hadamard_quant_int8: need -128 <= q_min <= q_max <= 127, q_max > 0");
+    if (rows == 0) return ok();
+    if (!X_f16 || !q || !s) return fail(QA_ERR_NULL, "qa_hadamard_quant_int8: NULL pointer");
+    if (!aligned(X_f16, 16) || !aligned(q, 8) || !aligned(s, 4))
+        return fail(QA_ERR_ALIGN, "qa_hadamard_quant_int8: X 16-byte, q 8-byte, s 4-byte aligned");
+    return device_status(qa::launch_hadamard_quant_i8(static_cast<const uint16_t*>(X_f16), rows, K, G, q_min, q_max,
+                                                      q, s, as_stream(stream)),
+                         "qa_hadamard_quant_int8");
+}
+
+size_t qa_qlinear_w4a8_workspace(int64_t M, int64_t K) {
+    if (M < 0 || K <= 0) return 0;
+    return w4a8_layout(M, K).total;
+}
+
+qa_status qa_qlinear_w4a8(const void* X_f16, int64_t M, int64_t K, const uint32_t* Wp, const float* s_w, int64_t N,
+                          int32_t G, void* out, qa_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+    if (!w4_group_ok(G) || M < 0 || N < 0 || K <= 0 || K % G != 0)
+        return fail(QA_ERR_SHAPE, "qa_qlinear_w4a8: need G in {64,128,256}, M, N >= 0, K > 0, K %% G == 0");
+    if (!valid_dtype(out_dtype)) return fail(QA_ERR_VALUE, "qa_qlinear_w4a8: bad out_dtype %d", (int)out_dtype);
+    if (M == 0 || N == 0) return ok();
+    if (!X_f16 || !Wp || !s_w || !out || !workspace) return fail(QA_ERR_NULL, "qa_qlinear_w4a8: NULL pointer");
+    if (!aligned(X_f16, 16) || !aligned(Wp, 16) || !aligned(s_w, 4) || !aligned(out, 4) ||
+        !aligned(workspace, kAlign))
+        return fail(QA_ERR_ALIGN, "qa_qlinear_w4a8: X, Wp 16-byte, workspace 256-byte, out/s_w 4-byte aligned");
+    const W4Layout L = w4a8_layout(M, K);
+    if (workspace_bytes < L.total)
+        return fail(QA_ERR_WORKSPACE, "qa_qlinear_w4a8: workspace %zu < %zu bytes", workspace_bytes, L.total);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    int8_t* xq = reinterpret_cast<int8_t*>(ws + L.xp);
+    float* s_x = reinterpret_cast<float*>(ws + L.s_x);
+    hipStream_t st = as_stream(stream);
+    hipError_t e =
+        qa::launch_hadamard_quant_i8(static_cast<const uint16_t*>(X_f16), M, K, G, -127, 127, xq, s_x, st);
+    if (e != hipSuccess) return device_status(e, "qa_qlinear_w4a8 (hadamard quant)");
+    return device_status(qa::launch_gemm_w4a8(xq, s_x, Wp, s_w, M, K, N, G, out, (int)out_dtype, st),
+                         "qa_qlinear_w4a8 (gemm)");
+}
+
 // ----------------------------------------------------------------- Kronecker transform (FlatQuant)
 qa_status qa_kron_quant_int4(const void* X_f16, int64_t rows, int64_t K, int64_t n1, int64_t n2, const float* P1,
                              const float* P2, qa_scale_mode mode, int32_t G, int32_t q_min, int32_t q_max,
@@ -613,6 +670,18 @@ qa_status qa_gemm_w4a4_group_acc(const uint32_t* Xp, const uint32_t* Wp, int64_t
         return fail(QA_ERR_ALIGN, "qa_gemm_w4a4_group_acc: Xp, Wp 16-byte, acc 4-byte aligned");
     return device_status(qa::launch_gemm_w4a4_group_acc(Xp, Wp, M, K, N, G, acc, as_stream(stream)),
                          "qa_gemm_w4a4_group_acc");
+}
+
+qa_status qa_gemm_w4a8_group_acc(const int8_t* Xq, const uint32_t* Wp, int64_t M, int64_t K, int64_t N, int32_t G,
+                                 int32_t* acc, void* stream) {
+    if (!w4_group_ok(G) || M < 0 || N < 0 || K <= 0 || K % G != 0)
+        return fail(QA_ERR_SHAPE, "qa_gemm_w4a8_group_acc: need G in {64,128,256}, M, N >= 0, K > 0, K %% G == 0");
+    if (M == 0 || N == 0) return ok();
+    if (!Xq || !Wp || !acc) return fail(QA_ERR_NULL, "qa_gemm_w4a8_group_acc: NULL pointer");
+    if (!aligned(Xq, 16) || !aligned(Wp, 16) || !aligned(acc, 4))
+        return fail(QA_ERR_ALIGN, "qa_gemm_w4a8_group_acc: Xq, Wp 16-byte, acc 4-byte aligned");
+    return device_status(qa::launch_gemm_w4a8_group_acc(Xq, Wp, M, K, N, G, acc, as_stream(stream)),
+                         "qa_gemm_w4a8_group_acc");
 }
 
 }  // extern "C"

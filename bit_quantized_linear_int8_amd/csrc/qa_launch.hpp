@@ -80,6 +80,8 @@ hipError_t launch_kron_quant_i4(const uint16_t* X, int64_t rows, int64_t n1, int
 hipError_t launch_hadamard_quant_i4(const uint16_t* X, int64_t rows, int64_t K, int G,
                                     bool per_group, int qmin, int qmax, uint32_t* packed, float* s,
                                     hipStream_t st);
+hipError_t launch_hadamard_quant_i8(const uint16_t* X, int64_t rows, int64_t K, int G, int qmin, int qmax,
+                                    int8_t* q, float* s, hipStream_t st);
 
 // int8 GEMM C = A * B^T (A [M x K], B [N x K]) with either an int32 store
 // (out_dtype < 0) or the LLM.int8() epilogue.
@@ -136,5 +138,10 @@ hipError_t launch_gemm_w4a4(const uint32_t* Xp, const float* s_x, const uint32_t
 
 hipError_t launch_gemm_w4a4_group_acc(const uint32_t* Xp, const uint32_t* Wp, int64_t M, int64_t K,
                                       int64_t N, int G, int32_t* acc, hipStream_t st);
+
+hipError_t launch_gemm_w4a8(const int8_t* Xq, const float* s_x, const uint32_t* Wp, const float* s_w, int64_t M,
+                            int64_t K, int64_t N, int G, void* out, int out_dtype, hipStream_t st);
+hipError_t launch_gemm_w4a8_group_acc(const int8_t* Xq, const uint32_t* Wp, int64_t M, int64_t K, int64_t N, int G,
+                                      int32_t* acc, hipStream_t st);
 
 }  // namespace qa

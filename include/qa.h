@@ -240,6 +240,42 @@ qa_status qa_qlinear_w4a4(const void* X_f16, int64_t M, int64_t K, const uint32_
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Hadamard rotation + per-row int8 codes  [GroupRot §二, §5.2: the rotation
+ * fused with dynamic per-token quantization; Scholia-IQ §2.2: 8-bit
+ * activations of W4A8]
+ *
+ *   X'[r] = X[r] * blockdiag(H_G) / sqrt(G)   (as qa_hadamard_quant_int4)
+ *   s[r]  = fl32(max_j |X'[r][j]| / q_max)     (1.0 for an all-zero row)
+ *   q[r][j] = clip(rint(fl32(X'[r][j] / s[r])), q_min, q_max)
+ *   X fp16 [rows x K]; q i8 [rows x K]; s f32 [rows]
+ * Errors: NULL pointers, rows < 0, K <= 0, K % 8 != 0, G not a power of two
+ * in [1, 256], K % G != 0, q_min > q_max, q_min < -128, q_max > 127,
+ * q_max <= 0, misaligned X (16 bytes) / q (8 bytes) / s.
+ * ------------------------------------------------------------------------- */
+qa_status qa_hadamard_quant_int8(const void* X_f16, int64_t rows, int64_t K, int32_t G, int32_t q_min,
+                                 int32_t q_max, int8_t* q, float* s, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * W4A8 group-Hadamard linear  [Scholia-IQ §2.1-§2.2: 4-bit weights, 8-bit
+ * activations; "从离群值到平坦线" §4: a transform fitted for W4A4 serves W4A8
+ * unchanged; GroupRot §5.2, §5.4]
+ *
+ *   (Xq, s_x) = qa_hadamard_quant_int8(X, G, -127, 127)   (on device)
+ *   acc_g[m][n] = sum_{k in group g} Xq[m][k] * qw[n][k]   (int32)
+ *   out[m][n]   = s_x[m] * sum_g s_w[n][g] * acc_g[m][n]
+ *   Wp, s_w  the offline W4A4 weight: qa_hadamard_quant_int4(W, G, PER_GROUP,
+ *            -7, 7): u32 [N x K/8], f32 [N x K/G]
+ *   out      [M x N] of out_dtype
+ *   workspace  qa_qlinear_w4a8_workspace(M, K) bytes (any content)
+ * Errors: NULL pointers, M < 0, N < 0, K <= 0, G not in {64, 128, 256},
+ * K % G != 0, misaligned pointers, bad out_dtype, small workspace.
+ * ------------------------------------------------------------------------- */
+size_t qa_qlinear_w4a8_workspace(int64_t M, int64_t K);
+qa_status qa_qlinear_w4a8(const void* X_f16, int64_t M, int64_t K, const uint32_t* Wp,
+                          const float* s_w, int64_t N, int32_t G, void* out, qa_dtype out_dtype,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Asymmetric (zero-point) row quantization  [Scholia-IQ §6: q = round(x/s) +
  * z, x^ = s (q - z), z the integer that stands for real 0; §6.2: the grid
  * shifted onto the data's range, q clipped to [q_min, q_max]]
@@ -424,10 +460,17 @@ qa_status qa_qlinear_kron_w4a4(const void* X_f16, int64_t M, int64_t K, int64_t 
  *   Xp u32 [M x K/8], Wp u32 [N x K/8]; acc i32 [M x N x K/G].
  *   Errors: NULL, M < 0, N < 0, K <= 0, G not in {64, 128, 256},
  *   K % G != 0, misaligned pointers.
+ *
+ * qa_gemm_w4a8_group_acc  [GroupRot §5.4; Scholia-IQ §2.2]
+ *   acc[m][n][g] = sum_{k in group g} Xq[m][k] * qw[n][k] from int8 codes
+ *   Xq i8 [M x K] and packed int4 Wp u32 [N x K/8]; acc i32 [M x N x K/G].
+ *   Errors as qa_gemm_w4a4_group_acc (Xq 16-byte aligned).
  * ------------------------------------------------------------------------- */
 qa_status qa_gemm_i8_i32(const int8_t* A, const int8_t* B, int64_t M, int64_t K, int64_t N,
                          int32_t* C, void* stream);
 qa_status qa_gemm_w4a4_group_acc(const uint32_t* Xp, const uint32_t* Wp, int64_t M, int64_t K,
+                                 int64_t N, int32_t G, int32_t* acc, void* stream);
+qa_status qa_gemm_w4a8_group_acc(const int8_t* Xq, const uint32_t* Wp, int64_t M, int64_t K,
                                  int64_t N, int32_t G, int32_t* acc, void* stream);
 
 #ifdef __cplusplus

@@ -143,6 +143,43 @@ def test_w4a4_argument_errors():
     assert g(A, None, 4, 512, 4, 128, OUT, None) == NULL
 
 
+def test_w4a8_argument_errors():
+    h = qa.lib().qa_hadamard_quant_int8
+    assert h(None, 4, 256, 128, -127, 127, B, OUT, None) == NULL
+    assert h(A, 4, 256, 96, -127, 127, B, OUT, None) == SHAPE           # not a power of two
+    assert h(A, 4, 200, 16, -127, 127, B, OUT, None) == SHAPE           # K % G
+    assert h(A, 4, 260, 4, -127, 127, B, OUT, None) == SHAPE            # K % 8
+    assert h(A, 4, 256, 128, -129, 127, B, OUT, None) == VALUE
+    assert h(A, 4, 256, 128, -127, 128, B, OUT, None) == VALUE
+    assert h(A, 4, 256, 128, 5, 4, B, OUT, None) == VALUE
+    assert h(MIS, 4, 256, 128, -127, 127, B, OUT, None) == ALIGN
+    assert h(A, 4, 256, 128, -127, 127, ctypes.c_void_p(0x20004), OUT, None) == ALIGN   # q 8-byte
+    assert h(A, 0, 256, 128, -127, 127, B, OUT, None) == OK
+    f = qa.lib().qa_qlinear_w4a8
+    base = [A, 16, 512, B, OUT, 32, 128, OUT, 0, WS, 1 << 30, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+    assert call(0, None) == NULL
+    assert call(9, None) == NULL
+    assert call(6, 32) == SHAPE
+    assert call(2, 320) == SHAPE
+    assert call(3, MIS) == ALIGN
+    assert call(8, 7) == VALUE
+    assert call(10, 16 * 512) == WORKSPACE                  # the int8 codes alone need M K bytes
+    assert call(1, 0) == OK
+    L = qa.lib()
+    for M, K in [(1, 64), (16, 512), (2048, 4096)]:
+        ws = L.qa_qlinear_w4a8_workspace(M, K)
+        assert ws >= M * K + 4 * M and ws % 256 == 0
+    g = qa.lib().qa_gemm_w4a8_group_acc
+    assert g(A, B, 4, 512, 4, 100, OUT, None) == SHAPE
+    assert g(A, None, 4, 512, 4, 128, OUT, None) == NULL
+    assert g(MIS, B, 4, 512, 4, 128, OUT, None) == ALIGN
+
+
 def test_gemm_i8_argument_errors():
     f = qa.lib().qa_gemm_i8_i32
     assert f(None, B, 4, 64, 4, OUT, None) == NULL
