@@ -35,6 +35,7 @@ constexpr int DEC_MAXSTEPS = DEC_MAXK / 64 / DEC_WAVES;   // MFMA steps per wave
 constexpr int DEC_LDA = DEC_MAXK + 16;     // LDS row stride of the codes (spreads banks)
 constexpr int DEC_OCAP = 64;               // outliers whose operands are staged in LDS
 static_assert(DEC_MAXK / 8 == DEC_THREADS, "one 8-column chunk of X per thread");
+static_assert(DEC_WAVES == 8, "the wave totals are read as two 16-byte vectors");
 
 __device__ __forceinline__ float half_lo(uint32_t v) { return h2f((uint16_t)(v & 0xffffu)); }
 __device__ __forceinline__ float half_hi(uint32_t v) { return h2f((uint16_t)(v >> 16)); }
@@ -56,6 +57,55 @@ __device__ __forceinline__ uint32_t pick4(const u32x4& v, int i) {
     return (i & 2) ? hi : lo;
 }
 
+// Maximum of an unsigned value over the 64 lanes, in every lane: DPP within
+// rows of 16, then gfx950's row-pair and half-wave swaps (no scalar round trip).
+__device__ __forceinline__ uint32_t wave_max_all_u32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));    // quad_perm [1,0,3,2]
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));    // quad_perm [2,3,0,1]
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));   // row_half_mirror
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));   // row_mirror
+    const auto p16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = max(p16[0], p16[1]);
+    const auto p32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return max(p32[0], p32[1]);
+}
+
+// Eight int8 codes rint(fl32(x / s)) of one chunk without a division, with
+// r = fl32(1 / s).  The fast code is rint(fma(x, r, 128)); a chunk holding a
+// value with |t - rint(t)| > 0.5 - 2^-16 (near a tie) is redone with
+//   q0 = fl32(x r),  e = x - q0 s (exact, one fused multiply-add),
+//   q  = fl32(q0 + e r)  (one fused multiply-add),
+// Markstein's correction step for division (P. W. Markstein, "Computation of
+// elementary functions on the IBM RISC System/6000 processor", 1990), which
+// is the correctly rounded fl32(x / s).  Both facts hold for every fp16 x and
+// every scale fl32(a / 127) of an fp16 a >= |x| -- the per-token scales here;
+// the test suite checks all 1.0e9 such pairs on the CPU.
+__device__ __forceinline__ u32x2 codes8_dec(const u32x4& v, float s, float r) {
+    float x[8], n[8];
+    float dmax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        x[j] = h2f((uint16_t)(v[j >> 1] >> (16 * (j & 1))));
+        const float t = __builtin_fmaf(x[j], r, 128.0f);
+        n[j] = __builtin_rintf(t);
+        dmax = fmaxf(dmax, __builtin_fabsf(t - n[j]));
+    }
+    if (dmax > 0.5f - 0x1p-16f) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float q0 = x[j] * r;
+            const float e = __builtin_fmaf(-q0, s, x[j]);
+            n[j] = __builtin_rintf(__builtin_fmaf(e, r, q0)) + 128.0f;
+        }
+    }
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lo = __builtin_amdgcn_cvt_pk_u8_f32(n[j], j, lo);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hi = __builtin_amdgcn_cvt_pk_u8_f32(n[j + 4], j, hi);
+    return u32x2{lo ^ 0x80808080u, hi ^ 0x80808080u};
+}
+
 template <int MB>
 __global__ __launch_bounds__(DEC_THREADS) void k_decode_mixed(const uint16_t* __restrict__ X, int M, int K,
                                                               const int8_t* __restrict__ Wq,
@@ -69,7 +119,7 @@ __global__ __launch_bounds__(DEC_THREADS) void k_decode_mixed(const uint16_t* __
     __shared__ float wo[DEC_OCAP][16];       // outlier weights w~   [h][channel]
     __shared__ uint32_t rmax[DEC_WAVES][MB];
     __shared__ float sx_s[16];
-    __shared__ int wtot[DEC_WAVES];
+    __shared__ __attribute__((aligned(16))) int wtot[DEC_WAVES];
 
     const int t = threadIdx.x, lane = t & 63, wave = wave_id();
     const int64_t n0 = (int64_t)blockIdx.x * 16;
@@ -120,14 +170,20 @@ __global__ __launch_bounds__(DEC_THREADS) void k_decode_mixed(const uint16_t* __
     }
     flags = own ? flags : 0u;
     const u32x4 keepw = u32x4{keep[0], keep[1], keep[2], keep[3]};   // 0xffff per ordinary column
+    {
+        uint32_t mine = 0u;                           // lane m keeps token m's maximum
 #pragma unroll
-    for (int m = 0; m < MB; ++m) {
-        uint32_t r = 0u;
+        for (int m = 0; m < MB; ++m) {
+            uint32_t r = 0u;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) r = pk_max_u16(r, xv[m][d] & 0x7fff7fffu & keep[d]);
-        const uint32_t a = wave_max_u32(max(r & 0xffffu, r >> 16));
-        if (lane == 0) rmax[wave][m] = a;
+            for (int d = 0; d < 4; ++d) r = pk_max_u16(r, xv[m][d] & 0x7fff7fffu & keep[d]);
+            const uint32_t a = wave_max_all_u32(max(r & 0xffffu, r >> 16));
+            mine = lane == m ? a : mine;
+        }
+        if (lane < MB) rmax[wave][lane] = mine;
     }
+
+    float s_l = 1.0f, r_l = 1.0f;                     // lane m < MB: scale of token m, its reciprocal
 
     // 2b. ascending outlier list (block-wide exclusive scan over the chunks,
     //     the in-wave part from one ballot per flag bit); the owner of an
@@ -143,8 +199,23 @@ __global__ __launch_bounds__(DEC_THREADS) void k_decode_mixed(const uint16_t* __
         if (lane == 0) wtot[wave] = wsum;
         lds_barrier();
 
+        // per-token scales: lane m < MB reduces token m over the waves
+        // (every wave does, so no further barrier is needed)
+        if (lane < MB) {
+            uint32_t ab = 0u;
+#pragma unroll
+            for (int w = 0; w < DEC_WAVES; ++w) ab = max(ab, rmax[w][lane]);
+            const float a = h2f((uint16_t)ab);
+            s_l = a == 0.0f ? 1.0f : a / 127.0f;
+            r_l = 1.0f / s_l;
+            if (wave == 0) sx_s[lane] = s_l;
+        }
+
+        const int4 wt0 = *reinterpret_cast<const int4*>(wtot), wt1 = *reinterpret_cast<const int4*>(wtot + 4);
+        const int wt[8] = {wt0.x, wt0.y, wt0.z, wt0.w, wt1.x, wt1.y, wt1.z, wt1.w};
         int off = below;
-        for (int w = 0; w < wave; ++w) off += wtot[w];
+#pragma unroll
+        for (int w = 0; w < DEC_WAVES; ++w) off += w < wave ? wt[w] : 0;
         uint32_t f = flags;
         while (f) {
             const int j = __builtin_ctz(f);
@@ -163,10 +234,21 @@ __global__ __launch_bounds__(DEC_THREADS) void k_decode_mixed(const uint16_t* __
     int count = 0;
 #pragma unroll
     for (int w = 0; w < DEC_WAVES; ++w) count += wtot[w];
+
+    // 2c. int8 codes of X into LDS (outlier columns -> 0 -> code 0; tokens
+    //     past M read zeros, have scale 1 and get codes 0, which no MFMA reads)
+    if (own) {
+#pragma unroll
+        for (int m = 0; m < MB; ++m) {
+            const float s = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s_l), m));
+            const float r = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r_l), m));
+            *reinterpret_cast<u32x2*>(aq + m * DEC_LDA + 8 * t) = codes8_dec(xv[m] & keepw, s, r);
+        }
+    }
     lds_barrier();
 
 
-    // 2c. start the gather of the outlier weights (first 64): the fp16 W[n][h]
+    // 2d. start the gather of the outlier weights (first 64): the fp16 W[n][h]
     //     or the int8 code Wq[n][h], as the aligned 32-bit word holding it.
     //     The loads are unconditional (the descriptor is selected) and their
     //     values are used only after the MFMA, so no wait lands here.
@@ -184,30 +266,6 @@ __global__ __launch_bounds__(DEC_THREADS) void k_decode_mixed(const uint16_t* __
         graw[q] = bload4(rsg, h < count ? (b & ~3u) : kOOB);
         gsh[q] = (b & 3u) * 8;
     }
-
-    // 2d. per-token scales (every thread derives the same values), int8 codes
-    float sxm[MB];
-#pragma unroll
-    for (int m = 0; m < MB; ++m) {
-        uint32_t ab = 0u;
-#pragma unroll
-        for (int w = 0; w < DEC_WAVES; ++w) ab = max(ab, rmax[w][m]);
-        const float a = h2f((uint16_t)ab);
-        sxm[m] = a == 0.0f ? 1.0f : a / 127.0f;
-        if (t == m) sx_s[m] = sxm[m];
-    }
-    if (own) {
-#pragma unroll
-        for (int m = 0; m < MB; ++m) {
-            if (m < M) {
-                const float s = sxm[m], r = 1.0f / s;
-                float xf[8];
-                unpack8(xv[m] & keepw, xf);                // outlier columns -> 0 -> code 0
-                *reinterpret_cast<u32x2*>(aq + m * DEC_LDA + 8 * t) = codes8_dyn(xf, s, r);
-            }
-        }
-    }
-    lds_barrier();
 
     // 3a. int32 MFMA over this wave's K steps
     v4i acc = v4i{0, 0, 0, 0};

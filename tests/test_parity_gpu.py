@@ -246,6 +246,23 @@ def test_mixed_decode_kernel_shapes(qa, M, K, N, tau, pass_w16):
     _mixed_case(qa, X, W, tau, 1, pass_w16)
 
 
+@pytest.mark.parametrize("tau", [float("inf"), 90.0])
+def test_mixed_decode_kernel_ties(qa, tau):
+    # the fused decode kernel's exact fallback: rows whose scale is exactly 1
+    # or 1/2 put many quotients on .5 ties, which round half to even
+    rng = np.random.default_rng(23)
+    M, K, N = 6, 1024, 48
+    X = (rng.integers(-200, 201, (M, K)) * 0.5).astype(np.float16)     # multiples of 0.5 in [-100, 100]
+    X[:, 7] = 127.0                                                      # absmax 127: s = 1
+    X[1] = (rng.integers(-127, 128, K) * 0.25 + 0.25).astype(np.float16) # s = 1/2 with x / s = k + 0.5
+    X[1, 7] = 63.5
+    # one-hot weight rows: output (m, n) is s_x[m] * code(m, k_n) * s_w[n] * 127,
+    # so a code off by one moves it by 1/127 of the largest output
+    W = np.zeros((N, K), np.float16)
+    W[np.arange(N), 20 * np.arange(N) + 3] = 1.0
+    _mixed_case(qa, X, W, tau, 0, False)
+
+
 def test_mixed_decode_kernel_many_outliers(qa):
     X, W, _ = synthetic.mixed_inputs(8, 4096, 96, seed=21, n_dims=300, p_token=0.6)
     for dt in (0, 1, 2):
