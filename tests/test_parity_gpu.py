@@ -296,6 +296,39 @@ def test_mixed_tail_split(qa, pass_w16):
     _mixed_case(qa, X, W, 6.0, 1, pass_w16)               # fp16 output
 
 
+@pytest.mark.parametrize("M,K,N,n_dims,pass_w16,tau", [
+    (2100, 528, 9000, 6, False, 6.0),        # 324 tiles, last K step partial, ragged M and N
+    (768, 4112, 22000, 5, True, 6.0),        # 258 tiles, 65 K steps
+    (1024, 1024, 17000, 150, False, 6.0),    # 268 tiles, 150 outlier columns: several staging passes
+    (1030, 2048, 16500, 0, False, float("inf")),  # 325 tiles, no outlier columns
+])
+def test_mixed_partial_rounds(qa, M, K, N, n_dims, pass_w16, tau):
+    """More 256 x 256 tiles than one round over the 256 CUs but not whole
+    rounds (the trailing columns take a second launch of smaller tiles), with
+    a partial last K step, ragged M and N and up to 150 outlier columns.
+    Sampled rows from every tile row, all columns."""
+    X, W, _ = synthetic.mixed_inputs(M, K, N, seed=M + N, n_dims=n_dims, p_token=0.7,
+                                     magnitude=("uniform", 6.5, 60.0))
+    rng = np.random.default_rng(M)
+    rows = np.unique(np.concatenate([np.arange(0, M, 256), np.arange(255, M, 256), [M - 1],
+                                     rng.choice(M, 6, replace=False)]))
+    _mixed_case(qa, X, W, tau, 1, pass_w16, rows=rows)
+
+
+def test_mixed_repeated_calls_one_workspace(qa):
+    # consecutive calls with different data through the same workspace
+    M, K, N = 600, 256, 30000
+    ws = torch.empty(qa.qa_qlinear_int8_mixed_workspace(M, K), dtype=torch.uint8, device=DEV)
+    for seed in (1, 2, 3):
+        X, W, _ = synthetic.mixed_inputs(M, K, N, seed=seed, n_dims=4, magnitude=("uniform", 6.5, 60.0))
+        Wq, s_w = qa.qa_quantize_rowwise_int8(dev(W))
+        out = qa.qa_qlinear_int8_mixed(dev(X), Wq, s_w, out_dtype=torch.float32, workspace=ws)
+        oWq, os_w = oracle.quant_rows(W)
+        rows = np.array([0, 255, 256, 511, 599])
+        ref = oracle.qlinear_int8_mixed(X, oWq, os_w[:, 0], tau=6.0, rows=rows)
+        assert_float_parity(as_f64(out)[rows], ref, torch.float32)
+
+
 def test_mixed_w8a8_config_sampled(qa):
     c = synthetic.config("w8a8_ffn")
     rng = np.random.default_rng(1)
