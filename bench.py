@@ -274,7 +274,7 @@ def cpu_baseline(c, nbytes, seconds):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build runs on a single MI355X and has no multi-GPU "
+        print("bench.py measures one GPU only: the library runs on a single MI355X and has no multi-GPU "
               "path (--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import torch

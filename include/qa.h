@@ -78,7 +78,7 @@ typedef enum {
     QA_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned */
     QA_ERR_VALUE = 4,       /* q_min > q_max, range outside the code type, NaN threshold, ... */
     QA_ERR_WORKSPACE = 5,   /* workspace smaller than the matching *_workspace() size */
-    QA_ERR_UNSUPPORTED = 6, /* a valid request this build does not implement */
+    QA_ERR_UNSUPPORTED = 6, /* a valid request that this library has no kernel for */
     QA_ERR_DEVICE = 7       /* a HIP launch failed; see qa_last_error() */
 } qa_status;
 
