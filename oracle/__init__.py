@@ -85,6 +85,8 @@ def lib() -> ctypes.CDLL:
             "orc_hadamard_quant_int8": (None, [P, I64, I64, I32, I32, I32, P, P]),
             "orc_w4a8_group_acc": (I64, [P, P, I64, I64, I64, I32, P, I64, P]),
             "orc_qlinear_w4a8": (None, [P, I64, I64, P, P, I64, I32, P, I64, P]),
+            "orc_hadamard_quant_int4_asym": (None, [P, I64, I64, I32, P, P, P]),
+            "orc_qlinear_w4a4_asym": (None, [P, I64, I64, P, P, I64, I32, P, I64, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -496,4 +498,30 @@ def qlinear_w4a8(X16, Wp, s_w, G: int, rows=None):
     r, nr = _rows(rows)
     out = np.zeros((nr if r is not None else M, N), np.float64)
     lib().orc_qlinear_w4a8(_ptr(h), M, K, _ptr(Wp), _ptr(sw), N, int(G), _ptr(r), nr, _ptr(out))
+    return out
+
+
+# ---------------------------------------------------------------- W4A4, zero-point activations
+def hadamard_quant_int4_asym(X16, G: int):
+    """-> (packed u32 [rows x K/8] holding q - 8, s f32 [rows], z i32 [rows] in [0, 15])."""
+    h = _h16(X16)
+    if h.ndim == 1:
+        h = h[None, :]
+    rows, K = h.shape
+    packed = np.zeros((rows, K // 8), np.uint32)
+    s = np.zeros(rows, np.float32)
+    z = np.zeros(rows, np.int32)
+    lib().orc_hadamard_quant_int4_asym(_ptr(h), rows, K, int(G), _ptr(packed), _ptr(s), _ptr(z))
+    return packed, s, z
+
+
+def qlinear_w4a4_asym(X16, Wp, s_w, G: int, rows=None):
+    h = _h16(X16)
+    M, K = h.shape
+    Wp = _c(Wp, np.uint32)
+    N = Wp.shape[0]
+    sw = _c(s_w, np.float32)
+    r, nr = _rows(rows)
+    out = np.zeros((nr if r is not None else M, N), np.float64)
+    lib().orc_qlinear_w4a4_asym(_ptr(h), M, K, _ptr(Wp), _ptr(sw), N, int(G), _ptr(r), nr, _ptr(out))
     return out

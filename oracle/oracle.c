@@ -904,3 +904,65 @@ void orc_qlinear_w4a8(const uint16_t* X, int64_t M, int64_t K, const uint32_t* W
     }
     free(wq);
 }
+
+/* ---------------------------------------------------------------------------
+ * W4A4 with zero-point activations  [Scholia-IQ §6 (q = round(x/s) + z,
+ * x^ = s (q - z)), §6.2 (the grid shifted onto the data's range, clip to
+ * [q_min, q_max]), §7.3; GroupRot §5.2, §5.4]
+ *   X' = X * blockdiag(H_G) (as for W4A4); per row (s, z) by the min-max rule
+ *   over [0, 15]; q = clip(rint(fl32(x'/s)) + z, 0, 15);
+ *   the weight is the W4A4 weight (symmetric int4 per G-group);
+ *   out[m][n] = s_x[m] * sum_g s_w[n][g] * sum_{k in g} (q[m][k] - z[m]) qw[n][k]
+ *   (integer sums exact, fp64).
+ * Packed activation codes: nibble = (q - 8) mod 16, i.e. the two's complement
+ * nibble of q - 8 (the packing of the symmetric codes); z is returned in
+ * [0, 15].
+ * ------------------------------------------------------------------------- */
+void orc_hadamard_quant_int4_asym(const uint16_t* X, int64_t rows, int64_t K, int32_t G,
+                                  uint32_t* packed, float* s, int32_t* z)
+{
+    size_t n = (size_t)(rows * K > 0 ? rows * K : 1);
+    float* xr = (float*)malloc(sizeof(float) * n);
+    int8_t* q = (int8_t*)malloc(n);
+    orc_hadamard_rows(X, rows, K, G, xr);
+    orc_quant_rows_asym_f32(xr, rows, K, 0, 15, q, s, z, NULL);
+    for (size_t i = 0; i < (size_t)(rows * K); ++i)
+        q[i] = (int8_t)(q[i] - 8);
+    orc_pack_int4(q, rows, K, packed);
+    free(q);
+    free(xr);
+}
+
+void orc_qlinear_w4a4_asym(const uint16_t* X, int64_t M, int64_t K, const uint32_t* Wp,
+                           const float* s_w, int64_t N, int32_t G, const int64_t* rows,
+                           int64_t nrows, double* out)
+{
+    if (!rows)
+        nrows = M;
+    int64_t ng = K / G;
+    int8_t* wq = (int8_t*)malloc((size_t)(N * K > 0 ? N * K : 1));
+    orc_unpack_int4(Wp, N, K, wq);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t ri = 0; ri < nrows; ++ri) {
+        int64_t m = rows ? rows[ri] : ri;
+        uint32_t* xp = (uint32_t*)malloc(sizeof(uint32_t) * (size_t)(K / 8 > 0 ? K / 8 : 1));
+        int8_t* xq = (int8_t*)malloc((size_t)K);
+        float s_x = 0.0f;
+        int32_t z_x = 0;
+        orc_hadamard_quant_int4_asym(X + m * K, 1, K, G, xp, &s_x, &z_x);
+        orc_unpack_int4(xp, 1, K, xq);           /* q - 8 */
+        for (int64_t n = 0; n < N; ++n) {
+            double sum = 0.0;
+            for (int64_t g = 0; g < ng; ++g) {
+                int64_t a = 0;
+                for (int64_t k = g * G; k < (g + 1) * G; ++k)
+                    a += ((int64_t)xq[k] + 8 - z_x) * (int64_t)wq[n * K + k];
+                sum += (double)s_w[n * ng + g] * (double)a;
+            }
+            out[ri * N + n] = (double)s_x * sum;
+        }
+        free(xq);
+        free(xp);
+    }
+    free(wq);
+}

@@ -493,6 +493,90 @@ def test_w4a8_error_below_w4a4():
     assert abs(e8 - e_w) < 0.05 * e_w
 
 
+# ------------------------------------------------------------------ W4A4, zero-point activations
+def test_w4a4_asym_worked_examples():
+    # G = 1 leaves the row unrotated.  Inference Quantization §6: data in [0, 6]
+    # on int4 spreads over all 16 levels with 0 at the bottom: s = 6/15, z = 0;
+    # 2.5, 7.5 and 12.5 round half to even
+    x = np.array([[0, 1, 2, 3, 4, 5, 6, 0]], np.float16)
+    p, s, z = oracle.hadamard_quant_int4_asym(x, 1)
+    assert s[0] == np.float32(6.0) / np.float32(15.0) and z[0] == 0
+    assert np.array_equal(oracle.unpack_int4(p, 8)[0] + 8, [0, 2, 5, 8, 10, 12, 15, 0])
+    assert np.array_equal(_unpack_np(p, 8)[0], [-8, -6, -3, 0, 2, 4, 7, -8])       # stored as q - 8
+    # §6.2: the range [-0.2, 1.7] puts real 0 exactly on the code z = 2
+    x = np.array([[-0.2, 1.7, 0.0, 0.0, 1.0, -0.1, 0.5, 0.0]], np.float16)
+    p, s, z = oracle.hadamard_quant_int4_asym(x, 1)
+    q = oracle.unpack_int4(p, 8)[0] + 8
+    assert z[0] == 2 and q[2] == 2 and q[0] == 0 and q[1] == 15
+    # a constant row: hi = lo after including 0 only when the row is all zero
+    p, s, z = oracle.hadamard_quant_int4_asym(np.zeros((1, 16), np.float16), 8)
+    assert s[0] == 1.0 and z[0] == 0 and not (oracle.unpack_int4(p, 16) + 8).any()
+
+
+@pytest.mark.parametrize("G", [8, 64, 128])
+def test_w4a4_asym_codes_reconstruct_the_rotated_row(G):
+    X, _, _ = synthetic.mixed_inputs(6, 512, 1, seed=31, n_dims=3, magnitude=("abs_normal", 30.0))
+    X[1] = np.abs(X[1])                                     # one-sided row
+    p, s, z = oracle.hadamard_quant_int4_asym(X, G)
+    H = scipy.linalg.hadamard(G).astype(np.float64)
+    xr = ((X.astype(np.float64).reshape(6, -1, G) @ H) * (1.0 / math.sqrt(G))).astype(np.float32).reshape(6, 512)
+    q = oracle.unpack_int4(p, 512).astype(np.int64) + 8
+    assert q.min() >= 0 and q.max() <= 15 and np.all((z >= 0) & (z <= 15))
+    lo = np.minimum(xr.min(axis=1), 0).astype(np.float64)
+    hi = np.maximum(xr.max(axis=1), 0).astype(np.float64)
+    # every value of [lo, hi] is representable: within half a step of s (q - z)
+    sd = s.astype(np.float64)[:, None]
+    assert np.all(np.abs(sd * (q - z[:, None]) - xr) <= 0.5 * sd * (1 + 1e-5))
+    assert np.all(np.abs(s - (hi - lo) / 15) <= 1e-6 * (hi - lo) / 15)
+    # real 0 sits within half a step of the grid point z
+    assert np.all(np.abs(np.rint(-lo / s.astype(np.float64)) - z) <= 0.5 + 1e-9)
+
+
+def test_w4a4_asym_linear_is_the_dequantized_product_and_bounded():
+    M, K, N, G = 10, 512, 18, 128
+    X, W, _ = synthetic.w4a4_inputs(M, K, N, seed=32)
+    X = np.abs(X)                                           # one-sided activations
+    Wp, s_w = oracle.hadamard_quant_int4(W, G, per_group=True)
+    out = oracle.qlinear_w4a4_asym(X, Wp, s_w, G)
+    p, s_x, z_x = oracle.hadamard_quant_int4_asym(X, G)
+    xd = (oracle.unpack_int4(p, K).astype(np.float64) + 8 - z_x[:, None]) * s_x.astype(np.float64)[:, None]
+    wd = _unpack_np(Wp, K) * np.repeat(s_w.astype(np.float64), G, axis=1)
+    mag = np.abs(xd) @ np.abs(wd).T
+    assert np.all(np.abs(out - xd @ wd.T) <= 1e-12 * mag)
+    H = scipy.linalg.hadamard(G).astype(np.float64) / math.sqrt(G)
+    xr = (X.astype(np.float64).reshape(M, -1, G) @ H).reshape(M, K)
+    wr = (W.astype(np.float64).reshape(N, -1, G) @ H).reshape(N, K)
+    sx = s_x.astype(np.float64) * (1 + 1e-6)
+    sw = np.repeat(np.abs(wr.astype(np.float32)).reshape(N, -1, G).max(axis=2) / 7, G, axis=1) * (1 + 1e-6)
+    B = 0.5 * sx[:, None] * ((np.abs(wr) + 0.5 * sw).sum(axis=1))[None, :] + 0.5 * np.abs(xr) @ sw.T
+    exact = X.astype(np.float64) @ W.astype(np.float64).T
+    assert np.all(np.abs(out - exact) <= B + 2.0 ** -20 * (np.abs(xr) @ np.abs(wr).T))
+    rows = np.array([9, 2])
+    assert np.array_equal(oracle.qlinear_w4a4_asym(X, Wp, s_w, G, rows=rows), out[rows])
+
+
+@pytest.mark.parametrize("seed", [33, 34])
+def test_w4a4_asym_lowers_the_error_of_one_sided_activations(seed):
+    # the point of the zero-point: one-sided rows (after the rotation their
+    # range is still lopsided) get a finer grid, (hi - lo)/15 against the
+    # symmetric absmax/7, so both the activation codes and the output are closer
+    M, K, N, G = 16, 1024, 24, 128
+    X, W, _ = synthetic.w4a4_inputs(M, K, N, seed=seed)
+    X = np.abs(X)
+    H = scipy.linalg.hadamard(G).astype(np.float64) / math.sqrt(G)
+    xr = (X.astype(np.float64).reshape(M, -1, G) @ H).reshape(M, K)
+    pa, sa, za = oracle.hadamard_quant_int4_asym(X, G)
+    ps, ss = oracle.hadamard_quant_int4(X, G, per_group=False)
+    ea = np.abs((oracle.unpack_int4(pa, K) + 8 - za[:, None]) * sa.astype(np.float64)[:, None] - xr).mean()
+    es = np.abs(oracle.unpack_int4(ps, K) * ss.astype(np.float64) - xr).mean()
+    assert ea < 0.9 * es
+    exact = X.astype(np.float64) @ W.astype(np.float64).T
+    Wp, s_w = oracle.hadamard_quant_int4(W, G, per_group=True)
+    e_asym = np.abs(oracle.qlinear_w4a4_asym(X, Wp, s_w, G) - exact).mean()
+    e_sym = np.abs(oracle.qlinear_w4a4(X, Wp, s_w, G) - exact).mean()
+    assert e_asym < e_sym
+
+
 # ------------------------------------------------------------------ SmoothQuant
 def _f32_ulp(x):
     x = np.abs(np.asarray(x, np.float32))
