@@ -14,8 +14,9 @@ Also reported (same JSON line, key "also"): whole-call throughput of the
 prefill-shape mixed linear, the W8A8 FFN shape, the W4A4 group-Hadamard
 linear, the SmoothQuant W8A8 linear on the prefill and FFN data and the
 top-2% decomposition and the zero-point W8A8 linear on the prefill data, and
-the Kronecker-transform W4A4 linear and the W4A8 group-Hadamard linear on the
-W4A4 data, in int8 TOPS against the dense int8 MFMA peak.
+the Kronecker-transform W4A4 linear, the W4A8 group-Hadamard linear and the
+W4A4 linear with zero-point activations (one-sided) on the W4A4 data, in int8
+TOPS against the dense int8 MFMA peak.
 
 roofline: the decode kernel's algorithmic bytes per launch / its average
 launch duration, from HIP events recorded on the launch stream around the
@@ -54,7 +55,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--only", default=None,
                    help="run one workload only (decode|prefill|w8a8|w4a4|smooth_prefill|smooth_ffn|topk_prefill|"
-                        "asym_prefill|kron_w4a4|w4a8|copy), for "
+                        "asym_prefill|kron_w4a4|w4a8|w4a4_asym|copy), for "
                         "profiling; copy is a plain "
                         "1 GiB device copy used to calibrate HBM byte counters")
     return p.parse_args()
@@ -236,6 +237,21 @@ def w4a4_workload(torch, qa, synthetic, dev):
     return c, fns, 2 * M * N * K
 
 
+def w4a4_asym_workload(torch, qa, synthetic, dev):
+    """The W4A4 weight with zero-point int4 activations; the activations are
+    made one-sided (|X|), the case the zero-point is for."""
+    c = synthetic.config("w4a4_hadamard")
+    M, K, N, G = c["M"], c["K"], c["N"], c["G"]
+    import numpy as np
+    X = torch.from_numpy(np.abs(c["X"])).to(dev)
+    Wp, s_w = qa.qa_hadamard_quant_int4(torch.from_numpy(c["W"]).to(dev), G, True)
+    c_w = qa.qa_w4_column_terms(Wp, s_w, K, G)
+    out = torch.empty((M, N), dtype=torch.float32, device=dev)
+    ws = torch.empty(qa.qa_qlinear_w4a4_asym_workspace(M, K), dtype=torch.uint8, device=dev)
+    fns = [lambda: qa.qa_qlinear_w4a4_asym(X, Wp, s_w, c_w, G=G, out=out, workspace=ws)]
+    return c, fns, 2 * M * N * K
+
+
 def w4a8_workload(torch, qa, synthetic, dev):
     """The W4A4 data with 8-bit activations: group-Hadamard int8 codes of X
     against the same offline per-group int4 weight."""
@@ -333,14 +349,15 @@ def main():
         torch.cuda.empty_cache()
 
     keys = ("prefill", "w8a8", "w4a4", "smooth_prefill", "smooth_ffn", "topk_prefill", "asym_prefill", "kron_w4a4",
-            "w4a8")
+            "w4a8", "w4a4_asym")
     run_also = (args.only is None and not args.no_also) or args.only in keys
     if run_also:
         todo = []
         for name, key in (("prefill_mixed", "prefill"), ("w8a8_ffn", "w8a8"), ("w4a4_hadamard", "w4a4"),
                           ("prefill_mixed", "smooth_prefill"), ("w8a8_ffn", "smooth_ffn"),
                           ("prefill_mixed", "topk_prefill"), ("prefill_mixed", "asym_prefill"),
-                          ("w4a4_hadamard", "kron_w4a4"), ("w4a4_hadamard", "w4a8")):
+                          ("w4a4_hadamard", "kron_w4a4"), ("w4a4_hadamard", "w4a8"),
+                          ("w4a4_hadamard", "w4a4_asym")):
             if args.only in (None, key):
                 todo.append((name, key))
         for name, key in todo:
@@ -356,6 +373,9 @@ def main():
             elif key == "kron_w4a4":
                 c, fns, ops = kron_workload(torch, qa, synthetic, dev)
                 name = "kron_w4a4: FlatQuant Kronecker transform (64 x 64) + W4A4, %s data" % name
+            elif key == "w4a4_asym":
+                c, fns, ops = w4a4_asym_workload(torch, qa, synthetic, dev)
+                name = "w4a4_asym: group-Hadamard W4A4, zero-point int4 activations, one-sided %s data" % name
             elif key == "w4a8":
                 c, fns, ops = w4a8_workload(torch, qa, synthetic, dev)
                 name = "w4a8: group-Hadamard int8 activations x per-group int4 weight, %s data" % name

@@ -33,6 +33,7 @@ EXPORTS = (
     "qa_hadamard_quant_int4", "qa_kron_quant_int4", "qa_qlinear_kron_w4a4_workspace", "qa_qlinear_kron_w4a4",
     "qa_qlinear_w4a4_workspace", "qa_qlinear_w4a4",
     "qa_hadamard_quant_int8", "qa_qlinear_w4a8_workspace", "qa_qlinear_w4a8",
+    "qa_hadamard_quant_int4_asym", "qa_w4_column_terms", "qa_qlinear_w4a4_asym_workspace", "qa_qlinear_w4a4_asym",
     "qa_gemm_i8_i32", "qa_gemm_w4a4_group_acc", "qa_gemm_w4a8_group_acc",
 )
 
@@ -91,6 +92,10 @@ def lib() -> ctypes.CDLL:
             "qa_qlinear_w4a8_workspace": (SZ, [I64, I64]),
             "qa_qlinear_w4a8": (S, [P, I64, I64, P, P, I64, I32, P, S, P, SZ, P]),
             "qa_gemm_w4a8_group_acc": (S, [P, P, I64, I64, I64, I32, P, P]),
+            "qa_hadamard_quant_int4_asym": (S, [P, I64, I64, I32, P, P, P, P]),
+            "qa_w4_column_terms": (S, [P, P, I64, I64, I32, P, P]),
+            "qa_qlinear_w4a4_asym_workspace": (SZ, [I64, I64]),
+            "qa_qlinear_w4a4_asym": (S, [P, I64, I64, P, P, P, I64, I32, P, S, P, SZ, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -458,6 +463,50 @@ def qa_qlinear_w4a8(X, Wp, s_w, G=128, out_dtype=torch.float32, out=None, worksp
     _check("qa_qlinear_w4a8",
            lib().qa_qlinear_w4a8(_p(X), M, K, _p(Wp), _p(s_w), N, int(G), _p(out), _DTYPE_CODE[out.dtype],
                                  _p(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def qa_hadamard_quant_int4_asym(X, G: int, stream=None):
+    """Hadamard rotation + zero-point int4 codes per row -> (packed u32 as int32 [rows x K/8] holding q - 8,
+    s f32 [rows], z i32 [rows])."""
+    _dev(X, "X", torch.float16)
+    rows, K = X.shape
+    packed = torch.empty((rows, K // 8), dtype=torch.int32, device=X.device)
+    s = torch.empty(rows, dtype=torch.float32, device=X.device)
+    z = torch.empty(rows, dtype=torch.int32, device=X.device)
+    _check("qa_hadamard_quant_int4_asym",
+           lib().qa_hadamard_quant_int4_asym(_p(X), rows, K, int(G), _p(packed), _p(s), _p(z), _stream(stream)))
+    return packed, s, z
+
+
+def qa_w4_column_terms(Wp, s_w, K: int, G: int, stream=None):
+    """c[n] = sum_g s_w[n][g] * sum_{k in g} qw[n][k] of a per-group int4 weight -> f32 [N]."""
+    _dev(Wp, "Wp", torch.int32)
+    _dev(s_w, "s_w", torch.float32)
+    N = Wp.shape[0]
+    c = torch.empty(N, dtype=torch.float32, device=Wp.device)
+    _check("qa_w4_column_terms", lib().qa_w4_column_terms(_p(Wp), _p(s_w), N, int(K), int(G), _p(c), _stream(stream)))
+    return c
+
+
+def qa_qlinear_w4a4_asym_workspace(M: int, K: int) -> int:
+    return int(lib().qa_qlinear_w4a4_asym_workspace(M, K))
+
+
+def qa_qlinear_w4a4_asym(X, Wp, s_w, c_w, G=128, out_dtype=torch.float32, out=None, workspace=None, stream=None):
+    """W4A4 group-Hadamard linear with zero-point int4 activations -> out [M x N]."""
+    _dev(X, "X", torch.float16)
+    _dev(Wp, "Wp", torch.int32)
+    _dev(s_w, "s_w", torch.float32)
+    _dev(c_w, "c_w", torch.float32)
+    M, K = X.shape
+    N = Wp.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=X.device)
+    workspace = _workspace(qa_qlinear_w4a4_asym_workspace(M, K), X.device, workspace)
+    _check("qa_qlinear_w4a4_asym",
+           lib().qa_qlinear_w4a4_asym(_p(X), M, K, _p(Wp), _p(s_w), _p(c_w), N, int(G), _p(out),
+                                      _DTYPE_CODE[out.dtype], _p(workspace), workspace.numel(), _stream(stream)))
     return out
 
 

@@ -931,11 +931,16 @@ struct W4Stage {
     static constexpr int LDS = C::STAGES * STAGE;
 };
 
-template <class C, int G, bool STORE_ACC, bool A8 = false>
+// ZX: zero-point activations (codes stored as q - 8, zero-points z_x in
+// [0, 15]): the epilogue subtracts (z_x[m] - 8) c_w[n] before the row scale,
+// c_w[n] = sum_g s_w[n][g] sum_{k in g} qw[n][k] (launch_w4_column_terms).
+template <class C, int G, bool STORE_ACC, bool A8 = false, bool ZX = false>
 __device__ __forceinline__ void w4a4_dma_body(const uint32_t* __restrict__ Xp, const float* __restrict__ s_x,
                                               const uint32_t* __restrict__ Wp, const float* __restrict__ s_w,
                                               int64_t M, int64_t K, int64_t N, void* __restrict__ out,
-                                              int out_dtype, int tiles_m, int tiles_n, uint8_t* smem, float* sws) {
+                                              int out_dtype, int tiles_m, int tiles_n, uint8_t* smem, float* sws,
+                                              const int32_t* __restrict__ z_x = nullptr,
+                                              const float* __restrict__ c_w = nullptr) {
     constexpr int SPG = G / 64;                       // MFMA steps per group
     using S = W4Stage<C, A8>;
     constexpr float SCALE = A8 ? 0x1p-4f : 0x1p-8f;   // the nibble shift(s) in each product
@@ -1101,17 +1106,34 @@ __device__ __forceinline__ void w4a4_dma_body(const uint32_t* __restrict__ Xp, c
     if constexpr (!STORE_ACC) {
         const rsrc_t rsx = make_rsrc(s_x + m0, (M - m0) * 4);
         const bool vec = (N & 3) == 0;
+        v4f cw[ZX ? C::FN : 1];
+        if constexpr (ZX) {
+            const rsrc_t rcw = make_rsrc(c_w + n0, (N - n0) * 4);
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j) {
+                const int cl = wn * C::TN + j * 16 + 4 * (lane >> 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) cw[j][e] = __builtin_bit_cast(float, bload4(rcw, (uint32_t)(cl + e) * 4));
+            }
+        }
+        const rsrc_t rzx = make_rsrc(ZX ? z_x + m0 : nullptr, ZX ? (M - m0) * 4 : 0);
 #pragma unroll
         for (int i = 0; i < C::FM; ++i) {
             const int rl = wm * C::TM + i * 16 + (lane & 15);
             const float sx = __builtin_bit_cast(float, bload4(rsx, (uint32_t)rl * 4));
+            const float zx = ZX ? (float)((int32_t)bload4(rzx, (uint32_t)rl * 4) - 8) : 0.0f;
             const int64_t row = m0 + rl;
 #pragma unroll
             for (int j = 0; j < C::FN; ++j) {
                 const int64_t col = n0 + wn * C::TN + j * 16 + 4 * (lane >> 4);
                 v4f o;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] = sx * f[i][j][e];
+                for (int e = 0; e < 4; ++e) {
+                    if constexpr (ZX)
+                        o[e] = sx * __builtin_fmaf(-zx, cw[j][e], f[i][j][e]);
+                    else
+                        o[e] = sx * f[i][j][e];
+                }
                 if (row < M && col < N) store_out4(out, out_dtype, row * N + col, o, vec, (int)(N - col < 4 ? N - col : 4));
             }
         }
@@ -1128,6 +1150,22 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_w4a4_dma(const uint32_t* __
     __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
     __shared__ __attribute__((aligned(16))) float sws[STORE_ACC ? 4 : W4D_SW_LDS];
     w4a4_dma_body<C, G, STORE_ACC>(Xp, s_x, Wp, s_w, M, K, N, out, out_dtype, tiles_m, tiles_n, smem, sws);
+}
+
+// W4A4 with zero-point activations.
+template <class C, int G>
+__global__ __launch_bounds__(C::THREADS) void k_gemm_w4a4z_dma(const uint32_t* __restrict__ Xp,
+                                                               const float* __restrict__ s_x,
+                                                               const int32_t* __restrict__ z_x,
+                                                               const uint32_t* __restrict__ Wp,
+                                                               const float* __restrict__ s_w,
+                                                               const float* __restrict__ c_w, int64_t M, int64_t K,
+                                                               int64_t N, void* __restrict__ out, int out_dtype,
+                                                               int tiles_m, int tiles_n) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
+    __shared__ __attribute__((aligned(16))) float sws[W4D_SW_LDS];
+    w4a4_dma_body<C, G, false, false, true>(Xp, s_x, Wp, s_w, M, K, N, out, out_dtype, tiles_m, tiles_n, smem, sws,
+                                            z_x, c_w);
 }
 
 // W4A8: int8 activation codes Xq [M x K] against the packed int4 weight.
@@ -1171,6 +1209,28 @@ hipError_t launch_gemm_w4a4(const uint32_t* Xp, const float* s_x, const uint32_t
         case 64: w4a4_dispatch<64, false>(Xp, s_x, Wp, s_w, M, K, N, out, out_dtype, st); break;
         case 128: w4a4_dispatch<128, false>(Xp, s_x, Wp, s_w, M, K, N, out, out_dtype, st); break;
         case 256: w4a4_dispatch<256, false>(Xp, s_x, Wp, s_w, M, K, N, out, out_dtype, st); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int G>
+static void w4a4z_dispatch(const uint32_t* Xp, const float* s_x, const int32_t* z_x, const uint32_t* Wp,
+                           const float* s_w, const float* c_w, int64_t M, int64_t K, int64_t N, void* out,
+                           int out_dtype, hipStream_t st) {
+    int tm, tn;
+    dim3 g = grid_of<CfgW4>(M, N, tm, tn);
+    hipLaunchKernelGGL((k_gemm_w4a4z_dma<CfgW4, G>), g, dim3(CfgW4::THREADS), 0, st, Xp, s_x, z_x, Wp, s_w, c_w, M,
+                       K, N, out, out_dtype, tm, tn);
+}
+
+hipError_t launch_gemm_w4a4_asym(const uint32_t* Xp, const float* s_x, const int32_t* z_x, const uint32_t* Wp,
+                                 const float* s_w, const float* c_w, int64_t M, int64_t K, int64_t N, int G,
+                                 void* out, int out_dtype, hipStream_t st) {
+    switch (G) {
+        case 64: w4a4z_dispatch<64>(Xp, s_x, z_x, Wp, s_w, c_w, M, K, N, out, out_dtype, st); break;
+        case 128: w4a4z_dispatch<128>(Xp, s_x, z_x, Wp, s_w, c_w, M, K, N, out, out_dtype, st); break;
+        case 256: w4a4z_dispatch<256>(Xp, s_x, z_x, Wp, s_w, c_w, M, K, N, out, out_dtype, st); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -877,65 +877,111 @@ __device__ __forceinline__ void fwht_chunk(const u32x4& v, double c, int lane, f
     for (int j = 0; j < 8; ++j) xo[j] = (float)(y[j] * c);
 }
 
+// Code formats of the per-row quantizers below: symmetric int4 (packed),
+// symmetric int8, and zero-point int4 (q = clip(rint(x / s) + z, 0, 15),
+// packed as the two's complement nibble q - 8).
+enum { HQ_I4 = 0, HQ_I8 = 1, HQ_I4Z = 2 };
+
+// Per-row parameters from the row's maximum magnitude `amax` (symmetric) or
+// its range [lo, hi] with lo <= 0 <= hi (zero-point, the min-max rule over
+// [0, 15]: s = fl32(fl32(hi - lo) / 15), 1.0 when hi == lo, and
+// z = clip(-rint(fl32(lo / s)), 0, 15)).
+struct RowParams {
+    float s, r;
+    int z;
+};
+
+template <int MODE>
+__device__ __forceinline__ RowParams row_params(float amax, float lo, float hi, int qmax) {
+    RowParams p;
+    p.z = 0;
+    if constexpr (MODE == HQ_I4Z) {
+        p.s = hi != lo ? (hi - lo) / 15.0f : 1.0f;
+        p.z = clampi(-(int)__builtin_rintf(lo / p.s), 0, 15);
+    } else {
+        p.s = amax == 0.0f ? 1.0f : amax / (float)qmax;
+    }
+    p.r = 1.0f / p.s;
+    return p;
+}
+
 // The codes of chunk ch (8 values, |x / s| <= q_max (1 + 2^-23)), clipped
-// below at qmin: I8, eight int8 codes at out + 8 ch; otherwise eight int4
+// below at qmin: HQ_I8, eight int8 codes at out + 8 ch; otherwise eight int4
 // codes packed into the word out[ch], element j in bits [4j+3:4j].
-template <bool I8>
-__device__ __forceinline__ void store_codes(void* out, int64_t ch, const float* x, float s, float r, int qmin) {
-    if constexpr (I8)
-        reinterpret_cast<u32x2*>(out)[ch] = clip_codes(codes8_dyn(x, s, r), qmin);
-    else
-        reinterpret_cast<uint32_t*>(out)[ch] = pack_codes(x, s, r, qmin);
+template <int MODE>
+__device__ __forceinline__ void store_codes(void* out, int64_t ch, const float* x, const RowParams& p, int qmin) {
+    if constexpr (MODE == HQ_I8) {
+        reinterpret_cast<u32x2*>(out)[ch] = clip_codes(codes8_dyn(x, p.s, p.r), qmin);
+    } else if constexpr (MODE == HQ_I4Z) {
+        int unused = 0;
+        const u32x2 q = codes8_asym(x, p.s, p.r, p.z, 0, 15, unused);
+        reinterpret_cast<uint32_t*>(out)[ch] = pack_nibbles(u32x2{q[0] ^ 0x08080808u, q[1] ^ 0x08080808u});
+    } else {
+        reinterpret_cast<uint32_t*>(out)[ch] = pack_codes(x, p.s, p.r, qmin);
+    }
+}
+
+// The magnitudes a row's parameters need, as non-negative fp32 bit patterns
+// (which order like the values): amax, or -lo and hi.
+__device__ __forceinline__ void range8(const float* x, float& amax, float& nlo, float& hi) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        amax = fmaxf(amax, __builtin_fabsf(x[j]));
+        nlo = fmaxf(nlo, -x[j]);
+        hi = fmaxf(hi, x[j]);
+    }
 }
 
 // Per-row scale, row held in registers (NC > 0) or recomputed (NC == 0).
-template <int G, int NC, bool I8>
+template <int G, int NC, int MODE>
 __global__ __launch_bounds__(256) void k_hq4_row(const uint16_t* __restrict__ X, int64_t rows, int64_t K,
                                                  int qmin, int qmax, double c, void* __restrict__ codes,
-                                                 float* __restrict__ s_out) {
+                                                 float* __restrict__ s_out, int32_t* __restrict__ z_out) {
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + wave_id();
     if (row >= rows) return;
     const int64_t nch = K >> 3;
     const rsrc_t rx = make_rsrc(X + row * K, K * 2);
-    void* pr = reinterpret_cast<uint8_t*>(codes) + row * nch * (I8 ? 8 : 4);
+    void* pr = reinterpret_cast<uint8_t*>(codes) + row * nch * (MODE == HQ_I8 ? 8 : 4);
     if constexpr (NC > 0) {
         u32x4 v[NC];
 #pragma unroll
         for (int i = 0; i < NC; ++i) v[i] = bload16(rx, (uint32_t)(lane + 64 * i) * 16);
         float xs[NC][8];
-        float amax = 0.0f;
+        float amax = 0.0f, nlo = 0.0f, hi = 0.0f;
 #pragma unroll
         for (int i = 0; i < NC; ++i) {
             fwht_chunk<G>(v[i], c, lane, xs[i]);
-            amax = fmaxf(amax, absmax8f(xs[i]));
+            range8(xs[i], amax, nlo, hi);
         }
-        amax = wave_max(amax);
-        const float s = amax == 0.0f ? 1.0f : amax / (float)qmax;
-        const float r = 1.0f / s;
-        if (lane == 0) s_out[row] = s;
+        const RowParams p = row_params<MODE>(wave_max(amax), -wave_max(nlo), wave_max(hi), qmax);
+        if (lane == 0) {
+            s_out[row] = p.s;
+            if (MODE == HQ_I4Z) z_out[row] = p.z;
+        }
 #pragma unroll
         for (int i = 0; i < NC; ++i) {
             const int64_t ch = lane + 64 * i;
-            if (ch < nch) store_codes<I8>(pr, ch, xs[i], s, r, qmin);
+            if (ch < nch) store_codes<MODE>(pr, ch, xs[i], p, qmin);
         }
     } else {
-        float amax = 0.0f;
+        float amax = 0.0f, nlo = 0.0f, hi = 0.0f;
         for (int64_t base = 0; base < nch; base += 64) {
             const int64_t ch = base + lane;
             float xo[8];
             fwht_chunk<G>(bload16(rx, (uint32_t)ch * 16), c, lane, xo);
-            amax = fmaxf(amax, absmax8f(xo));
+            range8(xo, amax, nlo, hi);
         }
-        amax = wave_max(amax);
-        const float s = amax == 0.0f ? 1.0f : amax / (float)qmax;
-        const float r = 1.0f / s;
-        if (lane == 0) s_out[row] = s;
+        const RowParams p = row_params<MODE>(wave_max(amax), -wave_max(nlo), wave_max(hi), qmax);
+        if (lane == 0) {
+            s_out[row] = p.s;
+            if (MODE == HQ_I4Z) z_out[row] = p.z;
+        }
         for (int64_t base = 0; base < nch; base += 64) {
             const int64_t ch = base + lane;
             float xo[8];
             fwht_chunk<G>(bload16(rx, (uint32_t)ch * 16), c, lane, xo);
-            if (ch < nch) store_codes<I8>(pr, ch, xo, s, r, qmin);
+            if (ch < nch) store_codes<MODE>(pr, ch, xo, p, qmin);
         }
     }
 }
@@ -951,15 +997,15 @@ __global__ __launch_bounds__(256) void k_hq4_row(const uint16_t* __restrict__ X,
 // in-block bits except the lowest log2(LPB) chunk bits, which sit in the lane
 // index and take one DPP quad exchange per bit.  The stages commute and every
 // partial sum is exact in fp64, so their order does not matter.
-template <int G, int NC, int WPR, bool I8>
+template <int G, int NC, int WPR, int MODE>
 __global__ __launch_bounds__(256) void k_hq4_row_reg(const uint16_t* __restrict__ X, int64_t rows, int64_t K,
                                                      int qmin, int qmax, double c, void* __restrict__ codes,
-                                                     float* __restrict__ s_out) {
+                                                     float* __restrict__ s_out, int32_t* __restrict__ z_out) {
     constexpr int CPB = G / 8;
     constexpr int LPB = CPB > NC ? CPB / NC : 1;
     static_assert(CPB >= 1 && LPB <= 4 && (LPB > 1 ? CPB % NC == 0 : NC % CPB == 0), "unsupported G / NC");
     static_assert(WPR == 1 || WPR == 2 || WPR == 4, "waves per row");
-    __shared__ uint32_t red[4];
+    __shared__ uint32_t red[3][4];
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int64_t row = (int64_t)blockIdx.x * (4 / WPR) + wave / WPR;
     const int part = wave % WPR;                      // which K / WPR slice of the row
@@ -1016,28 +1062,39 @@ __global__ __launch_bounds__(256) void k_hq4_row_reg(const uint16_t* __restrict_
             }
     }
     float xs[NC][8];
-    float amax = 0.0f;
+    float amax = 0.0f, nlo = 0.0f, hi = 0.0f;
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) xs[i][j] = (float)(y[i][j] * c);
-        amax = fmaxf(amax, absmax8f(xs[i]));
+        range8(xs[i], amax, nlo, hi);
     }
-    uint32_t ab = wave_max_u32(__builtin_bit_cast(uint32_t, amax));       // amax >= 0: bits order like values
+    // the maxima are >= 0, so their bit patterns order like their values
+    constexpr int NR = MODE == HQ_I4Z ? 3 : 1;
+    uint32_t ab[3] = {__builtin_bit_cast(uint32_t, amax), __builtin_bit_cast(uint32_t, nlo),
+                      __builtin_bit_cast(uint32_t, hi)};
+#pragma unroll
+    for (int k = 0; k < NR; ++k) ab[k] = wave_max_u32(ab[k]);
     if constexpr (WPR > 1) {
-        if (lane == 0) red[wave] = ab;
+        if (lane == 0)
+#pragma unroll
+            for (int k = 0; k < NR; ++k) red[k][wave] = ab[k];
         __syncthreads();
         const int w0 = wave - part;
 #pragma unroll
-        for (int q = 0; q < WPR; ++q) ab = max(ab, red[w0 + q]);
+        for (int q = 0; q < WPR; ++q)
+#pragma unroll
+            for (int k = 0; k < NR; ++k) ab[k] = max(ab[k], red[k][w0 + q]);
     }
     if (!live) return;
-    amax = __builtin_bit_cast(float, ab);
-    const float s = amax == 0.0f ? 1.0f : amax / (float)qmax;
-    const float r = 1.0f / s;
-    if (lane == 0 && part == 0) s_out[row] = s;
+    const RowParams p = row_params<MODE>(__builtin_bit_cast(float, ab[0]), -__builtin_bit_cast(float, ab[1]),
+                                         __builtin_bit_cast(float, ab[2]), qmax);
+    if (lane == 0 && part == 0) {
+        s_out[row] = p.s;
+        if (MODE == HQ_I4Z) z_out[row] = p.z;
+    }
 #pragma unroll
-    for (int i = 0; i < NC; ++i) store_codes<I8>(codes, ch0 + chunk(i), xs[i], s, r, qmin);
+    for (int i = 0; i < NC; ++i) store_codes<MODE>(codes, ch0 + chunk(i), xs[i], p, qmin);
 }
 
 // Per-group scale (G >= 8): the G/8 lanes of a block reduce their absmax.
@@ -1072,42 +1129,42 @@ constexpr bool hq4_row_reg_ok() {
     return G >= 8 && (G / 8 > NC ? (G / 8) / NC <= 4 && (G / 8) % NC == 0 : NC % (G / 8) == 0);
 }
 
-template <int G, int NC, int WPR, bool I8>
+template <int G, int NC, int WPR, int MODE>
 static bool hq4_row_reg_try(const uint16_t* X, int64_t rows, int64_t K, int qmin, int qmax, double c,
-                            void* codes, float* s, hipStream_t st) {
+                            void* codes, float* s, int32_t* z, hipStream_t st) {
     if constexpr (hq4_row_reg_ok<G, NC>()) {
         if (K != 512 * NC * WPR) return false;
         const dim3 grid((unsigned)((rows + 4 / WPR - 1) / (4 / WPR))), block(256);
-        hipLaunchKernelGGL((k_hq4_row_reg<G, NC, WPR, I8>), grid, block, 0, st, X, rows, K, qmin, qmax, c, codes,
-                           s);
+        hipLaunchKernelGGL((k_hq4_row_reg<G, NC, WPR, MODE>), grid, block, 0, st, X, rows, K, qmin, qmax, c, codes,
+                           s, z);
         return true;
     } else {
         return false;
     }
 }
 
-template <int G, bool I8 = false>
+template <int G, int MODE = HQ_I4>
 static void hq4_dispatch(const uint16_t* X, int64_t rows, int64_t K, bool per_group, int qmin, int qmax,
-                         void* codes, float* s, hipStream_t st) {
+                         void* codes, float* s, hipStream_t st, int32_t* z = nullptr) {
     const double c = 1.0 / __builtin_sqrt((double)G);
     const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
     if (per_group) {
-        if constexpr (G >= 8 && !I8)
+        if constexpr (G >= 8 && MODE == HQ_I4)
             hipLaunchKernelGGL((k_hq4_group<G>), grid, block, 0, st, X, rows, K, qmin, qmax, c,
                                static_cast<uint32_t*>(codes), s);
         return;
     }
     const int64_t nch = K / 8;
     // two waves per row where the lane mapping allows it (more waves to hide latency)
-    if (hq4_row_reg_try<G, 2, 1, I8>(X, rows, K, qmin, qmax, c, codes, s, st) ||
-        hq4_row_reg_try<G, 2, 2, I8>(X, rows, K, qmin, qmax, c, codes, s, st) ||
-        hq4_row_reg_try<G, 4, 2, I8>(X, rows, K, qmin, qmax, c, codes, s, st) ||
-        hq4_row_reg_try<G, 8, 1, I8>(X, rows, K, qmin, qmax, c, codes, s, st) ||
-        hq4_row_reg_try<G, 4, 1, I8>(X, rows, K, qmin, qmax, c, codes, s, st) ||
-        hq4_row_reg_try<G, 8, 2, I8>(X, rows, K, qmin, qmax, c, codes, s, st))
+    if (hq4_row_reg_try<G, 2, 1, MODE>(X, rows, K, qmin, qmax, c, codes, s, z, st) ||
+        hq4_row_reg_try<G, 2, 2, MODE>(X, rows, K, qmin, qmax, c, codes, s, z, st) ||
+        hq4_row_reg_try<G, 4, 2, MODE>(X, rows, K, qmin, qmax, c, codes, s, z, st) ||
+        hq4_row_reg_try<G, 8, 1, MODE>(X, rows, K, qmin, qmax, c, codes, s, z, st) ||
+        hq4_row_reg_try<G, 4, 1, MODE>(X, rows, K, qmin, qmax, c, codes, s, z, st) ||
+        hq4_row_reg_try<G, 8, 2, MODE>(X, rows, K, qmin, qmax, c, codes, s, z, st))
         return;
 #define QA_HQ(NC) \
-    hipLaunchKernelGGL((k_hq4_row<G, NC, I8>), grid, block, 0, st, X, rows, K, qmin, qmax, c, codes, s)
+    hipLaunchKernelGGL((k_hq4_row<G, NC, MODE>), grid, block, 0, st, X, rows, K, qmin, qmax, c, codes, s, z)
     if (nch <= 64) QA_HQ(1);
     else if (nch <= 128) QA_HQ(2);
     else if (nch <= 256) QA_HQ(4);
@@ -1133,19 +1190,66 @@ hipError_t launch_hadamard_quant_i4(const uint16_t* X, int64_t rows, int64_t K, 
     return hipGetLastError();
 }
 
+// Column terms of the zero-point correction, one thread per output channel
+// (an offline computation on the weight): the group sums of the signed
+// nibbles are exact integers, each product with the fp32 group scale is exact
+// in fp64, and the products are added over g ascending.
+__global__ __launch_bounds__(256) void k_w4_column_terms(const uint32_t* __restrict__ Wp, const float* __restrict__ s_w,
+                                                         int64_t N, int64_t K, int G, float* __restrict__ c) {
+    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (n >= N) return;
+    const int64_t words = K / 8, ng = K / G, wpg = G / 8;
+    const uint32_t* w = Wp + n * words;
+    double acc = 0.0;
+    for (int64_t g = 0; g < ng; ++g) {
+        int sum = 0;
+        for (int64_t i = g * wpg; i < (g + 1) * wpg; ++i) {
+            const uint32_t v = w[i];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sum += (int)(v << (28 - 4 * j)) >> 28;    // nibble j, sign-extended
+        }
+        acc += (double)s_w[n * ng + g] * (double)sum;
+    }
+    c[n] = (float)acc;
+}
+
+hipError_t launch_w4_column_terms(const uint32_t* Wp, const float* s_w, int64_t N, int64_t K, int G, float* c,
+                                  hipStream_t st) {
+    hipLaunchKernelGGL(k_w4_column_terms, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st, Wp, s_w, N, K, G, c);
+    return hipGetLastError();
+}
+
+// The same rotation with zero-point int4 codes per row (q - 8 packed, z in [0, 15]).
+hipError_t launch_hadamard_quant_i4_asym(const uint16_t* X, int64_t rows, int64_t K, int G, uint32_t* packed,
+                                         float* s, int32_t* z, hipStream_t st) {
+    switch (G) {
+        case 1: hq4_dispatch<1, HQ_I4Z>(X, rows, K, false, 0, 15, packed, s, st, z); break;
+        case 2: hq4_dispatch<2, HQ_I4Z>(X, rows, K, false, 0, 15, packed, s, st, z); break;
+        case 4: hq4_dispatch<4, HQ_I4Z>(X, rows, K, false, 0, 15, packed, s, st, z); break;
+        case 8: hq4_dispatch<8, HQ_I4Z>(X, rows, K, false, 0, 15, packed, s, st, z); break;
+        case 16: hq4_dispatch<16, HQ_I4Z>(X, rows, K, false, 0, 15, packed, s, st, z); break;
+        case 32: hq4_dispatch<32, HQ_I4Z>(X, rows, K, false, 0, 15, packed, s, st, z); break;
+        case 64: hq4_dispatch<64, HQ_I4Z>(X, rows, K, false, 0, 15, packed, s, st, z); break;
+        case 128: hq4_dispatch<128, HQ_I4Z>(X, rows, K, false, 0, 15, packed, s, st, z); break;
+        case 256: hq4_dispatch<256, HQ_I4Z>(X, rows, K, false, 0, 15, packed, s, st, z); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 // The same rotation with per-row int8 codes (W4A8 activations).
 hipError_t launch_hadamard_quant_i8(const uint16_t* X, int64_t rows, int64_t K, int G, int qmin, int qmax,
                                     int8_t* q, float* s, hipStream_t st) {
     switch (G) {
-        case 1: hq4_dispatch<1, true>(X, rows, K, false, qmin, qmax, q, s, st); break;
-        case 2: hq4_dispatch<2, true>(X, rows, K, false, qmin, qmax, q, s, st); break;
-        case 4: hq4_dispatch<4, true>(X, rows, K, false, qmin, qmax, q, s, st); break;
-        case 8: hq4_dispatch<8, true>(X, rows, K, false, qmin, qmax, q, s, st); break;
-        case 16: hq4_dispatch<16, true>(X, rows, K, false, qmin, qmax, q, s, st); break;
-        case 32: hq4_dispatch<32, true>(X, rows, K, false, qmin, qmax, q, s, st); break;
-        case 64: hq4_dispatch<64, true>(X, rows, K, false, qmin, qmax, q, s, st); break;
-        case 128: hq4_dispatch<128, true>(X, rows, K, false, qmin, qmax, q, s, st); break;
-        case 256: hq4_dispatch<256, true>(X, rows, K, false, qmin, qmax, q, s, st); break;
+        case 1: hq4_dispatch<1, HQ_I8>(X, rows, K, false, qmin, qmax, q, s, st); break;
+        case 2: hq4_dispatch<2, HQ_I8>(X, rows, K, false, qmin, qmax, q, s, st); break;
+        case 4: hq4_dispatch<4, HQ_I8>(X, rows, K, false, qmin, qmax, q, s, st); break;
+        case 8: hq4_dispatch<8, HQ_I8>(X, rows, K, false, qmin, qmax, q, s, st); break;
+        case 16: hq4_dispatch<16, HQ_I8>(X, rows, K, false, qmin, qmax, q, s, st); break;
+        case 32: hq4_dispatch<32, HQ_I8>(X, rows, K, false, qmin, qmax, q, s, st); break;
+        case 64: hq4_dispatch<64, HQ_I8>(X, rows, K, false, qmin, qmax, q, s, st); break;
+        case 128: hq4_dispatch<128, HQ_I8>(X, rows, K, false, qmin, qmax, q, s, st); break;
+        case 256: hq4_dispatch<256, HQ_I8>(X, rows, K, false, qmin, qmax, q, s, st); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

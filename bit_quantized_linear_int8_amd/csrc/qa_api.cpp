@@ -121,6 +121,20 @@ W4Layout w4a8_layout(int64_t M, int64_t K) {
     return L;
 }
 
+struct W4zLayout {
+    size_t xp, s_x, z_x, total;
+};
+
+W4zLayout w4z_layout(int64_t M, int64_t K) {
+    W4zLayout L;
+    size_t off = 0;
+    L.xp = off; off += up((size_t)M * (size_t)(K / 2));
+    L.s_x = off; off += up((size_t)M * 4);
+    L.z_x = off; off += up((size_t)M * 4);
+    L.total = off;
+    return L;
+}
+
 bool valid_dtype(qa_dtype d) { return d == QA_F32 || d == QA_F16 || d == QA_BF16; }
 
 }  // namespace
@@ -587,6 +601,65 @@ qa_status qa_qlinear_w4a8(const void* X_f16, int64_t M, int64_t K, const uint32_
     if (e != hipSuccess) return device_status(e, "qa_qlinear_w4a8 (hadamard quant)");
     return device_status(qa::launch_gemm_w4a8(xq, s_x, Wp, s_w, M, K, N, G, out, (int)out_dtype, st),
                          "qa_qlinear_w4a8 (gemm)");
+}
+
+// ----------------------------------------------------------------- W4A4, zero-point activations
+qa_status qa_hadamard_quant_int4_asym(const void* X_f16, int64_t rows, int64_t K, int32_t G, uint32_t* packed,
+                                      float* s, int32_t* z, void* stream) {
+    if (G < 1 || G > 256 || (G & (G - 1)) != 0)
+        return fail(QA_ERR_SHAPE, "qa_hadamard_quant_int4_asym: G must be a power of two in [1, 256] (G=%d)", G);
+    if (rows < 0 || K <= 0 || K % 8 != 0 || K % G != 0)
+        return fail(QA_ERR_SHAPE, "qa_hadamard_quant_int4_asym: need rows >= 0, K > 0, K %% 8 == 0, K %% G == 0");
+    if (rows == 0) return ok();
+    if (!X_f16 || !packed || !s || !z) return fail(QA_ERR_NULL, "qa_hadamard_quant_int4_asym: NULL pointer");
+    if (!aligned(X_f16, 16) || !aligned(packed, 4) || !aligned(s, 4) || !aligned(z, 4))
+        return fail(QA_ERR_ALIGN, "qa_hadamard_quant_int4_asym: X 16-byte, packed/s/z 4-byte aligned");
+    return device_status(qa::launch_hadamard_quant_i4_asym(static_cast<const uint16_t*>(X_f16), rows, K, G, packed, s,
+                                                           z, as_stream(stream)),
+                         "qa_hadamard_quant_int4_asym");
+}
+
+qa_status qa_w4_column_terms(const uint32_t* Wp, const float* s_w, int64_t N, int64_t K, int32_t G, float* c,
+                             void* stream) {
+    if (G < 8 || G > 256 || (G & (G - 1)) != 0 || N < 0 || K <= 0 || K % G != 0)
+        return fail(QA_ERR_SHAPE, "qa_w4_column_terms: need N >= 0, K > 0, G a power of two in [8, 256], K %% G == 0");
+    if (N == 0) return ok();
+    if (!Wp || !s_w || !c) return fail(QA_ERR_NULL, "qa_w4_column_terms: NULL pointer");
+    if (!aligned(Wp, 4) || !aligned(s_w, 4) || !aligned(c, 4))
+        return fail(QA_ERR_ALIGN, "qa_w4_column_terms: Wp, s_w, c 4-byte aligned");
+    return device_status(qa::launch_w4_column_terms(Wp, s_w, N, K, G, c, as_stream(stream)), "qa_w4_column_terms");
+}
+
+size_t qa_qlinear_w4a4_asym_workspace(int64_t M, int64_t K) {
+    if (M < 0 || K <= 0) return 0;
+    return w4z_layout(M, K).total;
+}
+
+qa_status qa_qlinear_w4a4_asym(const void* X_f16, int64_t M, int64_t K, const uint32_t* Wp, const float* s_w,
+                               const float* c_w, int64_t N, int32_t G, void* out, qa_dtype out_dtype, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    if (!w4_group_ok(G) || M < 0 || N < 0 || K <= 0 || K % G != 0)
+        return fail(QA_ERR_SHAPE, "qa_qlinear_w4a4_asym: need G in {64,128,256}, M, N >= 0, K > 0, K %% G == 0");
+    if (!valid_dtype(out_dtype)) return fail(QA_ERR_VALUE, "qa_qlinear_w4a4_asym: bad out_dtype %d", (int)out_dtype);
+    if (M == 0 || N == 0) return ok();
+    if (!X_f16 || !Wp || !s_w || !c_w || !out || !workspace)
+        return fail(QA_ERR_NULL, "qa_qlinear_w4a4_asym: NULL pointer");
+    if (!aligned(X_f16, 16) || !aligned(Wp, 16) || !aligned(s_w, 4) || !aligned(c_w, 4) || !aligned(out, 4) ||
+        !aligned(workspace, kAlign))
+        return fail(QA_ERR_ALIGN,
+                    "qa_qlinear_w4a4_asym: X, Wp 16-byte, workspace 256-byte, out/s_w/c_w 4-byte aligned");
+    const W4zLayout L = w4z_layout(M, K);
+    if (workspace_bytes < L.total)
+        return fail(QA_ERR_WORKSPACE, "qa_qlinear_w4a4_asym: workspace %zu < %zu bytes", workspace_bytes, L.total);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    uint32_t* xp = reinterpret_cast<uint32_t*>(ws + L.xp);
+    float* s_x = reinterpret_cast<float*>(ws + L.s_x);
+    int32_t* z_x = reinterpret_cast<int32_t*>(ws + L.z_x);
+    hipStream_t st = as_stream(stream);
+    hipError_t e = qa::launch_hadamard_quant_i4_asym(static_cast<const uint16_t*>(X_f16), M, K, G, xp, s_x, z_x, st);
+    if (e != hipSuccess) return device_status(e, "qa_qlinear_w4a4_asym (hadamard quant)");
+    return device_status(qa::launch_gemm_w4a4_asym(xp, s_x, z_x, Wp, s_w, c_w, M, K, N, G, out, (int)out_dtype, st),
+                         "qa_qlinear_w4a4_asym (gemm)");
 }
 
 // ----------------------------------------------------------------- Kronecker transform (FlatQuant)

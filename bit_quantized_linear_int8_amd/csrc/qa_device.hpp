@@ -196,10 +196,9 @@ __device__ __forceinline__ u32x2 clip_codes(u32x2 c, int qmin) {
     return u32x2{w[0], w[1]};
 }
 
-// Eight int4 codes of one chunk as one 32-bit word: element i in bits
-// [4i+3 : 4i], two's complement.
-__device__ __forceinline__ uint32_t pack_codes(const float* x, float s, float r, int qmin) {
-    const u32x2 c = clip_codes(codes8_dyn(x, s, r), qmin);
+// The low nibbles of eight bytes as one 32-bit word: byte i's nibble in
+// bits [4i+3 : 4i].
+__device__ __forceinline__ uint32_t pack_nibbles(u32x2 c) {
     uint32_t w[2];
 #pragma unroll
     for (int d = 0; d < 2; ++d) {
@@ -208,6 +207,12 @@ __device__ __forceinline__ uint32_t pack_codes(const float* x, float s, float r,
         w[d] = (a | (a >> 8)) & 0xffffu;
     }
     return w[0] | (w[1] << 16);
+}
+
+// Eight int4 codes of one chunk as one 32-bit word: element i in bits
+// [4i+3 : 4i], two's complement.
+__device__ __forceinline__ uint32_t pack_codes(const float* x, float s, float r, int qmin) {
+    return pack_nibbles(clip_codes(codes8_dyn(x, s, r), qmin));
 }
 
 // Largest magnitude of eight values.

@@ -82,6 +82,12 @@ hipError_t launch_hadamard_quant_i4(const uint16_t* X, int64_t rows, int64_t K, 
                                     hipStream_t st);
 hipError_t launch_hadamard_quant_i8(const uint16_t* X, int64_t rows, int64_t K, int G, int qmin, int qmax,
                                     int8_t* q, float* s, hipStream_t st);
+hipError_t launch_hadamard_quant_i4_asym(const uint16_t* X, int64_t rows, int64_t K, int G, uint32_t* packed,
+                                         float* s, int32_t* z, hipStream_t st);
+// Per output channel of a per-group int4 weight: c[n] = fl32(sum_g s_w[n][g] *
+// sum_{k in g} qw[n][k]), the sum in fp64 over g ascending.
+hipError_t launch_w4_column_terms(const uint32_t* Wp, const float* s_w, int64_t N, int64_t K, int G, float* c,
+                                  hipStream_t st);
 
 // int8 GEMM C = A * B^T (A [M x K], B [N x K]) with either an int32 store
 // (out_dtype < 0) or the LLM.int8() epilogue.
@@ -141,6 +147,11 @@ hipError_t launch_gemm_w4a4_group_acc(const uint32_t* Xp, const uint32_t* Wp, in
 
 hipError_t launch_gemm_w4a8(const int8_t* Xq, const float* s_x, const uint32_t* Wp, const float* s_w, int64_t M,
                             int64_t K, int64_t N, int G, void* out, int out_dtype, hipStream_t st);
+// W4A4 with zero-point activations: Xp holds q - 8 and z_x (in [0, 15]) the
+// zero-points; out = s_x[m] (sum_g s_w[n][g] acc_g - (z_x[m] - 8) c_w[n]).
+hipError_t launch_gemm_w4a4_asym(const uint32_t* Xp, const float* s_x, const int32_t* z_x, const uint32_t* Wp,
+                                 const float* s_w, const float* c_w, int64_t M, int64_t K, int64_t N, int G,
+                                 void* out, int out_dtype, hipStream_t st);
 hipError_t launch_gemm_w4a8_group_acc(const int8_t* Xq, const uint32_t* Wp, int64_t M, int64_t K, int64_t N, int G,
                                       int32_t* acc, hipStream_t st);
 

@@ -276,6 +276,52 @@ qa_status qa_qlinear_w4a8(const void* X_f16, int64_t M, int64_t K, const uint32_
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Hadamard rotation + zero-point int4 codes per row  [GroupRot §二, §5.2;
+ * Scholia-IQ §6 (q = round(x/s) + z, x^ = s (q - z)), §6.2 (the grid on the
+ * data's range, clip to [q_min, q_max])]
+ *
+ *   X'[r] = X[r] * blockdiag(H_G) / sqrt(G)       (as qa_hadamard_quant_int4)
+ *   [lo, hi] = [min(min X'[r], 0), max(max X'[r], 0)]
+ *   s[r] = fl32(fl32(hi - lo) / 15)   (1.0 when hi == lo)
+ *   z[r] = clip(-rint(fl32(lo / s[r])), 0, 15)
+ *   q = clip(rint(fl32(X'[r][j] / s[r])) + z[r], 0, 15), packed eight per
+ *   word as the two's complement nibble q - 8 (element 8w+i in bits
+ *   [4i+3:4i] of word w)
+ *   X fp16 [rows x K]; packed u32 [rows x K/8]; s f32, z i32 [rows]
+ * Errors: NULL pointers, rows < 0, K <= 0, K % 8 != 0, G not a power of two
+ * in [1, 256], K % G != 0, misaligned pointers.
+ * ------------------------------------------------------------------------- */
+qa_status qa_hadamard_quant_int4_asym(const void* X_f16, int64_t rows, int64_t K, int32_t G, uint32_t* packed,
+                                      float* s, int32_t* z, void* stream);
+
+/* Column terms of a per-group int4 weight (offline, with the weight):
+ *   c[n] = fl32(sum_g s_w[n][g] * sum_{k in group g} qw[n][k])   (fp64, g ascending)
+ *   Wp u32 [N x K/8], s_w f32 [N x K/G]; c f32 [N]
+ * Errors: NULL pointers, N < 0, K <= 0, G not a power of two in [8, 256],
+ * K % G != 0, misaligned pointers. */
+qa_status qa_w4_column_terms(const uint32_t* Wp, const float* s_w, int64_t N, int64_t K, int32_t G, float* c,
+                             void* stream);
+
+/* ---------------------------------------------------------------------------
+ * W4A4 linear with zero-point activations  [Scholia-IQ §6, §6.2, §7.3;
+ * GroupRot §5.2, §5.4]
+ *
+ *   (Xp, s_x, z_x) = qa_hadamard_quant_int4_asym(X, G)   (on device)
+ *   out[m][n] = s_x[m] * sum_g s_w[n][g] * sum_{k in g} (q[m][k] - z_x[m]) qw[n][k]
+ *             = s_x[m] * (sum_g s_w[n][g] sum_{k in g} (q - 8) qw - (z_x[m] - 8) c_w[n])
+ *   Wp, s_w  the offline W4A4 weight (qa_hadamard_quant_int4, PER_GROUP)
+ *   c_w      qa_w4_column_terms(Wp, s_w, G): f32 [N]
+ *   out      [M x N] of out_dtype
+ *   workspace  qa_qlinear_w4a4_asym_workspace(M, K) bytes (any content)
+ * Errors: NULL pointers, M < 0, N < 0, K <= 0, G not in {64, 128, 256},
+ * K % G != 0, misaligned pointers, bad out_dtype, small workspace.
+ * ------------------------------------------------------------------------- */
+size_t qa_qlinear_w4a4_asym_workspace(int64_t M, int64_t K);
+qa_status qa_qlinear_w4a4_asym(const void* X_f16, int64_t M, int64_t K, const uint32_t* Wp, const float* s_w,
+                               const float* c_w, int64_t N, int32_t G, void* out, qa_dtype out_dtype,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Asymmetric (zero-point) row quantization  [Scholia-IQ §6: q = round(x/s) +
  * z, x^ = s (q - z), z the integer that stands for real 0; §6.2: the grid
  * shifted onto the data's range, q clipped to [q_min, q_max]]

@@ -180,6 +180,38 @@ def test_w4a8_argument_errors():
     assert g(MIS, B, 4, 512, 4, 128, OUT, None) == ALIGN
 
 
+def test_w4a4_asym_argument_errors():
+    h = qa.lib().qa_hadamard_quant_int4_asym
+    assert h(None, 4, 256, 128, B, OUT, WS, None) == NULL
+    assert h(A, 4, 256, 128, B, OUT, None, None) == NULL
+    assert h(A, 4, 256, 96, B, OUT, WS, None) == SHAPE
+    assert h(A, 4, 200, 16, B, OUT, WS, None) == SHAPE
+    assert h(MIS, 4, 256, 128, B, OUT, WS, None) == ALIGN
+    assert h(A, 0, 256, 128, B, OUT, WS, None) == OK
+    c = qa.lib().qa_w4_column_terms
+    assert c(A, B, 16, 512, 4, OUT, None) == SHAPE                     # G < 8
+    assert c(A, B, 16, 500, 128, OUT, None) == SHAPE
+    assert c(None, B, 16, 512, 128, OUT, None) == NULL
+    assert c(A, B, 0, 512, 128, None, None) == OK
+    f = qa.lib().qa_qlinear_w4a4_asym
+    base = [A, 16, 512, B, OUT, OUT, 32, 128, OUT, 0, WS, 1 << 30, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+    assert call(0, None) == NULL
+    assert call(5, None) == NULL                                      # c_w
+    assert call(7, 32) == SHAPE
+    assert call(2, 320) == SHAPE
+    assert call(3, MIS) == ALIGN
+    assert call(9, 7) == VALUE
+    assert call(11, 16 * 256) == WORKSPACE                            # codes fit, scales and zero-points do not
+    assert call(1, 0) == OK
+    for M, K in [(1, 64), (2048, 4096)]:
+        assert qa.lib().qa_qlinear_w4a4_asym_workspace(M, K) >= M * K // 2 + 8 * M
+
+
 def test_gemm_i8_argument_errors():
     f = qa.lib().qa_gemm_i8_i32
     assert f(None, B, 4, 64, 4, OUT, None) == NULL
