@@ -1190,32 +1190,43 @@ hipError_t launch_hadamard_quant_i4(const uint16_t* X, int64_t rows, int64_t K, 
     return hipGetLastError();
 }
 
-// Column terms of the zero-point correction, one thread per output channel
-// (an offline computation on the weight): the group sums of the signed
-// nibbles are exact integers, each product with the fp32 group scale is exact
-// in fp64, and the products are added over g ascending.
+// Column terms of the zero-point correction (an offline computation on the
+// weight), one wave per output channel: lane l sums the signed nibbles of
+// groups l, l + 64, ... (exact integers; a group's words are read by one
+// lane, consecutive lanes reading consecutive groups), and lane 0 adds the
+// products with the fp32 group scales, each exact in fp64, over g ascending.
 __global__ __launch_bounds__(256) void k_w4_column_terms(const uint32_t* __restrict__ Wp, const float* __restrict__ s_w,
                                                          int64_t N, int64_t K, int G, float* __restrict__ c) {
-    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (n >= N) return;
+    __shared__ int gsum[4][512];
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int64_t n = (int64_t)blockIdx.x * 4 + wave;
     const int64_t words = K / 8, ng = K / G, wpg = G / 8;
+    if (n >= N) return;
     const uint32_t* w = Wp + n * words;
     double acc = 0.0;
-    for (int64_t g = 0; g < ng; ++g) {
-        int sum = 0;
-        for (int64_t i = g * wpg; i < (g + 1) * wpg; ++i) {
-            const uint32_t v = w[i];
+    for (int64_t g0 = 0; g0 < ng; g0 += 512) {
+        const int64_t gn = ng - g0 < 512 ? ng - g0 : 512;
+        for (int64_t g = lane; g < gn; g += 64) {
+            int sum = 0;
+            for (int64_t i = (g0 + g) * wpg; i < (g0 + g + 1) * wpg; ++i) {
+                const uint32_t v = w[i];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) sum += (int)(v << (28 - 4 * j)) >> 28;    // nibble j, sign-extended
+                for (int j = 0; j < 8; ++j) sum += (int)(v << (28 - 4 * j)) >> 28;    // nibble j, sign-extended
+            }
+            gsum[wave][g] = sum;
         }
-        acc += (double)s_w[n * ng + g] * (double)sum;
+        __builtin_amdgcn_s_waitcnt(0xC07F);                 // this wave's LDS writes (lgkmcnt(0))
+        __builtin_amdgcn_wave_barrier();
+        if (lane == 0)
+            for (int64_t g = 0; g < gn; ++g) acc += (double)s_w[n * ng + g0 + g] * (double)gsum[wave][g];
+        __builtin_amdgcn_wave_barrier();
     }
-    c[n] = (float)acc;
+    if (lane == 0) c[n] = (float)acc;
 }
 
 hipError_t launch_w4_column_terms(const uint32_t* Wp, const float* s_w, int64_t N, int64_t K, int G, float* c,
                                   hipStream_t st) {
-    hipLaunchKernelGGL(k_w4_column_terms, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st, Wp, s_w, N, K, G, c);
+    hipLaunchKernelGGL(k_w4_column_terms, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, st, Wp, s_w, N, K, G, c);
     return hipGetLastError();
 }
 
