@@ -754,6 +754,17 @@ __device__ __forceinline__ v4i unpack_hi_nibbles(u32x2 w) {
 
 constexpr int W4_SW_LDS = 4096;                 // floats of per-group weight scales kept in LDS
 
+// Slot of column c's scale for group g in a block's [group][column] table of
+// per-group weight scales: the columns are XOR-swizzled in 4-float quads by
+// the group, so the fill (consecutive threads take consecutive groups of one
+// column) spreads over the LDS banks and quads stay contiguous for 16-byte reads.
+template <int BN>
+__device__ __forceinline__ int sw_slot(int g, int c) {
+    static_assert(BN % 64 == 0, "column quads to swizzle");
+    constexpr int MASK = (BN / 4 < 32 ? BN / 4 : 32) - 1;
+    return g * BN + (c ^ ((g & MASK) << 2));
+}
+
 template <class C, int G, bool STORE_ACC>
 __global__ __launch_bounds__(C::THREADS) void k_gemm_w4a4(const uint32_t* __restrict__ Xp,
                                                           const float* __restrict__ s_x,
@@ -783,9 +794,20 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_w4a4(const uint32_t* __rest
     const bool sw_in_lds = !STORE_ACC && ng * C::BN <= W4_SW_LDS;
     const rsrc_t rsw = make_rsrc(s_w + (STORE_ACC ? 0 : n0 * ng), STORE_ACC ? 0 : (N - n0) * ng * 4);
     if (sw_in_lds) {
-        for (int t = threadIdx.x; t < ng * C::BN; t += C::THREADS) {
-            const int cc = t / (int)ng, g = t - cc * (int)ng;        // coalesced over g
-            sws[g * C::BN + cc] = __builtin_bit_cast(float, bload4(rsw, (uint32_t)t * 4)) * 0x1p-8f;
+        // all loads issued before the first write: one memory latency, not one per element
+        constexpr int PER = (W4_SW_LDS + C::THREADS - 1) / C::THREADS;
+        const int total = (int)ng * C::BN;
+        float v[PER];
+#pragma unroll
+        for (int it = 0; it < PER; ++it) {
+            const int t = threadIdx.x + it * C::THREADS;             // coalesced over g
+            v[it] = __builtin_bit_cast(float, bload4(rsw, (uint32_t)(t < total ? t : 0) * 4));
+        }
+#pragma unroll
+        for (int it = 0; it < PER; ++it) {
+            const int t = threadIdx.x + it * C::THREADS;
+            const int cc = t / (int)ng, g = t - cc * (int)ng;
+            if (t < total) sws[sw_slot<C::BN>(g, cc)] = v[it] * 0x1p-8f;
         }
     }
 
@@ -860,7 +882,7 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_w4a4(const uint32_t* __rest
                         float swj[C::FN];
 #pragma unroll
                         for (int j = 0; j < C::FN; ++j)
-                            swj[j] = sw_in_lds ? sws[g * C::BN + ccol[j]]
+                            swj[j] = sw_in_lds ? sws[sw_slot<C::BN>(g, ccol[j])]
                                                : __builtin_bit_cast(float, bload4(rsw, (uint32_t)(ccol[j] * ng + g) * 4)) *
                                                      0x1p-8f;
 #pragma unroll
@@ -908,8 +930,11 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_w4a4(const uint32_t* __rest
 // per row and stage (eight 16-byte chunks, XOR-swizzled by row % 8), and each
 // fragment's bytes are permuted (v_perm_b32) into the even/odd element order
 // the weight's nibble unpack produces, so both operands share one k order;
-// the products then carry 16 (weight in the high nibble) instead of 256.  A lane's fragment of one step is 8 packed bytes (row l % 16, bytes
-// 32 s + 8 (l / 16) of the stage), unpacked into the high nibbles.  The block's
+// the products then carry 16 (weight in the high nibble) instead of 256.  A
+// lane's fragment of one step is 8 packed bytes of row l % 16, unpacked into
+// the high nibbles: bytes 32 s + 8 (l / 16) of the stage for G = 64, and for
+// G >= 128 half s of the 16 bytes 16 (l / 16) .. + 15, read once per stage
+// (one 16-byte LDS read instead of two 8-byte ones, which conflict).  The block's
 // per-group weight scales (x 2^-8) are staged in LDS as [group][column] when
 // they fit.  Operands enter the MFMA in the transposed order of the int8 path
 // (lane l, element e: row l % 16, column 4 (l / 16) + e of a fragment).
@@ -934,7 +959,7 @@ struct W4Stage {
 // ZX: zero-point activations (codes stored as q - 8, zero-points z_x in
 // [0, 15]): the epilogue subtracts (z_x[m] - 8) c_w[n] before the row scale,
 // c_w[n] = sum_g s_w[n][g] sum_{k in g} qw[n][k] (launch_w4_column_terms).
-template <class C, int G, bool STORE_ACC, bool A8 = false, bool ZX = false>
+template <class C, int G, bool STORE_ACC, bool A8, bool ZX, bool SWL>
 __device__ __forceinline__ void w4a4_dma_body(const uint32_t* __restrict__ Xp, const float* __restrict__ s_x,
                                               const uint32_t* __restrict__ Wp, const float* __restrict__ s_w,
                                               int64_t M, int64_t K, int64_t N, void* __restrict__ out,
@@ -942,6 +967,11 @@ __device__ __forceinline__ void w4a4_dma_body(const uint32_t* __restrict__ Xp, c
                                               const int32_t* __restrict__ z_x = nullptr,
                                               const float* __restrict__ c_w = nullptr) {
     constexpr int SPG = G / 64;                       // MFMA steps per group
+    // G >= 128: K % G == 0 makes every stage whole, and both steps of a stage
+    // fall in one group, so the stage's k order may differ from the packed
+    // order as long as both operands take the same one (int32 sums are exact).
+    // (The per-group stores of STORE_ACC leave no registers for it.)
+    constexpr bool WIDE = SPG >= 2 && !STORE_ACC;
     using S = W4Stage<C, A8>;
     constexpr float SCALE = A8 ? 0x1p-4f : 0x1p-8f;   // the nibble shift(s) in each product
     int tm, tn;
@@ -955,15 +985,10 @@ __device__ __forceinline__ void w4a4_dma_body(const uint32_t* __restrict__ Xp, c
     const rsrc_t rsa = make_rsrc(reinterpret_cast<const uint8_t*>(Xp) + m0 * abytes, (M - m0) * abytes);
     const rsrc_t rsb = make_rsrc(reinterpret_cast<const uint8_t*>(Wp) + n0 * kbytes, (N - n0) * kbytes);
 
-    const bool sw_in_lds = !STORE_ACC && ng * C::BN <= W4D_SW_LDS;
+    // SWL: the block's scales staged in LDS (the launcher checks that they fit)
+    static_assert(!(SWL && STORE_ACC), "no scales with STORE_ACC");
+    constexpr bool sw_in_lds = SWL;
     const rsrc_t rsw = make_rsrc(s_w + (STORE_ACC ? 0 : n0 * ng), STORE_ACC ? 0 : (N - n0) * ng * 4);
-    if (sw_in_lds) {
-        for (int t = threadIdx.x; t < ng * C::BN; t += C::THREADS) {
-            const int cc = t / (int)ng, g = t - cc * (int)ng;           // coalesced over g
-            sws[g * C::BN + cc] = __builtin_bit_cast(float, bload4(rsw, (uint32_t)t * 4)) * SCALE;
-        }
-    }
-    __syncthreads();
 
     uint32_t oa[S::A_INS], ca[S::A_INS], ob[C::B_INS], cb[C::B_INS];
 #pragma unroll
@@ -1016,6 +1041,25 @@ __device__ __forceinline__ void w4a4_dma_body(const uint32_t* __restrict__ Xp, c
     issue(0);
     if (nk > 1) issue(1);
     if (nk > 2) issue(2);
+    // the block's scales, staged while the first stages' loads are in flight
+    if constexpr (sw_in_lds) {
+        // all loads issued before the first write: one memory latency, not one per element
+        constexpr int PER = W4D_SW_LDS / C::THREADS;
+        const int total = (int)ng * C::BN;
+        float v[PER];
+#pragma unroll
+        for (int it = 0; it < PER; ++it) {
+            const int t = threadIdx.x + it * C::THREADS;                // coalesced over g
+            v[it] = __builtin_bit_cast(float, bload4(rsw, (uint32_t)(t < total ? t : 0) * 4));
+        }
+#pragma unroll
+        for (int it = 0; it < PER; ++it) {
+            const int t = threadIdx.x + it * C::THREADS;
+            const int cc = t / (int)ng, g = t - cc * (int)ng;
+            if (t < total) sws[sw_slot<C::BN>(g, cc)] = v[it] * SCALE;
+        }
+    }
+    __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
         const int ahead = (kt + 2 < nk - 1 ? kt + 2 : nk - 1) - kt;   // stages issued after kt
         if (ahead >= 2)
@@ -1028,10 +1072,23 @@ __device__ __forceinline__ void w4a4_dma_body(const uint32_t* __restrict__ Xp, c
         if (kt + 3 < nk) issue(kt + 3);
         const uint8_t* sa = smem + (kt % C::STAGES) * S::STAGE;
         const uint8_t* sb = sa + S::LDS_A;
+        // WIDE: one 16-byte read per packed fragment covers the stage; step
+        // s2 takes its 8-byte half s2 (elements 32 (l / 16) + 16 s2 .. + 15).
+        u32x4 wa[WIDE && !A8 ? C::FM : 1], wb[WIDE ? C::FN : 1];
+        if constexpr (WIDE) {
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+                wb[j] = *reinterpret_cast<const u32x4*>(sb + swz64(wn * C::TN + j * 16 + (lane & 15), lane >> 4));
+            if constexpr (!A8) {
+#pragma unroll
+                for (int i = 0; i < C::FM; ++i)
+                    wa[i] = *reinterpret_cast<const u32x4*>(sa + swz64(wm * C::TM + i * 16 + (lane & 15), lane >> 4));
+            }
+        }
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
             const int step = 2 * kt + s2;
-            if (step >= nsteps) break;
+            if (!WIDE && step >= nsteps) break;
             const int byte = s2 * 32 + (lane >> 4) * 8;
             const int c = byte >> 4, within = byte & 15;
             v4i fa[C::FM], fb[C::FN];
@@ -1039,16 +1096,23 @@ __device__ __forceinline__ void w4a4_dma_body(const uint32_t* __restrict__ Xp, c
             for (int i = 0; i < C::FM; ++i) {
                 const int r = wm * C::TM + i * 16 + (lane & 15);
                 if constexpr (A8) {
-                    const int c8 = 4 * s2 + (lane >> 4);                  // elements 16 c8 .. 16 c8 + 15
+                    // elements 16 c8 .. 16 c8 + 15, the ones the weight fragment holds
+                    const int c8 = WIDE ? 2 * (lane >> 4) + s2 : 4 * s2 + (lane >> 4);
                     fa[i] = perm_even_odd(*reinterpret_cast<const u32x4*>(sa + r * 128 + ((c8 ^ (r & 7)) * 16)));
+                } else if constexpr (WIDE) {
+                    fa[i] = unpack_hi_nibbles(u32x2{wa[i][2 * s2], wa[i][2 * s2 + 1]});
                 } else {
                     fa[i] = unpack_hi_nibbles(*reinterpret_cast<const u32x2*>(sa + swz64(r, c) + within));
                 }
             }
 #pragma unroll
-            for (int j = 0; j < C::FN; ++j)
-                fb[j] = unpack_hi_nibbles(
-                    *reinterpret_cast<const u32x2*>(sb + swz64(wn * C::TN + j * 16 + (lane & 15), c) + within));
+            for (int j = 0; j < C::FN; ++j) {
+                if constexpr (WIDE)
+                    fb[j] = unpack_hi_nibbles(u32x2{wb[j][2 * s2], wb[j][2 * s2 + 1]});
+                else
+                    fb[j] = unpack_hi_nibbles(
+                        *reinterpret_cast<const u32x2*>(sb + swz64(wn * C::TN + j * 16 + (lane & 15), c) + within));
+            }
             // A group of at most two steps starts at a step known at compile
             // time (step = 2 kt + s2): its first MFMA takes a zero accumulator
             // instead of clearing the accumulators after each dequant.
@@ -1081,8 +1145,8 @@ __device__ __forceinline__ void w4a4_dma_body(const uint32_t* __restrict__ Xp, c
 #pragma unroll
                     for (int j = 0; j < C::FN; ++j) {
                         const int cl = wn * C::TN + j * 16 + 4 * (lane >> 4);   // block-local column
-                        if (sw_in_lds) {
-                            swj[j] = *reinterpret_cast<const v4f*>(sws + g * C::BN + cl);
+                        if constexpr (sw_in_lds) {
+                            swj[j] = *reinterpret_cast<const v4f*>(sws + sw_slot<C::BN>(g, cl));
                         } else {
 #pragma unroll
                             for (int e = 0; e < 4; ++e)
@@ -1103,10 +1167,18 @@ __device__ __forceinline__ void w4a4_dma_body(const uint32_t* __restrict__ Xp, c
             }
         }
     }
+    // the epilogue's row and column terms, loaded together ahead of their use
+    float sx[C::FM], zx[C::FM];
+    v4f cw[ZX ? C::FN : 1];
     if constexpr (!STORE_ACC) {
         const rsrc_t rsx = make_rsrc(s_x + m0, (M - m0) * 4);
-        const bool vec = (N & 3) == 0;
-        v4f cw[ZX ? C::FN : 1];
+        const rsrc_t rzx = make_rsrc(ZX ? z_x + m0 : nullptr, ZX ? (M - m0) * 4 : 0);
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) {
+            const int rl = wm * C::TM + i * 16 + (lane & 15);
+            sx[i] = __builtin_bit_cast(float, bload4(rsx, (uint32_t)rl * 4));
+            zx[i] = ZX ? (float)((int32_t)bload4(rzx, (uint32_t)rl * 4) - 8) : 0.0f;
+        }
         if constexpr (ZX) {
             const rsrc_t rcw = make_rsrc(c_w + n0, (N - n0) * 4);
 #pragma unroll
@@ -1116,12 +1188,12 @@ __device__ __forceinline__ void w4a4_dma_body(const uint32_t* __restrict__ Xp, c
                 for (int e = 0; e < 4; ++e) cw[j][e] = __builtin_bit_cast(float, bload4(rcw, (uint32_t)(cl + e) * 4));
             }
         }
-        const rsrc_t rzx = make_rsrc(ZX ? z_x + m0 : nullptr, ZX ? (M - m0) * 4 : 0);
+    }
+    if constexpr (!STORE_ACC) {
+        const bool vec = (N & 3) == 0;
 #pragma unroll
         for (int i = 0; i < C::FM; ++i) {
             const int rl = wm * C::TM + i * 16 + (lane & 15);
-            const float sx = __builtin_bit_cast(float, bload4(rsx, (uint32_t)rl * 4));
-            const float zx = ZX ? (float)((int32_t)bload4(rzx, (uint32_t)rl * 4) - 8) : 0.0f;
             const int64_t row = m0 + rl;
 #pragma unroll
             for (int j = 0; j < C::FN; ++j) {
@@ -1130,9 +1202,9 @@ __device__ __forceinline__ void w4a4_dma_body(const uint32_t* __restrict__ Xp, c
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     if constexpr (ZX)
-                        o[e] = sx * __builtin_fmaf(-zx, cw[j][e], f[i][j][e]);
+                        o[e] = sx[i] * __builtin_fmaf(-zx[i], cw[j][e], f[i][j][e]);
                     else
-                        o[e] = sx * f[i][j][e];
+                        o[e] = sx[i] * f[i][j][e];
                 }
                 if (row < M && col < N) store_out4(out, out_dtype, row * N + col, o, vec, (int)(N - col < 4 ? N - col : 4));
             }
@@ -1140,20 +1212,24 @@ __device__ __forceinline__ void w4a4_dma_body(const uint32_t* __restrict__ Xp, c
     }
 }
 
-template <class C, int G, bool STORE_ACC>
+template <class C, int G, bool STORE_ACC, bool SWL>
 __global__ __launch_bounds__(C::THREADS) void k_gemm_w4a4_dma(const uint32_t* __restrict__ Xp,
                                                               const float* __restrict__ s_x,
                                                               const uint32_t* __restrict__ Wp,
                                                               const float* __restrict__ s_w, int64_t M, int64_t K,
                                                               int64_t N, void* __restrict__ out, int out_dtype,
                                                               int tiles_m, int tiles_n) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
-    __shared__ __attribute__((aligned(16))) float sws[STORE_ACC ? 4 : W4D_SW_LDS];
-    w4a4_dma_body<C, G, STORE_ACC>(Xp, s_x, Wp, s_w, M, K, N, out, out_dtype, tiles_m, tiles_n, smem, sws);
+    // one LDS object, the stages and then the scale table: with a second
+    // __shared__ array the compiler makes each fragment read wait for every
+    // stage load in flight, which serializes the pipeline
+    __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS + (SWL ? 4 * W4D_SW_LDS : 0)];
+    float* sws = reinterpret_cast<float*>(smem + C::LDS);
+    w4a4_dma_body<C, G, STORE_ACC, false, false, SWL>(Xp, s_x, Wp, s_w, M, K, N, out, out_dtype, tiles_m, tiles_n,
+                                                      smem, sws);
 }
 
 // W4A4 with zero-point activations.
-template <class C, int G>
+template <class C, int G, bool SWL>
 __global__ __launch_bounds__(C::THREADS) void k_gemm_w4a4z_dma(const uint32_t* __restrict__ Xp,
                                                                const float* __restrict__ s_x,
                                                                const int32_t* __restrict__ z_x,
@@ -1162,27 +1238,36 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_w4a4z_dma(const uint32_t* _
                                                                const float* __restrict__ c_w, int64_t M, int64_t K,
                                                                int64_t N, void* __restrict__ out, int out_dtype,
                                                                int tiles_m, int tiles_n) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
-    __shared__ __attribute__((aligned(16))) float sws[W4D_SW_LDS];
-    w4a4_dma_body<C, G, false, false, true>(Xp, s_x, Wp, s_w, M, K, N, out, out_dtype, tiles_m, tiles_n, smem, sws,
-                                            z_x, c_w);
+    // one LDS object, the stages and then the scale table: with a second
+    // __shared__ array the compiler makes each fragment read wait for every
+    // stage load in flight, which serializes the pipeline
+    __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS + (SWL ? 4 * W4D_SW_LDS : 0)];
+    float* sws = reinterpret_cast<float*>(smem + C::LDS);
+    w4a4_dma_body<C, G, false, false, true, SWL>(Xp, s_x, Wp, s_w, M, K, N, out, out_dtype, tiles_m, tiles_n, smem,
+                                                 sws, z_x, c_w);
 }
 
 // W4A8: int8 activation codes Xq [M x K] against the packed int4 weight.
-template <class C, int G, bool STORE_ACC>
+template <class C, int G, bool STORE_ACC, bool SWL>
 __global__ __launch_bounds__(C::THREADS) void k_gemm_w4a8_dma(const int8_t* __restrict__ Xq,
                                                               const float* __restrict__ s_x,
                                                               const uint32_t* __restrict__ Wp,
                                                               const float* __restrict__ s_w, int64_t M, int64_t K,
                                                               int64_t N, void* __restrict__ out, int out_dtype,
                                                               int tiles_m, int tiles_n) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[W4Stage<C, true>::LDS];
-    __shared__ __attribute__((aligned(16))) float sws[STORE_ACC ? 4 : W4D_SW_LDS];
-    w4a4_dma_body<C, G, STORE_ACC, true>(reinterpret_cast<const uint32_t*>(Xq), s_x, Wp, s_w, M, K, N, out,
-                                         out_dtype, tiles_m, tiles_n, smem, sws);
+    // one LDS object, the stages and then the scale table: with a second
+    // __shared__ array the compiler makes each fragment read wait for every
+    // stage load in flight, which serializes the pipeline
+    __shared__ __attribute__((aligned(16))) uint8_t smem[W4Stage<C, true>::LDS + (SWL ? 4 * W4D_SW_LDS : 0)];
+    float* sws = reinterpret_cast<float*>(smem + W4Stage<C, true>::LDS);
+    w4a4_dma_body<C, G, STORE_ACC, true, false, SWL>(reinterpret_cast<const uint32_t*>(Xq), s_x, Wp, s_w, M, K, N,
+                                                     out, out_dtype, tiles_m, tiles_n, smem, sws);
 }
 
 using CfgW4 = CfgD<128, 256, 2, 4>;     // 8 waves, wave tile 64 x 64, LDS-DMA stages
+
+// Whether a CfgW4 block's per-group weight scales fit the LDS table.
+static bool w4_scales_fit(int64_t K, int G) { return (K / G) * CfgW4::BN <= W4D_SW_LDS; }
 
 template <int G, bool STORE_ACC>
 static void w4a4_dispatch(const uint32_t* Xp, const float* s_x, const uint32_t* Wp, const float* s_w, int64_t M,
@@ -1190,8 +1275,12 @@ static void w4a4_dispatch(const uint32_t* Xp, const float* s_x, const uint32_t* 
     int tm, tn;
     if (((M + 127) / 128) * ((N + 255) / 256) >= 256) {
         dim3 g = grid_of<CfgW4>(M, N, tm, tn);
-        hipLaunchKernelGGL((k_gemm_w4a4_dma<CfgW4, G, STORE_ACC>), g, dim3(CfgW4::THREADS), 0, st, Xp, s_x, Wp, s_w,
-                           M, K, N, out, out_dtype, tm, tn);
+        if (!STORE_ACC && w4_scales_fit(K, G))
+            hipLaunchKernelGGL((k_gemm_w4a4_dma<CfgW4, G, STORE_ACC, !STORE_ACC>), g, dim3(CfgW4::THREADS), 0, st, Xp,
+                               s_x, Wp, s_w, M, K, N, out, out_dtype, tm, tn);
+        else
+            hipLaunchKernelGGL((k_gemm_w4a4_dma<CfgW4, G, STORE_ACC, false>), g, dim3(CfgW4::THREADS), 0, st, Xp, s_x,
+                               Wp, s_w, M, K, N, out, out_dtype, tm, tn);
     } else if (((M + 127) / 128) * ((N + 127) / 128) >= 256) {
         dim3 g = grid_of<CfgMidR>(M, N, tm, tn);
         hipLaunchKernelGGL((k_gemm_w4a4<CfgMidR, G, STORE_ACC>), g, dim3(CfgMidR::THREADS), 0, st, Xp, s_x, Wp, s_w,
@@ -1220,8 +1309,12 @@ static void w4a4z_dispatch(const uint32_t* Xp, const float* s_x, const int32_t* 
                            int out_dtype, hipStream_t st) {
     int tm, tn;
     dim3 g = grid_of<CfgW4>(M, N, tm, tn);
-    hipLaunchKernelGGL((k_gemm_w4a4z_dma<CfgW4, G>), g, dim3(CfgW4::THREADS), 0, st, Xp, s_x, z_x, Wp, s_w, c_w, M,
-                       K, N, out, out_dtype, tm, tn);
+    if (w4_scales_fit(K, G))
+        hipLaunchKernelGGL((k_gemm_w4a4z_dma<CfgW4, G, true>), g, dim3(CfgW4::THREADS), 0, st, Xp, s_x, z_x, Wp, s_w,
+                           c_w, M, K, N, out, out_dtype, tm, tn);
+    else
+        hipLaunchKernelGGL((k_gemm_w4a4z_dma<CfgW4, G, false>), g, dim3(CfgW4::THREADS), 0, st, Xp, s_x, z_x, Wp, s_w,
+                           c_w, M, K, N, out, out_dtype, tm, tn);
 }
 
 hipError_t launch_gemm_w4a4_asym(const uint32_t* Xp, const float* s_x, const int32_t* z_x, const uint32_t* Wp,
@@ -1241,8 +1334,12 @@ static void w4a8_dispatch(const int8_t* Xq, const float* s_x, const uint32_t* Wp
                           int64_t K, int64_t N, void* out, int out_dtype, hipStream_t st) {
     int tm, tn;
     dim3 g = grid_of<CfgW4>(M, N, tm, tn);
-    hipLaunchKernelGGL((k_gemm_w4a8_dma<CfgW4, G, STORE_ACC>), g, dim3(CfgW4::THREADS), 0, st, Xq, s_x, Wp, s_w, M,
-                       K, N, out, out_dtype, tm, tn);
+    if (!STORE_ACC && w4_scales_fit(K, G))
+        hipLaunchKernelGGL((k_gemm_w4a8_dma<CfgW4, G, STORE_ACC, !STORE_ACC>), g, dim3(CfgW4::THREADS), 0, st, Xq,
+                           s_x, Wp, s_w, M, K, N, out, out_dtype, tm, tn);
+    else
+        hipLaunchKernelGGL((k_gemm_w4a8_dma<CfgW4, G, STORE_ACC, false>), g, dim3(CfgW4::THREADS), 0, st, Xq, s_x, Wp,
+                           s_w, M, K, N, out, out_dtype, tm, tn);
 }
 
 hipError_t launch_gemm_w4a8(const int8_t* Xq, const float* s_x, const uint32_t* Wp, const float* s_w, int64_t M,

@@ -14,6 +14,11 @@ usage: python profile_counters.py --kernel k_decode_mixed \\
            --source bit_quantized_linear_int8_amd/csrc/k_decode.hip \\
            --fetch F.db --write W.db --copy-fetch CF.db --copy-write CW.db \\
            [--copy-bytes 1073741824] [--workload decode_mixed] [--command "..."]
+
+       python profile_counters.py --mfma RUN.db [RUN.db ...]
+           matrix-core use per GEMM kernel from runs of SQ_VALU_MFMA_BUSY_CYCLES,
+           GRBM_GUI_ACTIVE, SQ_INSTS_VALU_MFMA_MOPS_I8, SQ_LDS_BANK_CONFLICT and
+           SQ_LDS_IDX_ACTIVE (median over dispatches); prints a table, writes nothing
 """
 from __future__ import annotations
 
@@ -58,7 +63,35 @@ def copy_value(db_path, counter):
     return max(max(v) for v in rows.values())
 
 
+# MI355X: 8 XCDs of 32 CUs x 4 SIMDs.  GRBM_GUI_ACTIVE, summed over its
+# instances, counts the kernel's active cycles once per XCD.
+XCDS, SIMDS = 8, 1024
+
+
+def mfma_table(paths):
+    counters = ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU_MFMA_MOPS_I8",
+                "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE")
+    print("%-58s %6s %10s %9s %12s %9s" % ("kernel", "disp", "cycles", "mfma_busy", "int8_ops", "lds_confl"))
+    for path in paths:
+        med = {c: per_dispatch(path, c) for c in counters}
+        for k in sorted(med["SQ_VALU_MFMA_BUSY_CYCLES"]):
+            v = {c: statistics.median(med[c][k]) for c in counters if k in med[c]}
+            if len(v) < len(counters) or v["SQ_INSTS_VALU_MFMA_MOPS_I8"] == 0:
+                continue
+            cycles = v["GRBM_GUI_ACTIVE"] / XCDS
+            busy = v["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * SIMDS)
+            ops = v["SQ_INSTS_VALU_MFMA_MOPS_I8"] * 512
+            conf = v["SQ_LDS_BANK_CONFLICT"] / max(v["SQ_LDS_IDX_ACTIVE"], 1.0)
+            name = k.split("(")[0].replace("void ", "")
+            print("%-58s %6d %10.0f %8.1f%% %12.4g %8.1f%%" % (name[:58], len(med["GRBM_GUI_ACTIVE"][k]), cycles,
+                                                          100 * busy, ops, 100 * conf))
+
+
 def main():
+    import sys
+    if len(sys.argv) > 1 and sys.argv[1] == "--mfma":
+        mfma_table(sys.argv[2:])
+        return
     p = argparse.ArgumentParser()
     p.add_argument("--kernel", required=True)
     p.add_argument("--source", required=True, help="kernel source, relative to the repository root")
