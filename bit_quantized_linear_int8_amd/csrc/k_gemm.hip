@@ -941,6 +941,11 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_w4a4(const uint32_t* __rest
 // ---------------------------------------------------------------------------
 constexpr int W4D_SW_LDS = 8192;                 // floats of per-group weight scales kept in LDS
 
+// Chunk swizzle of 128-byte LDS rows (W4A8 activation stages): a 16-byte
+// fragment read takes one chunk of 16 consecutive rows, and rows r and r + 8
+// (also two rows apart in a 256-byte bank window) get different chunks.
+__device__ __forceinline__ int swz128(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
 // The even/odd order of unpack_hi_nibbles for 16 int8 codes read in order.
 __device__ __forceinline__ v4i perm_even_odd(const u32x4& a) {
     return v4i{(int)__builtin_amdgcn_perm(a[1], a[0], 0x06040200u), (int)__builtin_amdgcn_perm(a[1], a[0], 0x07050301u),
@@ -997,7 +1002,7 @@ __device__ __forceinline__ void w4a4_dma_body(const uint32_t* __restrict__ Xp, c
         int r, c;
         if constexpr (A8) {
             r = P >> 3;
-            c = (P & 7) ^ (r & 7);
+            c = (P & 7) ^ swz128(r);
         } else {
             r = P >> 2;
             c = (P & 3) ^ ((r >> 1) & 3);
@@ -1098,7 +1103,7 @@ __device__ __forceinline__ void w4a4_dma_body(const uint32_t* __restrict__ Xp, c
                 if constexpr (A8) {
                     // elements 16 c8 .. 16 c8 + 15, the ones the weight fragment holds
                     const int c8 = WIDE ? 2 * (lane >> 4) + s2 : 4 * s2 + (lane >> 4);
-                    fa[i] = perm_even_odd(*reinterpret_cast<const u32x4*>(sa + r * 128 + ((c8 ^ (r & 7)) * 16)));
+                    fa[i] = perm_even_odd(*reinterpret_cast<const u32x4*>(sa + r * 128 + ((c8 ^ swz128(r)) * 16)));
                 } else if constexpr (WIDE) {
                     fa[i] = unpack_hi_nibbles(u32x2{wa[i][2 * s2], wa[i][2 * s2 + 1]});
                 } else {
