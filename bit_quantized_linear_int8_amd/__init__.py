@@ -30,7 +30,8 @@ EXPORTS = (
     "qa_quantize_rowwise_int8_asym", "qa_int8_row_sums", "qa_qlinear_int8_asym_workspace", "qa_qlinear_int8_asym",
     "qa_col_absmax_workspace", "qa_col_absmax", "qa_smooth_factors", "qa_quantize_smooth_int8",
     "qa_qlinear_int8_smooth_workspace", "qa_qlinear_int8_smooth",
-    "qa_hadamard_quant_int4", "qa_kron_quant_int4", "qa_qlinear_kron_w4a4_workspace", "qa_qlinear_kron_w4a4",
+    "qa_hadamard_quant_int4", "qa_kron_sizes", "qa_kron_quant_int4", "qa_qlinear_kron_w4a4_workspace",
+    "qa_qlinear_kron_w4a4",
     "qa_qlinear_w4a4_workspace", "qa_qlinear_w4a4",
     "qa_hadamard_quant_int8", "qa_qlinear_w4a8_workspace", "qa_qlinear_w4a8",
     "qa_hadamard_quant_int4_asym", "qa_w4_column_terms", "qa_qlinear_w4a4_asym_workspace", "qa_qlinear_w4a4_asym",
@@ -81,6 +82,7 @@ def lib() -> ctypes.CDLL:
             "qa_qlinear_int8_smooth_workspace": (SZ, [I64, I64]),
             "qa_qlinear_int8_smooth": (S, [P, I64, I64, P, S, P, P, I64, P, S, P, SZ, P]),
             "qa_hadamard_quant_int4": (S, [P, I64, I64, I32, S, I32, I32, P, P, P]),
+            "qa_kron_sizes": (S, [I64, P, P, P]),
             "qa_kron_quant_int4": (S, [P, I64, I64, I64, I64, P, P, S, I32, I32, I32, P, P, P]),
             "qa_qlinear_kron_w4a4_workspace": (SZ, [I64, I64]),
             "qa_qlinear_kron_w4a4": (S, [P, I64, I64, I64, I64, P, P, P, P, I64, I32, P, S, P, SZ, P]),
@@ -372,6 +374,14 @@ def qa_hadamard_quant_int4(X, G: int, per_group: bool, q_min=-7, q_max=7, stream
            lib().qa_hadamard_quant_int4(_p(X), rows, K, int(G), QA_SCALE_PER_GROUP if per_group else QA_SCALE_PER_ROW,
                                         int(q_min), int(q_max), _p(packed), _p(s), _stream(stream)))
     return packed, s
+
+
+def qa_kron_sizes(n: int):
+    """-> (n1, n2, has_kernel): n1 n2 = n, n1 <= n2, n1 + n2 smallest; has_kernel
+    tells whether the Kronecker entry points take that pair."""
+    n1, n2, hk = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_int32(0)
+    _check("qa_kron_sizes", lib().qa_kron_sizes(int(n), ctypes.byref(n1), ctypes.byref(n2), ctypes.byref(hk)))
+    return n1.value, n2.value, bool(hk.value)
 
 
 def qa_kron_quant_int4(X, P1, P2, G=None, q_min=-7, q_max=7, stream=None):

@@ -690,6 +690,21 @@ qa_status qa_kron_quant_int4(const void* X_f16, int64_t rows, int64_t K, int64_t
                          "qa_kron_quant_int4");
 }
 
+qa_status qa_kron_sizes(int64_t n, int64_t* n1, int64_t* n2, int32_t* has_kernel) {
+    if (!n1 || !n2) return fail(QA_ERR_NULL, "qa_kron_sizes: NULL n1 or n2");
+    if (n <= 0) return fail(QA_ERR_SHAPE, "qa_kron_sizes: need n > 0 (n=%lld)", (long long)n);
+    // for a fixed product the sum is smallest for the closest pair: walk down
+    // from floor(sqrt(n)) to the first divisor
+    int64_t d = (int64_t)std::sqrt((double)n);
+    while (d * d > n) --d;
+    while ((d + 1) * (d + 1) <= n) ++d;
+    while (n % d != 0) --d;
+    *n1 = d;
+    *n2 = n / d;
+    if (has_kernel) *has_kernel = qa::kron_supported(d, n / d, 0) ? 1 : 0;
+    return ok();
+}
+
 size_t qa_qlinear_kron_w4a4_workspace(int64_t M, int64_t K) { return qa_qlinear_w4a4_workspace(M, K); }
 
 qa_status qa_qlinear_kron_w4a4(const void* X_f16, int64_t M, int64_t K, int64_t n1, int64_t n2, const float* P1,

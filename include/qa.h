@@ -474,6 +474,24 @@ qa_status qa_kron_quant_int4(const void* X_f16, int64_t rows, int64_t K, int64_t
                              uint32_t* packed, float* s, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Kronecker factor sizes  [AIInfra-Q01, FlatQuant section (the split of P
+ * into P1 (x) P2 minimizes n1 + n2 under n1 n2 = n, n1 <= n2; n = 8192 gives
+ * 64 x 128); 从离群值到平坦线：FlatQuant 如何重塑 LLM 的 4-bit 量化格局, §2
+ * (4096 as 64 x 64)]
+ *
+ *   n1 = the largest divisor of n not above sqrt(n), n2 = n / n1: the pair
+ *   with n1 n2 = n, n1 <= n2 and the smallest n1 + n2.  Host arithmetic, no
+ *   device work.
+ *   n           transform width (K), > 0
+ *   n1, n2      host int64 outputs
+ *   has_kernel  host int32 output, may be NULL: 1 when qa_kron_quant_int4 and
+ *               qa_qlinear_kron_w4a4 have a kernel for (n1, n2), else 0
+ * Errors: NULL n1 or n2 (QA_ERR_NULL), n <= 0 (QA_ERR_SHAPE); the outputs
+ * are untouched on error.
+ * ------------------------------------------------------------------------- */
+qa_status qa_kron_sizes(int64_t n, int64_t* n1, int64_t* n2, int32_t* has_kernel);
+
+/* ---------------------------------------------------------------------------
  * W4A4 linear with the Kronecker transform  [AIInfra-Q01, FlatQuant section:
  * transform + dynamic int4 of X in one kernel, int4 GEMM with the
  * pre-transformed int4 weight]

@@ -419,3 +419,30 @@ def test_kron_argument_errors():
     assert callg(12, 5) == VALUE
     assert callg(14, 64) == WORKSPACE
     assert callg(1, 0) == OK
+
+
+def test_kron_sizes():
+    # the two splits the pages print (tests/golden/kron_sizes.json), then a
+    # brute-force minimal-sum search over every n up to 5000, then the oracle
+    import json
+    import oracle
+    with open(os.path.join(ROOT, "tests", "golden", "kron_sizes.json")) as f:
+        for c in json.load(f)["cases"]:
+            assert qa.qa_kron_sizes(c["n"]) == (c["n1_printed"], c["n2_printed"], True)
+    for n in range(1, 5001):
+        best = min((a + n // a, a) for a in range(1, n + 1) if n % a == 0 and a * a <= n)
+        n1, n2, _ = qa.qa_kron_sizes(n)
+        assert (n1, n2) == (best[1], n // best[1]), n
+    for n in (64, 96, 4096, 4224, 6144, 8192, 1 << 20, 3 * 5 * 7 * 11 * 13, 2 ** 31 - 1, (1 << 40) + 4):
+        assert qa.qa_kron_sizes(n)[:2] == oracle.kron_sizes(n), n
+    # a kernel exists for the minimal-sum splits of 64 .. 8192 (powers of two)
+    for k in range(6, 14):
+        assert qa.qa_kron_sizes(1 << k)[2], k
+    assert not qa.qa_kron_sizes(4224)[2] and not qa.qa_kron_sizes(1 << 14)[2]
+    n1, n2 = ctypes.c_int64(-5), ctypes.c_int64(-5)
+    L = qa.lib()
+    assert L.qa_kron_sizes(0, ctypes.byref(n1), ctypes.byref(n2), None) == SHAPE
+    assert L.qa_kron_sizes(-3, ctypes.byref(n1), ctypes.byref(n2), None) == SHAPE
+    assert (n1.value, n2.value) == (-5, -5)                    # untouched on error
+    assert L.qa_kron_sizes(12, None, ctypes.byref(n2), None) == NULL
+    assert L.qa_kron_sizes(12, ctypes.byref(n1), ctypes.byref(n2), None) == OK and (n1.value, n2.value) == (3, 4)
