@@ -426,7 +426,9 @@ def test_w4a4_linear_shapes(qa, M, K, N, G):
     assert_float_parity(as_f64(out), oracle.qlinear_w4a4(X, oWp, os_w, G), torch.float32)
 
 
-@pytest.mark.parametrize("M,K,N,G", [(1030, 320, 7976, 64), (2100, 384, 4100, 128), (1100, 512, 7700, 256)])
+@pytest.mark.parametrize("M,K,N,G", [(1030, 320, 7976, 64), (2100, 384, 4100, 128), (1100, 512, 7700, 256),
+                                     # K / G x 256 > 8192: the block's scales do not fit the LDS table
+                                     (2048, 8448, 4096, 64), (2050, 8192, 4100, 128)])
 def test_w4a4_linear_large_sampled(qa, M, K, N, G):
     """Shapes with >= 256 tiles of 128 x 256 (the eight-wave LDS-DMA kernel):
     ragged M and N, K ending half-way through a stage; sampled rows."""

@@ -116,6 +116,13 @@ def test_w4a4_asym_linear_large_sampled(qa, M, K, N, G):
     _w4z_case(qa, M, K, N, G, rows=rows, seed=M + G)
 
 
+@pytest.mark.parametrize("M,K,N,G", [(40, 8448, 96, 64), (33, 8192, 70, 128), (20, 16384, 40, 256)])
+def test_w4a4_asym_linear_scales_outside_lds(qa, M, K, N, G):
+    # K / G x 256 > 8192: the scales are read per group from memory instead of
+    # the block's LDS table
+    _w4z_case(qa, M, K, N, G, seed=K + G)
+
+
 def test_w4a4_asym_config_sampled(qa):
     # the W4A4 workload's shape, 2048 x 4096 x 4096, G = 128, activations made one-sided
     c = synthetic.config("w4a4_hadamard")

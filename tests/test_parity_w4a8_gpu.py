@@ -104,6 +104,13 @@ def test_w4a8_linear_shapes(qa, M, K, N, G):
     _w4a8_case(qa, M, K, N, G, seed=M + K + 2)
 
 
+@pytest.mark.parametrize("M,K,N,G", [(40, 8448, 96, 64), (33, 8192, 70, 128), (20, 16384, 40, 256)])
+def test_w4a8_linear_scales_outside_lds(qa, M, K, N, G):
+    # K / G x 256 > 8192: the scales are read per group from memory instead of
+    # the block's LDS table
+    _w4a8_case(qa, M, K, N, G, seed=K + G)
+
+
 @pytest.mark.parametrize("out_dtype", [1, 2])
 def test_w4a8_linear_out_dtypes(qa, out_dtype):
     _w4a8_case(qa, 40, 1024, 96, 128, out_dtype, seed=5)
