@@ -66,10 +66,13 @@ def log(*a):
 
 
 class GraphSteps:
-    """Capture `fns` (one launch sequence each) into one HIP graph."""
+    """Capture calls into HIP graphs: `run(k)` replays exactly k calls, taken
+    in turn from `fns` (call i runs fns[i % len(fns)])."""
 
     def __init__(self, torch, fns):
         self.torch = torch
+        self.fns = fns
+        self.n = len(fns)
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
@@ -77,35 +80,37 @@ class GraphSteps:
                 f()
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
-        self.g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(self.g):
-            for f in fns:
-                f()
-        self.n = len(fns)
+        self.graphs = {}
 
-    def replay(self):
-        self.g.replay()
+    def graph(self, k):
+        if k not in self.graphs:
+            g = self.torch.cuda.CUDAGraph()
+            with self.torch.cuda.graph(g):
+                for i in range(k):
+                    self.fns[i % self.n]()
+            self.graphs[k] = g
+        return self.graphs[k]
 
 
 def time_graph(torch, gs, steps, warmup):
-    """Replay the graph until `warmup` then exactly `steps` steps have run
-    (steps rounded up to whole graphs); returns (ms per step, steps run)."""
-    reps_w = max(1, -(-warmup // gs.n))
-    for _ in range(reps_w):
-        gs.replay()
-    reps = max(1, -(-steps // gs.n))
+    """Replay `warmup` untimed calls, then time exactly `steps` calls (one graph
+    holding that many) between HIP events on the replay stream; returns
+    (ms per call, wall ms per call, calls timed)."""
+    steps = max(1, int(steps))
+    g = gs.graph(steps)
+    if warmup > 0:
+        gs.graph(int(warmup)).replay()
+    g.replay()                              # first replay of a fresh graph uploads it: untimed
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record()
-    for _ in range(reps):
-        gs.replay()
+    g.replay()
     e1.record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3
-    n = reps * gs.n
-    return e0.elapsed_time(e1) / n, wall / n, n
+    return e0.elapsed_time(e1) / steps, wall / steps, steps
 
 
 def recorded_traffic(kernel, source):
@@ -387,7 +392,7 @@ def main():
                 name = "smoothquant_ffn: X/s per-tensor int8, %s data" % name
             else:
                 c, fns, ops = prefill_like(torch, qa, synthetic, dev, name)
-            gs = GraphSteps(torch, fns * 4)
+            gs = GraphSteps(torch, fns)
             st = min(args.steps, 64)
             log("[bench] %s: timing %d calls" % (name, st))
             ms, wall_ms, n = time_graph(torch, gs, st, min(args.warmup, 8))

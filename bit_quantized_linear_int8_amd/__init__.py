@@ -25,7 +25,7 @@ EXPORTS = (
     "qa_status_string", "qa_last_error",
     "qa_outlier_cols_workspace", "qa_outlier_cols", "qa_outlier_topk",
     "qa_quantize_rowwise_int8",
-    "qa_qlinear_int8_mixed_workspace", "qa_qlinear_int8_mixed",
+    "qa_qlinear_int8_mixed_workspace", "qa_qlinear_int8_mixed", "qa_qlinear_int8_mixed_offsets",
     "qa_qlinear_int8_topk_workspace", "qa_qlinear_int8_topk",
     "qa_quantize_rowwise_int8_asym", "qa_int8_row_sums", "qa_qlinear_int8_asym_workspace", "qa_qlinear_int8_asym",
     "qa_col_absmax_workspace", "qa_col_absmax", "qa_smooth_factors", "qa_quantize_smooth_int8",
@@ -71,6 +71,7 @@ def lib() -> ctypes.CDLL:
             "qa_quantize_rowwise_int8": (S, [P, I64, I64, P, I32, I32, P, P, P, P, P]),
             "qa_qlinear_int8_mixed_workspace": (SZ, [I64, I64]),
             "qa_qlinear_int8_mixed": (S, [P, I64, I64, P, P, P, I64, F, P, S, P, SZ, P]),
+            "qa_qlinear_int8_mixed_offsets": (S, [I64, I64, P]),
             "qa_quantize_rowwise_int8_asym": (S, [P, I64, I64, I32, I32, P, P, P, P, P]),
             "qa_int8_row_sums": (S, [P, I64, I64, P, P]),
             "qa_qlinear_int8_asym_workspace": (SZ, [I64, I64]),
@@ -139,10 +140,20 @@ def _dev(t, name, dtype=None):
     return t
 
 
-def _workspace(nbytes, device, ws):
+def _empty(stream, *args, **kw):
+    """torch.empty on the stream the library call runs on: the caching
+    allocator then keeps the block for that stream, so memory a call still
+    uses is not handed to work on another stream after it is released."""
+    if stream is None:
+        return torch.empty(*args, **kw)
+    with torch.cuda.stream(stream):
+        return torch.empty(*args, **kw)
+
+
+def _workspace(stream, nbytes, device, ws):
     if ws is not None:
         return ws
-    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    return _empty(stream, max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
 # ---------------------------------------------------------------- entry points
@@ -155,12 +166,12 @@ def qa_outlier_cols(X, threshold=6.0, scratch=None, stream=None):
     _dev(X, "X", torch.float16)
     M, K = X.shape
     dev = X.device
-    mask = torch.empty(K, dtype=torch.uint8, device=dev)
-    idx = torch.empty(K, dtype=torch.int32, device=dev)
-    count = torch.empty(1, dtype=torch.int32, device=dev)
-    colmax = torch.empty(K, dtype=torch.float32, device=dev)
+    mask = _empty(stream, K, dtype=torch.uint8, device=dev)
+    idx = _empty(stream, K, dtype=torch.int32, device=dev)
+    count = _empty(stream, 1, dtype=torch.int32, device=dev)
+    colmax = _empty(stream, K, dtype=torch.float32, device=dev)
     nb = qa_outlier_cols_workspace(K)
-    scratch = _workspace(nb, dev, scratch)
+    scratch = _workspace(stream, nb, dev, scratch)
     _check("qa_outlier_cols", lib().qa_outlier_cols(_p(X), M, K, float(threshold), _p(mask), _p(idx), _p(count),
                                                      _p(colmax), _p(scratch), scratch.numel(), _stream(stream)))
     return mask, idx, count, colmax
@@ -172,11 +183,11 @@ def qa_outlier_topk(X, k: int, scratch=None, stream=None):
     _dev(X, "X", torch.float16)
     M, K = X.shape
     dev = X.device
-    mask = torch.empty(K, dtype=torch.uint8, device=dev)
-    idx = torch.empty(K, dtype=torch.int32, device=dev)
-    count = torch.empty(1, dtype=torch.int32, device=dev)
-    colmax = torch.empty(K, dtype=torch.float32, device=dev)
-    scratch = _workspace(qa_outlier_cols_workspace(K), dev, scratch)
+    mask = _empty(stream, K, dtype=torch.uint8, device=dev)
+    idx = _empty(stream, K, dtype=torch.int32, device=dev)
+    count = _empty(stream, 1, dtype=torch.int32, device=dev)
+    colmax = _empty(stream, K, dtype=torch.float32, device=dev)
+    scratch = _workspace(stream, qa_outlier_cols_workspace(K), dev, scratch)
     _check("qa_outlier_topk", lib().qa_outlier_topk(_p(X), M, K, int(k), _p(mask), _p(idx), _p(count), _p(colmax),
                                                      _p(scratch), scratch.numel(), _stream(stream)))
     return mask, idx, count, colmax
@@ -192,8 +203,8 @@ def qa_quantize_rowwise_int8(X, mask=None, q_min=-127, q_max=127, s_in=None, z_i
     """-> (Xq i8 [rows x K], s f32 [rows] or None in static mode)."""
     _dev(X, "X", torch.float16)
     rows, K = X.shape
-    Xq = torch.empty((rows, K), dtype=torch.int8, device=X.device)
-    s_out = None if s_in is not None else torch.empty(rows, dtype=torch.float32, device=X.device)
+    Xq = _empty(stream, (rows, K), dtype=torch.int8, device=X.device)
+    s_out = None if s_in is not None else _empty(stream, rows, dtype=torch.float32, device=X.device)
     _check("qa_quantize_rowwise_int8",
            lib().qa_quantize_rowwise_int8(_p(X), rows, K, _p(mask), int(q_min), int(q_max), _p(s_in), _p(z_in),
                                           _p(Xq), _p(s_out), _stream(stream)))
@@ -215,12 +226,20 @@ def qa_qlinear_int8_mixed(X, Wq, s_w, W16=None, threshold=6.0, out_dtype=torch.f
     M, K = X.shape
     N = Wq.shape[0]
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=X.device)
-    workspace = _workspace(qa_qlinear_int8_mixed_workspace(M, K), X.device, workspace)
+        out = _empty(stream, (M, N), dtype=out_dtype, device=X.device)
+    workspace = _workspace(stream, qa_qlinear_int8_mixed_workspace(M, K), X.device, workspace)
     _check("qa_qlinear_int8_mixed",
            lib().qa_qlinear_int8_mixed(_p(X), M, K, _p(Wq), _p(s_w), _p(W16), N, float(threshold), _p(out),
                                        _DTYPE_CODE[out.dtype], _p(workspace), workspace.numel(), _stream(stream)))
     return out
+
+
+def qa_qlinear_int8_mixed_offsets(M: int, K: int):
+    """Byte offsets of (idx, count, s_x, Xq) in the workspace of an LLM.int8()
+    call with M tokens and K in-features."""
+    off = (ctypes.c_size_t * 4)()
+    _check("qa_qlinear_int8_mixed_offsets", lib().qa_qlinear_int8_mixed_offsets(int(M), int(K), off))
+    return tuple(int(v) for v in off)
 
 
 def qa_quantize_rowwise_int8_asym(X, q_min=-128, q_max=127, stream=None):
@@ -228,10 +247,10 @@ def qa_quantize_rowwise_int8_asym(X, q_min=-128, q_max=127, stream=None):
     _dev(X, "X", torch.float16)
     rows, K = X.shape
     d = X.device
-    q = torch.empty((rows, K), dtype=torch.int8, device=d)
-    s = torch.empty(rows, dtype=torch.float32, device=d)
-    z = torch.empty(rows, dtype=torch.int32, device=d)
-    rs = torch.empty(rows, dtype=torch.int32, device=d)
+    q = _empty(stream, (rows, K), dtype=torch.int8, device=d)
+    s = _empty(stream, rows, dtype=torch.float32, device=d)
+    z = _empty(stream, rows, dtype=torch.int32, device=d)
+    rs = _empty(stream, rows, dtype=torch.int32, device=d)
     _check("qa_quantize_rowwise_int8_asym",
            lib().qa_quantize_rowwise_int8_asym(_p(X), rows, K, int(q_min), int(q_max), _p(q), _p(s), _p(z), _p(rs),
                                                _stream(stream)))
@@ -242,7 +261,7 @@ def qa_int8_row_sums(A, stream=None):
     """Row sums of an int8 matrix -> i32 [rows]."""
     _dev(A, "A", torch.int8)
     rows, K = A.shape
-    sums = torch.empty(rows, dtype=torch.int32, device=A.device)
+    sums = _empty(stream, rows, dtype=torch.int32, device=A.device)
     _check("qa_int8_row_sums", lib().qa_int8_row_sums(_p(A), rows, K, _p(sums), _stream(stream)))
     return sums
 
@@ -263,8 +282,8 @@ def qa_qlinear_int8_asym(X, Wq, s_w, w_rowsum, z_w=None, out_dtype=torch.float16
     M, K = X.shape
     N = Wq.shape[0]
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=X.device)
-    workspace = _workspace(qa_qlinear_int8_asym_workspace(M, K), X.device, workspace)
+        out = _empty(stream, (M, N), dtype=out_dtype, device=X.device)
+    workspace = _workspace(stream, qa_qlinear_int8_asym_workspace(M, K), X.device, workspace)
     _check("qa_qlinear_int8_asym",
            lib().qa_qlinear_int8_asym(_p(X), M, K, _p(Wq), _p(s_w), _p(z_w), _p(w_rowsum), N, _p(out),
                                       _DTYPE_CODE[out.dtype], _p(workspace), workspace.numel(), _stream(stream)))
@@ -283,9 +302,9 @@ def qa_col_absmax(A, colmax=None, accumulate=False, scratch=None, stream=None):
     if colmax is None:
         if accumulate:
             raise ValueError("accumulate needs the running colmax")
-        colmax = torch.empty(K, dtype=torch.float32, device=A.device)
+        colmax = _empty(stream, K, dtype=torch.float32, device=A.device)
     _dev(colmax, "colmax", torch.float32)
-    scratch = _workspace(qa_col_absmax_workspace(K), A.device, scratch)
+    scratch = _workspace(stream, qa_col_absmax_workspace(K), A.device, scratch)
     _check("qa_col_absmax", lib().qa_col_absmax(_p(A), rows, K, _p(colmax), int(bool(accumulate)), _p(scratch),
                                                  scratch.numel(), _stream(stream)))
     return colmax
@@ -298,7 +317,7 @@ def qa_smooth_factors(act_absmax, w_absmax, alpha=0.5, stream=None):
     K = act_absmax.numel()
     if w_absmax.numel() != K:
         raise ValueError("act_absmax and w_absmax differ in length")
-    s = torch.empty(K, dtype=torch.float32, device=act_absmax.device)
+    s = _empty(stream, K, dtype=torch.float32, device=act_absmax.device)
     _check("qa_smooth_factors", lib().qa_smooth_factors(_p(act_absmax), _p(w_absmax), K, float(alpha), _p(s),
                                                          _stream(stream)))
     return s
@@ -309,8 +328,8 @@ def qa_quantize_smooth_int8(A, s, multiply=False, per_tensor=False, stream=None)
     _dev(A, "A", torch.float16)
     _dev(s, "s", torch.float32)
     rows, K = A.shape
-    q = torch.empty((rows, K), dtype=torch.int8, device=A.device)
-    s_out = torch.empty(rows, dtype=torch.float32, device=A.device)
+    q = _empty(stream, (rows, K), dtype=torch.int8, device=A.device)
+    s_out = _empty(stream, rows, dtype=torch.float32, device=A.device)
     _check("qa_quantize_smooth_int8",
            lib().qa_quantize_smooth_int8(_p(A), rows, K, _p(s), QA_SMOOTH_MULTIPLY if multiply else QA_SMOOTH_DIVIDE,
                                          QA_SCALE_PER_TENSOR if per_tensor else QA_SCALE_PER_ROW, _p(q), _p(s_out),
@@ -332,8 +351,8 @@ def qa_qlinear_int8_smooth(X, s, Wq, s_w, per_tensor=False, out_dtype=torch.floa
     M, K = X.shape
     N = Wq.shape[0]
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=X.device)
-    workspace = _workspace(qa_qlinear_int8_smooth_workspace(M, K), X.device, workspace)
+        out = _empty(stream, (M, N), dtype=out_dtype, device=X.device)
+    workspace = _workspace(stream, qa_qlinear_int8_smooth_workspace(M, K), X.device, workspace)
     _check("qa_qlinear_int8_smooth",
            lib().qa_qlinear_int8_smooth(_p(X), M, K, _p(s), QA_SCALE_PER_TENSOR if per_tensor else QA_SCALE_PER_ROW,
                                         _p(Wq), _p(s_w), N, _p(out), _DTYPE_CODE[out.dtype], _p(workspace),
@@ -356,8 +375,8 @@ def qa_qlinear_int8_topk(X, Wq, s_w, k: int, W16=None, out_dtype=torch.float16, 
     M, K = X.shape
     N = Wq.shape[0]
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=X.device)
-    workspace = _workspace(qa_qlinear_int8_topk_workspace(M, K), X.device, workspace)
+        out = _empty(stream, (M, N), dtype=out_dtype, device=X.device)
+    workspace = _workspace(stream, qa_qlinear_int8_topk_workspace(M, K), X.device, workspace)
     _check("qa_qlinear_int8_topk",
            lib().qa_qlinear_int8_topk(_p(X), M, K, int(k), _p(Wq), _p(s_w), _p(W16), N, _p(out),
                                       _DTYPE_CODE[out.dtype], _p(workspace), workspace.numel(), _stream(stream)))
@@ -368,8 +387,8 @@ def qa_hadamard_quant_int4(X, G: int, per_group: bool, q_min=-7, q_max=7, stream
     """-> (packed u32 as int32 [rows x K/8], s f32 [rows x (K/G if per_group else 1)])."""
     _dev(X, "X", torch.float16)
     rows, K = X.shape
-    packed = torch.empty((rows, K // 8), dtype=torch.int32, device=X.device)
-    s = torch.empty((rows, K // G if per_group else 1), dtype=torch.float32, device=X.device)
+    packed = _empty(stream, (rows, K // 8), dtype=torch.int32, device=X.device)
+    s = _empty(stream, (rows, K // G if per_group else 1), dtype=torch.float32, device=X.device)
     _check("qa_hadamard_quant_int4",
            lib().qa_hadamard_quant_int4(_p(X), rows, K, int(G), QA_SCALE_PER_GROUP if per_group else QA_SCALE_PER_ROW,
                                         int(q_min), int(q_max), _p(packed), _p(s), _stream(stream)))
@@ -392,8 +411,8 @@ def qa_kron_quant_int4(X, P1, P2, G=None, q_min=-7, q_max=7, stream=None):
     _dev(P2, "P2", torch.float32)
     rows, K = X.shape
     n1, n2 = P1.shape[0], P2.shape[0]
-    packed = torch.empty((rows, K // 8), dtype=torch.int32, device=X.device)
-    s = torch.empty((rows, K // G if G else 1), dtype=torch.float32, device=X.device)
+    packed = _empty(stream, (rows, K // 8), dtype=torch.int32, device=X.device)
+    s = _empty(stream, (rows, K // G if G else 1), dtype=torch.float32, device=X.device)
     _check("qa_kron_quant_int4",
            lib().qa_kron_quant_int4(_p(X), rows, K, n1, n2, _p(P1), _p(P2),
                                     QA_SCALE_PER_GROUP if G else QA_SCALE_PER_ROW, int(G or 0), int(q_min), int(q_max),
@@ -415,8 +434,8 @@ def qa_qlinear_kron_w4a4(X, P1, P2, Wp, s_w, G=128, out_dtype=torch.float32, out
     M, K = X.shape
     N = Wp.shape[0]
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=X.device)
-    workspace = _workspace(qa_qlinear_kron_w4a4_workspace(M, K), X.device, workspace)
+        out = _empty(stream, (M, N), dtype=out_dtype, device=X.device)
+    workspace = _workspace(stream, qa_qlinear_kron_w4a4_workspace(M, K), X.device, workspace)
     _check("qa_qlinear_kron_w4a4",
            lib().qa_qlinear_kron_w4a4(_p(X), M, K, P1.shape[0], P2.shape[0], _p(P1), _p(P2), _p(Wp), _p(s_w), N,
                                       int(G), _p(out), _DTYPE_CODE[out.dtype], _p(workspace), workspace.numel(),
@@ -436,8 +455,8 @@ def qa_qlinear_w4a4(X, Wp, s_w, G=128, out_dtype=torch.float32, out=None, worksp
     M, K = X.shape
     N = Wp.shape[0]
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=X.device)
-    workspace = _workspace(qa_qlinear_w4a4_workspace(M, K), X.device, workspace)
+        out = _empty(stream, (M, N), dtype=out_dtype, device=X.device)
+    workspace = _workspace(stream, qa_qlinear_w4a4_workspace(M, K), X.device, workspace)
     _check("qa_qlinear_w4a4",
            lib().qa_qlinear_w4a4(_p(X), M, K, _p(Wp), _p(s_w), N, int(G), _p(out), _DTYPE_CODE[out.dtype],
                                  _p(workspace), workspace.numel(), _stream(stream)))
@@ -448,8 +467,8 @@ def qa_hadamard_quant_int8(X, G: int, q_min=-127, q_max=127, stream=None):
     """Hadamard rotation + per-row int8 codes -> (q i8 [rows x K], s f32 [rows])."""
     _dev(X, "X", torch.float16)
     rows, K = X.shape
-    q = torch.empty((rows, K), dtype=torch.int8, device=X.device)
-    s = torch.empty(rows, dtype=torch.float32, device=X.device)
+    q = _empty(stream, (rows, K), dtype=torch.int8, device=X.device)
+    s = _empty(stream, rows, dtype=torch.float32, device=X.device)
     _check("qa_hadamard_quant_int8",
            lib().qa_hadamard_quant_int8(_p(X), rows, K, int(G), int(q_min), int(q_max), _p(q), _p(s),
                                         _stream(stream)))
@@ -468,8 +487,8 @@ def qa_qlinear_w4a8(X, Wp, s_w, G=128, out_dtype=torch.float32, out=None, worksp
     M, K = X.shape
     N = Wp.shape[0]
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=X.device)
-    workspace = _workspace(qa_qlinear_w4a8_workspace(M, K), X.device, workspace)
+        out = _empty(stream, (M, N), dtype=out_dtype, device=X.device)
+    workspace = _workspace(stream, qa_qlinear_w4a8_workspace(M, K), X.device, workspace)
     _check("qa_qlinear_w4a8",
            lib().qa_qlinear_w4a8(_p(X), M, K, _p(Wp), _p(s_w), N, int(G), _p(out), _DTYPE_CODE[out.dtype],
                                  _p(workspace), workspace.numel(), _stream(stream)))
@@ -481,9 +500,9 @@ def qa_hadamard_quant_int4_asym(X, G: int, stream=None):
     s f32 [rows], z i32 [rows])."""
     _dev(X, "X", torch.float16)
     rows, K = X.shape
-    packed = torch.empty((rows, K // 8), dtype=torch.int32, device=X.device)
-    s = torch.empty(rows, dtype=torch.float32, device=X.device)
-    z = torch.empty(rows, dtype=torch.int32, device=X.device)
+    packed = _empty(stream, (rows, K // 8), dtype=torch.int32, device=X.device)
+    s = _empty(stream, rows, dtype=torch.float32, device=X.device)
+    z = _empty(stream, rows, dtype=torch.int32, device=X.device)
     _check("qa_hadamard_quant_int4_asym",
            lib().qa_hadamard_quant_int4_asym(_p(X), rows, K, int(G), _p(packed), _p(s), _p(z), _stream(stream)))
     return packed, s, z
@@ -494,7 +513,7 @@ def qa_w4_column_terms(Wp, s_w, K: int, G: int, stream=None):
     _dev(Wp, "Wp", torch.int32)
     _dev(s_w, "s_w", torch.float32)
     N = Wp.shape[0]
-    c = torch.empty(N, dtype=torch.float32, device=Wp.device)
+    c = _empty(stream, N, dtype=torch.float32, device=Wp.device)
     _check("qa_w4_column_terms", lib().qa_w4_column_terms(_p(Wp), _p(s_w), N, int(K), int(G), _p(c), _stream(stream)))
     return c
 
@@ -512,8 +531,8 @@ def qa_qlinear_w4a4_asym(X, Wp, s_w, c_w, G=128, out_dtype=torch.float32, out=No
     M, K = X.shape
     N = Wp.shape[0]
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=X.device)
-    workspace = _workspace(qa_qlinear_w4a4_asym_workspace(M, K), X.device, workspace)
+        out = _empty(stream, (M, N), dtype=out_dtype, device=X.device)
+    workspace = _workspace(stream, qa_qlinear_w4a4_asym_workspace(M, K), X.device, workspace)
     _check("qa_qlinear_w4a4_asym",
            lib().qa_qlinear_w4a4_asym(_p(X), M, K, _p(Wp), _p(s_w), _p(c_w), N, int(G), _p(out),
                                       _DTYPE_CODE[out.dtype], _p(workspace), workspace.numel(), _stream(stream)))
@@ -525,7 +544,7 @@ def qa_gemm_i8_i32(A, B, stream=None):
     _dev(B, "B", torch.int8)
     M, K = A.shape
     N = B.shape[0]
-    C = torch.empty((M, N), dtype=torch.int32, device=A.device)
+    C = _empty(stream, (M, N), dtype=torch.int32, device=A.device)
     _check("qa_gemm_i8_i32", lib().qa_gemm_i8_i32(_p(A), _p(B), M, K, N, _p(C), _stream(stream)))
     return C
 
@@ -534,7 +553,7 @@ def qa_gemm_w4a4_group_acc(Xp, Wp, K: int, G: int, stream=None):
     _dev(Xp, "Xp", torch.int32)
     _dev(Wp, "Wp", torch.int32)
     M, N = Xp.shape[0], Wp.shape[0]
-    acc = torch.empty((M, N, K // G), dtype=torch.int32, device=Xp.device)
+    acc = _empty(stream, (M, N, K // G), dtype=torch.int32, device=Xp.device)
     _check("qa_gemm_w4a4_group_acc",
            lib().qa_gemm_w4a4_group_acc(_p(Xp), _p(Wp), M, K, N, int(G), _p(acc), _stream(stream)))
     return acc
@@ -545,7 +564,7 @@ def qa_gemm_w4a8_group_acc(Xq, Wp, G: int, stream=None):
     _dev(Wp, "Wp", torch.int32)
     M, K = Xq.shape
     N = Wp.shape[0]
-    acc = torch.empty((M, N, K // G), dtype=torch.int32, device=Xq.device)
+    acc = _empty(stream, (M, N, K // G), dtype=torch.int32, device=Xq.device)
     _check("qa_gemm_w4a8_group_acc",
            lib().qa_gemm_w4a8_group_acc(_p(Xq), _p(Wp), M, K, N, int(G), _p(acc), _stream(stream)))
     return acc

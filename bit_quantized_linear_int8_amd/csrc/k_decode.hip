@@ -111,7 +111,8 @@ __global__ __launch_bounds__(DEC_THREADS) void k_decode_mixed(const uint16_t* __
                                                               const int8_t* __restrict__ Wq,
                                                               const float* __restrict__ s_w,
                                                               const uint16_t* __restrict__ W16, int64_t N, float tau,
-                                                              void* __restrict__ out, int out_dtype) {
+                                                              void* __restrict__ out, int out_dtype,
+                                                              DecodeStages st) {
     __shared__ __attribute__((aligned(16))) int8_t aq[MB * DEC_LDA];
     __shared__ int32_t oidx[DEC_MAXK];
     __shared__ int32_t red[DEC_WAVES][256];
@@ -312,6 +313,20 @@ __global__ __launch_bounds__(DEC_THREADS) void k_decode_mixed(const uint16_t* __
         else
             static_cast<uint16_t*>(out)[o] = f2bf(v);
     }
+
+    // 4. workgroup 0 leaves the integer stages (outlier list, count, per-token
+    //    scales, codes) where the general path keeps them
+    if (blockIdx.x == 0) {
+        for (int h = t; h < count; h += DEC_THREADS) st.idx[h] = oidx[h];
+        if (t == 0) *st.count = count;
+        if (t < M) st.s_x[t] = sx_s[t];
+        const int cpr = K >> 4;                       // 16-byte chunks per row
+        for (int c = t; c < M * cpr; c += DEC_THREADS) {
+            const int r = c / cpr, j = c - r * cpr;
+            *reinterpret_cast<v4i*>(st.xq + (int64_t)r * K + 16 * j) =
+                *reinterpret_cast<const v4i*>(aq + r * DEC_LDA + 16 * j);
+        }
+    }
 }
 
 bool decode_supported(int64_t M, int64_t K) {
@@ -320,17 +335,17 @@ bool decode_supported(int64_t M, int64_t K) {
 
 hipError_t launch_decode_mixed(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* s_w,
                                const uint16_t* W16, int64_t N, float tau, void* out, int out_dtype,
-                               hipStream_t st) {
+                               const DecodeStages& stages, hipStream_t st) {
     const dim3 grid((unsigned)((N + 15) / 16)), block(DEC_THREADS);
     if (M <= 4)
         hipLaunchKernelGGL(k_decode_mixed<4>, grid, block, 0, st, X, (int)M, (int)K, Wq, s_w, W16, N, tau, out,
-                           out_dtype);
+                           out_dtype, stages);
     else if (M <= 8)
         hipLaunchKernelGGL(k_decode_mixed<8>, grid, block, 0, st, X, (int)M, (int)K, Wq, s_w, W16, N, tau, out,
-                           out_dtype);
+                           out_dtype, stages);
     else
         hipLaunchKernelGGL(k_decode_mixed<16>, grid, block, 0, st, X, (int)M, (int)K, Wq, s_w, W16, N, tau, out,
-                           out_dtype);
+                           out_dtype, stages);
     return hipGetLastError();
 }
 

@@ -229,6 +229,19 @@ size_t qa_qlinear_int8_mixed_workspace(int64_t M, int64_t K) {
     return mixed_layout(M, K).total;
 }
 
+qa_status qa_qlinear_int8_mixed_offsets(int64_t M, int64_t K, size_t* offsets) {
+    if (M <= 0 || K <= 0)
+        return fail(QA_ERR_SHAPE, "qa_qlinear_int8_mixed_offsets: need M, K > 0 (M=%lld K=%lld)", (long long)M,
+                    (long long)K);
+    if (!offsets) return fail(QA_ERR_NULL, "qa_qlinear_int8_mixed_offsets: NULL offsets");
+    const MixedLayout L = mixed_layout(M, K);
+    offsets[0] = L.idx;
+    offsets[1] = L.count;
+    offsets[2] = L.s_x;
+    offsets[3] = L.xq;
+    return ok();
+}
+
 qa_status qa_qlinear_int8_mixed(const void* X_f16, int64_t M, int64_t K, const int8_t* Wq, const float* s_w,
                                 const void* W_f16_or_null, int64_t N, float threshold, void* out,
                                 qa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
@@ -248,17 +261,17 @@ qa_status qa_qlinear_int8_mixed(const void* X_f16, int64_t M, int64_t K, const i
 
     const uint16_t* X = static_cast<const uint16_t*>(X_f16);
     hipStream_t st = as_stream(stream);
-    if (qa::decode_supported(M, K))
-        return device_status(qa::launch_decode_mixed(X, M, K, Wq, s_w, static_cast<const uint16_t*>(W_f16_or_null),
-                                                     N, threshold, out, (int)out_dtype, st),
-                             "qa_qlinear_int8_mixed (decode kernel)");
-
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     int32_t* idx = reinterpret_cast<int32_t*>(ws + L.idx);
     int32_t* count = reinterpret_cast<int32_t*>(ws + L.count);
     float* s_x = reinterpret_cast<float*>(ws + L.s_x);
     int8_t* xq = reinterpret_cast<int8_t*>(ws + L.xq);
     uint16_t* xo = reinterpret_cast<uint16_t*>(ws + L.xo);
+    if (qa::decode_supported(M, K))
+        return device_status(qa::launch_decode_mixed(X, M, K, Wq, s_w, static_cast<const uint16_t*>(W_f16_or_null),
+                                                     N, threshold, out, (int)out_dtype,
+                                                     qa::DecodeStages{idx, count, s_x, xq}, st),
+                             "qa_qlinear_int8_mixed (decode kernel)");
 
     hipError_t e;
     if (!(threshold < 65504.0f)) {

@@ -132,11 +132,19 @@ hipError_t launch_row_sums_i8(const int8_t* A, int64_t rows, int64_t K, int32_t*
 hipError_t launch_gemm_i8_mixed(const int8_t* Xq, const int8_t* Wq, int64_t M, int64_t K, int64_t N,
                                 const MixedEpilogue& ep, hipStream_t st);
 
-// Fused single-kernel LLM.int8() linear for decode shapes (no workspace).
+// Fused single-kernel LLM.int8() linear for decode shapes.  Its first
+// workgroup also stores the integer stages it computed (outlier list and
+// count, per-token scales, codes [M x K]) at these workspace addresses.
+struct DecodeStages {
+    int32_t* idx;
+    int32_t* count;
+    float* s_x;
+    int8_t* xq;
+};
 bool decode_supported(int64_t M, int64_t K);
 hipError_t launch_decode_mixed(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* s_w,
                                const uint16_t* W16, int64_t N, float tau, void* out, int out_dtype,
-                               hipStream_t st);
+                               const DecodeStages& stages, hipStream_t st);
 
 hipError_t launch_gemm_w4a4(const uint32_t* Xp, const float* s_x, const uint32_t* Wp,
                             const float* s_w, int64_t M, int64_t K, int64_t N, int G, void* out,

@@ -184,6 +184,24 @@ qa_status qa_qlinear_int8_mixed(const void* X_f16, int64_t M, int64_t K,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Where the integer stages of an LLM.int8() call sit in its workspace
+ * [AIInfra-Q01: detection and "a. 向量级量化"]
+ *
+ * After qa_qlinear_int8_mixed or qa_qlinear_int8_topk with M, N > 0 has
+ * completed on its stream, its workspace holds, at these byte offsets:
+ *   offsets[0]  idx    i32 [count]: the outlier columns O, ascending
+ *   offsets[1]  count  i32 [1]:     |O|
+ *   offsets[2]  s_x    f32 [M]:     the per-token scales
+ *   offsets[3]  Xq     i8 [M x K]:  the int8 codes the GEMM consumed
+ *                                   (0 in the columns of O)
+ * i.e. exactly the values qa_outlier_cols (or qa_outlier_topk) and
+ * qa_quantize_rowwise_int8 with that mask produce for the same X.  The
+ * offsets depend only on M and K.  offsets: a HOST array of 4 entries.
+ * Errors: M <= 0, K <= 0 (QA_ERR_SHAPE), offsets NULL (QA_ERR_NULL).
+ * ------------------------------------------------------------------------- */
+qa_status qa_qlinear_int8_mixed_offsets(int64_t M, int64_t K, size_t* offsets);
+
+/* ---------------------------------------------------------------------------
  * LLM.int8() linear with top-k decomposition  [AIInfra-Q01: decomposition
  * share raised to the top 1-2% of feature dimensions]
  *

@@ -446,3 +446,24 @@ def test_kron_sizes():
     assert (n1.value, n2.value) == (-5, -5)                    # untouched on error
     assert L.qa_kron_sizes(12, None, ctypes.byref(n2), None) == NULL
     assert L.qa_kron_sizes(12, ctypes.byref(n1), ctypes.byref(n2), None) == OK and (n1.value, n2.value) == (3, 4)
+
+
+def test_mixed_offsets():
+    """The workspace offsets of the integer stages: inside the workspace, 256-byte
+    aligned, non-overlapping, and the same for the top-k call; bad sizes and a
+    NULL array are rejected."""
+    L = qa.lib()
+    for M, K in [(1, 16), (8, 4096), (2048, 4096), (4096, 8192)]:
+        i, c, s, x = qa.qa_qlinear_int8_mixed_offsets(M, K)
+        ws = L.qa_qlinear_int8_mixed_workspace(M, K)
+        assert ws == L.qa_qlinear_int8_topk_workspace(M, K)
+        spans = sorted([(i, 4 * K), (c, 4), (s, 4 * M), (x, M * K)])
+        for (a, n), (b, _) in zip(spans, spans[1:]):
+            assert a + n <= b
+        assert spans[-1][0] + spans[-1][1] <= ws
+        assert all(v % 256 == 0 for v in (i, c, s, x))
+    off = (ctypes.c_size_t * 4)()
+    assert L.qa_qlinear_int8_mixed_offsets(0, 16, off) == SHAPE
+    assert L.qa_qlinear_int8_mixed_offsets(4, 0, off) == SHAPE
+    assert L.qa_qlinear_int8_mixed_offsets(4, 16, None) == NULL
+    assert qa.last_error()

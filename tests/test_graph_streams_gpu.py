@@ -151,3 +151,34 @@ def test_side_stream_and_graph_replays(qa):
         torch.cuda.synchronize()
         for name, out, _ in cases:
             assert np.array_equal(_bits(out), eager[name]), "graph replay %d: %s" % (rep, name)
+
+
+def test_stream_argument_keeps_internal_buffers_on_that_stream(qa):
+    """A call given stream= (not the current stream) allocates its output and
+    workspace on that stream, so when the workspace is released at return the
+    caching allocator does not hand it to work queued on the current stream
+    while the call's kernels, held back on the busy side stream, still use
+    it.  The current stream re-allocates and overwrites blocks of the
+    workspace's size right after each call; every result must equal the
+    eager one bit for bit."""
+    dev = "cuda:0"
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    M, K, N = 520, 1024, 1040
+    X, W, _ = synthetic.mixed_inputs(M, K, N, seed=17, n_dims=5)
+    X, W16 = d(X), d(W)
+    Wq, s_w = qa.qa_quantize_rowwise_int8(W16)
+    ref = _bits(qa.qa_qlinear_int8_mixed(X, Wq, s_w, threshold=6.0, out_dtype=torch.float16))
+    nbytes = qa.qa_qlinear_int8_mixed_workspace(M, K)
+    side = torch.cuda.Stream()                       # default priority
+    a = torch.randn(3072, 3072, device=dev)
+    torch.cuda.synchronize()
+    for trial in range(3):
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            busy = a @ a                             # the side stream is still busy when the call returns
+        out = qa.qa_qlinear_int8_mixed(X, Wq, s_w, threshold=6.0, out_dtype=torch.float16, stream=side)
+        junk = [torch.full((nbytes,), 0xA5, dtype=torch.uint8, device=dev) for _ in range(4)]
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        assert np.array_equal(_bits(out), ref), "trial %d" % trial
+        del busy, junk

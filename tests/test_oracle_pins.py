@@ -588,8 +588,9 @@ def test_smoothquant_page_example():
     per-tensor W8A8 error 0.108 without and 0.054 with alpha = 0.5 smoothing,
     and an equivalence error of order 1e-6."""
     g = golden("smoothquant_toy.json")
-    X, W = synthetic.smoothquant_toy(g["T"], g["C_in"], g["C_out"], g["outlier_channel"], g["outlier_gain"],
-                                     g["w_gain"], g["seed"])
+    X = np.array([[int(v, 16) for v in row] for row in g["X_f32_bits"]], np.uint32).view(np.float32)
+    W = np.array([[int(v, 16) for v in row] for row in g["W_f32_bits"]], np.uint32).view(np.float32)
+    assert X.shape == (g["T"], g["C_in"]) and W.shape == (g["C_in"], g["C_out"])
     Wt = np.ascontiguousarray(W.T)                     # our layout: [out x in]
     Y = X.astype(np.float64) @ W.astype(np.float64)
     s = oracle.smooth_factors(oracle.col_absmax(X), oracle.col_absmax(Wt), g["alpha"])

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import synthetic
-from test_parity_gpu import DEV, ODT, as_f64, assert_float_parity, dev, host
+from test_parity_gpu import DEV, ODT, as_f64, assert_float_parity, dev, host, tile_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -116,7 +116,7 @@ def test_asym_linear_large_k(qa):
 @pytest.mark.parametrize("asym_w", [False, True])
 def test_asym_linear_prefill_size_sampled(qa, asym_w):
     c = synthetic.config("prefill_mixed")
-    _asym_case(qa, c["X"], c["W"], asym_w, c["out_dtype"], rows=np.array([0, 3, 1500, 2047]))
+    _asym_case(qa, c["X"], c["W"], asym_w, c["out_dtype"], rows=tile_rows(c["M"], 256, extra=2))
 
 
 def test_asym_linear_tail_split(qa):

@@ -42,6 +42,16 @@ def as_f64(t):
     return t.float().cpu().numpy().astype(np.float64)
 
 
+def tile_rows(M, tile=128, extra=0, seed=0):
+    """First and last row of every `tile`-row block (so every row tile of a
+    128-, 256- or larger-row tiling is reached), plus `extra` random rows."""
+    rng = np.random.default_rng(seed)
+    r = [np.arange(0, M, tile), np.arange(tile - 1, M, tile), [M - 1]]
+    if extra:
+        r.append(rng.choice(M, min(M, extra), replace=False))
+    return np.unique(np.concatenate(r)).astype(np.int64)
+
+
 def assert_float_parity(got, ref, dtype):
     ref = np.asarray(ref, np.float64)
     tol = 1e-3 * np.abs(ref).max()
@@ -168,7 +178,7 @@ def test_gemm_i8_i32_big_tiles(qa):
     A = rng.integers(-127, 128, (M, K), dtype=np.int8)
     B = rng.integers(-127, 128, (N, K), dtype=np.int8)
     C = host(qa.qa_gemm_i8_i32(dev(A), dev(B)))
-    rows = np.unique(np.concatenate([[0, 255, 256, M - 1], rng.choice(M, size=24, replace=False)]))
+    rows = tile_rows(M, 256, extra=8, seed=11)
     assert np.array_equal(C[rows], oracle.gemm_i8_i32(A, B, rows=rows))
 
 
@@ -181,17 +191,39 @@ def test_gemm_i8_i32_largest_tiles(qa, K):
     A = rng.integers(-128, 128, (M, K), dtype=np.int8)
     B = rng.integers(-128, 128, (N, K), dtype=np.int8)
     C = host(qa.qa_gemm_i8_i32(dev(A), dev(B)))
-    rows = np.unique(np.concatenate([[0, 255, 256, 8191, M - 1], rng.choice(M, size=11, replace=False)]))
+    rows = tile_rows(M, 256, extra=8, seed=K)
     assert np.array_equal(C[rows], oracle.gemm_i8_i32(A, B, rows=rows))
 
 
 # ============================================================ LLM.int8() mixed linear
+def check_int8_stages(qa, ws, X, mask, oidx):
+    """The integer stages a call left in its workspace -- outlier list and
+    count, per-token scales, int8 codes (0 in the outlier columns) -- bit for
+    bit against the oracle's outlier set and its row quantization with that
+    mask."""
+    M, K = X.shape
+    o_idx, o_cnt, o_sx, o_xq = qa.qa_qlinear_int8_mixed_offsets(M, K)
+    w = host(ws)
+    cnt = int(w[o_cnt:o_cnt + 4].view(np.int32)[0])
+    assert cnt == len(oidx), "outlier count %d vs %d" % (cnt, len(oidx))
+    assert np.array_equal(w[o_idx:o_idx + 4 * cnt].view(np.int32), oidx)
+    oq, os_ = oracle.quant_rows(X, mask=mask)
+    assert np.array_equal(w[o_sx:o_sx + 4 * M].view(np.float32), os_[:, 0])
+    got = w[o_xq:o_xq + M * K].view(np.int8).reshape(M, K)
+    bad = np.argwhere(got != oq)
+    assert bad.size == 0, "%d codes differ, first at %s" % (len(bad), bad[:4].tolist())
+
+
 def _mixed_case(qa, X, W, tau, out_dtype, pass_w16, rows=None):
     Wq, s_w = qa.qa_quantize_rowwise_int8(dev(W))
     oWq, os_w = oracle.quant_rows(W)
     assert np.array_equal(host(Wq), oWq) and np.array_equal(host(s_w), os_w[:, 0])
+    M, K = X.shape
+    ws = torch.full((qa.qa_qlinear_int8_mixed_workspace(M, K),), 0x5A, dtype=torch.uint8, device=DEV)
     out = qa.qa_qlinear_int8_mixed(dev(X), Wq, s_w, W16=dev(W) if pass_w16 else None, threshold=tau,
-                                   out_dtype=ODT[out_dtype])
+                                   out_dtype=ODT[out_dtype], workspace=ws)
+    om, oidx, _ = oracle.outlier_cols(X, tau)
+    check_int8_stages(qa, ws, X, om, oidx)
     ref = oracle.qlinear_int8_mixed(X, oWq, os_w[:, 0], W16=W if pass_w16 else None, tau=tau, rows=rows)
     got = as_f64(out)
     if rows is not None:
@@ -281,9 +313,22 @@ def test_mixed_decode_config(qa):
 
 def test_mixed_prefill_config_sampled(qa):
     c = synthetic.config("prefill_mixed")
-    rng = np.random.default_rng(0)
-    rows = np.unique(np.concatenate([[0, c["M"] - 1], rng.choice(c["M"], 30, replace=False)]))
+    rows = tile_rows(c["M"], 128, extra=16)
     _mixed_case(qa, c["X"], c["W"], c["tau"], c["out_dtype"], c["pass_w16"], rows=rows)
+
+
+@pytest.mark.parametrize("out_dtype", [0, 1])
+def test_mixed_decode_config_one_hot_codes(qa, out_dtype):
+    """The decode workload's X (8 x 4096, six planted outlier dims) with
+    threshold 6 against a one-hot weight W[n][n] = 1 (N = K = 4096): output
+    (m, n) is code(m, n) * s_x[m] (times w~ = 1 plus x in an outlier column),
+    so one code off by one moves an output by s_x[m], about 1/127 of the row's
+    largest output -- far outside the tolerance."""
+    c = synthetic.config("decode_mixed")
+    K = c["K"]
+    W = np.zeros((K, K), np.float16)
+    W[np.arange(K), np.arange(K)] = 1.0
+    _mixed_case(qa, c["X"], W, 6.0, out_dtype, False)
 
 
 @pytest.mark.parametrize("pass_w16", [False, True])
@@ -331,8 +376,7 @@ def test_mixed_repeated_calls_one_workspace(qa):
 
 def test_mixed_w8a8_config_sampled(qa):
     c = synthetic.config("w8a8_ffn")
-    rng = np.random.default_rng(1)
-    rows = np.unique(np.concatenate([[0, c["M"] - 1], rng.choice(c["M"], 10, replace=False)]))
+    rows = tile_rows(c["M"], 256, extra=4, seed=1)
     _mixed_case(qa, c["X"], c["W"], c["tau"], c["out_dtype"], c["pass_w16"], rows=rows)
 
 
@@ -354,11 +398,9 @@ def test_mixed_is_deterministic(qa):
 
 
 # ============================================================ Hadamard + int4
-@pytest.mark.parametrize("G", [1, 2, 4, 8, 16, 32, 64, 128, 256])
-@pytest.mark.parametrize("per_group", [False, True])
+@pytest.mark.parametrize("G,per_group", [(G, False) for G in (1, 2, 4, 8, 16, 32, 64, 128, 256)] +
+                         [(G, True) for G in (8, 16, 32, 64, 128, 256)])          # per-group scales need G >= 8
 def test_hadamard_quant_int4(qa, G, per_group):
-    if per_group and G < 8:
-        pytest.skip("per-group scales need G >= 8")
     rows, K = 13, max(G, 8) * 5
     X, _, _ = synthetic.w4a4_inputs(rows, K, 1, seed=G, n_dims=min(3, K // 16))
     X[1, :] = 0
@@ -438,7 +480,7 @@ def test_w4a4_linear_large_sampled(qa, M, K, N, G):
     assert np.array_equal(host(Wp).view(np.uint32), oWp)
     out = as_f64(qa.qa_qlinear_w4a4(dev(X), Wp, s_w, G=G))
     rng = np.random.default_rng(M)
-    rows = np.unique(np.concatenate([[0, 127, 128, M - 1], rng.choice(M, 12, replace=False)]))
+    rows = tile_rows(M, 128, extra=4, seed=M)
     assert_float_parity(out[rows], oracle.qlinear_w4a4(X, oWp, os_w, G, rows=rows), torch.float32)
 
 
@@ -449,12 +491,12 @@ def test_w4a4_config_sampled(qa):
     oWp, os_w = oracle.hadamard_quant_int4(c["W"], G, True)
     assert np.array_equal(host(Wp).view(np.uint32), oWp)
     out = as_f64(qa.qa_qlinear_w4a4(dev(c["X"]), Wp, s_w, G=G))
-    rng = np.random.default_rng(2)
-    rows = np.unique(np.concatenate([[0, c["M"] - 1], rng.choice(c["M"], 40, replace=False)]))
+    rows = tile_rows(c["M"], 128, extra=8, seed=2)
     ref = oracle.qlinear_w4a4(c["X"], oWp, os_w, G, rows=rows)
     assert_float_parity(out[rows], ref, torch.float32)
     # int32 group accumulators of the same call, bit exact on sampled rows
     Xp, _ = qa.qa_hadamard_quant_int4(dev(c["X"]), G, False)
     acc = host(qa.qa_gemm_w4a4_group_acc(Xp, Wp, c["K"], G))
     oXp, _ = oracle.hadamard_quant_int4(c["X"], G, False)
-    assert np.array_equal(acc[rows[:8]], oracle.w4a4_group_acc(oXp, oWp, c["K"], G, rows=rows[:8]))
+    r = rows[::3]
+    assert np.array_equal(acc[r], oracle.w4a4_group_acc(oXp, oWp, c["K"], G, rows=r))

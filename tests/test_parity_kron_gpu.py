@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import synthetic
-from test_parity_gpu import ODT, as_f64, assert_float_parity, dev, host
+from test_parity_gpu import ODT, as_f64, assert_float_parity, dev, host, tile_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -107,4 +107,4 @@ def test_kron_linear_out_dtypes(qa, out_dtype):
 
 def test_kron_linear_w4a4_size_sampled(qa):
     # the W4A4 workload's shape: 2048 x 4096 x 4096, 64 x 64 factors, G = 128
-    _kron_linear(qa, 2048, 4096, 4096, 64, 64, 128, 0, rows=np.array([0, 1, 1023, 2047]), seed=11)
+    _kron_linear(qa, 2048, 4096, 4096, 64, 64, 128, 0, rows=tile_rows(2048, 128), seed=11)

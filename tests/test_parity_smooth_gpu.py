@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import synthetic
-from test_parity_gpu import DEV, ODT, as_f64, assert_float_parity, dev, host
+from test_parity_gpu import DEV, ODT, as_f64, assert_float_parity, dev, host, tile_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -153,11 +153,11 @@ def _full_size(qa, name, per_tensor, rows):
 
 @pytest.mark.parametrize("per_tensor", [False, True])
 def test_qlinear_smooth_prefill_size_sampled(qa, per_tensor):
-    _full_size(qa, "prefill_mixed", per_tensor, np.array([0, 1, 777, 1024, 2047]))
+    _full_size(qa, "prefill_mixed", per_tensor, tile_rows(2048, 256, extra=2))
 
 
 def test_qlinear_smooth_ffn_size_sampled(qa):
-    _full_size(qa, "w8a8_ffn", True, np.array([0, 2049, 4095]))
+    _full_size(qa, "w8a8_ffn", True, tile_rows(4096, 256))
 
 
 def test_smoothing_lowers_error_on_device(qa):

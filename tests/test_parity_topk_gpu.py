@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import synthetic
-from test_parity_gpu import DEV, ODT, as_f64, assert_float_parity, dev, host
+from test_parity_gpu import DEV, ODT, as_f64, assert_float_parity, check_int8_stages, dev, host, tile_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -75,7 +75,12 @@ def _topk_case(qa, X, W, k, out_dtype, pass_w16, rows=None):
     Wq, s_w = qa.qa_quantize_rowwise_int8(dev(W))
     oWq, os_w = oracle.quant_rows(W)
     assert np.array_equal(host(Wq), oWq)
-    out = qa.qa_qlinear_int8_topk(dev(X), Wq, s_w, k, W16=dev(W) if pass_w16 else None, out_dtype=ODT[out_dtype])
+    M, K = X.shape
+    ws = torch.full((qa.qa_qlinear_int8_topk_workspace(M, K),), 0x5A, dtype=torch.uint8, device=DEV)
+    out = qa.qa_qlinear_int8_topk(dev(X), Wq, s_w, k, W16=dev(W) if pass_w16 else None, out_dtype=ODT[out_dtype],
+                                  workspace=ws)
+    om, oidx, _ = oracle.outlier_topk(X, k)
+    check_int8_stages(qa, ws, X, om, oidx)
     ref = oracle.qlinear_int8_topk(X, oWq, os_w[:, 0], W16=W if pass_w16 else None, k=k, rows=rows)
     got = as_f64(out)
     if rows is not None:
@@ -101,7 +106,7 @@ def test_topk_linear_out_dtypes(qa, out_dtype):
 def test_topk_linear_prefill_size_sampled(qa, share):
     c = synthetic.config("prefill_mixed")
     k = qa.topk_count(share, c["K"])
-    rows = np.array([0, 5, 1000, 2047])
+    rows = tile_rows(c["M"], 256)
     _topk_case(qa, c["X"], c["W"], k, c["out_dtype"], False, rows=rows)
 
 

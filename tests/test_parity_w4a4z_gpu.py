@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import synthetic
-from test_parity_gpu import ODT, as_f64, assert_float_parity, dev, host
+from test_parity_gpu import ODT, as_f64, assert_float_parity, dev, host, tile_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -112,7 +112,7 @@ def test_w4a4_asym_linear_out_dtypes(qa, out_dtype):
 @pytest.mark.parametrize("M,K,N,G", [(1030, 320, 7976, 64), (2100, 384, 4100, 128)])
 def test_w4a4_asym_linear_large_sampled(qa, M, K, N, G):
     rng = np.random.default_rng(M + 9)
-    rows = np.unique(np.concatenate([[0, 127, 128, M - 1], rng.choice(M, 12, replace=False)]))
+    rows = tile_rows(M, 128, extra=4)
     _w4z_case(qa, M, K, N, G, rows=rows, seed=M + G)
 
 
@@ -134,7 +134,7 @@ def test_w4a4_asym_config_sampled(qa):
     c_w = qa.qa_w4_column_terms(Wp, s_w, c["K"], G)
     out = as_f64(qa.qa_qlinear_w4a4_asym(dev(X), Wp, s_w, c_w, G=G))
     rng = np.random.default_rng(6)
-    rows = np.unique(np.concatenate([[0, c["M"] - 1], rng.choice(c["M"], 40, replace=False)]))
+    rows = tile_rows(c["M"], 128, extra=8)
     assert_float_parity(out[rows], oracle.qlinear_w4a4_asym(X, oWp, os_w, G, rows=rows), torch.float32)
     p, s, z = qa.qa_hadamard_quant_int4_asym(dev(X), G)
     op, os_, oz = oracle.hadamard_quant_int4_asym(X[rows[:8]], G)

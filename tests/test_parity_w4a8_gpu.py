@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import synthetic
-from test_parity_gpu import ODT, as_f64, assert_float_parity, dev, host
+from test_parity_gpu import ODT, as_f64, assert_float_parity, dev, host, tile_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -119,7 +119,7 @@ def test_w4a8_linear_out_dtypes(qa, out_dtype):
 @pytest.mark.parametrize("M,K,N,G", [(1030, 320, 7976, 64), (2100, 384, 4100, 128), (1100, 512, 7700, 256)])
 def test_w4a8_linear_large_sampled(qa, M, K, N, G):
     rng = np.random.default_rng(M + 3)
-    rows = np.unique(np.concatenate([[0, 127, 128, M - 1], rng.choice(M, 12, replace=False)]))
+    rows = tile_rows(M, 128, extra=4)
     _w4a8_case(qa, M, K, N, G, rows=rows, seed=M + G)
 
 
@@ -132,7 +132,7 @@ def test_w4a8_config_sampled(qa):
     assert np.array_equal(host(Wp).view(np.uint32), oWp)
     out = as_f64(qa.qa_qlinear_w4a8(dev(c["X"]), Wp, s_w, G=G))
     rng = np.random.default_rng(4)
-    rows = np.unique(np.concatenate([[0, c["M"] - 1], rng.choice(c["M"], 40, replace=False)]))
+    rows = tile_rows(c["M"], 128, extra=8)
     assert_float_parity(out[rows], oracle.qlinear_w4a8(c["X"], oWp, os_w, G, rows=rows), torch.float32)
     Xq, s_x = qa.qa_hadamard_quant_int8(dev(c["X"]), G)
     oXq, os_x = oracle.hadamard_quant_int8(c["X"][rows[:8]], G)
