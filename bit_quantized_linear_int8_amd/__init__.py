@@ -26,6 +26,7 @@ EXPORTS = (
     "qa_outlier_cols_workspace", "qa_outlier_cols", "qa_outlier_topk",
     "qa_quantize_rowwise_int8",
     "qa_qlinear_int8_mixed_workspace", "qa_qlinear_int8_mixed", "qa_qlinear_int8_mixed_offsets",
+    "qa_qlinear_int8_mixed_noalloc",
     "qa_qlinear_int8_topk_workspace", "qa_qlinear_int8_topk",
     "qa_quantize_rowwise_int8_asym", "qa_int8_row_sums", "qa_qlinear_int8_asym_workspace", "qa_qlinear_int8_asym",
     "qa_col_absmax_workspace", "qa_col_absmax", "qa_smooth_factors", "qa_quantize_smooth_int8",
@@ -72,6 +73,7 @@ def lib() -> ctypes.CDLL:
             "qa_qlinear_int8_mixed_workspace": (SZ, [I64, I64]),
             "qa_qlinear_int8_mixed": (S, [P, I64, I64, P, P, P, I64, F, P, S, P, SZ, P]),
             "qa_qlinear_int8_mixed_offsets": (S, [I64, I64, P]),
+            "qa_qlinear_int8_mixed_noalloc": (S, [P, I64, I64, P, P, P, I64, F, P, S, P]),
             "qa_quantize_rowwise_int8_asym": (S, [P, I64, I64, I32, I32, P, P, P, P, P]),
             "qa_int8_row_sums": (S, [P, I64, I64, P, P]),
             "qa_qlinear_int8_asym_workspace": (SZ, [I64, I64]),
@@ -231,6 +233,29 @@ def qa_qlinear_int8_mixed(X, Wq, s_w, W16=None, threshold=6.0, out_dtype=torch.f
     _check("qa_qlinear_int8_mixed",
            lib().qa_qlinear_int8_mixed(_p(X), M, K, _p(Wq), _p(s_w), _p(W16), N, float(threshold), _p(out),
                                        _DTYPE_CODE[out.dtype], _p(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 40 << 20
+
+
+def qa_qlinear_int8_mixed_noalloc(X, Wq, s_w, out, W16=None, threshold=6.0, stream=None):
+    """LLM.int8() mixed-precision linear into the caller's `out` [M x N] (fp32,
+    fp16 or bf16) with the library's static per-GPU scratch: nothing is
+    allocated, here or in the library.  Calls that overlap on one GPU race."""
+    _dev(X, "X", torch.float16)
+    _dev(Wq, "Wq", torch.int8)
+    _dev(s_w, "s_w", torch.float32)
+    _dev(out, "out")
+    if W16 is not None:
+        _dev(W16, "W16", torch.float16)
+    M, K = X.shape
+    N = Wq.shape[0]
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out must be [%d x %d]" % (M, N))
+    _check("qa_qlinear_int8_mixed_noalloc",
+           lib().qa_qlinear_int8_mixed_noalloc(_p(X), M, K, _p(Wq), _p(s_w), _p(W16), N, float(threshold), _p(out),
+                                               _DTYPE_CODE[out.dtype], _stream(stream)))
     return out
 
 

@@ -139,6 +139,86 @@ bool valid_dtype(qa_dtype d) { return d == QA_F32 || d == QA_F16 || d == QA_BF16
 
 }  // namespace
 
+namespace qa {
+
+qa_status record_error(qa_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+qa_status mixed_validate(const char* fn, const void* X_f16, int64_t M, int64_t K, const int8_t* Wq,
+                         const float* s_w, const void* W_f16_or_null, int64_t N, float threshold, const void* out,
+                         qa_dtype out_dtype, bool with_workspace, const void* workspace, size_t workspace_bytes,
+                         bool* empty) {
+    *empty = false;
+    if (M < 0 || N < 0 || K <= 0 || K % 16 != 0 || K > kMaxK_i8)
+        return fail(QA_ERR_SHAPE, "%s: need M, N >= 0, 0 < K <= %lld, K %% 16 == 0", fn, (long long)kMaxK_i8);
+    if (std::isnan(threshold)) return fail(QA_ERR_VALUE, "%s: threshold is NaN", fn);
+    if (!valid_dtype(out_dtype)) return fail(QA_ERR_VALUE, "%s: bad out_dtype %d", fn, (int)out_dtype);
+    if (M == 0 || N == 0) {
+        *empty = true;
+        return ok();
+    }
+    if (!X_f16 || !Wq || !s_w || !out || (with_workspace && !workspace))
+        return fail(QA_ERR_NULL, "%s: NULL pointer", fn);
+    if (!aligned(X_f16, 16) || !aligned(Wq, 16) || !aligned(s_w, 4) || (with_workspace && !aligned(workspace, kAlign)) ||
+        (W_f16_or_null && !aligned(W_f16_or_null, 2)) || !aligned(out, 4))
+        return fail(QA_ERR_ALIGN, "%s: X, Wq 16-byte, workspace 256-byte, out/s_w 4-byte aligned", fn);
+    if (with_workspace && workspace_bytes < mixed_layout(M, K).total)
+        return fail(QA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, workspace_bytes, mixed_layout(M, K).total);
+    return ok();
+}
+
+qa_status mixed_run(const char* fn, const void* X_f16, int64_t M, int64_t K, const int8_t* Wq, const float* s_w,
+                    const void* W_f16_or_null, int64_t N, float threshold, void* out, qa_dtype out_dtype,
+                    void* workspace, void* stream) {
+    const MixedLayout L = mixed_layout(M, K);
+    const uint16_t* X = static_cast<const uint16_t*>(X_f16);
+    hipStream_t st = as_stream(stream);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    int32_t* idx = reinterpret_cast<int32_t*>(ws + L.idx);
+    int32_t* count = reinterpret_cast<int32_t*>(ws + L.count);
+    float* s_x = reinterpret_cast<float*>(ws + L.s_x);
+    int8_t* xq = reinterpret_cast<int8_t*>(ws + L.xq);
+    uint16_t* xo = reinterpret_cast<uint16_t*>(ws + L.xo);
+    if (decode_supported(M, K)) {
+        const hipError_t e = launch_decode_mixed(X, M, K, Wq, s_w, static_cast<const uint16_t*>(W_f16_or_null), N,
+                                                 threshold, out, (int)out_dtype, DecodeStages{idx, count, s_x, xq}, st);
+        return e == hipSuccess ? ok() : fail(QA_ERR_DEVICE, "%s (decode kernel): %s", fn, hipGetErrorString(e));
+    }
+    hipError_t e;
+    if (!(threshold < 65504.0f)) {
+        // no finite fp16 magnitude exceeds the threshold: no outlier columns
+        e = launch_rowquant_i8_no_outliers(X, M, K, xq, s_x, count, st);
+        if (e != hipSuccess) return fail(QA_ERR_DEVICE, "%s (row quantization): %s", fn, hipGetErrorString(e));
+    } else {
+        int segs = 1;
+        e = launch_outlier_flags(X, M, K, threshold, ws + L.cmax, &segs, st);
+        if (e != hipSuccess) return fail(QA_ERR_DEVICE, "%s (outlier columns): %s", fn, hipGetErrorString(e));
+        e = launch_rowquant_i8_flags(X, M, K, ws + L.cmax, segs, xq, s_x, idx, count, xo, st);
+        if (e != hipSuccess) return fail(QA_ERR_DEVICE, "%s (row quantization): %s", fn, hipGetErrorString(e));
+    }
+    MixedEpilogue ep;
+    ep.s_x = s_x;
+    ep.s_w = s_w;
+    ep.X = X;
+    ep.W16 = static_cast<const uint16_t*>(W_f16_or_null);
+    ep.Wq = Wq;
+    ep.idx = idx;
+    ep.count = count;
+    ep.Xo = rowquant_writes_xo(K) ? xo : nullptr;
+    ep.out = out;
+    ep.ldo = N;
+    ep.out_dtype = (int)out_dtype;
+    e = launch_gemm_i8_mixed(xq, Wq, M, K, N, ep, st);
+    return e == hipSuccess ? ok() : fail(QA_ERR_DEVICE, "%s (gemm): %s", fn, hipGetErrorString(e));
+}
+
+}  // namespace qa
+
 extern "C" {
 
 const char* qa_status_string(qa_status s) {
@@ -245,59 +325,12 @@ qa_status qa_qlinear_int8_mixed_offsets(int64_t M, int64_t K, size_t* offsets) {
 qa_status qa_qlinear_int8_mixed(const void* X_f16, int64_t M, int64_t K, const int8_t* Wq, const float* s_w,
                                 const void* W_f16_or_null, int64_t N, float threshold, void* out,
                                 qa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
-    if (M < 0 || N < 0 || K <= 0 || K % 16 != 0 || K > kMaxK_i8)
-        return fail(QA_ERR_SHAPE, "qa_qlinear_int8_mixed: need M, N >= 0, 0 < K <= %lld, K %% 16 == 0",
-                    (long long)kMaxK_i8);
-    if (std::isnan(threshold)) return fail(QA_ERR_VALUE, "qa_qlinear_int8_mixed: threshold is NaN");
-    if (!valid_dtype(out_dtype)) return fail(QA_ERR_VALUE, "qa_qlinear_int8_mixed: bad out_dtype %d", (int)out_dtype);
-    if (M == 0 || N == 0) return ok();
-    if (!X_f16 || !Wq || !s_w || !out || !workspace) return fail(QA_ERR_NULL, "qa_qlinear_int8_mixed: NULL pointer");
-    if (!aligned(X_f16, 16) || !aligned(Wq, 16) || !aligned(s_w, 4) || !aligned(workspace, kAlign) ||
-        (W_f16_or_null && !aligned(W_f16_or_null, 2)) || !aligned(out, 4))
-        return fail(QA_ERR_ALIGN, "qa_qlinear_int8_mixed: X, Wq 16-byte, workspace 256-byte, out/s_w 4-byte aligned");
-    const MixedLayout L = mixed_layout(M, K);
-    if (workspace_bytes < L.total)
-        return fail(QA_ERR_WORKSPACE, "qa_qlinear_int8_mixed: workspace %zu < %zu bytes", workspace_bytes, L.total);
-
-    const uint16_t* X = static_cast<const uint16_t*>(X_f16);
-    hipStream_t st = as_stream(stream);
-    uint8_t* ws = static_cast<uint8_t*>(workspace);
-    int32_t* idx = reinterpret_cast<int32_t*>(ws + L.idx);
-    int32_t* count = reinterpret_cast<int32_t*>(ws + L.count);
-    float* s_x = reinterpret_cast<float*>(ws + L.s_x);
-    int8_t* xq = reinterpret_cast<int8_t*>(ws + L.xq);
-    uint16_t* xo = reinterpret_cast<uint16_t*>(ws + L.xo);
-    if (qa::decode_supported(M, K))
-        return device_status(qa::launch_decode_mixed(X, M, K, Wq, s_w, static_cast<const uint16_t*>(W_f16_or_null),
-                                                     N, threshold, out, (int)out_dtype,
-                                                     qa::DecodeStages{idx, count, s_x, xq}, st),
-                             "qa_qlinear_int8_mixed (decode kernel)");
-
-    hipError_t e;
-    if (!(threshold < 65504.0f)) {
-        // no finite fp16 magnitude exceeds the threshold: no outlier columns
-        e = qa::launch_rowquant_i8_no_outliers(X, M, K, xq, s_x, count, st);
-        if (e != hipSuccess) return device_status(e, "qa_qlinear_int8_mixed (row quantization)");
-    } else {
-        int segs = 1;
-        e = qa::launch_outlier_flags(X, M, K, threshold, ws + L.cmax, &segs, st);
-        if (e != hipSuccess) return device_status(e, "qa_qlinear_int8_mixed (outlier columns)");
-        e = qa::launch_rowquant_i8_flags(X, M, K, ws + L.cmax, segs, xq, s_x, idx, count, xo, st);
-        if (e != hipSuccess) return device_status(e, "qa_qlinear_int8_mixed (row quantization)");
-    }
-    qa::MixedEpilogue ep;
-    ep.s_x = s_x;
-    ep.s_w = s_w;
-    ep.X = X;
-    ep.W16 = static_cast<const uint16_t*>(W_f16_or_null);
-    ep.Wq = Wq;
-    ep.idx = idx;
-    ep.count = count;
-    ep.Xo = qa::rowquant_writes_xo(K) ? xo : nullptr;
-    ep.out = out;
-    ep.ldo = N;
-    ep.out_dtype = (int)out_dtype;
-    return device_status(qa::launch_gemm_i8_mixed(xq, Wq, M, K, N, ep, st), "qa_qlinear_int8_mixed (gemm)");
+    bool empty = false;
+    const qa_status v = qa::mixed_validate("qa_qlinear_int8_mixed", X_f16, M, K, Wq, s_w, W_f16_or_null, N,
+                                           threshold, out, out_dtype, true, workspace, workspace_bytes, &empty);
+    if (v != QA_OK || empty) return v;
+    return qa::mixed_run("qa_qlinear_int8_mixed", X_f16, M, K, Wq, s_w, W_f16_or_null, N, threshold, out,
+                         out_dtype, workspace, stream);
 }
 
 // ----------------------------------------------------------------- top-k mixed linear

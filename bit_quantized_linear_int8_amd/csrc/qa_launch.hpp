@@ -6,7 +6,23 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "qa.h"
+
 namespace qa {
+
+// Shared by the C entry points (qa_api.cpp): record an error message for
+// qa_last_error() and return s; check every argument of an LLM.int8() call
+// (no HIP call; *empty is set for M == 0 or N == 0, a valid no-op); enqueue
+// the call's kernels on a workspace of at least qa_qlinear_int8_mixed_workspace
+// bytes.
+qa_status record_error(qa_status s, const char* fmt, ...);
+qa_status mixed_validate(const char* fn, const void* X_f16, int64_t M, int64_t K, const int8_t* Wq,
+                         const float* s_w, const void* W_f16_or_null, int64_t N, float threshold, const void* out,
+                         qa_dtype out_dtype, bool with_workspace, const void* workspace, size_t workspace_bytes,
+                         bool* empty);
+qa_status mixed_run(const char* fn, const void* X_f16, int64_t M, int64_t K, const int8_t* Wq, const float* s_w,
+                    const void* W_f16_or_null, int64_t N, float threshold, void* out, qa_dtype out_dtype,
+                    void* workspace, void* stream);
 
 // Scratch of the outlier-column scan: up to 32 row segments' partial flag
 // words (one 64-bit word per 64 columns) and partial column maxima [K], all

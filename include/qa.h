@@ -202,6 +202,33 @@ qa_status qa_qlinear_int8_mixed(const void* X_f16, int64_t M, int64_t K,
 qa_status qa_qlinear_int8_mixed_offsets(int64_t M, int64_t K, size_t* offsets);
 
 /* ---------------------------------------------------------------------------
+ * LLM.int8() mixed linear without a workspace  -- for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.
+ *
+ * Same arguments, kernels and results as qa_qlinear_int8_mixed, minus the
+ * workspace: the call's scratch lives in a static device array of
+ * QA_NOALLOC_SCRATCH_BYTES (40 MiB) that every GPU the library runs on holds
+ * until the process ends.  The call allocates nothing (no hipMalloc, hipFree
+ * or allocating library routine); the caller still provides X, Wq, s_w,
+ * W_f16 and out.  Nothing in the scratch needs clearing: every slot a call
+ * reads was written earlier in the same call.  All calls on one GPU share
+ * that one array, so calls that overlap on one GPU (on different streams,
+ * without ordering between them) race and give undefined results; calls on
+ * one stream, or otherwise ordered, are safe.  After the call the scratch
+ * holds the integer stages at the offsets of qa_qlinear_int8_mixed_offsets
+ * (until the next call on that GPU).
+ * Errors: as qa_qlinear_int8_mixed, and QA_ERR_WORKSPACE when
+ * qa_qlinear_int8_mixed_workspace(M, K) > QA_NOALLOC_SCRATCH_BYTES (e.g.
+ * M x K above about 33.5 million); QA_ERR_DEVICE if the scratch's device
+ * address cannot be looked up.
+ * ------------------------------------------------------------------------- */
+#define QA_NOALLOC_SCRATCH_BYTES ((size_t)40 << 20)
+qa_status qa_qlinear_int8_mixed_noalloc(const void* X_f16, int64_t M, int64_t K, const int8_t* Wq,
+                                        const float* s_w, const void* W_f16_or_null, int64_t N, float threshold,
+                                        void* out, qa_dtype out_dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
  * LLM.int8() linear with top-k decomposition  [AIInfra-Q01: decomposition
  * share raised to the top 1-2% of feature dimensions]
  *

@@ -467,3 +467,22 @@ def test_mixed_offsets():
     assert L.qa_qlinear_int8_mixed_offsets(4, 0, off) == SHAPE
     assert L.qa_qlinear_int8_mixed_offsets(4, 16, None) == NULL
     assert qa.last_error()
+
+
+def test_noalloc_argument_errors():
+    """The workspace-free LLM.int8() call checks its arguments, and the size of
+    the static scratch, before any HIP call."""
+    L = qa.lib()
+
+    def call(X=A, M=16, K=256, Wq=B, s_w=OUT, N=32, tau=6.0, out=OUT, dt=1):
+        return L.qa_qlinear_int8_mixed_noalloc(X, M, K, Wq, s_w, None, N, tau, out, dt, None)
+
+    assert call(X=None) == NULL and call(out=None) == NULL
+    assert call(M=-1) == SHAPE and call(K=24) == SHAPE
+    assert call(X=MIS) == ALIGN
+    assert call(tau=math.nan) == VALUE and call(dt=3) == VALUE
+    assert call(M=0) == OK and call(N=0) == OK
+    assert L.qa_qlinear_int8_mixed_workspace(4096, 16384) > qa.NOALLOC_SCRATCH_BYTES
+    assert call(M=4096, K=16384) == WORKSPACE
+    assert "static scratch" in qa.last_error()
+    assert L.qa_qlinear_int8_mixed_workspace(4096, 8192) <= qa.NOALLOC_SCRATCH_BYTES
