@@ -5,40 +5,47 @@
 // few KB.  Every workgroup owns 16 output channels and has eight waves; wave w
 // multiplies the 64-byte K steps w, w + 8, w + 16, ... so each weight load
 // instruction of the block covers 16 rows x 512 contiguous bytes.  A workgroup
-//   1. issues its X loads (thread t owns the 8-column chunk t of every token),
-//      the scale of the channel it writes in the epilogue, then ALL of its
-//      weight loads (directly in the B-operand layout of
-//      v_mfma_i32_16x16x64_i8, 16 bytes per lane and step),
+//   1. loads X (thread t owns the 8-column chunks t and t + 512 of every
+//      token) and the scale of the channel it writes in the epilogue, and only
+//      once this wave's X has arrived issues ALL of its weight loads (directly
+//      in the B-operand layout of v_mfma_i32_16x16x64_i8, 16 bytes per lane
+//      and step).  Issued behind the weight requests, the X requests (hits on
+//      lines every workgroup reads) queue behind weight misses in the caches
+//      and arrive about 1.5 us later; issued first and waited for, they
+//      arrive early and the weight stream finishes no later;
 //   2. while the weight bytes are in flight, recomputes -- identically in every
-//      workgroup -- the outlier columns (column max over the tokens, on the
-//      sign-cleared fp16 bit patterns with packed 16-bit max), the per-token
-//      scales and the int8 codes of X into LDS (the A operand), the ascending
-//      outlier list, the fp16 outlier activations, and starts the gather of
-//      the fp16 outlier weights,
+//      workgroup -- the outlier columns (column max over the tokens on the
+//      sign-cleared fp16 bit patterns, compared as integers with a threshold
+//      pattern), the per-token maxima over the other columns (a reduce-scatter
+//      over the lanes), the per-token scales, the ascending outlier list and
+//      the fp16 outlier activations, and the int8 codes of X into LDS (the A
+//      operand); then starts the gather of the fp16 outlier weights,
 //   3. multiplies its K steps on the MFMA, sums the eight int32 partial tiles
 //      in LDS, dequantizes by s_x[m] * s_w[n] and adds the outlier product.
-// Loads retire in order (vmcnt), so the X loads go first: the prologue only
-// waits for X, not for the weight stream behind it.
+// Its barriers wait only for LDS traffic, so the weight stream stays in
+// flight across them.
 //
 // Method: AIInfra 05Quantization01, LLM.int8(): outlier columns by magnitude
 // threshold, "a. 向量级量化" (per-token / per-channel absmax scales),
 // "b. INT8 矩阵乘法与反量化" (int32 accumulation, outer-product dequant) and
 // the merge with the fp16 outlier product; Quantization explained part 2 §1.2.
+#include <cmath>
+#include <cstring>
+
 #include "qa_device.hpp"
 #include "qa_launch.hpp"
 
 namespace qa {
 
-constexpr int DEC_MAXK = 4096;             // K <= 4096, K % 256 == 0
 constexpr int DEC_WAVES = 8, DEC_THREADS = 64 * DEC_WAVES;
-constexpr int DEC_MAXSTEPS = DEC_MAXK / 64 / DEC_WAVES;   // MFMA steps per wave
-constexpr int DEC_LDA = DEC_MAXK + 16;     // LDS row stride of the codes (spreads banks)
-constexpr int DEC_OCAP = 64;               // outliers whose operands are staged in LDS
-static_assert(DEC_MAXK / 8 == DEC_THREADS, "one 8-column chunk of X per thread");
+constexpr int DEC_CHUNK_K = 8 * DEC_THREADS;    // columns covered by one chunk per thread (4096)
+constexpr int DEC_OCAP = 64;                    // outliers whose operands are staged in LDS
 static_assert(DEC_WAVES == 8, "the wave totals are read as two 16-byte vectors");
 
-__device__ __forceinline__ float half_lo(uint32_t v) { return h2f((uint16_t)(v & 0xffffu)); }
-__device__ __forceinline__ float half_hi(uint32_t v) { return h2f((uint16_t)(v >> 16)); }
+typedef unsigned short u16x2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t u32_of(u16x2v v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ u16x2v v_of(uint32_t v) { return __builtin_bit_cast(u16x2v, v); }
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS accesses
 // (lgkmcnt(0)), not for its global loads, so the weight stream stays in
@@ -57,17 +64,39 @@ __device__ __forceinline__ uint32_t pick4(const u32x4& v, int i) {
     return (i & 2) ? hi : lo;
 }
 
-// Maximum of an unsigned value over the 64 lanes, in every lane: DPP within
-// rows of 16, then gfx950's row-pair and half-wave swaps (no scalar round trip).
-__device__ __forceinline__ uint32_t wave_max_all_u32(uint32_t v) {
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));    // quad_perm [1,0,3,2]
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));    // quad_perm [2,3,0,1]
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));   // row_half_mirror
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));   // row_mirror
-    const auto p16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-    v = max(p16[0], p16[1]);
-    const auto p32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-    return max(p32[0], p32[1]);
+// Two 16-bit maxima per lane with the value of another lane (DPP move, then
+// v_pk_max_u16; the packed max takes no DPP operand on gfx9).
+template <int CTRL>
+__device__ __forceinline__ uint32_t pkmax_dpp(uint32_t v) {
+    return pk_max_u16(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false));
+}
+
+// Reduce-scatter of eight per-token values (two 16-bit maxima each) over the
+// 64 lanes: on return lane L holds the wave-wide maximum of token L >> 3 (both
+// halves, not yet combined).  Three halving steps -- v_permlane32_swap pairs
+// tokens (m, m + 4), v_permlane16_swap pairs (0, 2) and (1, 3), a row_ror:8
+// move pairs the last two -- then three DPP steps within groups of 8 lanes.
+// 18 VALU instructions instead of 8 full wave reductions.
+__device__ __forceinline__ uint32_t reduce_scatter8(const uint32_t* v) {
+    uint32_t a[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {      // lanes 0-31: token m, lanes 32-63: token m + 4
+        const auto p = __builtin_amdgcn_permlane32_swap(v[m], v[m + 4], false, false);
+        a[m] = pk_max_u16(p[0], p[1]);
+    }
+    uint32_t b[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {      // rows 0..3: tokens m, m + 2, m + 4, m + 6
+        const auto p = __builtin_amdgcn_permlane16_swap(a[m], a[m + 2], false, false);
+        b[m] = pk_max_u16(p[0], p[1]);
+    }
+    const bool hi8 = (__lane_id() & 8) != 0;   // lanes with bit 3 set keep the odd tokens
+    const uint32_t mine = hi8 ? b[1] : b[0], other = hi8 ? b[0] : b[1];
+    uint32_t r = pk_max_u16(mine, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)other, 0x128, 0xF, 0xF, false));  // row_ror:8
+    r = pkmax_dpp<0xB1>(r);            // quad_perm [1,0,3,2]
+    r = pkmax_dpp<0x4E>(r);            // quad_perm [2,3,0,1]
+    r = pkmax_dpp<0x141>(r);           // row_half_mirror
+    return r;
 }
 
 // Eight int8 codes rint(fl32(x / s)) of one chunk without a division, with
@@ -79,8 +108,9 @@ __device__ __forceinline__ uint32_t wave_max_all_u32(uint32_t v) {
 // elementary functions on the IBM RISC System/6000 processor", 1990), which
 // is the correctly rounded fl32(x / s).  Both facts hold for every fp16 x and
 // every scale fl32(a / 127) of an fp16 a >= |x| -- the per-token scales here;
-// the test suite checks all 1.0e9 such pairs on the CPU.
-__device__ __forceinline__ u32x2 codes8_dec(const u32x4& v, float s, float r) {
+// the test suite checks all 1.0e9 such pairs on the CPU.  The codes are
+// returned biased by 128 (bytes rint + 128); the caller un-biases and masks.
+__device__ __forceinline__ u32x2 codes8_biased(const u32x4& v, float s, float r) {
     float x[8], n[8];
     float dmax = 0.0f;
 #pragma unroll
@@ -103,194 +133,285 @@ __device__ __forceinline__ u32x2 codes8_dec(const u32x4& v, float s, float r) {
     for (int j = 0; j < 4; ++j) lo = __builtin_amdgcn_cvt_pk_u8_f32(n[j], j, lo);
 #pragma unroll
     for (int j = 0; j < 4; ++j) hi = __builtin_amdgcn_cvt_pk_u8_f32(n[j + 4], j, hi);
-    return u32x2{lo ^ 0x80808080u, hi ^ 0x80808080u};
+    return u32x2{lo, hi};
 }
 
-template <int MB>
-__global__ __launch_bounds__(DEC_THREADS) void k_decode_mixed(const uint16_t* __restrict__ X, int M, int K,
-                                                              const int8_t* __restrict__ Wq,
-                                                              const float* __restrict__ s_w,
-                                                              const uint16_t* __restrict__ W16, int64_t N, float tau,
-                                                              void* __restrict__ out, int out_dtype,
-                                                              DecodeStages st) {
-    __shared__ __attribute__((aligned(16))) int8_t aq[MB * DEC_LDA];
-    __shared__ int32_t oidx[DEC_MAXK];
+// Barrier over the eight activation waves only (the weight waves may be
+// stalled issuing their loads): an LDS counter, set to zero before the first
+// workgroup barrier, that every activation wave increments once its LDS
+// writes are done, then waits for until all eight have.
+__device__ __forceinline__ void activation_barrier(int* ctr, int lane) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);      // this wave's LDS writes are done
+    if (lane == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < DEC_WAVES)
+        __builtin_amdgcn_s_sleep(1);
+    asm volatile("" ::: "memory");
+}
+
+// MB: tokens per block (4, 8 or 16); CH: 8-column chunks per thread (K <= 4096 CH).
+//
+// Sixteen waves in two roles, two of each per SIMD.  Activation waves 0-7
+// (threads t < 512) load X and compute everything that depends only on it;
+// weight waves 8-15 issue the weight stream and run the MFMAs.  A wave that
+// issues more loads than its compute unit can keep in flight stalls until
+// earlier ones return -- about 2 us for this 64 KB per workgroup -- so the
+// weight loads are issued by waves that have nothing else to do meanwhile.
+template <int MB, int CH>
+__global__ __launch_bounds__(2 * DEC_THREADS) void k_decode_mixed(const uint16_t* __restrict__ X, int M, int K,
+                                                                  const int8_t* __restrict__ Wq,
+                                                                  const float* __restrict__ s_w,
+                                                                  const uint16_t* __restrict__ W16, int64_t N,
+                                                                  uint32_t thr1, void* __restrict__ out,
+                                                                  int out_dtype, DecodeStages st) {
+    constexpr int MAXK = DEC_CHUNK_K * CH;
+    constexpr int LDA = MAXK + 16;                  // LDS row stride of the codes (spreads banks)
+    constexpr int STEPS = MAXK / 64 / DEC_WAVES;    // MFMA steps per weight wave
+    constexpr int NG = MB > 8 ? 2 : 1;              // groups of eight tokens for the lane reductions
+    __shared__ __attribute__((aligned(16))) int8_t aq[MB * LDA];
+    __shared__ int16_t oidx[MAXK];
     __shared__ int32_t red[DEC_WAVES][256];
     __shared__ float xo[DEC_OCAP][16];       // outlier activations  [h][m]
     __shared__ float wo[DEC_OCAP][16];       // outlier weights w~   [h][channel]
-    __shared__ uint32_t rmax[DEC_WAVES][MB];
+    __shared__ __attribute__((aligned(16))) uint32_t rmax[16][DEC_WAVES];   // [token][activation wave]
     __shared__ float sx_s[16];
-    __shared__ __attribute__((aligned(16))) int wtot[DEC_WAVES];
+    __shared__ __attribute__((aligned(16))) int wtot[CH][DEC_WAVES];
+    __shared__ int abar;
+    __shared__ int count_s;
 
-    const int t = threadIdx.x, lane = t & 63, wave = wave_id();
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const bool act = wave < DEC_WAVES;
+    const int t = threadIdx.x & (DEC_THREADS - 1);    // index within the role
     const int64_t n0 = (int64_t)blockIdx.x * 16;
     const int S = K >> 6;                             // 64-byte MFMA steps in K
     const int nch = K >> 3;                           // 8-column chunks of X
-    const bool own = t < nch;
-
-    // 1a. X chunk t of every token (tokens past M read zeros)
-    const rsrc_t rsx = make_rsrc(X, (int64_t)M * K * 2);
-    u32x4 xv[MB];
-#pragma unroll
-    for (int m = 0; m < MB; ++m) xv[m] = bload16(rsx, own ? (uint32_t)(m * K + 8 * t) * 2 : kOOB);
-    // 1b. scale of channel n0 + t % 16 (outlier gather and epilogue), ahead of
-    //     the weight stream so that nothing in the prologue waits for the latter
     const rsrc_t rsn = make_rsrc(s_w + n0, (N - n0) * 4);
-    const float swg = __builtin_bit_cast(float, bload4(rsn, (uint32_t)(t & 15) * 4));
-    // Every wave has issued its X loads before any wave issues weight loads,
-    // so the X requests are not queued behind weight traffic (no wait here).
-    __builtin_amdgcn_s_barrier();
-    // 1c. the weight slice: row n0 + lane % 16, bytes 64 s + 16 (lane / 16) of step s = wave + 8 j
-    v4i wv[DEC_MAXSTEPS];
+    const float swg = __builtin_bit_cast(float, bload4(rsn, (uint32_t)(t & 15) * 4));   // scale of channel n0 + t % 16
     const rsrc_t rsw = make_rsrc(Wq + n0 * K, (N - n0) * K);       // channels past N read zeros
-    {
-        const uint32_t wo0 = (uint32_t)((lane & 15) * K + 16 * (lane >> 4));
+    if (threadIdx.x == 0) abar = 0;
+
+    v4i acc = v4i{0, 0, 0, 0};
+    int count = 0;
+    if (act) {
+        // ---------------------------------------------------------------- activation waves
+        // 1. X chunks t + 512 c of every token (tokens past M and chunks past K read zeros)
+        const rsrc_t rsx = make_rsrc(X, (int64_t)M * K * 2);
+        u32x4 xv[CH][MB];
 #pragma unroll
-        for (int j = 0; j < DEC_MAXSTEPS; ++j) {
-            const int s = wave + DEC_WAVES * j;
-            wv[j] = __builtin_bit_cast(v4i, bload16(rsw, s < S ? wo0 + 64 * s : kOOB));
+        for (int c = 0; c < CH; ++c) {
+            const int ch = t + DEC_THREADS * c;
+#pragma unroll
+            for (int m = 0; m < MB; ++m) xv[c][m] = bload16(rsx, ch < nch ? (uint32_t)(m * K + 8 * ch) * 2 : kOOB);
         }
-    }
+        // the weight waves issue their stream once every activation wave holds its X
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        lds_barrier();                                                  // barrier 1
 
-    // 2a. column max over the tokens on |x| bit patterns (fp16 magnitudes order
-    //     like their bits), outlier flags of the chunk (8 bits), then the
-    //     per-token absmax over the non-outlier columns.
-    uint32_t cm[4] = {0u, 0u, 0u, 0u};
+        // 2a. column max over the tokens on |x| bit patterns (fp16 magnitudes
+        //     order like their bits); column j is an outlier when that max is
+        //     >= thr1 (the threshold as an fp16 pattern, see launch_decode_mixed).
+        //     keep: 0xffff per ordinary column.  Then the per-token maxima over
+        //     the ordinary columns, reduce-scattered over the lanes.
+        uint32_t keep[CH][4];
+        uint32_t flags[CH];
+        uint32_t rm[NG * 8];
 #pragma unroll
-    for (int m = 0; m < MB; ++m)
+        for (int m = 0; m < NG * 8; ++m) rm[m] = 0u;
+        const u16x2v T = u16x2v{(unsigned short)thr1, (unsigned short)thr1};
 #pragma unroll
-        for (int d = 0; d < 4; ++d) cm[d] = pk_max_u16(cm[d], xv[m][d] & 0x7fff7fffu);
-    uint32_t flags = 0;
-    uint32_t keep[4];
+        for (int c = 0; c < CH; ++c) {
+            uint32_t cm[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        const bool olo = half_lo(cm[d]) > tau, ohi = half_hi(cm[d]) > tau;
-        flags |= (olo ? 1u : 0u) << (2 * d);
-        flags |= (ohi ? 1u : 0u) << (2 * d + 1);
-        keep[d] = (olo ? 0u : 0xffffu) | (ohi ? 0u : 0xffff0000u);
-    }
-    flags = own ? flags : 0u;
-    const u32x4 keepw = u32x4{keep[0], keep[1], keep[2], keep[3]};   // 0xffff per ordinary column
-    {
-        uint32_t mine = 0u;                           // lane m keeps token m's maximum
+            for (int m = 0; m < MB; ++m)
 #pragma unroll
-        for (int m = 0; m < MB; ++m) {
-            uint32_t r = 0u;
+                for (int d = 0; d < 4; ++d) cm[d] = pk_max_u16(cm[d], xv[c][m][d] & 0x7fff7fffu);
+            uint32_t f = 0u;
 #pragma unroll
-            for (int d = 0; d < 4; ++d) r = pk_max_u16(r, xv[m][d] & 0x7fff7fffu & keep[d]);
-            const uint32_t a = wave_max_all_u32(max(r & 0xffffu, r >> 16));
-            mine = lane == m ? a : mine;
+            for (int d = 0; d < 4; ++d) {
+                // 1 per ordinary half (thr1 - cm > 0), 0 per outlier half
+                const u16x2v k1 = __builtin_elementwise_min(__builtin_elementwise_sub_sat(T, v_of(cm[d])),
+                                                            u16x2v{1, 1});
+                keep[c][d] = u32_of(u16x2v{0, 0} - k1);
+                const uint32_t kb = u32_of(k1);
+                f |= ((kb & 1u) | ((kb >> 15) & 2u)) << (2 * d);
+            }
+            flags[c] = (t + DEC_THREADS * c < nch) ? (~f & 0xffu) : 0u;
+#pragma unroll
+            for (int m = 0; m < MB; ++m) {
+                const uint32_t r01 = pk_max_u16(xv[c][m][0] & 0x7fff7fffu & keep[c][0],
+                                                xv[c][m][1] & 0x7fff7fffu & keep[c][1]);
+                const uint32_t r23 = pk_max_u16(xv[c][m][2] & 0x7fff7fffu & keep[c][2],
+                                                xv[c][m][3] & 0x7fff7fffu & keep[c][3]);
+                rm[m] = pk_max_u16(rm[m], pk_max_u16(r01, r23));
+            }
         }
-        if (lane < MB) rmax[wave][lane] = mine;
-    }
-
-    float s_l = 1.0f, r_l = 1.0f;                     // lane m < MB: scale of token m, its reciprocal
-
-    // 2b. ascending outlier list (block-wide exclusive scan over the chunks,
-    //     the in-wave part from one ballot per flag bit); the owner of an
-    //     outlier column also stages its activations.
-    {
-        int below = 0, wsum = 0;
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            const uint64_t mb = __ballot((flags >> b) & 1u);
-            below += bits_below(mb);
-            wsum += __popcll(mb);
+        for (int g = 0; g < NG; ++g) {
+            const uint32_t r = reduce_scatter8(rm + 8 * g);
+            const uint32_t a = max(r & 0xffffu, r >> 16);
+            if ((lane & 7) == 0) rmax[8 * g + (lane >> 3)][wave] = a;
         }
-        if (lane == 0) wtot[wave] = wsum;
-        lds_barrier();
 
-        // per-token scales: lane m < MB reduces token m over the waves
-        // (every wave does, so no further barrier is needed)
+        // 2b. ascending outlier list: the columns of chunk set 0 (chunks t) come
+        //     before those of set 1 (chunks t + 512); within a set, an exclusive
+        //     scan over the chunks, the in-wave part from one ballot per flag bit
+        //     (skipped by waves without outlier columns).  The owner of an
+        //     outlier column also stages its activations.
+        uint32_t anyf = 0u;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) anyf |= flags[c];
+        const bool any = __ballot(anyf != 0u) != 0ull;
+        int below[CH], wsum[CH];
+#pragma unroll
+        for (int c = 0; c < CH; ++c) below[c] = wsum[c] = 0;
+        if (any) {
+#pragma unroll
+            for (int c = 0; c < CH; ++c)
+#pragma unroll
+                for (int b = 0; b < 8; ++b) {
+                    const uint64_t mb = __ballot((flags[c] >> b) & 1u);
+                    below[c] += bits_below(mb);
+                    wsum[c] += __popcll(mb);
+                }
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (int c = 0; c < CH; ++c) wtot[c][wave] = wsum[c];
+        }
+        activation_barrier(&abar, lane);
+
+        // per-token scales: lane m < MB reduces token m over the waves (every
+        // activation wave does, so no further barrier is needed)
+        float s_l = 1.0f, r_l = 1.0f;
         if (lane < MB) {
-            uint32_t ab = 0u;
-#pragma unroll
-            for (int w = 0; w < DEC_WAVES; ++w) ab = max(ab, rmax[w][lane]);
+            const u32x4 r0 = *reinterpret_cast<const u32x4*>(&rmax[lane][0]);
+            const u32x4 r1 = *reinterpret_cast<const u32x4*>(&rmax[lane][4]);
+            const uint32_t ab = max(max(max(r0[0], r0[1]), max(r0[2], r0[3])),
+                                    max(max(r1[0], r1[1]), max(r1[2], r1[3])));
             const float a = h2f((uint16_t)ab);
             s_l = a == 0.0f ? 1.0f : a / 127.0f;
             r_l = 1.0f / s_l;
             if (wave == 0) sx_s[lane] = s_l;
         }
 
-        const int4 wt0 = *reinterpret_cast<const int4*>(wtot), wt1 = *reinterpret_cast<const int4*>(wtot + 4);
-        const int wt[8] = {wt0.x, wt0.y, wt0.z, wt0.w, wt1.x, wt1.y, wt1.z, wt1.w};
-        int off = below;
+        int total0 = 0, wbase[CH];
 #pragma unroll
-        for (int w = 0; w < DEC_WAVES; ++w) off += w < wave ? wt[w] : 0;
-        uint32_t f = flags;
-        while (f) {
-            const int j = __builtin_ctz(f);
-            f &= f - 1u;
-            oidx[off] = 8 * t + j;
-            if (off < DEC_OCAP) {
+        for (int c = 0; c < CH; ++c) {
+            const int4 wt0 = *reinterpret_cast<const int4*>(&wtot[c][0]);
+            const int4 wt1 = *reinterpret_cast<const int4*>(&wtot[c][4]);
+            const int wt[8] = {wt0.x, wt0.y, wt0.z, wt0.w, wt1.x, wt1.y, wt1.z, wt1.w};
+            int tot = 0, bs = 0;
 #pragma unroll
-                for (int m = 0; m < MB; ++m) {
-                    const uint32_t w32 = pick4(xv[m], j >> 1);
-                    xo[off][m] = (j & 1) ? half_hi(w32) : half_lo(w32);
+            for (int w = 0; w < DEC_WAVES; ++w) {
+                tot += wt[w];
+                bs += w < wave ? wt[w] : 0;
+            }
+            wbase[c] = bs + (c == 1 ? total0 : 0);
+            if (c == 0) total0 = tot;
+            count += tot;
+        }
+        if (t == 0) count_s = count;
+        if (any) {
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                uint32_t f = flags[c];
+                int o = wbase[c] + below[c];
+                while (f) {
+                    const int j = __builtin_ctz(f);
+                    f &= f - 1u;
+                    oidx[o] = (int16_t)(8 * (t + DEC_THREADS * c) + j);
+                    if (o < DEC_OCAP) {
+#pragma unroll
+                        for (int m = 0; m < MB; ++m) {
+                            const uint32_t w32 = pick4(xv[c][m], j >> 1);
+                            xo[o][m] = h2f((uint16_t)((j & 1) ? (w32 >> 16) : (w32 & 0xffffu)));
+                        }
+                    }
+                    ++o;
                 }
             }
-            ++off;
         }
-    }
-    int count = 0;
-#pragma unroll
-    for (int w = 0; w < DEC_WAVES; ++w) count += wtot[w];
 
-    // 2c. int8 codes of X into LDS (outlier columns -> 0 -> code 0; tokens
-    //     past M read zeros, have scale 1 and get codes 0, which no MFMA reads)
-    if (own) {
+        // 2c. int8 codes of X into LDS: biased codes from the division-free
+        //     rounding, un-biased (XOR 0x80) and zeroed in the outlier columns
+        //     by the byte mask of the keep words; tokens past M read zeros, have
+        //     scale 1 and get codes 0, which no MFMA reads
 #pragma unroll
-        for (int m = 0; m < MB; ++m) {
-            const float s = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s_l), m));
-            const float r = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r_l), m));
-            *reinterpret_cast<u32x2*>(aq + m * DEC_LDA + 8 * t) = codes8_dec(xv[m] & keepw, s, r);
+        for (int c = 0; c < CH; ++c) {
+            const int ch = t + DEC_THREADS * c;
+            if (ch < nch) {
+                const uint32_t kb0 = __builtin_amdgcn_perm(keep[c][1], keep[c][0], 0x06040200u);
+                const uint32_t kb1 = __builtin_amdgcn_perm(keep[c][3], keep[c][2], 0x06040200u);
+#pragma unroll
+                for (int m = 0; m < MB; ++m) {
+                    const float s = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s_l), m));
+                    const float r = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r_l), m));
+                    const u32x2 q = codes8_biased(xv[c][m], s, r);
+                    *reinterpret_cast<u32x2*>(aq + m * LDA + 8 * ch) =
+                        u32x2{(q[0] ^ 0x80808080u) & kb0, (q[1] ^ 0x80808080u) & kb1};
+                }
+            }
         }
-    }
-    lds_barrier();
-
-
-    // 2d. start the gather of the outlier weights (first 64): the fp16 W[n][h]
-    //     or the int8 code Wq[n][h], as the aligned 32-bit word holding it.
-    //     The loads are unconditional (the descriptor is selected) and their
-    //     values are used only after the MFMA, so no wait lands here.
-    const int gch = t & 15, gh = t >> 4;              // channel n0 + gch, outlier slots gh + 32 q
-    const rsrc_t rs16 = make_rsrc(W16 ? W16 + n0 * K : nullptr, W16 ? (N - n0) * K * 2 : 0);
-    const rsrc_t rsg = W16 ? rs16 : rsw;
-    constexpr int GQ = DEC_OCAP / (DEC_THREADS / 16);
-    uint32_t graw[GQ], gsh[GQ];
+        lds_barrier();                                                  // barrier 2: codes, list, scales
+        lds_barrier();                                                  // barrier 3: partial tiles
+    } else {
+        // ---------------------------------------------------------------- weight waves
+        const int ww = wave - DEC_WAVES;
+        lds_barrier();                                                  // barrier 1: X is in
+        // the weight slice: row n0 + lane % 16, bytes 64 s + 16 (lane / 16) of step s = ww + 8 j
+        v4i wv[STEPS];
+        {
+            const uint32_t wo0 = (uint32_t)((lane & 15) * K + 16 * (lane >> 4));
 #pragma unroll
-    for (int q = 0; q < GQ; ++q) {
-        const int h = gh + (DEC_THREADS / 16) * q;
-        const uint32_t k = (uint32_t)oidx[h < count ? h : 0];
-        const uint32_t e = (uint32_t)gch * K + k;     // element offset in the channel block
-        const uint32_t b = W16 ? 2 * e : e;           // byte offset
-        graw[q] = bload4(rsg, h < count ? (b & ~3u) : kOOB);
-        gsh[q] = (b & 3u) * 8;
-    }
-
-    // 3a. int32 MFMA over this wave's K steps
-    v4i acc = v4i{0, 0, 0, 0};
-    const int arow = lane & 15;
-#pragma unroll
-    for (int j = 0; j < DEC_MAXSTEPS; ++j) {
-        const int s = wave + DEC_WAVES * j;
-        if (s < S) {
-            v4i fa = v4i{0, 0, 0, 0};
-            if (arow < M) fa = *reinterpret_cast<const v4i*>(aq + arow * DEC_LDA + 64 * s + 16 * (lane >> 4));
-            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa, wv[j], acc, 0, 0, 0);
+            for (int j = 0; j < STEPS; ++j) {
+                const int s = ww + DEC_WAVES * j;
+                wv[j] = __builtin_bit_cast(v4i, bload16(rsw, s < S ? wo0 + 64 * s : kOOB));
+            }
         }
-    }
-    // acc: lane l, element e = token 4 (l / 16) + e, channel l % 16
+        lds_barrier();                                                  // barrier 2
+        count = count_s;
+        // start the gather of the outlier weights (first 64): the fp16 W[n][h]
+        // or the int8 code Wq[n][h], as the aligned 32-bit word holding it; the
+        // loads are unconditional (the descriptor is selected) and queue behind
+        // the weight stream, whose use waits for them anyway
+        const int gch = t & 15, gh = t >> 4;          // channel n0 + gch, outlier slots gh + 32 q
+        const rsrc_t rs16 = make_rsrc(W16 ? W16 + n0 * K : nullptr, W16 ? (N - n0) * K * 2 : 0);
+        const rsrc_t rsg = W16 ? rs16 : rsw;
+        constexpr int GQ = DEC_OCAP / (DEC_THREADS / 16);
+        uint32_t graw[GQ], gsh[GQ];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) red[wave][(4 * (lane >> 4) + e) * 16 + (lane & 15)] = acc[e];
+        for (int q = 0; q < GQ; ++q) {
+            const int h = gh + (DEC_THREADS / 16) * q;
+            const uint32_t k = (uint32_t)oidx[h < count ? h : 0];
+            const uint32_t e = (uint32_t)gch * K + k;     // element offset in the channel block
+            const uint32_t b = W16 ? 2 * e : e;           // byte offset
+            graw[q] = bload4(rsg, h < count ? (b & ~3u) : kOOB);
+            gsh[q] = (b & 3u) * 8;
+        }
+        // 3a. int32 MFMA over this wave's K steps
+        const int arow = lane & 15;
 #pragma unroll
-    for (int q = 0; q < GQ; ++q) {
-        const uint32_t v = graw[q] >> gsh[q];         // zero for an empty slot
-        wo[gh + (DEC_THREADS / 16) * q][gch] = W16 ? h2f((uint16_t)v) : h2f(f2h(swg * (float)(int8_t)(uint8_t)v));
+        for (int j = 0; j < STEPS; ++j) {
+            const int s = ww + DEC_WAVES * j;
+            if (s < S) {
+                v4i fa = v4i{0, 0, 0, 0};
+                if (arow < M) fa = *reinterpret_cast<const v4i*>(aq + arow * LDA + 64 * s + 16 * (lane >> 4));
+                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa, wv[j], acc, 0, 0, 0);
+            }
+        }
+        // acc: lane l, element e = token 4 (l / 16) + e, channel l % 16
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[ww][(4 * (lane >> 4) + e) * 16 + (lane & 15)] = acc[e];
+#pragma unroll
+        for (int q = 0; q < GQ; ++q) {
+            const uint32_t v = graw[q] >> gsh[q];         // zero for an empty slot
+            wo[gh + (DEC_THREADS / 16) * q][gch] = W16 ? h2f((uint16_t)v) : h2f(f2h(swg * (float)(int8_t)(uint8_t)v));
+        }
+        lds_barrier();                                                  // barrier 3
+        return;
     }
-    lds_barrier();
 
-    // 3b. epilogue: thread t < 256 -> token m = t / 16, channel n0 + t % 16
+    // 3b. epilogue (activation threads t < 256): token m = t / 16, channel n0 + t % 16
     const int m = t >> 4, ch = t & 15;
     const int64_t n = n0 + ch;
     if (t < 256 && m < M && n < N) {
@@ -321,31 +442,64 @@ __global__ __launch_bounds__(DEC_THREADS) void k_decode_mixed(const uint16_t* __
         if (t == 0) *st.count = count;
         if (t < M) st.s_x[t] = sx_s[t];
         const int cpr = K >> 4;                       // 16-byte chunks per row
-        for (int c = t; c < M * cpr; c += DEC_THREADS) {
-            const int r = c / cpr, j = c - r * cpr;
+        for (int q = t; q < M * cpr; q += DEC_THREADS) {
+            const int r = q / cpr, j = q - r * cpr;
             *reinterpret_cast<v4i*>(st.xq + (int64_t)r * K + 16 * j) =
-                *reinterpret_cast<const v4i*>(aq + r * DEC_LDA + 16 * j);
+                *reinterpret_cast<const v4i*>(aq + r * LDA + 16 * j);
         }
     }
 }
 
 bool decode_supported(int64_t M, int64_t K) {
-    return M >= 1 && M <= 16 && K >= 256 && K <= DEC_MAXK && K % 256 == 0;
+    if (M < 1 || K < 256 || K % 256 != 0) return false;
+    return (M <= 16 && K <= DEC_CHUNK_K) || (M <= 8 && K <= 2 * DEC_CHUNK_K);
+}
+
+// The threshold as an fp16 bit pattern: column j is an outlier when
+// max_i |X[i][j]| > tau (fp32), i.e. when its largest |x| pattern is >= thr1,
+// with thr1 = 1 + the pattern of the largest fp16 <= tau (0 when tau < 0: every
+// column; 0x7c00 when tau >= 65504: no finite magnitude exceeds it).
+static uint32_t threshold_pattern(float tau) {
+    if (!(tau >= 0.0f)) return 0u;
+    if (tau >= 65504.0f) return 0x7c00u;
+    uint32_t lo = 0, hi = 0x7bff;                     // largest pattern p with value(p) <= tau
+    while (lo < hi) {
+        const uint32_t mid = (lo + hi + 1) / 2;
+        const int e = (int)(mid >> 10), f = (int)(mid & 1023);
+        const double v = e == 0 ? std::ldexp((double)f, -24) : std::ldexp((double)(f | 1024), e - 25);
+        if (v <= (double)tau)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo + 1;
+}
+
+template <int MB, int CH>
+static void launch_mb(const dim3& grid, hipStream_t st, const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq,
+                      const float* s_w, const uint16_t* W16, int64_t N, uint32_t thr1, void* out, int out_dtype,
+                      const DecodeStages& stages) {
+    hipLaunchKernelGGL((k_decode_mixed<MB, CH>), grid, dim3(2 * DEC_THREADS), 0, st, X, (int)M, (int)K, Wq, s_w, W16, N,
+                       thr1, out, out_dtype, stages);
 }
 
 hipError_t launch_decode_mixed(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* s_w,
                                const uint16_t* W16, int64_t N, float tau, void* out, int out_dtype,
                                const DecodeStages& stages, hipStream_t st) {
-    const dim3 grid((unsigned)((N + 15) / 16)), block(DEC_THREADS);
-    if (M <= 4)
-        hipLaunchKernelGGL(k_decode_mixed<4>, grid, block, 0, st, X, (int)M, (int)K, Wq, s_w, W16, N, tau, out,
-                           out_dtype, stages);
-    else if (M <= 8)
-        hipLaunchKernelGGL(k_decode_mixed<8>, grid, block, 0, st, X, (int)M, (int)K, Wq, s_w, W16, N, tau, out,
-                           out_dtype, stages);
-    else
-        hipLaunchKernelGGL(k_decode_mixed<16>, grid, block, 0, st, X, (int)M, (int)K, Wq, s_w, W16, N, tau, out,
-                           out_dtype, stages);
+    const dim3 grid((unsigned)((N + 15) / 16));
+    const uint32_t thr1 = threshold_pattern(tau);
+    if (K > DEC_CHUNK_K) {
+        if (M <= 4)
+            launch_mb<4, 2>(grid, st, X, M, K, Wq, s_w, W16, N, thr1, out, out_dtype, stages);
+        else
+            launch_mb<8, 2>(grid, st, X, M, K, Wq, s_w, W16, N, thr1, out, out_dtype, stages);
+    } else if (M <= 4) {
+        launch_mb<4, 1>(grid, st, X, M, K, Wq, s_w, W16, N, thr1, out, out_dtype, stages);
+    } else if (M <= 8) {
+        launch_mb<8, 1>(grid, st, X, M, K, Wq, s_w, W16, N, thr1, out, out_dtype, stages);
+    } else {
+        launch_mb<16, 1>(grid, st, X, M, K, Wq, s_w, W16, N, thr1, out, out_dtype, stages);
+    }
     return hipGetLastError();
 }
 

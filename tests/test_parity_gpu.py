@@ -268,11 +268,13 @@ def test_mixed_outlier_staging_paths(qa, M, K, N, n_dims, pass_w16):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 256, 1), (3, 512, 17), (4, 768, 40), (7, 1024, 33), (8, 4096, 64),
-                                   (9, 2048, 48), (12, 256, 100), (16, 4096, 20)])
+                                   (9, 2048, 48), (12, 256, 100), (16, 4096, 20),
+                                   # K above 4096 (M <= 8): two 8-column chunks per thread
+                                   (8, 8192, 48), (5, 6144, 40), (3, 4352, 17), (1, 8192, 100)])
 @pytest.mark.parametrize("tau", [6.0, float("inf"), -1.0])
 @pytest.mark.parametrize("pass_w16", [True, False])
 def test_mixed_decode_kernel_shapes(qa, M, K, N, tau, pass_w16):
-    # M <= 16 with K % 256 == 0, K <= 4096 runs the fused single-kernel path
+    # M <= 16 with K % 256 == 0, K <= 4096 (or M <= 8, K <= 8192) runs the fused single-kernel path
     X, W, _ = synthetic.mixed_inputs(M, K, N, seed=M * 13 + K + N, n_dims=6, magnitude=("abs_normal", 20.0),
                                      p_token=1.0)
     _mixed_case(qa, X, W, tau, 1, pass_w16)
@@ -295,10 +297,37 @@ def test_mixed_decode_kernel_ties(qa, tau):
     _mixed_case(qa, X, W, tau, 0, False)
 
 
-def test_mixed_decode_kernel_many_outliers(qa):
-    X, W, _ = synthetic.mixed_inputs(8, 4096, 96, seed=21, n_dims=300, p_token=0.6)
+@pytest.mark.parametrize("K", [4096, 8192])
+def test_mixed_decode_kernel_many_outliers(qa, K):
+    X, W, _ = synthetic.mixed_inputs(8, K, 96, seed=21 + K, n_dims=300, p_token=0.6)
     for dt in (0, 1, 2):
         _mixed_case(qa, X, W, 6.0, dt, False)
+
+
+@pytest.mark.parametrize("tau", [6.0, 1e-3, 0.0, 65504.0, 100.0])
+def test_mixed_decode_kernel_thresholds(qa, tau):
+    """Thresholds that are and are not fp16 values, zero, the largest finite
+    fp16 and values just below magnitudes present in X: the decode kernel
+    compares fp16 patterns against the threshold's pattern, which must pick
+    exactly the columns with max |x| > tau."""
+    X, W, _ = synthetic.mixed_inputs(6, 1024, 40, seed=int(tau * 7) % 1000 + 3, n_dims=5,
+                                     magnitude=("uniform", 6.0, 120.0))
+    X[1, 5] = np.float16(6.0)
+    X[2, 9] = np.float16(100.0)
+    X[3, 11] = np.float16(np.nextafter(np.float16(100.0), np.float16(0)))
+    X[0, 12] = np.float16(1e-3)
+    _mixed_case(qa, X, W, tau, 0, True)
+
+
+def test_mixed_decode_k8192_one_hot_codes(qa):
+    """The pages' 8192 hidden size at decode (8 tokens), six planted outlier
+    dims, threshold 6, a one-hot weight: every int8 code is visible in the
+    output, and the integer stages are compared bit for bit."""
+    X, _, _ = synthetic.mixed_inputs(8, 8192, 1, seed=77, n_dims=6, magnitude=("abs_normal", 20.0), p_token=1.0)
+    N = 2048
+    W = np.zeros((N, 8192), np.float16)
+    W[np.arange(N), 4 * np.arange(N) + 1] = 1.0
+    _mixed_case(qa, X, W, 6.0, 0, False)
 
 
 def test_mixed_tiny_config(qa):
