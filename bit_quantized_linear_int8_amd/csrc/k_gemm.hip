@@ -190,10 +190,15 @@ struct CfgD {
     static constexpr int BK = 64, STAGES = 4, THREADS = 64 * NW;
     static constexpr int TM = BM / WM, TN = BN / WN;
     static constexpr int FM = TM / 16, FN = TN / 16;
-    static constexpr int A_INS = BM / (16 * NW), B_INS = BN / (16 * NW);   // 1 KB loads per wave per stage
+    // 1 KB DMA instructions (16 rows) per stage; instruction i is issued by
+    // wave i % NW.  A splits evenly over the waves; B may not (then the
+    // first B_TOT % NW waves issue one more).
+    static constexpr int A_TOT = BM / 16, B_TOT = BN / 16;
+    static constexpr int QA = A_TOT / NW, QB = (B_TOT + NW - 1) / NW;
+    static constexpr int A_INS = BM / (16 * NW), B_INS = BN / (16 * NW);   // per wave (even splits)
     static constexpr int LDS_A = BM * BK, LDS_B = BN * BK, STAGE = LDS_A + LDS_B;
     static constexpr int LDS = STAGES * STAGE;
-    static_assert(A_INS * 16 * NW == BM && B_INS * 16 * NW == BN, "stage rows must split evenly over waves");
+    static_assert(BM % 16 == 0 && BN % 16 == 0 && A_TOT % NW == 0, "stage rows must split over waves");
 };
 
 __device__ __forceinline__ int swz64(int r, int c) { return r * 64 + ((c ^ ((r >> 1) & 3)) << 4); }
@@ -218,18 +223,20 @@ __device__ __forceinline__ void mainloop_i8_dma(rsrc_t rsa, rsrc_t rsb, uint32_t
                                                 v4i (&acc)[C::FM][C::FN], F&& after_issue = F{}) {
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int wm = wave / C::WN, wn = wave % C::WN;
-    constexpr int PER_STAGE = C::A_INS + C::B_INS;
-    uint32_t oa[C::A_INS], ca[C::A_INS], ob[C::B_INS], cb[C::B_INS];
+    constexpr bool B_EVEN = C::B_TOT % C::NW == 0;
+    constexpr int PL = C::QA + C::B_TOT / C::NW, PH = C::QA + C::QB;   // loads per stage of a wave
+    const bool bhi = B_EVEN || wave < C::B_TOT % C::NW;                // this wave issues QB B loads
+    uint32_t oa[C::QA], ca[C::QA], ob[C::QB], cb[C::QB];
 #pragma unroll
-    for (int q = 0; q < C::A_INS; ++q) {
-        const int P = (wave * C::A_INS + q) * 64 + lane;      // physical 16-byte chunk of the stage
+    for (int q = 0; q < C::QA; ++q) {
+        const int P = (q * C::NW + wave) * 64 + lane;        // physical 16-byte chunk of the stage
         const int r = P >> 2, c = (P & 3) ^ ((r >> 1) & 3);
         oa[q] = (uint32_t)r * K + c * 16;
         ca[q] = c * 16;
     }
 #pragma unroll
-    for (int q = 0; q < C::B_INS; ++q) {
-        const int P = (wave * C::B_INS + q) * 64 + lane;
+    for (int q = 0; q < C::QB; ++q) {
+        const int P = (q * C::NW + wave) * 64 + lane;
         const int r = P >> 2, c = (P & 3) ^ ((r >> 1) & 3);
         ob[q] = (uint32_t)r * K + c * 16;
         cb[q] = c * 16;
@@ -239,13 +246,32 @@ __device__ __forceinline__ void mainloop_i8_dma(rsrc_t rsa, rsrc_t rsb, uint32_t
         uint8_t* st = smem + (kt % C::STAGES) * C::STAGE;
         const uint32_t k0 = (uint32_t)kt * C::BK;
 #pragma unroll
-        for (int q = 0; q < C::A_INS; ++q)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)(st + (wave * C::A_INS + q) * 1024), 16,
+        for (int q = 0; q < C::QA; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)(st + (q * C::NW + wave) * 1024), 16,
                                                      k0 + ca[q] < K ? oa[q] + k0 : kOOB, 0, 0, 0);
 #pragma unroll
-        for (int q = 0; q < C::B_INS; ++q)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void*)(st + C::LDS_A + (wave * C::B_INS + q) * 1024),
-                                                     16, k0 + cb[q] < K ? ob[q] + k0 : kOOB, 0, 0, 0);
+        for (int q = 0; q < C::QB; ++q)
+            if (B_EVEN || q < C::QB - 1 || bhi)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void*)(st + C::LDS_A + (q * C::NW + wave) * 1024),
+                                                         16, k0 + cb[q] < K ? ob[q] + k0 : kOOB, 0, 0, 0);
+    };
+    // wait until at most `ahead` younger stages of this wave's loads are in flight
+    auto wait_stage = [&](int ahead) __attribute__((always_inline)) {
+        if (bhi) {
+            if (ahead >= 2)
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PH));
+            else if (ahead == 1)
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(PH));
+            else
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        } else {
+            if (ahead >= 2)
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PL));
+            else if (ahead == 1)
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(PL));
+            else
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        }
     };
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
@@ -261,29 +287,37 @@ __device__ __forceinline__ void mainloop_i8_dma(rsrc_t rsa, rsrc_t rsb, uint32_t
     // them), hence before it arrived at the barrier of iteration kt.
     const int c = lane >> 4;
     for (int kt = 0; kt < nk; ++kt) {
-        const int ahead = (kt + 2 < nk - 1 ? kt + 2 : nk - 1) - kt;   // stages issued after kt
-        if (ahead >= 2)
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PER_STAGE));
-        else if (ahead == 1)
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_STAGE));
-        else
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        wait_stage((kt + 2 < nk - 1 ? kt + 2 : nk - 1) - kt);        // stages issued after kt
         block_barrier();
         if (kt + 3 < nk) issue(kt + 3);
         const uint8_t* sa = smem + (kt % C::STAGES) * C::STAGE;
         const uint8_t* sb = sa + C::LDS_A;
-        v4i fa[C::FM], fb[C::FN];
+        v4i fa[C::FM];
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+            fa[i] = *reinterpret_cast<const v4i*>(sa + swz64(wm * C::TM + i * 16 + (lane & 15), c));
+        // B fragments one ahead of their MFMAs, so that each fragment's LDS
+        // latency hides behind the previous fragment's MFMAs: the scheduling
+        // groups fix the order [A reads, B0, B1] [MFMA x FM] ([B j+1] [MFMA x FM])...
+        v4i fb[C::FN];
 #pragma unroll
         for (int j = 0; j < C::FN; ++j)
             fb[j] = *reinterpret_cast<const v4i*>(sb + swz64(wn * C::TN + j * 16 + (lane & 15), c));
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-            fa[i] = *reinterpret_cast<const v4i*>(sa + swz64(wm * C::TM + i * 16 + (lane & 15), c));
+        for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-            for (int j = 0; j < C::FN; ++j)
+            for (int i = 0; i < C::FM; ++i)
                 acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fb[j], fa[i], acc[i][j], 0, 0, 0);
+        if constexpr (C::FN > 4) {
+            __builtin_amdgcn_sched_group_barrier(0x100, C::FM + 2, 0);     // DS reads: A, B0, B1
+            __builtin_amdgcn_sched_group_barrier(0x008, C::FM, 0);         // MFMAs of B0
+#pragma unroll
+            for (int j = 1; j + 1 < C::FN; ++j) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         // read B j+1
+                __builtin_amdgcn_sched_group_barrier(0x008, C::FM, 0);     // MFMAs of B j
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, C::FM, 0);         // MFMAs of the last B
+        }
     }
     __syncthreads();
 }
@@ -367,67 +401,94 @@ __device__ __forceinline__ void store_out4(void* out, int dtype, int64_t off, co
     }
 }
 
+// tsn: output columns per tile (the tile computes C::BN >= tsn columns and
+// stores the first tsn; tsn = C::BN except for the one-round wide tiles).
 template <class C>
 __global__ __launch_bounds__(C::THREADS) void k_gemm_i8_mixed(const int8_t* __restrict__ Xq,
                                                               const int8_t* __restrict__ Wq, int64_t M,
                                                               int64_t K, int64_t N, MixedEpilogue ep,
-                                                              int tiles_m, int tiles_n) {
+                                                              int tiles_m, int tiles_n, int tsn) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
     int tm, tn;
     tile_of_block(blockIdx.x, tiles_m, tiles_n, tm, tn);
-    const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
+    const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * tsn;
+    const int64_t nlim = n0 + tsn < N ? n0 + tsn : N;     // columns this tile stores: [n0, nlim)
     v4i acc[C::FM][C::FN];
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int wm = wave / C::WN, wn = wave % C::WN;
     const int64_t rb = m0 + wm * C::TM, cb = n0 + wn * C::TN;
 
     // The epilogue's scales and the outlier count are loaded before the main
-    // loop so their latency hides behind it.
+    // loop so their latency hides behind it (with many column fragments the
+    // channel scales are loaded after it: registers are short).
+    constexpr bool LATE = C::FN > 4;
     const rsrc_t rsw = make_rsrc(ep.s_w + cb, (N - cb) * 4);
     const rsrc_t rsx = make_rsrc(ep.s_x + rb, (M - rb) * 4);
     const int cnt = (int)bload4(make_rsrc(ep.count, 4), 0);
     float sw[C::FN][4], sxv[C::FM];
+    auto load_scales = [&]() __attribute__((always_inline)) {
+        if constexpr (!LATE) {
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j)
+            for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            sw[j][e] = __builtin_bit_cast(float, bload4(rsw, (uint32_t)(j * 16 + 4 * (lane >> 4) + e) * 4));
+                for (int e = 0; e < 4; ++e)
+                    sw[j][e] = __builtin_bit_cast(float, bload4(rsw, (uint32_t)(j * 16 + 4 * (lane >> 4) + e) * 4));
+        }
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i)
-        sxv[i] = __builtin_bit_cast(float, bload4(rsx, (uint32_t)(i * 16 + (lane & 15)) * 4));
+        for (int i = 0; i < C::FM; ++i)
+            sxv[i] = __builtin_bit_cast(float, bload4(rsx, (uint32_t)(i * 16 + (lane & 15)) * 4));
+    };
+    if constexpr (!LATE) load_scales();
 
     // Up to PRE outlier columns: the list is read here with the scales, and
-    // the gather of this thread's row of X or w~ is issued in the main loop's
-    // hook, behind the first stages' loads; the values wait in registers.
-    constexpr int PRE = OUTLIER_PREFETCH;
-    static_assert(C::THREADS >= C::BM + C::BN, "one thread per gathered row");
+    // the gather of this thread's row(s) of X or w~ is issued in the main
+    // loop's hook, behind the first stages' loads; the values wait in registers.
+    // (Not with many column fragments, whose accumulators leave no registers:
+    // those columns are staged after the main loop.)
+    constexpr int PRE = LATE ? 0 : OUTLIER_PREFETCH;
+    constexpr int PR = (C::BM + C::BN + C::THREADS - 1) / C::THREADS;   // gathered rows per thread
     const rsrc_t rxo = make_rsrc(ep.X + m0 * K, (M - m0) * K * 2);
     const rsrc_t rwo = ep.W16 ? make_rsrc(ep.W16 + n0 * K, (N - n0) * K * 2) : make_rsrc(ep.Wq + n0 * K, (N - n0) * K);
     const rsrc_t rsn = make_rsrc(ep.s_w + n0, (N - n0) * 4);
-    const int prow = threadIdx.x;                             // gather row: X rows, then W rows
-    const bool pisx = prow < C::BM;
-    const uint32_t prr = pisx ? prow : prow - C::BM;
-    uint32_t pk[PRE], pv[PRE];
+    uint32_t pk[PRE > 0 ? PRE : 1], pv[PR][PRE > 0 ? PRE : 1];
     {
         const rsrc_t ridx = make_rsrc(ep.idx, (int64_t)PRE * 4);
 #pragma unroll
         for (int u = 0; u < PRE; ++u) pk[u] = bload4(ridx, (uint32_t)u * 4);
     }
-    const float pswr = pisx || ep.W16 ? 0.0f : __builtin_bit_cast(float, bload4(rsn, prr * 4));
+    // gather row p of the block: X rows [0, BM), then W rows
     auto prefetch = [&]() __attribute__((always_inline)) {
-        const bool any = cnt > 0 && cnt <= PRE && prow < C::BM + C::BN;
 #pragma unroll
-        for (int u = 0; u < PRE; ++u) {
-            const bool ok = any && u < cnt;
-            if (pisx)
-                pv[u] = bload2(rxo, ok ? (prr * (uint32_t)K + pk[u]) * 2 : kOOB);
-            else if (ep.W16)
-                pv[u] = bload2(rwo, ok ? (prr * (uint32_t)K + pk[u]) * 2 : kOOB);
-            else
-                pv[u] = bload1(rwo, ok ? prr * (uint32_t)K + pk[u] : kOOB);
+        for (int pr = 0; pr < PR; ++pr) {
+            const int prow = threadIdx.x + pr * C::THREADS;
+            const bool pisx = prow < C::BM;
+            const uint32_t prr = pisx ? prow : prow - C::BM;
+            const bool any = cnt > 0 && cnt <= PRE && prow < C::BM + C::BN;
+#pragma unroll
+            for (int u = 0; u < PRE; ++u) {
+                const bool ok = any && u < cnt;
+                if (pisx)
+                    pv[pr][u] = bload2(rxo, ok ? (prr * (uint32_t)K + pk[u]) * 2 : kOOB);
+                else if (ep.W16)
+                    pv[pr][u] = bload2(rwo, ok ? (prr * (uint32_t)K + pk[u]) * 2 : kOOB);
+                else
+                    pv[pr][u] = bload1(rwo, ok ? prr * (uint32_t)K + pk[u] : kOOB);
+            }
         }
     };
     mainloop_any<C>(Xq, Wq, M, N, K, m0, n0, smem, acc, prefetch);
+    // LATE: the channel scales of the tile's columns go to LDS (after the
+    // outlier staging area), read per fragment in the epilogue
+    constexpr int SWE_OFF = ((C::BM + C::BN) * (96 + 8) * 2 + (96 + C::BN) * 4 + 15) / 16 * 16;
+    float* swe = reinterpret_cast<float*>(smem + SWE_OFF);
+    if constexpr (LATE) {
+        static_assert(SWE_OFF + C::BN * 4 <= C::LDS, "epilogue scales exceed LDS");
+        load_scales();
+        for (int r = threadIdx.x; r < C::BN; r += C::THREADS)
+            swe[r] = __builtin_bit_cast(float, bload4(rsn, (uint32_t)r * 4));
+        // visible to the epilogue through the barriers below (staging) or this one
+        __syncthreads();
+    }
 
     // Epilogue, one 16-row fragment at a time: dequantize C * s_x[m] * s_w[n],
     // then add the fp16 outlier product on v_mfma_f32_16x16x32_f16 (operands
@@ -451,7 +512,9 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_i8_mixed(const int8_t* __re
     int* hidx = reinterpret_cast<int*>(smem + (C::BM + C::BN) * OST * 2);
     float* swl = reinterpret_cast<float*>(hidx + OCAP);
     static_assert((C::BM + C::BN) * OST * 2 + (OCAP + C::BN) * 4 <= C::LDS, "outlier staging exceeds LDS");
-    const bool use_xo = ep.Xo != nullptr && cnt <= XO_CAP;
+    // (the row quantizer writes the compact rows only for counts above
+    // OUTLIER_PREFETCH, which the other configurations gather themselves)
+    const bool use_xo = ep.Xo != nullptr && cnt > OUTLIER_PREFETCH && cnt <= XO_CAP;
     auto stage = [&](int hs) __attribute__((always_inline)) {
         const int hn = cnt - hs < OCAP ? cnt - hs : OCAP;
         const int hp = (hn + 31) & ~31;
@@ -516,16 +579,23 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_i8_mixed(const int8_t* __re
             }
         }
     };
-    if (cnt > 0 && cnt <= PRE) {
-        if (prow < C::BM + C::BN) {                         // the prefetched columns, zero-padded to 32
+    if (PRE > 0 && cnt > 0 && cnt <= PRE) {
 #pragma unroll
-            for (int u = 0; u < 32; ++u) {
-                uint16_t hv = 0;
-                if (u < PRE && u < cnt) {
-                    hv = (uint16_t)pv[u < PRE ? u : 0];
-                    if (!pisx && !ep.W16) hv = f2h(pswr * (float)(int8_t)(uint8_t)pv[u < PRE ? u : 0]);
+        for (int pr = 0; pr < PR; ++pr) {
+            const int prow = threadIdx.x + pr * C::THREADS;
+            if (prow < C::BM + C::BN) {                     // the prefetched columns, zero-padded to 32
+                const bool pisx = prow < C::BM;
+                const float pswr = pisx || ep.W16 ? 0.0f
+                                                  : __builtin_bit_cast(float, bload4(rsn, (uint32_t)(prow - C::BM) * 4));
+#pragma unroll
+                for (int u = 0; u < 32; ++u) {
+                    uint16_t hv = 0;
+                    if (u < PRE && u < cnt) {
+                        hv = (uint16_t)pv[pr][u < PRE ? u : 0];
+                        if (!pisx && !ep.W16) hv = f2h(pswr * (float)(int8_t)(uint8_t)pv[pr][u < PRE ? u : 0]);
+                    }
+                    xo[prow * OST + u] = __builtin_bit_cast(_Float16, hv);
                 }
-                xo[prow * OST + u] = __builtin_bit_cast(_Float16, hv);
             }
         }
         __syncthreads();
@@ -534,15 +604,21 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_i8_mixed(const int8_t* __re
         __syncthreads();
     }
     const _Float16* wo = xo + C::BM * OST;
-    const bool vec = ((ep.ldo | N) & 3) == 0;
+    const bool vec = ((ep.ldo | N | tsn) & 3) == 0;
     static_for<C::FM>([&](auto I) __attribute__((always_inline)) {
         constexpr int i = decltype(I)::value;
         const float sx = sxv[i];
         v4f cf[C::FN];
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j)
+        for (int j = 0; j < C::FN; ++j) {
+            v4f s4;
+            if constexpr (LATE)
+                s4 = *reinterpret_cast<const v4f*>(swe + wn * C::TN + j * 16 + 4 * (lane >> 4));
+            else
+                s4 = v4f{sw[j][0], sw[j][1], sw[j][2], sw[j][3]};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) cf[j][e] = (float)acc[i][j][e] * sx * sw[j][e];
+            for (int e = 0; e < 4; ++e) cf[j][e] = (float)acc[i][j][e] * sx * s4[e];
+        }
         for (int hs = 0; hs < cnt; hs += OCAP) {
             if (cnt > OCAP) {                                 // gather this pass (block-uniform)
                 __syncthreads();
@@ -565,8 +641,9 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_i8_mixed(const int8_t* __re
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) {
             const int64_t col = cb + j * 16 + 4 * (lane >> 4);
-            if (row < M && col < N)
-                store_out4(ep.out, ep.out_dtype, row * ep.ldo + col, cf[j], vec, (int)(N - col < 4 ? N - col : 4));
+            if (row < M && col < nlim)
+                store_out4(ep.out, ep.out_dtype, row * ep.ldo + col, cf[j], vec,
+                           (int)(nlim - col < 4 ? nlim - col : 4));
         }
     });
 }
@@ -695,14 +772,35 @@ static int64_t tail_split(int64_t M, int64_t N) {
     return cols >= 1 && split < N ? split : 0;
 }
 
+// One-round wide tiles: when 256 x 256 tiles would leave a partial second
+// round, 256-row tiles computing 352 columns (wave tile 64 x 176) with a
+// column stride tsn <= 352 chosen so that all tiles fit one round over the
+// 256 CUs -- e.g. 2048 x 11008: 8 x 32 tiles of 256 x 344, against 1.34
+// rounds of 256 x 256.  Returns the stride, or 0 when this does not apply.
+using CfgWide = CfgD<256, 352, 4, 2>;  // 8 waves, wave tile 64 x 176, LDS-DMA stages
+static int wide_stride(int64_t M, int64_t N) {
+    const int64_t tm = (M + 255) / 256;
+    if (tm > 256 || ((M + 255) / 256) * ((N + 255) / 256) <= 256) return 0;
+    const int64_t tn = 256 / tm;                              // tile columns that fit the round
+    const int64_t tsn = ((N + tn - 1) / tn + 7) / 8 * 8;      // stride, a multiple of 8
+    return tsn <= CfgWide::BN ? (int)tsn : 0;
+}
+
 hipError_t launch_gemm_i8_mixed(const int8_t* Xq, const int8_t* Wq, int64_t M, int64_t K, int64_t N,
                                 const MixedEpilogue& ep, hipStream_t st) {
     int tm, tn;
     if (pick_cfg(M, N) == 2) {
+        if (const int tsn = wide_stride(M, N)) {
+            tm = (int)((M + 255) / 256);
+            tn = (int)((N + tsn - 1) / tsn);
+            hipLaunchKernelGGL(k_gemm_i8_mixed<CfgWide>, dim3((unsigned)(tm * tn)), dim3(CfgWide::THREADS), 0, st,
+                               Xq, Wq, M, K, N, ep, tm, tn, tsn);
+            return hipGetLastError();
+        }
         if (const int64_t split = tail_split(M, N)) {
             dim3 g = grid_of<CfgBig>(M, split, tm, tn);
             hipLaunchKernelGGL(k_gemm_i8_mixed<CfgBig>, g, dim3(CfgBig::THREADS), 0, st, Xq, Wq, M, K, split, ep,
-                               tm, tn);
+                               tm, tn, CfgBig::BN);
             const int esz = ep.out_dtype == 0 ? 4 : 2;
             MixedEpilogue et = ep;
             et.s_w = ep.s_w + split;
@@ -711,7 +809,7 @@ hipError_t launch_gemm_i8_mixed(const int8_t* Xq, const int8_t* Wq, int64_t M, i
             et.out = static_cast<uint8_t*>(ep.out) + split * esz;
             g = grid_of<CfgTail>(M, N - split, tm, tn);
             hipLaunchKernelGGL(k_gemm_i8_mixed<CfgTail>, g, dim3(CfgTail::THREADS), 0, st, Xq, Wq + split * K, M, K,
-                               N - split, et, tm, tn);
+                               N - split, et, tm, tn, CfgTail::BN);
             return hipGetLastError();
         }
     }
@@ -719,19 +817,19 @@ hipError_t launch_gemm_i8_mixed(const int8_t* Xq, const int8_t* Wq, int64_t M, i
         case 2: {
             dim3 g = grid_of<CfgBig>(M, N, tm, tn);
             hipLaunchKernelGGL(k_gemm_i8_mixed<CfgBig>, g, dim3(CfgBig::THREADS), 0, st, Xq, Wq, M, K, N, ep, tm,
-                               tn);
+                               tn, CfgBig::BN);
             break;
         }
         case 1: {
             dim3 g = grid_of<CfgMid>(M, N, tm, tn);
             hipLaunchKernelGGL(k_gemm_i8_mixed<CfgMid>, g, dim3(CfgMid::THREADS), 0, st, Xq, Wq, M, K, N, ep, tm,
-                               tn);
+                               tn, CfgMid::BN);
             break;
         }
         default: {
             dim3 g = grid_of<CfgSmall>(M, N, tm, tn);
             hipLaunchKernelGGL(k_gemm_i8_mixed<CfgSmall>, g, dim3(CfgSmall::THREADS), 0, st, Xq, Wq, M, K, N, ep,
-                               tm, tn);
+                               tm, tn, CfgSmall::BN);
         }
     }
     return hipGetLastError();
@@ -954,6 +1052,7 @@ __device__ __forceinline__ v4i perm_even_odd(const u32x4& a) {
 
 template <class C, bool A8>
 struct W4Stage {
+    static_assert(C::A_INS * 16 * C::NW == C::BM && C::B_INS * 16 * C::NW == C::BN, "even stage split");
     static constexpr int A_ROW = A8 ? 128 : 64;                 // activation bytes per row and stage
     static constexpr int LDS_A = C::BM * A_ROW;
     static constexpr int A_INS = A8 ? 2 * C::A_INS : C::A_INS;  // 1 KB DMA instructions per wave
