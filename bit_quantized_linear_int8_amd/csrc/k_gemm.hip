@@ -1368,6 +1368,176 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_w4a8_dma(const int8_t* __re
                                                      out, out_dtype, tiles_m, tiles_n, smem, sws);
 }
 
+// ---------------------------------------------------------------------------
+// W4 GEMMs with groups smaller than one MFMA step (G = 8, 16, 32: a 64-deep
+// MFMA would sum over several groups).  Each group's int32 sum is formed on
+// the VALU: v_dot8_i32_i4 (eight signed nibble products per instruction)
+// for int4 activations; for int8 activations (A8) v_dot4_i32_i8 on the codes
+// in even / odd element order against the weight nibbles moved into the high
+// half of each byte (products x 16, the 2^-4 is exact in the dequant).  64 x 64
+// outputs per 256-thread block, 4 x 4 per thread; K in chunks of 64 elements
+// staged in LDS with the chunk's per-group weight scales.
+//   out[m][n] = s_x[m] (sum_g s_w[n][g] acc_g[m][n] - (ZX ? (z_x[m] - 8) c_w[n] : 0))
+// or, with STORE_ACC, acc_g[m][n] into acc [M x N x K/G] (int32).
+// ---------------------------------------------------------------------------
+template <int G, bool A8, bool ZX, bool STORE_ACC>
+__global__ __launch_bounds__(256) void k_gemm_w4_small_g(const uint8_t* __restrict__ Xa, const float* __restrict__ s_x,
+                                                         const int32_t* __restrict__ z_x,
+                                                         const uint32_t* __restrict__ Wp,
+                                                         const float* __restrict__ s_w, const float* __restrict__ c_w,
+                                                         int64_t M, int64_t K, int64_t N, void* __restrict__ out,
+                                                         int out_dtype) {
+    static_assert(G == 8 || G == 16 || G == 32, "groups below one MFMA step");
+    constexpr int KC = 64;                            // K elements per chunk
+    constexpr int AW = A8 ? KC / 4 : KC / 8;          // activation words per row and chunk
+    constexpr int WW = KC / 8;                        // weight words per row and chunk
+    constexpr int NGC = KC / G;                       // groups per chunk
+    __shared__ uint32_t As[64][AW + 1];
+    __shared__ uint32_t Bs[64][WW + 1];
+    __shared__ float Ss[64][NGC + 1];
+    const int64_t m0 = (int64_t)blockIdx.y * 64, n0 = (int64_t)blockIdx.x * 64;
+    const int t = threadIdx.x, tx = t & 15, ty = t >> 4;
+    const int64_t ng = K / G;
+    const uint32_t abytes = (uint32_t)(A8 ? K : K / 2), wbytes = (uint32_t)(K / 2);
+    const rsrc_t ra = make_rsrc(Xa + m0 * abytes, (M - m0) * abytes);
+    const rsrc_t rw = make_rsrc(reinterpret_cast<const uint8_t*>(Wp) + n0 * wbytes, (N - n0) * wbytes);
+    const rsrc_t rs = make_rsrc(STORE_ACC ? nullptr : s_w + n0 * ng, STORE_ACC ? 0 : (N - n0) * ng * 4);
+    float f[4][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) f[r][c] = 0.0f;
+    for (int64_t kc = 0; kc < K; kc += KC) {
+        // stage the chunk: 16-byte loads, bytes past the row's end read zero
+        const uint32_t ka = (uint32_t)(A8 ? kc : kc / 2), kw = (uint32_t)(kc / 2);
+        for (int q = t; q < 64 * (AW / 4); q += 256) {
+            const int r = q / (AW / 4), c4 = q % (AW / 4);
+            const uint32_t o = ka + 16 * c4;
+            const u32x4 v = bload16(ra, o < abytes ? (uint32_t)r * abytes + o : kOOB);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) As[r][4 * c4 + d] = v[d];
+        }
+        for (int q = t; q < 64 * (WW / 4); q += 256) {
+            const int r = q / (WW / 4), c4 = q % (WW / 4);
+            const uint32_t o = kw + 16 * c4;
+            const u32x4 v = bload16(rw, o < wbytes ? (uint32_t)r * wbytes + o : kOOB);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) Bs[r][4 * c4 + d] = v[d];
+        }
+        if constexpr (!STORE_ACC) {
+            for (int q = t; q < 64 * NGC; q += 256) {
+                const int c = q / NGC, gg = q % NGC;
+                const int64_t g = kc / G + gg;
+                Ss[c][gg] = g < ng ? __builtin_bit_cast(float, bload4(rs, (uint32_t)(c * ng + g) * 4)) : 0.0f;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int gg = 0; gg < NGC; ++gg) {
+            int acc[4][4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc[r][c] = 0;
+#pragma unroll
+            for (int w = 0; w < G / 8; ++w) {            // weight words of the group
+                const int wi = gg * (G / 8) + w;
+                uint32_t b[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) b[c] = Bs[4 * tx + c][wi];
+                if constexpr (A8) {
+                    uint32_t be[4], bo[4];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        be[c] = (b[c] << 4) & 0xF0F0F0F0u;   // elements 0, 2, 4, 6 (x 16)
+                        bo[c] = b[c] & 0xF0F0F0F0u;          // elements 1, 3, 5, 7 (x 16)
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const uint32_t a0 = As[4 * ty + r][2 * wi], a1 = As[4 * ty + r][2 * wi + 1];
+                        const int ae = (int)__builtin_amdgcn_perm(a1, a0, 0x06040200u);
+                        const int ao = (int)__builtin_amdgcn_perm(a1, a0, 0x07050301u);
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            acc[r][c] = __builtin_amdgcn_sdot4(ae, (int)be[c], acc[r][c], false);
+                            acc[r][c] = __builtin_amdgcn_sdot4(ao, (int)bo[c], acc[r][c], false);
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int a = (int)As[4 * ty + r][wi];
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) acc[r][c] = __builtin_amdgcn_sdot8(a, (int)b[c], acc[r][c], false);
+                    }
+                }
+            }
+            const int64_t g = kc / G + gg;
+            if constexpr (STORE_ACC) {
+                if (g < ng) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int64_t m = m0 + 4 * ty + r;
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            const int64_t n = n0 + 4 * tx + c;
+                            if (m < M && n < N)
+                                static_cast<int32_t*>(out)[(m * N + n) * ng + g] = A8 ? acc[r][c] >> 4 : acc[r][c];
+                        }
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        f[r][c] = __builtin_fmaf(Ss[4 * tx + c][gg] * (A8 ? 0x1p-4f : 1.0f), (float)acc[r][c], f[r][c]);
+            }
+        }
+        __syncthreads();
+    }
+    if constexpr (!STORE_ACC) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t m = m0 + 4 * ty + r;
+            if (m >= M) continue;
+            const float sx = s_x[m];
+            const float zp = ZX ? (float)(z_x[m] - 8) : 0.0f;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int64_t n = n0 + 4 * tx + c;
+                if (n >= N) continue;
+                float v = f[r][c];
+                if constexpr (ZX) v = __builtin_fmaf(-zp, c_w[n], v);
+                store_out(out, out_dtype, m * N + n, sx * v);
+            }
+        }
+    }
+}
+
+template <bool A8, bool ZX, bool STORE_ACC>
+static hipError_t launch_w4_small_g(const uint8_t* Xa, const float* s_x, const int32_t* z_x, const uint32_t* Wp,
+                                    const float* s_w, const float* c_w, int64_t M, int64_t K, int64_t N, int G,
+                                    void* out, int out_dtype, hipStream_t st) {
+    const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64));
+    switch (G) {
+        case 8:
+            hipLaunchKernelGGL((k_gemm_w4_small_g<8, A8, ZX, STORE_ACC>), grid, dim3(256), 0, st, Xa, s_x, z_x, Wp, s_w,
+                               c_w, M, K, N, out, out_dtype);
+            break;
+        case 16:
+            hipLaunchKernelGGL((k_gemm_w4_small_g<16, A8, ZX, STORE_ACC>), grid, dim3(256), 0, st, Xa, s_x, z_x, Wp,
+                               s_w, c_w, M, K, N, out, out_dtype);
+            break;
+        case 32:
+            hipLaunchKernelGGL((k_gemm_w4_small_g<32, A8, ZX, STORE_ACC>), grid, dim3(256), 0, st, Xa, s_x, z_x, Wp,
+                               s_w, c_w, M, K, N, out, out_dtype);
+            break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 using CfgW4 = CfgD<128, 256, 2, 4>;     // 8 waves, wave tile 64 x 64, LDS-DMA stages
 
 // Whether a CfgW4 block's per-group weight scales fit the LDS table.
@@ -1402,7 +1572,9 @@ hipError_t launch_gemm_w4a4(const uint32_t* Xp, const float* s_x, const uint32_t
         case 64: w4a4_dispatch<64, false>(Xp, s_x, Wp, s_w, M, K, N, out, out_dtype, st); break;
         case 128: w4a4_dispatch<128, false>(Xp, s_x, Wp, s_w, M, K, N, out, out_dtype, st); break;
         case 256: w4a4_dispatch<256, false>(Xp, s_x, Wp, s_w, M, K, N, out, out_dtype, st); break;
-        default: return hipErrorInvalidValue;
+        default:
+            return launch_w4_small_g<false, false, false>(reinterpret_cast<const uint8_t*>(Xp), s_x, nullptr, Wp, s_w,
+                                                          nullptr, M, K, N, G, out, out_dtype, st);
     }
     return hipGetLastError();
 }
@@ -1428,7 +1600,9 @@ hipError_t launch_gemm_w4a4_asym(const uint32_t* Xp, const float* s_x, const int
         case 64: w4a4z_dispatch<64>(Xp, s_x, z_x, Wp, s_w, c_w, M, K, N, out, out_dtype, st); break;
         case 128: w4a4z_dispatch<128>(Xp, s_x, z_x, Wp, s_w, c_w, M, K, N, out, out_dtype, st); break;
         case 256: w4a4z_dispatch<256>(Xp, s_x, z_x, Wp, s_w, c_w, M, K, N, out, out_dtype, st); break;
-        default: return hipErrorInvalidValue;
+        default:
+            return launch_w4_small_g<false, true, false>(reinterpret_cast<const uint8_t*>(Xp), s_x, z_x, Wp, s_w, c_w, M,
+                                                         K, N, G, out, out_dtype, st);
     }
     return hipGetLastError();
 }
@@ -1452,7 +1626,9 @@ hipError_t launch_gemm_w4a8(const int8_t* Xq, const float* s_x, const uint32_t* 
         case 64: w4a8_dispatch<64, false>(Xq, s_x, Wp, s_w, M, K, N, out, out_dtype, st); break;
         case 128: w4a8_dispatch<128, false>(Xq, s_x, Wp, s_w, M, K, N, out, out_dtype, st); break;
         case 256: w4a8_dispatch<256, false>(Xq, s_x, Wp, s_w, M, K, N, out, out_dtype, st); break;
-        default: return hipErrorInvalidValue;
+        default:
+            return launch_w4_small_g<true, false, false>(reinterpret_cast<const uint8_t*>(Xq), s_x, nullptr, Wp, s_w,
+                                                         nullptr, M, K, N, G, out, out_dtype, st);
     }
     return hipGetLastError();
 }
@@ -1463,7 +1639,9 @@ hipError_t launch_gemm_w4a8_group_acc(const int8_t* Xq, const uint32_t* Wp, int6
         case 64: w4a8_dispatch<64, true>(Xq, nullptr, Wp, nullptr, M, K, N, acc, 0, st); break;
         case 128: w4a8_dispatch<128, true>(Xq, nullptr, Wp, nullptr, M, K, N, acc, 0, st); break;
         case 256: w4a8_dispatch<256, true>(Xq, nullptr, Wp, nullptr, M, K, N, acc, 0, st); break;
-        default: return hipErrorInvalidValue;
+        default:
+            return launch_w4_small_g<true, false, true>(reinterpret_cast<const uint8_t*>(Xq), nullptr, nullptr, Wp,
+                                                        nullptr, nullptr, M, K, N, G, acc, 0, st);
     }
     return hipGetLastError();
 }
@@ -1474,7 +1652,9 @@ hipError_t launch_gemm_w4a4_group_acc(const uint32_t* Xp, const uint32_t* Wp, in
         case 64: w4a4_dispatch<64, true>(Xp, nullptr, Wp, nullptr, M, K, N, acc, 0, st); break;
         case 128: w4a4_dispatch<128, true>(Xp, nullptr, Wp, nullptr, M, K, N, acc, 0, st); break;
         case 256: w4a4_dispatch<256, true>(Xp, nullptr, Wp, nullptr, M, K, N, acc, 0, st); break;
-        default: return hipErrorInvalidValue;
+        default:
+            return launch_w4_small_g<false, false, true>(reinterpret_cast<const uint8_t*>(Xp), nullptr, nullptr, Wp,
+                                                         nullptr, nullptr, M, K, N, G, acc, 0, st);
     }
     return hipGetLastError();
 }

@@ -573,14 +573,25 @@ __global__ __launch_bounds__(256) void k_rowquant_i8(const uint16_t* __restrict_
         }
         if constexpr (!STATIC) {
             float amax = 0.0f;
+            if constexpr (MASK == MASK_BYTES) {
 #pragma unroll
-            for (int i = 0; i < NC; ++i) {
-                float x[8];
-                unpack8(v[i], x);
-                if constexpr (MASK == MASK_BYTES) apply_mask(x, mk[i]);
-                amax = fmaxf(amax, absmax8(x));
+                for (int i = 0; i < NC; ++i) {
+                    float x[8];
+                    unpack8(v[i], x);
+                    apply_mask(x, mk[i]);
+                    amax = fmaxf(amax, absmax8(x));
+                }
+                amax = wave_max(amax);
+            } else {
+                // on the sign-cleared fp16 patterns (they order like the
+                // magnitudes), two per instruction; DPP lane reduction
+                uint32_t am = 0u;
+#pragma unroll
+                for (int i = 0; i < NC; ++i)
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) am = pk_max_u16(am, v[i][d] & 0x7fff7fffu);
+                amax = h2f((uint16_t)wave_max_u32(max(am & 0xffffu, am >> 16)));
             }
-            amax = wave_max(amax);
             s = amax == 0.0f ? 1.0f : amax / (float)qmax;
             r = 1.0f / s;
             if (lane == 0) s_out[row] = s;
@@ -589,14 +600,18 @@ __global__ __launch_bounds__(256) void k_rowquant_i8(const uint16_t* __restrict_
         for (int i = 0; i < NC; ++i) {
             const int64_t ch = lane + 64 * i;
             if (ch < nch) {
-                float x[8];
-                unpack8(v[i], x);
                 u32x2 c;
                 if constexpr (STATIC) {
+                    float x[8];
+                    unpack8(v[i], x);
                     c = codes8_static(x, mk[i], s, z, qmin, qmax);
-                } else {
-                    if constexpr (MASK == MASK_BYTES) apply_mask(x, mk[i]);
+                } else if constexpr (MASK == MASK_BYTES) {
+                    float x[8];
+                    unpack8(v[i], x);
+                    apply_mask(x, mk[i]);
                     c = clip_codes(codes8_dyn(x, s, r), qmin);
+                } else {
+                    c = clip_codes(codes8_dyn_h(v[i], s, r), qmin);
                 }
                 *reinterpret_cast<u32x2*>(qr + ch * 8) = c;
             }

@@ -575,13 +575,15 @@ size_t qa_qlinear_w4a4_workspace(int64_t M, int64_t K) {
     return w4_layout(M, K).total;
 }
 
-static bool w4_group_ok(int32_t G) { return G == 64 || G == 128 || G == 256; }
+// Every power of two from 8 to 256: G >= 64 on the MFMA GEMMs, 8 <= G <= 32
+// on the VALU dot-product kernels (a 64-deep MFMA step would span groups).
+static bool w4_group_ok(int32_t G) { return G >= 8 && G <= 256 && (G & (G - 1)) == 0; }
 
 qa_status qa_qlinear_w4a4(const void* X_f16, int64_t M, int64_t K, const uint32_t* Wp, const float* s_w, int64_t N,
                           int32_t G, void* out, qa_dtype out_dtype, void* workspace, size_t workspace_bytes,
                           void* stream) {
     if (!w4_group_ok(G) || M < 0 || N < 0 || K <= 0 || K % G != 0)
-        return fail(QA_ERR_SHAPE, "qa_qlinear_w4a4: need G in {64,128,256}, M, N >= 0, K > 0, K %% G == 0");
+        return fail(QA_ERR_SHAPE, "qa_qlinear_w4a4: need G a power of two in [8, 256], M, N >= 0, K > 0, K %% G == 0");
     if (!valid_dtype(out_dtype)) return fail(QA_ERR_VALUE, "qa_qlinear_w4a4: bad out_dtype %d", (int)out_dtype);
     if (M == 0 || N == 0) return ok();
     if (!X_f16 || !Wp || !s_w || !out || !workspace) return fail(QA_ERR_NULL, "qa_qlinear_w4a4: NULL pointer");
@@ -628,7 +630,7 @@ qa_status qa_qlinear_w4a8(const void* X_f16, int64_t M, int64_t K, const uint32_
                           int32_t G, void* out, qa_dtype out_dtype, void* workspace, size_t workspace_bytes,
                           void* stream) {
     if (!w4_group_ok(G) || M < 0 || N < 0 || K <= 0 || K % G != 0)
-        return fail(QA_ERR_SHAPE, "qa_qlinear_w4a8: need G in {64,128,256}, M, N >= 0, K > 0, K %% G == 0");
+        return fail(QA_ERR_SHAPE, "qa_qlinear_w4a8: need G a power of two in [8, 256], M, N >= 0, K > 0, K %% G == 0");
     if (!valid_dtype(out_dtype)) return fail(QA_ERR_VALUE, "qa_qlinear_w4a8: bad out_dtype %d", (int)out_dtype);
     if (M == 0 || N == 0) return ok();
     if (!X_f16 || !Wp || !s_w || !out || !workspace) return fail(QA_ERR_NULL, "qa_qlinear_w4a8: NULL pointer");
@@ -685,7 +687,7 @@ qa_status qa_qlinear_w4a4_asym(const void* X_f16, int64_t M, int64_t K, const ui
                                const float* c_w, int64_t N, int32_t G, void* out, qa_dtype out_dtype, void* workspace,
                                size_t workspace_bytes, void* stream) {
     if (!w4_group_ok(G) || M < 0 || N < 0 || K <= 0 || K % G != 0)
-        return fail(QA_ERR_SHAPE, "qa_qlinear_w4a4_asym: need G in {64,128,256}, M, N >= 0, K > 0, K %% G == 0");
+        return fail(QA_ERR_SHAPE, "qa_qlinear_w4a4_asym: need G a power of two in [8, 256], M, N >= 0, K > 0, K %% G == 0");
     if (!valid_dtype(out_dtype)) return fail(QA_ERR_VALUE, "qa_qlinear_w4a4_asym: bad out_dtype %d", (int)out_dtype);
     if (M == 0 || N == 0) return ok();
     if (!X_f16 || !Wp || !s_w || !c_w || !out || !workspace)
@@ -757,7 +759,7 @@ qa_status qa_qlinear_kron_w4a4(const void* X_f16, int64_t M, int64_t K, int64_t 
                                const float* P2, const uint32_t* Wp, const float* s_w, int64_t N, int32_t G, void* out,
                                qa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
     if (!w4_group_ok(G) || M < 0 || N < 0 || K <= 0 || K % G != 0 || n1 <= 0 || n2 <= 0 || n1 * n2 != K)
-        return fail(QA_ERR_SHAPE, "qa_qlinear_kron_w4a4: need G in {64,128,256}, M, N >= 0, K %% G == 0, n1 n2 == K");
+        return fail(QA_ERR_SHAPE, "qa_qlinear_kron_w4a4: need G a power of two in [8, 256], M, N >= 0, K %% G == 0, n1 n2 == K");
     if (!qa::kron_supported(n1, n2, 0))
         return fail(QA_ERR_UNSUPPORTED, "qa_qlinear_kron_w4a4: no kernel for n1=%lld n2=%lld", (long long)n1,
                     (long long)n2);
@@ -797,7 +799,7 @@ qa_status qa_gemm_i8_i32(const int8_t* A, const int8_t* B, int64_t M, int64_t K,
 qa_status qa_gemm_w4a4_group_acc(const uint32_t* Xp, const uint32_t* Wp, int64_t M, int64_t K, int64_t N, int32_t G,
                                  int32_t* acc, void* stream) {
     if (!w4_group_ok(G) || M < 0 || N < 0 || K <= 0 || K % G != 0)
-        return fail(QA_ERR_SHAPE, "qa_gemm_w4a4_group_acc: need G in {64,128,256}, M, N >= 0, K > 0, K %% G == 0");
+        return fail(QA_ERR_SHAPE, "qa_gemm_w4a4_group_acc: need G a power of two in [8, 256], M, N >= 0, K > 0, K %% G == 0");
     if (M == 0 || N == 0) return ok();
     if (!Xp || !Wp || !acc) return fail(QA_ERR_NULL, "qa_gemm_w4a4_group_acc: NULL pointer");
     if (!aligned(Xp, 16) || !aligned(Wp, 16) || !aligned(acc, 4))
@@ -809,7 +811,7 @@ qa_status qa_gemm_w4a4_group_acc(const uint32_t* Xp, const uint32_t* Wp, int64_t
 qa_status qa_gemm_w4a8_group_acc(const int8_t* Xq, const uint32_t* Wp, int64_t M, int64_t K, int64_t N, int32_t G,
                                  int32_t* acc, void* stream) {
     if (!w4_group_ok(G) || M < 0 || N < 0 || K <= 0 || K % G != 0)
-        return fail(QA_ERR_SHAPE, "qa_gemm_w4a8_group_acc: need G in {64,128,256}, M, N >= 0, K > 0, K %% G == 0");
+        return fail(QA_ERR_SHAPE, "qa_gemm_w4a8_group_acc: need G a power of two in [8, 256], M, N >= 0, K > 0, K %% G == 0");
     if (M == 0 || N == 0) return ok();
     if (!Xq || !Wp || !acc) return fail(QA_ERR_NULL, "qa_gemm_w4a8_group_acc: NULL pointer");
     if (!aligned(Xq, 16) || !aligned(Wp, 16) || !aligned(acc, 4))

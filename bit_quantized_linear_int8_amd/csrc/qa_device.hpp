@@ -120,6 +120,30 @@ __device__ __forceinline__ u32x2 codes8_dyn(const float* x, float s, float r) {
     return u32x2{lo ^ 0x80808080u, hi ^ 0x80808080u};
 }
 
+// codes8_dyn on the eight fp16 values of a 16-byte chunk (widened inside the
+// fused multiply-adds, so no separate conversions on the fast path).
+__device__ __forceinline__ u32x2 codes8_dyn_h(const u32x4& v, float s, float r) {
+    float x[8], n[8];
+    float dmax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        x[j] = h2f((uint16_t)(v[j >> 1] >> (16 * (j & 1))));
+        const float t = __builtin_fmaf(x[j], r, 128.0f);
+        n[j] = __builtin_rintf(t);
+        dmax = fmaxf(dmax, __builtin_fabsf(t - n[j]));
+    }
+    if (dmax > 0.5f - 0x1p-14f) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) n[j] = __builtin_rintf(x[j] / s) + 128.0f;
+    }
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lo = __builtin_amdgcn_cvt_pk_u8_f32(n[j], j, lo);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hi = __builtin_amdgcn_cvt_pk_u8_f32(n[j + 4], j, hi);
+    return u32x2{lo ^ 0x80808080u, hi ^ 0x80808080u};
+}
+
 // Quantize one value whose quotient by the scale is bounded by q_max(1+2^-23)
 // (dynamic absmax scales): the quotient is formed with the reciprocal r and
 // the exact IEEE division is used only when that product lies within 2^-14

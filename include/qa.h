@@ -276,7 +276,7 @@ qa_status qa_hadamard_quant_int4(const void* X_f16, int64_t rows, int64_t K, int
  *           u32 [N x K/8], f32 [N x K/G]
  *   out     [M x N] of out_dtype
  *   workspace  qa_qlinear_w4a4_workspace(M, K) bytes (any content)
- * Errors: NULL pointers, M < 0, N < 0, K <= 0, G not in {64, 128, 256},
+ * Errors: NULL pointers, M < 0, N < 0, K <= 0, G not a power of two in [8, 256],
  * K % G != 0, misaligned pointers, bad out_dtype, small workspace.
  * ------------------------------------------------------------------------- */
 size_t qa_qlinear_w4a4_workspace(int64_t M, int64_t K);
@@ -312,7 +312,7 @@ qa_status qa_hadamard_quant_int8(const void* X_f16, int64_t rows, int64_t K, int
  *            -7, 7): u32 [N x K/8], f32 [N x K/G]
  *   out      [M x N] of out_dtype
  *   workspace  qa_qlinear_w4a8_workspace(M, K) bytes (any content)
- * Errors: NULL pointers, M < 0, N < 0, K <= 0, G not in {64, 128, 256},
+ * Errors: NULL pointers, M < 0, N < 0, K <= 0, G not a power of two in [8, 256],
  * K % G != 0, misaligned pointers, bad out_dtype, small workspace.
  * ------------------------------------------------------------------------- */
 size_t qa_qlinear_w4a8_workspace(int64_t M, int64_t K);
@@ -358,7 +358,7 @@ qa_status qa_w4_column_terms(const uint32_t* Wp, const float* s_w, int64_t N, in
  *   c_w      qa_w4_column_terms(Wp, s_w, G): f32 [N]
  *   out      [M x N] of out_dtype
  *   workspace  qa_qlinear_w4a4_asym_workspace(M, K) bytes (any content)
- * Errors: NULL pointers, M < 0, N < 0, K <= 0, G not in {64, 128, 256},
+ * Errors: NULL pointers, M < 0, N < 0, K <= 0, G not a power of two in [8, 256],
  * K % G != 0, misaligned pointers, bad out_dtype, small workspace.
  * ------------------------------------------------------------------------- */
 size_t qa_qlinear_w4a4_asym_workspace(int64_t M, int64_t K);
@@ -547,7 +547,7 @@ qa_status qa_kron_sizes(int64_t n, int64_t* n1, int64_t* n2, int32_t* has_kernel
  *            PER_GROUP, G, -7, 7): u32 [N x K/8], f32 [N x K/G]
  *   out      [M x N] of out_dtype
  *   workspace  qa_qlinear_kron_w4a4_workspace(M, K) bytes (any content)
- * Errors: NULL pointers, M < 0, N < 0, G not in {64, 128, 256}, K % G != 0,
+ * Errors: NULL pointers, M < 0, N < 0, G not a power of two in [8, 256], K % G != 0,
  * n1 n2 != K, unsupported sizes, misaligned pointers, bad out_dtype, small
  * workspace.
  * ------------------------------------------------------------------------- */
@@ -567,7 +567,7 @@ qa_status qa_qlinear_kron_w4a4(const void* X_f16, int64_t M, int64_t K, int64_t 
  * qa_gemm_w4a4_group_acc  [GroupRot §5.4]
  *   acc[m][n][g] = sum_{k in group g} qx[m][k] * qw[n][k] from packed int4
  *   Xp u32 [M x K/8], Wp u32 [N x K/8]; acc i32 [M x N x K/G].
- *   Errors: NULL, M < 0, N < 0, K <= 0, G not in {64, 128, 256},
+ *   Errors: NULL, M < 0, N < 0, K <= 0, G not a power of two in [8, 256],
  *   K % G != 0, misaligned pointers.
  *
  * qa_gemm_w4a8_group_acc  [GroupRot §5.4; Scholia-IQ §2.2]

@@ -133,7 +133,9 @@ def test_w4a4_argument_errors():
         a[i] = v
         return f(*a)
     assert call(0, None) == NULL
-    assert call(6, 32) == SHAPE
+    assert call(6, 4) == SHAPE                                 # G below 8
+    assert call(6, 48) == SHAPE                                # not a power of two
+    assert call(6, 512) == SHAPE
     assert call(2, 320) == SHAPE
     assert call(3, MIS) == ALIGN
     assert call(8, 7) == VALUE
@@ -164,7 +166,8 @@ def test_w4a8_argument_errors():
         return f(*a)
     assert call(0, None) == NULL
     assert call(9, None) == NULL
-    assert call(6, 32) == SHAPE
+    assert call(6, 4) == SHAPE
+    assert call(6, 24) == SHAPE
     assert call(2, 320) == SHAPE
     assert call(3, MIS) == ALIGN
     assert call(8, 7) == VALUE
@@ -202,7 +205,8 @@ def test_w4a4_asym_argument_errors():
         return f(*a)
     assert call(0, None) == NULL
     assert call(5, None) == NULL                                      # c_w
-    assert call(7, 32) == SHAPE
+    assert call(7, 4) == SHAPE
+    assert call(7, 1024) == SHAPE
     assert call(2, 320) == SHAPE
     assert call(3, MIS) == ALIGN
     assert call(9, 7) == VALUE
@@ -415,7 +419,8 @@ def test_kron_argument_errors():
     assert callg(0, None) == NULL
     assert callg(10, 96) == SHAPE
     assert callg(3, 32) == SHAPE
-    assert g(A, 16, 96, 8, 12, B, OUT, B, OUT, 32, 32, OUT, 0, WS, 1 << 30, None) == SHAPE     # G
+    assert g(A, 16, 96, 8, 12, B, OUT, B, OUT, 32, 4, OUT, 0, WS, 1 << 30, None) == SHAPE      # G below 8
+    assert g(A, 16, 96, 8, 12, B, OUT, B, OUT, 32, 64, OUT, 0, WS, 1 << 30, None) == SHAPE     # K % G
     assert callg(12, 5) == VALUE
     assert callg(14, 64) == WORKSPACE
     assert callg(1, 0) == OK
