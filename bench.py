@@ -16,7 +16,11 @@ linear, the SmoothQuant W8A8 linear on the prefill and FFN data and the
 top-2% decomposition and the zero-point W8A8 linear on the prefill data, and
 the Kronecker-transform W4A4 linear, the W4A8 group-Hadamard linear and the
 W4A4 linear with zero-point activations (one-sided) on the W4A4 data, in int8
-TOPS against the dense int8 MFMA peak.
+TOPS against the dense int8 MFMA peak.  Each also carries `gemm_roofline`:
+the GEMM kernels' own time per call, the sum of their average rocprofv3
+durations recorded in profiles/kernel_times.json for that workload (null while
+the record is missing or any kernel source has changed since it was taken),
+and the int8 TOPS and fraction of the dense peak that time gives.
 
 roofline: the decode kernel's algorithmic bytes per launch / its average
 launch duration, from HIP events recorded on the launch stream around the
@@ -128,6 +132,31 @@ def recorded_traffic(kernel, source):
     if not rec or rec.get("source") != source or rec.get("source_sha256") != sha:
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def recorded_gemm_time(key):
+    """GEMM-kernel time per call of workload `key` from profiles/kernel_times.json
+    (rocprofv3 --kernel-trace of `bench.py --only key`, written by
+    profile_counters.py): the sum of the average durations of its k_gemm_*
+    kernels, each of which runs once per call.  (None, reason) when the record
+    is missing or any kernel source changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "kernel_times.json")
+    if not os.path.exists(path):
+        return None, None, "no profiles/kernel_times.json"
+    with open(path) as f:
+        rec = json.load(f).get(key)
+    if rec is None:
+        return None, None, "no record for %s" % key
+    csrc = os.path.join(ROOT, "bit_quantized_linear_int8_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as fh:
+            if rec["sources_sha256"].get(name) != hashlib.sha256(fh.read()).hexdigest():
+                return None, None, "kernel sources changed since the record (%s)" % name
+    gemm = {k: v for k, v in rec["kernels"].items() if "k_gemm" in k}
+    if not gemm or len({v["calls"] for v in gemm.values()}) != 1:
+        return None, None, "record has no single set of GEMM launches"
+    return sum(v["avg_us"] for v in gemm.values()), sorted(gemm), rec["command"]
 
 
 # --------------------------------------------------------------------------- workloads
@@ -397,9 +426,19 @@ def main():
             log("[bench] %s: timing %d calls" % (name, st))
             ms, wall_ms, n = time_graph(torch, gs, st, min(args.warmup, 8))
             tops = ops / (ms * 1e-3) / 1e12
-            also.append({"workload": name, "M": c["M"], "K": c["K"], "N": c["N"], "ms_per_call": round(ms, 5),
-                         "int8_tops": round(tops, 2), "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
-                         "calls": n, "note": "whole call (all kernels), graph replay, weights warm"})
+            gus, gnames, gsrc = recorded_gemm_time(key)
+            if gus is None:
+                gemm = {"kernel_us": None, "reason": gsrc}
+            else:
+                gt = ops / (gus * 1e-6) / 1e12
+                gemm = {"bound": "mfma", "kernels": gnames, "kernel_us": round(gus, 3), "achieved": round(gt, 2),
+                        "peak": INT8_PEAK_TOPS, "unit": "TOPS", "frac": round(gt / INT8_PEAK_TOPS, 4),
+                        "weights": "warm (one weight, re-read every call)",
+                        "source": "profiles/kernel_times.json[%s]: %s" % (key, gsrc)}
+            also.append({"workload": name, "key": key, "M": c["M"], "K": c["K"], "N": c["N"],
+                         "ms_per_call": round(ms, 5), "int8_tops": round(tops, 2),
+                         "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4), "calls": n,
+                         "note": "whole call (all kernels), graph replay, weights warm", "gemm_roofline": gemm})
             log("[bench] %s: %.3f ms per call, %.1f TOPS" % (name, ms, tops))
             del fns, gs
             torch.cuda.empty_cache()

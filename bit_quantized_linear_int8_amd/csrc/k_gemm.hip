@@ -1039,6 +1039,13 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_w4a4(const uint32_t* __rest
 // ---------------------------------------------------------------------------
 constexpr int W4D_SW_LDS = 8192;                 // floats of per-group weight scales kept in LDS
 
+// Accumulator start value of a group: the int32 MFMA sum is added to the bit
+// pattern of 1.5 * 2^23, whose binade [2^23, 2^24) has a spacing of 1, so for
+// |sum| <= 2^22 the accumulator reads as the float 1.5 * 2^23 + sum and one
+// exact subtraction gives float(sum) -- no int-to-float conversion.
+constexpr int32_t kAccMagic = 0x4B400000;
+constexpr float kAccMagicF = 12582912.0f;
+
 // Chunk swizzle of 128-byte LDS rows (W4A8 activation stages): a 16-byte
 // fragment read takes one chunk of 16 consecutive rows, and rows r and r + 8
 // (also two rows apart in a 256-byte bank window) get different chunks.
@@ -1164,6 +1171,40 @@ __device__ __forceinline__ void w4a4_dma_body(const uint32_t* __restrict__ Xp, c
         }
     }
     __syncthreads();
+    // f += (accumulator - magic) * (group g's scale), per output
+    auto dequant = [&](int g) __attribute__((always_inline)) {
+        v4f swj[C::FN];
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+            const int cl = wn * C::TN + j * 16 + 4 * (lane >> 4);   // block-local column
+            if constexpr (sw_in_lds) {
+                swj[j] = *reinterpret_cast<const v4f*>(sws + sw_slot<C::BN>(g, cl));
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    swj[j][e] = __builtin_bit_cast(float, bload4(rsw, (uint32_t)((cl + e) * ng + g) * 4)) * SCALE;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    // (a named copy: clang's __builtin_bit_cast of a vector element
+                    // expression reads element 0)
+                    const int32_t a = acc[i][j][e];
+                    f[i][j][e] = __builtin_fmaf(__builtin_bit_cast(float, a) - kAccMagicF, swj[j][e], f[i][j][e]);
+                }
+                if constexpr (SPG > 2) acc[i][j] = v4i{kAccMagic, kAccMagic, kAccMagic, kAccMagic};
+            }
+    };
+    if constexpr (!STORE_ACC && SPG > 2) {
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j) acc[i][j] = v4i{kAccMagic, kAccMagic, kAccMagic, kAccMagic};
+    }
     for (int kt = 0; kt < nk; ++kt) {
         const int ahead = (kt + 2 < nk - 1 ? kt + 2 : nk - 1) - kt;   // stages issued after kt
         if (ahead >= 2)
@@ -1218,15 +1259,16 @@ __device__ __forceinline__ void w4a4_dma_body(const uint32_t* __restrict__ Xp, c
                         *reinterpret_cast<const u32x2*>(sb + swz64(wn * C::TN + j * 16 + (lane & 15), c) + within));
             }
             // A group of at most two steps starts at a step known at compile
-            // time (step = 2 kt + s2): its first MFMA takes a zero accumulator
-            // instead of clearing the accumulators after each dequant.
+            // time (step = 2 kt + s2): its first MFMA takes the start value (zero,
+            // or kAccMagic where the dequant reads the sum as a float) instead of
+            // resetting the accumulators after each dequant.
             const bool fresh = SPG <= 2 && (SPG == 1 || s2 == 0);
+            const v4i acc0 = STORE_ACC ? v4i{0, 0, 0, 0} : v4i{kAccMagic, kAccMagic, kAccMagic, kAccMagic};
 #pragma unroll
             for (int i = 0; i < C::FM; ++i)
 #pragma unroll
                 for (int j = 0; j < C::FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fb[j], fa[i], fresh ? v4i{0, 0, 0, 0} : acc[i][j],
-                                                                      0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fb[j], fa[i], fresh ? acc0 : acc[i][j], 0, 0, 0);
             if ((step + 1) % SPG == 0) {
                 const int g = step / SPG;
                 if constexpr (STORE_ACC) {
@@ -1245,28 +1287,7 @@ __device__ __forceinline__ void w4a4_dma_body(const uint32_t* __restrict__ Xp, c
                         }
                     }
                 } else {
-                    v4f swj[C::FN];
-#pragma unroll
-                    for (int j = 0; j < C::FN; ++j) {
-                        const int cl = wn * C::TN + j * 16 + 4 * (lane >> 4);   // block-local column
-                        if constexpr (sw_in_lds) {
-                            swj[j] = *reinterpret_cast<const v4f*>(sws + sw_slot<C::BN>(g, cl));
-                        } else {
-#pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                swj[j][e] = __builtin_bit_cast(float, bload4(rsw, (uint32_t)((cl + e) * ng + g) * 4)) *
-                                            SCALE;
-                        }
-                    }
-#pragma unroll
-                    for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-                        for (int j = 0; j < C::FN; ++j) {
-#pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                f[i][j][e] = __builtin_fmaf((float)acc[i][j][e], swj[j][e], f[i][j][e]);
-                            if constexpr (SPG > 2) acc[i][j] = v4i{0, 0, 0, 0};
-                        }
+                    dequant(g);
                 }
             }
         }

@@ -19,6 +19,13 @@ usage: python profile_counters.py --kernel k_decode_mixed \\
            matrix-core use per GEMM kernel from runs of SQ_VALU_MFMA_BUSY_CYCLES,
            GRBM_GUI_ACTIVE, SQ_INSTS_VALU_MFMA_MOPS_I8, SQ_LDS_BANK_CONFLICT and
            SQ_LDS_IDX_ACTIVE (median over dispatches); prints a table, writes nothing
+
+       python profile_counters.py --stats RUN.db
+           kernel durations of a --kernel-trace run (the table the profiles/ summaries hold)
+
+       python profile_counters.py --kernel-times RUN.db WORKLOAD "COMMAND"
+           call counts and average durations of the library's kernels in one
+           workload's run (bench.py --only WORKLOAD) into profiles/kernel_times.json
 """
 from __future__ import annotations
 
@@ -87,10 +94,73 @@ def mfma_table(paths):
                                                           100 * busy, ops, 100 * conf))
 
 
+def kernel_durations(db_path):
+    """{kernel name: [duration in us per dispatch]} from a --kernel-trace run."""
+    db = sqlite3.connect(db_path)
+    cur = db.cursor()
+    cols = [d[1] for d in cur.execute("pragma table_info(kernels)")]
+    ci = {c: i for i, c in enumerate(cols)}
+    name_col = "kernel_name" if "kernel_name" in ci else "name"
+    out = collections.OrderedDict()
+    for r in cur.execute("select * from kernels order by start"):
+        out.setdefault(r[ci[name_col]], []).append((r[ci["end"]] - r[ci["start"]]) / 1000.0)
+    return out
+
+
+def stats_table(db_path):
+    """Kernel duration table (calls, avg, median, min, max in us, share of the
+    summed time) of one rocprofv3 --kernel-trace database."""
+    d = kernel_durations(db_path)
+    total = sum(sum(v) for v in d.values()) or 1.0
+    print("%-70s %6s %9s %9s %9s %9s %6s" % ("kernel", "calls", "avg_us", "med_us", "min_us", "max_us", "pct"))
+    for k, v in sorted(d.items(), key=lambda kv: -sum(kv[1])):
+        print("%-70s %6d %9.2f %9.2f %9.2f %9.2f %6.2f" % (k.split("(")[0].replace("void ", "")[:70], len(v),
+                                                            statistics.mean(v), statistics.median(v), min(v), max(v),
+                                                            100.0 * sum(v) / total))
+
+
+def record_kernel_times(db_path, workload, command):
+    """Every library kernel's call count and average duration in one
+    workload's --kernel-trace run, into profiles/kernel_times.json under the
+    workload's name, with the SHA-256 of every kernel source file (bench.py
+    uses a record only while all of them are unchanged)."""
+    d = kernel_durations(db_path)
+    csrc = os.path.join(ROOT, "bit_quantized_linear_int8_amd", "csrc")
+    shas = {}
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            shas[f] = hashlib.sha256(fh.read()).hexdigest()
+    rec = {"command": command, "sources_sha256": shas, "kernels": {}}
+    for k, v in d.items():
+        if not k.startswith("void qa::") and not k.startswith("qa::"):
+            continue
+        rec["kernels"][k.split("(")[0].replace("void ", "")] = {
+            "calls": len(v), "avg_us": round(statistics.mean(v), 3), "median_us": round(statistics.median(v), 3)}
+    if not rec["kernels"]:
+        raise SystemExit("no library kernel in %s" % db_path)
+    path = os.path.join(ROOT, "profiles", "kernel_times.json")
+    data = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            data = json.load(f)
+    data[workload] = rec
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps({workload: rec["kernels"]}, indent=1))
+
+
 def main():
     import sys
     if len(sys.argv) > 1 and sys.argv[1] == "--mfma":
         mfma_table(sys.argv[2:])
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--stats":
+        stats_table(sys.argv[2])
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--kernel-times":
+        # --kernel-times RUN.db WORKLOAD "COMMAND"
+        record_kernel_times(sys.argv[2], sys.argv[3], sys.argv[4])
         return
     p = argparse.ArgumentParser()
     p.add_argument("--kernel", required=True)
