@@ -385,15 +385,13 @@ __device__ __forceinline__ void store_out(void* out, int dtype, int64_t off, flo
 // a multiple of 4 and all four are in range, else only the first n are.
 __device__ __forceinline__ void store_out4(void* out, int dtype, int64_t off, const v4f& v, bool vec, int n) {
     if (vec) {
-        if (dtype == 0) {
+        // (two packed conversions per four values, v_cvt_pk_f16_f32 / v_cvt_pk_bf16_f32)
+        if (dtype == 0)
             *reinterpret_cast<v4f*>(static_cast<float*>(out) + off) = v;
-        } else {
-            uint16_t h[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) h[e] = dtype == 1 ? f2h(v[e]) : f2bf(v[e]);
-            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + off) =
-                u32x2{(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
-        }
+        else if (dtype == 1)
+            *reinterpret_cast<v4h*>(static_cast<uint16_t*>(out) + off) = __builtin_convertvector(v, v4h);
+        else
+            *reinterpret_cast<v4bf*>(static_cast<uint16_t*>(out) + off) = __builtin_convertvector(v, v4bf);
     } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -512,9 +510,9 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_i8_mixed(const int8_t* __re
     int* hidx = reinterpret_cast<int*>(smem + (C::BM + C::BN) * OST * 2);
     float* swl = reinterpret_cast<float*>(hidx + OCAP);
     static_assert((C::BM + C::BN) * OST * 2 + (OCAP + C::BN) * 4 <= C::LDS, "outlier staging exceeds LDS");
-    // (the row quantizer writes the compact rows only for counts above
-    // OUTLIER_PREFETCH, which the other configurations gather themselves)
-    const bool use_xo = ep.Xo != nullptr && cnt > OUTLIER_PREFETCH && cnt <= XO_CAP;
+    // (the row quantizer writes the compact rows for every nonzero count;
+    // configurations that prefetch up to PRE columns gather those themselves)
+    const bool use_xo = ep.Xo != nullptr && cnt > PRE && cnt <= XO_CAP;
     auto stage = [&](int hs) __attribute__((always_inline)) {
         const int hn = cnt - hs < OCAP ? cnt - hs : OCAP;
         const int hp = (hn + 31) & ~31;
@@ -547,35 +545,49 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_i8_mixed(const int8_t* __re
             }
         }
         __syncthreads();                                      // the column list
-        const int hl = threadIdx.x & 31, rs = threadIdx.x >> 5;
-        for (int hq = 0; hq < hp; hq += 32) {
-            const int h = hq + hl;
-            const bool hok = h < hn;
-            const uint32_t k = (uint32_t)hidx[h];
-            for (int rb = use_xo ? C::BM : 0; rb < C::BM + C::BN; rb += RSTEP * GB) {
-                uint32_t v[GB];
+        // the (row, column) pairs of the real columns, GB per thread and
+        // batch, all issued before any is written: a pass with up to
+        // GB * THREADS pairs costs one load latency
+        const int r0 = use_xo ? C::BM : 0;                       // rows to gather: [r0, BM + BN)
+        const int npair = (C::BM + C::BN - r0) * hn;
+        for (int pb = 0; pb < npair; pb += GB * C::THREADS) {
+            uint32_t v[GB];
+            int pr[GB], ph[GB];
 #pragma unroll
-                for (int u = 0; u < GB; ++u) {
-                    const int r = rb + rs + RSTEP * u;
-                    const bool ok = hok && r < C::BM + C::BN;
-                    const bool isx = r < C::BM;
-                    const uint32_t rr = isx ? r : r - C::BM;
-                    if (isx)
-                        v[u] = bload2(rxo, ok ? (rr * (uint32_t)K + k) * 2 : kOOB);
-                    else if (ep.W16)
-                        v[u] = bload2(rwo, ok ? (rr * (uint32_t)K + k) * 2 : kOOB);
-                    else
-                        v[u] = bload1(rwo, ok ? rr * (uint32_t)K + k : kOOB);
-                }
+            for (int u = 0; u < GB; ++u) {
+                const int pi = pb + (int)threadIdx.x + u * C::THREADS;
+                const bool ok = pi < npair;
+                const int q = ok ? pi : 0;
+                const int rq = q / hn;
+                pr[u] = ok ? r0 + rq : -1;
+                ph[u] = q - rq * hn;
+                const uint32_t k = (uint32_t)hidx[ph[u]];
+                const int r = r0 + rq;
+                const bool isx = r < C::BM;
+                const uint32_t rr = isx ? r : r - C::BM;
+                if (isx)
+                    v[u] = bload2(rxo, ok ? (rr * (uint32_t)K + k) * 2 : kOOB);
+                else if (ep.W16)
+                    v[u] = bload2(rwo, ok ? (rr * (uint32_t)K + k) * 2 : kOOB);
+                else
+                    v[u] = bload1(rwo, ok ? rr * (uint32_t)K + k : kOOB);
+            }
 #pragma unroll
-                for (int u = 0; u < GB; ++u) {
-                    const int r = rb + rs + RSTEP * u;
-                    if (r < C::BM + C::BN) {
-                        uint16_t hv = (uint16_t)v[u];
-                        if (r >= C::BM && !ep.W16) hv = hok ? f2h(swl[r - C::BM] * (float)(int8_t)(uint8_t)v[u]) : 0;
-                        xo[r * OST + h] = __builtin_bit_cast(_Float16, hv);
-                    }
+            for (int u = 0; u < GB; ++u) {
+                const int r = pr[u];
+                if (r >= 0) {
+                    uint16_t hv = (uint16_t)v[u];
+                    if (r >= C::BM && !ep.W16) hv = f2h(swl[r - C::BM] * (float)(int8_t)(uint8_t)v[u]);
+                    xo[r * OST + ph[u]] = __builtin_bit_cast(_Float16, hv);
                 }
+            }
+        }
+        // zero padding of the gathered rows up to the 32-column slab
+        if (hp > hn) {
+            const int pw = hp - hn;
+            for (int q = threadIdx.x; q < (C::BM + C::BN - r0) * pw; q += C::THREADS) {
+                const int rq = q / pw;
+                xo[(r0 + rq) * OST + hn + (q - rq * pw)] = __builtin_bit_cast(_Float16, (uint16_t)0);
             }
         }
     };

@@ -544,11 +544,10 @@ __global__ __launch_bounds__(256) void k_rowquant_i8(const uint16_t* __restrict_
             mask_of(lane + 64 * i, v[i], mk[i]);
         }
         if constexpr (MASK == MASK_FLAGS) {
-            // this row's outlier values, in list order, into xo[row][0 .. XO_CAP),
-            // when the GEMM will read them (more columns than it prefetches)
+            // this row's outlier values, in list order, into xo[row][0 .. XO_CAP)
             const int64_t nw = (K + 63) / 64, per = (nw + 255) / 256;
             const uint32_t t0 = wtot[0], t1 = wtot[1], t2 = wtot[2];
-            if (xo && t0 + t1 + t2 + wtot[3] > (uint32_t)OUTLIER_PREFETCH) {
+            if (xo && t0 + t1 + t2 + wtot[3] > 0u) {
 #pragma unroll
                 for (int i = 0; i < NC; ++i) {
                     const int64_t ch = lane + 64 * i;

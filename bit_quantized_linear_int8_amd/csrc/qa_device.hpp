@@ -9,6 +9,8 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
 
 #define QA_WAVE 64
 
@@ -24,13 +26,9 @@ __device__ __forceinline__ uint16_t f2h(float f) {
     return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs; NaN stays NaN).
+// fp32 -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32; NaN stays NaN).
 __device__ __forceinline__ uint16_t f2bf(float f) {
-    uint32_t u = __builtin_bit_cast(uint32_t, f);
-    if ((u & 0x7fffffffu) > 0x7f800000u)
-        return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // Maximum over the 64 lanes of a wave (every lane receives it).

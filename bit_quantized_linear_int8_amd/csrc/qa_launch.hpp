@@ -46,8 +46,10 @@ hipError_t launch_rowquant_i8(const uint16_t* X, int64_t rows, int64_t K, const 
 // the first XO_CAP outlier columns, written by the flag-masked row
 // quantizer and read by the GEMM epilogue with contiguous loads.
 constexpr int XO_CAP = 256;
-// Up to this many outlier columns the GEMM gathers X and w~ itself (issued
-// behind its first pipeline stages); the compact rows serve larger counts.
+// Up to this many outlier columns the GEMM configurations with registers to
+// spare gather X and w~ themselves (issued behind their first pipeline
+// stages); the compact rows (written for every nonzero count) serve larger
+// counts and the register-bound wide configuration.
 constexpr int OUTLIER_PREFETCH = 8;
 
 // Dynamic [-127, 127] row quantization with the outlier flags of `scratch`
