@@ -526,9 +526,13 @@ __global__ __launch_bounds__(256) void k_rowquant_i8(const uint16_t* __restrict_
         z = z_in ? z_in[row] : 0;
     }
     // chunk ch: fp16 bits with MASK_FLAGS already applied, byte mask for MASK_BYTES
+    uint32_t fbl = 0u;                                  // flag byte of the last chunk masked
     auto mask_of = [&](int64_t ch, u32x4& v, u32x2& mk) {
         mk = u32x2{0u, 0u};
-        if constexpr (MASK == MASK_FLAGS) v &= lut[ch < nch ? flb[ch] : 0];
+        if constexpr (MASK == MASK_FLAGS) {
+            fbl = ch < nch ? flb[ch] : 0u;
+            v &= lut[fbl];
+        }
         if constexpr (MASK == MASK_BYTES) mk = bload8(rm, (uint32_t)ch * 8);
     };
     auto load = [&](int64_t ch, u32x4& v, u32x2& mk) {
@@ -538,37 +542,12 @@ __global__ __launch_bounds__(256) void k_rowquant_i8(const uint16_t* __restrict_
     if constexpr (NC > 0) {
         u32x4 v[NC];
         u32x2 mk[NC];
+        uint32_t fbv[NC];
 #pragma unroll
         for (int i = 0; i < NC; ++i) {
             v[i] = vpre[i];
             mask_of(lane + 64 * i, v[i], mk[i]);
-        }
-        if constexpr (MASK == MASK_FLAGS) {
-            // this row's outlier values, in list order, into xo[row][0 .. XO_CAP)
-            const int64_t nw = (K + 63) / 64, per = (nw + 255) / 256;
-            const uint32_t t0 = wtot[0], t1 = wtot[1], t2 = wtot[2];
-            if (xo && t0 + t1 + t2 + wtot[3] > 0u) {
-#pragma unroll
-                for (int i = 0; i < NC; ++i) {
-                    const int64_t ch = lane + 64 * i;
-                    const uint32_t fb = ch < nch ? flb[ch] : 0u;
-                    if (fb) {
-                        const int64_t w = ch >> 3;
-                        const int ow = (int)((w / per) >> 6);          // wave that ranked word w
-                        const uint32_t woff = (ow > 0 ? t0 : 0u) + (ow > 1 ? t1 : 0u) + (ow > 2 ? t2 : 0u);
-                        const unsigned long long fw = flw[w];
-                        const int sh = (int)(ch & 7) * 8;
-                        uint32_t rank = wpre[w] + woff + (uint32_t)__popcll(sh ? fw & ((1ull << sh) - 1ull) : 0ull);
-                        for (int b = 0; b < 8; ++b) {
-                            if ((fb >> b) & 1u) {
-                                if (rank < (uint32_t)XO_CAP)
-                                    xo[row * XO_CAP + rank] = (uint16_t)(vpre[i][b >> 1] >> (16 * (b & 1)));
-                                ++rank;
-                            }
-                        }
-                    }
-                }
-            }
+            fbv[i] = fbl;
         }
         if constexpr (!STATIC) {
             float amax = 0.0f;
@@ -613,6 +592,34 @@ __global__ __launch_bounds__(256) void k_rowquant_i8(const uint16_t* __restrict_
                     c = clip_codes(codes8_dyn_h(v[i], s, r), qmin);
                 }
                 *reinterpret_cast<u32x2*>(qr + ch * 8) = c;
+            }
+        }
+        if constexpr (MASK == MASK_FLAGS) {
+            // this row's outlier values, in list order, into xo[row][0 .. XO_CAP)
+            // (after the codes: its LDS reads wait behind their stores)
+            const int64_t nw = (K + 63) / 64, per = (nw + 255) / 256;
+            const uint32_t t0 = wtot[0], t1 = wtot[1], t2 = wtot[2];
+            if (xo && t0 + t1 + t2 + wtot[3] > 0u) {
+#pragma unroll
+                for (int i = 0; i < NC; ++i) {
+                    const int64_t ch = lane + 64 * i;
+                    const uint32_t fb = fbv[i];
+                    if (fb) {
+                        const int64_t w = ch >> 3;
+                        const int ow = (int)((w / per) >> 6);          // wave that ranked word w
+                        const uint32_t woff = (ow > 0 ? t0 : 0u) + (ow > 1 ? t1 : 0u) + (ow > 2 ? t2 : 0u);
+                        const unsigned long long fw = flw[w];
+                        const int sh = (int)(ch & 7) * 8;
+                        uint32_t rank = wpre[w] + woff + (uint32_t)__popcll(sh ? fw & ((1ull << sh) - 1ull) : 0ull);
+                        for (int b = 0; b < 8; ++b) {
+                            if ((fb >> b) & 1u) {
+                                if (rank < (uint32_t)XO_CAP)
+                                    xo[row * XO_CAP + rank] = (uint16_t)(vpre[i][b >> 1] >> (16 * (b & 1)));
+                                ++rank;
+                            }
+                        }
+                    }
+                }
             }
         }
     } else {
