@@ -59,9 +59,10 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--only", default=None,
                    help="run one workload only (decode|prefill|w8a8|w4a4|smooth_prefill|smooth_ffn|topk_prefill|"
-                        "asym_prefill|kron_w4a4|w4a8|w4a4_asym|copy), for "
+                        "asym_prefill|kron_w4a4|w4a8|w4a4_asym|copy|floor), for "
                         "profiling; copy is a plain "
-                        "1 GiB device copy used to calibrate HBM byte counters")
+                        "1 GiB device copy used to calibrate HBM byte counters; floor sweeps the plain "
+                        "read of the decode step's bytes (qa_probe_stream_read) and an empty launch")
     return p.parse_args()
 
 
@@ -299,6 +300,39 @@ def w4a8_workload(torch, qa, synthetic, dev):
     return c, fns, 2 * M * N * K
 
 
+def read_floor(torch, qa, dev, steps, warmup):
+    """The single-launch floor the decode kernel is measured against: one plain
+    read of the decode step's bytes (16,924,672 B at 8 x 4096 x 4096) per
+    launch, from as many buffer copies as the decode bench uses (every launch
+    reads HBM), timed like the decode steps (HIP-graph replay, events around
+    exactly `steps` launches), over workgroup counts, bytes per lane and
+    load, and loads in flight per lane; and the same grid with nothing to
+    read (the launch cost)."""
+    M = K = N = 4096
+    nbytes = N * K + 4 * N + 2 * 8 * K + 2 * 8 * N
+    copies = max(2, -(-2 * MALL_BYTES // nbytes))
+    bufs = [torch.ones(nbytes, dtype=torch.uint8, device=dev) for _ in range(copies)]
+    sink = torch.empty(2048 * 512, dtype=torch.int32, device=dev)
+    steps, warmup = min(int(steps), 256), min(int(warmup), 32)
+
+    def run(nb, wgs, lb, u):
+        fns = [(lambda b=b: qa.qa_probe_stream_read(b, nb, wgs, lb, u, sink=sink)) for b in bufs]
+        ms, _, n = time_graph(torch, GraphSteps(torch, fns), steps, warmup)
+        return ms * 1e3
+    empty = run(0, 256, 16, 1)
+    sweep = []
+    for wgs in (256, 512, 1024, 2048):
+        for lb in (16, 8, 4):
+            for u in (1, 4, 8):
+                us = run(nbytes, wgs, lb, u)
+                sweep.append({"wgs": wgs, "lane_bytes": lb, "unroll": u, "us": round(us, 3),
+                              "GBs": round(nbytes / (us * 1e-6) / 1e9, 1)})
+                log("[floor] wgs %4d lane_bytes %2d unroll %d: %.3f us" % (wgs, lb, u, us))
+    best = min(sweep, key=lambda r: r["us"])
+    return {"bytes": nbytes, "copies": copies, "launches_timed": steps, "empty_launch_us": round(empty, 3),
+            "best": best, "sweep": sweep}
+
+
 # --------------------------------------------------------------------------- CPU oracle baseline
 def cpu_baseline(c, nbytes, seconds):
     import numpy as np
@@ -352,6 +386,9 @@ def main():
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / reps
         print(json.dumps({"copy_bytes": n, "ms": round(ms, 4), "read_write_GBs": round(2 * n / (ms * 1e-3) / 1e9, 1)}))
+        return
+    if args.only == "floor":
+        print(json.dumps({"floor": read_floor(torch, qa, dev, args.steps, args.warmup)}), flush=True)
         return
     if args.only in (None, "decode"):
         log("[bench] decode_mixed: building inputs")

@@ -37,6 +37,7 @@ EXPORTS = (
     "qa_hadamard_quant_int8", "qa_qlinear_w4a8_workspace", "qa_qlinear_w4a8",
     "qa_hadamard_quant_int4_asym", "qa_w4_column_terms", "qa_qlinear_w4a4_asym_workspace", "qa_qlinear_w4a4_asym",
     "qa_gemm_i8_i32", "qa_gemm_w4a4_group_acc", "qa_gemm_w4a8_group_acc",
+    "qa_probe_stream_read",
 )
 
 _DTYPE_CODE = {torch.float32: QA_F32, torch.float16: QA_F16, torch.bfloat16: QA_BF16}
@@ -101,6 +102,7 @@ def lib() -> ctypes.CDLL:
             "qa_w4_column_terms": (S, [P, P, I64, I64, I32, P, P]),
             "qa_qlinear_w4a4_asym_workspace": (SZ, [I64, I64]),
             "qa_qlinear_w4a4_asym": (S, [P, I64, I64, P, P, P, I64, I32, P, S, P, SZ, P]),
+            "qa_probe_stream_read": (S, [P, SZ, I32, I32, I32, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -593,3 +595,15 @@ def qa_gemm_w4a8_group_acc(Xq, Wp, G: int, stream=None):
     _check("qa_gemm_w4a8_group_acc",
            lib().qa_gemm_w4a8_group_acc(_p(Xq), _p(Wp), M, K, N, int(G), _p(acc), _stream(stream)))
     return acc
+
+
+def qa_probe_stream_read(src, nbytes: int, wgs: int, lane_bytes: int = 16, unroll: int = 4, sink=None, stream=None):
+    """Measurement helper: read src[0 .. nbytes) once (the single-launch HBM read floor)."""
+    _dev(src, "src", None)
+    if sink is None:
+        sink = _empty(stream, (int(wgs) * 512,), dtype=torch.int32, device=src.device)
+    _check("qa_probe_stream_read",
+           lib().qa_probe_stream_read(_p(src), int(nbytes), int(wgs), int(lane_bytes), int(unroll), _p(sink),
+                                      _stream(stream)))
+    return sink
+

@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libqa.so")
 
 ARCH = "gfx950"
 SOURCES = ["qa_api.cpp", "qa_noalloc.hip", "k_quant.hip", "k_smooth.hip", "k_kron.hip", "k_gemm.hip",
-           "k_decode.hip"]
+           "k_decode.hip", "k_probe.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -820,4 +820,19 @@ qa_status qa_gemm_w4a8_group_acc(const int8_t* Xq, const uint32_t* Wp, int64_t M
                          "qa_gemm_w4a8_group_acc");
 }
 
+qa_status qa_probe_stream_read(const void* src, size_t bytes, int32_t wgs, int32_t lane_bytes, int32_t unroll,
+                               uint32_t* sink, void* stream) {
+    if (wgs < 1 || wgs > 65536) return fail(QA_ERR_SHAPE, "qa_probe_stream_read: need wgs in [1, 65536]");
+    if (lane_bytes != 4 && lane_bytes != 8 && lane_bytes != 16)
+        return fail(QA_ERR_VALUE, "qa_probe_stream_read: lane_bytes must be 4, 8 or 16");
+    if (unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8)
+        return fail(QA_ERR_VALUE, "qa_probe_stream_read: unroll must be 1, 2, 4 or 8");
+    if (!src || !sink) return fail(QA_ERR_NULL, "qa_probe_stream_read: NULL pointer");
+    if (!aligned(src, 16) || !aligned(sink, 4))
+        return fail(QA_ERR_ALIGN, "qa_probe_stream_read: src 16-byte, sink 4-byte aligned");
+    return device_status(qa::launch_stream_read(static_cast<const uint8_t*>(src), (uint64_t)bytes, wgs, lane_bytes,
+                                                unroll, sink, as_stream(stream)),
+                         "qa_probe_stream_read");
+}
+
 }  // extern "C"

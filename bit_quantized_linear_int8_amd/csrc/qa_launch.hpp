@@ -160,6 +160,11 @@ struct DecodeStages {
     int8_t* xq;
 };
 bool decode_supported(int64_t M, int64_t K);
+// Measurement helper: `bytes` of src read by `wgs` workgroups of 512 threads,
+// lane_bytes (4, 8, 16) per lane and load, `unroll` (1, 2, 4, 8) loads in flight.
+hipError_t launch_stream_read(const uint8_t* src, uint64_t bytes, int wgs, int lane_bytes, int unroll, uint32_t* sink,
+                              hipStream_t st);
+
 hipError_t launch_decode_mixed(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* s_w,
                                const uint16_t* W16, int64_t N, float tau, void* out, int out_dtype,
                                const DecodeStages& stages, hipStream_t st);

@@ -582,6 +582,27 @@ qa_status qa_gemm_w4a4_group_acc(const uint32_t* Xp, const uint32_t* Wp, int64_t
 qa_status qa_gemm_w4a8_group_acc(const int8_t* Xq, const uint32_t* Wp, int64_t M, int64_t K,
                                  int64_t N, int32_t G, int32_t* acc, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Measurement helper, not part of the method: the single-launch HBM read
+ * floor that the decode kernel (one launch streaming the whole int8 weight)
+ * is compared with.
+ *
+ * qa_probe_stream_read
+ *   Reads src[0 .. bytes) once with wgs workgroups of 512 threads, each a
+ *   contiguous slice; every load instruction moves lane_bytes bytes per lane
+ *   (64 * lane_bytes contiguous bytes per wave instruction) and `unroll`
+ *   loads per lane are in flight before any is used.  The data are folded
+ *   into a value stored to sink[wg * 512 + thread] only if it equals a fixed
+ *   constant (so sink is normally left untouched; it must hold wgs * 512
+ *   u32).  bytes == 0 launches the same grid with nothing to read (the cost
+ *   of the launch itself).
+ *   src: device, 16-byte aligned; sink: device u32 [wgs * 512].
+ *   Errors: NULL pointers, wgs not in [1, 65536], lane_bytes not 4, 8 or 16,
+ *   unroll not 1, 2, 4 or 8, misaligned src.
+ * ------------------------------------------------------------------------- */
+qa_status qa_probe_stream_read(const void* src, size_t bytes, int32_t wgs, int32_t lane_bytes, int32_t unroll,
+                               uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

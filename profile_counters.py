@@ -20,6 +20,10 @@ usage: python profile_counters.py --kernel k_decode_mixed \\
            GRBM_GUI_ACTIVE, SQ_INSTS_VALU_MFMA_MOPS_I8, SQ_LDS_BANK_CONFLICT and
            SQ_LDS_IDX_ACTIVE (median over dispatches); prints a table, writes nothing
 
+       python profile_counters.py --waves RUN.db [RUN.db ...]
+           VALU use and s_waitcnt share per kernel from runs of SQ_WAVE_CYCLES, SQ_BUSY_CYCLES,
+           SQ_WAIT_ANY, SQ_WAIT_INST_ANY, SQ_ACTIVE_INST_VALU, SQ_ACTIVE_INST_ANY, GRBM_GUI_ACTIVE
+
        python profile_counters.py --stats RUN.db
            kernel durations of a --kernel-trace run (the table the profiles/ summaries hold)
 
@@ -94,6 +98,34 @@ def mfma_table(paths):
                                                           100 * busy, ops, 100 * conf))
 
 
+def waves_table(paths):
+    """VALU use and waiting of each library kernel from runs of SQ_WAVE_CYCLES,
+    SQ_BUSY_CYCLES, SQ_WAIT_ANY, SQ_WAIT_INST_ANY, SQ_ACTIVE_INST_VALU,
+    SQ_ACTIVE_INST_ANY and GRBM_GUI_ACTIVE (median over dispatches):
+    valu_busy = SQ_ACTIVE_INST_VALU x 4 / (SIMDs x cycles), the share of SIMD
+    cycles issuing VALU work (a wave64 VALU instruction occupies a SIMD for 4
+    cycles); wait = SQ_WAIT_ANY / SQ_WAVE_CYCLES, the share of wave-cycles
+    spent in s_waitcnt; inst_wait = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES, waiting
+    for an instruction to issue."""
+    counters = ("SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU",
+                "SQ_ACTIVE_INST_ANY", "GRBM_GUI_ACTIVE")
+    print("%-58s %6s %10s %9s %7s %9s" % ("kernel", "disp", "cycles", "valu_busy", "wait", "inst_wait"))
+    for path in paths:
+        med = {c: per_dispatch(path, c) for c in counters}
+        for k in sorted(med["SQ_WAVE_CYCLES"]):
+            if "qa::" not in k:
+                continue
+            v = {c: statistics.median(med[c][k]) for c in counters if k in med[c]}
+            if len(v) < len(counters) or v["SQ_WAVE_CYCLES"] == 0:
+                continue
+            cycles = v["GRBM_GUI_ACTIVE"] / XCDS
+            valu = v["SQ_ACTIVE_INST_VALU"] * 4 / (cycles * SIMDS)
+            name = k.split("(")[0].replace("void ", "")
+            print("%-58s %6d %10.0f %8.1f%% %6.1f%% %8.1f%%" % (name[:58], len(med["GRBM_GUI_ACTIVE"][k]), cycles,
+                                                          100 * valu, 100 * v["SQ_WAIT_ANY"] / v["SQ_WAVE_CYCLES"],
+                                                          100 * v["SQ_WAIT_INST_ANY"] / v["SQ_WAVE_CYCLES"]))
+
+
 def kernel_durations(db_path):
     """{kernel name: [duration in us per dispatch]} from a --kernel-trace run."""
     db = sqlite3.connect(db_path)
@@ -154,6 +186,9 @@ def main():
     import sys
     if len(sys.argv) > 1 and sys.argv[1] == "--mfma":
         mfma_table(sys.argv[2:])
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--waves":
+        waves_table(sys.argv[2:])
         return
     if len(sys.argv) > 1 and sys.argv[1] == "--stats":
         stats_table(sys.argv[2])

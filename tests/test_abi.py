@@ -491,3 +491,14 @@ def test_noalloc_argument_errors():
     assert call(M=4096, K=16384) == WORKSPACE
     assert "static scratch" in qa.last_error()
     assert L.qa_qlinear_int8_mixed_workspace(4096, 8192) <= qa.NOALLOC_SCRATCH_BYTES
+
+
+def test_probe_stream_read_argument_errors():
+    p = qa.lib().qa_probe_stream_read
+    assert p(A, 1 << 20, 0, 16, 4, OUT, None) == SHAPE
+    assert p(A, 1 << 20, 65537, 16, 4, OUT, None) == SHAPE
+    assert p(A, 1 << 20, 256, 12, 4, OUT, None) == VALUE
+    assert p(A, 1 << 20, 256, 16, 3, OUT, None) == VALUE
+    assert p(None, 1 << 20, 256, 16, 4, OUT, None) == NULL
+    assert p(A, 1 << 20, 256, 16, 4, None, None) == NULL
+    assert p(MIS, 1 << 20, 256, 16, 4, OUT, None) == ALIGN
