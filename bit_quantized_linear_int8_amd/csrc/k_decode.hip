@@ -188,6 +188,10 @@ __global__ __launch_bounds__(2 * DEC_THREADS) void k_decode_mixed(const uint16_t
     const rsrc_t rsn = make_rsrc(s_w + n0, (N - n0) * 4);
     const float swg = __builtin_bit_cast(float, bload4(rsn, (uint32_t)(t & 15) * 4));   // scale of channel n0 + t % 16
     const rsrc_t rsw = make_rsrc(Wq + n0 * K, (N - n0) * K);       // channels past N read zeros
+    // Read the arguments used only late (the second 64 bytes of the argument
+    // block) into registers now: a scalar-cache miss after the weight stream
+    // has started waits behind it in the memory queues.
+    asm volatile("" ::"s"(out_dtype), "s"(st.idx), "s"(st.count), "s"(st.s_x), "s"(st.xq), "s"(out));
     if (threadIdx.x == 0) abar = 0;
 
     v4i acc = v4i{0, 0, 0, 0};
@@ -388,16 +392,18 @@ __global__ __launch_bounds__(2 * DEC_THREADS) void k_decode_mixed(const uint16_t
             graw[q] = bload4(rsg, h < count ? (b & ~3u) : kOOB);
             gsh[q] = (b & 3u) * 8;
         }
-        // 3a. int32 MFMA over this wave's K steps
+        // 3a. int32 MFMA over this wave's K steps.  The MFMAs are unconditional
+        // (a step past the end has an all-zero weight fragment, so it adds
+        // nothing): under a branch on s < S the compiler moves the step's
+        // weight load into the branch, behind barrier 2, where its whole
+        // latency lands after the activation codes.
         const int arow = lane & 15;
 #pragma unroll
         for (int j = 0; j < STEPS; ++j) {
             const int s = ww + DEC_WAVES * j;
-            if (s < S) {
-                v4i fa = v4i{0, 0, 0, 0};
-                if (arow < M) fa = *reinterpret_cast<const v4i*>(aq + arow * LDA + 64 * s + 16 * (lane >> 4));
-                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa, wv[j], acc, 0, 0, 0);
-            }
+            v4i fa = v4i{0, 0, 0, 0};
+            if (arow < M && s < S) fa = *reinterpret_cast<const v4i*>(aq + arow * LDA + 64 * s + 16 * (lane >> 4));
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa, wv[j], acc, 0, 0, 0);
         }
         // acc: lane l, element e = token 4 (l / 16) + e, channel l % 16
 #pragma unroll
