@@ -6,13 +6,14 @@
 // multiplies the 64-byte K steps w, w + 8, w + 16, ... so each weight load
 // instruction of the block covers 16 rows x 512 contiguous bytes.  A workgroup
 //   1. loads X (thread t owns the 8-column chunks t and t + 512 of every
-//      token) and the scale of the channel it writes in the epilogue, and only
-//      once this wave's X has arrived issues ALL of its weight loads (directly
-//      in the B-operand layout of v_mfma_i32_16x16x64_i8, 16 bytes per lane
-//      and step).  Issued behind the weight requests, the X requests (hits on
-//      lines every workgroup reads) queue behind weight misses in the caches
-//      and arrive about 1.5 us later; issued first and waited for, they
-//      arrive early and the weight stream finishes no later;
+//      token) and the scale of the channel it writes in the epilogue; once
+//      every X request of the block has been issued, the weight waves issue
+//      ALL of their weight loads (directly in the B-operand layout of
+//      v_mfma_i32_16x16x64_i8, 16 bytes per lane and step).  Issued behind
+//      the weight requests, the X requests (hits on lines every workgroup
+//      reads) queue behind weight misses in the caches and arrive about
+//      1.5 us later; issued first, they keep their place ahead of the weight
+//      stream, and the stream need not wait for them to arrive;
 //   2. while the weight bytes are in flight, recomputes -- identically in every
 //      workgroup -- the outlier columns (column max over the tokens on the
 //      sign-cleared fp16 bit patterns, compared as integers with a threshold
@@ -207,9 +208,9 @@ __global__ __launch_bounds__(2 * DEC_THREADS) void k_decode_mixed(const uint16_t
 #pragma unroll
             for (int m = 0; m < MB; ++m) xv[c][m] = bload16(rsx, ch < nch ? (uint32_t)(m * K + 8 * ch) * 2 : kOOB);
         }
-        // the weight waves issue their stream once every activation wave holds its X
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // the weight waves issue their stream once every X request is issued
         lds_barrier();                                                  // barrier 1
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
         // 2a. column max over the tokens on |x| bit patterns (fp16 magnitudes
         //     order like their bits); column j is an outlier when that max is
@@ -361,7 +362,7 @@ __global__ __launch_bounds__(2 * DEC_THREADS) void k_decode_mixed(const uint16_t
     } else {
         // ---------------------------------------------------------------- weight waves
         const int ww = wave - DEC_WAVES;
-        lds_barrier();                                                  // barrier 1: X is in
+        lds_barrier();                                                  // barrier 1: X requests issued
         // the weight slice: row n0 + lane % 16, bytes 64 s + 16 (lane / 16) of step s = ww + 8 j
         v4i wv[STEPS];
         {
