@@ -591,7 +591,7 @@ __global__ __launch_bounds__(256) void k_rowquant_i8(const uint16_t* __restrict_
                 } else {
                     c = clip_codes(codes8_dyn_h(v[i], s, r), qmin);
                 }
-                *reinterpret_cast<u32x2*>(qr + ch * 8) = c;
+                st_codes8(qr + ch * 8, c);
             }
         }
         if constexpr (MASK == MASK_FLAGS) {
@@ -652,7 +652,7 @@ __global__ __launch_bounds__(256) void k_rowquant_i8(const uint16_t* __restrict_
                 if constexpr (MASK == MASK_BYTES) apply_mask(x, mk);
                 c = clip_codes(codes8_dyn(x, s, r), qmin);
             }
-            *reinterpret_cast<u32x2*>(qr + ch * 8) = c;
+            st_codes8(qr + ch * 8, c);
         }
     }
 }
@@ -798,14 +798,14 @@ __global__ __launch_bounds__(256) void k_rowquant_i8_asym(const uint16_t* __rest
             if (ch < nch) {
                 float x[8];
                 unpack8(v[i], x);
-                *reinterpret_cast<u32x2*>(qr + ch * 8) = codes8_asym(x, s, r, z, qmin, qmax, sum);
+                st_codes8(qr + ch * 8, codes8_asym(x, s, r, z, qmin, qmax, sum));
             }
         }
     } else {
         for (int64_t ch = lane; ch < nch; ch += 64) {
             float x[8];
             unpack8(bload16(rx, (uint32_t)ch * 16), x);
-            *reinterpret_cast<u32x2*>(qr + ch * 8) = codes8_asym(x, s, r, z, qmin, qmax, sum);
+            st_codes8(qr + ch * 8, codes8_asym(x, s, r, z, qmin, qmax, sum));
         }
     }
     sum = wave_sum_i32(sum);

@@ -118,7 +118,7 @@ __global__ __launch_bounds__(256) void k_smoothquant_i8(const uint16_t* __restri
 #pragma unroll
             for (int i = 0; i < NC; ++i) {
                 const int64_t ch = lane + 64 * i;
-                if (ch < nch) *reinterpret_cast<u32x2*>(qr + ch * 8) = codes8_dyn(x[i], s, r);
+                if (ch < nch) st_codes8(qr + ch * 8, codes8_dyn(x[i], s, r));
             }
         }
     } else {
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256) void k_smoothquant_i8(const uint16_t* __restri
             for (int64_t ch = lane; ch < nch; ch += 64) {
                 float x[8];
                 load_smooth(ch, x);
-                *reinterpret_cast<u32x2*>(qr + ch * 8) = codes8_dyn(x, s, r);
+                st_codes8(qr + ch * 8, codes8_dyn(x, s, r));
             }
         }
     }

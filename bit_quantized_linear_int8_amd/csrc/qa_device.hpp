@@ -62,6 +62,14 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
 }
 
+// Store of 8 code bytes per lane where a wave instruction covers whole
+// 128-byte lines (consecutive lanes, consecutive 8-byte pieces): the
+// non-temporal hint streams them to memory during the kernel instead of
+// leaving them dirty in L2 for the write-back at its end.
+__device__ __forceinline__ void st_codes8(int8_t* p, u32x2 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
+}
+
 __device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
