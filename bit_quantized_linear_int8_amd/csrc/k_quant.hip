@@ -930,15 +930,38 @@ __device__ __forceinline__ RowParams row_params(float amax, float lo, float hi, 
 // below at qmin: HQ_I8, eight int8 codes at out + 8 ch; otherwise eight int4
 // codes packed into the word out[ch], element j in bits [4j+3:4j].
 template <int MODE>
-__device__ __forceinline__ void store_codes(void* out, int64_t ch, const float* x, const RowParams& p, int qmin) {
-    if constexpr (MODE == HQ_I8) {
-        reinterpret_cast<u32x2*>(out)[ch] = clip_codes(codes8_dyn(x, p.s, p.r), qmin);
-    } else if constexpr (MODE == HQ_I4Z) {
+__device__ __forceinline__ uint32_t code_word(const float* x, const RowParams& p, int qmin) {
+    if constexpr (MODE == HQ_I4Z) {
         int unused = 0;
         const u32x2 q = codes8_asym(x, p.s, p.r, p.z, 0, 15, unused);
-        reinterpret_cast<uint32_t*>(out)[ch] = pack_nibbles(u32x2{q[0] ^ 0x08080808u, q[1] ^ 0x08080808u});
+        return pack_nibbles(u32x2{q[0] ^ 0x08080808u, q[1] ^ 0x08080808u});
     } else {
-        reinterpret_cast<uint32_t*>(out)[ch] = pack_codes(x, p.s, p.r, qmin);
+        return pack_codes(x, p.s, p.r, qmin);
+    }
+}
+
+template <int MODE>
+__device__ __forceinline__ void store_codes(void* out, int64_t ch, const float* x, const RowParams& p, int qmin) {
+    if constexpr (MODE == HQ_I8)
+        reinterpret_cast<u32x2*>(out)[ch] = clip_codes(codes8_dyn(x, p.s, p.r), qmin);
+    else
+        reinterpret_cast<uint32_t*>(out)[ch] = code_word<MODE>(x, p, qmin);
+}
+
+// 4 x 4 transpose inside each quad of lanes: on return lane 4b + j holds in
+// w[k] what lane 4b + k held in w[j] (two exchange steps, lane bit 0 with
+// register bit 0, then lane bit 1 with register bit 1; DPP quad moves).
+__device__ __forceinline__ void quad_transpose(uint32_t* w, int lane) {
+    uint32_t a[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w[r ^ 1], 0xB1, 0xF, 0xF, false);
+        a[r] = ((lane ^ r) & 1) ? o : w[r];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a[r ^ 2], 0x4E, 0xF, 0xF, false);
+        w[r] = ((lane ^ r) & 2) ? o : a[r];
     }
 }
 
@@ -1114,8 +1137,25 @@ __global__ __launch_bounds__(256) void k_hq4_row_reg(const uint16_t* __restrict_
         s_out[row] = p.s;
         if (MODE == HQ_I4Z) z_out[row] = p.z;
     }
+    if constexpr (MODE != HQ_I8 && NC == 4 && (LPB == 4 || LPB == 1)) {
+        // four packed words per lane, made contiguous (with LPB == 4 the quad
+        // transpose gives lane 4b + j the chunks 16b + 4j .. 16b + 4j + 3), so
+        // a wave stores 1 KB of whole lines, streamed out like the int8 codes
+        uint32_t w[4];
 #pragma unroll
-    for (int i = 0; i < NC; ++i) store_codes<MODE>(codes, ch0 + chunk(i), xs[i], p, qmin);
+        for (int i = 0; i < 4; ++i) w[i] = code_word<MODE>(xs[i], p, qmin);
+        if constexpr (LPB == 4) quad_transpose(w, lane);
+        uint32_t* pw = static_cast<uint32_t*>(codes) + ch0 + (LPB == 4 ? (lane >> 2) * 16 + (lane & 3) * 4 : lane * 4);
+        if ((reinterpret_cast<uintptr_t>(codes) & 15u) == 0) {
+            __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, reinterpret_cast<u32x4*>(pw));
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) pw[k] = w[k];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NC; ++i) store_codes<MODE>(codes, ch0 + chunk(i), xs[i], p, qmin);
+    }
 }
 
 // Per-group scale (G >= 8): the G/8 lanes of a block reduce their absmax.
