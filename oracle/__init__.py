@@ -87,6 +87,7 @@ def lib() -> ctypes.CDLL:
             "orc_qlinear_w4a8": (None, [P, I64, I64, P, P, I64, I32, P, I64, P]),
             "orc_hadamard_quant_int4_asym": (None, [P, I64, I64, I32, P, P, P]),
             "orc_qlinear_w4a4_asym": (None, [P, I64, I64, P, P, I64, I32, P, I64, P]),
+            "orc_w4_column_terms": (None, [P, P, I64, I64, I32, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -513,6 +514,16 @@ def hadamard_quant_int4_asym(X16, G: int):
     z = np.zeros(rows, np.int32)
     lib().orc_hadamard_quant_int4_asym(_ptr(h), rows, K, int(G), _ptr(packed), _ptr(s), _ptr(z))
     return packed, s, z
+
+
+def w4_column_terms(Wp, s_w, K: int, G: int):
+    """c[n] = fl32(sum_g s_w[n][g] * sum_{k in g} qw[n][k]) (zero-point term, per output column)."""
+    Wp = _c(Wp, np.uint32)
+    N = Wp.shape[0]
+    sw = _c(s_w, np.float32)
+    c = np.zeros(N, np.float32)
+    lib().orc_w4_column_terms(_ptr(Wp), _ptr(sw), N, int(K), int(G), _ptr(c))
+    return c
 
 
 def qlinear_w4a4_asym(X16, Wp, s_w, G: int, rows=None):

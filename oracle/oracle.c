@@ -933,6 +933,31 @@ void orc_hadamard_quant_int4_asym(const uint16_t* X, int64_t rows, int64_t K, in
     free(xr);
 }
 
+/* Column term of the zero-point linear  [Scholia-IQ §6: dequantization
+ * s (q - z), so sum_k (q - z) w splits into sum_k q w - z sum_k w;
+ * GroupRot §5.4: per-group weight scales]
+ *   c[n] = fl32( sum_g s_w[n][g] * sum_{k in g} qw[n][k] )
+ * the group sums exact (int64), the sum over the groups in fp64 with g
+ * ascending, rounded once to fp32.
+ * ------------------------------------------------------------------------- */
+void orc_w4_column_terms(const uint32_t* Wp, const float* s_w, int64_t N, int64_t K, int32_t G, float* c)
+{
+    int64_t ng = K / G;
+    int8_t* wq = (int8_t*)malloc((size_t)(N * K > 0 ? N * K : 1));
+    orc_unpack_int4(Wp, N, K, wq);
+    for (int64_t n = 0; n < N; ++n) {
+        double sum = 0.0;
+        for (int64_t g = 0; g < ng; ++g) {
+            int64_t a = 0;
+            for (int64_t k = g * G; k < (g + 1) * G; ++k)
+                a += (int64_t)wq[n * K + k];
+            sum += (double)s_w[n * ng + g] * (double)a;
+        }
+        c[n] = (float)sum;
+    }
+    free(wq);
+}
+
 void orc_qlinear_w4a4_asym(const uint16_t* X, int64_t M, int64_t K, const uint32_t* Wp,
                            const float* s_w, int64_t N, int32_t G, const int64_t* rows,
                            int64_t nrows, double* out)

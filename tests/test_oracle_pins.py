@@ -555,6 +555,44 @@ def test_w4a4_asym_linear_is_the_dequantized_product_and_bounded():
     assert np.array_equal(oracle.qlinear_w4a4_asym(X, Wp, s_w, G, rows=rows), out[rows])
 
 
+def test_w4_column_terms_hand_example_and_closed_forms():
+    # one column, K = 16, G = 8: nibbles 1..8 (8 reads as -8) in group 0, all -1 in group 1
+    q = np.array([[1, 2, 3, 4, 5, 6, 7, -8, -1, -1, -1, -1, -1, -1, -1, -1]], np.int8)
+    Wp = oracle.pack_int4(q)
+    c = oracle.w4_column_terms(Wp, np.array([[0.5, 0.25]], np.float32), 16, 8)
+    assert c[0] == np.float32(0.5 * 20 + 0.25 * -8)              # 8.0
+    # one group: a single product, rounded once
+    rng = np.random.default_rng(36)
+    q = rng.integers(-8, 8, (5, 64)).astype(np.int8)
+    s = rng.uniform(0.001, 0.1, (5, 1)).astype(np.float32)
+    c = oracle.w4_column_terms(oracle.pack_int4(q), s, 64, 64)
+    assert np.array_equal(c, (s[:, 0].astype(np.float64) * q.astype(np.int64).sum(axis=1)).astype(np.float32))
+    # an all-zero weight
+    assert not oracle.w4_column_terms(oracle.pack_int4(np.zeros((3, 32), np.int8)),
+                                      np.ones((3, 4), np.float32), 32, 8).any()
+
+
+def test_w4_column_terms_split_the_zero_point_linear():
+    # the zero-point linear (pinned above to the dequantized product) is the
+    # symmetric group products of the stored codes q - 8 minus (z - 8) times
+    # the column term; only c's rounding to fp32 separates the two
+    M, K, N, G = 6, 512, 14, 128
+    X, W, _ = synthetic.w4a4_inputs(M, K, N, seed=35)
+    X = np.abs(X)
+    Wp, s_w = oracle.hadamard_quant_int4(W, G, per_group=True)
+    c = oracle.w4_column_terms(Wp, s_w, K, G).astype(np.float64)
+    p, s_x, z_x = oracle.hadamard_quant_int4_asym(X, G)
+    acc = oracle.w4a4_group_acc(p, Wp, K, G).astype(np.float64)      # sum_{k in g} (q - 8) qw
+    sym = (acc * s_w.astype(np.float64)[None, :, :]).sum(axis=2)
+    sx = s_x.astype(np.float64)[:, None]
+    zm = (z_x.astype(np.float64) - 8)[:, None]
+    split = sx * (sym - zm * c[None, :])
+    out = oracle.qlinear_w4a4_asym(X, Wp, s_w, G)
+    mag = sx * ((np.abs(acc) * s_w.astype(np.float64)[None, :, :]).sum(axis=2) + np.abs(zm * c[None, :]))
+    assert np.all(np.abs(out - split) <= sx * np.abs(zm) * np.abs(c)[None, :] * 2.0 ** -23 + 1e-12 * mag)
+    assert np.any(zm != 0)
+
+
 @pytest.mark.parametrize("seed", [33, 34])
 def test_w4a4_asym_lowers_the_error_of_one_sided_activations(seed):
     # the point of the zero-point: one-sided rows (after the rotation their

@@ -76,11 +76,7 @@ def test_w4_column_terms(qa, N, K, G):
     Wp = rng.integers(0, 2 ** 32, (N, K // 8), dtype=np.uint64).astype(np.uint32)
     s_w = rng.uniform(0.001, 0.1, (N, K // G)).astype(np.float32)
     c = host(qa.qa_w4_column_terms(dev(Wp.view(np.int32)), dev(s_w), K, G))
-    q = oracle.unpack_int4(Wp, K).astype(np.int64).reshape(N, K // G, G).sum(axis=2)
-    ref = np.zeros(N, np.float64)
-    for g in range(K // G):                               # the same fp64 sum, g ascending
-        ref = ref + s_w[:, g].astype(np.float64) * q[:, g]
-    assert np.array_equal(c, ref.astype(np.float32))
+    assert np.array_equal(c, oracle.w4_column_terms(Wp, s_w, K, G))
 
 
 # ============================================================ linear
