@@ -1137,7 +1137,26 @@ __global__ __launch_bounds__(256) void k_hq4_row_reg(const uint16_t* __restrict_
         s_out[row] = p.s;
         if (MODE == HQ_I4Z) z_out[row] = p.z;
     }
-    if constexpr (MODE != HQ_I8 && NC == 4 && (LPB == 4 || LPB == 1)) {
+    if constexpr (MODE == HQ_I8 && NC == 4) {
+        // eight int8 codes per chunk: the wave's 256 chunks (2 KB) go through
+        // LDS so that each of its two stores covers 1 KB of whole lines
+        __shared__ u32x2 stg[4][64 * NC];
+#pragma unroll
+        for (int i = 0; i < NC; ++i) stg[wave][chunk(i)] = clip_codes(codes8_dyn(xs[i], p.s, p.r), qmin);
+        __builtin_amdgcn_wave_barrier();
+        const u32x4* sv = reinterpret_cast<const u32x4*>(stg[wave]);
+        const u32x4 a = sv[lane], b = sv[64 + lane];                  // chunks 2l, 2l + 1 and 128 + 2l, 129 + 2l
+        u32x2* pw = static_cast<u32x2*>(codes) + ch0;
+        if ((reinterpret_cast<uintptr_t>(codes) & 15u) == 0) {
+            __builtin_nontemporal_store(a, reinterpret_cast<u32x4*>(pw + 2 * lane));
+            __builtin_nontemporal_store(b, reinterpret_cast<u32x4*>(pw + 128 + 2 * lane));
+        } else {
+            pw[2 * lane] = u32x2{a[0], a[1]};
+            pw[2 * lane + 1] = u32x2{a[2], a[3]};
+            pw[128 + 2 * lane] = u32x2{b[0], b[1]};
+            pw[129 + 2 * lane] = u32x2{b[2], b[3]};
+        }
+    } else if constexpr (MODE != HQ_I8 && NC == 4 && (LPB == 4 || LPB == 1)) {
         // four packed words per lane, made contiguous (with LPB == 4 the quad
         // transpose gives lane 4b + j the chunks 16b + 4j .. 16b + 4j + 3), so
         // a wave stores 1 KB of whole lines, streamed out like the int8 codes
