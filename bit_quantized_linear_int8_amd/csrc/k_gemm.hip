@@ -798,9 +798,155 @@ static int wide_stride(int64_t M, int64_t N) {
     return tsn <= CfgWide::BN ? (int)tsn : 0;
 }
 
+// ---------------------------------------------------------------------------
+// Decode-size (M <= 16) int8 GEMM with the mixed epilogue: the weight stream
+// of the fused decode kernel, fed with codes that a quantizer already made.
+// 16 output channels per 512-thread workgroup; wave w multiplies the 64-byte
+// K steps w, w + 8, ..., each weight load covering 16 rows x 512 contiguous
+// bytes, the token codes loaded the same way (from L2: every workgroup reads
+// them).  Batches of GV_BATCH steps per wave, two in flight; the MFMAs are
+// unconditional (steps past K, tokens past M and channels past N load zeros).
+// The eight partial tiles are summed in LDS; threads t < 256 (token t / 16,
+// channel t % 16) dequantize by s_x[m] s_w[n] and add the fp16 outlier
+// product, staged GV_OC columns at a time with all gathers in flight, summed
+// in list order.
+// ---------------------------------------------------------------------------
+constexpr int GV_WAVES = 8, GV_THREADS = 64 * GV_WAVES, GV_BATCH = 8, GV_OC = 128;
+
+__global__ __launch_bounds__(GV_THREADS) void k_gemv_i8_mixed(const int8_t* __restrict__ Xq,
+                                                              const int8_t* __restrict__ Wq, int M, int64_t K,
+                                                              int64_t N, MixedEpilogue ep) {
+    __shared__ int red[GV_WAVES][256];
+    __shared__ float xo_s[GV_OC][16], wo_s[GV_OC][16];
+    const int lane = threadIdx.x & 63, wave = wave_id(), t = threadIdx.x;
+    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    const int S = (int)((K + 63) >> 6);                           // 64-byte K steps (the last one may be partial)
+    const rsrc_t rsw = make_rsrc(Wq + n0 * K, (N - n0) * K);      // channels past N read zeros
+    const rsrc_t rsa = make_rsrc(Xq, (int64_t)M * K);             // tokens past M read zeros
+    const uint32_t kl = 16u * (uint32_t)(lane >> 4);              // this lane's 16 bytes of a step
+    const uint32_t o0 = (uint32_t)(lane & 15) * (uint32_t)K + kl;
+    const int nb = (S + GV_WAVES * GV_BATCH - 1) / (GV_WAVES * GV_BATCH);
+    v4i wa[GV_BATCH], aa[GV_BATCH], wb[GV_BATCH], ab[GV_BATCH];
+    auto issue = [&](int b, v4i (&w)[GV_BATCH], v4i (&a)[GV_BATCH]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < GV_BATCH; ++j) {
+            const int s = wave + GV_WAVES * (b * GV_BATCH + j);
+            const bool ok = s < S && 64u * (uint32_t)s + kl < (uint32_t)K;
+            w[j] = __builtin_bit_cast(v4i, bload16(rsw, ok ? o0 + 64u * (uint32_t)s : kOOB));
+            a[j] = __builtin_bit_cast(v4i, bload16(rsa, ok ? o0 + 64u * (uint32_t)s : kOOB));
+        }
+    };
+    auto mult = [&](const v4i (&w)[GV_BATCH], const v4i (&a)[GV_BATCH], v4i& acc) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < GV_BATCH; ++j) acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[j], w[j], acc, 0, 0, 0);
+    };
+    // No branches around the loads or the MFMAs: a batch past the end loads
+    // zeros (and its MFMAs add nothing), so the compiler keeps every load of
+    // a batch ahead of the previous batch's MFMAs and waits for exact counts.
+    v4i acc = v4i{0, 0, 0, 0};
+    issue(0, wa, aa);
+    for (int b = 0; b < nb; b += 2) {
+        issue(b + 1, wb, ab);
+        __builtin_amdgcn_sched_barrier(0);          // the next batch's loads go out before these MFMAs wait
+        mult(wa, aa, acc);
+        issue(b + 2, wa, aa);
+        __builtin_amdgcn_sched_barrier(0);
+        mult(wb, ab, acc);
+    }
+    // acc: lane l, element e = token 4 (l / 16) + e, channel l % 16
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[wave][(4 * (lane >> 4) + e) * 16 + (lane & 15)] = acc[e];
+
+    const int cnt = (int)bload4(make_rsrc(ep.count, 4), 0);
+    const int m = t >> 4, ch = t & 15;
+    const int64_t n = n0 + ch;
+    float v = 0.0f;
+    __syncthreads();
+    if (t < 256) {
+        int32_t c = 0;
+#pragma unroll
+        for (int w = 0; w < GV_WAVES; ++w) c += red[w][t];
+        const float sx = m < M ? ep.s_x[m] : 0.0f;
+        const float sw = n < N ? ep.s_w[n] : 0.0f;
+        v = (float)c * sx * sw;
+    }
+    const rsrc_t rsx = make_rsrc(ep.X, (int64_t)M * K * 2);
+    const rsrc_t rsn = make_rsrc(ep.s_w + n0, (N - n0) * 4);
+    const rsrc_t rwo = ep.W16 ? make_rsrc(ep.W16 + n0 * K, (N - n0) * K * 2) : make_rsrc(ep.Wq + n0 * K, (N - n0) * K);
+    // outlier columns GV_OC at a time: waves 0-3 gather the tokens' values
+    // X[r][k], waves 4-7 the channels' w~[n0 + r][k] (16 rows x GV_OC columns
+    // each, pair q of a wave group = column q / 16, row q % 16), all loads of
+    // a pass in flight before any is written
+    constexpr int PP = GV_OC * 16 / (GV_THREADS / 2);              // pairs per thread
+    const int tt = t & (GV_THREADS / 2 - 1);
+    for (int hs = 0; hs < cnt; hs += GV_OC) {
+        const int hn = cnt - hs < GV_OC ? cnt - hs : GV_OC;
+        const rsrc_t ridx = make_rsrc(ep.idx + hs, (int64_t)hn * 4);
+        uint32_t kk[PP], g[PP];
+#pragma unroll
+        for (int u = 0; u < PP; ++u) {
+            const int h = (tt + u * (GV_THREADS / 2)) >> 4;
+            kk[u] = bload4(ridx, h < hn ? (uint32_t)h * 4 : kOOB);
+        }
+        if (wave < GV_WAVES / 2) {
+#pragma unroll
+            for (int u = 0; u < PP; ++u) {
+                const int q = tt + u * (GV_THREADS / 2), h = q >> 4, r = q & 15;
+                g[u] = bload2(rsx, h < hn && r < M ? ((uint32_t)r * (uint32_t)K + kk[u]) * 2 : kOOB);
+            }
+#pragma unroll
+            for (int u = 0; u < PP; ++u) {
+                const int q = tt + u * (GV_THREADS / 2);
+                xo_s[q >> 4][q & 15] = h2f((uint16_t)g[u]);
+            }
+        } else if (ep.W16) {
+#pragma unroll
+            for (int u = 0; u < PP; ++u) {
+                const int q = tt + u * (GV_THREADS / 2), h = q >> 4, r = q & 15;
+                g[u] = bload2(rwo, h < hn ? ((uint32_t)r * (uint32_t)K + kk[u]) * 2 : kOOB);
+            }
+#pragma unroll
+            for (int u = 0; u < PP; ++u) {
+                const int q = tt + u * (GV_THREADS / 2);
+                wo_s[q >> 4][q & 15] = h2f((uint16_t)g[u]);
+            }
+        } else {
+            const float swr = __builtin_bit_cast(float, bload4(rsn, (uint32_t)(tt & 15) * 4));   // row tt % 16
+#pragma unroll
+            for (int u = 0; u < PP; ++u) {
+                const int q = tt + u * (GV_THREADS / 2), h = q >> 4, r = q & 15;
+                g[u] = bload1(rwo, h < hn ? (uint32_t)r * (uint32_t)K + kk[u] : kOOB);
+            }
+#pragma unroll
+            for (int u = 0; u < PP; ++u) {
+                const int q = tt + u * (GV_THREADS / 2);
+                wo_s[q >> 4][q & 15] = h2f(f2h(swr * (float)(int8_t)(uint8_t)g[u]));
+            }
+        }
+        __syncthreads();
+        if (t < 256)
+            for (int h = 0; h < hn; ++h) v = v + xo_s[h][m] * wo_s[h][ch];
+        __syncthreads();
+    }
+    if (t < 256 && m < M && n < N) {
+        const int64_t o = (int64_t)m * ep.ldo + n;
+        if (ep.out_dtype == 0)
+            static_cast<float*>(ep.out)[o] = v;
+        else if (ep.out_dtype == 1)
+            static_cast<uint16_t*>(ep.out)[o] = f2h(v);
+        else
+            static_cast<uint16_t*>(ep.out)[o] = f2bf(v);
+    }
+}
+
 hipError_t launch_gemm_i8_mixed(const int8_t* Xq, const int8_t* Wq, int64_t M, int64_t K, int64_t N,
                                 const MixedEpilogue& ep, hipStream_t st) {
     int tm, tn;
+    if (M <= 16) {
+        hipLaunchKernelGGL(k_gemv_i8_mixed, dim3((unsigned)((N + 15) / 16)), dim3(GV_THREADS), 0, st, Xq, Wq, (int)M,
+                           K, N, ep);
+        return hipGetLastError();
+    }
     if (pick_cfg(M, N) == 2) {
         if (const int tsn = wide_stride(M, N)) {
             tm = (int)((M + 255) / 256);

@@ -267,6 +267,21 @@ def test_mixed_outlier_staging_paths(qa, M, K, N, n_dims, pass_w16):
     _mixed_case(qa, X, W, 6.0, 1, pass_w16)
 
 
+@pytest.mark.parametrize("M,K,N,n_dims,pass_w16,out_dtype", [
+    (8, 8208, 100, 20, True, 1),     # K % 64 = 16: a partial last K step; three batches of steps (odd)
+    (16, 12288, 33, 6, False, 0),    # K past the fused decode kernel: three batches, 16 tokens, ragged N
+    (3, 1040, 300, 150, False, 1),   # more outlier columns than one staging pass (128)
+    (13, 2064, 70, 300, True, 2),    # three staging passes, bf16 out
+    (1, 8192, 17, 0, False, 1),      # no outlier columns, one token
+])
+def test_mixed_gemv_shapes(qa, M, K, N, n_dims, pass_w16, out_dtype):
+    # decode-size calls (M <= 16) that the fused decode kernel does not take
+    # run the int8 GEMM as a weight-streaming GEMV
+    X, W, _ = synthetic.mixed_inputs(M, K, N, seed=M * 5 + K + n_dims, n_dims=n_dims, p_token=0.8,
+                                     magnitude=("uniform", 6.5, 60.0))
+    _mixed_case(qa, X, W, 6.0, out_dtype, pass_w16)
+
+
 @pytest.mark.parametrize("M,K,N", [(1, 256, 1), (3, 512, 17), (4, 768, 40), (7, 1024, 33), (8, 4096, 64),
                                    (9, 2048, 48), (12, 256, 100), (16, 4096, 20),
                                    # K above 4096 (M <= 8): two 8-column chunks per thread
