@@ -806,23 +806,102 @@ static int wide_stride(int64_t M, int64_t N) {
 // bytes, the token codes loaded the same way (from L2: every workgroup reads
 // them).  Batches of GV_BATCH steps per wave, two in flight; the MFMAs are
 // unconditional (steps past K, tokens past M and channels past N load zeros).
-// The eight partial tiles are summed in LDS; threads t < 256 (token t / 16,
-// channel t % 16) dequantize by s_x[m] s_w[n] and add the fp16 outlier
-// product, staged GV_OC columns at a time with all gathers in flight, summed
-// in list order.
+// Everything the epilogue reads that does not depend on the products -- the
+// outlier count, the scales and the first GV_OC outlier columns of X and w~
+// -- is requested before the weight stream, so only the partial-tile sum,
+// the dequantization and the outlier FMAs remain after it.  Threads t < 256
+// (token t / 16, channel t % 16) dequantize by s_x[m] s_w[n] and add the
+// fp16 outlier product, summed in list order.
 // ---------------------------------------------------------------------------
 constexpr int GV_WAVES = 8, GV_THREADS = 64 * GV_WAVES, GV_BATCH = 8, GV_OC = 128;
+constexpr int GV_PP = GV_OC * 16 / (GV_THREADS / 2);              // gathered pairs per thread and pass
+constexpr int GV_ALDS = 65536;                                    // codes staged in LDS up to M K bytes
 
+// ALDS: the codes (M K <= GV_ALDS, K % 1024 == 0, K <= 8192, so at most two
+// batches per wave) come into LDS once per
+// workgroup by LDS-DMA, rows padded by 16 bytes (the 16 token rows of a
+// fragment read hit distinct banks), instead of every wave loading its own
+// fragments: that halves the requests in flight beside the weight stream.
+template <bool ALDS>
 __global__ __launch_bounds__(GV_THREADS) void k_gemv_i8_mixed(const int8_t* __restrict__ Xq,
                                                               const int8_t* __restrict__ Wq, int M, int64_t K,
                                                               int64_t N, MixedEpilogue ep) {
     __shared__ int red[GV_WAVES][256];
     __shared__ float xo_s[GV_OC][16], wo_s[GV_OC][16];
+    __shared__ __attribute__((aligned(16))) uint8_t aq[ALDS ? GV_ALDS + 16 * 16 : 1];
+    const int lda = (int)K + 16;
     const int lane = threadIdx.x & 63, wave = wave_id(), t = threadIdx.x;
     const int64_t n0 = (int64_t)blockIdx.x * 16;
+    const int m = t >> 4, ch = t & 15;                            // the epilogue's token and channel (t < 256)
+    const int64_t n = n0 + ch;
+    const rsrc_t rsa = make_rsrc(Xq, (int64_t)M * K);             // tokens past M read zeros
+    if constexpr (ALDS) {
+        // chunk q = 1 KB of row q / (K / 1024): one DMA instruction, 16 bytes per lane
+        const int cpr = (int)(K >> 10), tc = M * cpr;
+#pragma unroll
+        for (int j = 0; j < GV_ALDS / 1024 / GV_WAVES; ++j) {
+            const int q = wave + GV_WAVES * j;
+            if (q < tc) {
+                const int r = q / cpr, c = q - r * cpr;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)(aq + r * lda + 1024 * c), 16,
+                                                         (uint32_t)(r * K + 1024 * c + 16 * lane), 0, 0, 0);
+            }
+        }
+    }
+
+    // the epilogue's inputs: the first pass's column list (requested first,
+    // so that waiting for it does not wait for the weights), the count and
+    // the scales, then, behind the first weight batch, the first pass of
+    // outlier operands -- waves 0-3 gather X[r][k] (2 bytes), waves 4-7 the
+    // source of w~, W16[n0 + r][k] (2 bytes) or Wq[n0 + r][k] (1 byte); pair q
+    // of a wave group is column q / 16, row q % 16; each element is read as
+    // the aligned word holding it
+    const int tt = t & (GV_THREADS / 2 - 1), gr = tt & 15;        // this thread's gathered row
+    uint32_t kk[GV_PP], graw[GV_PP], gsh[GV_PP];
+    // the column list of a pass, read without the count (the list buffer
+    // holds K entries; entries past the count are never used)
+    auto load_idx = [&](int hs) __attribute__((always_inline)) {
+        const rsrc_t ridx = make_rsrc(ep.idx ? ep.idx + hs : nullptr, ep.idx ? (K - hs) * 4 : 0);
+#pragma unroll
+        for (int u = 0; u < GV_PP; ++u) kk[u] = bload4(ridx, (uint32_t)((tt + u * (GV_THREADS / 2)) >> 4) * 4);
+    };
+    load_idx(0);
+    const int cntv = (int)bload4(make_rsrc(ep.count, 4), 0);    // made uniform after the products
+    const float sx = __builtin_bit_cast(float, bload4(make_rsrc(ep.s_x, (int64_t)M * 4), t < 256 ? (uint32_t)m * 4 : kOOB));
+    const rsrc_t rsn = make_rsrc(ep.s_w + n0, (N - n0) * 4);
+    const float sw = __builtin_bit_cast(float, bload4(rsn, (uint32_t)ch * 4));
+    const bool xw = wave < GV_WAVES / 2;                          // this wave gathers X (else the weight)
+    const rsrc_t rsx = make_rsrc(ep.X, (int64_t)M * K * 2);
+    const rsrc_t rwo = ep.W16 ? make_rsrc(ep.W16 + n0 * K, (N - n0) * K * 2) : make_rsrc(ep.Wq + n0 * K, (N - n0) * K);
+    const rsrc_t rg = xw ? rsx : rwo;                             // wave-uniform
+    const uint32_t esz = xw || ep.W16 ? 2u : 1u;
+    const bool rok = !xw || gr < M;
+    const float swr = __builtin_bit_cast(float, bload4(rsn, (uint32_t)gr * 4));   // scale of weight row gr
+    auto gather = [&](int hs, int cnt) __attribute__((always_inline)) {
+        const int hn = cnt - hs < GV_OC ? cnt - hs : GV_OC;
+#pragma unroll
+        for (int u = 0; u < GV_PP; ++u) {
+            const int h = (tt + u * (GV_THREADS / 2)) >> 4;
+            const uint32_t o = ((uint32_t)gr * (uint32_t)K + kk[u]) * esz;         // byte offset of the element
+            graw[u] = bload4(rg, h < hn && rok ? (o & ~3u) : kOOB);
+            gsh[u] = (o & 3u) * 8;
+        }
+    };
+    auto stage = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < GV_PP; ++u) {
+            const int h = (tt + u * (GV_THREADS / 2)) >> 4;
+            const uint32_t v = graw[u] >> gsh[u];
+            if (xw)
+                xo_s[h][gr] = h2f((uint16_t)v);
+            else
+                wo_s[h][gr] = ep.W16 ? h2f((uint16_t)v) : h2f(f2h(swr * (float)(int8_t)(uint8_t)v));
+        }
+    };
+
+    // the int32 products
     const int S = (int)((K + 63) >> 6);                           // 64-byte K steps (the last one may be partial)
     const rsrc_t rsw = make_rsrc(Wq + n0 * K, (N - n0) * K);      // channels past N read zeros
-    const rsrc_t rsa = make_rsrc(Xq, (int64_t)M * K);             // tokens past M read zeros
     const uint32_t kl = 16u * (uint32_t)(lane >> 4);              // this lane's 16 bytes of a step
     const uint32_t o0 = (uint32_t)(lane & 15) * (uint32_t)K + kl;
     const int nb = (S + GV_WAVES * GV_BATCH - 1) / (GV_WAVES * GV_BATCH);
@@ -833,7 +912,19 @@ __global__ __launch_bounds__(GV_THREADS) void k_gemv_i8_mixed(const int8_t* __re
             const int s = wave + GV_WAVES * (b * GV_BATCH + j);
             const bool ok = s < S && 64u * (uint32_t)s + kl < (uint32_t)K;
             w[j] = __builtin_bit_cast(v4i, bload16(rsw, ok ? o0 + 64u * (uint32_t)s : kOOB));
-            a[j] = __builtin_bit_cast(v4i, bload16(rsa, ok ? o0 + 64u * (uint32_t)s : kOOB));
+            if constexpr (!ALDS) a[j] = __builtin_bit_cast(v4i, bload16(rsa, ok ? o0 + 64u * (uint32_t)s : kOOB));
+        }
+    };
+    // ALDS: this wave's fragments of batch b from the staged codes (rows past
+    // M repeat row M - 1: their products land in tokens that are not stored;
+    // steps past K meet all-zero weight fragments)
+    const int arow = (lane & 15) < M ? (lane & 15) : M - 1;
+    auto afrag = [&](int b, v4i (&a)[GV_BATCH]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < GV_BATCH; ++j) {
+            const int s = wave + GV_WAVES * (b * GV_BATCH + j);
+            const int off = arow * lda + 64 * (s < S ? s : 0) + (int)kl;
+            a[j] = *reinterpret_cast<const v4i*>(aq + off);
         }
     };
     auto mult = [&](const v4i (&w)[GV_BATCH], const v4i (&a)[GV_BATCH], v4i& acc) __attribute__((always_inline)) {
@@ -845,88 +936,59 @@ __global__ __launch_bounds__(GV_THREADS) void k_gemv_i8_mixed(const int8_t* __re
     // a batch ahead of the previous batch's MFMAs and waits for exact counts.
     v4i acc = v4i{0, 0, 0, 0};
     issue(0, wa, aa);
-    for (int b = 0; b < nb; b += 2) {
-        issue(b + 1, wb, ab);
-        __builtin_amdgcn_sched_barrier(0);          // the next batch's loads go out before these MFMAs wait
+    __builtin_amdgcn_sched_barrier(0);              // the first weight batch goes out before any wait
+    // the first pass's gathers wait only for the list and the count
+    // (requested before the weight loads), not for the weights
+    gather(0, cntv);
+    if constexpr (ALDS) {
+        // nb <= 2 here: both batches in flight, then one wait (this barrier
+        // also makes every wave's codes visible)
+        if (nb > 1) issue(1, wb, ab);
+        __syncthreads();
+        afrag(0, aa);
         mult(wa, aa, acc);
-        issue(b + 2, wa, aa);
-        __builtin_amdgcn_sched_barrier(0);
-        mult(wb, ab, acc);
+        if (nb > 1) {
+            afrag(1, ab);
+            mult(wb, ab, acc);
+        }
+    } else if (nb == 1) {
+        mult(wa, aa, acc);
+    } else {
+        int b = 0;
+        do {                                        // nb >= 2: no guard for the compiler to sink batch 0 behind
+            issue(b + 1, wb, ab);
+            __builtin_amdgcn_sched_barrier(0);      // the next batch's loads go out before these MFMAs wait
+            mult(wa, aa, acc);
+            issue(b + 2, wa, aa);
+            __builtin_amdgcn_sched_barrier(0);
+            mult(wb, ab, acc);
+            b += 2;
+        } while (b < nb);
     }
     // acc: lane l, element e = token 4 (l / 16) + e, channel l % 16
 #pragma unroll
     for (int e = 0; e < 4; ++e) red[wave][(4 * (lane >> 4) + e) * 16 + (lane & 15)] = acc[e];
-
-    const int cnt = (int)bload4(make_rsrc(ep.count, 4), 0);
-    const int m = t >> 4, ch = t & 15;
-    const int64_t n = n0 + ch;
-    float v = 0.0f;
+    stage();
     __syncthreads();
+    const int cnt = __builtin_amdgcn_readfirstlane(cntv);       // block-uniform
+    float v = 0.0f;
     if (t < 256) {
         int32_t c = 0;
 #pragma unroll
         for (int w = 0; w < GV_WAVES; ++w) c += red[w][t];
-        const float sx = m < M ? ep.s_x[m] : 0.0f;
-        const float sw = n < N ? ep.s_w[n] : 0.0f;
         v = (float)c * sx * sw;
     }
-    const rsrc_t rsx = make_rsrc(ep.X, (int64_t)M * K * 2);
-    const rsrc_t rsn = make_rsrc(ep.s_w + n0, (N - n0) * 4);
-    const rsrc_t rwo = ep.W16 ? make_rsrc(ep.W16 + n0 * K, (N - n0) * K * 2) : make_rsrc(ep.Wq + n0 * K, (N - n0) * K);
-    // outlier columns GV_OC at a time: waves 0-3 gather the tokens' values
-    // X[r][k], waves 4-7 the channels' w~[n0 + r][k] (16 rows x GV_OC columns
-    // each, pair q of a wave group = column q / 16, row q % 16), all loads of
-    // a pass in flight before any is written
-    constexpr int PP = GV_OC * 16 / (GV_THREADS / 2);              // pairs per thread
-    const int tt = t & (GV_THREADS / 2 - 1);
     for (int hs = 0; hs < cnt; hs += GV_OC) {
+        if (hs > 0) {                                             // later passes (block-uniform)
+            __syncthreads();
+            load_idx(hs);
+            gather(hs, cnt);
+            stage();
+            __syncthreads();
+        }
         const int hn = cnt - hs < GV_OC ? cnt - hs : GV_OC;
-        const rsrc_t ridx = make_rsrc(ep.idx + hs, (int64_t)hn * 4);
-        uint32_t kk[PP], g[PP];
-#pragma unroll
-        for (int u = 0; u < PP; ++u) {
-            const int h = (tt + u * (GV_THREADS / 2)) >> 4;
-            kk[u] = bload4(ridx, h < hn ? (uint32_t)h * 4 : kOOB);
-        }
-        if (wave < GV_WAVES / 2) {
-#pragma unroll
-            for (int u = 0; u < PP; ++u) {
-                const int q = tt + u * (GV_THREADS / 2), h = q >> 4, r = q & 15;
-                g[u] = bload2(rsx, h < hn && r < M ? ((uint32_t)r * (uint32_t)K + kk[u]) * 2 : kOOB);
-            }
-#pragma unroll
-            for (int u = 0; u < PP; ++u) {
-                const int q = tt + u * (GV_THREADS / 2);
-                xo_s[q >> 4][q & 15] = h2f((uint16_t)g[u]);
-            }
-        } else if (ep.W16) {
-#pragma unroll
-            for (int u = 0; u < PP; ++u) {
-                const int q = tt + u * (GV_THREADS / 2), h = q >> 4, r = q & 15;
-                g[u] = bload2(rwo, h < hn ? ((uint32_t)r * (uint32_t)K + kk[u]) * 2 : kOOB);
-            }
-#pragma unroll
-            for (int u = 0; u < PP; ++u) {
-                const int q = tt + u * (GV_THREADS / 2);
-                wo_s[q >> 4][q & 15] = h2f((uint16_t)g[u]);
-            }
-        } else {
-            const float swr = __builtin_bit_cast(float, bload4(rsn, (uint32_t)(tt & 15) * 4));   // row tt % 16
-#pragma unroll
-            for (int u = 0; u < PP; ++u) {
-                const int q = tt + u * (GV_THREADS / 2), h = q >> 4, r = q & 15;
-                g[u] = bload1(rwo, h < hn ? (uint32_t)r * (uint32_t)K + kk[u] : kOOB);
-            }
-#pragma unroll
-            for (int u = 0; u < PP; ++u) {
-                const int q = tt + u * (GV_THREADS / 2);
-                wo_s[q >> 4][q & 15] = h2f(f2h(swr * (float)(int8_t)(uint8_t)g[u]));
-            }
-        }
-        __syncthreads();
         if (t < 256)
             for (int h = 0; h < hn; ++h) v = v + xo_s[h][m] * wo_s[h][ch];
-        __syncthreads();
     }
     if (t < 256 && m < M && n < N) {
         const int64_t o = (int64_t)m * ep.ldo + n;
@@ -943,8 +1005,12 @@ hipError_t launch_gemm_i8_mixed(const int8_t* Xq, const int8_t* Wq, int64_t M, i
                                 const MixedEpilogue& ep, hipStream_t st) {
     int tm, tn;
     if (M <= 16) {
-        hipLaunchKernelGGL(k_gemv_i8_mixed, dim3((unsigned)((N + 15) / 16)), dim3(GV_THREADS), 0, st, Xq, Wq, (int)M,
-                           K, N, ep);
+        const dim3 g((unsigned)((N + 15) / 16));
+        // the staged path handles at most two batches per wave: K <= 8192
+        if (M * K <= GV_ALDS && K % 1024 == 0 && K <= 2 * GV_WAVES * GV_BATCH * 64)
+            hipLaunchKernelGGL(k_gemv_i8_mixed<true>, g, dim3(GV_THREADS), 0, st, Xq, Wq, (int)M, K, N, ep);
+        else
+            hipLaunchKernelGGL(k_gemv_i8_mixed<false>, g, dim3(GV_THREADS), 0, st, Xq, Wq, (int)M, K, N, ep);
         return hipGetLastError();
     }
     if (pick_cfg(M, N) == 2) {

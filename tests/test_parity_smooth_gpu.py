@@ -131,6 +131,19 @@ def test_qlinear_smooth_decode_shapes(qa, M):
     assert_float_parity(as_f64(out), ref, torch.float16)
 
 
+@pytest.mark.parametrize("M,K,N", [(4, 8192, 33), (2, 3072, 50), (9, 8192, 100), (16, 5120, 40)])
+def test_qlinear_smooth_gemv_shapes(qa, M, K, N):
+    # decode-size calls run the int8 GEMM as a GEMV: codes staged in LDS while
+    # M K <= 64 KB (K = 8192: two batches of K steps per wave, K = 3072: one),
+    # else loaded per wave
+    X, W, _ = synthetic.mixed_inputs(M, K, N, seed=M + K + N, n_dims=5, p_token=1.0)
+    s = factors(X, W)
+    Wq, s_w = oracle.smooth_quantize(W, s, oracle.SMOOTH_MULTIPLY)
+    out = qa.qa_qlinear_int8_smooth(dev(X), dev(s), dev(Wq), dev(s_w), out_dtype=torch.float16)
+    ref = oracle.qlinear_int8_smooth(X, s, Wq, s_w)
+    assert_float_parity(as_f64(out), ref, torch.float16)
+
+
 def _full_size(qa, name, per_tensor, rows):
     c = synthetic.config(name)
     X, W = c["X"], c["W"]

@@ -96,6 +96,15 @@ def test_topk_linear_shapes(qa, M, K, N, k, pass_w16):
     _topk_case(qa, X, W, k, 0, pass_w16)
 
 
+@pytest.mark.parametrize("M,K,N,k,pass_w16", [(4, 8192, 40, 30, False), (3, 8192, 20, 200, True),
+                                              (16, 2048, 70, 100, False), (12, 8192, 24, 140, False)])
+def test_topk_linear_gemv_shapes(qa, M, K, N, k, pass_w16):
+    # decode sizes: the GEMV with codes in LDS (or per wave past 64 KB), one
+    # or two staging passes of the fp16 product
+    X, W, _ = synthetic.mixed_inputs(M, K, N, seed=M * 3 + k, n_dims=6, p_token=0.9)
+    _topk_case(qa, X, W, k, 1, pass_w16)
+
+
 @pytest.mark.parametrize("out_dtype", [0, 1, 2])
 def test_topk_linear_out_dtypes(qa, out_dtype):
     X, W, _ = synthetic.mixed_inputs(40, 512, 96, seed=45, n_dims=3, x_dist="t3")
