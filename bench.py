@@ -16,7 +16,9 @@ linear, the SmoothQuant W8A8 linear on the prefill and FFN data and the
 top-2% decomposition and the zero-point W8A8 linear on the prefill data, and
 the Kronecker-transform W4A4 linear, the W4A8 group-Hadamard linear and the
 W4A4 linear with zero-point activations (one-sided) on the W4A4 data, in int8
-TOPS against the dense int8 MFMA peak.  Each also carries `gemm_roofline`:
+TOPS against the dense int8 MFMA peak; and the SmoothQuant and top-2% linears
+at the decode shape (smooth_decode, topk_decode), in GB/s like the headline,
+each with `gemv_roofline` from its recorded k_gemv_i8_mixed time.  Each also carries `gemm_roofline`:
 the GEMM kernels' own time per call, the sum of their average rocprofv3
 durations recorded in profiles/kernel_times.json for that workload (null while
 the record is missing or any kernel source has changed since it was taken),
@@ -59,7 +61,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--only", default=None,
                    help="run one workload only (decode|prefill|w8a8|w4a4|smooth_prefill|smooth_ffn|topk_prefill|"
-                        "asym_prefill|kron_w4a4|w4a8|w4a4_asym|copy|floor), for "
+                        "asym_prefill|kron_w4a4|w4a8|w4a4_asym|smooth_decode|topk_decode|copy|floor), for "
                         "profiling; copy is a plain "
                         "1 GiB device copy used to calibrate HBM byte counters; floor sweeps the plain "
                         "read of the decode step's bytes (qa_probe_stream_read) and an empty launch")
@@ -135,11 +137,12 @@ def recorded_traffic(kernel, source):
     return rec.get("hbm_bytes_per_launch")
 
 
-def recorded_gemm_time(key):
+def recorded_gemm_time(key, tag="k_gemm"):
     """GEMM-kernel time per call of workload `key` from profiles/kernel_times.json
     (rocprofv3 --kernel-trace of `bench.py --only key`, written by
-    profile_counters.py): the sum of the average durations of its k_gemm_*
-    kernels, each of which runs once per call.  (None, reason) when the record
+    profile_counters.py): the sum of the average durations of its kernels
+    whose names contain `tag` (k_gemm_*, or k_gemv_* at decode sizes), each
+    of which runs once per call.  (None, reason) when the record
     is missing or any kernel source changed since it was taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "kernel_times.json")
@@ -154,7 +157,7 @@ def recorded_gemm_time(key):
         with open(os.path.join(csrc, name), "rb") as fh:
             if rec["sources_sha256"].get(name) != hashlib.sha256(fh.read()).hexdigest():
                 return None, None, "kernel sources changed since the record (%s)" % name
-    gemm = {k: v for k, v in rec["kernels"].items() if "k_gemm" in k}
+    gemm = {k: v for k, v in rec["kernels"].items() if tag in k}
     if not gemm or len({v["calls"] for v in gemm.values()}) != 1:
         return None, None, "record has no single set of GEMM launches"
     return sum(v["avg_us"] for v in gemm.values()), sorted(gemm), rec["command"]
@@ -227,6 +230,35 @@ def topk_workload(torch, qa, synthetic, dev, name, share):
     ws = torch.empty(qa.qa_qlinear_int8_topk_workspace(M, K), dtype=torch.uint8, device=dev)
     fns = [lambda: qa.qa_qlinear_int8_topk(X, Wq, s_w, k, out=out, workspace=ws)]
     return c, fns, 2 * M * N * K, k
+
+
+def decode_variant_workload(torch, qa, synthetic, dev, kind):
+    """The SmoothQuant (per-token) or top-2% linear at the decode shape, over
+    weight copies like the decode headline (every call streams its weight
+    from HBM); -> (config, calls, algorithmic bytes per call, label)."""
+    c = synthetic.config("decode_mixed")
+    M, K, N = c["M"], c["K"], c["N"]
+    X = torch.from_numpy(c["X"]).to(dev)
+    W16 = torch.from_numpy(c["W"]).to(dev)
+    out = torch.empty((M, N), dtype=torch.float16, device=dev)
+    if kind == "smooth":
+        s = qa.qa_smooth_factors(qa.qa_col_absmax(X), qa.qa_col_absmax(W16), 0.5)
+        Wq, s_w = qa.qa_quantize_smooth_int8(W16, s, multiply=True)
+        ws = torch.empty(qa.qa_qlinear_int8_smooth_workspace(M, K), dtype=torch.uint8, device=dev)
+        call = lambda W: (lambda: qa.qa_qlinear_int8_smooth(X, s, W, s_w, out=out, workspace=ws))
+        nbytes = N * K + 4 * N + 2 * M * K + 4 * K + 2 * M * N
+        label = "smooth_decode: SmoothQuant W8A8 (X/s per-token int8), decode_mixed data"
+    else:
+        Wq, s_w = qa.qa_quantize_rowwise_int8(W16)
+        k = qa.topk_count(0.02, K)
+        ws = torch.empty(qa.qa_qlinear_int8_topk_workspace(M, K), dtype=torch.uint8, device=dev)
+        call = lambda W: (lambda: qa.qa_qlinear_int8_topk(X, W, s_w, k, out=out, workspace=ws))
+        nbytes = N * K + 4 * N + 2 * M * K + 2 * M * N
+        label = "topk_decode: LLM.int8() with the top 2%% (%d) of dims in fp16, decode_mixed data" % k
+    del W16
+    copies = max(2, -(-2 * MALL_BYTES // (N * K)))
+    Wqs = [Wq] + [Wq.clone() for _ in range(copies - 1)]
+    return c, [call(W) for W in Wqs], nbytes, label
 
 
 def asym_workload(torch, qa, synthetic, dev, name):
@@ -420,7 +452,7 @@ def main():
         torch.cuda.empty_cache()
 
     keys = ("prefill", "w8a8", "w4a4", "smooth_prefill", "smooth_ffn", "topk_prefill", "asym_prefill", "kron_w4a4",
-            "w4a8", "w4a4_asym")
+            "w4a8", "w4a4_asym", "smooth_decode", "topk_decode")
     run_also = (args.only is None and not args.no_also) or args.only in keys
     if run_also:
         todo = []
@@ -428,11 +460,35 @@ def main():
                           ("prefill_mixed", "smooth_prefill"), ("w8a8_ffn", "smooth_ffn"),
                           ("prefill_mixed", "topk_prefill"), ("prefill_mixed", "asym_prefill"),
                           ("w4a4_hadamard", "kron_w4a4"), ("w4a4_hadamard", "w4a8"),
-                          ("w4a4_hadamard", "w4a4_asym")):
+                          ("w4a4_hadamard", "w4a4_asym"), ("decode_mixed", "smooth_decode"),
+                          ("decode_mixed", "topk_decode")):
             if args.only in (None, key):
                 todo.append((name, key))
         for name, key in todo:
             log("[bench] %s: building inputs" % key)
+            if key in ("smooth_decode", "topk_decode"):
+                c, fns, nbytes, name = decode_variant_workload(torch, qa, synthetic, dev, key.split("_")[0])
+                gs = GraphSteps(torch, fns)
+                log("[bench] %s: timing %d calls" % (name, args.steps))
+                ms, wall_ms, n = time_graph(torch, gs, args.steps, args.warmup)
+                gbs = nbytes / (ms * 1e-3) / 1e9
+                gus, gnames, gsrc = recorded_gemm_time(key, "k_gemv")
+                if gus is None:
+                    gemv = {"kernel_us": None, "reason": gsrc}
+                else:
+                    gemv = {"bound": "hbm", "kernels": gnames, "kernel_us": round(gus, 3),
+                            "achieved": round(nbytes / (gus * 1e-6) / 1e9, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(nbytes / (gus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                            "source": "profiles/kernel_times.json[%s]: %s" % (key, gsrc)}
+                also.append({"workload": name, "key": key, "M": c["M"], "K": c["K"], "N": c["N"],
+                             "ms_per_call": round(ms, 6), "GBs": round(gbs, 2), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                             "bytes_per_call": nbytes, "calls": n,
+                             "note": "whole call (all kernels), graph replay over weight copies",
+                             "gemv_roofline": gemv})
+                log("[bench] %s: %.2f us per call, %.1f GB/s" % (name, ms * 1e3, gbs))
+                del fns, gs
+                torch.cuda.empty_cache()
+                continue
             if key == "w4a4":
                 c, fns, ops = w4a4_workload(torch, qa, synthetic, dev)
             elif key == "smooth_prefill":
