@@ -41,6 +41,7 @@ namespace qa {
 constexpr int DEC_WAVES = 8, DEC_THREADS = 64 * DEC_WAVES;
 constexpr int DEC_CHUNK_K = 8 * DEC_THREADS;    // columns covered by one chunk per thread (4096)
 constexpr int DEC_OCAP = 64;                    // outliers whose operands are staged in LDS
+constexpr int DEC_OCAP_TOPK = 256;              // the same for the top-k set (k <= 256 takes this kernel)
 static_assert(DEC_WAVES == 8, "the wave totals are read as two 16-byte vectors");
 
 typedef unsigned short u16x2v __attribute__((ext_vector_type(2)));
@@ -140,14 +141,185 @@ __device__ __forceinline__ u32x2 codes8_biased(const u32x4& v, float s, float r)
 // Barrier over the eight activation waves only (the weight waves may be
 // stalled issuing their loads): an LDS counter, set to zero before the first
 // workgroup barrier, that every activation wave increments once its LDS
-// writes are done, then waits for until all eight have.
-__device__ __forceinline__ void activation_barrier(int* ctr, int lane) {
+// writes are done, then waits for until it reaches `target` (8 times the
+// number of such barriers passed so far, this one included).
+__device__ __forceinline__ void activation_barrier(int* ctr, int lane, int target) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0xC07F);      // this wave's LDS writes are done
     if (lane == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < DEC_WAVES)
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target)
         __builtin_amdgcn_s_sleep(1);
     asm volatile("" ::: "memory");
+}
+
+// Inclusive sum over the 64 lanes: DPP row shifts within rows of 16, then
+// the totals of the rows below (lanes 15, 31, 47) added by row.
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v, int lane) {
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);   // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);   // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);   // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);   // row_shr:8
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 47);
+    const int row = lane >> 4;
+    return v + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+}
+
+// One radix digit of the k-th largest key: lane l holds the counts h[0..B-1]
+// of digits D - B l, D - B l - 1, ... (descending from the top digit D); the
+// digit holding the `rem`-th largest key (1 <= rem <= the total) and the
+// number of keys in higher digits, plus that digit's count, the same in
+// every lane.
+template <int B>
+__device__ __forceinline__ void pick_digit(const uint32_t* h, uint32_t rem, int top, int lane, uint32_t& digit,
+                                           uint32_t& above_out, uint32_t& count_out) {
+    uint32_t cs = 0u;
+#pragma unroll
+    for (int i = 0; i < B; ++i) cs += h[i];
+    const uint32_t incl = wave_incl_sum(cs, lane);
+    uint32_t above = incl - cs, dg = 0u, he = 0u;
+    bool found = false;
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+        if (!found && above + h[i] >= rem) {
+            dg = (uint32_t)(top - B * lane - i);
+            he = h[i];
+            found = true;
+        } else if (!found) {
+            above += h[i];
+        }
+    }
+    const int src = __builtin_ctzll(__ballot(incl - cs < rem && rem <= incl));
+    digit = (uint32_t)__builtin_amdgcn_readlane((int)dg, src);
+    above_out = (uint32_t)__builtin_amdgcn_readlane((int)above, src);
+    count_out = (uint32_t)__builtin_amdgcn_readlane((int)he, src);
+}
+
+// The top-k flags of this thread's chunks (bit j of flags[c]: column
+// 8 (t + 512 c) + j is taken) from its packed column-max keys cmx (chunks at
+// or past nch hold no columns); called by every activation wave with the same
+// k.  red and hist2 are [8][256] and cleared; nbar returns the target of the
+// next activation barrier.
+template <int CH>
+__device__ __forceinline__ void topk_flags(const uint32_t (&cmx)[CH][4], uint32_t k, int nch, int t, int lane,
+                                           int wave, int32_t* red, uint32_t* hist2, uint32_t* tie_tot, int* abar,
+                                           uint32_t* flags, int& nbar) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) flags[c] = 0u;
+    nbar = DEC_WAVES;
+    if (k == 0) return;
+    // high digit: bits 14..8 of the key (bit 15, the sign, is clear)
+    uint32_t* h1 = reinterpret_cast<uint32_t*>(red) + 256 * wave + 128 * (lane & 1);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        if (t + DEC_THREADS * c < nch) {
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t v = cmx[c][d];
+                __hip_atomic_fetch_add(h1 + ((v >> 8) & 0x7fu), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                __hip_atomic_fetch_add(h1 + (v >> 24), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+        }
+    }
+    activation_barrier(abar, lane, DEC_WAVES);
+    uint32_t h[4];
+    {
+        uint32_t hh = 0u, hl = 0u;                    // digits 127 - 2 lane and 126 - 2 lane
+#pragma unroll
+        for (int w = 0; w < DEC_WAVES; ++w)
+#pragma unroll
+            for (int cp = 0; cp < 2; ++cp) {
+                const uint32_t* q = reinterpret_cast<const uint32_t*>(red) + 256 * w + 128 * cp + 126 - 2 * lane;
+                hl += q[0];
+                hh += q[1];
+            }
+        h[0] = hh;
+        h[1] = hl;
+    }
+    uint32_t d1, a1, n1;
+    pick_digit<2>(h, k, 127, lane, d1, a1, n1);
+    const uint32_t rem = k - a1;                      // keys still to take from digit d1: 1 <= rem <= n1
+    // low digit over the keys in high digit d1
+    uint32_t* h2 = hist2 + 256 * wave;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        if (t + DEC_THREADS * c < nch) {
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t v = cmx[c][d];
+                if (((v >> 8) & 0x7fu) == d1)
+                    __hip_atomic_fetch_add(h2 + (v & 0xffu), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                if ((v >> 24) == d1)
+                    __hip_atomic_fetch_add(h2 + ((v >> 16) & 0xffu), 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+        }
+    }
+    activation_barrier(abar, lane, 2 * DEC_WAVES);
+    {
+        u32x4 a = u32x4{0u, 0u, 0u, 0u};              // digits 252 - 4 lane .. 255 - 4 lane
+#pragma unroll
+        for (int w = 0; w < DEC_WAVES; ++w) a += *reinterpret_cast<const u32x4*>(hist2 + 256 * w + 252 - 4 * lane);
+        h[0] = a[3];
+        h[1] = a[2];
+        h[2] = a[1];
+        h[3] = a[0];
+    }
+    uint32_t d2, a2, neq;
+    pick_digit<4>(h, rem, 255, lane, d2, a2, neq);
+    const uint32_t kth = (d1 << 8) | d2, take = rem - a2;   // keys equal to kth: neq, of which take are taken
+    uint32_t eq[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        uint32_t gt = 0u, e = 0u;
+        if (t + DEC_THREADS * c < nch) {
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t lo = cmx[c][d] & 0xffffu, hi = cmx[c][d] >> 16;
+                gt |= ((lo > kth ? 1u : 0u) | (hi > kth ? 2u : 0u)) << (2 * d);
+                e |= ((lo == kth ? 1u : 0u) | (hi == kth ? 2u : 0u)) << (2 * d);
+            }
+        }
+        flags[c] = gt;
+        eq[c] = e;
+    }
+    nbar = 3 * DEC_WAVES;
+    if (take == neq) {                                // every tie taken (the same branch in every wave)
+#pragma unroll
+        for (int c = 0; c < CH; ++c) flags[c] |= eq[c];
+        return;
+    }
+    // ties split: rank the equal keys in column order (chunk set 0, then 1)
+    uint32_t below[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const uint32_t n = (uint32_t)__builtin_popcount(eq[c]);
+        const uint32_t incl = wave_incl_sum(n, lane);
+        below[c] = incl - n;
+        if (lane == 63) tie_tot[DEC_WAVES * c + wave] = incl;
+    }
+    activation_barrier(abar, lane, 3 * DEC_WAVES);
+    nbar = 4 * DEC_WAVES;
+    uint32_t base = 0u;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        uint32_t before = 0u, tot = 0u;
+#pragma unroll
+        for (int w = 0; w < DEC_WAVES; ++w) {
+            const uint32_t x = tie_tot[DEC_WAVES * c + w];
+            tot += x;
+            before += w < wave ? x : 0u;
+        }
+        uint32_t r = base + before + below[c], e = eq[c];
+        while (e) {
+            const int b = __builtin_ctz(e);
+            e &= e - 1u;
+            if (r < take) flags[c] |= 1u << b;
+            ++r;
+        }
+        base += tot;
+    }
 }
 
 // MB: tokens per block (4, 8 or 16); CH: 8-column chunks per thread (K <= 4096 CH).
@@ -158,22 +330,36 @@ __device__ __forceinline__ void activation_barrier(int* ctr, int lane) {
 // issues more loads than its compute unit can keep in flight stalls until
 // earlier ones return -- about 2 us for this 64 KB per workgroup -- so the
 // weight loads are issued by waves that have nothing else to do meanwhile.
-template <int MB, int CH>
+//
+// TOPK: the outlier set is the k = thr1 columns of largest column maximum
+// (equal maxima: lower column first) instead of those above a threshold.  The
+// activation waves find the k-th largest key (the sign-cleared fp16 pattern
+// of the column maximum; patterns order like magnitudes) by a two-digit radix
+// select -- per-wave histograms of the high byte in LDS (two copies by lane
+// parity, fewer same-address atomics), the digit from a lane scan that every
+// wave does itself, the same for the low byte over the keys in that high
+// digit -- then take the keys above it and, in column order, as many keys
+// equal to it as are still missing (a ballot scan over the ties, skipped
+// when every tie is taken).
+template <int MB, int CH, bool TOPK>
 __global__ __launch_bounds__(2 * DEC_THREADS) void k_decode_mixed(const uint16_t* __restrict__ X, int M, int K,
                                                                   const int8_t* __restrict__ Wq,
                                                                   const float* __restrict__ s_w,
                                                                   const uint16_t* __restrict__ W16, int64_t N,
                                                                   uint32_t thr1, void* __restrict__ out,
                                                                   int out_dtype, DecodeStages st) {
+    constexpr int OCAP = TOPK ? DEC_OCAP_TOPK : DEC_OCAP;
     constexpr int MAXK = DEC_CHUNK_K * CH;
     constexpr int LDA = MAXK + 16;                  // LDS row stride of the codes (spreads banks)
     constexpr int STEPS = MAXK / 64 / DEC_WAVES;    // MFMA steps per weight wave
     constexpr int NG = MB > 8 ? 2 : 1;              // groups of eight tokens for the lane reductions
     __shared__ __attribute__((aligned(16))) int8_t aq[MB * LDA];
     __shared__ int16_t oidx[MAXK];
-    __shared__ int32_t red[DEC_WAVES][256];
-    __shared__ float xo[DEC_OCAP][16];       // outlier activations  [h][m]
-    __shared__ float wo[DEC_OCAP][16];       // outlier weights w~   [h][channel]
+    __shared__ __attribute__((aligned(16))) int32_t red[DEC_WAVES][256];
+    __shared__ float xo[OCAP][16];           // outlier activations  [h][m]
+    __shared__ float wo[OCAP][16];           // outlier weights w~   [h][channel]
+    __shared__ __attribute__((aligned(16))) uint32_t hist2[TOPK ? DEC_WAVES : 1][256];   // low-digit histograms
+    __shared__ uint32_t tie_tot[TOPK ? CH : 1][DEC_WAVES];
     __shared__ __attribute__((aligned(16))) uint32_t rmax[16][DEC_WAVES];   // [token][activation wave]
     __shared__ float sx_s[16];
     __shared__ __attribute__((aligned(16))) int wtot[CH][DEC_WAVES];
@@ -208,6 +394,10 @@ __global__ __launch_bounds__(2 * DEC_THREADS) void k_decode_mixed(const uint16_t
 #pragma unroll
             for (int m = 0; m < MB; ++m) xv[c][m] = bload16(rsx, ch < nch ? (uint32_t)(m * K + 8 * ch) * 2 : kOOB);
         }
+        if constexpr (TOPK) {   // clear the histograms (the high-digit ones live in red until the epilogue)
+            reinterpret_cast<u32x4*>(&red[0][0])[t] = u32x4{0u, 0u, 0u, 0u};
+            reinterpret_cast<u32x4*>(&hist2[0][0])[t] = u32x4{0u, 0u, 0u, 0u};
+        }
         // the weight waves issue their stream once every X request is issued
         lds_barrier();                                                  // barrier 1
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -220,27 +410,50 @@ __global__ __launch_bounds__(2 * DEC_THREADS) void k_decode_mixed(const uint16_t
         uint32_t keep[CH][4];
         uint32_t flags[CH];
         uint32_t rm[NG * 8];
+        int nbar = DEC_WAVES;                         // activation-barrier target of step 2b
 #pragma unroll
         for (int m = 0; m < NG * 8; ++m) rm[m] = 0u;
+        if constexpr (TOPK) {
+            uint32_t cmx[CH][4];
+#pragma unroll
+            for (int c = 0; c < CH; ++c)
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    uint32_t a = 0u;
+#pragma unroll
+                    for (int m = 0; m < MB; ++m) a = pk_max_u16(a, xv[c][m][d] & 0x7fff7fffu);
+                    cmx[c][d] = a;
+                }
+            topk_flags<CH>(cmx, thr1, nch, t, lane, wave, &red[0][0], &hist2[0][0], &tie_tot[0][0], &abar, flags,
+                           nbar);
+#pragma unroll
+            for (int c = 0; c < CH; ++c)
+#pragma unroll
+                for (int d = 0; d < 4; ++d)
+                    keep[c][d] = (((flags[c] >> (2 * d)) & 1u) ? 0u : 0xffffu) |
+                                 (((flags[c] >> (2 * d + 1)) & 1u) ? 0u : 0xffff0000u);
+        }
         const u16x2v T = u16x2v{(unsigned short)thr1, (unsigned short)thr1};
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-            uint32_t cm[4] = {0u, 0u, 0u, 0u};
+            if constexpr (!TOPK) {
+                uint32_t cm[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int m = 0; m < MB; ++m)
+                for (int m = 0; m < MB; ++m)
 #pragma unroll
-                for (int d = 0; d < 4; ++d) cm[d] = pk_max_u16(cm[d], xv[c][m][d] & 0x7fff7fffu);
-            uint32_t f = 0u;
+                    for (int d = 0; d < 4; ++d) cm[d] = pk_max_u16(cm[d], xv[c][m][d] & 0x7fff7fffu);
+                uint32_t f = 0u;
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                // 1 per ordinary half (thr1 - cm > 0), 0 per outlier half
-                const u16x2v k1 = __builtin_elementwise_min(__builtin_elementwise_sub_sat(T, v_of(cm[d])),
-                                                            u16x2v{1, 1});
-                keep[c][d] = u32_of(u16x2v{0, 0} - k1);
-                const uint32_t kb = u32_of(k1);
-                f |= ((kb & 1u) | ((kb >> 15) & 2u)) << (2 * d);
+                for (int d = 0; d < 4; ++d) {
+                    // 1 per ordinary half (thr1 - cm > 0), 0 per outlier half
+                    const u16x2v k1 = __builtin_elementwise_min(__builtin_elementwise_sub_sat(T, v_of(cm[d])),
+                                                                u16x2v{1, 1});
+                    keep[c][d] = u32_of(u16x2v{0, 0} - k1);
+                    const uint32_t kb = u32_of(k1);
+                    f |= ((kb & 1u) | ((kb >> 15) & 2u)) << (2 * d);
+                }
+                flags[c] = (t + DEC_THREADS * c < nch) ? (~f & 0xffu) : 0u;
             }
-            flags[c] = (t + DEC_THREADS * c < nch) ? (~f & 0xffu) : 0u;
 #pragma unroll
             for (int m = 0; m < MB; ++m) {
                 const uint32_t r01 = pk_max_u16(xv[c][m][0] & 0x7fff7fffu & keep[c][0],
@@ -283,7 +496,7 @@ __global__ __launch_bounds__(2 * DEC_THREADS) void k_decode_mixed(const uint16_t
 #pragma unroll
             for (int c = 0; c < CH; ++c) wtot[c][wave] = wsum[c];
         }
-        activation_barrier(&abar, lane);
+        activation_barrier(&abar, lane, nbar);
 
         // per-token scales: lane m < MB reduces token m over the waves (every
         // activation wave does, so no further barrier is needed)
@@ -325,7 +538,7 @@ __global__ __launch_bounds__(2 * DEC_THREADS) void k_decode_mixed(const uint16_t
                     const int j = __builtin_ctz(f);
                     f &= f - 1u;
                     oidx[o] = (int16_t)(8 * (t + DEC_THREADS * c) + j);
-                    if (o < DEC_OCAP) {
+                    if (o < OCAP) {
 #pragma unroll
                         for (int m = 0; m < MB; ++m) {
                             const uint32_t w32 = pick4(xv[c][m], j >> 1);
@@ -382,7 +595,7 @@ __global__ __launch_bounds__(2 * DEC_THREADS) void k_decode_mixed(const uint16_t
         const int gch = t & 15, gh = t >> 4;          // channel n0 + gch, outlier slots gh + 32 q
         const rsrc_t rs16 = make_rsrc(W16 ? W16 + n0 * K : nullptr, W16 ? (N - n0) * K * 2 : 0);
         const rsrc_t rsg = W16 ? rs16 : rsw;
-        constexpr int GQ = DEC_OCAP / (DEC_THREADS / 16);
+        constexpr int GQ = OCAP / (DEC_THREADS / 16);
         uint32_t graw[GQ], gsh[GQ];
 #pragma unroll
         for (int q = 0; q < GQ; ++q) {
@@ -426,9 +639,9 @@ __global__ __launch_bounds__(2 * DEC_THREADS) void k_decode_mixed(const uint16_t
 #pragma unroll
         for (int w = 0; w < DEC_WAVES; ++w) c += red[w][t];
         float v = (float)c * sx_s[m] * swg;
-        const int hs = count < DEC_OCAP ? count : DEC_OCAP;
+        const int hs = count < OCAP ? count : OCAP;
         for (int h = 0; h < hs; ++h) v = v + xo[h][m] * wo[h][ch];
-        for (int h = DEC_OCAP; h < count; ++h) {          // beyond the staged outliers
+        for (int h = OCAP; h < count; ++h) {              // beyond the staged outliers
             const int k = oidx[h];
             const float wt = W16 ? h2f(W16[n * K + k]) : h2f(f2h(swg * (float)Wq[n * K + k]));
             v = v + h2f(X[(int64_t)m * K + k]) * wt;
@@ -482,31 +695,47 @@ static uint32_t threshold_pattern(float tau) {
     return lo + 1;
 }
 
-template <int MB, int CH>
+template <int MB, int CH, bool TOPK>
 static void launch_mb(const dim3& grid, hipStream_t st, const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq,
                       const float* s_w, const uint16_t* W16, int64_t N, uint32_t thr1, void* out, int out_dtype,
                       const DecodeStages& stages) {
-    hipLaunchKernelGGL((k_decode_mixed<MB, CH>), grid, dim3(2 * DEC_THREADS), 0, st, X, (int)M, (int)K, Wq, s_w, W16, N,
-                       thr1, out, out_dtype, stages);
+    hipLaunchKernelGGL((k_decode_mixed<MB, CH, TOPK>), grid, dim3(2 * DEC_THREADS), 0, st, X, (int)M, (int)K, Wq, s_w,
+                       W16, N, thr1, out, out_dtype, stages);
+}
+
+template <bool TOPK>
+static void launch_decode(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* s_w,
+                          const uint16_t* W16, int64_t N, uint32_t thr1, void* out, int out_dtype,
+                          const DecodeStages& stages, hipStream_t st) {
+    const dim3 grid((unsigned)((N + 15) / 16));
+    if (K > DEC_CHUNK_K) {
+        if (M <= 4)
+            launch_mb<4, 2, TOPK>(grid, st, X, M, K, Wq, s_w, W16, N, thr1, out, out_dtype, stages);
+        else
+            launch_mb<8, 2, TOPK>(grid, st, X, M, K, Wq, s_w, W16, N, thr1, out, out_dtype, stages);
+    } else if (M <= 4) {
+        launch_mb<4, 1, TOPK>(grid, st, X, M, K, Wq, s_w, W16, N, thr1, out, out_dtype, stages);
+    } else if (M <= 8) {
+        launch_mb<8, 1, TOPK>(grid, st, X, M, K, Wq, s_w, W16, N, thr1, out, out_dtype, stages);
+    } else {
+        launch_mb<16, 1, TOPK>(grid, st, X, M, K, Wq, s_w, W16, N, thr1, out, out_dtype, stages);
+    }
 }
 
 hipError_t launch_decode_mixed(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* s_w,
                                const uint16_t* W16, int64_t N, float tau, void* out, int out_dtype,
                                const DecodeStages& stages, hipStream_t st) {
-    const dim3 grid((unsigned)((N + 15) / 16));
-    const uint32_t thr1 = threshold_pattern(tau);
-    if (K > DEC_CHUNK_K) {
-        if (M <= 4)
-            launch_mb<4, 2>(grid, st, X, M, K, Wq, s_w, W16, N, thr1, out, out_dtype, stages);
-        else
-            launch_mb<8, 2>(grid, st, X, M, K, Wq, s_w, W16, N, thr1, out, out_dtype, stages);
-    } else if (M <= 4) {
-        launch_mb<4, 1>(grid, st, X, M, K, Wq, s_w, W16, N, thr1, out, out_dtype, stages);
-    } else if (M <= 8) {
-        launch_mb<8, 1>(grid, st, X, M, K, Wq, s_w, W16, N, thr1, out, out_dtype, stages);
-    } else {
-        launch_mb<16, 1>(grid, st, X, M, K, Wq, s_w, W16, N, thr1, out, out_dtype, stages);
-    }
+    launch_decode<false>(X, M, K, Wq, s_w, W16, N, threshold_pattern(tau), out, out_dtype, stages, st);
+    return hipGetLastError();
+}
+
+int64_t decode_topk_max() { return DEC_OCAP_TOPK; }
+
+hipError_t launch_decode_topk(const uint16_t* X, int64_t M, int64_t K, int64_t k, const int8_t* Wq, const float* s_w,
+                              const uint16_t* W16, int64_t N, void* out, int out_dtype, const DecodeStages& stages,
+                              hipStream_t st) {
+    if (k < 0 || k > K || k > DEC_OCAP_TOPK) return hipErrorInvalidValue;
+    launch_decode<true>(X, M, K, Wq, s_w, W16, N, (uint32_t)k, out, out_dtype, stages, st);
     return hipGetLastError();
 }
 

@@ -221,14 +221,21 @@ hipError_t launch_outlier_flags(const uint16_t* X, int64_t M, int64_t K, float t
 // the flag consumers see exactly the top-k set.  Thread t owns the TC
 // consecutive columns [t TC, t TC + TC), TC = K / 1024 rounded up to a power
 // of two, so a flag word is assembled from 64 / TC threads.
+// FROMX (M <= 16 rows, M K <= 2^17): no scan before it; the block takes the column maxima
+// from X itself (sign-cleared fp16 patterns, max over the rows) and leaves
+// them as segment 0's partial maxima, as the scan would have.
 // ---------------------------------------------------------------------------
 constexpr int TOPK_MAXK = 32768;
 constexpr int TOPK_THREADS = 1024;
 constexpr int TOPK_WAVES = TOPK_THREADS / 64;
+constexpr int TOPK_FROMX_ROWS = 16;
+constexpr int64_t TOPK_FROMX_ELEMS = 16 * 8192;       // one CU reads at most 256 KB of X
 
+template <bool FROMX>
 __global__ __launch_bounds__(TOPK_THREADS) void k_topk_select(unsigned long long* __restrict__ flags_p,
-                                                              const uint32_t* __restrict__ cmax_p, int nseg,
-                                                              int64_t K, int64_t k) {
+                                                              uint32_t* __restrict__ cmax_p, int nseg,
+                                                              int64_t K, int64_t k, const uint16_t* __restrict__ X,
+                                                              int M) {
     __shared__ uint16_t keys[TOPK_MAXK];
     __shared__ uint32_t hist[TOPK_WAVES][256];
     __shared__ unsigned long long wout[TOPK_MAXK / 64];
@@ -236,10 +243,36 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk_select(unsigned long long
     __shared__ uint32_t sel[2];                         // digit found, count above it
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int64_t nw = (K + 63) / 64;
+    if constexpr (FROMX) {
+        // four columns per thread and pass, all rows' loads in flight at once
+        const rsrc_t rx = make_rsrc(X, (int64_t)M * K * 2);
+        for (int64_t j0 = 0; j0 < K; j0 += 4 * TOPK_THREADS) {
+            uint32_t v[4][TOPK_FROMX_ROWS];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int i = 0; i < TOPK_FROMX_ROWS; ++i) {
+                    const int64_t j = j0 + u * TOPK_THREADS + t;
+                    v[u][i] = bload2(rx, i < M && j < K ? (uint32_t)(i * K + j) * 2 : kOOB);
+                }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                uint32_t m = 0u;
+#pragma unroll
+                for (int i = 0; i < TOPK_FROMX_ROWS; ++i) m = max(m, v[u][i] & 0x7fffu);
+                const int64_t j = j0 + u * TOPK_THREADS + t;
+                if (j < K) {
+                    const float cm = h2f((uint16_t)m);
+                    keys[j] = f2h(cm);                  // the same key the scan + merge give
+                    cmax_p[j] = __builtin_bit_cast(uint32_t, cm);
+                }
+            }
+        }
+    }
     // merge the segments: four columns per thread and pass, all 4 x OC_SEG_MAX
     // loads in flight before the first is used (out-of-range ones read 0)
     const rsrc_t rc = make_rsrc(cmax_p, (int64_t)nseg * K * 4);
-    for (int64_t j0 = 0; j0 < K; j0 += 4 * TOPK_THREADS) {
+    for (int64_t j0 = 0; !FROMX && j0 < K; j0 += 4 * TOPK_THREADS) {
         uint32_t v[4][OC_SEG_MAX];
 #pragma unroll
         for (int u = 0; u < 4; ++u)
@@ -348,10 +381,17 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk_select(unsigned long long
 
 hipError_t launch_outlier_topk_flags(const uint16_t* X, int64_t M, int64_t K, int64_t k, void* scratch, int* segs,
                                      hipStream_t st) {
-    *segs = outlier_scan(X, M, K, __builtin_inff(), scratch, true, st);
     unsigned long long* flags_p = static_cast<unsigned long long*>(scratch);
     uint32_t* cmax_p = reinterpret_cast<uint32_t*>(flags_p + OC_SEG_MAX * ((K + 63) / 64));
-    hipLaunchKernelGGL(k_topk_select, dim3(1), dim3(TOPK_THREADS), 0, st, flags_p, cmax_p, *segs, K, k);
+    if (M <= TOPK_FROMX_ROWS && M * K <= TOPK_FROMX_ELEMS) {   // one launch: column maxima from X in the block
+        *segs = 1;
+        hipLaunchKernelGGL(k_topk_select<true>, dim3(1), dim3(TOPK_THREADS), 0, st, flags_p, cmax_p, 1, K, k, X,
+                           (int)M);
+    } else {
+        *segs = outlier_scan(X, M, K, __builtin_inff(), scratch, true, st);
+        hipLaunchKernelGGL(k_topk_select<false>, dim3(1), dim3(TOPK_THREADS), 0, st, flags_p, cmax_p, *segs, K, k,
+                           X, (int)M);
+    }
     return hipGetLastError();
 }
 

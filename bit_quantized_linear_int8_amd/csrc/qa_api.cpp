@@ -360,6 +360,10 @@ qa_status qa_qlinear_int8_topk(const void* X_f16, int64_t M, int64_t K, int64_t 
     float* s_x = reinterpret_cast<float*>(ws + L.s_x);
     int8_t* xq = reinterpret_cast<int8_t*>(ws + L.xq);
     uint16_t* xo = reinterpret_cast<uint16_t*>(ws + L.xo);
+    if (qa::decode_supported(M, K) && k <= qa::decode_topk_max())
+        return device_status(qa::launch_decode_topk(X, M, K, k, Wq, s_w, static_cast<const uint16_t*>(W_f16_or_null),
+                                                    N, out, (int)out_dtype, qa::DecodeStages{idx, count, s_x, xq}, st),
+                             "qa_qlinear_int8_topk (decode kernel)");
     int segs = 1;
     hipError_t e = qa::launch_outlier_topk_flags(X, M, K, k, ws + L.cmax, &segs, st);
     if (e != hipSuccess) return device_status(e, "qa_qlinear_int8_topk (top-k columns)");

@@ -168,6 +168,13 @@ hipError_t launch_stream_read(const uint8_t* src, uint64_t bytes, int wgs, int l
 hipError_t launch_decode_mixed(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* s_w,
                                const uint16_t* W16, int64_t N, float tau, void* out, int out_dtype,
                                const DecodeStages& stages, hipStream_t st);
+// The same with the outlier set = the k columns of largest column maximum
+// (ties: lower column first); needs decode_supported(M, K) and
+// 0 <= k <= min(K, decode_topk_max()).
+int64_t decode_topk_max();
+hipError_t launch_decode_topk(const uint16_t* X, int64_t M, int64_t K, int64_t k, const int8_t* Wq, const float* s_w,
+                              const uint16_t* W16, int64_t N, void* out, int out_dtype, const DecodeStages& stages,
+                              hipStream_t st);
 
 hipError_t launch_gemm_w4a4(const uint32_t* Xp, const float* s_x, const uint32_t* Wp,
                             const float* s_w, int64_t M, int64_t K, int64_t N, int G, void* out,

@@ -36,7 +36,8 @@ def check_topk(qa, X, k, scratch=None):
 # ============================================================ top-k set
 @pytest.mark.parametrize("M,K,k", [(1, 8, 0), (1, 8, 3), (1, 8, 8), (3, 40, 5), (37, 520, 13), (130, 1032, 40),
                                    (257, 4096, 41), (257, 4096, 82), (300, 8192, 164), (16, 32768, 655),
-                                   (5, 32768, 32768)])
+                                   (5, 32768, 32768), (16, 8192, 300), (7, 8000, 8000), (17, 1000, 30),
+                                   (2, 65536 // 2, 100)])
 def test_topk_set_shapes(qa, M, K, k):
     X, _, _ = synthetic.mixed_inputs(M, K, 1, seed=M * 11 + K + k, n_dims=min(9, K // 8), p_token=0.5)
     check_topk(qa, X, k)
@@ -50,8 +51,9 @@ def test_topk_set_with_ties(qa, k):
     check_topk(qa, X, k)
 
 
-def test_topk_zero_columns_and_dirty_scratch(qa):
-    X = np.zeros((20, 1024), np.float16)
+@pytest.mark.parametrize("M", [20, 8])
+def test_topk_zero_columns_and_dirty_scratch(qa, M):
+    X = np.zeros((M, 1024), np.float16)
     X[3, 700] = 2.0
     X[5, 10] = -2.0
     X[7, 999] = 0.5
@@ -96,13 +98,42 @@ def test_topk_linear_shapes(qa, M, K, N, k, pass_w16):
     _topk_case(qa, X, W, k, 0, pass_w16)
 
 
-@pytest.mark.parametrize("M,K,N,k,pass_w16", [(4, 8192, 40, 30, False), (3, 8192, 20, 200, True),
-                                              (16, 2048, 70, 100, False), (12, 8192, 24, 140, False)])
+@pytest.mark.parametrize("M,K,N,k,pass_w16", [(12, 8192, 24, 140, False), (5, 4096, 50, 300, False),
+                                              (16, 2048, 70, 257, True), (2, 4112, 33, 20, False)])
 def test_topk_linear_gemv_shapes(qa, M, K, N, k, pass_w16):
-    # decode sizes: the GEMV with codes in LDS (or per wave past 64 KB), one
-    # or two staging passes of the fp16 product
+    # decode sizes outside the fused kernel (M > 8 at K > 4096, k > 256, K not
+    # a multiple of 256): the GEMV with codes in LDS (or per wave past 64 KB),
+    # one or two staging passes of the fp16 product
     X, W, _ = synthetic.mixed_inputs(M, K, N, seed=M * 3 + k, n_dims=6, p_token=0.9)
     _topk_case(qa, X, W, k, 1, pass_w16)
+
+
+@pytest.mark.parametrize("M,K,N,k,pass_w16", [(4, 8192, 40, 30, False), (3, 8192, 20, 200, True),
+                                              (16, 2048, 70, 100, False), (8, 8192, 48, 256, False),
+                                              (1, 256, 16, 1, True), (9, 4096, 100, 82, False)])
+def test_topk_linear_decode_shapes(qa, M, K, N, k, pass_w16):
+    # the fused decode kernel (M <= 16, K <= 4096, or M <= 8, K <= 8192, k <= 256)
+    X, W, _ = synthetic.mixed_inputs(M, K, N, seed=M * 5 + k, n_dims=6, p_token=0.9)
+    _topk_case(qa, X, W, k, 1, pass_w16)
+
+
+@pytest.mark.parametrize("M,K,k", [(8, 256, 5), (8, 256, 256), (3, 1024, 100), (16, 4096, 256), (5, 8192, 77),
+                                   (8, 8192, 256), (2, 512, 0), (4, 768, 13)])
+def test_topk_linear_decode_ties(qa, M, K, k):
+    # small integers: few distinct column maxima, so the k-th falls inside a
+    # run of equal keys that the fused kernel must split in column order
+    rng = np.random.default_rng(M * 1000 + K + k)
+    X = rng.integers(-5, 6, size=(M, K)).astype(np.float16)
+    _, W, _ = synthetic.mixed_inputs(1, K, 40, seed=k, n_dims=0)
+    _topk_case(qa, X, W, k, 0, False)
+
+
+@pytest.mark.parametrize("k", [0, 3, 256])
+def test_topk_linear_decode_zero_input(qa, k):
+    # every key 0: all ties, taken from column 0 up
+    X = np.zeros((6, 1024), np.float16)
+    _, W, _ = synthetic.mixed_inputs(1, 1024, 24, seed=3, n_dims=0)
+    _topk_case(qa, X, W, k, 1, True)
 
 
 @pytest.mark.parametrize("out_dtype", [0, 1, 2])
