@@ -483,7 +483,7 @@ __device__ __forceinline__ u32x2 codes8_static(const float* x, u32x2 mk, float s
 
 constexpr int RQ_FLAG_WORDS = 2048;             // merged flag words in LDS: K <= 131072
 
-template <int NC, bool STATIC, int MASK>
+template <int NC, bool STATIC, int MASK, int WPR>
 __global__ __launch_bounds__(256) void k_rowquant_i8(const uint16_t* __restrict__ X, int64_t rows, int64_t K,
                                                      const uint8_t* __restrict__ mask, int nseg, int qmin, int qmax,
                                                      const float* __restrict__ s_in, const int32_t* __restrict__ z_in,
@@ -495,18 +495,37 @@ __global__ __launch_bounds__(256) void k_rowquant_i8(const uint16_t* __restrict_
     __shared__ uint32_t wpre[MASK == MASK_FLAGS && NC > 0 ? RQ_FLAG_WORDS : 1];
     __shared__ uint32_t wtot[4];
     __shared__ int wsum[4];
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + wave_id();
+    __shared__ uint32_t pmx[WPR > 1 ? 4 : 1];
+    static_assert(WPR == 1 || (WPR == 2 && NC >= 2), "two waves per row need a row held in registers");
+    constexpr int NCW = NC / WPR;                     // chunks per lane of this wave
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int64_t row = (int64_t)blockIdx.x * (4 / WPR) + wave / WPR;
+    const int part = wave % WPR;                      // which half of the row (WPR == 2)
     const bool live = row < rows;
+    // chunk i of this lane: the wave's part of the row, lane-interleaved
+    auto cho = [&](int i) -> int64_t { return (int64_t)part * 64 * NCW + lane + 64 * i; };
     const int64_t nch = K >> 3;
     const rsrc_t rx = make_rsrc(X + (live ? row : 0) * K, live ? K * 2 : 0);
-    // A row held in registers is loaded before the flag merge below, so the
-    // two latencies overlap (loads retire in order: waiting for the flag
-    // words also waits for these).
-    u32x4 vpre[NC > 0 ? NC : 1];
+    // With the row held in registers (K <= 8192: at most 128 flag words, one
+    // per thread) the flag words are requested first and the row right after
+    // them; loads retire in order, so the flag merge waits only for the flag
+    // words, and the block barrier behind it waits only for LDS traffic.  Each
+    // wave then waits for its own row alone, not for the slowest of the block.
+    constexpr bool EARLY = MASK == MASK_FLAGS && NC > 0;
+    u32x2 fpre[EARLY ? OC_SEG_MAX : 1];
+    if constexpr (EARLY) {
+        const int64_t nw = (K + 63) / 64;
+        const rsrc_t rf = make_rsrc(mask, (int64_t)nseg * nw * 8);
+        const bool mine = (int64_t)threadIdx.x < nw;
+#pragma unroll
+        for (int sg = 0; sg < OC_SEG_MAX; ++sg)
+            fpre[sg] = bload8(rf, mine && sg < nseg ? (uint32_t)(sg * nw + threadIdx.x) * 8 : kOOB);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    u32x4 vpre[NC > 0 ? NCW : 1];
     if constexpr (NC > 0) {
 #pragma unroll
-        for (int i = 0; i < NC; ++i) vpre[i] = bload16(rx, (uint32_t)(lane + 64 * i) * 16);
+        for (int i = 0; i < NCW; ++i) vpre[i] = bload16(rx, (uint32_t)cho(i) * 16);
     }
     if constexpr (MASK == MASK_FLAGS) {
         const uint32_t b = threadIdx.x;              // keep words of an 8-bit outlier pattern
@@ -520,15 +539,25 @@ __global__ __launch_bounds__(256) void k_rowquant_i8(const uint16_t* __restrict_
         // thread t merges the flag words [t per, (t + 1) per)
         const int64_t per = (nw + 255) / 256, w0 = (int64_t)threadIdx.x * per, w1 = w0 + per < nw ? w0 + per : nw;
         uint32_t own = 0u;
-        for (int64_t w = w0; w < w1; ++w) {
+        if constexpr (EARLY) {
+            // merged in every thread (threads past the last word read zeros),
+            // so the loads above are not moved into a branch behind the row's
             unsigned long long f = 0ull;
 #pragma unroll
-            for (int sg = 0; sg < OC_SEG_MAX; ++sg) {         // all loads in flight at once
-                const u32x2 a = bload8(rf, sg < nseg ? (uint32_t)(sg * nw + w) * 8 : kOOB);
-                f |= a[0] | ((unsigned long long)a[1] << 32);
+            for (int sg = 0; sg < OC_SEG_MAX; ++sg) f |= fpre[sg][0] | ((unsigned long long)fpre[sg][1] << 32);
+            own = (uint32_t)__popcll(f);
+            if (w0 < w1) flw[w0] = f;
+        } else {
+            for (int64_t w = w0; w < w1; ++w) {
+                unsigned long long f = 0ull;
+#pragma unroll
+                for (int sg = 0; sg < OC_SEG_MAX; ++sg) {         // all loads in flight at once
+                    const u32x2 a = bload8(rf, sg < nseg ? (uint32_t)(sg * nw + w) * 8 : kOOB);
+                    f |= a[0] | ((unsigned long long)a[1] << 32);
+                }
+                flw[w] = f;
+                own += (uint32_t)__popcll(f);
             }
-            flw[w] = f;
-            own += (uint32_t)__popcll(f);
         }
         if constexpr (NC > 0) {
             if (xo) {
@@ -548,14 +577,26 @@ __global__ __launch_bounds__(256) void k_rowquant_i8(const uint16_t* __restrict_
                 }
             }
         }
-        __syncthreads();
+        if constexpr (EARLY) {
+            // LDS writes done, then the barrier; the row loads stay in flight
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_waitcnt(0xC07F);      // gfx9 encoding: lgkmcnt(0) only
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        } else {
+            __syncthreads();
+        }
         if (blockIdx.x == 0)
             outlier_compact([&](int64_t w) -> unsigned long long { return w < nw ? flw[w] : 0ull; }, nullptr, 0, K,
                             nullptr, idx, count, nullptr, wsum);
     }
     if constexpr (MASK == MASK_NONE)
         if (count && blockIdx.x == 0 && threadIdx.x == 0) *count = 0;
-    if (!live) return;
+    // (with two waves per row and a dynamic scale, every wave reaches the
+    // exchange of the row maximum below first)
+    constexpr bool XCHG = WPR > 1 && !STATIC;
+    if constexpr (!XCHG)
+        if (!live) return;
     const rsrc_t rm = make_rsrc(mask, MASK == MASK_BYTES ? K : 0);
     const uint8_t* flb = reinterpret_cast<const uint8_t*>(flw);
     int8_t* qr = q + row * K;
@@ -580,43 +621,56 @@ __global__ __launch_bounds__(256) void k_rowquant_i8(const uint16_t* __restrict_
         mask_of(ch, v, mk);
     };
     if constexpr (NC > 0) {
-        u32x4 v[NC];
-        u32x2 mk[NC];
-        uint32_t fbv[NC];
+        u32x4 v[NCW];
+        u32x2 mk[NCW];
+        uint32_t fbv[NCW];
 #pragma unroll
-        for (int i = 0; i < NC; ++i) {
+        for (int i = 0; i < NCW; ++i) {
             v[i] = vpre[i];
-            mask_of(lane + 64 * i, v[i], mk[i]);
+            mask_of(cho(i), v[i], mk[i]);
             fbv[i] = fbl;
         }
         if constexpr (!STATIC) {
-            float amax = 0.0f;
+            // the row maximum as a non-negative float's bit pattern (these
+            // order like the values), combined over the row's waves
+            uint32_t ab;
             if constexpr (MASK == MASK_BYTES) {
+                float a = 0.0f;
 #pragma unroll
-                for (int i = 0; i < NC; ++i) {
+                for (int i = 0; i < NCW; ++i) {
                     float x[8];
                     unpack8(v[i], x);
                     apply_mask(x, mk[i]);
-                    amax = fmaxf(amax, absmax8(x));
+                    a = fmaxf(a, absmax8(x));
                 }
-                amax = wave_max(amax);
+                ab = __builtin_bit_cast(uint32_t, wave_max(a));
             } else {
                 // on the sign-cleared fp16 patterns (they order like the
                 // magnitudes), two per instruction; DPP lane reduction
                 uint32_t am = 0u;
 #pragma unroll
-                for (int i = 0; i < NC; ++i)
+                for (int i = 0; i < NCW; ++i)
 #pragma unroll
                     for (int d = 0; d < 4; ++d) am = pk_max_u16(am, v[i][d] & 0x7fff7fffu);
-                amax = h2f((uint16_t)wave_max_u32(max(am & 0xffffu, am >> 16)));
+                ab = __builtin_bit_cast(uint32_t, h2f((uint16_t)wave_max_u32(max(am & 0xffffu, am >> 16))));
             }
+            if constexpr (XCHG) {
+                if (lane == 0) pmx[wave] = ab;
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_s_waitcnt(0xC07F);      // gfx9 encoding: lgkmcnt(0) only
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+                ab = max(pmx[wave & ~1], pmx[wave | 1]);
+                if (!live) return;
+            }
+            const float amax = __builtin_bit_cast(float, ab);
             s = amax == 0.0f ? 1.0f : amax / (float)qmax;
             r = 1.0f / s;
-            if (lane == 0) s_out[row] = s;
+            if (lane == 0 && part == 0) s_out[row] = s;
         }
 #pragma unroll
-        for (int i = 0; i < NC; ++i) {
-            const int64_t ch = lane + 64 * i;
+        for (int i = 0; i < NCW; ++i) {
+            const int64_t ch = cho(i);
             if (ch < nch) {
                 u32x2 c;
                 if constexpr (STATIC) {
@@ -641,8 +695,8 @@ __global__ __launch_bounds__(256) void k_rowquant_i8(const uint16_t* __restrict_
             const uint32_t t0 = wtot[0], t1 = wtot[1], t2 = wtot[2];
             if (xo && t0 + t1 + t2 + wtot[3] > 0u) {
 #pragma unroll
-                for (int i = 0; i < NC; ++i) {
-                    const int64_t ch = lane + 64 * i;
+                for (int i = 0; i < NCW; ++i) {
+                    const int64_t ch = cho(i);
                     const uint32_t fb = fbv[i];
                     if (fb) {
                         const int64_t w = ch >> 3;
@@ -701,10 +755,14 @@ template <bool STATIC, int MASK>
 static void rowquant_dispatch(const uint16_t* X, int64_t rows, int64_t K, const uint8_t* mask, int nseg, int qmin,
                               int qmax, const float* s_in, const int32_t* z_in, int8_t* q, float* s_out, int32_t* idx,
                               int32_t* count, hipStream_t st, uint16_t* xo = nullptr) {
-    const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+    // two waves per row when the row is held in registers in two or more
+    // chunks per lane (more waves in flight, half the dependent work per wave)
     const int64_t nch = K / 8;
-#define QA_RQ(NC) hipLaunchKernelGGL((k_rowquant_i8<NC, STATIC, MASK>), grid, block, 0, st, X, rows, K, mask, nseg, \
-                                     qmin, qmax, s_in, z_in, q, s_out, idx, count, xo)
+    const int wpr = nch > 64 && nch <= 1024 ? 2 : 1;
+    const dim3 grid((unsigned)((rows + 4 / wpr - 1) / (4 / wpr))), block(256);
+#define QA_RQ_W(NC, W) hipLaunchKernelGGL((k_rowquant_i8<NC, STATIC, MASK, W>), grid, block, 0, st, X, rows, K, mask, \
+                                          nseg, qmin, qmax, s_in, z_in, q, s_out, idx, count, xo)
+#define QA_RQ(NC) QA_RQ_W(NC, (NC >= 2 ? 2 : 1))
     if (nch <= 64) QA_RQ(1);
     else if (nch <= 128) QA_RQ(2);
     else if (nch <= 256) QA_RQ(4);
@@ -712,6 +770,7 @@ static void rowquant_dispatch(const uint16_t* X, int64_t rows, int64_t K, const 
     else if (nch <= 1024) QA_RQ(16);
     else QA_RQ(0);
 #undef QA_RQ
+#undef QA_RQ_W
 }
 
 hipError_t launch_rowquant_i8(const uint16_t* X, int64_t rows, int64_t K, const uint8_t* mask, int qmin, int qmax,
