@@ -491,16 +491,17 @@ __global__ __launch_bounds__(256) void k_rowquant_i8(const uint16_t* __restrict_
                                                      int32_t* __restrict__ idx, int32_t* __restrict__ count,
                                                      uint16_t* __restrict__ xo) {
     __shared__ u32x4 lut[MASK == MASK_FLAGS ? 256 : 1];
-    __shared__ unsigned long long flw[MASK == MASK_FLAGS ? RQ_FLAG_WORDS : 1];
-    __shared__ uint32_t wpre[MASK == MASK_FLAGS && NC > 0 ? RQ_FLAG_WORDS : 1];
+    // (a row held in registers has K <= 8192: at most 128 flag words)
+    __shared__ unsigned long long flw[MASK == MASK_FLAGS ? (NC > 0 ? 128 : RQ_FLAG_WORDS) : 1];
+    __shared__ uint32_t wpre[MASK == MASK_FLAGS && NC > 0 ? 128 : 1];
     __shared__ uint32_t wtot[4];
     __shared__ int wsum[4];
     __shared__ uint32_t pmx[WPR > 1 ? 4 : 1];
-    static_assert(WPR == 1 || (WPR == 2 && NC >= 2), "two waves per row need a row held in registers");
+    static_assert(WPR == 1 || ((WPR == 2 || WPR == 4) && NC >= WPR), "waves per row need a row held in registers");
     constexpr int NCW = NC / WPR;                     // chunks per lane of this wave
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int64_t row = (int64_t)blockIdx.x * (4 / WPR) + wave / WPR;
-    const int part = wave % WPR;                      // which half of the row (WPR == 2)
+    const int part = wave % WPR;                      // which part of the row
     const bool live = row < rows;
     // chunk i of this lane: the wave's part of the row, lane-interleaved
     auto cho = [&](int i) -> int64_t { return (int64_t)part * 64 * NCW + lane + 64 * i; };
@@ -578,11 +579,7 @@ __global__ __launch_bounds__(256) void k_rowquant_i8(const uint16_t* __restrict_
             }
         }
         if constexpr (EARLY) {
-            // LDS writes done, then the barrier; the row loads stay in flight
-            asm volatile("" ::: "memory");
-            __builtin_amdgcn_s_waitcnt(0xC07F);      // gfx9 encoding: lgkmcnt(0) only
-            __builtin_amdgcn_s_barrier();
-            asm volatile("" ::: "memory");
+            lds_only_barrier();                      // the row loads stay in flight
         } else {
             __syncthreads();
         }
@@ -655,12 +652,10 @@ __global__ __launch_bounds__(256) void k_rowquant_i8(const uint16_t* __restrict_
                 ab = __builtin_bit_cast(uint32_t, h2f((uint16_t)wave_max_u32(max(am & 0xffffu, am >> 16))));
             }
             if constexpr (XCHG) {
-                if (lane == 0) pmx[wave] = ab;
-                asm volatile("" ::: "memory");
-                __builtin_amdgcn_s_waitcnt(0xC07F);      // gfx9 encoding: lgkmcnt(0) only
-                __builtin_amdgcn_s_barrier();
-                asm volatile("" ::: "memory");
-                ab = max(pmx[wave & ~1], pmx[wave | 1]);
+                if (lane == 0) pmx[wave] = ab & 0x7fffffffu;      // (a -0.0 maximum would order last)
+                lds_only_barrier();
+#pragma unroll
+                for (int q = 0; q < WPR; ++q) ab = max(ab, pmx[wave - part + q]);
                 if (!live) return;
             }
             const float amax = __builtin_bit_cast(float, ab);
@@ -755,14 +750,15 @@ template <bool STATIC, int MASK>
 static void rowquant_dispatch(const uint16_t* X, int64_t rows, int64_t K, const uint8_t* mask, int nseg, int qmin,
                               int qmax, const float* s_in, const int32_t* z_in, int8_t* q, float* s_out, int32_t* idx,
                               int32_t* count, hipStream_t st, uint16_t* xo = nullptr) {
-    // two waves per row when the row is held in registers in two or more
-    // chunks per lane (more waves in flight, half the dependent work per wave)
+    // several waves per row when the row is held in registers in two or more
+    // chunks per lane (more waves in flight, less dependent work per wave):
+    // two for 2 to 8 chunks, four for 16 (four measured slightly slower at 8)
     const int64_t nch = K / 8;
-    const int wpr = nch > 64 && nch <= 1024 ? 2 : 1;
+    const int wpr = nch > 512 && nch <= 1024 ? 4 : nch > 64 && nch <= 512 ? 2 : 1;
     const dim3 grid((unsigned)((rows + 4 / wpr - 1) / (4 / wpr))), block(256);
 #define QA_RQ_W(NC, W) hipLaunchKernelGGL((k_rowquant_i8<NC, STATIC, MASK, W>), grid, block, 0, st, X, rows, K, mask, \
                                           nseg, qmin, qmax, s_in, z_in, q, s_out, idx, count, xo)
-#define QA_RQ(NC) QA_RQ_W(NC, (NC >= 2 ? 2 : 1))
+#define QA_RQ(NC) QA_RQ_W(NC, (NC >= 16 ? 4 : NC >= 2 ? 2 : 1))
     if (nch <= 64) QA_RQ(1);
     else if (nch <= 128) QA_RQ(2);
     else if (nch <= 256) QA_RQ(4);
@@ -808,9 +804,9 @@ hipError_t launch_rowquant_i8_no_outliers(const uint16_t* X, int64_t rows, int64
 // Asymmetric (zero-point) row quantization: per row, the min-max grid over
 // [lo, hi] = [min(min x, 0), max(max x, 0)]: s = fl32(fl32(hi - lo) / (qmax -
 // qmin)) (1.0 when hi == lo), z = clip(qmin - rint(fl32(lo / s))), codes
-// clip(rint(fl32(x / s)) + z), and the row sum of the codes (int32).  One
-// wave per row as in k_rowquant_i8 (chunks past the row read 0, which is in
-// the range anyway).
+// clip(rint(fl32(x / s)) + z), and the row sum of the codes (int32).  WPR
+// waves per row as in k_rowquant_i8, combining their minima, maxima and code
+// sums through LDS (chunks past the row read 0, which is in the range anyway).
 // Codes: |x / s| <= (qmax - qmin)(1 + 2^-23) <= 255.0001, so t = fma(x, r, 256)
 // with r = fl32(1/s) lies in (0, 512): |x r - x/s| <= 255.0001 * 2^-24, the
 // rounding of t adds at most 2^-16 and fl(x/s) is within 2^-17 of x/s, so
@@ -855,24 +851,30 @@ __device__ __forceinline__ int wave_sum_i32(int v) {
     return v;
 }
 
-template <int NC>
+template <int NC, int WPR>
 __global__ __launch_bounds__(256) void k_rowquant_i8_asym(const uint16_t* __restrict__ X, int64_t rows, int64_t K,
                                                           int qmin, int qmax, int8_t* __restrict__ q,
                                                           float* __restrict__ s_out, int32_t* __restrict__ z_out,
                                                           int32_t* __restrict__ rowsum) {
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + wave_id();
-    if (row >= rows) return;
+    static_assert(WPR == 1 || ((WPR == 2 || WPR == 4) && NC >= WPR), "waves per row need a row held in registers");
+    constexpr int NCW = NC / WPR;
+    __shared__ uint32_t xr[WPR > 1 ? 3 : 1][4];
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int64_t row = (int64_t)blockIdx.x * (4 / WPR) + wave / WPR;
+    const int part = wave % WPR;
+    const bool live = row < rows;
+    if (WPR == 1 && !live) return;                    // (several waves per row all reach the exchanges)
     const int64_t nch = K >> 3;
-    const rsrc_t rx = make_rsrc(X + row * K, K * 2);
+    const rsrc_t rx = make_rsrc(X + (live ? row : 0) * K, live ? K * 2 : 0);
     int8_t* qr = q + row * K;
     float lo = 0.0f, hi = 0.0f;
-    u32x4 v[NC > 0 ? NC : 1];
+    u32x4 v[NC > 0 ? NCW : 1];
+    auto cho = [&](int i) -> int64_t { return (int64_t)part * 64 * NCW + lane + 64 * i; };
     if constexpr (NC > 0) {
 #pragma unroll
-        for (int i = 0; i < NC; ++i) v[i] = bload16(rx, (uint32_t)(lane + 64 * i) * 16);
+        for (int i = 0; i < NCW; ++i) v[i] = bload16(rx, (uint32_t)cho(i) * 16);
 #pragma unroll
-        for (int i = 0; i < NC; ++i) {
+        for (int i = 0; i < NCW; ++i) {
             float x[8];
             unpack8(v[i], x);
             minmax8(x, lo, hi);
@@ -886,15 +888,33 @@ __global__ __launch_bounds__(256) void k_rowquant_i8_asym(const uint16_t* __rest
     }
     hi = wave_max(hi);
     lo = -wave_max(-lo);
+    if constexpr (WPR > 1) {
+        // hi >= 0 and -lo >= 0: with the sign bit cleared (a part of the row
+        // that is all zeros gives -lo = -0.0, whose pattern is 0x80000000)
+        // their bit patterns order like the values
+        if (lane == 0) {
+            xr[0][wave] = __builtin_bit_cast(uint32_t, hi) & 0x7fffffffu;
+            xr[1][wave] = __builtin_bit_cast(uint32_t, -lo) & 0x7fffffffu;
+        }
+        lds_only_barrier();
+        uint32_t h = 0u, l = 0u;
+#pragma unroll
+        for (int w = 0; w < WPR; ++w) {
+            h = max(h, xr[0][wave - part + w]);
+            l = max(l, xr[1][wave - part + w]);
+        }
+        hi = __builtin_bit_cast(float, h);
+        lo = -__builtin_bit_cast(float, l);
+    }
     const float s = hi != lo ? (hi - lo) / (float)(qmax - qmin) : 1.0f;
     const int z = clampi(qmin - (int)__builtin_rintf(lo / s), qmin, qmax);
     const float r = 1.0f / s;
     int sum = 0;
     if constexpr (NC > 0) {
 #pragma unroll
-        for (int i = 0; i < NC; ++i) {
-            const int64_t ch = lane + 64 * i;
-            if (ch < nch) {
+        for (int i = 0; i < NCW; ++i) {
+            const int64_t ch = cho(i);
+            if (live && ch < nch) {
                 float x[8];
                 unpack8(v[i], x);
                 st_codes8(qr + ch * 8, codes8_asym(x, s, r, z, qmin, qmax, sum));
@@ -908,6 +928,14 @@ __global__ __launch_bounds__(256) void k_rowquant_i8_asym(const uint16_t* __rest
         }
     }
     sum = wave_sum_i32(sum);
+    if constexpr (WPR > 1) {
+        if (lane == 0) xr[2][wave] = (uint32_t)sum;
+        lds_only_barrier();
+        sum = 0;
+#pragma unroll
+        for (int w = 0; w < WPR; ++w) sum += (int)xr[2][wave - part + w];
+        if (!live || part != 0) return;
+    }
     if (lane == 0) {
         s_out[row] = s;
         z_out[row] = z;
@@ -917,10 +945,12 @@ __global__ __launch_bounds__(256) void k_rowquant_i8_asym(const uint16_t* __rest
 
 hipError_t launch_rowquant_i8_asym(const uint16_t* X, int64_t rows, int64_t K, int qmin, int qmax, int8_t* q,
                                    float* s_out, int32_t* z_out, int32_t* rowsum, hipStream_t st) {
-    const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+    // waves per row as in the symmetric quantizer
     const int64_t nch = K / 8;
-#define QA_RA(NC) hipLaunchKernelGGL((k_rowquant_i8_asym<NC>), grid, block, 0, st, X, rows, K, qmin, qmax, q, s_out, \
-                                     z_out, rowsum)
+    const int wpr = nch > 512 && nch <= 1024 ? 4 : nch > 64 && nch <= 512 ? 2 : 1;
+    const dim3 grid((unsigned)((rows + 4 / wpr - 1) / (4 / wpr))), block(256);
+#define QA_RA(NC) hipLaunchKernelGGL((k_rowquant_i8_asym<NC, (NC >= 16 ? 4 : NC >= 2 ? 2 : 1)>), grid, block, 0, st, X, \
+                                     rows, K, qmin, qmax, q, s_out, z_out, rowsum)
     if (nch <= 64) QA_RA(1);
     else if (nch <= 128) QA_RA(2);
     else if (nch <= 256) QA_RA(4);

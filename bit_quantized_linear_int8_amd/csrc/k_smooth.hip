@@ -35,10 +35,11 @@ hipError_t launch_smooth_factors(const float* cx, const float* cw, int64_t K, fl
 }
 
 // ---------------------------------------------------------------------------
-// Smoothing + int8 quantization.  One wave per row (four rows per 256-thread
-// block); lane l owns the 8-column chunks l + 64 i.  NC > 0 holds the smoothed
-// row in registers (K <= 512 NC) and reads X once; NC == 0 reads the row twice
-// (absmax pass, codes pass).  The factor vector is read with the row (it is
+// Smoothing + int8 quantization.  NC > 0 holds the smoothed row in registers
+// (K <= 512 NC) and reads X once, split over WPR waves (part p of the row's
+// WPR waves owns chunks p 64 NC / WPR + l + 64 i in lane l), which combine
+// their row maxima through LDS; NC == 0 is one wave per row, lane l owning
+// the chunks l + 64 i, and reads the row twice (absmax pass, codes pass).  The factor vector is read with the row (it is
 // shared by every row, so after the first rows it comes from the caches).
 //
 // Phases:
@@ -64,16 +65,22 @@ __device__ __forceinline__ void smooth8(const u32x4& v, const u32x4& f0, const u
     }
 }
 
-template <int NC, int OP, int PHASE>
+template <int NC, int OP, int PHASE, int WPR>
 __global__ __launch_bounds__(256) void k_smoothquant_i8(const uint16_t* __restrict__ X, int64_t rows, int64_t K,
                                                         const float* __restrict__ sm, int8_t* __restrict__ q,
                                                         float* __restrict__ s_out, int32_t* __restrict__ count) {
+    static_assert(WPR == 1 || ((WPR == 2 || WPR == 4) && NC >= WPR), "waves per row need a row held in registers");
+    constexpr int NCW = NC / WPR;
+    constexpr bool XCHG = WPR > 1 && PHASE != SQ_CODES;      // row maxima combined over the row's waves
+    __shared__ uint32_t pmx[XCHG ? 4 : 1];
     if (PHASE != SQ_ROWMAX && count && blockIdx.x == 0 && threadIdx.x == 0) *count = 0;
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + wave_id();
-    if (row >= rows) return;
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int64_t row = (int64_t)blockIdx.x * (4 / WPR) + wave / WPR;
+    const int part = wave % WPR;
+    const bool live = row < rows;
+    if (!XCHG && !live) return;
     const int64_t nch = K >> 3;
-    const rsrc_t rx = make_rsrc(X + row * K, K * 2);
+    const rsrc_t rx = make_rsrc(X + (live ? row : 0) * K, live ? K * 2 : 0);
     const rsrc_t rs = make_rsrc(sm, K * 4);
     int8_t* qr = q + row * K;
     float s = 1.0f, r = 1.0f;
@@ -81,43 +88,58 @@ __global__ __launch_bounds__(256) void k_smoothquant_i8(const uint16_t* __restri
         s = s_out[row];
         r = 1.0f / s;
     }
+    auto cho = [&](int i) -> int64_t { return (int64_t)part * 64 * NCW + lane + 64 * i; };
     auto load_smooth = [&](int64_t ch, float* x) {
         const u32x4 v = bload16(rx, (uint32_t)ch * 16);
         const u32x4 f0 = bload16(rs, (uint32_t)ch * 32);
         const u32x4 f1 = bload16(rs, (uint32_t)ch * 32 + 16);
         smooth8<OP>(v, f0, f1, ch < nch, x);
     };
-    auto finish_scale = [&](float amax) {
+    // returns false in the waves of a row past the end (after the exchange)
+    auto finish_scale = [&](float amax) -> bool {
         amax = wave_max(amax);
+        if constexpr (XCHG) {
+            // amax >= 0: with the sign bit cleared (-0.0 would order last)
+            // its bit pattern orders like the value
+            if (lane == 0) pmx[wave] = __builtin_bit_cast(uint32_t, amax) & 0x7fffffffu;
+            lds_only_barrier();
+            uint32_t ab = 0u;
+#pragma unroll
+            for (int w = 0; w < WPR; ++w) ab = max(ab, pmx[wave - part + w]);
+            amax = __builtin_bit_cast(float, ab);
+            if (!live) return false;
+        }
         if constexpr (PHASE == SQ_ROWMAX) {
-            if (lane == 0) s_out[row] = amax;
+            if (lane == 0 && part == 0) s_out[row] = amax;
         } else {
             s = amax == 0.0f ? 1.0f : amax / 127.0f;
             r = 1.0f / s;
-            if (lane == 0) s_out[row] = s;
+            if (lane == 0 && part == 0) s_out[row] = s;
         }
+        return true;
     };
     if constexpr (NC > 0) {
-        float x[NC][8];
-        u32x4 v[NC], f0[NC], f1[NC];
+        float x[NCW][8];
+        u32x4 v[NCW], f0[NCW], f1[NCW];
 #pragma unroll
-        for (int i = 0; i < NC; ++i) {                 // every load of the row in flight at once
-            const uint32_t ch = (uint32_t)(lane + 64 * i);
+        for (int i = 0; i < NCW; ++i) {                // every load of the wave's part in flight at once
+            const uint32_t ch = (uint32_t)cho(i);
             v[i] = bload16(rx, ch * 16);
             f0[i] = bload16(rs, ch * 32);
             f1[i] = bload16(rs, ch * 32 + 16);
         }
         float amax = 0.0f;
 #pragma unroll
-        for (int i = 0; i < NC; ++i) {
-            smooth8<OP>(v[i], f0[i], f1[i], lane + 64 * i < nch, x[i]);
+        for (int i = 0; i < NCW; ++i) {
+            smooth8<OP>(v[i], f0[i], f1[i], live && cho(i) < nch, x[i]);
             if constexpr (PHASE != SQ_CODES) amax = fmaxf(amax, absmax8f(x[i]));
         }
-        if constexpr (PHASE != SQ_CODES) finish_scale(amax);
+        if constexpr (PHASE != SQ_CODES)
+            if (!finish_scale(amax)) return;
         if constexpr (PHASE != SQ_ROWMAX) {
 #pragma unroll
-            for (int i = 0; i < NC; ++i) {
-                const int64_t ch = lane + 64 * i;
+            for (int i = 0; i < NCW; ++i) {
+                const int64_t ch = cho(i);
                 if (ch < nch) st_codes8(qr + ch * 8, codes8_dyn(x[i], s, r));
             }
         }
@@ -162,10 +184,14 @@ __global__ __launch_bounds__(1024) void k_tensor_scale(float* __restrict__ s, in
 template <int OP, int PHASE>
 static void smoothquant_dispatch(const uint16_t* X, int64_t rows, int64_t K, const float* sm, int8_t* q,
                                  float* s_out, int32_t* count, hipStream_t st) {
-    const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+    // four waves per row for rows of 16 chunks per lane, else one (two waves
+    // per row measured slightly slower on 8 chunks, where the per-value
+    // division dominates)
     const int64_t nch = K / 8;
-#define QA_SQ(NC) hipLaunchKernelGGL((k_smoothquant_i8<NC, OP, PHASE>), grid, block, 0, st, X, rows, K, sm, q, s_out, \
-                                     count)
+    const int wpr = nch > 512 && nch <= 1024 ? 4 : 1;
+    const dim3 grid((unsigned)((rows + 4 / wpr - 1) / (4 / wpr))), block(256);
+#define QA_SQ(NC) hipLaunchKernelGGL((k_smoothquant_i8<NC, OP, PHASE, (NC >= 16 ? 4 : 1)>), grid, block, 0, st, X, \
+                                     rows, K, sm, q, s_out, count)
     if (nch <= 64) QA_SQ(1);
     else if (nch <= 128) QA_SQ(2);
     else if (nch <= 256) QA_SQ(4);

@@ -187,6 +187,16 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return max(a, b);
 }
 
+// Workgroup barrier that waits for this wave's LDS accesses only (gfx9
+// s_waitcnt encoding lgkmcnt(0)); its global loads and stores stay in flight.
+// The memory clobbers keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_only_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Number of set bits of a 64-bit lane mask held by lanes below this one.
 __device__ __forceinline__ int bits_below(uint64_t m) {
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));

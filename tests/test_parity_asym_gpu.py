@@ -34,12 +34,32 @@ def check_asym_rows(qa, X, q_min=-128, q_max=127):
 
 # ============================================================ quantizer
 @pytest.mark.parametrize("rows,K", [(1, 8), (5, 24), (9, 520), (33, 1032), (17, 2056), (6, 4096), (4, 8200),
-                                    (3, 8192), (2, 16392)])
+                                    (3, 8192), (2, 16392),
+                                    # 16 chunks per lane over four waves, the last wave's chunks past the row
+                                    (7, 6000)])
 def test_asym_quant_shapes(qa, rows, K):
     X, _, _ = synthetic.mixed_inputs(rows, K, 1, seed=rows * 3 + K, n_dims=min(4, K // 8), p_token=0.75)
     if rows > 2:
         X[1, :] = 0                                        # zero row: s = 1, z = q_min
         X[2, :] = np.abs(X[2, :]) + np.float16(0.5)        # one-sided row
+    check_asym_rows(qa, X)
+
+
+@pytest.mark.parametrize("K", [4096, 8192])
+def test_asym_quant_zero_parts(qa, K):
+    # a row's parts are quantized by different waves (halves at K = 4096,
+    # quarters at K = 8192): the negative end of a row held by one part while
+    # another part is all +0.0 or all -0.0 must still set the row's range
+    rng = np.random.default_rng(K)
+    X = np.zeros((6, K), np.float16)
+    h = K // 4
+    X[0, :h] = rng.normal(0, 3, h)                    # values in the first part only
+    X[1, -h:] = rng.normal(0, 3, h)                   # values in the last part only
+    X[2, :h] = -np.abs(rng.normal(0, 3, h))           # negative first part, -0.0 elsewhere
+    X[2, h:] = np.float16(-0.0)
+    X[3, h:2 * h] = -np.abs(rng.normal(0, 3, h))      # negative second part only
+    X[4, :] = np.float16(-0.0)                        # all -0.0: the zero row's scale and zero point
+    X[5, -1] = np.float16(-7.0)                       # one negative value at the end
     check_asym_rows(qa, X)
 
 

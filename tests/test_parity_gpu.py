@@ -105,7 +105,9 @@ def test_outlier_cols_reuses_dirty_scratch(qa):
 
 # ============================================================ row quantization
 @pytest.mark.parametrize("rows,K", [(1, 8), (5, 24), (9, 520), (33, 1032), (17, 2056), (6, 4096), (4, 8200),
-                                    (3, 8192), (2, 16392)])
+                                    (3, 8192), (2, 16392),
+                                    # 16 chunks per lane over four waves, the last wave's chunks past the row
+                                    (7, 6000)])
 @pytest.mark.parametrize("with_mask", [False, True])
 def test_rowquant_dynamic(qa, rows, K, with_mask):
     X, _, _ = synthetic.mixed_inputs(rows, K, 1, seed=rows + K, n_dims=min(4, K // 8), p_token=0.75)
@@ -260,6 +262,8 @@ def test_mixed_many_outliers(qa):
     (70, 1024, 260, 300, False),     # count > 256: X gathered as well
     (40, 8208, 96, 20, True),        # K > 8192: rows not held in registers, X gathered
     (513, 1024, 1030, 40, False),    # big tiles with a tail launch, count between the prefetch and one pass
+    (37, 8192, 130, 40, True),       # rows of 16 chunks per lane quantized by four waves each, compact rows
+    (100, 6144, 260, 12, False),     # the same with a row shorter than the four waves' chunks
 ])
 def test_mixed_outlier_staging_paths(qa, M, K, N, n_dims, pass_w16):
     X, W, dims = synthetic.mixed_inputs(M, K, N, seed=M + n_dims, n_dims=n_dims, p_token=0.6,

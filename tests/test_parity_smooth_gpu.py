@@ -70,7 +70,8 @@ def test_smooth_factors_within_one_ulp(qa, alpha):
 
 
 # ============================================================ smoothing + quantization
-SHAPES = [(1, 8), (5, 24), (9, 520), (33, 1032), (17, 2056), (6, 4096), (4, 8200), (3, 8192), (2, 16392)]
+SHAPES = [(1, 8), (5, 24), (9, 520), (33, 1032), (17, 2056), (6, 4096), (4, 8200), (3, 8192), (2, 16392),
+          (7, 6000)]
 
 
 @pytest.mark.parametrize("rows,K", SHAPES)
