@@ -655,14 +655,21 @@ __global__ __launch_bounds__(2 * DEC_THREADS) void k_decode_mixed(const uint16_t
             static_cast<uint16_t*>(out)[o] = f2bf(v);
     }
 
-    // 4. workgroup 0 leaves the integer stages (outlier list, count, per-token
-    //    scales, codes) where the general path keeps them
+    // 4. the integer stages (outlier list, count, per-token scales, codes)
+    //    go where the general path keeps them: workgroup 0 writes the list,
+    //    count and scales, and every workgroup an equal share of the 16-byte
+    //    chunks of the codes (all of them hold the same codes), so that no
+    //    single workgroup carries the whole 32 KB store at the kernel's end
     if (blockIdx.x == 0) {
         for (int h = t; h < count; h += DEC_THREADS) st.idx[h] = oidx[h];
         if (t == 0) *st.count = count;
         if (t < M) st.s_x[t] = sx_s[t];
+    }
+    {
         const int cpr = K >> 4;                       // 16-byte chunks per row
-        for (int q = t; q < M * cpr; q += DEC_THREADS) {
+        const int total = M * cpr, per = (total + (int)gridDim.x - 1) / (int)gridDim.x;
+        const int q0 = (int)blockIdx.x * per, q1 = q0 + per < total ? q0 + per : total;
+        for (int q = q0 + t; q < q1; q += DEC_THREADS) {
             const int r = q / cpr, j = q - r * cpr;
             *reinterpret_cast<v4i*>(st.xq + (int64_t)r * K + 16 * j) =
                 *reinterpret_cast<const v4i*>(aq + r * LDA + 16 * j);

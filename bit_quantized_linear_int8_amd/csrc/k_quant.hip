@@ -435,9 +435,11 @@ hipError_t launch_col_absmax(const uint16_t* A, int64_t rows, int64_t K, float* 
 }
 
 // ---------------------------------------------------------------------------
-// Row-wise int8 quantization: one wave per row, 8 elements (16 bytes) per
-// lane and chunk.  NC > 0 keeps the row in registers (K <= 512 * NC); NC == 0
-// reads the row twice (absmax pass, then quantize pass).
+// Row-wise int8 quantization, 8 elements (16 bytes) per lane and chunk.
+// NC > 0 keeps the row in registers (K <= 512 * NC), split over the WPR waves
+// of the row (part p owns chunks p 64 NC / WPR + l + 64 i in lane l), which
+// combine the row maximum through LDS; NC == 0 is one wave per row and reads
+// the row twice (absmax pass, then quantize pass).
 //
 // Masks: MASK_BYTES -- caller's byte per column (nonzero = masked), applied per
 // value; MASK_FLAGS -- outlier flag bits: every workgroup ORs the outlier

@@ -137,15 +137,17 @@ def test_rowquant_ties_take_the_even_code(qa):
 
 
 @pytest.mark.parametrize("q_min,q_max", [(-128, 127), (-127, 127), (0, 15), (-8, 7)])
-def test_rowquant_static_affine(qa, q_min, q_max):
-    rng = np.random.default_rng(q_max)
-    X = (rng.normal(0, 4, (7, 264))).astype(np.float16)
+# K = 264: one wave per row; 4096 and 6000: rows split over two and four waves
+@pytest.mark.parametrize("K", [264, 4096, 6000])
+def test_rowquant_static_affine(qa, q_min, q_max, K):
+    rng = np.random.default_rng(q_max + K)
+    X = (rng.normal(0, 4, (7, K))).astype(np.float16)
     X[0, :6] = [0.5, 1.5, 2.5, -0.5, -1.5, -2.5]
     s_in = rng.uniform(0.01, 1.0, 7).astype(np.float32)
     s_in[0] = 1.0
     z_in = rng.integers(-20, 20, 7).astype(np.int32)
     z_in[0] = 0
-    mask = (rng.random(264) < 0.05).astype(np.uint8)
+    mask = (rng.random(K) < 0.05).astype(np.uint8)
     Xq, _ = qa.qa_quantize_rowwise_int8(dev(X), mask=dev(mask), q_min=q_min, q_max=q_max, s_in=dev(s_in),
                                         z_in=dev(z_in))
     oq, _ = oracle.quant_rows(X, mask=mask, qmin=q_min, qmax=q_max, s_in=s_in, z_in=z_in)
