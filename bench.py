@@ -18,9 +18,9 @@ the Kronecker-transform W4A4 linear, the W4A8 group-Hadamard linear and the
 W4A4 linear with zero-point activations (one-sided) on the W4A4 data, in int8
 TOPS against the dense int8 MFMA peak; and the SmoothQuant and top-2% linears
 at the decode shape (smooth_decode, topk_decode), in GB/s like the headline,
-each with `gemv_roofline` from its recorded kernel time (the decode-size GEMV
-k_gemv_i8_mixed for SmoothQuant; for top-k the fused decode kernel, which is
-the whole call).  Each prefill-size entry carries `gemm_roofline`:
+each with `gemv_roofline` from the recorded time of the fused decode kernel,
+which is the whole call at this shape.  Each prefill-size entry carries
+`gemm_roofline`:
 the GEMM kernels' own time per call, the sum of their average rocprofv3
 durations recorded in profiles/kernel_times.json for that workload (null while
 the record is missing or any kernel source has changed since it was taken),
@@ -474,9 +474,8 @@ def main():
                 log("[bench] %s: timing %d calls" % (name, args.steps))
                 ms, wall_ms, n = time_graph(torch, gs, args.steps, args.warmup)
                 gbs = nbytes / (ms * 1e-3) / 1e9
-                # the SmoothQuant call's product runs on the decode-size GEMV; the
-                # top-k call is one launch of the fused decode kernel
-                gus, gnames, gsrc = recorded_gemm_time(key, "k_decode_mixed" if key == "topk_decode" else "k_gemv")
+                # both calls are one launch of the fused decode kernel at this shape
+                gus, gnames, gsrc = recorded_gemm_time(key, "k_decode_mixed")
                 if gus is None:
                     gemv = {"kernel_us": None, "reason": gsrc}
                 else:

@@ -26,10 +26,17 @@
 // Its barriers wait only for LDS traffic, so the weight stream stays in
 // flight across them.
 //
+// SmoothQuant mode (SM = 1 per-token, 2 per-tensor scales): no outlier
+// columns; step 2 instead divides every value by its column's migration
+// factor (IEEE fp32 division, as the separate smoothing quantizer does),
+// takes the per-token maxima of the smoothed values and codes them; the
+// weight is the offline-smoothed int8 weight.
+//
 // Method: AIInfra 05Quantization01, LLM.int8(): outlier columns by magnitude
 // threshold, "a. 向量级量化" (per-token / per-channel absmax scales),
 // "b. INT8 矩阵乘法与反量化" (int32 accumulation, outer-product dequant) and
-// the merge with the fp16 outlier product; Quantization explained part 2 §1.2.
+// the merge with the fp16 outlier product; Quantization explained part 2 §1.2;
+// SmoothQuant: Quantization explained part 2 §4.2 (X / s by column), §4.4.
 #include <cmath>
 #include <cstring>
 
@@ -341,13 +348,16 @@ __device__ __forceinline__ void topk_flags(const uint32_t (&cmx)[CH][4], uint32_
 // digit -- then take the keys above it and, in column order, as many keys
 // equal to it as are still missing (a ballot scan over the ties, skipped
 // when every tie is taken).
-template <int MB, int CH, bool TOPK>
+template <int MB, int CH, bool TOPK, int SM>
 __global__ __launch_bounds__(2 * DEC_THREADS) void k_decode_mixed(const uint16_t* __restrict__ X, int M, int K,
                                                                   const int8_t* __restrict__ Wq,
                                                                   const float* __restrict__ s_w,
                                                                   const uint16_t* __restrict__ W16, int64_t N,
                                                                   uint32_t thr1, void* __restrict__ out,
-                                                                  int out_dtype, DecodeStages st) {
+                                                                  int out_dtype, DecodeStages st,
+                                                                  const float* __restrict__ sm) {
+    // (the smoothed values of a lane's chunk are held in registers: one chunk, at most 8 tokens)
+    static_assert(SM == 0 || (!TOPK && CH == 1 && MB <= 8), "SmoothQuant mode: K <= 4096, M <= 8");
     constexpr int OCAP = TOPK ? DEC_OCAP_TOPK : DEC_OCAP;
     constexpr int MAXK = DEC_CHUNK_K * CH;
     constexpr int LDA = MAXK + 16;                  // LDS row stride of the codes (spreads banks)
@@ -379,6 +389,7 @@ __global__ __launch_bounds__(2 * DEC_THREADS) void k_decode_mixed(const uint16_t
     // block) into registers now: a scalar-cache miss after the weight stream
     // has started waits behind it in the memory queues.
     asm volatile("" ::"s"(out_dtype), "s"(st.idx), "s"(st.count), "s"(st.s_x), "s"(st.xq), "s"(out));
+    (void)sm;
     if (threadIdx.x == 0) abar = 0;
 
     v4i acc = v4i{0, 0, 0, 0};
@@ -393,6 +404,12 @@ __global__ __launch_bounds__(2 * DEC_THREADS) void k_decode_mixed(const uint16_t
             const int ch = t + DEC_THREADS * c;
 #pragma unroll
             for (int m = 0; m < MB; ++m) xv[c][m] = bload16(rsx, ch < nch ? (uint32_t)(m * K + 8 * ch) * 2 : kOOB);
+        }
+        u32x4 fv[SM ? 2 : 1];                         // SmoothQuant: the factors of the lane's 8 columns
+        if constexpr (SM != 0) {
+            const rsrc_t rsf = make_rsrc(sm, (int64_t)K * 4);
+            fv[0] = bload16(rsf, t < nch ? (uint32_t)t * 32 : kOOB);
+            fv[1] = bload16(rsf, t < nch ? (uint32_t)t * 32 + 16 : kOOB);
         }
         if constexpr (TOPK) {   // clear the histograms (the high-digit ones live in red until the epilogue)
             reinterpret_cast<u32x4*>(&red[0][0])[t] = u32x4{0u, 0u, 0u, 0u};
@@ -434,8 +451,40 @@ __global__ __launch_bounds__(2 * DEC_THREADS) void k_decode_mixed(const uint16_t
                                  (((flags[c] >> (2 * d + 1)) & 1u) ? 0u : 0xffff0000u);
         }
         const u16x2v T = u16x2v{(unsigned short)thr1, (unsigned short)thr1};
+        // SmoothQuant: y = fl32(x / f) for the lane's chunk and every token (0
+        // past the row), per-token maxima of |y| as bit patterns (non-negative
+        // floats order like their bits), one wave reduction per token
+        float y[SM ? MB : 1][8];
+        if constexpr (SM != 0) {
+            const bool valid = t < nch;
+            // (each element is copied to a scalar before the bit cast: a bit
+            // cast of a vector-element expression read element 0 here)
+            float fl[8];
 #pragma unroll
-        for (int c = 0; c < CH; ++c) {
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t f0 = fv[0][d], f1 = fv[1][d];
+                fl[d] = __builtin_bit_cast(float, f0);
+                fl[d + 4] = __builtin_bit_cast(float, f1);
+            }
+#pragma unroll
+            for (int m = 0; m < MB; ++m) {
+                float x[8];
+                unpack8(xv[0][m], x);
+                uint32_t a = 0u;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    y[m][j] = valid ? x[j] / fl[j] : 0.0f;
+                    a = max(a, __builtin_bit_cast(uint32_t, y[m][j]) & 0x7fffffffu);
+                }
+                a = wave_max_u32(a);
+                if (lane == 0) rmax[m][wave] = a;
+            }
+            flags[0] = 0u;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) keep[0][d] = 0xffffffffu;
+        }
+#pragma unroll
+        for (int c = 0; c < (SM ? 0 : CH); ++c) {
             if constexpr (!TOPK) {
                 uint32_t cm[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -464,7 +513,7 @@ __global__ __launch_bounds__(2 * DEC_THREADS) void k_decode_mixed(const uint16_t
             }
         }
 #pragma unroll
-        for (int g = 0; g < NG; ++g) {
+        for (int g = 0; g < (SM ? 0 : NG); ++g) {
             const uint32_t r = reduce_scatter8(rm + 8 * g);
             const uint32_t a = max(r & 0xffffu, r >> 16);
             if ((lane & 7) == 0) rmax[8 * g + (lane >> 3)][wave] = a;
@@ -501,15 +550,22 @@ __global__ __launch_bounds__(2 * DEC_THREADS) void k_decode_mixed(const uint16_t
         // per-token scales: lane m < MB reduces token m over the waves (every
         // activation wave does, so no further barrier is needed)
         float s_l = 1.0f, r_l = 1.0f;
-        if (lane < MB) {
-            const u32x4 r0 = *reinterpret_cast<const u32x4*>(&rmax[lane][0]);
-            const u32x4 r1 = *reinterpret_cast<const u32x4*>(&rmax[lane][4]);
-            const uint32_t ab = max(max(max(r0[0], r0[1]), max(r0[2], r0[3])),
-                                    max(max(r1[0], r1[1]), max(r1[2], r1[3])));
-            const float a = h2f((uint16_t)ab);
-            s_l = a == 0.0f ? 1.0f : a / 127.0f;
-            r_l = 1.0f / s_l;
-            if (wave == 0) sx_s[lane] = s_l;
+        {
+            uint32_t ab = 0u;
+            if (lane < MB) {
+                const u32x4 r0 = *reinterpret_cast<const u32x4*>(&rmax[lane][0]);
+                const u32x4 r1 = *reinterpret_cast<const u32x4*>(&rmax[lane][4]);
+                ab = max(max(max(r0[0], r0[1]), max(r0[2], r0[3])), max(max(r1[0], r1[1]), max(r1[2], r1[3])));
+            }
+            // SmoothQuant per-tensor: the maximum over every token (tokens past M are 0)
+            if constexpr (SM == 2) ab = wave_max_u32(ab);
+            if (lane < MB) {
+                // LLM.int8(): an fp16 magnitude pattern; SmoothQuant: an fp32 one
+                const float a = SM ? __builtin_bit_cast(float, ab) : h2f((uint16_t)ab);
+                s_l = a == 0.0f ? 1.0f : a / 127.0f;
+                r_l = 1.0f / s_l;
+                if (wave == 0) sx_s[lane] = s_l;
+            }
         }
 
         int total0 = 0, wbase[CH];
@@ -564,9 +620,14 @@ __global__ __launch_bounds__(2 * DEC_THREADS) void k_decode_mixed(const uint16_t
                 for (int m = 0; m < MB; ++m) {
                     const float s = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s_l), m));
                     const float r = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r_l), m));
-                    const u32x2 q = codes8_biased(xv[c][m], s, r);
-                    *reinterpret_cast<u32x2*>(aq + m * LDA + 8 * ch) =
-                        u32x2{(q[0] ^ 0x80808080u) & kb0, (q[1] ^ 0x80808080u) & kb1};
+                    if constexpr (SM != 0) {
+                        // two's-complement codes of the smoothed values (no outlier columns)
+                        *reinterpret_cast<u32x2*>(aq + m * LDA + 8 * ch) = codes8_dyn(y[m], s, r);
+                    } else {
+                        const u32x2 q = codes8_biased(xv[c][m], s, r);
+                        *reinterpret_cast<u32x2*>(aq + m * LDA + 8 * ch) =
+                            u32x2{(q[0] ^ 0x80808080u) & kb0, (q[1] ^ 0x80808080u) & kb1};
+                    }
                 }
             }
         }
@@ -702,12 +763,12 @@ static uint32_t threshold_pattern(float tau) {
     return lo + 1;
 }
 
-template <int MB, int CH, bool TOPK>
+template <int MB, int CH, bool TOPK, int SM = 0>
 static void launch_mb(const dim3& grid, hipStream_t st, const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq,
                       const float* s_w, const uint16_t* W16, int64_t N, uint32_t thr1, void* out, int out_dtype,
-                      const DecodeStages& stages) {
-    hipLaunchKernelGGL((k_decode_mixed<MB, CH, TOPK>), grid, dim3(2 * DEC_THREADS), 0, st, X, (int)M, (int)K, Wq, s_w,
-                       W16, N, thr1, out, out_dtype, stages);
+                      const DecodeStages& stages, const float* sm = nullptr) {
+    hipLaunchKernelGGL((k_decode_mixed<MB, CH, TOPK, SM>), grid, dim3(2 * DEC_THREADS), 0, st, X, (int)M, (int)K, Wq,
+                       s_w, W16, N, thr1, out, out_dtype, stages, sm);
 }
 
 template <bool TOPK>
@@ -737,6 +798,28 @@ hipError_t launch_decode_mixed(const uint16_t* X, int64_t M, int64_t K, const in
 }
 
 int64_t decode_topk_max() { return DEC_OCAP_TOPK; }
+
+bool decode_smooth_supported(int64_t M, int64_t K) { return M >= 1 && M <= 8 && K >= 256 && K % 256 == 0 && K <= DEC_CHUNK_K; }
+
+hipError_t launch_decode_smooth(const uint16_t* X, int64_t M, int64_t K, const float* sm, bool per_tensor,
+                                const int8_t* Wq, const float* s_w, int64_t N, void* out, int out_dtype,
+                                const DecodeStages& stages, hipStream_t st) {
+    if (!decode_smooth_supported(M, K)) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((N + 15) / 16));
+    // (no outlier columns: the threshold pattern is above every finite magnitude)
+    if (M <= 4) {
+        if (per_tensor)
+            launch_mb<4, 1, false, 2>(grid, st, X, M, K, Wq, s_w, nullptr, N, 0x7c00u, out, out_dtype, stages, sm);
+        else
+            launch_mb<4, 1, false, 1>(grid, st, X, M, K, Wq, s_w, nullptr, N, 0x7c00u, out, out_dtype, stages, sm);
+    } else {
+        if (per_tensor)
+            launch_mb<8, 1, false, 2>(grid, st, X, M, K, Wq, s_w, nullptr, N, 0x7c00u, out, out_dtype, stages, sm);
+        else
+            launch_mb<8, 1, false, 1>(grid, st, X, M, K, Wq, s_w, nullptr, N, 0x7c00u, out, out_dtype, stages, sm);
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_decode_topk(const uint16_t* X, int64_t M, int64_t K, int64_t k, const int8_t* Wq, const float* s_w,
                               const uint16_t* W16, int64_t N, void* out, int out_dtype, const DecodeStages& stages,

@@ -534,6 +534,13 @@ qa_status qa_qlinear_int8_smooth(const void* X_f16, int64_t M, int64_t K, const 
     int8_t* xq = reinterpret_cast<int8_t*>(ws + L.xq);
     hipStream_t st = as_stream(stream);
     const uint16_t* X = static_cast<const uint16_t*>(X_f16);
+    if (qa::decode_smooth_supported(M, K)) {
+        // decode shapes: one launch of the fused decode kernel (the count is
+        // 0, so the outlier list slot is never written)
+        return device_status(qa::launch_decode_smooth(X, M, K, s, mode == QA_SCALE_PER_TENSOR, Wq, s_w, N, out,
+                                                      (int)out_dtype, qa::DecodeStages{count, count, s_x, xq}, st),
+                             "qa_qlinear_int8_smooth (decode kernel)");
+    }
     hipError_t e = qa::launch_smoothquant_i8(X, M, K, s, false, mode == QA_SCALE_PER_TENSOR, xq, s_x, count, st);
     if (e != hipSuccess) return device_status(e, "qa_qlinear_int8_smooth (smoothing quantization)");
     qa::MixedEpilogue ep;
