@@ -396,6 +396,7 @@ def test_mixed_tail_split(qa, pass_w16):
     (768, 4112, 22000, 5, True, 6.0),        # 258 tiles, 65 K steps
     (1024, 1024, 17000, 150, False, 6.0),    # 268 tiles, 150 outlier columns: several staging passes
     (1030, 2048, 16500, 0, False, float("inf")),  # 325 tiles, no outlier columns
+    (2048, 64, 11008, 0, True, -1.0),        # 344 tiles, K below one staging pass: every column an outlier
 ])
 def test_mixed_partial_rounds(qa, M, K, N, n_dims, pass_w16, tau):
     """More 256 x 256 tiles than one round over the 256 CUs but not whole
