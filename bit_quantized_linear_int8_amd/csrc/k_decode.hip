@@ -799,7 +799,9 @@ hipError_t launch_decode_mixed(const uint16_t* X, int64_t M, int64_t K, const in
 
 int64_t decode_topk_max() { return DEC_OCAP_TOPK; }
 
-bool decode_smooth_supported(int64_t M, int64_t K) { return M >= 1 && M <= 8 && K >= 256 && K % 256 == 0 && K <= DEC_CHUNK_K; }
+bool decode_smooth_supported(int64_t M, int64_t K) {
+    return M >= 1 && M <= 8 && K >= 256 && K % 256 == 0 && K <= DEC_CHUNK_K;
+}
 
 hipError_t launch_decode_smooth(const uint16_t* X, int64_t M, int64_t K, const float* sm, bool per_tensor,
                                 const int8_t* Wq, const float* s_w, int64_t N, void* out, int out_dtype,

@@ -656,6 +656,7 @@ __global__ __launch_bounds__(256) void k_rowquant_i8(const uint16_t* __restrict_
             if constexpr (XCHG) {
                 if (lane == 0) pmx[wave] = ab & 0x7fffffffu;      // (a -0.0 maximum would order last)
                 lds_only_barrier();
+                ab = 0u;                                            // every wave of the row, this one included
 #pragma unroll
                 for (int q = 0; q < WPR; ++q) ab = max(ab, pmx[wave - part + q]);
                 if (!live) return;

@@ -39,8 +39,9 @@ hipError_t launch_smooth_factors(const float* cx, const float* cw, int64_t K, fl
 // (K <= 512 NC) and reads X once, split over WPR waves (part p of the row's
 // WPR waves owns chunks p 64 NC / WPR + l + 64 i in lane l), which combine
 // their row maxima through LDS; NC == 0 is one wave per row, lane l owning
-// the chunks l + 64 i, and reads the row twice (absmax pass, codes pass).  The factor vector is read with the row (it is
-// shared by every row, so after the first rows it comes from the caches).
+// the chunks l + 64 i, and reads the row twice (absmax pass, codes pass).
+// The factor vector is read with the row (it is shared by every row, so
+// after the first rows it comes from the caches).
 //
 // Phases:
 //   SQ_ROW     per-row dynamic scale: s_out[row] = fl32(absmax / 127), codes
