@@ -356,8 +356,11 @@ __global__ __launch_bounds__(2 * DEC_THREADS) void k_decode_mixed(const uint16_t
                                                                   uint32_t thr1, void* __restrict__ out,
                                                                   int out_dtype, DecodeStages st,
                                                                   const float* __restrict__ sm) {
-    // (the smoothed values of a lane's chunk are held in registers: one chunk, at most 8 tokens)
-    static_assert(SM == 0 || (!TOPK && CH == 1 && MB <= 8), "SmoothQuant mode: K <= 4096, M <= 8");
+    static_assert(SM == 0 || !TOPK, "SmoothQuant mode has no outlier set");
+    // SmoothQuant: the smoothed values are held in registers from the maxima
+    // to the codes when they fit (one chunk, at most 8 tokens); otherwise the
+    // codes pass divides again (the same IEEE operation, the same values)
+    constexpr bool HOLD = SM != 0 && CH == 1 && MB <= 8;
     constexpr int OCAP = TOPK ? DEC_OCAP_TOPK : DEC_OCAP;
     constexpr int MAXK = DEC_CHUNK_K * CH;
     constexpr int LDA = MAXK + 16;                  // LDS row stride of the codes (spreads banks)
@@ -405,11 +408,15 @@ __global__ __launch_bounds__(2 * DEC_THREADS) void k_decode_mixed(const uint16_t
 #pragma unroll
             for (int m = 0; m < MB; ++m) xv[c][m] = bload16(rsx, ch < nch ? (uint32_t)(m * K + 8 * ch) * 2 : kOOB);
         }
-        u32x4 fv[SM ? 2 : 1];                         // SmoothQuant: the factors of the lane's 8 columns
+        u32x4 fv[SM ? CH : 1][2];                     // SmoothQuant: the factors of each chunk's 8 columns
         if constexpr (SM != 0) {
             const rsrc_t rsf = make_rsrc(sm, (int64_t)K * 4);
-            fv[0] = bload16(rsf, t < nch ? (uint32_t)t * 32 : kOOB);
-            fv[1] = bload16(rsf, t < nch ? (uint32_t)t * 32 + 16 : kOOB);
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                const int ch = t + DEC_THREADS * c;
+                fv[c][0] = bload16(rsf, ch < nch ? (uint32_t)ch * 32 : kOOB);
+                fv[c][1] = bload16(rsf, ch < nch ? (uint32_t)ch * 32 + 16 : kOOB);
+            }
         }
         if constexpr (TOPK) {   // clear the histograms (the high-digit ones live in red until the epilogue)
             reinterpret_cast<u32x4*>(&red[0][0])[t] = u32x4{0u, 0u, 0u, 0u};
@@ -418,6 +425,18 @@ __global__ __launch_bounds__(2 * DEC_THREADS) void k_decode_mixed(const uint16_t
         // the weight waves issue their stream once every X request is issued
         lds_barrier();                                                  // barrier 1
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if constexpr (SM != 0) {
+            // Pin the loaded X and factors here: the smoothing divisions are
+            // plain arithmetic that the compiler otherwise hoists above barrier 1
+            // (with the waits for X they need), which holds the weight waves
+            // at that barrier until X has arrived.
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+#pragma unroll
+                for (int m = 0; m < MB; ++m) asm volatile("" : "+v"(xv[c][m]));
+                asm volatile("" : "+v"(fv[c][0]), "+v"(fv[c][1]));
+            }
+        }
 
         // 2a. column max over the tokens on |x| bit patterns (fp16 magnitudes
         //     order like their bits); column j is an outlier when that max is
@@ -451,37 +470,47 @@ __global__ __launch_bounds__(2 * DEC_THREADS) void k_decode_mixed(const uint16_t
                                  (((flags[c] >> (2 * d + 1)) & 1u) ? 0u : 0xffff0000u);
         }
         const u16x2v T = u16x2v{(unsigned short)thr1, (unsigned short)thr1};
-        // SmoothQuant: y = fl32(x / f) for the lane's chunk and every token (0
+        // SmoothQuant: y = fl32(x / f) for the lane's chunks and every token (0
         // past the row), per-token maxima of |y| as bit patterns (non-negative
         // floats order like their bits), one wave reduction per token
-        float y[SM ? MB : 1][8];
-        if constexpr (SM != 0) {
-            const bool valid = t < nch;
-            // (each element is copied to a scalar before the bit cast: a bit
-            // cast of a vector-element expression read element 0 here)
-            float fl[8];
+        // (each factor element is copied to a scalar before its bit cast: a
+        // bit cast of a vector-element expression read element 0 here)
+        // Past the row X reads 0 and the divisor is taken as 1, so y = 0 there
+        // with no branch: a division under a condition became a branch whose
+        // X load the compiler sank past barrier 1, behind the weight stream.
+        auto smooth_chunk = [&](int c, int m, float* y8) __attribute__((always_inline)) {
+            const bool valid = t + DEC_THREADS * c < nch;
+            float x[8];
+            unpack8(xv[c][m], x);
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
-                const uint32_t f0 = fv[0][d], f1 = fv[1][d];
-                fl[d] = __builtin_bit_cast(float, f0);
-                fl[d + 4] = __builtin_bit_cast(float, f1);
+                const uint32_t f0 = fv[SM ? c : 0][0][d], f1 = fv[SM ? c : 0][1][d];
+                y8[d] = x[d] / (valid ? __builtin_bit_cast(float, f0) : 1.0f);
+                y8[d + 4] = x[d + 4] / (valid ? __builtin_bit_cast(float, f1) : 1.0f);
             }
+        };
+        float y[HOLD ? MB : 1][8];
+        if constexpr (SM != 0) {
 #pragma unroll
             for (int m = 0; m < MB; ++m) {
-                float x[8];
-                unpack8(xv[0][m], x);
                 uint32_t a = 0u;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    y[m][j] = valid ? x[j] / fl[j] : 0.0f;
-                    a = max(a, __builtin_bit_cast(uint32_t, y[m][j]) & 0x7fffffffu);
+                for (int c = 0; c < CH; ++c) {
+                    float yt[8];
+                    float* yc = HOLD ? y[HOLD ? m : 0] : yt;
+                    smooth_chunk(c, m, yc);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) a = max(a, __builtin_bit_cast(uint32_t, yc[j]) & 0x7fffffffu);
                 }
                 a = wave_max_u32(a);
                 if (lane == 0) rmax[m][wave] = a;
             }
-            flags[0] = 0u;
 #pragma unroll
-            for (int d = 0; d < 4; ++d) keep[0][d] = 0xffffffffu;
+            for (int c = 0; c < CH; ++c) {
+                flags[c] = 0u;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) keep[c][d] = 0xffffffffu;
+            }
         }
 #pragma unroll
         for (int c = 0; c < (SM ? 0 : CH); ++c) {
@@ -622,7 +651,9 @@ __global__ __launch_bounds__(2 * DEC_THREADS) void k_decode_mixed(const uint16_t
                     const float r = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r_l), m));
                     if constexpr (SM != 0) {
                         // two's-complement codes of the smoothed values (no outlier columns)
-                        *reinterpret_cast<u32x2*>(aq + m * LDA + 8 * ch) = codes8_dyn(y[m], s, r);
+                        float yt[8];
+                        if constexpr (!HOLD) smooth_chunk(c, m, yt);
+                        *reinterpret_cast<u32x2*>(aq + m * LDA + 8 * ch) = codes8_dyn(HOLD ? y[HOLD ? m : 0] : yt, s, r);
                     } else {
                         const u32x2 q = codes8_biased(xv[c][m], s, r);
                         *reinterpret_cast<u32x2*>(aq + m * LDA + 8 * ch) =
@@ -799,8 +830,26 @@ hipError_t launch_decode_mixed(const uint16_t* X, int64_t M, int64_t K, const in
 
 int64_t decode_topk_max() { return DEC_OCAP_TOPK; }
 
+// SmoothQuant in the fused kernel: the shapes whose smoothing fits the
+// registers of four waves per SIMD without spilling (M <= 8 at K <= 4096,
+// M <= 4 at K <= 8192); larger ones keep the smoothing quantizer + GEMV.
 bool decode_smooth_supported(int64_t M, int64_t K) {
-    return M >= 1 && M <= 8 && K >= 256 && K % 256 == 0 && K <= DEC_CHUNK_K;
+    if (M < 1 || K < 256 || K % 256 != 0) return false;
+    return (M <= 8 && K <= DEC_CHUNK_K) || (M <= 4 && K <= 2 * DEC_CHUNK_K);
+}
+
+template <int SM>
+static void launch_smooth_sm(const dim3& grid, hipStream_t st, const uint16_t* X, int64_t M, int64_t K,
+                             const int8_t* Wq, const float* s_w, int64_t N, void* out, int out_dtype,
+                             const DecodeStages& stages, const float* sm) {
+    // (no outlier columns: the threshold pattern is above every finite magnitude)
+    constexpr uint32_t NOT = 0x7c00u;
+    if (K > DEC_CHUNK_K)
+        launch_mb<4, 2, false, SM>(grid, st, X, M, K, Wq, s_w, nullptr, N, NOT, out, out_dtype, stages, sm);
+    else if (M <= 4)
+        launch_mb<4, 1, false, SM>(grid, st, X, M, K, Wq, s_w, nullptr, N, NOT, out, out_dtype, stages, sm);
+    else
+        launch_mb<8, 1, false, SM>(grid, st, X, M, K, Wq, s_w, nullptr, N, NOT, out, out_dtype, stages, sm);
 }
 
 hipError_t launch_decode_smooth(const uint16_t* X, int64_t M, int64_t K, const float* sm, bool per_tensor,
@@ -808,18 +857,10 @@ hipError_t launch_decode_smooth(const uint16_t* X, int64_t M, int64_t K, const f
                                 const DecodeStages& stages, hipStream_t st) {
     if (!decode_smooth_supported(M, K)) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((N + 15) / 16));
-    // (no outlier columns: the threshold pattern is above every finite magnitude)
-    if (M <= 4) {
-        if (per_tensor)
-            launch_mb<4, 1, false, 2>(grid, st, X, M, K, Wq, s_w, nullptr, N, 0x7c00u, out, out_dtype, stages, sm);
-        else
-            launch_mb<4, 1, false, 1>(grid, st, X, M, K, Wq, s_w, nullptr, N, 0x7c00u, out, out_dtype, stages, sm);
-    } else {
-        if (per_tensor)
-            launch_mb<8, 1, false, 2>(grid, st, X, M, K, Wq, s_w, nullptr, N, 0x7c00u, out, out_dtype, stages, sm);
-        else
-            launch_mb<8, 1, false, 1>(grid, st, X, M, K, Wq, s_w, nullptr, N, 0x7c00u, out, out_dtype, stages, sm);
-    }
+    if (per_tensor)
+        launch_smooth_sm<2>(grid, st, X, M, K, Wq, s_w, N, out, out_dtype, stages, sm);
+    else
+        launch_smooth_sm<1>(grid, st, X, M, K, Wq, s_w, N, out, out_dtype, stages, sm);
     return hipGetLastError();
 }
 

@@ -178,7 +178,8 @@ hipError_t launch_decode_topk(const uint16_t* X, int64_t M, int64_t K, int64_t k
 // The SmoothQuant linear for decode shapes in the same single kernel: X / sm by
 // column (IEEE fp32 division), per-token or (per_tensor) one scale, int8 codes,
 // the product with the offline-smoothed weight; no outlier columns.  Needs
-// decode_smooth_supported(M, K) (M <= 8, K % 256 == 0, K <= 4096).
+// decode_smooth_supported(M, K) (M <= 8 at K <= 4096, M <= 4 at K <= 8192,
+// K % 256 == 0).
 bool decode_smooth_supported(int64_t M, int64_t K);
 hipError_t launch_decode_smooth(const uint16_t* X, int64_t M, int64_t K, const float* sm, bool per_tensor,
                                 const int8_t* Wq, const float* s_w, int64_t N, void* out, int out_dtype,

@@ -486,8 +486,9 @@ qa_status qa_quantize_smooth_int8(const void* A_f16, int64_t rows, int64_t K, co
  *   out     [M x N] of out_dtype
  *   workspace  qa_qlinear_int8_smooth_workspace(M, K) bytes (any content);
  *           after the call it holds s_x and Xq
- * Decode shapes (M <= 8, K % 256 == 0, K <= 4096) run as one kernel that
- * smooths, quantizes and multiplies; the results are the same bits.
+ * Decode shapes (K % 256 == 0 with M <= 8 at K <= 4096 or M <= 4 at
+ * K <= 8192) run as one kernel that smooths, quantizes and multiplies; the
+ * results are the same bits.
  * Errors: NULL pointers, M < 0, N < 0, K <= 0, K % 16 != 0, K > 131072,
  * misaligned pointers, bad mode or out_dtype, small workspace.
  * ------------------------------------------------------------------------- */

@@ -136,7 +136,7 @@ def test_qlinear_smooth_decode_shapes(qa, M):
 @pytest.mark.parametrize("K,N", [(256, 1), (1024, 40), (3072, 100), (4096, 33)])
 @pytest.mark.parametrize("per_tensor", [False, True])
 def test_qlinear_smooth_decode_kernel_shapes(qa, M, K, N, per_tensor):
-    # M <= 8 with K % 256 == 0, K <= 4096 runs the fused single-kernel path
+    # M <= 8 with K % 256 == 0, K <= 4096 runs the fused single-kernel path (smoothed values held)
     X, W, _ = synthetic.mixed_inputs(M, K, N, seed=M * 7 + K + N, n_dims=5, p_token=1.0)
     if M > 2:
         X[1, :] = 0                                        # an all-zero token: scale 1 (per token)
@@ -146,6 +146,36 @@ def test_qlinear_smooth_decode_kernel_shapes(qa, M, K, N, per_tensor):
     out = qa.qa_qlinear_int8_smooth(dev(X), dev(s), dev(Wq), dev(s_w), per_tensor=per_tensor, out_dtype=ODT[odt])
     ref = oracle.qlinear_int8_smooth(X, s, Wq, s_w, per_tensor=per_tensor)
     assert_float_parity(as_f64(out), ref, ODT[odt])
+
+
+@pytest.mark.parametrize("M", [1, 3, 4])
+@pytest.mark.parametrize("K,N", [(4352, 17), (8192, 48)])
+@pytest.mark.parametrize("per_tensor", [False, True])
+def test_qlinear_smooth_decode_kernel_k8192(qa, M, K, N, per_tensor):
+    # M <= 4 with K up to 8192 (the pages' hidden size): two chunks per lane,
+    # the division redone in the codes pass instead of held
+    X, W, _ = synthetic.mixed_inputs(M, K, N, seed=M * 11 + K + N, n_dims=5, p_token=1.0)
+    s = factors(X, W)
+    Wq, s_w = oracle.smooth_quantize(W, s, oracle.SMOOTH_MULTIPLY)
+    out = qa.qa_qlinear_int8_smooth(dev(X), dev(s), dev(Wq), dev(s_w), per_tensor=per_tensor, out_dtype=torch.float32)
+    ref = oracle.qlinear_int8_smooth(X, s, Wq, s_w, per_tensor=per_tensor)
+    assert_float_parity(as_f64(out), ref, torch.float32)
+
+
+def test_qlinear_smooth_decode_k8192_one_hot_codes(qa):
+    """4 tokens at K = 8192 against a one-hot int8 weight: every smoothed
+    code and scale of the fused kernel's two-chunk path, bit for bit."""
+    M, K = 4, 8192
+    X, W, _ = synthetic.mixed_inputs(M, K, 64, seed=81, n_dims=6, magnitude=("abs_normal", 20.0), p_token=1.0)
+    s = factors(X, W)
+    Wq = np.zeros((K, K), np.int8)
+    Wq[np.arange(K), np.arange(K)] = 127
+    out = host(qa.qa_qlinear_int8_smooth(dev(X), dev(s), dev(Wq), dev(np.ones(K, np.float32)),
+                                         out_dtype=torch.float32))
+    oq, os_ = oracle.smooth_quantize(X, s, oracle.SMOOTH_DIVIDE)
+    want = (127 * oq.astype(np.int32)).astype(np.float32) * np.asarray(os_, np.float32).reshape(-1, 1)
+    bad = np.argwhere(out != want)
+    assert bad.size == 0, "%d outputs differ, first at %s" % (len(bad), bad[:4].tolist())
 
 
 @pytest.mark.parametrize("per_tensor", [False, True])
@@ -168,10 +198,10 @@ def test_qlinear_smooth_decode_one_hot_codes(qa, per_tensor):
     assert bad.size == 0, "%d outputs differ, first at %s" % (len(bad), bad[:4].tolist())
 
 
-@pytest.mark.parametrize("M,K,N", [(4, 8192, 33), (12, 3072, 50), (9, 8192, 100), (16, 5120, 40)])
+@pytest.mark.parametrize("M,K,N", [(5, 8192, 33), (12, 3072, 50), (9, 8192, 100), (16, 5120, 40)])
 def test_qlinear_smooth_gemv_shapes(qa, M, K, N):
-    # decode-size calls that the fused decode kernel does not take (M > 8 or
-    # K > 4096) run the int8 GEMM as a GEMV: codes staged in LDS while
+    # decode-size calls that the fused decode kernel does not take (M > 8, or
+    # M > 4 with K > 4096) run the int8 GEMM as a GEMV: codes staged in LDS while
     # M K <= 64 KB (K = 8192: two batches of K steps per wave, K = 3072: one),
     # else loaded per wave
     X, W, _ = synthetic.mixed_inputs(M, K, N, seed=M + K + N, n_dims=5, p_token=1.0)
