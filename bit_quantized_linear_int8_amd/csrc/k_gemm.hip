@@ -666,63 +666,110 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_i8_mixed(const int8_t* __re
 //   a[n] = r_w[n] - K z_w[n],  r_x / r_w = row sums of the codes,
 // evaluated in int32 (exact while the result fits, K <= 32768), then
 // out = that * s_x[m] * s_w[n].  ZW = false: symmetric weight (z_w = 0).
+// tsn: output columns per tile, as for k_gemm_i8_mixed.
 // ---------------------------------------------------------------------------
 template <class C, bool ZW>
 __global__ __launch_bounds__(C::THREADS) void k_gemm_i8_asym(const int8_t* __restrict__ Xq,
                                                              const int8_t* __restrict__ Wq, int64_t M, int64_t K,
-                                                             int64_t N, AsymEpilogue ep, int tiles_m, int tiles_n) {
+                                                             int64_t N, AsymEpilogue ep, int tiles_m, int tiles_n,
+                                                             int tsn) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
     int tm, tn;
     tile_of_block(blockIdx.x, tiles_m, tiles_n, tm, tn);
-    const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
+    const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * tsn;
+    const int64_t nlim = n0 + tsn < N ? n0 + tsn : N;     // columns this tile stores: [n0, nlim)
     v4i acc[C::FM][C::FN];
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int wm = wave / C::WN, wn = wave % C::WN;
     const int64_t rb = m0 + wm * C::TM, cb = n0 + wn * C::TN;
-    // per-column and per-row terms, loaded before the main loop
-    const rsrc_t rsw = make_rsrc(ep.s_w + cb, (N - cb) * 4);
-    const rsrc_t rrw = make_rsrc(ep.r_w + cb, (N - cb) * 4);
-    const rsrc_t rzw = make_rsrc(ZW ? ep.z_w + cb : ep.r_w, ZW ? (N - cb) * 4 : 0);
+    // Per-column and per-row terms, loaded before the main loop; with many
+    // column fragments (registers are short) they are loaded after it, the
+    // column terms of the tile into LDS, read per fragment.
+    constexpr bool LATE = C::FN > 4;
+    constexpr int CT = LATE ? 1 : C::FN;
     const rsrc_t rsx = make_rsrc(ep.s_x + rb, (M - rb) * 4);
     const rsrc_t rzx = make_rsrc(ep.z_x + rb, (M - rb) * 4);
     const rsrc_t rrx = make_rsrc(ZW ? ep.r_x + rb : ep.z_x, ZW ? (M - rb) * 4 : 0);
-    float sw[C::FN][4], sxv[C::FM];
-    int32_t an[C::FN][4], zwv[ZW ? C::FN : 1][4], zxv[C::FM], rxv[ZW ? C::FM : 1];
+    float sw[CT][4], sxv[C::FM];
+    int32_t an[CT][4], zwv[ZW ? CT : 1][4], zxv[C::FM], rxv[ZW ? C::FM : 1];
+    auto load_rows = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t off = (uint32_t)(j * 16 + 4 * (lane >> 4) + e) * 4;
-            sw[j][e] = __builtin_bit_cast(float, bload4(rsw, off));
-            const int32_t z = ZW ? (int32_t)bload4(rzw, off) : 0;
-            an[j][e] = (int32_t)bload4(rrw, off) - (int32_t)K * z;
-            if constexpr (ZW) zwv[j][e] = z;
+        for (int i = 0; i < C::FM; ++i) {
+            const uint32_t off = (uint32_t)(i * 16 + (lane & 15)) * 4;
+            sxv[i] = __builtin_bit_cast(float, bload4(rsx, off));
+            zxv[i] = (int32_t)bload4(rzx, off);
+            if constexpr (ZW) rxv[i] = (int32_t)bload4(rrx, off);
         }
+    };
+    if constexpr (!LATE) {
+        const rsrc_t rsw = make_rsrc(ep.s_w + cb, (N - cb) * 4);
+        const rsrc_t rrw = make_rsrc(ep.r_w + cb, (N - cb) * 4);
+        const rsrc_t rzw = make_rsrc(ZW ? ep.z_w + cb : ep.r_w, ZW ? (N - cb) * 4 : 0);
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i) {
-        const uint32_t off = (uint32_t)(i * 16 + (lane & 15)) * 4;
-        sxv[i] = __builtin_bit_cast(float, bload4(rsx, off));
-        zxv[i] = (int32_t)bload4(rzx, off);
-        if constexpr (ZW) rxv[i] = (int32_t)bload4(rrx, off);
+        for (int j = 0; j < CT; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t off = (uint32_t)(j * 16 + 4 * (lane >> 4) + e) * 4;
+                sw[j][e] = __builtin_bit_cast(float, bload4(rsw, off));
+                const int32_t z = ZW ? (int32_t)bload4(rzw, off) : 0;
+                an[j][e] = (int32_t)bload4(rrw, off) - (int32_t)K * z;
+                if constexpr (ZW) zwv[j][e] = z;
+            }
+        load_rows();
     }
     mainloop_any<C>(Xq, Wq, M, N, K, m0, n0, smem, acc);
-    const bool vec = ((ep.ldo | N) & 3) == 0;
+    // LATE: s_w, a and z_w of the tile's C::BN columns, LDS being free after
+    // the main loop (it ends with a barrier)
+    float* swe = reinterpret_cast<float*>(smem);
+    int32_t* ane = reinterpret_cast<int32_t*>(smem) + C::BN;
+    int32_t* zwe = reinterpret_cast<int32_t*>(smem) + 2 * C::BN;
+    if constexpr (LATE) {
+        static_assert(3 * C::BN * 4 <= C::LDS, "epilogue terms exceed LDS");
+        load_rows();
+        const rsrc_t rsn = make_rsrc(ep.s_w + n0, (N - n0) * 4);
+        const rsrc_t rrn = make_rsrc(ep.r_w + n0, (N - n0) * 4);
+        const rsrc_t rzn = make_rsrc(ZW ? ep.z_w + n0 : ep.r_w, ZW ? (N - n0) * 4 : 0);
+        for (int r = threadIdx.x; r < C::BN; r += C::THREADS) {
+            const uint32_t off = (uint32_t)r * 4;
+            const int32_t z = ZW ? (int32_t)bload4(rzn, off) : 0;
+            swe[r] = __builtin_bit_cast(float, bload4(rsn, off));
+            ane[r] = (int32_t)bload4(rrn, off) - (int32_t)K * z;
+            zwe[r] = z;
+        }
+        __syncthreads();
+    }
+    const bool vec = ((ep.ldo | N | tsn) & 3) == 0;
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) {
         const int64_t row = rb + i * 16 + (lane & 15);
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) {
+            v4f s4;
+            v4i a4, z4;
+            if constexpr (LATE) {
+                const int t = wn * C::TN + j * 16 + 4 * (lane >> 4);
+                s4 = *reinterpret_cast<const v4f*>(swe + t);
+                a4 = *reinterpret_cast<const v4i*>(ane + t);
+                z4 = *reinterpret_cast<const v4i*>(zwe + t);
+            } else {
+                const int jj = LATE ? 0 : j;
+                s4 = v4f{sw[jj][0], sw[jj][1], sw[jj][2], sw[jj][3]};
+                a4 = v4i{an[jj][0], an[jj][1], an[jj][2], an[jj][3]};
+                if constexpr (ZW) z4 = v4i{zwv[jj][0], zwv[jj][1], zwv[jj][2], zwv[jj][3]};
+                else z4 = v4i{0, 0, 0, 0};
+            }
             v4f cf;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 // wrap-around int32 arithmetic: exact whenever the result fits
-                uint32_t c = (uint32_t)acc[i][j][e] - (uint32_t)zxv[i] * (uint32_t)an[j][e];
-                if constexpr (ZW) c -= (uint32_t)zwv[j][e] * (uint32_t)rxv[i];
-                cf[e] = (float)(int32_t)c * sxv[i] * sw[j][e];
+                uint32_t c = (uint32_t)acc[i][j][e] - (uint32_t)zxv[i] * (uint32_t)a4[e];
+                if constexpr (ZW) c -= (uint32_t)z4[e] * (uint32_t)rxv[i];
+                cf[e] = (float)(int32_t)c * sxv[i] * s4[e];
             }
             const int64_t col = cb + j * 16 + 4 * (lane >> 4);
-            if (row < M && col < N)
-                store_out4(ep.out, ep.out_dtype, row * ep.ldo + col, cf, vec, (int)(N - col < 4 ? N - col : 4));
+            if (row < M && col < nlim)
+                store_out4(ep.out, ep.out_dtype, row * ep.ldo + col, cf, vec,
+                           (int)(nlim - col < 4 ? nlim - col : 4));
         }
     }
 }
@@ -1910,10 +1957,17 @@ static void launch_asym_cfgs(const int8_t* Xq, const int8_t* Wq, int64_t M, int6
                              const AsymEpilogue& ep, hipStream_t st) {
     int tm, tn;
     if (pick_cfg(M, N) == 2) {
+        if (const int tsn = wide_stride(M, N)) {
+            tm = (int)((M + 255) / 256);
+            tn = (int)((N + tsn - 1) / tsn);
+            hipLaunchKernelGGL((k_gemm_i8_asym<CfgWide, ZW>), dim3((unsigned)(tm * tn)), dim3(CfgWide::THREADS), 0,
+                               st, Xq, Wq, M, K, N, ep, tm, tn, tsn);
+            return;
+        }
         if (const int64_t split = tail_split(M, N)) {
             dim3 g = grid_of<CfgBig>(M, split, tm, tn);
             hipLaunchKernelGGL((k_gemm_i8_asym<CfgBig, ZW>), g, dim3(CfgBig::THREADS), 0, st, Xq, Wq, M, K, split,
-                               ep, tm, tn);
+                               ep, tm, tn, CfgBig::BN);
             const int esz = ep.out_dtype == 0 ? 4 : 2;
             AsymEpilogue et = ep;
             et.s_w = ep.s_w + split;
@@ -1922,7 +1976,7 @@ static void launch_asym_cfgs(const int8_t* Xq, const int8_t* Wq, int64_t M, int6
             et.out = static_cast<uint8_t*>(ep.out) + split * esz;
             g = grid_of<CfgTail>(M, N - split, tm, tn);
             hipLaunchKernelGGL((k_gemm_i8_asym<CfgTail, ZW>), g, dim3(CfgTail::THREADS), 0, st, Xq, Wq + split * K,
-                               M, K, N - split, et, tm, tn);
+                               M, K, N - split, et, tm, tn, CfgTail::BN);
             return;
         }
     }
@@ -1930,19 +1984,19 @@ static void launch_asym_cfgs(const int8_t* Xq, const int8_t* Wq, int64_t M, int6
         case 2: {
             dim3 g = grid_of<CfgBig>(M, N, tm, tn);
             hipLaunchKernelGGL((k_gemm_i8_asym<CfgBig, ZW>), g, dim3(CfgBig::THREADS), 0, st, Xq, Wq, M, K, N, ep,
-                               tm, tn);
+                               tm, tn, CfgBig::BN);
             break;
         }
         case 1: {
             dim3 g = grid_of<CfgMid>(M, N, tm, tn);
             hipLaunchKernelGGL((k_gemm_i8_asym<CfgMid, ZW>), g, dim3(CfgMid::THREADS), 0, st, Xq, Wq, M, K, N, ep,
-                               tm, tn);
+                               tm, tn, CfgMid::BN);
             break;
         }
         default: {
             dim3 g = grid_of<CfgSmall>(M, N, tm, tn);
             hipLaunchKernelGGL((k_gemm_i8_asym<CfgSmall, ZW>), g, dim3(CfgSmall::THREADS), 0, st, Xq, Wq, M, K, N,
-                               ep, tm, tn);
+                               ep, tm, tn, CfgSmall::BN);
         }
     }
 }

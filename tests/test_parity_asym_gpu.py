@@ -140,6 +140,20 @@ def test_asym_linear_prefill_size_sampled(qa, asym_w):
 
 
 def test_asym_linear_tail_split(qa):
-    M, K, N = 300, 128, 129 * 256 + 72
+    # 16 x 43 tiles of 256 x 256: two whole rounds over the 256 CUs, the
+    # trailing 2816 columns in a second launch of 128 x 256 tiles
+    M, K, N = 4096, 64, 11008
     X, W, _ = synthetic.mixed_inputs(M, K, N, seed=63, n_dims=3)
-    _asym_case(qa, X, W, True, 1)
+    _asym_case(qa, X, W, True, 1, rows=tile_rows(M, 128, extra=4))
+
+
+@pytest.mark.parametrize("M,K,N,asym_w,rows", [
+    (300, 128, 129 * 256 + 72, True, False),   # 2 x 126 tiles of 256 x 264, ragged M and N
+    (3000, 528, 6000, False, True),            # 12 x 21 tiles of 256 x 288, partial last K step
+    (2048, 64, 11008, True, True),             # 8 x 32 tiles of 256 x 344
+])
+def test_asym_linear_wide_tiles(qa, M, K, N, asym_w, rows):
+    # one-round wide tiles: each computes 352 columns and stores its stride
+    X, W, _ = synthetic.mixed_inputs(M, K, N, seed=M + N, n_dims=3, p_token=0.75)
+    X[: M // 4] = np.abs(X[: M // 4])
+    _asym_case(qa, X, W, asym_w, 2 if rows else 1, rows=tile_rows(M, 256, extra=6) if rows else None)
